@@ -1,0 +1,358 @@
+"""CPU oracle for the fused top-k Mixture-of-Experts SwiGLU layer.
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the product path may import or call this
+module: only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline``
+leg of ``bench.py`` use it.  It shares no code with the HIP library.
+
+It is deliberately plain and slow: numpy, float64 arithmetic for every
+floating-point value it produces, no blocking or fusion.  Where a step takes
+a discrete decision on floating-point values (which experts a token selects,
+which groups stay eligible) the decision is taken on float32 values, the
+precision of the kernel, as the rounding of the decision inputs is part of
+what the layer computes.
+
+Source pages (cited by title and section):
+
+* [MKR] "Mixture-of-Experts Kernels: Routing, Permutation, and Grouped GEMM"
+  (book chapter): section 1 (layer definition, model table), section 2 (route,
+  align, grouped GEMM, combine; flat row r = t*k + j), section 3 (two ground-truth
+  implementations: per-expert loop and dense run-all-then-mask), section 4
+  (sigmoid + selection-bias + group-limited routing), section 5 (the
+  sorted_ids / expert_ids / padded-total contract), section 6 (GEMM1 gathers
+  x rows r//k against W13[e] = [W1;W3], GEMM2 multiplies by the router weight
+  and stores at row r, combine sums the k slots), section 10 (test matrix).
+* [CKM] "Custom Kernels for Mixture-of-Experts": device-resident dispatch
+  metadata (grouped GEMM section).
+* [FMK] "fused-moe-kernel" skill page: padding ids must be >= the number of
+  valid rows (Common Pitfalls).
+
+Readings where the pages leave a step open (each also listed in the design doc):
+
+1. ties: the lower expert index (and the lower group index) wins;
+2. softmax-top-k-renormalise selects on the fp32 logits; because softmax is
+   monotone and the full-softmax denominator cancels in the renormalisation,
+   the weights equal a softmax over the k selected logits ([MKR] section 3);
+3. slot order j is the selection order (descending score, ties by index);
+4. the sigmoid score used for selection is sigma(l) evaluated in float64 and
+   rounded to the nearest float32; the biased score and the group score are
+   float32 additions;
+5. sentinel = T*k; buffer tails past the padded total hold the sentinel in
+   sorted_ids and -1 in expert_ids;
+6. for bf16 layers the SwiGLU activation a (GEMM2's input) is rounded to bf16
+   (round-to-nearest-even); all other intermediates stay in float64 here.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+SOFTMAX_TOPK_RENORM = 0
+TOPK_THEN_SOFTMAX = 1
+SIGMOID_BIAS_GROUPED = 2
+
+
+# --------------------------------------------------------------------------- rounding
+
+def bf16_round(a) -> np.ndarray:
+    """Round float64 values to the nearest bf16 value (8 significant bits,
+    ties to even), returned as float64.  Normal range only (|a| >= 2^-126 or 0),
+    which covers every value this layer produces."""
+    a = np.asarray(a, dtype=np.float64)
+    m, e = np.frexp(a)                 # a = m * 2**e with 0.5 <= |m| < 1
+    q = np.rint(m * 256.0) / 256.0     # keep 8 significant bits, half to even
+    return np.ldexp(q, e)
+
+
+def f32(a) -> np.ndarray:
+    return np.asarray(a, dtype=np.float32)
+
+
+# --------------------------------------------------------------------------- routing ([MKR] s3, s4)
+
+def router_logits(x, wg) -> np.ndarray:
+    """logits[t, e] = sum_h x[t, h] * Wg[e, h]  (float64)."""
+    return np.asarray(x, np.float64) @ np.asarray(wg, np.float64).T
+
+
+def order_first(values_row, candidates=None) -> np.ndarray:
+    """Indices sorted by the order rule: a before b iff v_a > v_b, or v_a == v_b and
+    a < b.  Optionally restricted to ``candidates`` (an index array)."""
+    v = np.asarray(values_row)
+    idx = np.arange(v.shape[0]) if candidates is None else np.asarray(candidates)
+    vv = v[idx]
+    o = np.lexsort((idx, -vv.astype(np.float64)))   # primary: value desc, secondary: index asc
+    return idx[o]
+
+
+def sigmoid_f32(logits32) -> np.ndarray:
+    """sigma(l) = 1/(1+exp(-l)) evaluated in float64, rounded to float32."""
+    l = np.asarray(logits32, np.float64)
+    with np.errstate(over="ignore"):
+        s = 1.0 / (1.0 + np.exp(-l))
+    return s.astype(np.float32)
+
+
+def route(logits32, k, mode, offset=None, bias=None, n_group=0, topk_group=0,
+          scaling=1.0):
+    """Route every token from its float32 router logits.
+
+    Returns (ids int32 [T, k], w float64 [T, k]); slot j of token t is flat row t*k+j.
+
+    * SOFTMAX_TOPK_RENORM ([MKR] s1 table: Mixtral, Qwen3; s3 ``route``): softmax over
+      all E logits, top-k, renormalise the k weights to sum to 1.  Selection on the
+      logits, weights = exp(l_j - l_0) / sum_i exp(l_i - l_0) over the k selected.
+    * TOPK_THEN_SOFTMAX ([MKR] s1 table: gpt-oss): top-k logits first, then softmax over
+      those k.  Same arithmetic as the previous mode.
+    * SIGMOID_BIAS_GROUPED ([MKR] s4): s = sigmoid(l); c = s + bias selects; each group of
+      E/n_group contiguous experts scores the sum of its two largest c; the best
+      ``topk_group`` groups stay eligible; top-k by c inside them; weights are the
+      unbiased s of the chosen experts renormalised and multiplied by ``scaling``.
+    ``offset`` (float32 [E]) is added to the logits before anything else (a float32 add).
+    """
+    l = f32(logits32)
+    T, E = l.shape
+    if offset is not None:
+        l = (l + f32(offset)[None, :]).astype(np.float32)
+    ids = np.zeros((T, k), np.int32)
+    w = np.zeros((T, k), np.float64)
+    if mode in (SOFTMAX_TOPK_RENORM, TOPK_THEN_SOFTMAX):
+        for t in range(T):
+            sel = order_first(l[t])[:k]
+            ids[t] = sel
+            ls = l[t, sel].astype(np.float64)
+            ex = np.exp(ls - ls[0])
+            w[t] = ex / ex.sum()
+        return ids, w
+    if mode != SIGMOID_BIAS_GROUPED:
+        raise ValueError(mode)
+    s = sigmoid_f32(l)
+    b = np.zeros(E, np.float32) if bias is None else f32(bias)
+    c = (s + b[None, :]).astype(np.float32)
+    for t in range(T):
+        if n_group and topk_group:
+            gsz = E // n_group
+            gscore = np.zeros(n_group, np.float32)
+            for g in range(n_group):
+                members = np.arange(g * gsz, (g + 1) * gsz)
+                top2 = order_first(c[t], members)[:2]
+                gscore[g] = np.float32(c[t, top2[0]]) + np.float32(c[t, top2[1]])
+            kept = order_first(gscore)[:topk_group]
+            cand = np.concatenate([np.arange(g * gsz, (g + 1) * gsz) for g in sorted(kept)])
+        else:
+            cand = None
+        sel = order_first(c[t], cand)[:k]
+        ids[t] = sel
+        sw = s[t, sel].astype(np.float64)
+        w[t] = scaling * sw / sw.sum()
+    return ids, w
+
+
+# --------------------------------------------------------------------------- align ([MKR] s5)
+
+def align_capacity(T, k, E, block_m) -> int:
+    """Worst-case padded length: the largest multiple of block_m not above
+    T*k + min(E, T*k)*(block_m-1) (each non-empty expert pads by at most block_m-1)."""
+    R = T * k
+    bound = R + min(E, R) * (block_m - 1)
+    return (bound // block_m) * block_m
+
+
+def align_argsort(topk_ids, E, block_m, cap=None):
+    """Histogram, pad to block_m, exclusive scan, scatter; rows grouped by a stable sort.
+
+    Returns dict(sorted_ids, expert_ids, total, counts) with buffers of length ``cap``
+    (default: the padded total) and cap // block_m.
+    """
+    flat = np.asarray(topk_ids, np.int64).reshape(-1)
+    R = flat.size
+    counts = np.bincount(flat, minlength=E)
+    padded = (counts + block_m - 1) // block_m * block_m
+    starts = np.cumsum(padded) - padded
+    total = int(padded.sum())
+    if cap is None:
+        cap = total
+    sorted_ids = np.full(cap, R, np.int32)
+    order = np.argsort(flat, kind="stable")
+    first_of = np.cumsum(counts) - counts                 # unpadded run start per expert
+    rank = np.arange(R) - first_of[flat[order]]
+    sorted_ids[starts[flat[order]] + rank] = order
+    expert_ids = np.full(cap // block_m, -1, np.int32)
+    tiles = np.repeat(np.arange(E, dtype=np.int32), padded // block_m)
+    expert_ids[: tiles.size] = tiles
+    return dict(sorted_ids=sorted_ids, expert_ids=expert_ids, total=total,
+                counts=counts.astype(np.int32))
+
+
+def align_counting(topk_ids, E, block_m, cap=None):
+    """The same table without a sort: one counting pass, an exclusive scan over the
+    padded counts, then a running cursor per expert while walking rows in order
+    ([MKR] s11, first exercise).  Plain Python loops."""
+    flat = [int(v) for v in np.asarray(topk_ids).reshape(-1)]
+    R = len(flat)
+    counts = [0] * E
+    for e in flat:
+        counts[e] += 1
+    start = [0] * E
+    run = 0
+    for e in range(E):
+        start[e] = run
+        run += -(-counts[e] // block_m) * block_m
+    total = run
+    if cap is None:
+        cap = total
+    sorted_ids = [R] * cap
+    cursor = [0] * E
+    for r, e in enumerate(flat):
+        sorted_ids[start[e] + cursor[e]] = r
+        cursor[e] += 1
+    expert_ids = [-1] * (cap // block_m)
+    for e in range(E):
+        for j in range(-(-counts[e] // block_m)):
+            expert_ids[start[e] // block_m + j] = e
+    return dict(sorted_ids=np.array(sorted_ids, np.int32),
+                expert_ids=np.array(expert_ids, np.int32), total=total,
+                counts=np.array(counts, np.int32))
+
+
+# --------------------------------------------------------------------------- expert math ([MKR] s1, s3, s6)
+
+def silu(z):
+    """silu(z) = z * sigmoid(z) = z / (1 + exp(-z))  (float64)."""
+    z = np.asarray(z, np.float64)
+    with np.errstate(over="ignore"):
+        return z / (1.0 + np.exp(-z))
+
+
+def _split_w13(w13):
+    w13 = np.asarray(w13, np.float64)
+    I = w13.shape[1] // 2
+    return w13[:, :I, :], w13[:, I:, :]        # gate rows (W1) first, then up rows (W3)
+
+
+def moe_loop(x, w13, w2, ids, w, round_a=False, return_rows=False):
+    """Per-expert loop ([MKR] s3 ``moe_loop``): for each expert gather the token rows
+    routed to it (flat rows r, token r // k), run the SwiGLU expert once on them, scale
+    by the router weight of row r, then sum each token's k slots in slot order."""
+    x = np.asarray(x, np.float64)
+    w2 = np.asarray(w2, np.float64)
+    W1, W3 = _split_w13(w13)
+    T, H = x.shape
+    E = W1.shape[0]
+    ids = np.asarray(ids)
+    k = ids.shape[1]
+    flat_ids = ids.reshape(-1)
+    flat_w = np.asarray(w, np.float64).reshape(-1)
+    y = np.zeros((T * k, H))
+    for e in range(E):
+        rows = np.nonzero(flat_ids == e)[0]
+        if rows.size == 0:
+            continue                                   # an empty expert does nothing
+        xe = x[rows // k]
+        a = silu(xe @ W1[e].T) * (xe @ W3[e].T)
+        if round_a:
+            a = bf16_round(a)
+        y[rows] = flat_w[rows, None] * (a @ w2[e].T)
+    out = np.zeros((T, H))
+    for j in range(k):                                 # combine: slot order
+        out += y[j::k]
+    return (out, y) if return_rows else out
+
+
+def moe_dense(x, w13, w2, ids, w, round_a=False):
+    """Dense version ([MKR] s3 ``moe_dense``): run every expert on every token, then
+    weight by a [T, E] gate matrix holding the k routed weights per token."""
+    x = np.asarray(x, np.float64)
+    w2 = np.asarray(w2, np.float64)
+    W1, W3 = _split_w13(w13)
+    T, H = x.shape
+    E = W1.shape[0]
+    gate = np.zeros((T, E))
+    ids = np.asarray(ids)
+    wv = np.asarray(w, np.float64)
+    for t in range(T):
+        for j in range(ids.shape[1]):
+            gate[t, ids[t, j]] += wv[t, j]
+    out = np.zeros((T, H))
+    for e in range(E):
+        a = silu(x @ W1[e].T) * (x @ W3[e].T)
+        if round_a:
+            a = bf16_round(a)
+        out += gate[:, e:e + 1] * (a @ w2[e].T)
+    return out
+
+
+def moe_bruteforce(x, w13, w2, ids, w, round_a=False):
+    """Scalar Python loops per (token, slot, output element); tiny inputs only."""
+    x = np.asarray(x, np.float64).tolist()
+    w13 = np.asarray(w13, np.float64)
+    w2 = np.asarray(w2, np.float64).tolist()
+    I = w13.shape[1] // 2
+    w13 = w13.tolist()
+    T = len(x)
+    H = len(x[0])
+    out = [[0.0] * H for _ in range(T)]
+    for t in range(T):
+        for j, e in enumerate(np.asarray(ids)[t].tolist()):
+            wt = float(np.asarray(w)[t, j])
+            a = []
+            for i in range(I):
+                g = sum(x[t][h] * w13[e][i][h] for h in range(H))
+                u = sum(x[t][h] * w13[e][I + i][h] for h in range(H))
+                ai = (g / (1.0 + math.exp(-g)) if g > -700 else 0.0) * u
+                if round_a:
+                    ai = float(bf16_round(ai))
+                a.append(ai)
+            for h in range(H):
+                out[t][h] += wt * sum(a[i] * w2[e][h][i] for i in range(I))
+    return np.array(out)
+
+
+def moe_layer(x, wg, w13, w2, k, mode, offset=None, bias=None, n_group=0, topk_group=0,
+              scaling=1.0, round_a=False):
+    """Whole layer: float64 router logits rounded to float32, routing, per-expert loop."""
+    logits32 = router_logits(x, wg).astype(np.float32)
+    ids, w = route(logits32, k, mode, offset, bias, n_group, topk_group, scaling)
+    out = moe_loop(x, w13, w2, ids, w, round_a=round_a)
+    return out, ids, w, logits32
+
+
+def expert_flops(T, k, H, I) -> int:
+    """Useful expert FLOPs: 2 * T * k * 3 * H * I (two GEMMs of 2I and I outputs)."""
+    return 2 * T * k * 3 * H * I
+
+
+# --------------------------------------------------------------------------- routing margins
+
+def selection_margin(logits32, k, mode, offset=None, bias=None, n_group=0, topk_group=0):
+    """Per token, the smallest gap between a selected score and the best unselected one
+    (and, for the grouped router, between the last kept and first dropped group score),
+    measured on the float32 selection scores.  A token whose margin is below the error
+    bound of its logits may be routed either way by a correct implementation."""
+    l = f32(logits32)
+    T, E = l.shape
+    if offset is not None:
+        l = (l + f32(offset)[None, :]).astype(np.float32)
+    if mode == SIGMOID_BIAS_GROUPED:
+        s = sigmoid_f32(l)
+        b = np.zeros(E, np.float32) if bias is None else f32(bias)
+        sc = (s + b[None, :]).astype(np.float32).astype(np.float64)
+    else:
+        sc = l.astype(np.float64)
+    m = np.full(T, np.inf)
+    for t in range(T):
+        o = order_first(sc[t])
+        if k < E:
+            m[t] = sc[t, o[k - 1]] - sc[t, o[k]]
+        if mode == SIGMOID_BIAS_GROUPED and n_group and topk_group and topk_group < n_group:
+            gsz = E // n_group
+            g = np.array([np.sort(sc[t, i * gsz:(i + 1) * gsz])[-2:].sum() for i in range(n_group)])
+            go = np.sort(g)[::-1]
+            m[t] = min(m[t], go[topk_group - 1] - go[topk_group])
+            # within the kept groups, the k-th vs (k+1)-th candidate
+            kept = order_first(g.astype(np.float64))[:topk_group]
+            cand = np.concatenate([np.arange(i * gsz, (i + 1) * gsz) for i in kept])
+            oc = order_first(sc[t], cand)
+            if len(oc) > k:
+                m[t] = min(m[t], sc[t, oc[k - 1]] - sc[t, oc[k]])
+    return m

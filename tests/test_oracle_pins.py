@@ -1,0 +1,391 @@
+"""Pins of the CPU oracle to facts outside itself: values the pages print for worked
+examples (tests/golden/*.json, each with its citation), closed forms, library routines,
+brute force and invariants.  CPU only."""
+import itertools
+import json
+import math
+import os
+from decimal import Decimal, getcontext
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import moe_oracle as O
+from synth import inputs as S
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def gold(name):
+    with open(os.path.join(GOLD, name)) as f:
+        return json.load(f)
+
+
+# ----------------------------------------------------------------------------- align
+
+def test_align_worked_example_both_implementations():
+    g = gold("align_worked_example.json")
+    ids = np.array(g["topk_ids"], np.int32)
+    assert ids.reshape(-1).tolist() == g["flat"]
+    for impl in (O.align_argsort, O.align_counting):
+        r = impl(ids, g["num_experts"], g["block_m"])
+        assert r["sorted_ids"].tolist() == g["sorted_ids"]
+        assert r["expert_ids"].tolist() == g["expert_ids"]
+        assert r["total"] == g["total"]
+        assert round(100 * (1 - g["useful"] / r["total"])) == g["waste_percent"]
+
+
+def test_align_padded_totals_match_printed_test_matrix():
+    g = gold("fused_test_matrix.json")
+    bm = g["block_m"]
+    for name, c in g["cases"].items():
+        ids = S.ids_with_counts(c["loads"], c["k"], seed=3).numpy()
+        assert ids.shape == (c["T"], c["k"])
+        for impl in (O.align_argsort, O.align_counting):
+            r = impl(ids, c["E"], bm)
+            assert r["total"] == c["padded"], name
+            assert r["counts"].tolist() == c["loads"]
+
+
+def _check_align_invariants(ids, E, bm, r, cap):
+    flat = ids.reshape(-1)
+    R = flat.size
+    counts = r["counts"]
+    assert counts.sum() == R
+    total = r["total"]
+    assert total % bm == 0 and total <= cap
+    si, ei = r["sorted_ids"], r["expert_ids"]
+    assert si.size == cap and ei.size == cap // bm
+    real = si[:total][si[:total] < R]
+    assert sorted(real.tolist()) == list(range(R))             # every row exactly once
+    assert np.all(si[total:] == R) and np.all(ei[total // bm:] == -1)
+    tiles = ei[: total // bm]
+    assert np.all(np.diff(tiles) >= 0)                         # experts ascending
+    for e in range(E):
+        nt = int((tiles == e).sum())
+        assert nt == -(-int(counts[e]) // bm)                  # ceil(n_e / BM) tiles, none if empty
+    for p in range(total // bm):                               # each tile's rows belong to its expert,
+        blk = si[p * bm:(p + 1) * bm]                          # in ascending order, sentinel after
+        v = blk[blk < R]
+        assert np.all(flat[v] == tiles[p])
+        assert np.all(np.diff(v) > 0)
+        nv = v.size
+        assert np.all(blk[:nv] < R) and np.all(blk[nv:] == R)
+
+
+@pytest.mark.parametrize("bm", [1, 4, 16, 64, 128, 256])
+@pytest.mark.parametrize("T,k,E,skew", [(1, 8, 256, 0.0), (37, 1, 8, 0.0), (64, 2, 8, 0.0),
+                                          (300, 8, 128, 1.2), (50, 4, 16, 0.0)])
+def test_align_invariants_and_implementations_agree(bm, T, k, E, skew):
+    ids = S.random_topk_ids(T, k, E, seed=T + E, skew=skew).numpy()
+    cap = O.align_capacity(T, k, E, bm)
+    a = O.align_argsort(ids, E, bm, cap)
+    b = O.align_counting(ids, E, bm, cap)
+    for key in ("sorted_ids", "expert_ids", "counts"):
+        assert np.array_equal(a[key], b[key]), key
+    assert a["total"] == b["total"]
+    _check_align_invariants(ids, E, bm, a, cap)
+
+
+def test_align_edge_counts():
+    """Experts at 0, 1, BM-1, BM, BM+1 rows, and one expert receiving every token."""
+    bm = 16
+    loads = [0, 1, bm - 1, bm, bm + 1, 0, 2 * bm, 3]
+    k = 2
+    pad = (-sum(loads)) % k
+    loads[-1] += pad
+    ids = S.ids_with_counts(loads, k, seed=5).numpy()
+    cap = O.align_capacity(ids.shape[0], k, len(loads), bm)
+    r = O.align_argsort(ids, len(loads), bm, cap)
+    _check_align_invariants(ids, len(loads), bm, r, cap)
+    assert r["total"] == sum(-(-c // bm) * bm for c in loads)
+    hot = S.random_topk_ids(100, 4, 16, seed=1, hot=3).numpy()
+    r = O.align_counting(hot, 16, bm, O.align_capacity(100, 4, 16, bm))
+    assert r["counts"][3] == 100
+    _check_align_invariants(hot, 16, bm, r, O.align_capacity(100, 4, 16, bm))
+
+
+def test_align_capacity_is_tight_bound():
+    # every non-empty expert pads by at most BM-1 rows; the bound is reached when every
+    # expert has exactly one row beyond a multiple of BM
+    T, k, E, bm = 8, 2, 4, 4
+    loads = [5, 5, 1, 5]
+    ids = S.ids_with_counts(loads, k).numpy()
+    r = O.align_argsort(ids, E, bm)
+    assert r["total"] == 8 + 8 + 4 + 8 == 28
+    assert O.align_capacity(T, k, E, bm) >= r["total"]
+    assert O.align_capacity(1, 8, 256, 64) == 8 * 64
+
+
+# ----------------------------------------------------------------------------- routing
+
+def test_tiny_layer_counts_and_flops():
+    g = gold("tiny_layer.json")
+    lay = S.make_layer(S.WORKLOADS["tiny"])
+    x, wg = lay.x.numpy(), lay.wg.numpy()
+    logits32 = O.router_logits(x, wg).astype(np.float32)
+    ids, w = O.route(logits32, g["k"], O.SOFTMAX_TOPK_RENORM)
+    counts = np.bincount(ids.reshape(-1), minlength=g["E"])
+    assert counts.tolist() == g["tokens_per_expert"]
+    assert counts.sum() == g["sum"]
+    fl = O.expert_flops(g["T"], g["k"], g["H"], g["I"])
+    assert fl == 4718592
+    assert round(fl / 1e6, 1) == g["routed_mflop"]
+    assert round(fl * g["E"] / g["k"] / 1e6, 1) == g["dense_mflop"]
+
+
+def test_test_matrix_loads():
+    g = gold("fused_test_matrix.json")
+    for name, c in g["cases"].items():
+        x, wg, w1, w3, w2, k = S.page_test_case(name)
+        logits32 = O.router_logits(x.numpy(), wg.numpy()).astype(np.float32)
+        ids, _ = O.route(logits32, k, O.SOFTMAX_TOPK_RENORM)
+        assert np.bincount(ids.reshape(-1), minlength=c["E"]).tolist() == c["loads"], name
+        assert O.align_argsort(ids, c["E"], g["block_m"])["total"] == c["padded"]
+
+
+def test_grouped_router_worked_example():
+    g = gold("grouped_router_example.json")
+    logits, bias = S.page_grouped_router_logits()
+    l32 = logits.numpy().astype(np.float32)
+    args = dict(n_group=g["n_group"], topk_group=g["topk_group"], scaling=g["scaling"])
+    ids0, _ = O.route(l32, g["k"], O.SIGMOID_BIAS_GROUPED, bias=np.zeros(16, np.float32), **args)
+    assert ids0.tolist() == g["ids_no_bias"]
+    ids1, w1 = O.route(l32, g["k"], O.SIGMOID_BIAS_GROUPED, bias=bias.numpy(), **args)
+    assert ids1.tolist() == g["ids_with_bias"]
+    gsz = g["E"] // g["n_group"]
+    assert [sorted(set((r // gsz).tolist())) for r in ids1] == g["groups_per_token"]
+    assert np.allclose(w1, np.array(g["weights_right_3dp"]), atol=5e-4 + 1e-9)
+    assert np.allclose(w1.sum(1), g["scaling"])
+    # the bias leak: weights from the biased scores instead of the unbiased ones
+    s = O.sigmoid_f32(l32).astype(np.float64)
+    c = s + bias.numpy().astype(np.float64)[None, :]
+    cb = np.take_along_axis(c, ids1.astype(np.int64), 1)
+    w_bug = g["scaling"] * cb / cb.sum(1, keepdims=True)
+    assert np.allclose(w_bug, np.array(g["weights_bias_leak_3dp"]), atol=5e-4 + 1e-9)
+    assert round(float(np.abs(w1 - w_bug).max()), 3) == g["max_weight_error_bias_leak_3dp"]
+
+
+def test_softmax_renorm_matches_library_softmax_topk():
+    """Reduces to torch.softmax -> torch.topk -> renormalise (float64) when no two
+    logits tie."""
+    rng = np.random.default_rng(0)
+    l32 = rng.standard_normal((200, 64)).astype(np.float32)
+    for k in (1, 2, 4, 8):
+        ids, w = O.route(l32, k, O.SOFTMAX_TOPK_RENORM)
+        p = torch.softmax(torch.from_numpy(l32.astype(np.float64)), dim=-1)
+        tw, tid = torch.topk(p, k, dim=-1)
+        tw = tw / tw.sum(-1, keepdim=True)
+        assert np.array_equal(ids, tid.numpy())
+        assert np.allclose(w, tw.numpy(), rtol=1e-13, atol=0)
+        ids2, w2 = O.route(l32, k, O.TOPK_THEN_SOFTMAX)   # identical arithmetic by the identity
+        assert np.array_equal(ids, ids2) and np.array_equal(w, w2)
+        if k == 1:
+            assert np.all(w == 1.0)
+
+
+def test_route_ties_lower_index_wins():
+    l32 = np.array([[1.0, 3.0, 3.0, 2.0, 3.0]], np.float32)
+    ids, _ = O.route(l32, 2, O.SOFTMAX_TOPK_RENORM)
+    assert ids.tolist() == [[1, 2]]
+    ids, _ = O.route(l32, 4, O.SOFTMAX_TOPK_RENORM)
+    assert ids.tolist() == [[1, 2, 4, 3]]
+    # groups: two groups with equal scores -> the lower group is kept
+    l = np.zeros((1, 8), np.float32)
+    ids, w = O.route(l, 2, O.SIGMOID_BIAS_GROUPED, n_group=2, topk_group=1, scaling=2.5)
+    assert ids.tolist() == [[0, 1]] and np.allclose(w, 1.25)
+
+
+def test_route_offset_applies_to_selection_and_weights():
+    rng = np.random.default_rng(1)
+    l32 = rng.standard_normal((64, 16)).astype(np.float32)
+    off = np.zeros(16, np.float32)
+    off[:2] = 3.0
+    ids_o, w_o = O.route(l32, 4, O.TOPK_THEN_SOFTMAX, offset=off)
+    ids_s, w_s = O.route((l32 + off).astype(np.float32), 4, O.TOPK_THEN_SOFTMAX)
+    assert np.array_equal(ids_o, ids_s) and np.array_equal(w_o, w_s)
+    assert (np.isin(ids_o, [0, 1]).sum(1) == 2).mean() > 0.8
+
+
+def _brute_grouped(c_row, s_row, k, n_group, topk_group, scaling):
+    """Enumerate every choice of groups, then every k-subset inside them."""
+    E = c_row.size
+    gsz = E // n_group
+    gs = [sorted(c_row[g * gsz:(g + 1) * gsz].tolist())[-2:] for g in range(n_group)]
+    gscore = [np.float32(a) + np.float32(b) for a, b in gs]
+    best = max(itertools.combinations(range(n_group), topk_group),
+               key=lambda G: (sorted([gscore[g] for g in G], reverse=True), [-g for g in G]))
+    cand = [e for g in sorted(best) for e in range(g * gsz, (g + 1) * gsz)]
+    sel = max(itertools.combinations(cand, k), key=lambda S_: (sorted([c_row[e] for e in S_], reverse=True),
+                                                              [-e for e in sorted(S_)]))
+    sel = sorted(sel, key=lambda e: (-c_row[e], e))
+    sw = np.array([s_row[e] for e in sel], np.float64)
+    return sel, scaling * sw / sw.sum()
+
+
+def test_grouped_router_brute_force():
+    rng = np.random.default_rng(2)
+    E, k, G, TG = 12, 3, 4, 2
+    l32 = rng.standard_normal((40, E)).astype(np.float32)
+    bias = (rng.standard_normal(E) * 0.3).astype(np.float32)
+    ids, w = O.route(l32, k, O.SIGMOID_BIAS_GROUPED, bias=bias, n_group=G, topk_group=TG, scaling=2.5)
+    s = O.sigmoid_f32(l32)
+    c = (s + bias[None]).astype(np.float32)
+    for t in range(40):
+        sel, wb = _brute_grouped(c[t], s[t], k, G, TG, 2.5)
+        assert ids[t].tolist() == sel
+        assert np.allclose(w[t], wb, rtol=1e-14)
+
+
+def test_sigmoid_f32_is_correctly_rounded():
+    getcontext().prec = 60
+    rng = np.random.default_rng(3)
+    vals = np.concatenate([rng.standard_normal(400) * 4, rng.uniform(-30, 30, 400),
+                           np.array([0.0, 1.0, -1.0, 20.0, -20.0])]).astype(np.float32)
+    got = O.sigmoid_f32(vals)
+    for v, s in zip(vals.tolist(), got.tolist()):
+        ex = Decimal(1) / (Decimal(1) + (-Decimal(v)).exp())
+        lo = np.float32(s)
+        # the float32 neighbours of s must both be farther from the exact value
+        up = np.nextafter(lo, np.float32(2))
+        dn = np.nextafter(lo, np.float32(-1))
+        d = abs(Decimal(float(lo)) - ex)
+        assert d <= abs(Decimal(float(up)) - ex) and d <= abs(Decimal(float(dn)) - ex), v
+
+
+# ----------------------------------------------------------------------------- rounding
+
+def test_bf16_round_matches_torch_conversion():
+    rng = np.random.default_rng(4)
+    v = np.concatenate([rng.standard_normal(100000) * 10.0 ** rng.integers(-8, 8, 100000),
+                        np.array([1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, -(1.0 + 2 ** -8), 0.0])])
+    v32 = v.astype(np.float32)                                 # exactly representable inputs
+    ref = torch.from_numpy(v32).to(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(O.bf16_round(v32.astype(np.float64)), ref)
+    # ties go to even: 1 + 2^-8 lies halfway between 1 and 1 + 2^-7
+    assert O.bf16_round(1.0 + 2 ** -8) == 1.0
+    assert O.bf16_round(1.0 + 3 * 2 ** -8) == 1.0 + 2 ** -6
+
+
+# ----------------------------------------------------------------------------- expert math
+
+def _rand_layer(T, H, I, E, k, seed, mode=O.SOFTMAX_TOPK_RENORM):
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((T, H))
+    wg = rng.standard_normal((E, H)) / math.sqrt(H)
+    w13 = rng.standard_normal((E, 2 * I, H)) / math.sqrt(H)
+    w2 = rng.standard_normal((E, H, I)) / math.sqrt(I)
+    l32 = O.router_logits(x, wg).astype(np.float32)
+    ids, w = O.route(l32, k, mode, n_group=2 if mode == 2 else 0, topk_group=1 if mode == 2 else 0,
+                     scaling=2.5 if mode == 2 else 1.0)
+    return x, wg, w13, w2, ids, w
+
+
+def test_silu_known_value():
+    # silu(1) = 1 / (1 + e^-1)
+    assert O.silu(1.0) == pytest.approx(0.7310585786300049, rel=1e-15)
+    # the layer reduces to it for H = I = E = k = 1 with unit weights
+    out = O.moe_loop(np.ones((1, 1)), np.ones((1, 2, 1)), np.ones((1, 1, 1)),
+                     np.zeros((1, 1), np.int32), np.ones((1, 1)))
+    assert out[0, 0] == pytest.approx(0.7310585786300049, rel=1e-15)
+
+
+def test_gate_and_up_roles():
+    """W13 = [W1; W3]: the gate half goes through silu.  A very negative gate
+    pre-activation switches the expert off whatever the up half is."""
+    rng = np.random.default_rng(5)
+    H, I = 8, 6
+    x = np.abs(rng.standard_normal((3, H))) + 0.1
+    w13 = rng.standard_normal((1, 2 * I, H))
+    w13[0, :I] = -40.0                                   # gate rows
+    w2 = rng.standard_normal((1, H, I))
+    ids = np.zeros((3, 1), np.int32)
+    out = O.moe_loop(x, w13, w2, ids, np.ones((3, 1)))
+    assert np.abs(out).max() < 1e-30
+    w13b = w13.copy()
+    w13b[0, :I], w13b[0, I:] = w13[0, I:], w13[0, :I]     # swapped halves are not off
+    assert np.abs(O.moe_loop(x, w13b, w2, ids, np.ones((3, 1)))).max() > 1e-3
+
+
+@pytest.mark.parametrize("mode", [0, 1, 2])
+def test_loop_dense_bruteforce_agree(mode):
+    x, wg, w13, w2, ids, w = _rand_layer(6, 8, 6, 4, 2, seed=10 + mode, mode=mode)
+    a = O.moe_loop(x, w13, w2, ids, w)
+    b = O.moe_dense(x, w13, w2, ids, w)
+    c = O.moe_bruteforce(x, w13, w2, ids, w)
+    assert np.abs(a - b).max() <= 1e-13 * np.abs(a).max()
+    assert np.abs(a - c).max() <= 1e-13 * np.abs(a).max()
+    ar = O.moe_loop(x, w13, w2, ids, w, round_a=True)
+    cr = O.moe_bruteforce(x, w13, w2, ids, w, round_a=True)
+    assert np.abs(ar - cr).max() <= 1e-12 * np.abs(ar).max()
+    assert np.abs(ar - a).max() > 0                   # the bf16 rounding point is real
+
+
+def test_loop_vs_dense_tiny_layer():
+    g = gold("tiny_layer.json")
+    lay = S.make_layer(S.WORKLOADS["tiny"])
+    x, wg, w13, w2 = (t.numpy() for t in (lay.x, lay.wg, lay.w13, lay.w2))
+    out, ids, w, _ = O.moe_layer(x, wg, w13, w2, 2, O.SOFTMAX_TOPK_RENORM)
+    dense = O.moe_dense(x, w13, w2, ids, w)
+    assert np.abs(out - dense).max() <= 1e-12 + g["max_abs_loop_minus_dense"]
+
+
+def test_k_equals_E_is_dense_softmax_mixture():
+    """k = E with renormalisation: every expert weighted by the full softmax."""
+    x, wg, w13, w2, _, _ = _rand_layer(5, 8, 6, 4, 4, seed=20)
+    l32 = O.router_logits(x, wg).astype(np.float32)
+    ids, w = O.route(l32, 4, O.SOFTMAX_TOPK_RENORM)
+    p = torch.softmax(torch.from_numpy(l32.astype(np.float64)), -1).numpy()
+    assert np.allclose(np.take_along_axis(p, ids.astype(np.int64), 1), w, rtol=1e-13)
+    out = O.moe_loop(x, w13, w2, ids, w)
+    ref = O.moe_bruteforce(x, w13, w2, np.tile(np.arange(4, dtype=np.int32), (5, 1)), p)
+    assert np.allclose(out, ref, rtol=1e-12, atol=1e-14)
+
+
+def test_metamorphic_properties():
+    x, wg, w13, w2, ids, w = _rand_layer(9, 8, 6, 5, 2, seed=30)
+    out = O.moe_loop(x, w13, w2, ids, w)
+    # scaling every W2 by 2 scales the output by exactly 2
+    assert np.array_equal(O.moe_loop(x, w13, 2 * w2, ids, w), 2 * out)
+    # permuting tokens permutes the output rows
+    perm = np.random.default_rng(0).permutation(9)
+    assert np.allclose(O.moe_loop(x[perm], w13, w2, ids[perm], w[perm]), out[perm], rtol=1e-14)
+    # relabelling experts (router rows, weights, ids together) leaves the output unchanged
+    rel = np.random.default_rng(1).permutation(5)
+    inv = np.argsort(rel)
+    out2 = O.moe_loop(x, w13[rel], w2[rel], inv[ids].astype(np.int32), w)
+    assert np.allclose(out2, out, rtol=1e-14)
+    # slot j's weight multiplies expert ids[t, j]: doubling expert e's W2 adds w_e * F_e
+    e = int(ids[0, 0])
+    w2b = w2.copy()
+    w2b[e] *= 2
+    only_e = np.where(ids == e, w, 0.0)
+    f_e = O.moe_loop(x, w13, w2, ids, only_e)
+    assert np.allclose(O.moe_loop(x, w13, w2b, ids, w), out + f_e, rtol=1e-13, atol=1e-15)
+    # an expert that receives no rows never influences the output
+    unused = [q for q in range(5) if q not in ids]
+    if unused:
+        w13c = w13.copy()
+        w13c[unused[0]] = np.nan
+        assert np.array_equal(O.moe_loop(x, w13c, w2, ids, w), out)
+
+
+def test_identical_experts_sum_of_weights():
+    """Two identical experts: the output is (sum of the token's weights) x one expert;
+    the grouped router's weights sum to its scale."""
+    rng = np.random.default_rng(7)
+    T, H, I = 4, 8, 6
+    x = rng.standard_normal((T, H))
+    one13 = rng.standard_normal((1, 2 * I, H))
+    one2 = rng.standard_normal((1, H, I))
+    ref = O.moe_loop(x, one13, one2, np.zeros((T, 1), np.int32), np.ones((T, 1)))
+    l32 = rng.standard_normal((T, 4)).astype(np.float32)
+    ids, w = O.route(l32, 2, O.SIGMOID_BIAS_GROUPED, n_group=2, topk_group=1, scaling=2.5)
+    out = O.moe_loop(x, np.repeat(one13, 4, 0), np.repeat(one2, 4, 0), ids, w)
+    assert np.allclose(out, 2.5 * ref, rtol=1e-13)
+
+
+def test_selection_margin():
+    l32 = np.array([[1.0, 0.5, 0.25, 0.0]], np.float32)
+    assert O.selection_margin(l32, 2, 0)[0] == pytest.approx(0.25)
