@@ -1,0 +1,182 @@
+"""Benchmark of the fused top-k MoE SwiGLU layer on one MI355X.
+
+One step = route -> align -> GEMM1+SwiGLU -> GEMM2 x weight -> combine over one batch of
+seeded synthetic input already resident in HBM, each stage through the C ABI on the
+current HIP stream.  Prints ONE JSON line.
+
+  python bench.py [--steps K] [--warmup W] [--workload mixtral|deepseek_decode|...] [--T n]
+
+Default workload: the Mixtral-8x7B-shaped prefill layer (T=4096, H=4096, I=14336, E=8,
+k=2, bf16), metric = useful TFLOPS = 2*T*k*3*H*I / step time.  Decode workloads report
+weight GB/s = active experts * 3*H*I*2 B / step time.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE layer TFLOPS (2·T·k·3HI/t) prefill; weight GB/s at decode; % of roofline"
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="mixtral")
+    ap.add_argument("--T", type=int, default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-tokens", type=int, default=None)
+    return ap.parse_args()
+
+
+def cpu_baseline(wl, lay, sample_T):
+    """Time the CPU oracle (routing + per-expert loop) on the first sample_T tokens."""
+    import numpy as np
+    from oracle import moe_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        cores = os.cpu_count() or 1
+    x = lay.x[:sample_T].float().cpu().numpy()
+    wg = lay.wg.float().cpu().numpy()
+    w13 = lay.w13.float().cpu().numpy()
+    w2 = lay.w2.float().cpu().numpy()
+    kw = dict(offset=None if lay.offset is None else lay.offset.cpu().numpy(),
+              bias=None if lay.bias is None else lay.bias.cpu().numpy(),
+              n_group=wl.n_group, topk_group=wl.topk_group, scaling=wl.scaling,
+              round_a=wl.dtype == "bf16")
+    t0 = time.perf_counter()
+    out, ids, _, _ = O.moe_layer(x, wg, w13, w2, wl.k, wl.mode, **kw)
+    dt = time.perf_counter() - t0
+    flops = 2 * sample_T * wl.k * 3 * wl.H * wl.I
+    if wl.T <= 256:  # decode: weight bytes of the experts the sample activates
+        active = len(set(ids.reshape(-1).tolist()))
+        value, unit = active * 3 * wl.H * wl.I * 2 / dt / 1e9, "GB/s"
+    else:
+        value, unit = flops / dt / 1e12, "TFLOPS"
+    return {"value": value, "unit": unit, "cores": int(cores), "kind": "oracle",
+            "sample": f"{sample_T} of {wl.T} tokens of the same layer (numpy float64 oracle, "
+                      f"route + per-expert loop), {dt:.2f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: this layer's benchmark runs on a single MI355X "
+              "(no sharding); run it with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import mixture_experts_layer_27_amd as m
+    from synth import inputs as S
+
+    wl = S.WORKLOADS[args.workload]
+    if args.T is not None:
+        wl = wl.with_T(args.T)
+    dev = "cuda"
+    lay = S.make_layer(wl, device=dev, seed=0)
+    T, H, I, E, k = wl.T, wl.H, wl.I, wl.E, wl.k
+    dt = m.BF16 if wl.dtype == "bf16" else m.F32
+    cfg = m.route_cfg(wl.mode, lay.offset, lay.bias, wl.n_group, wl.topk_group, wl.scaling)
+    bm = m.moe_preferred_block_m(T, H, I, E, k, dt)
+    variant = m.moe_auto_variant(T, H, I, E, k, dt)
+    cap = m.moe_align_capacity(T, k, E, bm)
+    R = T * k
+    # rotate activation batches for decode so successive steps route differently
+    nx = 8 if T <= 256 else 1
+    xs = [lay.x] + [S.make_x(wl, device=dev, seed=1000 + i) for i in range(nx - 1)]
+    i32 = dict(dtype=torch.int32, device=dev)
+    ids = torch.empty(T, k, **i32)
+    w = torch.empty(T, k, dtype=torch.float32, device=dev)
+    logits = torch.empty(T, E, dtype=torch.float32, device=dev)
+    sorted_ids = torch.empty(cap, **i32)
+    expert_ids = torch.empty(cap // bm, **i32)
+    ntpp = torch.empty(1, **i32)
+    counts = torch.empty(E, **i32)
+    aws = torch.empty(max(16, m.moe_align_workspace_size(T, k, E, bm)), dtype=torch.uint8, device=dev)
+    a = torch.empty(R, I, dtype=lay.x.dtype, device=dev)
+    y = torch.empty(R, H, dtype=torch.float32, device=dev)
+    out = torch.empty(T, H, dtype=lay.x.dtype, device=dev)
+    lib = m.lib
+    import ctypes
+    P = lambda t: ctypes.c_void_p(t.data_ptr())
+    stream = torch.cuda.current_stream()
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+
+    def step(i, timed):
+        x = xs[i % nx]
+        m.check(lib.moe_route(P(x), P(lay.wg), T, H, E, k, dt, ctypes.byref(cfg), P(ids), P(w),
+                              P(logits), None, 0, sp), "route")
+        m.check(lib.moe_align(P(ids), T, k, E, bm, P(sorted_ids), P(expert_ids), P(ntpp), P(counts),
+                              P(aws), aws.numel(), sp), "align")
+        if timed:
+            ev[i][0].record(stream)
+        m.check(lib.moe_gemm1_swiglu(P(x), P(lay.w13), P(sorted_ids), P(expert_ids), P(ntpp), T, H, I,
+                                     E, k, bm, dt, variant, P(a), sp), "gemm1")
+        if timed:
+            ev[i][1].record(stream)
+        m.check(lib.moe_gemm2_weighted(P(a), P(lay.w2), P(w), P(sorted_ids), P(expert_ids), P(ntpp),
+                                       T, H, I, E, k, bm, dt, variant, P(y), sp), "gemm2")
+        m.check(lib.moe_combine(P(y), T, H, k, dt, P(out), sp), "combine")
+
+    for i in range(args.warmup):
+        step(i, False)
+    torch.cuda.synchronize()
+    active = []
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    t_start.record(stream)
+    for i in range(args.steps):
+        step(i, True)
+        if T <= 256:
+            active.append((counts > 0).sum())
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    ms = t_start.elapsed_time(t_end) / args.steps
+    g1_ms = sum(s.elapsed_time(e) for s, e in ev) / args.steps
+    flops = wl.flops
+    g1_flops = 2 * R * 2 * I * H
+    decode = T <= 256
+    if decode:
+        n_act = float(torch.stack(active).float().mean().item())
+        wbytes = n_act * 3 * H * I * 2
+        value, unit = wbytes / (ms * 1e-3) / 1e9, "GB/s"
+        g1_bytes = n_act * 2 * I * H * 2
+        roof = {"bound": "hbm", "achieved": g1_bytes / (g1_ms * 1e-3) / 1e9, "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "traffic": None}
+    else:
+        value, unit = flops / (ms * 1e-3) / 1e12, "TFLOPS"
+        roof = {"bound": "mfma", "achieved": g1_flops / (g1_ms * 1e-3) / 1e12,
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "traffic": None}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["kernel"] = "moe_gemm_bf16_kernel<GEMM1+SwiGLU>"
+    roof["kernel_ms"] = g1_ms
+    rec = {"metric": METRIC, "value": value, "unit": unit, "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": wl.dtype, "data": "synthetic",
+           "config": {"workload": f"{wl.name}", "T": T, "H": H, "I": I, "E": E, "k": k,
+                      "route_mode": wl.mode, "block_m": bm, "variant": variant,
+                      "parallelism": "single-gpu"},
+           "roofline": roof}
+    if decode:
+        rec["config"]["active_experts"] = n_act
+    if not args.no_cpu_baseline:
+        st = args.cpu_sample_tokens or (min(T, 512) if not decode else T)
+        rec["cpu_baseline"] = cpu_baseline(wl, lay, st)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

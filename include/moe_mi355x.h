@@ -1,0 +1,193 @@
+/*
+ * moe_mi355x.h -- C ABI of a fused top-k Mixture-of-Experts SwiGLU FFN layer for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The layer (definition: "Mixture-of-Experts Kernels: Routing, Permutation, and
+ * Grouped GEMM", section 1; data flow: section 2):
+ *
+ *   logits = x . Wg^T                      router GEMM, fp32            (moe_route)
+ *   (topk_ids, topk_w) = rule(logits)      softmax/sigmoid + top-k      (moe_route)
+ *   sorted_ids, expert_ids, padded total   histogram/pad/scan/scatter   (moe_align)
+ *   a[r] = silu(x[r/k] W1[e]^T) * (x[r/k] W3[e]^T)   gathered GEMM1     (moe_gemm1_swiglu)
+ *   y[r] = topk_w[r] * a[r] W2[e]^T                  GEMM2 x weight     (moe_gemm2_weighted)
+ *   out[t] = sum_j y[t*k + j]                        combine            (moe_combine)
+ *
+ * where r = t*k + j is the flat routed row of token t, slot j, and e = topk_ids[t][j].
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - All tensor pointers are DEVICE pointers owned by the caller; the library
+ *   allocates nothing, frees nothing and keeps no device state between calls.
+ * - `stream` is a hipStream_t (NULL = the legacy default stream).  Every call only
+ *   enqueues kernels on it: no host<->device copy, no synchronisation, no
+ *   decision that depends on device data, so every call can be captured in a
+ *   HIP graph.  The library is thread-safe and reentrant.
+ * - Arguments are validated on the host before anything is enqueued.  On any
+ *   error nothing is enqueued, outputs are untouched, and moe_last_error()
+ *   returns a thread-local message.  A failed kernel launch returns MOE_ERR_HIP.
+ * - Not checked on the device (preconditions): topk_ids values lie in [0, E)
+ *   and each token's k ids are distinct (both hold for ids from moe_route);
+ *   sorted_ids / expert_ids / num_tokens_post_padded come from moe_align with the
+ *   same T, k, E, block_m.
+ * - Layouts (row-major, "nn.Linear" [out, in] weights, section 11 of the
+ *   routing/grouped GEMM page):  x [T,H];  Wg [E,H];  W13 [E,2I,H] whose rows
+ *   0..I-1 are the gate projection W1[e] and rows I..2I-1 the up projection W3[e];
+ *   W2 [E,H,I];  topk_ids [T,k] int32;  topk_w [T,k] fp32;  out [T,H].
+ * - Element types: MOE_BF16 means x, Wg, W13, W2 and out are bf16 and the SwiGLU
+ *   activation a is stored as bf16 (it is GEMM2's input); MOE_F32 means all of
+ *   them are fp32.  Accumulation is fp32 in both; logits, topk_w and y are fp32.
+ * - Limits: 1 <= k <= 16, k <= E <= 512, T >= 0, T*k < 2^31; for MOE_BF16, H and I
+ *   are multiples of 64; x, W13, W2, out, a and y 16-byte aligned.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = -1,   /* null/misaligned pointer, size out of range, bad mode */
+  MOE_ERR_UNSUPPORTED = -2,   /* valid request outside this build's limits            */
+  MOE_ERR_WORKSPACE = -3,     /* workspace pointer NULL or smaller than required      */
+  MOE_ERR_HIP = -4            /* a HIP call failed (launch error)                     */
+} moe_status;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+
+/* Routing rules ("Mixture-of-Experts Kernels: Routing, Permutation, and Grouped GEMM",
+ * section 1 model table, section 3 `route`, section 4 grouped router). */
+typedef enum {
+  /* softmax over all E logits, top-k, weights renormalised to sum to 1 (Mixtral, Qwen3) */
+  MOE_ROUTE_SOFTMAX_TOPK_RENORM = 0,
+  /* top-k logits first, then softmax over those k (gpt-oss)                             */
+  MOE_ROUTE_TOPK_THEN_SOFTMAX = 1,
+  /* s = sigmoid(logit); c = s + select_bias chooses; groups of E/n_group contiguous
+   * experts are scored by the sum of their two largest c, the best topk_group groups
+   * stay eligible, top-k by c inside them; weights = routed_scaling * s / sum(s) over
+   * the chosen experts, from the UNBIASED s (DeepSeek-V3)                              */
+  MOE_ROUTE_SIGMOID_BIAS_GROUPED = 2
+} moe_route_mode;
+
+typedef struct {
+  int32_t mode;               /* moe_route_mode                                          */
+  const float* logit_offset;  /* device [E] or NULL: added (fp32) to every logit before   *
+                               * selection and weighting                                  */
+  const float* select_bias;   /* device [E] or NULL: mode 2 only, selection-only bias     */
+  int32_t n_group;            /* mode 2: number of groups (divides E); 0 = no grouping    */
+  int32_t topk_group;         /* mode 2: groups kept; 0 = no grouping                     */
+  float routed_scaling;       /* mode 2: weight scale (2.5 for DeepSeek-V3); else ignored */
+} moe_route_cfg;
+
+/* ---------------------------------------------------------------------------------- */
+/* Router.  Computes logits = x . Wg^T in fp32 and applies cfg's rule.
+ *   topk_ids [T,k] int32: chosen experts, slot j in selection order (descending
+ *            selection score, ties to the lower expert index; groups likewise).
+ *   topk_w   [T,k] fp32: router weights of those slots.
+ *   logits_out [T,E] fp32 or NULL: the raw x . Wg^T (before logit_offset).
+ *   ws: scratch of moe_route_workspace_size(T,E) bytes (may be 0 when logits_out
+ *       is given).
+ * Selection decisions are taken on fp32 values: (logit + offset) for modes 0/1;
+ * for mode 2 on c = s + bias with s = sigmoid(logit+offset) rounded to nearest fp32
+ * and group scores c_a + c_b in fp32. */
+moe_status moe_route(const void* x, const void* wg, int T, int H, int E, int k, moe_dtype dt,
+                     const moe_route_cfg* cfg, int32_t* topk_ids, float* topk_w,
+                     float* logits_out, void* ws, size_t ws_bytes, void* stream);
+size_t moe_route_workspace_size(int T, int E);
+
+/* The selection/weighting half of moe_route on caller-supplied fp32 logits [T,E]
+ * (the same device code as moe_route's epilogue). */
+moe_status moe_route_from_logits(const float* logits, int T, int E, int k,
+                                 const moe_route_cfg* cfg, int32_t* topk_ids, float* topk_w,
+                                 void* stream);
+
+/* ---------------------------------------------------------------------------------- */
+/* Align ("Mixture-of-Experts Kernels: ...", section 5; "fused-moe-kernel", Core
+ * Technique).  From topk_ids [T,k] builds the block-aligned indirection table:
+ *   expert_counts[e]  = n_e, rows routed to e (optional output, may be NULL);
+ *   padded_e          = ceil(n_e / block_m) * block_m;  start_e = exclusive scan;
+ *   *num_tokens_post_padded = total = sum_e padded_e;
+ *   sorted_ids[start_e + i] = the i-th flat row r (ascending r) with topk_ids = e, and
+ *                           the sentinel T*k on the padding positions and on the tail
+ *                           [total, cap);
+ *   expert_ids[p]      = expert owning rows [p*block_m, (p+1)*block_m) for p < total/
+ *                           block_m (empty experts own no tile), -1 on [total/block_m,
+ *                           cap/block_m).
+ * Buffers are sized for the worst case cap = moe_align_capacity(T,k,E,block_m), so the
+ * call is graph-capturable; the result is bit-exact and deterministic.
+ * block_m: a power of two in [1, 256].  ws: moe_align_workspace_size(...) bytes. */
+int64_t moe_align_capacity(int T, int k, int E, int block_m);
+size_t moe_align_workspace_size(int T, int k, int E, int block_m);
+moe_status moe_align(const int32_t* topk_ids, int T, int k, int E, int block_m,
+                     int32_t* sorted_ids, int32_t* expert_ids,
+                     int32_t* num_tokens_post_padded, int32_t* expert_counts,
+                     void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------------- */
+/* Expert computation ("Mixture-of-Experts Kernels: ...", section 6).
+ * Tiles past the device-side padded total exit at once; sentinel rows are never
+ * stored; tiles of an expert with no rows do not exist, so its weights are never
+ * read. */
+
+/* Variant of the expert GEMMs: 0 = automatic (from T, k, E, H, I on the host),
+ * 1 = prefill (MFMA tiles staged through LDS), 2 = decode (weight streaming, small M). */
+enum { MOE_VARIANT_AUTO = 0, MOE_VARIANT_PREFILL = 1, MOE_VARIANT_DECODE = 2 };
+
+/* block_m that moe_forward's automatic variant wants moe_align to use. */
+int moe_preferred_block_m(int T, int H, int I, int E, int k, moe_dtype dt);
+/* The variant moe_forward will run for these sizes (1 or 2). */
+int moe_auto_variant(int T, int H, int I, int E, int k, moe_dtype dt);
+
+/* GEMM1 + SwiGLU: a[r, :] (dtype dt, [T*k, I]) for every non-sentinel row r of the
+ * table; rows never routed are left untouched. */
+moe_status moe_gemm1_swiglu(const void* x, const void* w13, const int32_t* sorted_ids,
+                            const int32_t* expert_ids, const int32_t* num_tokens_post_padded,
+                            int T, int H, int I, int E, int k, int block_m, moe_dtype dt,
+                            int variant, void* a, void* stream);
+
+/* GEMM2 x router weight: y[r, :] = topk_w[r] * a[r] . W2[e]^T (fp32, [T*k, H]). */
+moe_status moe_gemm2_weighted(const void* a, const void* w2, const float* topk_w,
+                              const int32_t* sorted_ids, const int32_t* expert_ids,
+                              const int32_t* num_tokens_post_padded, int T, int H, int I,
+                              int E, int k, int block_m, moe_dtype dt, int variant, float* y,
+                              void* stream);
+
+/* Combine: out[t, :] = sum_{j<k} y[t*k + j, :] in slot order (fp32), rounded once to
+ * dt.  Every routed row of y must have been written. */
+moe_status moe_combine(const float* y, int T, int H, int k, moe_dtype dt, void* out,
+                       void* stream);
+
+/* GEMM1+SwiGLU, GEMM2 x weight and combine.  ws: moe_forward_workspace_size bytes
+ * (holds a and y). */
+size_t moe_forward_workspace_size(int T, int H, int I, int E, int k, moe_dtype dt);
+moe_status moe_forward(const void* x, const void* w13, const void* w2, const float* topk_w,
+                       const int32_t* sorted_ids, const int32_t* expert_ids,
+                       const int32_t* num_tokens_post_padded, int T, int H, int I, int E,
+                       int k, int block_m, moe_dtype dt, int variant, void* out, void* ws,
+                       size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------------- */
+/* The whole layer: route -> align (block_m = moe_preferred_block_m) -> forward.
+ * topk_ids_out / topk_w_out ([T,k]) optionally receive the routing; when NULL the
+ * routing lives in the workspace.  ws: moe_layer_workspace_size bytes. */
+size_t moe_layer_workspace_size(int T, int H, int I, int E, int k, moe_dtype dt);
+moe_status moe_layer(const void* x, const void* wg, const void* w13, const void* w2,
+                     const moe_route_cfg* cfg, int T, int H, int I, int E, int k, moe_dtype dt,
+                     void* out, int32_t* topk_ids_out, float* topk_w_out, void* ws,
+                     size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------------- */
+const char* moe_status_string(int status);
+/* Detail of the last error on the calling thread ("" if none). */
+const char* moe_last_error(void);
+/* Library version string. */
+const char* moe_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_MI355X_H */

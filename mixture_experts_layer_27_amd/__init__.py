@@ -1,0 +1,202 @@
+"""Python binding of libmoe_mi355x.so (fused top-k MoE SwiGLU layer for MI355X).
+
+Argument marshalling only: every step of the layer runs in the library's HIP
+kernels.  torch supplies device memory (outputs and workspaces are allocated
+here as torch tensors) and the current HIP stream.  The C entry points and their
+contracts are declared in include/moe_mi355x.h; each function below has the same
+name and forwards to it.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+from ._lib import lib, LIB_PATH, MoeError, RouteCfg, check  # noqa: F401
+
+F32, BF16 = 0, 1
+ROUTE_SOFTMAX_TOPK_RENORM, ROUTE_TOPK_THEN_SOFTMAX, ROUTE_SIGMOID_BIAS_GROUPED = 0, 1, 2
+VARIANT_AUTO, VARIANT_PREFILL, VARIANT_DECODE = 0, 1, 2
+
+__all__ = [
+    "moe_route", "moe_route_from_logits", "moe_align", "moe_align_capacity",
+    "moe_gemm1_swiglu", "moe_gemm2_weighted", "moe_combine", "moe_forward", "moe_layer",
+    "moe_preferred_block_m", "moe_auto_variant", "moe_layer_workspace_size",
+    "moe_forward_workspace_size", "moe_align_workspace_size", "moe_route_workspace_size",
+    "route_cfg", "MoeError", "LIB_PATH",
+]
+
+
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.float32:
+        return F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _p(t):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensors must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _ws(nbytes: int, device) -> torch.Tensor:
+    return torch.empty(max(int(nbytes), 16), dtype=torch.uint8, device=device)
+
+
+def route_cfg(mode: int, logit_offset=None, select_bias=None, n_group: int = 0,
+              topk_group: int = 0, routed_scaling: float = 1.0) -> RouteCfg:
+    """Build the moe_route_cfg struct (keeps references to the device tensors)."""
+    c = RouteCfg()
+    c.mode = int(mode)
+    c.logit_offset = None if logit_offset is None else logit_offset.data_ptr()
+    c.select_bias = None if select_bias is None else select_bias.data_ptr()
+    c.n_group = int(n_group)
+    c.topk_group = int(topk_group)
+    c.routed_scaling = float(routed_scaling)
+    c._keep = (logit_offset, select_bias)
+    for t in (logit_offset, select_bias):
+        if t is not None and (t.dtype != torch.float32 or not t.is_cuda or not t.is_contiguous()):
+            raise ValueError("offset/bias must be contiguous fp32 GPU tensors")
+    return c
+
+
+def moe_route_workspace_size(T: int, E: int) -> int:
+    return lib.moe_route_workspace_size(T, E)
+
+
+def moe_route(x, wg, k, cfg: RouteCfg, logits_out=None):
+    """-> (topk_ids int32 [T,k], topk_w fp32 [T,k]); fills logits_out [T,E] if given."""
+    T, H = x.shape
+    E = wg.shape[0]
+    ids = torch.empty(T, k, dtype=torch.int32, device=x.device)
+    w = torch.empty(T, k, dtype=torch.float32, device=x.device)
+    nws = 0 if logits_out is not None else lib.moe_route_workspace_size(T, E)
+    ws = _ws(nws, x.device)
+    check(lib.moe_route(_p(x), _p(wg), T, H, E, k, _dt(x), ctypes.byref(cfg), _p(ids), _p(w),
+                        _p(logits_out), _p(ws), ws.numel(), _stream()), "moe_route")
+    return ids, w
+
+
+def moe_route_from_logits(logits, k, cfg: RouteCfg):
+    T, E = logits.shape
+    ids = torch.empty(T, k, dtype=torch.int32, device=logits.device)
+    w = torch.empty(T, k, dtype=torch.float32, device=logits.device)
+    check(lib.moe_route_from_logits(_p(logits), T, E, k, ctypes.byref(cfg), _p(ids), _p(w),
+                                    _stream()), "moe_route_from_logits")
+    return ids, w
+
+
+def moe_align_capacity(T: int, k: int, E: int, block_m: int) -> int:
+    return lib.moe_align_capacity(T, k, E, block_m)
+
+
+def moe_align_workspace_size(T: int, k: int, E: int, block_m: int) -> int:
+    return lib.moe_align_workspace_size(T, k, E, block_m)
+
+
+def moe_align(topk_ids, E: int, block_m: int, out=None):
+    """-> (sorted_ids [cap], expert_ids [cap/block_m], num_tokens_post_padded [1],
+    expert_counts [E]), all int32 on the GPU.  ``out`` may supply those four buffers."""
+    T, k = topk_ids.shape
+    cap = lib.moe_align_capacity(T, k, E, block_m)
+    dev = topk_ids.device
+    if out is None:
+        sorted_ids = torch.empty(max(cap, 1), dtype=torch.int32, device=dev)[:cap]
+        expert_ids = torch.empty(max(cap // block_m, 1), dtype=torch.int32, device=dev)[:cap // block_m]
+        ntpp = torch.empty(1, dtype=torch.int32, device=dev)
+        counts = torch.empty(E, dtype=torch.int32, device=dev)
+    else:
+        sorted_ids, expert_ids, ntpp, counts = out
+    ws = _ws(lib.moe_align_workspace_size(T, k, E, block_m), dev)
+    check(lib.moe_align(_p(topk_ids), T, k, E, block_m, _p(sorted_ids), _p(expert_ids), _p(ntpp),
+                        _p(counts), _p(ws), ws.numel(), _stream()), "moe_align")
+    return sorted_ids, expert_ids, ntpp, counts
+
+
+def moe_preferred_block_m(T, H, I, E, k, dtype) -> int:
+    return lib.moe_preferred_block_m(T, H, I, E, k, dtype)
+
+
+def moe_auto_variant(T, H, I, E, k, dtype) -> int:
+    return lib.moe_auto_variant(T, H, I, E, k, dtype)
+
+
+def moe_gemm1_swiglu(x, w13, sorted_ids, expert_ids, ntpp, k, block_m, variant=0, a=None):
+    T, H = x.shape
+    E, I2, _ = w13.shape
+    I = I2 // 2
+    if a is None:
+        a = torch.zeros(T * k, I, dtype=x.dtype, device=x.device)
+    check(lib.moe_gemm1_swiglu(_p(x), _p(w13), _p(sorted_ids), _p(expert_ids), _p(ntpp), T, H, I,
+                               E, k, block_m, _dt(x), variant, _p(a), _stream()),
+          "moe_gemm1_swiglu")
+    return a
+
+
+def moe_gemm2_weighted(a, w2, topk_w, sorted_ids, expert_ids, ntpp, T, k, block_m, variant=0,
+                       y=None):
+    E, H, I = w2.shape
+    if y is None:
+        y = torch.zeros(T * k, H, dtype=torch.float32, device=a.device)
+    check(lib.moe_gemm2_weighted(_p(a), _p(w2), _p(topk_w), _p(sorted_ids), _p(expert_ids),
+                                 _p(ntpp), T, H, I, E, k, block_m, _dt(a), variant, _p(y),
+                                 _stream()), "moe_gemm2_weighted")
+    return y
+
+
+def moe_combine(y, T, k, dtype, out=None):
+    H = y.shape[1]
+    if out is None:
+        out = torch.empty(T, H, dtype=dtype, device=y.device)
+    check(lib.moe_combine(_p(y), T, H, k, _dt(out), _p(out), _stream()), "moe_combine")
+    return out
+
+
+def moe_forward_workspace_size(T, H, I, E, k, dtype) -> int:
+    return lib.moe_forward_workspace_size(T, H, I, E, k, dtype)
+
+
+def moe_forward(x, w13, w2, topk_w, sorted_ids, expert_ids, ntpp, k, block_m, variant=0,
+                out=None, ws=None):
+    T, H = x.shape
+    E, I2, _ = w13.shape
+    I = I2 // 2
+    if out is None:
+        out = torch.empty(T, H, dtype=x.dtype, device=x.device)
+    if ws is None:
+        ws = _ws(lib.moe_forward_workspace_size(T, H, I, E, k, _dt(x)), x.device)
+    check(lib.moe_forward(_p(x), _p(w13), _p(w2), _p(topk_w), _p(sorted_ids), _p(expert_ids),
+                          _p(ntpp), T, H, I, E, k, block_m, _dt(x), variant, _p(out), _p(ws),
+                          ws.numel(), _stream()), "moe_forward")
+    return out
+
+
+def moe_layer_workspace_size(T, H, I, E, k, dtype) -> int:
+    return lib.moe_layer_workspace_size(T, H, I, E, k, dtype)
+
+
+def moe_layer(x, wg, w13, w2, k, cfg: RouteCfg, out=None, ws=None, topk_ids_out=None,
+              topk_w_out=None):
+    """route -> align -> GEMM1+SwiGLU -> GEMM2 x weight -> combine; returns out [T,H]."""
+    T, H = x.shape
+    E, I2, _ = w13.shape
+    I = I2 // 2
+    if out is None:
+        out = torch.empty(T, H, dtype=x.dtype, device=x.device)
+    if ws is None:
+        ws = _ws(lib.moe_layer_workspace_size(T, H, I, E, k, _dt(x)), x.device)
+    check(lib.moe_layer(_p(x), _p(wg), _p(w13), _p(w2), ctypes.byref(cfg), T, H, I, E, k, _dt(x),
+                        _p(out), _p(topk_ids_out), _p(topk_w_out), _p(ws), ws.numel(),
+                        _stream()), "moe_layer")
+    return out

@@ -1,0 +1,52 @@
+// Internal host-side launchers of the HIP kernels (not exported; moe_api.cpp is the
+// only caller).  All sizes are validated by the caller.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+struct RouteArgs {
+  int mode;
+  const float* offset;   // [E] or null
+  const float* bias;     // [E] or null
+  int n_group, topk_group;
+  float scaling;
+};
+
+// router
+hipError_t launch_router_logits(const void* x, const void* wg, int T, int H, int E, bool bf16,
+                                float* logits, hipStream_t s);
+hipError_t launch_topk(const float* logits, int T, int E, int k, const RouteArgs& a,
+                       int32_t* ids, float* w, hipStream_t s);
+
+// align
+size_t align_ws_bytes(int R, int E);
+hipError_t launch_align(const int32_t* ids, int R, int E, int bm, int64_t cap,
+                        int32_t* sorted_ids, int32_t* expert_ids, int32_t* ntpp,
+                        int32_t* counts, int32_t* ws_hist, hipStream_t s);
+
+// expert GEMMs
+struct GemmArgs {
+  const void* A;             // GEMM1: x [T,H]; GEMM2: a [R,I]
+  const void* B;             // GEMM1: W13 [E,2I,H]; GEMM2: W2 [E,H,I]
+  void* C;                   // GEMM1: a [R,I] (bf16/f32); GEMM2: y [R,H] f32
+  const float* topk_w;       // GEMM2 only
+  const int32_t* sorted_ids;
+  const int32_t* expert_ids;
+  const int32_t* ntpp;
+  int T, H, I, E, k, block_m;
+  int64_t cap;               // capacity of sorted_ids
+};
+
+// variant: 1 prefill, 2 decode
+hipError_t launch_gemm1(const GemmArgs& g, bool bf16, int variant, hipStream_t s);
+hipError_t launch_gemm2(const GemmArgs& g, bool bf16, int variant, hipStream_t s);
+hipError_t launch_combine(const float* y, int T, int H, int k, bool bf16, void* out,
+                          hipStream_t s);
+
+// which prefill tile height the MFMA kernels use for a given align block_m (0 = none)
+int prefill_tile_m(int block_m);
+
+}  // namespace moe

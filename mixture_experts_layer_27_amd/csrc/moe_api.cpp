@@ -1,0 +1,422 @@
+// Host side of the C ABI declared in include/moe_mi355x.h: argument validation,
+// workspace sizing, variant choice from host-known sizes, kernel dispatch.
+// Nothing here allocates, copies or synchronises; every call only enqueues work.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "../../include/moe_mi355x.h"
+#include "launch.hpp"
+
+namespace {
+
+thread_local std::string g_err;
+
+moe_status fail(moe_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+moe_status ok() {
+  g_err.clear();
+  return MOE_OK;
+}
+
+moe_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(MOE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool valid_dt(int dt) { return dt == MOE_F32 || dt == MOE_BF16; }
+size_t esize(moe_dtype dt) { return dt == MOE_BF16 ? 2 : 4; }
+size_t round_up(size_t v) { return (v + 255) & ~static_cast<size_t>(255); }
+bool is_pow2(int v) { return v > 0 && (v & (v - 1)) == 0; }
+
+constexpr int kMaxE = 512;
+constexpr int kMaxK = 16;
+
+moe_status check_tke(int T, int k, int E) {
+  if (T < 0) return fail(MOE_ERR_INVALID_ARG, "T=%d must be >= 0", T);
+  if (k < 1 || k > kMaxK) return fail(MOE_ERR_UNSUPPORTED, "k=%d outside [1, %d]", k, kMaxK);
+  if (E < k) return fail(MOE_ERR_INVALID_ARG, "E=%d must be >= k=%d", E, k);
+  if (E > kMaxE) return fail(MOE_ERR_UNSUPPORTED, "E=%d above %d", E, kMaxE);
+  if (static_cast<int64_t>(T) * k >= (int64_t(1) << 31))
+    return fail(MOE_ERR_UNSUPPORTED, "T*k=%lld does not fit int32",
+                static_cast<long long>(T) * k);
+  return MOE_OK;
+}
+
+int64_t capacity(int T, int k, int E, int bm) {
+  const int64_t R = static_cast<int64_t>(T) * k;
+  const int64_t bound = R + std::min<int64_t>(E, R) * (bm - 1);
+  return bound / bm * bm;
+}
+
+moe_status check_route_cfg(const moe_route_cfg* cfg, int E, int k) {
+  if (!cfg) return fail(MOE_ERR_INVALID_ARG, "cfg is NULL");
+  if (cfg->mode < 0 || cfg->mode > 2) return fail(MOE_ERR_INVALID_ARG, "mode=%d", cfg->mode);
+  if (cfg->mode != MOE_ROUTE_SIGMOID_BIAS_GROUPED) {
+    if (cfg->select_bias)
+      return fail(MOE_ERR_INVALID_ARG, "select_bias is only meaningful for the sigmoid router");
+    return MOE_OK;
+  }
+  const int ng = cfg->n_group, tg = cfg->topk_group;
+  if (ng == 0 && tg == 0) return MOE_OK;
+  if (ng <= 0 || tg <= 0) return fail(MOE_ERR_INVALID_ARG, "n_group=%d topk_group=%d", ng, tg);
+  if (ng > 64) return fail(MOE_ERR_UNSUPPORTED, "n_group=%d above 64", ng);
+  if (E % ng != 0) return fail(MOE_ERR_INVALID_ARG, "n_group=%d does not divide E=%d", ng, E);
+  if (E / ng < 2) return fail(MOE_ERR_INVALID_ARG, "groups need >= 2 experts (E/n_group=%d)", E / ng);
+  if (tg > ng) return fail(MOE_ERR_INVALID_ARG, "topk_group=%d > n_group=%d", tg, ng);
+  if (static_cast<int64_t>(tg) * (E / ng) < k)
+    return fail(MOE_ERR_INVALID_ARG, "topk_group*E/n_group=%d < k=%d", tg * (E / ng), k);
+  return MOE_OK;
+}
+
+moe_route_cfg default_cfg() {
+  moe_route_cfg c;
+  std::memset(&c, 0, sizeof(c));
+  c.routed_scaling = 1.f;
+  return c;
+}
+
+moe::RouteArgs route_args(const moe_route_cfg* cfg) {
+  moe::RouteArgs a;
+  a.mode = cfg->mode;
+  a.offset = cfg->logit_offset;
+  a.bias = cfg->select_bias;
+  a.n_group = cfg->mode == 2 ? cfg->n_group : 0;
+  a.topk_group = cfg->mode == 2 ? cfg->topk_group : 0;
+  a.scaling = cfg->mode == 2 ? cfg->routed_scaling : 1.f;
+  return a;
+}
+
+int auto_variant(int T, int H, int I, int E, int k, moe_dtype dt) {
+  (void)H; (void)I;
+  if (dt != MOE_BF16) return MOE_VARIANT_PREFILL;
+  const int64_t R = static_cast<int64_t>(T) * k;
+  // decode when the average expert holds at most 8 routed rows
+  return R <= 8 * static_cast<int64_t>(E) ? MOE_VARIANT_DECODE : MOE_VARIANT_PREFILL;
+}
+
+int preferred_bm(int T, int H, int I, int E, int k, moe_dtype dt) {
+  if (dt != MOE_BF16) return 16;
+  return auto_variant(T, H, I, E, k, dt) == MOE_VARIANT_DECODE ? 32 : 128;
+}
+
+moe_status check_gemm_common(int T, int H, int I, int E, int k, int block_m, int dt,
+                             int variant) {
+  moe_status st = check_tke(T, k, E);
+  if (st != MOE_OK) return st;
+  if (!valid_dt(dt)) return fail(MOE_ERR_INVALID_ARG, "dtype=%d", dt);
+  if (H <= 0 || I <= 0) return fail(MOE_ERR_INVALID_ARG, "H=%d I=%d must be > 0", H, I);
+  if (!is_pow2(block_m) || block_m > 256)
+    return fail(MOE_ERR_INVALID_ARG, "block_m=%d must be a power of two <= 256", block_m);
+  if (variant < 0 || variant > 2) return fail(MOE_ERR_INVALID_ARG, "variant=%d", variant);
+  if (dt == MOE_BF16) {
+    if (H % 64 || I % 64)
+      return fail(MOE_ERR_UNSUPPORTED, "bf16 path needs H, I multiples of 64 (H=%d I=%d)", H, I);
+    if (moe::prefill_tile_m(block_m) == 0)
+      return fail(MOE_ERR_UNSUPPORTED, "bf16 expert GEMMs need block_m >= 32 (got %d)", block_m);
+  }
+  if (static_cast<int64_t>(T) * k * std::max(H, I) >= (int64_t(1) << 40))
+    return fail(MOE_ERR_UNSUPPORTED, "tensor too large");
+  return MOE_OK;
+}
+
+int resolve_variant(int variant, int T, int H, int I, int E, int k, moe_dtype dt) {
+  return variant == MOE_VARIANT_AUTO ? auto_variant(T, H, I, E, k, dt) : variant;
+}
+
+moe::GemmArgs gemm_args(const void* A, const void* B, void* C, const float* topk_w,
+                        const int32_t* sorted_ids, const int32_t* expert_ids,
+                        const int32_t* ntpp, int T, int H, int I, int E, int k, int block_m) {
+  moe::GemmArgs g;
+  g.A = A; g.B = B; g.C = C; g.topk_w = topk_w;
+  g.sorted_ids = sorted_ids; g.expert_ids = expert_ids; g.ntpp = ntpp;
+  g.T = T; g.H = H; g.I = I; g.E = E; g.k = k; g.block_m = block_m;
+  g.cap = capacity(T, k, E, block_m);
+  return g;
+}
+
+size_t forward_ws(int T, int H, int I, int k, moe_dtype dt) {
+  const size_t R = static_cast<size_t>(T) * k;
+  return round_up(R * I * esize(dt)) + round_up(R * H * sizeof(float));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_version(void) { return "moe_mi355x 0.1 (gfx950)"; }
+
+const char* moe_status_string(int status) {
+  switch (status) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_INVALID_ARG: return "MOE_ERR_INVALID_ARG";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED";
+    case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP";
+    default: return "MOE_ERR_UNKNOWN";
+  }
+}
+
+const char* moe_last_error(void) { return g_err.c_str(); }
+
+// ------------------------------------------------------------------------------ route
+size_t moe_route_workspace_size(int T, int E) {
+  if (T <= 0 || E <= 0) return 0;
+  return round_up(static_cast<size_t>(T) * E * sizeof(float));
+}
+
+moe_status moe_route(const void* x, const void* wg, int T, int H, int E, int k, moe_dtype dt,
+                     const moe_route_cfg* cfg, int32_t* topk_ids, float* topk_w,
+                     float* logits_out, void* ws, size_t ws_bytes, void* stream) {
+  moe_status st = check_tke(T, k, E);
+  if (st != MOE_OK) return st;
+  if (!valid_dt(dt)) return fail(MOE_ERR_INVALID_ARG, "dtype=%d", dt);
+  if (H <= 0) return fail(MOE_ERR_INVALID_ARG, "H=%d", H);
+  if ((st = check_route_cfg(cfg, E, k)) != MOE_OK) return st;
+  if (T == 0) return ok();
+  if (!x || !wg || !topk_ids || !topk_w) return fail(MOE_ERR_INVALID_ARG, "NULL tensor pointer");
+  if (dt == MOE_BF16) {
+    if (H % 64) return fail(MOE_ERR_UNSUPPORTED, "bf16 router needs H %% 64 == 0 (H=%d)", H);
+    if (!aligned16(x) || !aligned16(wg)) return fail(MOE_ERR_INVALID_ARG, "x/Wg not 16-byte aligned");
+  }
+  float* logits = logits_out;
+  if (!logits) {
+    if (!ws || ws_bytes < moe_route_workspace_size(T, E))
+      return fail(MOE_ERR_WORKSPACE, "route workspace needs %zu bytes",
+                  moe_route_workspace_size(T, E));
+    logits = static_cast<float*>(ws);
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = moe::launch_router_logits(x, wg, T, H, E, dt == MOE_BF16, logits, s);
+  if (e != hipSuccess) return hip_status(e, "router logits");
+  e = moe::launch_topk(logits, T, E, k, route_args(cfg), topk_ids, topk_w, s);
+  return hip_status(e, "top-k");
+}
+
+moe_status moe_route_from_logits(const float* logits, int T, int E, int k,
+                                 const moe_route_cfg* cfg, int32_t* topk_ids, float* topk_w,
+                                 void* stream) {
+  moe_status st = check_tke(T, k, E);
+  if (st != MOE_OK) return st;
+  if ((st = check_route_cfg(cfg, E, k)) != MOE_OK) return st;
+  if (T == 0) return ok();
+  if (!logits || !topk_ids || !topk_w) return fail(MOE_ERR_INVALID_ARG, "NULL tensor pointer");
+  hipError_t e = moe::launch_topk(logits, T, E, k, route_args(cfg), topk_ids, topk_w,
+                                  static_cast<hipStream_t>(stream));
+  return hip_status(e, "top-k");
+}
+
+// ------------------------------------------------------------------------------ align
+int64_t moe_align_capacity(int T, int k, int E, int block_m) {
+  if (T < 0 || k < 1 || E < 1 || block_m < 1) return -1;
+  return capacity(T, k, E, block_m);
+}
+
+size_t moe_align_workspace_size(int T, int k, int E, int block_m) {
+  (void)block_m;
+  if (T <= 0 || k < 1 || E < 1) return 0;
+  return round_up(moe::align_ws_bytes(T * k, E));
+}
+
+moe_status moe_align(const int32_t* topk_ids, int T, int k, int E, int block_m,
+                     int32_t* sorted_ids, int32_t* expert_ids,
+                     int32_t* num_tokens_post_padded, int32_t* expert_counts, void* ws,
+                     size_t ws_bytes, void* stream) {
+  moe_status st = check_tke(T, k, E);
+  if (st != MOE_OK) return st;
+  if (!is_pow2(block_m) || block_m > 256)
+    return fail(MOE_ERR_INVALID_ARG, "block_m=%d must be a power of two <= 256", block_m);
+  const int64_t cap = capacity(T, k, E, block_m);
+  if (cap >= (int64_t(1) << 31)) return fail(MOE_ERR_UNSUPPORTED, "capacity %lld too large",
+                                             static_cast<long long>(cap));
+  if (!num_tokens_post_padded) return fail(MOE_ERR_INVALID_ARG, "num_tokens_post_padded is NULL");
+  if (T > 0 && (!topk_ids || !sorted_ids || !expert_ids))
+    return fail(MOE_ERR_INVALID_ARG, "NULL tensor pointer");
+  const size_t need = moe_align_workspace_size(T, k, E, block_m);
+  if (need > 0 && (!ws || ws_bytes < need))
+    return fail(MOE_ERR_WORKSPACE, "align workspace needs %zu bytes", need);
+  hipError_t e = moe::launch_align(topk_ids, T * k, E, block_m, cap, sorted_ids, expert_ids,
+                                   num_tokens_post_padded, expert_counts,
+                                   static_cast<int32_t*>(ws), static_cast<hipStream_t>(stream));
+  return hip_status(e, "align");
+}
+
+// ------------------------------------------------------------------------------ forward
+int moe_auto_variant(int T, int H, int I, int E, int k, moe_dtype dt) {
+  return auto_variant(T, H, I, E, k, dt);
+}
+
+int moe_preferred_block_m(int T, int H, int I, int E, int k, moe_dtype dt) {
+  return preferred_bm(T, H, I, E, k, dt);
+}
+
+moe_status moe_gemm1_swiglu(const void* x, const void* w13, const int32_t* sorted_ids,
+                            const int32_t* expert_ids, const int32_t* num_tokens_post_padded,
+                            int T, int H, int I, int E, int k, int block_m, moe_dtype dt,
+                            int variant, void* a, void* stream) {
+  moe_status st = check_gemm_common(T, H, I, E, k, block_m, dt, variant);
+  if (st != MOE_OK) return st;
+  if (T == 0) return ok();
+  if (!x || !w13 || !sorted_ids || !expert_ids || !num_tokens_post_padded || !a)
+    return fail(MOE_ERR_INVALID_ARG, "NULL tensor pointer");
+  if (!aligned16(x) || !aligned16(w13) || !aligned16(a))
+    return fail(MOE_ERR_INVALID_ARG, "x/W13/a not 16-byte aligned");
+  const int v = resolve_variant(variant, T, H, I, E, k, dt);
+  moe::GemmArgs g = gemm_args(x, w13, a, nullptr, sorted_ids, expert_ids,
+                              num_tokens_post_padded, T, H, I, E, k, block_m);
+  return hip_status(moe::launch_gemm1(g, dt == MOE_BF16, v, static_cast<hipStream_t>(stream)),
+                    "gemm1");
+}
+
+moe_status moe_gemm2_weighted(const void* a, const void* w2, const float* topk_w,
+                              const int32_t* sorted_ids, const int32_t* expert_ids,
+                              const int32_t* num_tokens_post_padded, int T, int H, int I,
+                              int E, int k, int block_m, moe_dtype dt, int variant, float* y,
+                              void* stream) {
+  moe_status st = check_gemm_common(T, H, I, E, k, block_m, dt, variant);
+  if (st != MOE_OK) return st;
+  if (T == 0) return ok();
+  if (!a || !w2 || !topk_w || !sorted_ids || !expert_ids || !num_tokens_post_padded || !y)
+    return fail(MOE_ERR_INVALID_ARG, "NULL tensor pointer");
+  if (!aligned16(a) || !aligned16(w2) || !aligned16(y))
+    return fail(MOE_ERR_INVALID_ARG, "a/W2/y not 16-byte aligned");
+  const int v = resolve_variant(variant, T, H, I, E, k, dt);
+  moe::GemmArgs g = gemm_args(a, w2, y, topk_w, sorted_ids, expert_ids, num_tokens_post_padded,
+                              T, H, I, E, k, block_m);
+  return hip_status(moe::launch_gemm2(g, dt == MOE_BF16, v, static_cast<hipStream_t>(stream)),
+                    "gemm2");
+}
+
+moe_status moe_combine(const float* y, int T, int H, int k, moe_dtype dt, void* out,
+                       void* stream) {
+  if (T < 0 || H <= 0 || k < 1 || k > kMaxK) return fail(MOE_ERR_INVALID_ARG, "T/H/k out of range");
+  if (!valid_dt(dt)) return fail(MOE_ERR_INVALID_ARG, "dtype=%d", dt);
+  if (T == 0) return ok();
+  if (!y || !out) return fail(MOE_ERR_INVALID_ARG, "NULL tensor pointer");
+  return hip_status(moe::launch_combine(y, T, H, k, dt == MOE_BF16, out,
+                                        static_cast<hipStream_t>(stream)),
+                    "combine");
+}
+
+size_t moe_forward_workspace_size(int T, int H, int I, int E, int k, moe_dtype dt) {
+  (void)E;
+  if (T <= 0 || H <= 0 || I <= 0 || k < 1 || !valid_dt(dt)) return 0;
+  return forward_ws(T, H, I, k, dt);
+}
+
+moe_status moe_forward(const void* x, const void* w13, const void* w2, const float* topk_w,
+                       const int32_t* sorted_ids, const int32_t* expert_ids,
+                       const int32_t* num_tokens_post_padded, int T, int H, int I, int E,
+                       int k, int block_m, moe_dtype dt, int variant, void* out, void* ws,
+                       size_t ws_bytes, void* stream) {
+  moe_status st = check_gemm_common(T, H, I, E, k, block_m, dt, variant);
+  if (st != MOE_OK) return st;
+  if (T == 0) return ok();
+  if (!x || !w13 || !w2 || !topk_w || !sorted_ids || !expert_ids || !num_tokens_post_padded ||
+      !out)
+    return fail(MOE_ERR_INVALID_ARG, "NULL tensor pointer");
+  if (!aligned16(x) || !aligned16(w13) || !aligned16(w2) || !aligned16(out))
+    return fail(MOE_ERR_INVALID_ARG, "x/W13/W2/out not 16-byte aligned");
+  const size_t need = forward_ws(T, H, I, k, dt);
+  if (!ws || ws_bytes < need) return fail(MOE_ERR_WORKSPACE, "forward workspace needs %zu bytes", need);
+  if (!aligned16(ws)) return fail(MOE_ERR_INVALID_ARG, "workspace not 16-byte aligned");
+  const size_t R = static_cast<size_t>(T) * k;
+  uint8_t* base = static_cast<uint8_t*>(ws);
+  void* a = base;
+  float* y = reinterpret_cast<float*>(base + round_up(R * I * esize(dt)));
+  const int v = resolve_variant(variant, T, H, I, E, k, dt);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool bf = dt == MOE_BF16;
+  moe::GemmArgs g1 = gemm_args(x, w13, a, nullptr, sorted_ids, expert_ids,
+                               num_tokens_post_padded, T, H, I, E, k, block_m);
+  hipError_t e = moe::launch_gemm1(g1, bf, v, s);
+  if (e != hipSuccess) return hip_status(e, "gemm1");
+  moe::GemmArgs g2 = gemm_args(a, w2, y, topk_w, sorted_ids, expert_ids, num_tokens_post_padded,
+                               T, H, I, E, k, block_m);
+  e = moe::launch_gemm2(g2, bf, v, s);
+  if (e != hipSuccess) return hip_status(e, "gemm2");
+  return hip_status(moe::launch_combine(y, T, H, k, bf, out, s), "combine");
+}
+
+// ------------------------------------------------------------------------------ layer
+namespace {
+struct LayerPlan {
+  int bm;
+  int64_t cap;
+  size_t off_logits, off_ids, off_w, off_sorted, off_eids, off_ntpp, off_counts, off_align,
+      off_fwd, total;
+};
+
+LayerPlan plan_layer(int T, int H, int I, int E, int k, moe_dtype dt) {
+  LayerPlan p;
+  p.bm = preferred_bm(T, H, I, E, k, dt);
+  p.cap = capacity(T, k, E, p.bm);
+  const size_t R = static_cast<size_t>(T) * k;
+  size_t off = 0;
+  p.off_logits = off; off += round_up(static_cast<size_t>(T) * E * sizeof(float));
+  p.off_ids = off; off += round_up(R * sizeof(int32_t));
+  p.off_w = off; off += round_up(R * sizeof(float));
+  p.off_sorted = off; off += round_up(static_cast<size_t>(p.cap) * sizeof(int32_t));
+  p.off_eids = off; off += round_up(static_cast<size_t>(p.cap / p.bm) * sizeof(int32_t));
+  p.off_ntpp = off; off += round_up(sizeof(int32_t));
+  p.off_counts = off; off += round_up(static_cast<size_t>(E) * sizeof(int32_t));
+  p.off_align = off; off += round_up(moe::align_ws_bytes(static_cast<int>(R), E));
+  p.off_fwd = off; off += forward_ws(T, H, I, k, dt);
+  p.total = off;
+  return p;
+}
+}  // namespace
+
+size_t moe_layer_workspace_size(int T, int H, int I, int E, int k, moe_dtype dt) {
+  if (T <= 0 || H <= 0 || I <= 0 || E <= 0 || k < 1 || !valid_dt(dt)) return 0;
+  return plan_layer(T, H, I, E, k, dt).total;
+}
+
+moe_status moe_layer(const void* x, const void* wg, const void* w13, const void* w2,
+                     const moe_route_cfg* cfg, int T, int H, int I, int E, int k, moe_dtype dt,
+                     void* out, int32_t* topk_ids_out, float* topk_w_out, void* ws,
+                     size_t ws_bytes, void* stream) {
+  moe_status st = check_gemm_common(T, H, I, E, k, 32, dt, MOE_VARIANT_AUTO);
+  if (st != MOE_OK) return st;
+  if ((st = check_route_cfg(cfg, E, k)) != MOE_OK) return st;
+  if (T == 0) return ok();
+  if (!x || !wg || !w13 || !w2 || !out) return fail(MOE_ERR_INVALID_ARG, "NULL tensor pointer");
+  if (dt == MOE_BF16 && (!aligned16(x) || !aligned16(wg) || !aligned16(w13) || !aligned16(w2) ||
+                         !aligned16(out)))
+    return fail(MOE_ERR_INVALID_ARG, "tensor not 16-byte aligned");
+  const LayerPlan p = plan_layer(T, H, I, E, k, dt);
+  if (!ws || ws_bytes < p.total) return fail(MOE_ERR_WORKSPACE, "layer workspace needs %zu bytes", p.total);
+  if (!aligned16(ws)) return fail(MOE_ERR_INVALID_ARG, "workspace not 16-byte aligned");
+  uint8_t* b = static_cast<uint8_t*>(ws);
+  float* logits = reinterpret_cast<float*>(b + p.off_logits);
+  int32_t* ids = topk_ids_out ? topk_ids_out : reinterpret_cast<int32_t*>(b + p.off_ids);
+  float* tw = topk_w_out ? topk_w_out : reinterpret_cast<float*>(b + p.off_w);
+  int32_t* sorted = reinterpret_cast<int32_t*>(b + p.off_sorted);
+  int32_t* eids = reinterpret_cast<int32_t*>(b + p.off_eids);
+  int32_t* ntpp = reinterpret_cast<int32_t*>(b + p.off_ntpp);
+  int32_t* counts = reinterpret_cast<int32_t*>(b + p.off_counts);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = moe::launch_router_logits(x, wg, T, H, E, dt == MOE_BF16, logits, s);
+  if (e != hipSuccess) return hip_status(e, "router logits");
+  e = moe::launch_topk(logits, T, E, k, route_args(cfg), ids, tw, s);
+  if (e != hipSuccess) return hip_status(e, "top-k");
+  e = moe::launch_align(ids, T * k, E, p.bm, p.cap, sorted, eids, ntpp, counts,
+                        reinterpret_cast<int32_t*>(b + p.off_align), s);
+  if (e != hipSuccess) return hip_status(e, "align");
+  return moe_forward(x, w13, w2, tw, sorted, eids, ntpp, T, H, I, E, k, p.bm, dt,
+                     MOE_VARIANT_AUTO, out, b + p.off_fwd, forward_ws(T, H, I, k, dt), stream);
+}
+
+}  // extern "C"

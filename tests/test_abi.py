@@ -1,0 +1,143 @@
+"""Host-only checks of the C ABI (no GPU): the library loads, exports every symbol
+the header declares, validates its arguments before touching the device, and its
+host-side sizing agrees with the oracle's definitions."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from oracle import moe_oracle as O
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_mi355x.h")
+
+OK, INVALID, UNSUPPORTED, WORKSPACE, HIPERR = 0, -1, -2, -3, -4
+FAKE = ctypes.c_void_p(1 << 20)          # aligned non-null pointer, never dereferenced
+
+
+@pytest.fixture(scope="module")
+def L():
+    from mixture_experts_layer_27_amd import _lib
+    return _lib
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for must in ("moe_route", "moe_route_from_logits", "moe_align", "moe_align_capacity",
+                 "moe_forward", "moe_gemm1_swiglu", "moe_gemm2_weighted", "moe_combine",
+                 "moe_layer", "moe_status_string", "moe_last_error"):
+        assert must in names
+
+
+def test_library_exports_every_declared_symbol(L):
+    for name in declared_functions():
+        assert hasattr(L.lib, name), name
+    assert L.lib.moe_version().startswith(b"moe_mi355x")
+
+
+def test_status_strings(L):
+    assert L.lib.moe_status_string(0) == b"MOE_OK"
+    assert L.lib.moe_status_string(-3) == b"MOE_ERR_WORKSPACE"
+
+
+def test_align_capacity_matches_oracle(L):
+    for T in (0, 1, 7, 64, 4096):
+        for k in (1, 2, 8):
+            for E in (8, 128, 256):
+                if k > E:
+                    continue
+                for bm in (1, 4, 16, 32, 64, 128, 256):
+                    assert L.lib.moe_align_capacity(T, k, E, bm) == O.align_capacity(T, k, E, bm)
+
+
+def cfg(L, mode=0, ng=0, tg=0, scale=1.0, bias=None):
+    c = L.RouteCfg()
+    c.mode, c.n_group, c.topk_group, c.routed_scaling = mode, ng, tg, scale
+    c.select_bias = bias
+    return c
+
+
+def route(L, c, T=4, H=64, E=8, k=2, dt=1, x=FAKE, ws_bytes=1 << 20):
+    return L.lib.moe_route(x, FAKE, T, H, E, k, dt, ctypes.byref(c), FAKE, FAKE, None, FAKE,
+                           ws_bytes, None)
+
+
+def test_route_validation(L):
+    assert route(L, cfg(L), k=0) == UNSUPPORTED
+    assert route(L, cfg(L), k=17, E=32) == UNSUPPORTED
+    assert route(L, cfg(L), k=9, E=8) == INVALID
+    assert route(L, cfg(L), E=513) == UNSUPPORTED
+    assert route(L, cfg(L, mode=3)) == INVALID
+    assert route(L, cfg(L), H=96) == UNSUPPORTED                 # bf16 needs H % 64 == 0
+    assert route(L, cfg(L), x=ctypes.c_void_p((1 << 20) + 2)) == INVALID   # misaligned
+    assert route(L, cfg(L), x=None) == INVALID
+    assert route(L, cfg(L), ws_bytes=16) == WORKSPACE            # logits need T*E*4 bytes
+    assert route(L, cfg(L, mode=0, bias=1 << 20)) == INVALID     # bias only for sigmoid router
+    # grouped router constraints
+    assert route(L, cfg(L, 2, ng=3, tg=1), E=8) == INVALID       # 3 does not divide 8
+    assert route(L, cfg(L, 2, ng=8, tg=1), E=8) == INVALID       # groups of one expert
+    assert route(L, cfg(L, 2, ng=4, tg=5), E=8) == INVALID       # keep more groups than exist
+    assert route(L, cfg(L, 2, ng=4, tg=1), E=8, k=4) == INVALID  # 1 group of 2 < k = 4
+    assert route(L, cfg(L, 2, ng=4, tg=0), E=8) == INVALID
+    assert route(L, cfg(L), T=-1) == INVALID
+    assert route(L, cfg(L), T=0) == OK                           # nothing to do, nothing enqueued
+    assert b"k=" in L.lib.moe_last_error() or L.lib.moe_last_error() == b""
+
+
+def test_align_validation(L):
+    f = L.lib.moe_align
+    assert f(FAKE, 4, 2, 8, 3, FAKE, FAKE, FAKE, None, FAKE, 1 << 20, None) == INVALID
+    assert f(FAKE, 4, 2, 8, 512, FAKE, FAKE, FAKE, None, FAKE, 1 << 20, None) == INVALID
+    assert f(FAKE, 4, 2, 8, 16, FAKE, FAKE, None, None, FAKE, 1 << 20, None) == INVALID
+    assert f(None, 4, 2, 8, 16, FAKE, FAKE, FAKE, None, FAKE, 1 << 20, None) == INVALID
+    # large R needs the segment-histogram scratch
+    need = L.lib.moe_align_workspace_size(8192, 8, 128, 128)
+    assert need >= (8192 * 8 // 256) * 128 * 4
+    assert f(FAKE, 8192, 8, 128, 128, FAKE, FAKE, FAKE, None, FAKE, need - 1, None) == WORKSPACE
+    assert f(FAKE, 8192, 8, 128, 128, FAKE, FAKE, FAKE, None, None, 0, None) == WORKSPACE
+
+
+def test_forward_validation(L):
+    f = L.lib.moe_forward
+    args = lambda **kw: dict(dict(T=4, H=64, I=64, E=8, k=2, bm=32, dt=1, var=0, ws=1 << 24), **kw)
+
+    def call(**kw):
+        a = args(**kw)
+        return f(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, a["T"], a["H"], a["I"], a["E"], a["k"],
+                 a["bm"], a["dt"], a["var"], FAKE, FAKE, a["ws"], None)
+
+    assert call(bm=16) == UNSUPPORTED          # bf16 MFMA tiles need block_m >= 32
+    assert call(bm=48) == INVALID
+    assert call(I=96) == UNSUPPORTED           # bf16 needs I % 64 == 0
+    assert call(dt=5) == INVALID
+    assert call(var=3) == INVALID
+    assert call(ws=100) == WORKSPACE
+    assert call(H=0) == INVALID
+    need = L.lib.moe_forward_workspace_size(4, 64, 64, 8, 2, 1)
+    assert need >= 8 * 64 * 2 + 8 * 64 * 4
+    assert call(ws=need - 1) == WORKSPACE
+
+
+def test_layer_workspace_and_variants(L):
+    lib = L.lib
+    # decode shapes pick the small-M variant, prefill shapes the MFMA tiles
+    assert lib.moe_auto_variant(1, 7168, 2048, 256, 8, 1) == 2
+    assert lib.moe_auto_variant(4096, 4096, 14336, 8, 2, 1) == 1
+    for T, H, I, E, k in [(4096, 4096, 14336, 8, 2), (64, 7168, 2048, 256, 8), (64, 64, 96, 8, 2)]:
+        dt = 0 if I == 96 else 1
+        bm = lib.moe_preferred_block_m(T, H, I, E, k, dt)
+        ws = lib.moe_layer_workspace_size(T, H, I, E, k, dt)
+        R = T * k
+        assert ws >= lib.moe_forward_workspace_size(T, H, I, E, k, dt) + R * 8 + T * E * 4 \
+            + lib.moe_align_capacity(T, k, E, bm) * 4
+        c = cfg(L)
+        st = lib.moe_layer(FAKE, FAKE, FAKE, FAKE, ctypes.byref(c), T, H, I, E, k, dt, FAKE, None,
+                           None, FAKE, ws - 1, None)
+        assert st == WORKSPACE

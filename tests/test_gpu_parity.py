@@ -1,0 +1,310 @@
+"""GPU parity of the HIP path against the CPU oracle, through the C ABI, on seeded
+inputs small enough for the oracle to finish in seconds while spanning several tiles
+and ragged tails.  Integer outputs (routing ids, align tables) must be bit-exact;
+fp32 layers within 1e-5 normwise relative error; bf16 layers within 2e-2 of the
+output RMS (max abs error)."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import moe_oracle as O
+from synth import inputs as S
+from tests.gpu_util import (bf16_tol_check, compact_experts, f32_tol_check, lib_cfg,
+                            logit_error_bound, np64, route_kwargs)
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _sync():
+    torch.cuda.synchronize()
+
+
+# ------------------------------------------------------------------------------ align
+
+def _align_case(lib, ids_np, E, bm):
+    ids = torch.from_numpy(np.ascontiguousarray(ids_np, np.int32)).to(DEV)
+    T, k = ids_np.shape
+    sorted_ids, expert_ids, ntpp, counts = lib.moe_align(ids, E, bm)
+    _sync()
+    cap = O.align_capacity(T, k, E, bm)
+    ref = O.align_argsort(ids_np, E, bm, cap)
+    assert sorted_ids.numel() == cap
+    assert int(ntpp.item()) == ref["total"]
+    assert np.array_equal(counts.cpu().numpy(), ref["counts"])
+    assert np.array_equal(expert_ids.cpu().numpy(), ref["expert_ids"])
+    assert np.array_equal(sorted_ids.cpu().numpy(), ref["sorted_ids"])
+
+
+def test_align_worked_example(lib):
+    ids = np.array([[2, 3, 4], [1, 2, 4], [1, 3, 4], [1, 2, 3]], np.int32)
+    _align_case(lib, ids, 5, 4)
+
+
+@pytest.mark.parametrize("bm", [1, 16, 32, 64, 128, 256])
+@pytest.mark.parametrize("T,k,E,skew", [
+    (1, 8, 256, 0.0), (16, 8, 256, 0.0), (64, 8, 256, 0.5), (37, 1, 8, 0.0), (64, 2, 8, 0.0),
+    (1000, 8, 128, 1.2),          # single work-group path, skewed
+    (2048, 8, 256, 0.0),          # R = 16384: multi-launch path
+    (8192, 8, 128, 0.0),          # R = 65536: multi-launch path, many segments
+    (4096, 2, 8, 0.0),            # R = 8192: largest single work-group case
+    (4097, 2, 8, 0.0),            # R = 8194: smallest multi-launch case, ragged last segment
+])
+def test_align_bitexact(lib, bm, T, k, E, skew):
+    ids = S.random_topk_ids(T, k, E, seed=T * 31 + E + bm, skew=skew).numpy()
+    _align_case(lib, ids, E, bm)
+
+
+@pytest.mark.parametrize("bm", [16, 64])
+def test_align_edge_counts(lib, bm):
+    loads = [0, 1, bm - 1, bm, bm + 1, 0, 2 * bm, 3 * bm + 5]
+    k = 2
+    loads[-1] += (-sum(loads)) % k
+    ids = S.ids_with_counts(loads, k, seed=9).numpy()
+    _align_case(lib, ids, len(loads), bm)
+    hot = S.random_topk_ids(3000, 4, 16, seed=2, hot=5).numpy()     # one expert gets every token
+    _align_case(lib, hot, 16, bm)
+    _align_case(lib, S.random_topk_ids(1, 1, 8, seed=0).numpy(), 8, bm)
+
+
+# ------------------------------------------------------------------------------ routing
+
+def _route_from_logits_case(lib, l32, k, mode, offset=None, bias=None, ng=0, tg=0, scale=1.0):
+    T, E = l32.shape
+    dl = torch.from_numpy(l32).to(DEV)
+    off = None if offset is None else torch.from_numpy(offset).to(DEV)
+    bi = None if bias is None else torch.from_numpy(bias).to(DEV)
+    cfg = lib.route_cfg(mode, off, bi, ng, tg, scale)
+    ids, w = lib.moe_route_from_logits(dl, k, cfg)
+    _sync()
+    rid, rw = O.route(l32, k, mode, offset, bias, ng, tg, scale)
+    assert np.array_equal(ids.cpu().numpy(), rid)
+    np.testing.assert_allclose(w.cpu().numpy(), rw, rtol=3e-7, atol=0)
+
+
+@pytest.mark.parametrize("T,E,k", [(1, 8, 2), (257, 8, 2), (300, 128, 8), (64, 256, 8), (33, 512, 16),
+                                   (100, 64, 1), (50, 16, 16)])
+@pytest.mark.parametrize("mode", [0, 1])
+def test_route_from_logits_softmax(lib, T, E, k, mode):
+    rng = np.random.default_rng(T * E + k)
+    l32 = rng.standard_normal((T, E)).astype(np.float32)
+    _route_from_logits_case(lib, l32, k, mode)
+    # exact ties everywhere: logits on a coarse grid
+    lq = (np.round(l32 * 2) / 2).astype(np.float32)
+    _route_from_logits_case(lib, lq, k, mode)
+    off = (rng.standard_normal(E) * 2).astype(np.float32)
+    _route_from_logits_case(lib, l32, k, mode, offset=off)
+
+
+@pytest.mark.parametrize("T,E,k,ng,tg", [(64, 256, 8, 8, 4), (300, 256, 8, 8, 4), (17, 16, 4, 4, 2),
+                                         (40, 64, 6, 0, 0), (33, 512, 8, 64, 3)])
+def test_route_from_logits_grouped(lib, T, E, k, ng, tg):
+    rng = np.random.default_rng(T + E)
+    l32 = rng.standard_normal((T, E)).astype(np.float32)
+    bias = (rng.standard_normal(E) * np.sqrt(0.1)).astype(np.float32)
+    _route_from_logits_case(lib, l32, k, 2, bias=bias, ng=ng, tg=tg, scale=2.5)
+    lq = (np.round(l32 * 4) / 4).astype(np.float32)                    # ties
+    _route_from_logits_case(lib, lq, k, 2, bias=np.zeros(E, np.float32), ng=ng, tg=tg, scale=2.5)
+
+
+def test_route_grouped_page_example(lib):
+    logits, bias = S.page_grouped_router_logits()
+    _route_from_logits_case(lib, logits.numpy(), 4, 2, bias=bias.numpy(), ng=4, tg=2, scale=2.5)
+
+
+@pytest.mark.parametrize("T,H,E,k,mode", [(300, 512, 8, 2, 0), (64, 1024, 128, 8, 0),
+                                          (16, 7168 // 4, 256, 8, 2), (1, 2048, 256, 8, 2),
+                                          (200, 2880, 128, 4, 1)])
+def test_route_fused_logits(lib, T, H, E, k, mode):
+    """moe_route: fp32-accumulated logits within their error bound of the float64 ones;
+    ids identical to the oracle's on every token whose selection margin exceeds twice that
+    bound.  (Bit-exact routing from identical logits is test_route_from_logits_*.)"""
+    g = torch.Generator(device="cpu").manual_seed(T + H)
+    x = torch.randn(T, H, generator=g).to(torch.bfloat16)
+    wg = (torch.randn(E, H, generator=g) / H ** 0.5).to(torch.bfloat16)
+    bias = (torch.randn(E, generator=g) * 0.3).float() if mode == 2 else None
+    ng, tg, sc = (8, 4, 2.5) if mode == 2 else (0, 0, 1.0)
+    logits = torch.empty(T, E, dtype=torch.float32, device=DEV)
+    cfg = lib.route_cfg(mode, None, None if bias is None else bias.to(DEV), ng, tg, sc)
+    ids, w = lib.moe_route(x.to(DEV), wg.to(DEV), k, cfg, logits_out=logits)
+    _sync()
+    x64, wg64 = np64(x), np64(wg)
+    ref = O.router_logits(x64, wg64)
+    bound = logit_error_bound(x64, wg64)
+    got = logits.cpu().numpy().astype(np.float64)
+    assert np.all(np.abs(got - ref) <= bound[:, None])
+    bn = None if bias is None else bias.numpy()
+    rid, _ = O.route(ref.astype(np.float32), k, mode, None, bn, ng, tg, sc)
+    margin = O.selection_margin(ref.astype(np.float32), k, mode, None, bn, ng, tg)
+    clear = margin > 2 * bound
+    assert clear.mean() > 0.5
+    assert np.array_equal(ids.cpu().numpy()[clear], rid[clear])
+    # weights move with the logits: |dw| <= w * (|dl_j| + |dl_0|) for the softmax rules
+    _, rw = O.route(ref.astype(np.float32), k, mode, None, bn, ng, tg, sc)
+    tol = 4 * bound[clear, None] * (sc if mode == 2 else 1.0) + 1e-6
+    assert np.all(np.abs(w.cpu().numpy()[clear] - rw[clear]) <= tol)
+
+
+# ------------------------------------------------------------------------------ expert GEMMs
+
+def _forward_case(lib, x, wg, w13, w2, k, mode, bm, variant, offset=None, bias=None, ng=0, tg=0,
+                  scale=1.0, check_rows=True):
+    """Oracle routing -> GPU align + forward -> compare with the oracle loop."""
+    dt_bf16 = x.dtype == torch.bfloat16
+    x64, wg64, w13_64, w2_64 = np64(x), np64(wg), np64(w13), np64(w2)
+    l32 = O.router_logits(x64, wg64).astype(np.float32)
+    ids, w = O.route(l32, k, mode, offset, bias, ng, tg, scale)
+    w32 = w.astype(np.float32)
+    ref = O.moe_loop(x64, w13_64, w2_64, ids, w32.astype(np.float64), round_a=dt_bf16)
+    T, H = x.shape
+    I = w13.shape[1] // 2
+    dx, d13, d2 = x.to(DEV), w13.to(DEV), w2.to(DEV)
+    dids = torch.from_numpy(ids).to(DEV)
+    dw = torch.from_numpy(w32).to(DEV)
+    sorted_ids, expert_ids, ntpp, counts = lib.moe_align(dids, w13.shape[0], bm)
+    # canaries: a and y get an extra guard row block after the R routed rows
+    R = T * k
+    a = torch.full((R + 8, I), float("nan"), dtype=x.dtype, device=DEV)
+    y = torch.full((R + 8, H), float("nan"), dtype=torch.float32, device=DEV)
+    lib.moe_gemm1_swiglu(dx, d13, sorted_ids, expert_ids, ntpp, k, bm, variant, a=a)
+    lib.moe_gemm2_weighted(a, d2, dw, sorted_ids, expert_ids, ntpp, T, k, bm, variant, y=y)
+    out = lib.moe_combine(y, T, k, x.dtype)
+    out_fwd = lib.moe_forward(dx, d13, d2, dw, sorted_ids, expert_ids, ntpp, k, bm, variant)
+    _sync()
+    if check_rows:
+        assert not torch.isnan(a[:R]).any() and not torch.isnan(y[:R]).any()
+        assert torch.isnan(a[R:]).all() and torch.isnan(y[R:]).all()     # nothing past row R
+    assert torch.equal(out, out_fwd)
+    got = np64(out)
+    if dt_bf16:
+        r = bf16_tol_check(got, ref)
+        # the GPU mirrors the oracle's rounding points: errors are ~ one bf16 ulp of out
+        assert np.mean(np.abs(got - ref)) / np.sqrt(np.mean(ref ** 2)) < 2e-3
+        return r
+    return f32_tol_check(got, ref)
+
+
+def test_forward_fp32_tiny_layer(lib):
+    lay = S.make_layer(S.WORKLOADS["tiny"])
+    for bm in (1, 4, 16, 64):
+        _forward_case(lib, lay.x, lay.wg, lay.w13, lay.w2, 2, 0, bm, 0)
+
+
+@pytest.mark.parametrize("case", ["uniform", "skewed", "decode", "top1"])
+def test_forward_page_test_matrix(lib, case):
+    x, wg, w1, w3, w2, k = S.page_test_case(case)
+    w13 = torch.cat([w1, w3], dim=1)
+    r = _forward_case(lib, x, wg, w13, w2, k, 0, 16, 0)
+    assert r <= 1e-5
+
+
+BF16_SHAPES = [
+    # T, H, I, E, k, mode, skew-offset
+    (200, 256, 192, 8, 2, 0, None),
+    (129, 512, 128, 64, 8, 0, "hot"),
+    (37, 128, 320, 16, 1, 0, None),
+    (64, 256, 128, 32, 4, 1, "zipf"),
+    (24, 512, 256, 64, 8, 2, None),
+    (1, 1024, 256, 256, 8, 2, None),
+]
+
+
+@pytest.mark.parametrize("shape", BF16_SHAPES)
+@pytest.mark.parametrize("bm,variant", [(32, 1), (64, 1), (128, 1), (256, 1), (32, 2), (64, 2)])
+def test_forward_bf16(lib, shape, bm, variant):
+    T, H, I, E, k, mode, skew = shape
+    g = torch.Generator(device="cpu").manual_seed(T * 7 + H + I + E)
+    x = torch.randn(T, H, generator=g).to(torch.bfloat16)
+    wg = (torch.randn(E, H, generator=g) / H ** 0.5).to(torch.bfloat16)
+    w13 = (torch.randn(E, 2 * I, H, generator=g) / H ** 0.5).to(torch.bfloat16)
+    w2 = (torch.randn(E, H, I, generator=g) / I ** 0.5).to(torch.bfloat16)
+    off = None
+    if skew == "hot":
+        off = np.zeros(E, np.float32)
+        off[:8] = 3.0
+    elif skew == "zipf":
+        off = (0.5 * np.log(np.arange(1, E + 1, dtype=np.float64) ** -1.2)).astype(np.float32)
+    bias = (torch.randn(E, generator=g) * 0.3).numpy().astype(np.float32) if mode == 2 else None
+    ng, tg, sc = ((8, 4, 2.5) if E >= 64 else (4, 2, 2.5)) if mode == 2 else (0, 0, 1.0)
+    _forward_case(lib, x, wg, w13, w2, k, mode, bm, variant, off, bias, ng, tg, sc)
+
+
+# ------------------------------------------------------------------------------ whole layer
+
+def _layer_vs_oracle(lib, wl, lay):
+    cfg = lib_cfg(lib, wl, lay)
+    T, k = wl.T, wl.k
+    ids = torch.empty(T, k, dtype=torch.int32, device=DEV)
+    w = torch.empty(T, k, dtype=torch.float32, device=DEV)
+    out = lib.moe_layer(lay.x, lay.wg, lay.w13, lay.w2, k, cfg, topk_ids_out=ids, topk_w_out=w)
+    _sync()
+    x64, wg64 = np64(lay.x), np64(lay.wg)
+    ref_logits = O.router_logits(x64, wg64)
+    kw = route_kwargs(wl, lay)
+    rid, rw = O.route(ref_logits.astype(np.float32), k, wl.mode, **kw)
+    margin = O.selection_margin(ref_logits.astype(np.float32), k, wl.mode, kw["offset"], kw["bias"],
+                                wl.n_group, wl.topk_group)
+    bound = logit_error_bound(x64, wg64)
+    gids = ids.cpu().numpy()
+    same = np.all(gids == rid, axis=1)
+    assert np.all(same | (margin <= 2 * bound)), "routing differs on a token with a clear margin"
+    assert same.mean() > 0.5
+    # the reference output uses the oracle's own routing; tokens routed differently (near
+    # ties within the logits' error bound) are left out of the element-wise comparison
+    ref = O.moe_loop(x64[same], np64(lay.w13), np64(lay.w2), rid[same], rw[same],
+                     round_a=wl.dtype == "bf16")
+    got = np64(out)[same]
+    if wl.dtype == "bf16":
+        return bf16_tol_check(got, ref)
+    return f32_tol_check(got, ref)
+
+
+def test_layer_tiny(lib):
+    wl = S.WORKLOADS["tiny"]
+    lay = S.make_layer(wl, device=DEV)
+    _layer_vs_oracle(lib, wl, lay)
+    # the page's printed loads are reproduced by the GPU router
+    ids = torch.empty(64, 2, dtype=torch.int32, device=DEV)
+    lib.moe_layer(lay.x, lay.wg, lay.w13, lay.w2, 2, lib_cfg(lib, wl, lay), topk_ids_out=ids)
+    counts = np.bincount(ids.cpu().numpy().reshape(-1), minlength=8).tolist()
+    assert counts == [19, 11, 15, 15, 21, 15, 18, 14]
+
+
+@pytest.mark.parametrize("name,T,scale", [("mixtral", 96, 16), ("qwen3_skewed", 64, 8),
+                                          ("deepseek_decode", 16, 8), ("gptoss", 128, 8),
+                                          ("qwen3_balanced", 40, 8)])
+def test_layer_reduced(lib, name, T, scale):
+    base = S.WORKLOADS[name]
+    wl = base.scaled(T=T, H=base.H // scale // 64 * 64 or 64, I=base.I // scale // 64 * 64 or 64)
+    lay = S.make_layer(wl, device=DEV, seed=3)
+    _layer_vs_oracle(lib, wl, lay)
+
+
+def test_layer_hip_graph_replays(lib):
+    """The whole layer captured once in a HIP graph; replays with new activations (so the
+    routing changes) match eager runs."""
+    wl = S.WORKLOADS["qwen3_skewed"].scaled(T=96, H=256, I=128)
+    lay = S.make_layer(wl, device=DEV, seed=5)
+    cfg = lib_cfg(lib, wl, lay)
+    x = lay.x.clone()
+    ws = torch.empty(lib.moe_layer_workspace_size(wl.T, wl.H, wl.I, wl.E, wl.k, 1), dtype=torch.uint8,
+                     device=DEV)
+    out = torch.empty_like(x)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        lib.moe_layer(x, lay.wg, lay.w13, lay.w2, wl.k, cfg, out=out, ws=ws)
+    torch.cuda.current_stream().wait_stream(s)
+    _sync()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        lib.moe_layer(x, lay.wg, lay.w13, lay.w2, wl.k, cfg, out=out, ws=ws)
+    for seed in range(4):
+        xn = S.make_x(wl, device=DEV, seed=100 + seed)
+        x.copy_(xn)
+        graph.replay()
+        _sync()
+        got = out.clone()
+        ref = lib.moe_layer(xn, lay.wg, lay.w13, lay.w2, wl.k, cfg)
+        _sync()
+        assert torch.equal(got, ref)
