@@ -308,10 +308,7 @@ hipError_t run_bf16(const GemmArgs& g, hipStream_t s) {
 template <int MODE>
 hipError_t dispatch_bf16(const GemmArgs& g, int variant, hipStream_t s) {
   const int bm = g.block_m;
-  if (variant == 2) {                     // small-M tiles
-    if (bm % 32 == 0) return run_bf16<MODE, 32, 128, 1, 2>(g, s);
-    return hipErrorInvalidValue;
-  }
+  if (variant == 2) return MODE == 1 ? launch_decode_gemm1(g, s) : launch_decode_gemm2(g, s);
   if (bm % 128 == 0) return run_bf16<MODE, 128, 128, 2, 2>(g, s);
   if (bm % 64 == 0) return run_bf16<MODE, 64, 128, 1, 2>(g, s);
   if (bm % 32 == 0) return run_bf16<MODE, 32, 128, 1, 2>(g, s);

@@ -46,6 +46,10 @@ hipError_t launch_gemm2(const GemmArgs& g, bool bf16, int variant, hipStream_t s
 hipError_t launch_combine(const float* y, int T, int H, int k, bool bf16, void* out,
                           hipStream_t s);
 
+// small-M weight-streaming variant (decode.hip); any power-of-two block_m
+hipError_t launch_decode_gemm1(const GemmArgs& g, hipStream_t s);
+hipError_t launch_decode_gemm2(const GemmArgs& g, hipStream_t s);
+
 // which prefill tile height the MFMA kernels use for a given align block_m (0 = none)
 int prefill_tile_m(int block_m);
 

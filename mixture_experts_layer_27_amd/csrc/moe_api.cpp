@@ -109,7 +109,11 @@ int auto_variant(int T, int H, int I, int E, int k, moe_dtype dt) {
 
 int preferred_bm(int T, int H, int I, int E, int k, moe_dtype dt) {
   if (dt != MOE_BF16) return 16;
-  return auto_variant(T, H, I, E, k, dt) == MOE_VARIANT_DECODE ? 32 : 128;
+  return auto_variant(T, H, I, E, k, dt) == MOE_VARIANT_DECODE ? 64 : 128;
+}
+
+int resolve_variant(int variant, int T, int H, int I, int E, int k, moe_dtype dt) {
+  return variant == MOE_VARIANT_AUTO ? auto_variant(T, H, I, E, k, dt) : variant;
 }
 
 moe_status check_gemm_common(int T, int H, int I, int E, int k, int block_m, int dt,
@@ -124,16 +128,13 @@ moe_status check_gemm_common(int T, int H, int I, int E, int k, int block_m, int
   if (dt == MOE_BF16) {
     if (H % 64 || I % 64)
       return fail(MOE_ERR_UNSUPPORTED, "bf16 path needs H, I multiples of 64 (H=%d I=%d)", H, I);
-    if (moe::prefill_tile_m(block_m) == 0)
-      return fail(MOE_ERR_UNSUPPORTED, "bf16 expert GEMMs need block_m >= 32 (got %d)", block_m);
+    const int v = resolve_variant(variant, T, H, I, E, k, static_cast<moe_dtype>(dt));
+    if (v == MOE_VARIANT_PREFILL && moe::prefill_tile_m(block_m) == 0)
+      return fail(MOE_ERR_UNSUPPORTED, "bf16 prefill tiles need block_m >= 32 (got %d)", block_m);
   }
   if (static_cast<int64_t>(T) * k * std::max(H, I) >= (int64_t(1) << 40))
     return fail(MOE_ERR_UNSUPPORTED, "tensor too large");
   return MOE_OK;
-}
-
-int resolve_variant(int variant, int T, int H, int I, int E, int k, moe_dtype dt) {
-  return variant == MOE_VARIANT_AUTO ? auto_variant(T, H, I, E, k, dt) : variant;
 }
 
 moe::GemmArgs gemm_args(const void* A, const void* B, void* C, const float* topk_w,

@@ -113,7 +113,7 @@ def test_forward_validation(L):
         return f(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, a["T"], a["H"], a["I"], a["E"], a["k"],
                  a["bm"], a["dt"], a["var"], FAKE, FAKE, a["ws"], None)
 
-    assert call(bm=16) == UNSUPPORTED          # bf16 MFMA tiles need block_m >= 32
+    assert call(bm=16, var=1) == UNSUPPORTED   # bf16 MFMA prefill tiles need block_m >= 32
     assert call(bm=48) == INVALID
     assert call(I=96) == UNSUPPORTED           # bf16 needs I % 64 == 0
     assert call(dt=5) == INVALID
