@@ -35,6 +35,8 @@ def parse():
     ap.add_argument("--T", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=None)
+    ap.add_argument("--block-m", type=int, default=None,
+                    help="align block_m (the expert GEMM tile height follows it)")
     return ap.parse_args()
 
 
@@ -88,7 +90,7 @@ def main():
     T, H, I, E, k = wl.T, wl.H, wl.I, wl.E, wl.k
     dt = m.BF16 if wl.dtype == "bf16" else m.F32
     cfg = m.route_cfg(wl.mode, lay.offset, lay.bias, wl.n_group, wl.topk_group, wl.scaling)
-    bm = m.moe_preferred_block_m(T, H, I, E, k, dt)
+    bm = args.block_m or m.moe_preferred_block_m(T, H, I, E, k, dt)
     variant = m.moe_auto_variant(T, H, I, E, k, dt)
     cap = m.moe_align_capacity(T, k, E, bm)
     R = T * k
@@ -173,7 +175,7 @@ def main():
     if decode:
         rec["config"]["active_experts"] = n_act
     if not args.no_cpu_baseline:
-        st = args.cpu_sample_tokens or (min(T, 512) if not decode else T)
+        st = args.cpu_sample_tokens or T
         rec["cpu_baseline"] = cpu_baseline(wl, lay, st)
     print(json.dumps(rec), flush=True)
 

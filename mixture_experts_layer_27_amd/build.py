@@ -16,7 +16,7 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmoe_mi355x.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["align.hip", "route.hip", "gemm.hip", "decode.hip", "moe_api.cpp"]
+SOURCES = ["align.hip", "route.hip", "gemm.hip", "gemm_pipe.hip", "decode.hip", "moe_api.cpp"]
 HEADERS = ["common.hpp", "launch.hpp"]
 
 # -packed-fp32-ops is off: no v_pk_{add,mul,fma}_f32 anywhere in the device code.

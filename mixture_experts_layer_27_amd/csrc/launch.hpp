@@ -50,6 +50,10 @@ hipError_t launch_combine(const float* y, int T, int H, int k, bool bf16, void* 
 hipError_t launch_decode_gemm1(const GemmArgs& g, hipStream_t s);
 hipError_t launch_decode_gemm2(const GemmArgs& g, hipStream_t s);
 
+// pipelined large-tile prefill kernels (gemm_pipe.hip); tile_m 128 or 256
+hipError_t launch_pipe_gemm1(const GemmArgs& g, int tile_m, hipStream_t s);
+hipError_t launch_pipe_gemm2(const GemmArgs& g, int tile_m, hipStream_t s);
+
 // which prefill tile height the MFMA kernels use for a given align block_m (0 = none)
 int prefill_tile_m(int block_m);
 

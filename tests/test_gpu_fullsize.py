@@ -1,0 +1,120 @@
+"""Parity at the full workload sizes, in the launch configuration the benchmark times
+(moe_layer: route -> align -> expert GEMMs -> combine in one call).
+
+The oracle cannot run whole layers of this size in seconds, so it is checked on
+sampled tokens (routing, then the per-expert loop on those tokens alone; rows are
+independent), plus properties that hold at any size: every routed row appears once in
+the align table (bit-exact against the oracle's align on the oracle's own routing),
+counts sum to T*k, ids are distinct per token, weights sum to 1 (or the scale)."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import moe_oracle as O
+from synth import inputs as S
+from tests.gpu_util import (bf16_tol_check, compact_experts, f32_tol_check, lib_cfg,
+                            logit_error_bound, np64, route_kwargs)
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _check_layer(lib, wl, lay, n_sample, seed=0):
+    T, k, E = wl.T, wl.k, wl.E
+    print(f"[fullsize] {wl.name} T={T} H={wl.H} I={wl.I} E={E} k={k}", flush=True)
+    cfg = lib_cfg(lib, wl, lay)
+    ids = torch.empty(T, k, dtype=torch.int32, device=DEV)
+    w = torch.empty(T, k, dtype=torch.float32, device=DEV)
+    out = lib.moe_layer(lay.x, lay.wg, lay.w13, lay.w2, k, cfg, topk_ids_out=ids, topk_w_out=w)
+    torch.cuda.synchronize()
+    gids = ids.cpu().numpy()
+    gw = w.cpu().numpy().astype(np.float64)
+    # properties of the routing at full size
+    assert gids.min() >= 0 and gids.max() < E
+    assert all(len(set(r)) == k for r in gids.tolist())
+    np.testing.assert_allclose(gw.sum(1), wl.scaling if wl.mode == 2 else 1.0, rtol=1e-5)
+    assert np.bincount(gids.reshape(-1), minlength=E).sum() == T * k
+
+    # oracle routing of every token, GPU align on it vs the oracle's align (bit-exact)
+    x64 = np64(lay.x)
+    wg64 = np64(lay.wg)
+    logits = O.router_logits(x64, wg64)
+    kw = route_kwargs(wl, lay)
+    rid, rw = O.route(logits.astype(np.float32), k, wl.mode, **kw)
+    bm = lib.moe_preferred_block_m(T, wl.H, wl.I, E, k, 1 if wl.dtype == "bf16" else 0)
+    sorted_ids, expert_ids, ntpp, counts = lib.moe_align(torch.from_numpy(rid).to(DEV), E, bm)
+    cap = O.align_capacity(T, k, E, bm)
+    ref_al = O.align_argsort(rid, E, bm, cap)
+    assert int(ntpp.item()) == ref_al["total"]
+    assert np.array_equal(sorted_ids.cpu().numpy(), ref_al["sorted_ids"])
+    assert np.array_equal(expert_ids.cpu().numpy(), ref_al["expert_ids"])
+    assert np.array_equal(counts.cpu().numpy(), ref_al["counts"])
+    empty = int((ref_al["counts"] == 0).sum())
+
+    # routing agreement: identical wherever the selection margin exceeds the logit bound
+    margin = O.selection_margin(logits.astype(np.float32), k, wl.mode, kw["offset"], kw["bias"],
+                                wl.n_group, wl.topk_group)
+    bound = logit_error_bound(x64, wg64)
+    same = np.all(gids == rid, axis=1)
+    assert np.all(same | (margin <= 2 * bound))
+
+    # sampled outputs against the per-expert loop oracle
+    rng = np.random.default_rng(seed)
+    cand = np.nonzero(same)[0]
+    pick = np.unique(np.concatenate([cand[:1], cand[-1:], rng.choice(cand, min(n_sample, cand.size),
+                                                                     replace=False)]))
+    ids_c, w13c, w2c = compact_experts(rid[pick], lay.w13, lay.w2)
+    ref = O.moe_loop(x64[pick], w13c, w2c, ids_c, rw[pick], round_a=wl.dtype == "bf16")
+    got = np64(out[torch.from_numpy(pick).to(DEV)])
+    if wl.dtype == "bf16":
+        r, rel = bf16_tol_check(got, ref)
+    else:
+        r = f32_tol_check(got, ref)
+    print(f"[fullsize] {wl.name} T={T}: sampled {pick.size} tokens, err {r:.3e}, "
+          f"routing agreement {same.mean():.4f}, empty experts {empty}", flush=True)
+    return r
+
+
+def test_fullsize_tiny():
+    import mixture_experts_layer_27_amd as lib
+    wl = S.WORKLOADS["tiny"]
+    lay = S.make_layer(wl, device=DEV)
+    _check_layer(lib, wl, lay, 64)
+
+
+@pytest.mark.parametrize("name,n", [("mixtral", 12), ("qwen3_balanced", 6), ("qwen3_skewed", 6),
+                                    ("gptoss", 6)])
+def test_fullsize_prefill(name, n):
+    import mixture_experts_layer_27_amd as lib
+    wl = S.WORKLOADS[name]
+    lay = S.make_layer(wl, device=DEV)
+    _check_layer(lib, wl, lay, n)
+    del lay
+    torch.cuda.empty_cache()
+
+
+def test_fullsize_qwen3_skewed_small_T_empty_experts():
+    """The skewed router at decode batch sizes leaves many experts without rows: they get
+    no tiles (checked through the align table) and the layer still matches."""
+    import mixture_experts_layer_27_amd as lib
+    base = S.WORKLOADS["qwen3_skewed"]
+    lay = S.make_layer(base, device=DEV)
+    for T in (1, 16, 64):
+        wl = base.with_T(T)
+        sub = S.Layer(wl, lay.x[:T].contiguous(), lay.wg, lay.w13, lay.w2, lay.offset, lay.bias)
+        _check_layer(lib, wl, sub, 4)
+    del lay
+    torch.cuda.empty_cache()
+
+
+def test_fullsize_deepseek_decode():
+    import mixture_experts_layer_27_amd as lib
+    base = S.WORKLOADS["deepseek_decode"].with_T(256)
+    lay = S.make_layer(base, device=DEV)
+    for T, n in ((1, 1), (16, 3), (64, 3), (256, 3)):
+        wl = base.with_T(T)
+        x = S.make_x(wl, device=DEV, seed=77 + T)
+        sub = S.Layer(wl, x, lay.wg, lay.w13, lay.w2, lay.offset, lay.bias)
+        _check_layer(lib, wl, sub, n)
+    del lay
+    torch.cuda.empty_cache()
