@@ -35,6 +35,9 @@ def parse():
     ap.add_argument("--T", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=None)
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="run one plain device copy of this many MiB first (a known-size "
+                         "kernel that calibrates HBM byte counters)")
     ap.add_argument("--block-m", type=int, default=None,
                     help="align block_m (the expert GEMM tile height follows it)")
     return ap.parse_args()
@@ -133,17 +136,21 @@ def main():
                                        T, H, I, E, k, bm, dt, variant, P(y), sp), "gemm2")
         m.check(lib.moe_combine(P(y), T, H, k, dt, P(out), sp), "combine")
 
+    if args.copy_probe_mib:
+        src = torch.empty(args.copy_probe_mib << 19, dtype=torch.int16, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     for i in range(args.warmup):
         step(i, False)
     torch.cuda.synchronize()
-    active = []
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     t_start.record(stream)
     for i in range(args.steps):
         step(i, True)
-        if T <= 256:
-            active.append((counts > 0).sum())
     t_end.record(stream)
     torch.cuda.synchronize()
     ms = t_start.elapsed_time(t_end) / args.steps
@@ -152,7 +159,12 @@ def main():
     g1_flops = 2 * R * 2 * I * H
     decode = T <= 256
     if decode:
-        n_act = float(torch.stack(active).float().mean().item())
+        # active experts of each timed step, recomputed outside the timed region
+        act = []
+        for i in range(args.steps):
+            step(i, False)
+            act.append(int((counts > 0).sum().item()))
+        n_act = sum(act) / len(act)
         wbytes = n_act * 3 * H * I * 2
         value, unit = wbytes / (ms * 1e-3) / 1e9, "GB/s"
         g1_bytes = n_act * 2 * I * H * 2

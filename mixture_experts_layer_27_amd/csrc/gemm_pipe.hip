@@ -6,7 +6,7 @@
 //   at (wave base + 16 * lane), so the LDS swizzle is applied on the global side: lane i
 //   of an instruction fetches the logical chunk that belongs at physical slot i.
 // * NSTAGE-deep ring of BK=32 stages (64-byte LDS rows; chunk c of row m lives at
-//   c ^ ((m >> 1) & 3), conflict-free for both the 16-row DMA writes and the 32-row MFMA
+//   c ^ sw4(m), conflict-free for both the 16-row DMA writes and the 32-row MFMA
 //   operand reads).  Stage kt+NSTAGE-1 is issued while stage kt is consumed; one
 //   barrier per stage, preceded by an explicit vmcnt wait for this wave's own loads.
 // * v_mfma_f32_32x32x16_bf16, WM x WN waves, each holding (BM/WM) x (BN/WN) fp32
@@ -54,8 +54,13 @@ struct PCfg {
   static_assert(NSTAGE * STAGE <= 160 * 1024, "LDS");
 };
 
+// LDS swizzle of 64-byte rows: chunk c of row m sits at c ^ sw(m).  sw(m) =
+// ((m >> 1) ^ (m >> 3)) & 3 keeps the MFMA operand reads (rows m..m+31, one chunk)
+// conflict-free whether the LDS serves 8 lanes x 16 B per cycle over 32 banks or
+// 16 lanes x 16 B over 64 banks.
+__device__ __forceinline__ int sw4(int row) { return ((row >> 1) ^ (row >> 3)) & 3; }
 __device__ __forceinline__ int pswz(int row, int chunk) {
-  return row * 64 + ((chunk ^ ((row >> 1) & 3)) << 4);
+  return row * 64 + ((chunk ^ sw4(row)) << 4);
 }
 
 __device__ __forceinline__ int xcd_remap(int bid, int G) {
@@ -143,7 +148,7 @@ moe_gemm_pipe_kernel(PArgs p) {
     const int m = 16 * (w + C::NW * j) + lrow;
     const int r = srow[m];
     const int arow = r < p.R ? r / p.gather_div : 0;
-    a_src[j] = p.A + static_cast<int64_t>(arow) * K + ((pch ^ ((m >> 1) & 3)) << 3);
+    a_src[j] = p.A + static_cast<int64_t>(arow) * K + ((pch ^ sw4(m)) << 3);
   }
   const uint16_t* b_base = p.B + static_cast<int64_t>(e) * p.b_expert_stride;
   const uint16_t* b_src[C::LB];
@@ -161,7 +166,7 @@ moe_gemm_pipe_kernel(PArgs p) {
       if (col >= p.N) col = 0;
       brow = col;
     }
-    b_src[j] = b_base + static_cast<int64_t>(brow) * K + ((pch ^ ((n >> 1) & 3)) << 3);
+    b_src[j] = b_base + static_cast<int64_t>(brow) * K + ((pch ^ sw4(n)) << 3);
   }
 
   auto issue = [&](int kt) {
