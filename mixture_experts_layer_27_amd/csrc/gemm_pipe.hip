@@ -9,9 +9,12 @@
 //   c ^ sw4(m), conflict-free for both the 16-row DMA writes and the 32-row MFMA
 //   operand reads).  Stage kt+NSTAGE-1 is issued while stage kt is consumed; one
 //   barrier per stage, preceded by an explicit vmcnt wait for this wave's own loads.
-// * v_mfma_f32_32x32x16_bf16, WM x WN waves, each holding (BM/WM) x (BN/WN) fp32
-//   accumulators; GEMM1 B tiles interleave 32-row gate and up blocks so that SwiGLU
+// * v_mfma_f32_32x32x16_bf16, 2 x 2 waves (one per SIMD), each holding a (BM/2) x (BN/2)
+//   fp32 accumulator tile (up to 128 x 128 = 256 AGPRs); LDS fragments are double-buffered
+//   in registers so the MFMAs of one k16 step overlap the LDS reads of the next; GEMM1 B tiles interleave 32-row gate and up blocks so that SwiGLU
 //   runs in registers.
+#include <type_traits>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -35,38 +38,59 @@ struct PArgs {
   int mtiles, nblocks;
 };
 
-template <int MODE, int BM, int BN, int WM, int WN, int NSTAGE>
+template <int MODE, int BM, int BN, int WM, int WN, int BK_, int NSTAGE>
 struct PCfg {
   static constexpr int NW = WM * WN;
   static constexpr int NT = NW * kWave;
-  static constexpr int BK = 32;
-  static constexpr int ROWB = BK * 2;                 // 64 bytes per LDS row
+  static constexpr int BK = BK_;                      // K elements per stage (32 or 64)
+  static constexpr int ROWB = BK * 2;                 // bytes per LDS row
+  static constexpr int CPR = BK / 8;                  // 16-byte chunks per row
+  static constexpr int RPI = kWave / CPR;             // rows per DMA instruction (1 KB)
+  static constexpr int KS = BK / 16;                  // k16 MFMA steps per stage
   static constexpr int WTM = BM / WM, WTN = BN / WN;
   static constexpr int FM = WTM / 32, FN = WTN / 32;
-  static constexpr int LA = BM / 16 / NW;             // DMA instructions per wave per stage (A)
-  static constexpr int LB = BN / 16 / NW;             // (B)
+  static constexpr int LA = BM / RPI / NW;            // DMA instructions per wave per stage (A)
+  static constexpr int LB = BN / RPI / NW;            // (B)
   static constexpr int L = LA + LB;
   static constexpr int SA = BM * ROWB, SB = BN * ROWB;
   static constexpr int STAGE = SA + SB;
-  static_assert(BM % (16 * NW) == 0 && BN % (16 * NW) == 0, "DMA rows per wave");
+  static_assert(BK == 32 || BK == 64, "stage depth");
+  static_assert(BM % (RPI * NW) == 0 && BN % (RPI * NW) == 0, "DMA rows per wave");
   static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile");
   static_assert(MODE != 1 || WTN % 64 == 0, "GEMM1 wave tile holds gate/up pairs");
-  static_assert(NSTAGE * STAGE <= 160 * 1024, "LDS");
+  static_assert(NSTAGE >= 2 && NSTAGE * STAGE <= 160 * 1024 - BM * 4, "LDS");
 };
 
-// LDS swizzle of 64-byte rows: chunk c of row m sits at c ^ sw(m).  sw(m) =
-// ((m >> 1) ^ (m >> 3)) & 3 keeps the MFMA operand reads (rows m..m+31, one chunk)
-// conflict-free whether the LDS serves 8 lanes x 16 B per cycle over 32 banks or
-// 16 lanes x 16 B over 64 banks.
+// LDS swizzles (chunk c of row m lives at physical chunk c ^ sw(m)).  64-byte rows:
+// sw = ((m >> 1) ^ (m >> 3)) & 3; 128-byte rows: sw = (m >> 1) & 7.  Both spread the
+// MFMA operand reads (rows m..m+31 at one logical chunk) over all banks.
 __device__ __forceinline__ int sw4(int row) { return ((row >> 1) ^ (row >> 3)) & 3; }
+template <int BK>
+__device__ __forceinline__ int swz(int row) { return BK == 32 ? sw4(row) : ((row >> 1) & 7); }
+template <int BK>
 __device__ __forceinline__ int pswz(int row, int chunk) {
-  return row * 64 + ((chunk ^ sw4(row)) << 4);
+  return row * (BK * 2) + ((chunk ^ swz<BK>(row)) << 4);
 }
 
-__device__ __forceinline__ int xcd_remap(int bid, int G) {
-  const int xcd = bid & 7, j = bid >> 3, q = G >> 3, rmd = G & 7;
-  return (xcd < rmd ? xcd * (q + 1) : rmd * (q + 1) + (xcd - rmd) * q) + j;
+// Work-group -> (m-tile, n-block).  Work-groups are dealt round-robin over the 8 XCDs
+// (bid % 8) and each XCD runs its share in bid order, so bid = 8*j + xcd is the j-th
+// work-group of that XCD.  Slots are cut into groups of GM m-tiles x GN n-blocks
+// (grouped raster: m-groups outer, n-groups inner); group g runs on XCD g % 8, its
+// GM*GN tiles back to back.  The tiles running together on one XCD then share GM A
+// tiles (token rows) and GN B tiles (expert weight blocks) through that XCD's L2.
+// Returns false for the padding slots of the last groups.
+template <int GM, int GN>
+__device__ __forceinline__ bool grouped_slot(int bid, int mtiles, int nblocks, int& mt, int& nb) {
+  constexpr int GS = GM * GN;
+  const int xcd = bid & 7, j = bid >> 3;
+  const int g = (j / GS) * 8 + xcd, pos = j % GS;
+  const int ngroups_n = (nblocks + GN - 1) / GN;
+  const int gm = g / ngroups_n, gn = g % ngroups_n;
+  mt = gm * GM + pos % GM;
+  nb = gn * GN + pos / GM;
+  return mt < mtiles && nb < nblocks;
 }
+constexpr int kGroupM = 4, kGroupN = 8;
 
 // 16-byte global -> LDS DMA (global_load_lds_dwordx4): lane i writes lds_base + 16*i.
 // Issued from inline assembly so that the compiler's wait-count insertion does not treat
@@ -79,6 +103,14 @@ __device__ __forceinline__ void dma16(const void* gptr, const MOE_LDS void* lds_
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(gptr), "s"(l) : "memory", "m0");
 }
 
+// 4-byte global -> LDS DMA used as an L2 prefetch: each lane touches one cache line;
+// the bytes land in a scratch LDS slot nobody reads.
+__device__ __forceinline__ void prefetch_line(const void* gptr, const MOE_LDS void* lds_base) {
+  const uint32_t l = __builtin_amdgcn_readfirstlane(
+      static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds_base)));
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" : : "v"(gptr), "s"(l) : "memory", "m0");
+}
+
 // work-group barrier that also keeps the compiler from moving LDS accesses across it,
 // without the vmcnt(0) that __syncthreads() implies (the DMA ring stays in flight)
 __device__ __forceinline__ void barrier_keep_vm() {
@@ -87,10 +119,10 @@ __device__ __forceinline__ void barrier_keep_vm() {
   asm volatile("" ::: "memory");
 }
 
-// wait until at most n of this wave's vector-memory ops are outstanding (n <= 63)
-__device__ __forceinline__ void wait_vm(int n) {
-  // s_waitcnt immediate for gfx9: vmcnt[3:0] | expcnt(7)<<4 | lgkmcnt(15)<<8 | vmcnt[5:4]<<14
+// s_waitcnt immediate for gfx9: vmcnt[3:0] | expcnt(7)<<4 | lgkmcnt(15)<<8 | vmcnt[5:4]<<14
 #define MOE_VMW(N) __builtin_amdgcn_s_waitcnt(((N) & 15) | (7 << 4) | (15 << 8) | (((N) >> 4) << 14))
+// wait until at most n of this wave's vector-memory ops are outstanding
+__device__ __forceinline__ void wait_vm(int n) {
   switch (n) {
     case 0: MOE_VMW(0); break;
     case 1: MOE_VMW(1); break;
@@ -101,33 +133,33 @@ __device__ __forceinline__ void wait_vm(int n) {
     case 6: MOE_VMW(6); break;
     case 7: MOE_VMW(7); break;
     case 8: MOE_VMW(8); break;
-    case 9: MOE_VMW(9); break;
     case 10: MOE_VMW(10); break;
-    case 11: MOE_VMW(11); break;
     case 12: MOE_VMW(12); break;
-    case 13: MOE_VMW(13); break;
     case 14: MOE_VMW(14); break;
-    case 15: MOE_VMW(15); break;
     case 16: MOE_VMW(16); break;
-    case 18: MOE_VMW(18); break;
     case 20: MOE_VMW(20); break;
     case 24: MOE_VMW(24); break;
     case 32: MOE_VMW(32); break;
-    default: MOE_VMW(0); break;
+    default: MOE_VMW(0); break;      // conservative: everything done
   }
-#undef MOE_VMW
 }
 
-template <int MODE, int BM, int BN, int WM, int WN, int NSTAGE>
+template <int N>
+__device__ __forceinline__ void wait_vm_c() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+template <int MODE, int BM, int BN, int WM, int WN, int BK, int NSTAGE, int PFD>
 __global__ void __launch_bounds__(WM * WN * 64)
 moe_gemm_pipe_kernel(PArgs p) {
-  using C = PCfg<MODE, BM, BN, WM, WN, NSTAGE>;
+  using C = PCfg<MODE, BM, BN, WM, WN, BK, NSTAGE>;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[NSTAGE * C::STAGE];
   __shared__ int srow[BM];
+  __shared__ __attribute__((aligned(256))) uint8_t pf_sink[PFD > 0 ? 256 : 4];
 
-  const int G = p.mtiles * p.nblocks;
-  const int logical = xcd_remap(blockIdx.x, G);
-  const int mt = logical % p.mtiles, nb = logical / p.mtiles;
+  int mt, nb;
+  if (!grouped_slot<kGroupM, kGroupN>(blockIdx.x, p.mtiles, p.nblocks, mt, nb)) return;
   const int total = *p.ntpp;
   if (mt * BM >= total) return;
   const int e = p.expert_ids[(mt * BM) / p.block_m];
@@ -139,22 +171,22 @@ moe_gemm_pipe_kernel(PArgs p) {
   for (int m = tid; m < BM; m += C::NT) srow[m] = p.sorted_ids[static_cast<int64_t>(mt) * BM + m];
   __syncthreads();
 
-  // DMA sources: instruction j of wave w covers tile rows 16*(w + NW*j) .. +16;
-  // lane -> row (lane >> 2), physical chunk (lane & 3), logical chunk pc ^ ((row>>1)&3)
-  const int lrow = lane >> 2, pch = lane & 3;
+  // DMA sources: instruction j of wave w fills tile rows RPI*(w + NW*j) .. +RPI (1 KB);
+  // lane -> row lane / CPR, physical chunk lane % CPR, logical chunk pch ^ swz(row)
+  const int lrow = lane / C::CPR, pch = lane % C::CPR;
   const uint16_t* a_src[C::LA];
 #pragma unroll
   for (int j = 0; j < C::LA; ++j) {
-    const int m = 16 * (w + C::NW * j) + lrow;
+    const int m = C::RPI * (w + C::NW * j) + lrow;
     const int r = srow[m];
     const int arow = r < p.R ? r / p.gather_div : 0;
-    a_src[j] = p.A + static_cast<int64_t>(arow) * K + ((pch ^ sw4(m)) << 3);
+    a_src[j] = p.A + static_cast<int64_t>(arow) * K + ((pch ^ swz<BK>(m)) << 3);
   }
   const uint16_t* b_base = p.B + static_cast<int64_t>(e) * p.b_expert_stride;
   const uint16_t* b_src[C::LB];
 #pragma unroll
   for (int j = 0; j < C::LB; ++j) {
-    const int n = 16 * (w + C::NW * j) + lrow;
+    const int n = C::RPI * (w + C::NW * j) + lrow;
     int brow;
     if (MODE == 1) {
       const int blk = n >> 5;
@@ -166,8 +198,38 @@ moe_gemm_pipe_kernel(PArgs p) {
       if (col >= p.N) col = 0;
       brow = col;
     }
-    b_src[j] = b_base + static_cast<int64_t>(brow) * K + ((pch ^ sw4(n)) << 3);
+    b_src[j] = b_base + static_cast<int64_t>(brow) * K + ((pch ^ swz<BK>(n)) << 3);
   }
+
+  // L2 prefetch of stage kt+PFD: lane l of wave w touches A row and B row
+  // (BM/NW)*w + l (rows wrap when a wave has fewer than 64 of them)
+  const uint16_t* pfa = nullptr;
+  const uint16_t* pfb = nullptr;
+  if constexpr (PFD > 0) {
+    const int m = (BM / C::NW) * w + lane % (BM / C::NW);
+    const int r = srow[m];
+    pfa = p.A + static_cast<int64_t>(r < p.R ? r / p.gather_div : 0) * K;
+    const int n = (BN / C::NW) * w + lane % (BN / C::NW);
+    int brow;
+    if (MODE == 1) {
+      const int blk = n >> 5;
+      int col = nb * (BN / 2) + (blk >> 1) * 32 + (n & 31);
+      if (col >= p.N) col = 0;
+      brow = (blk & 1) ? p.I + col : col;
+    } else {
+      int col = nb * BN + n;
+      if (col >= p.N) col = 0;
+      brow = col;
+    }
+    pfb = b_base + static_cast<int64_t>(brow) * K;
+  }
+  auto prefetch = [&](int kt) {
+    if constexpr (PFD > 0) {
+      prefetch_line(pfa + kt * C::BK, (MOE_LDS void*)pf_sink);
+      prefetch_line(pfb + kt * C::BK, (MOE_LDS void*)pf_sink);
+    }
+  };
+  constexpr int P = PFD > 0 ? 2 : 0;      // prefetch instructions per wave per stage
 
   auto issue = [&](int kt) {
     uint8_t* st = smem + (kt % NSTAGE) * C::STAGE;
@@ -190,59 +252,143 @@ moe_gemm_pipe_kernel(PArgs p) {
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
   const int nk = K / C::BK;
-#pragma unroll
-  for (int s = 0; s < NSTAGE - 1; ++s)
-    if (s < nk) issue(s);
-
-  for (int kt = 0; kt < nk; ++kt) {
-    // stages issued after kt and still allowed in flight
-    const int ahead = min(NSTAGE - 2, nk - 1 - kt);
-    wait_vm(ahead * C::L);
-    barrier_keep_vm();
-    if (kt + NSTAGE - 1 < nk) issue(kt + NSTAGE - 1);
+  // Fragments of k16 step ks of stage kt: A rows of this wave's M slice, B rows of its
+  // N slice; lanes 0-31 take logical chunk 2*ks, lanes 32-63 chunk 2*ks+1 of each row.
+  auto read_frags = [&](int kt, int ks, bf16x8 (&fa)[C::FM], bf16x8 (&fb)[C::FN]) {
     const uint8_t* sa = smem + (kt % NSTAGE) * C::STAGE;
     const uint8_t* sb = sa + C::SA;
+    const int ch = 2 * ks + (lane >> 5);
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const int ch = 2 * ks + (lane >> 5);
-      bf16x8 af[C::FM], bfr[C::FN];
-#pragma unroll
-      for (int i = 0; i < C::FM; ++i) {
-        const int row = wm * C::WTM + i * 32 + (lane & 31);
-        af[i] = *reinterpret_cast<const bf16x8*>(sa + pswz(row, ch));
-      }
-#pragma unroll
-      for (int j = 0; j < C::FN; ++j) {
-        const int row = wn * C::WTN + j * 32 + (lane & 31);
-        bfr[j] = *reinterpret_cast<const bf16x8*>(sb + pswz(row, ch));
-      }
-#pragma unroll
-      for (int i = 0; i < C::FM; ++i)
-#pragma unroll
-        for (int j = 0; j < C::FN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+    for (int i = 0; i < C::FM; ++i) {
+      const int row = wm * C::WTM + i * 32 + (lane & 31);
+      fa[i] = *reinterpret_cast<const bf16x8*>(sa + pswz<BK>(row, ch));
     }
+#pragma unroll
+    for (int j = 0; j < C::FN; ++j) {
+      const int row = wn * C::WTN + j * 32 + (lane & 31);
+      fb[j] = *reinterpret_cast<const bf16x8*>(sb + pswz<BK>(row, ch));
+    }
+  };
+  auto mfma_all = [&](const bf16x8 (&fa)[C::FM], const bf16x8 (&fb)[C::FN]) {
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+      for (int j = 0; j < C::FN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+  };
+
+  // Fragments are double-buffered in registers: the reads of k16 step q+1 are issued
+  // before the MFMAs of step q.  sched_barrier(0) pins each group in place so the
+  // scheduler does not sink the reads next to their first use (exposing LDS latency).
+  bf16x8 fa[2][C::FM], fb[2][C::FN];
+  using T_ = std::true_type;
+  using F_ = std::false_type;
+
+  if constexpr (NSTAGE >= 3) {
+    // Ring of NSTAGE stages, NSTAGE-1 in flight.  The barrier that publishes stage kt+1
+    // sits before the last k16 step of stage kt, so the first fragments of kt+1 are read
+    // while that step computes.  The slot refilled after it, (kt+NSTAGE-1) % NSTAGE, held
+    // stage kt-1, which every wave finished reading before reaching the barrier.  The
+    // loop is split into branch-free phases so the compiler's LDS wait counts are exact:
+    //   steady (stage kt+NSTAGE-1 exists): wait for kt+1, refill the ring;
+    //   drain  (kt+1 exists, nothing left to issue): wait for kt+1 only;
+    //   last   (kt = nk-1): no barrier.
+    auto stage = [&](auto has_next, auto refill, int kt, int vm_allowed) {
+#pragma unroll
+      for (int ks = 0; ks < C::KS; ++ks) {
+        if (ks + 1 < C::KS) {
+          read_frags(kt, ks + 1, fa[(ks + 1) & 1], fb[(ks + 1) & 1]);
+        } else if constexpr (decltype(has_next)::value) {
+          // issued so far: stages 0 .. kt+NSTAGE-2; stage kt+1 must be complete, so
+          // only the NSTAGE-3 stages after it may still be in flight
+          if constexpr (decltype(refill)::value) wait_vm_c<(NSTAGE - 3) * C::L>();
+          else wait_vm(vm_allowed);
+          barrier_keep_vm();
+          if constexpr (decltype(refill)::value) issue(kt + NSTAGE - 1);
+          read_frags(kt + 1, 0, fa[0], fb[0]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        mfma_all(fa[ks & 1], fb[ks & 1]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+#pragma unroll
+    for (int s = 0; s < NSTAGE - 1; ++s)
+      if (s < nk) issue(s);
+    wait_vm(min(NSTAGE - 2, nk - 1) * C::L);
+    barrier_keep_vm();
+    read_frags(0, 0, fa[0], fb[0]);
+    int kt = 0;
+    for (; kt + NSTAGE <= nk; ++kt) stage(T_{}, T_{}, kt, 0);
+    for (; kt + 1 < nk; ++kt) stage(T_{}, F_{}, kt, (min(kt + NSTAGE - 2, nk - 1) - (kt + 1)) * C::L);
+    stage(F_{}, F_{}, kt, 0);
+  } else {
+    // Two stages: stage kt+1 is loaded while stage kt computes.  The barrier at the
+    // start of each stage both publishes it (after this wave's own wait) and frees the
+    // other slot, which held stage kt-1.
+    // With PFD > 0, stage kt+1+PFD is also touched into L2 right after stage kt+1's DMA,
+    // so the DMA of each stage finds its lines resident; the wait below lets those
+    // prefetches stay in flight.
+    auto stage = [&](auto refill, int kt, int vm_allowed) {
+      wait_vm(vm_allowed);
+      barrier_keep_vm();
+      if constexpr (decltype(refill)::value) {
+        issue(kt + 1);
+        if (kt + 1 + PFD < nk) prefetch(kt + 1 + PFD);
+      }
+      read_frags(kt, 0, fa[0], fb[0]);
+#pragma unroll
+      for (int ks = 0; ks < C::KS; ++ks) {
+        if (ks + 1 < C::KS) read_frags(kt, ks + 1, fa[(ks + 1) & 1], fb[(ks + 1) & 1]);
+        __builtin_amdgcn_sched_barrier(0);
+        mfma_all(fa[ks & 1], fb[ks & 1]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+    issue(0);
+    int npf = 0;
+    for (int d = 1; d <= PFD && d < nk; ++d, ++npf) prefetch(d);
+    int kt = 0;
+    // stage 0 waits behind the warm-up prefetches; stage kt >= 1 behind PF(kt+PFD) only
+    for (; kt + 1 < nk; ++kt) {
+      stage(T_{}, kt, kt == 0 ? npf * P : (kt + PFD < nk ? P : 0));
+    }
+    stage(F_{}, kt, kt == 0 ? npf * P : (kt + PFD < nk ? P : 0));
   }
 
   // ---- epilogue.  D layout (32x32): lane holds column (lane & 31),
   //      rows 8*(v/4) + 4*(lane/32) + (v%4), v = 0..15.
   if (MODE == 1) {
-    uint16_t* out = static_cast<uint16_t*>(p.C);
+    // SwiGLU in registers, bf16 tile staged in LDS (the ring is free once every wave is
+    // past its last stage), then written as 16-byte row chunks: one 256-byte row
+    // segment per 16 lanes instead of 2-byte scattered stores.
+    constexpr int NA = BN / 2;                          // a-columns of the tile
+    constexpr int ROWS = NA * 2 + 16;                   // padded row stride (bytes)
+    static_assert(BM * ROWS <= NSTAGE * C::STAGE, "epilogue tile fits the ring");
+    __syncthreads();
 #pragma unroll
     for (int i = 0; i < C::FM; ++i) {
 #pragma unroll
       for (int q = 0; q < C::FN / 2; ++q) {
-        const int col = nb * (BN / 2) + (wn * C::WTN) / 2 + q * 32 + (lane & 31);
-        if (col >= p.N) continue;
+        const int lc = (wn * C::WTN) / 2 + q * 32 + (lane & 31);
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const int m = wm * C::WTM + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-          const int r = srow[m];
-          if (r >= p.R) continue;
           const float g = acc[i][2 * q][v], u = acc[i][2 * q + 1][v];
-          out[static_cast<int64_t>(r) * p.N + col] = f32_to_bf16(g / (1.f + __expf(-g)) * u);
+          *reinterpret_cast<uint16_t*>(smem + m * ROWS + lc * 2) = f32_to_bf16(g / (1.f + __expf(-g)) * u);
         }
       }
+    }
+    __syncthreads();
+    uint16_t* out = static_cast<uint16_t*>(p.C);
+    constexpr int CPR = NA / 8;                          // 16-byte chunks per row
+    for (int idx = tid; idx < BM * CPR; idx += C::NT) {
+      const int m = idx / CPR, c = idx % CPR;
+      const int r = srow[m];
+      const int col = nb * NA + c * 8;
+      if (r >= p.R || col >= p.N) continue;
+      *reinterpret_cast<u32x4*>(out + static_cast<int64_t>(r) * p.N + col) =
+          *reinterpret_cast<const u32x4*>(smem + m * ROWS + c * 16);
     }
   } else {
     float* out = static_cast<float*>(p.C);
@@ -264,7 +410,7 @@ moe_gemm_pipe_kernel(PArgs p) {
   }
 }
 
-template <int MODE, int BM, int BN, int WM, int WN, int NSTAGE>
+template <int MODE, int BM, int BN, int WM, int WN, int BK, int NSTAGE, int PFD>
 hipError_t run_pipe(const GemmArgs& g, hipStream_t s) {
   PArgs p{};
   const bool g1 = MODE == 1;
@@ -285,9 +431,12 @@ hipError_t run_pipe(const GemmArgs& g, hipStream_t s) {
   p.mtiles = static_cast<int>(g.cap / BM);
   const int ncols = g1 ? BN / 2 : BN;
   p.nblocks = (p.N + ncols - 1) / ncols;
-  const int64_t G = static_cast<int64_t>(p.mtiles) * p.nblocks;
+  // every (group, position) slot: ceil over groups of kGroupM x kGroupN, 8 XCDs at a time
+  const int64_t groups = static_cast<int64_t>((p.mtiles + kGroupM - 1) / kGroupM) *
+                         ((p.nblocks + kGroupN - 1) / kGroupN);
+  const int64_t G = (groups + 7) / 8 * 8 * kGroupM * kGroupN;
   if (G == 0) return hipSuccess;
-  hipLaunchKernelGGL((moe_gemm_pipe_kernel<MODE, BM, BN, WM, WN, NSTAGE>),
+  hipLaunchKernelGGL((moe_gemm_pipe_kernel<MODE, BM, BN, WM, WN, BK, NSTAGE, PFD>),
                      dim3(static_cast<unsigned>(G)), dim3(WM * WN * 64), 0, s, p);
   return hipGetLastError();
 }
@@ -297,14 +446,14 @@ hipError_t run_pipe(const GemmArgs& g, hipStream_t s) {
 // Tile choice for the pipelined prefill kernels; returns hipErrorInvalidValue when
 // block_m does not allow a 128/256-row tile (callers fall back to gemm.hip's tiles).
 hipError_t launch_pipe_gemm1(const GemmArgs& g, int tile_m, hipStream_t s) {
-  if (tile_m == 256) return run_pipe<1, 256, 256, 2, 4, 4>(g, s);
-  if (tile_m == 128) return run_pipe<1, 128, 256, 2, 4, 4>(g, s);
+  if (tile_m == 256) return run_pipe<1, 256, 256, 2, 2, 64, 2, 0>(g, s);
+  if (tile_m == 128) return run_pipe<1, 128, 256, 2, 2, 64, 3, 0>(g, s);
   return hipErrorInvalidValue;
 }
 
 hipError_t launch_pipe_gemm2(const GemmArgs& g, int tile_m, hipStream_t s) {
-  if (tile_m == 256) return run_pipe<2, 256, 256, 2, 4, 4>(g, s);
-  if (tile_m == 128) return run_pipe<2, 128, 256, 2, 4, 4>(g, s);
+  if (tile_m == 256) return run_pipe<2, 256, 256, 2, 2, 64, 2, 2>(g, s);
+  if (tile_m == 128) return run_pipe<2, 128, 256, 2, 2, 64, 3, 0>(g, s);
   return hipErrorInvalidValue;
 }
 

@@ -109,7 +109,11 @@ int auto_variant(int T, int H, int I, int E, int k, moe_dtype dt) {
 
 int preferred_bm(int T, int H, int I, int E, int k, moe_dtype dt) {
   if (dt != MOE_BF16) return 16;
-  return auto_variant(T, H, I, E, k, dt) == MOE_VARIANT_DECODE ? 64 : 128;
+  if (auto_variant(T, H, I, E, k, dt) == MOE_VARIANT_DECODE) return 64;
+  // 256-row MFMA tiles once the average expert fills several of them (the padding of
+  // each expert's last tile is then a small fraction); 128-row tiles otherwise
+  const int64_t avg = static_cast<int64_t>(T) * k / E;
+  return avg >= 1024 ? 256 : 128;
 }
 
 int resolve_variant(int variant, int T, int H, int I, int E, int k, moe_dtype dt) {
