@@ -43,6 +43,33 @@ def parse():
     return ap.parse_args()
 
 
+KERNEL_SOURCES = ("gemm_pipe.hip", "decode.hip", "gemm.hip", "common.hpp")
+
+
+def kernel_digest() -> str:
+    """sha256 over the sources of the expert-GEMM kernels (ties counter data to them)."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "mixture_experts_layer_27_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(key: str):
+    """HBM bytes per GEMM1 launch from the committed FETCH_SIZE/WRITE_SIZE passes
+    (profiles/traffic.json), or None when they were taken on different kernel sources."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as fh:
+            rec = json.load(fh).get(key)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("kernel_sha256") != kernel_digest():
+        return None
+    return rec["traffic_bytes_per_launch"]
+
+
 def cpu_baseline(wl, lay, sample_T):
     """Time the CPU oracle (routing + per-expert loop) on the first sample_T tokens."""
     import numpy as np
@@ -169,13 +196,15 @@ def main():
         value, unit = wbytes / (ms * 1e-3) / 1e9, "GB/s"
         g1_bytes = n_act * 2 * I * H * 2
         roof = {"bound": "hbm", "achieved": g1_bytes / (g1_ms * 1e-3) / 1e9, "peak": PEAK_HBM_GBS,
-                "unit": "GB/s", "traffic": None}
+                "unit": "GB/s", "traffic": measured_traffic(f"{wl.name}_T{T}")}
     else:
         value, unit = flops / (ms * 1e-3) / 1e12, "TFLOPS"
         roof = {"bound": "mfma", "achieved": g1_flops / (g1_ms * 1e-3) / 1e12,
-                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "traffic": None}
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "traffic": measured_traffic(f"{wl.name}_T{T}")}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["kernel"] = "moe_gemm_bf16_kernel<GEMM1+SwiGLU>"
+    roof["kernel"] = ("moe_decode_kernel<GEMM1+SwiGLU>" if variant == m.VARIANT_DECODE
+                      else "moe_gemm_pipe_kernel<GEMM1+SwiGLU>")
     roof["kernel_ms"] = g1_ms
     rec = {"metric": METRIC, "value": value, "unit": unit, "n_gpus": 1, "steps": args.steps,
            "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",

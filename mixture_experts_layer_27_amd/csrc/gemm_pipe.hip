@@ -36,6 +36,7 @@ struct PArgs {
   int64_t b_expert_stride;
   int block_m;
   int mtiles, nblocks;
+  int n_outer;             // raster order of the tile groups (see grouped_slot)
 };
 
 template <int MODE, int BM, int BN, int WM, int WN, int BK_, int NSTAGE>
@@ -74,18 +75,30 @@ __device__ __forceinline__ int pswz(int row, int chunk) {
 
 // Work-group -> (m-tile, n-block).  Work-groups are dealt round-robin over the 8 XCDs
 // (bid % 8) and each XCD runs its share in bid order, so bid = 8*j + xcd is the j-th
-// work-group of that XCD.  Slots are cut into groups of GM m-tiles x GN n-blocks
-// (grouped raster: m-groups outer, n-groups inner); group g runs on XCD g % 8, its
-// GM*GN tiles back to back.  The tiles running together on one XCD then share GM A
-// tiles (token rows) and GN B tiles (expert weight blocks) through that XCD's L2.
-// Returns false for the padding slots of the last groups.
+// work-group of that XCD.  Slots are cut into groups of GM m-tiles x GN n-blocks; group
+// g runs on XCD g % 8, its GM*GN tiles back to back, so the tiles running together on
+// one XCD share GM A tiles (token rows) and GN B tiles (expert weight blocks) through
+// that XCD's L2.  Group order: with n_outer, n-groups outer and m-groups inner (the
+// groups in flight at once on the 8 XCDs cover many m-tiles of the same weight
+// columns); otherwise m-groups outer (an XCD's consecutive groups reuse the same token
+// rows while the weight columns advance).  The host picks n_outer when there are more
+// m-tiles than n-blocks.  Returns false for the padding slots of the last groups.
 template <int GM, int GN>
-__device__ __forceinline__ bool grouped_slot(int bid, int mtiles, int nblocks, int& mt, int& nb) {
+__device__ __forceinline__ bool grouped_slot(int bid, int mtiles, int nblocks, bool n_outer,
+                                             int& mt, int& nb) {
   constexpr int GS = GM * GN;
   const int xcd = bid & 7, j = bid >> 3;
   const int g = (j / GS) * 8 + xcd, pos = j % GS;
-  const int ngroups_n = (nblocks + GN - 1) / GN;
-  const int gm = g / ngroups_n, gn = g % ngroups_n;
+  int gm, gn;
+  if (n_outer) {
+    const int ngroups_m = (mtiles + GM - 1) / GM;
+    gn = g / ngroups_m;
+    gm = g % ngroups_m;
+  } else {
+    const int ngroups_n = (nblocks + GN - 1) / GN;
+    gm = g / ngroups_n;
+    gn = g % ngroups_n;
+  }
   mt = gm * GM + pos % GM;
   nb = gn * GN + pos / GM;
   return mt < mtiles && nb < nblocks;
@@ -159,7 +172,7 @@ moe_gemm_pipe_kernel(PArgs p) {
   __shared__ __attribute__((aligned(256))) uint8_t pf_sink[PFD > 0 ? 256 : 4];
 
   int mt, nb;
-  if (!grouped_slot<kGroupM, kGroupN>(blockIdx.x, p.mtiles, p.nblocks, mt, nb)) return;
+  if (!grouped_slot<kGroupM, kGroupN>(blockIdx.x, p.mtiles, p.nblocks, p.n_outer, mt, nb)) return;
   const int total = *p.ntpp;
   if (mt * BM >= total) return;
   const int e = p.expert_ids[(mt * BM) / p.block_m];
@@ -431,6 +444,7 @@ hipError_t run_pipe(const GemmArgs& g, hipStream_t s) {
   p.mtiles = static_cast<int>(g.cap / BM);
   const int ncols = g1 ? BN / 2 : BN;
   p.nblocks = (p.N + ncols - 1) / ncols;
+  p.n_outer = p.mtiles > p.nblocks;
   // every (group, position) slot: ceil over groups of kGroupM x kGroupN, 8 XCDs at a time
   const int64_t groups = static_cast<int64_t>((p.mtiles + kGroupM - 1) / kGroupM) *
                          ((p.nblocks + kGroupN - 1) / kGroupN);
