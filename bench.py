@@ -34,6 +34,8 @@ def parse():
     ap.add_argument("--workload", default="mixtral")
     ap.add_argument("--T", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--eager", action="store_true",
+                    help="time eager launches instead of HIP-graph replays of the step")
     ap.add_argument("--cpu-sample-tokens", type=int, default=None)
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB first (a known-size "
@@ -143,26 +145,25 @@ def main():
     import ctypes
     P = lambda t: ctypes.c_void_p(t.data_ptr())
     stream = torch.cuda.current_stream()
-    sp = ctypes.c_void_p(stream.cuda_stream)
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(args.steps)]
 
-    def step(i, timed):
+    def launch(i, sp, g1_events=None):
+        """One step: route -> align -> GEMM1+SwiGLU -> GEMM2 x weight -> combine on stream sp."""
         x = xs[i % nx]
         m.check(lib.moe_route(P(x), P(lay.wg), T, H, E, k, dt, ctypes.byref(cfg), P(ids), P(w),
                               P(logits), None, 0, sp), "route")
         m.check(lib.moe_align(P(ids), T, k, E, bm, P(sorted_ids), P(expert_ids), P(ntpp), P(counts),
                               P(aws), aws.numel(), sp), "align")
-        if timed:
-            ev[i][0].record(stream)
+        if g1_events:
+            g1_events[0].record(torch.cuda.current_stream())
         m.check(lib.moe_gemm1_swiglu(P(x), P(lay.w13), P(sorted_ids), P(expert_ids), P(ntpp), T, H, I,
                                      E, k, bm, dt, variant, P(a), sp), "gemm1")
-        if timed:
-            ev[i][1].record(stream)
+        if g1_events:
+            g1_events[1].record(torch.cuda.current_stream())
         m.check(lib.moe_gemm2_weighted(P(a), P(lay.w2), P(w), P(sorted_ids), P(expert_ids), P(ntpp),
                                        T, H, I, E, k, bm, dt, variant, P(y), sp), "gemm2")
         m.check(lib.moe_combine(P(y), T, H, k, dt, P(out), sp), "combine")
 
+    cur_sp = lambda: ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
     if args.copy_probe_mib:
         src = torch.empty(args.copy_probe_mib << 19, dtype=torch.int16, device=dev).fill_(1)
         dst = torch.empty_like(src)
@@ -171,17 +172,45 @@ def main():
         torch.cuda.synchronize()
         del src, dst
     for i in range(args.warmup):
-        step(i, False)
+        launch(i, cur_sp())
     torch.cuda.synchronize()
+
+    # the step as HIP graphs (one per activation batch): the library only enqueues work,
+    # so a whole layer is capturable and replays without host launch gaps
+    graphs = []
+    if not args.eager:
+        cs = torch.cuda.Stream()
+        cs.wait_stream(stream)
+        for i in range(nx):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=cs):
+                launch(i, cur_sp())
+            graphs.append(g)
+        torch.cuda.synchronize()
+        for i in range(args.warmup):
+            graphs[i % nx].replay()
+        torch.cuda.synchronize()
+
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
     t_start.record(stream)
     for i in range(args.steps):
-        step(i, True)
+        if graphs:
+            graphs[i % nx].replay()
+        else:
+            launch(i, cur_sp())
     t_end.record(stream)
     torch.cuda.synchronize()
     ms = t_start.elapsed_time(t_end) / args.steps
-    g1_ms = sum(s.elapsed_time(e) for s, e in ev) / args.steps
+
+    # GEMM1 launch duration: HIP events bracketing the kernel on its own stream, K eager steps
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    for i in range(args.steps):
+        launch(i, cur_sp(), ev[i])
+    torch.cuda.synchronize()
+    g1_ms = sum(s_.elapsed_time(e_) for s_, e_ in ev) / args.steps
     flops = wl.flops
     g1_flops = 2 * R * 2 * I * H
     decode = T <= 256
@@ -189,7 +218,7 @@ def main():
         # active experts of each timed step, recomputed outside the timed region
         act = []
         for i in range(args.steps):
-            step(i, False)
+            launch(i, cur_sp())
             act.append(int((counts > 0).sum().item()))
         n_act = sum(act) / len(act)
         wbytes = n_act * 3 * H * I * 2
@@ -211,6 +240,7 @@ def main():
            "vs_baseline": None, "dtype": wl.dtype, "data": "synthetic",
            "config": {"workload": f"{wl.name}", "T": T, "H": H, "I": I, "E": E, "k": k,
                       "route_mode": wl.mode, "block_m": bm, "variant": variant,
+                      "timing": "eager" if args.eager else "hip-graph replay",
                       "parallelism": "single-gpu"},
            "roofline": roof}
     if decode:

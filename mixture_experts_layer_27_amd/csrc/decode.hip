@@ -6,9 +6,9 @@
 // Operand swap: the weights are the MFMA "A" side (16 weight rows per v_mfma_f32_16x16x32_bf16)
 // and the few routed token rows are the "B" side (16 tokens per MFMA), so a tile with a
 // single routed row still feeds whole MFMAs from the weight stream.  Weights go straight
-// from HBM to registers: lane l owns weight row (l & 15) and 16*CH contiguous bytes of the
-// current K step, so four lanes read 64*CH contiguous bytes of each row; the same
-// k-permutation is used for the token rows, which leaves the dot products unchanged.
+// from HBM to registers: lane l owns weight row (l & 15); in each K step of 32*CH elements
+// the four lanes of a row read 64 contiguous bytes per load instruction (16 rows per
+// instruction), in the natural MFMA k order, and the token rows are read the same way.
 //
 // Work item = (align tile of block_m <= 64 rows, block of weight rows).  GEMM1 items hold
 // 16 gate rows + the 16 matching up rows (16 output columns of a, SwiGLU in the epilogue);
@@ -64,8 +64,11 @@ moe_decode_kernel(DArgs p) {
     if (MODE == 1) { wrow0 = blk * 16 + row16; wrow1 = p.I + blk * 16 + row16; }
     else { wrow0 = blk * 32 + row16; wrow1 = blk * 32 + 16 + row16; }
     const uint16_t* wb = p.A + static_cast<int64_t>(e) * p.a_expert_stride;
-    const uint16_t* w0 = wb + static_cast<int64_t>(wrow0) * K + g * 8 * CH;
-    const uint16_t* w1 = wb + static_cast<int64_t>(wrow1) * K + g * 8 * CH;
+    // step layout: MFMA substep c (k32 slice c of the step) takes, in lane group g, the
+    // 8 elements at c*32 + g*8, so one load instruction reads 64 contiguous bytes of each
+    // of the 16 rows (four lanes per row)
+    const uint16_t* w0 = wb + static_cast<int64_t>(wrow0) * K + g * 8;
+    const uint16_t* w1 = wb + static_cast<int64_t>(wrow1) * K + g * 8;
 
     for (int m0 = 0; m0 < p.block_m; m0 += 16 * kMaxTG) {
       // rows of this pass (up to 64) and how many 16-row groups hold a routed row
@@ -87,7 +90,7 @@ moe_decode_kernel(DArgs p) {
       for (int q = 0; q < kMaxTG; ++q) {
         const int r = rows_s[q * 16 + row16];
         const int xrow = r < p.R ? r / p.gather_div : 0;
-        xr[q] = p.X + static_cast<int64_t>(xrow) * K + g * 8 * CH;
+        xr[q] = p.X + static_cast<int64_t>(xrow) * K + g * 8;
       }
       f32x4 acc[kMaxTG][2];
 #pragma unroll
@@ -100,15 +103,15 @@ moe_decode_kernel(DArgs p) {
         bf16x8 a0[CH], a1[CH];
 #pragma unroll
         for (int c = 0; c < CH; ++c) {
-          a0[c] = __builtin_nontemporal_load(reinterpret_cast<const bf16x8*>(w0 + k0) + c);
-          a1[c] = __builtin_nontemporal_load(reinterpret_cast<const bf16x8*>(w1 + k0) + c);
+          a0[c] = __builtin_nontemporal_load(reinterpret_cast<const bf16x8*>(w0 + k0 + c * 32));
+          a1[c] = __builtin_nontemporal_load(reinterpret_cast<const bf16x8*>(w1 + k0 + c * 32));
         }
 #pragma unroll
         for (int q = 0; q < kMaxTG; ++q) {
           if (q < ntg) {
             bf16x8 b[CH];
 #pragma unroll
-            for (int c = 0; c < CH; ++c) b[c] = reinterpret_cast<const bf16x8*>(xr[q] + k0)[c];
+            for (int c = 0; c < CH; ++c) b[c] = *reinterpret_cast<const bf16x8*>(xr[q] + k0 + c * 32);
 #pragma unroll
             for (int c = 0; c < CH; ++c) {
               acc[q][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0[c], b[c], acc[q][0], 0, 0, 0);
