@@ -1,8 +1,9 @@
 """Benchmark of the fused top-k MoE SwiGLU layer on one MI355X.
 
-One step = route -> align -> GEMM1+SwiGLU -> GEMM2 x weight -> combine over one batch of
-seeded synthetic input already resident in HBM, each stage through the C ABI on the
-current HIP stream.  Prints ONE JSON line.
+One step = one moe_layer call through the C ABI (route -> align -> GEMM1+SwiGLU -> GEMM2 x
+weight -> combine) over one batch of seeded synthetic input already resident in HBM, on
+the current HIP stream.  Prints ONE JSON line.  The GEMM1 launch duration for the
+roofline is taken in separate eager steps that call the stages one by one.
 
   python bench.py [--steps K] [--warmup W] [--workload mixtral|deepseek_decode|...] [--T n]
 
@@ -41,7 +42,8 @@ def parse():
                     help="run one plain device copy of this many MiB first (a known-size "
                          "kernel that calibrates HBM byte counters)")
     ap.add_argument("--block-m", type=int, default=None,
-                    help="align block_m (the expert GEMM tile height follows it)")
+                    help="align block_m (the expert GEMM tile height follows it); times the "
+                         "stage-by-stage calls instead of moe_layer")
     return ap.parse_args()
 
 
@@ -132,12 +134,13 @@ def main():
     i32 = dict(dtype=torch.int32, device=dev)
     ids = torch.empty(T, k, **i32)
     w = torch.empty(T, k, dtype=torch.float32, device=dev)
-    logits = torch.empty(T, E, dtype=torch.float32, device=dev)
+    rws = torch.empty(max(16, m.moe_route_workspace_size(T, H, E, dt)), dtype=torch.uint8, device=dev)
     sorted_ids = torch.empty(cap, **i32)
     expert_ids = torch.empty(cap // bm, **i32)
     ntpp = torch.empty(1, **i32)
     counts = torch.empty(E, **i32)
     aws = torch.empty(max(16, m.moe_align_workspace_size(T, k, E, bm)), dtype=torch.uint8, device=dev)
+    lws = torch.empty(m.moe_layer_workspace_size(T, H, I, E, k, dt), dtype=torch.uint8, device=dev)
     a = torch.empty(R, I, dtype=lay.x.dtype, device=dev)
     y = torch.empty(R, H, dtype=torch.float32, device=dev)
     out = torch.empty(T, H, dtype=lay.x.dtype, device=dev)
@@ -145,12 +148,13 @@ def main():
     import ctypes
     P = lambda t: ctypes.c_void_p(t.data_ptr())
     stream = torch.cuda.current_stream()
+    staged = args.block_m is not None
 
-    def launch(i, sp, g1_events=None):
-        """One step: route -> align -> GEMM1+SwiGLU -> GEMM2 x weight -> combine on stream sp."""
+    def launch_staged(i, sp, g1_events=None):
+        """route -> align -> GEMM1+SwiGLU -> GEMM2 x weight -> combine, one call each."""
         x = xs[i % nx]
         m.check(lib.moe_route(P(x), P(lay.wg), T, H, E, k, dt, ctypes.byref(cfg), P(ids), P(w),
-                              P(logits), None, 0, sp), "route")
+                              None, P(rws), rws.numel(), sp), "route")
         m.check(lib.moe_align(P(ids), T, k, E, bm, P(sorted_ids), P(expert_ids), P(ntpp), P(counts),
                               P(aws), aws.numel(), sp), "align")
         if g1_events:
@@ -162,6 +166,14 @@ def main():
         m.check(lib.moe_gemm2_weighted(P(a), P(lay.w2), P(w), P(sorted_ids), P(expert_ids), P(ntpp),
                                        T, H, I, E, k, bm, dt, variant, P(y), sp), "gemm2")
         m.check(lib.moe_combine(P(y), T, H, k, dt, P(out), sp), "combine")
+
+    def launch(i, sp):
+        """One step: the whole layer in one library call."""
+        if staged:
+            return launch_staged(i, sp)
+        x = xs[i % nx]
+        m.check(lib.moe_layer(P(x), P(lay.wg), P(lay.w13), P(lay.w2), ctypes.byref(cfg), T, H, I, E,
+                              k, dt, P(out), P(ids), P(w), P(lws), lws.numel(), sp), "layer")
 
     cur_sp = lambda: ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
     if args.copy_probe_mib:
@@ -208,7 +220,7 @@ def main():
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(args.steps)]
     for i in range(args.steps):
-        launch(i, cur_sp(), ev[i])
+        launch_staged(i, cur_sp(), ev[i])
     torch.cuda.synchronize()
     g1_ms = sum(s_.elapsed_time(e_) for s_, e_ in ev) / args.steps
     flops = wl.flops
@@ -219,7 +231,7 @@ def main():
         act = []
         for i in range(args.steps):
             launch(i, cur_sp())
-            act.append(int((counts > 0).sum().item()))
+            act.append(int(torch.unique(ids).numel()))
         n_act = sum(act) / len(act)
         wbytes = n_act * 3 * H * I * 2
         value, unit = wbytes / (ms * 1e-3) / 1e9, "GB/s"
@@ -241,6 +253,7 @@ def main():
            "config": {"workload": f"{wl.name}", "T": T, "H": H, "I": I, "E": E, "k": k,
                       "route_mode": wl.mode, "block_m": bm, "variant": variant,
                       "timing": "eager" if args.eager else "hip-graph replay",
+                      "step": "stage-by-stage calls" if staged else "moe_layer",
                       "parallelism": "single-gpu"},
            "roofline": roof}
     if decode:

@@ -89,15 +89,17 @@ typedef struct {
  *            selection score, ties to the lower expert index; groups likewise).
  *   topk_w   [T,k] fp32: router weights of those slots.
  *   logits_out [T,E] fp32 or NULL: the raw x . Wg^T (before logit_offset).
- *   ws: scratch of moe_route_workspace_size(T,E) bytes (may be 0 when logits_out
- *       is given).
+ *   ws: scratch of at least moe_route_workspace_size(T,H,E,dt) bytes, always
+ *       required: it holds the logits (for bf16 at T <= 64, the partial logits of
+ *       the K-split router GEMM, added in a fixed order, so results stay
+ *       deterministic).  logits_out, when given, receives a copy of the summed logits.
  * Selection decisions are taken on fp32 values: (logit + offset) for modes 0/1;
  * for mode 2 on c = s + bias with s = sigmoid(logit+offset) rounded to nearest fp32
  * and group scores c_a + c_b in fp32. */
 moe_status moe_route(const void* x, const void* wg, int T, int H, int E, int k, moe_dtype dt,
                      const moe_route_cfg* cfg, int32_t* topk_ids, float* topk_w,
                      float* logits_out, void* ws, size_t ws_bytes, void* stream);
-size_t moe_route_workspace_size(int T, int E);
+size_t moe_route_workspace_size(int T, int H, int E, moe_dtype dt);
 
 /* The selection/weighting half of moe_route on caller-supplied fp32 logits [T,E]
  * (the same device code as moe_route's epilogue). */

@@ -71,8 +71,8 @@ def route_cfg(mode: int, logit_offset=None, select_bias=None, n_group: int = 0,
     return c
 
 
-def moe_route_workspace_size(T: int, E: int) -> int:
-    return lib.moe_route_workspace_size(T, E)
+def moe_route_workspace_size(T: int, H: int, E: int, dtype: int) -> int:
+    return lib.moe_route_workspace_size(T, H, E, dtype)
 
 
 def moe_route(x, wg, k, cfg: RouteCfg, logits_out=None):
@@ -81,8 +81,7 @@ def moe_route(x, wg, k, cfg: RouteCfg, logits_out=None):
     E = wg.shape[0]
     ids = torch.empty(T, k, dtype=torch.int32, device=x.device)
     w = torch.empty(T, k, dtype=torch.float32, device=x.device)
-    nws = 0 if logits_out is not None else lib.moe_route_workspace_size(T, E)
-    ws = _ws(nws, x.device)
+    ws = _ws(lib.moe_route_workspace_size(T, H, E, _dt(x)), x.device)
     check(lib.moe_route(_p(x), _p(wg), T, H, E, k, _dt(x), ctypes.byref(cfg), _p(ids), _p(w),
                         _p(logits_out), _p(ws), ws.numel(), _stream()), "moe_route")
     return ids, w

@@ -27,7 +27,7 @@ class RouteCfg(ctypes.Structure):
 
 _SIGS = {
     "moe_route": (_i, [_p, _p, _i, _i, _i, _i, _i, _p, _p, _p, _p, _p, _sz, _p]),
-    "moe_route_workspace_size": (_sz, [_i, _i]),
+    "moe_route_workspace_size": (_sz, [_i, _i, _i, _i]),
     "moe_route_from_logits": (_i, [_p, _i, _i, _i, _p, _p, _p, _p]),
     "moe_align_capacity": (ctypes.c_int64, [_i, _i, _i, _i]),
     "moe_align_workspace_size": (_sz, [_i, _i, _i, _i]),

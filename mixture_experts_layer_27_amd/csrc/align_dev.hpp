@@ -1,0 +1,139 @@
+// Device-side building blocks of moe_align (histogram -> pad -> scan -> stable scatter),
+// shared by the align kernels and the fused small-batch routing kernel.
+// ("Mixture-of-Experts Kernels: Routing, Permutation, and Grouped GEMM", section 5.)
+//
+// Written for latency: at decode batch sizes the whole table is a few hundred rows,
+// so the cost is the number of dependent LDS / memory round trips, not bandwidth.
+// Every phase is one pass of independent accesses per thread (no per-element search,
+// no runtime division: block_m is a power of two).
+#pragma once
+#include "common.hpp"
+
+namespace moe {
+namespace alignd {
+
+constexpr int kAlignThreads = 1024;
+constexpr int kAlignWaves = kAlignThreads / kWave;
+constexpr int kSegRows = 256;        // rows per segment in the multi-launch path
+constexpr int kMaxE = 512;
+
+__device__ __forceinline__ int log2_pow2(int v) { return __builtin_ctz(static_cast<unsigned>(v)); }
+
+// Histogram of rows [r0, r1) into lds_cnt[0..E) (LDS atomics).
+__device__ inline void segment_histogram(const int32_t* __restrict__ ids, int r0, int r1,
+                                         int* __restrict__ lds_cnt) {
+  const int lane = lane_id();
+  for (int r = r0 + lane; r < r1; r += kWave) atomicAdd(&lds_cnt[ids[r]], 1);
+}
+
+// Stable scatter of rows [r0, r1) by the calling wave; run[e] holds the next free
+// position of expert e for this segment (LDS, owned by this wave).  Rows of equal
+// expert inside a 64-row chunk are ranked with a ballot match loop.
+__device__ inline void segment_scatter(const int32_t* __restrict__ ids, int r0, int r1,
+                                       int* __restrict__ run, int32_t* __restrict__ sorted_ids) {
+  const int lane = lane_id();
+  const uint64_t lt = lanemask_lt();
+  for (int base = r0; base < r1; base += kWave) {
+    const int r = base + lane;
+    const bool valid = r < r1;
+    const int e = valid ? ids[r] : -1;
+    uint64_t remaining = __ballot(valid);
+    while (remaining) {
+      const int leader = __ffsll(static_cast<unsigned long long>(remaining)) - 1;
+      const int le = read_lane(e, leader);
+      const uint64_t m = __ballot(e == le);
+      const int start = run[le];                       // every lane reads before the leader writes
+      if (e == le) sorted_ids[start + __popcll(m & lt)] = r;
+      __builtin_amdgcn_wave_barrier();
+      if (lane == leader) run[le] = start + __popcll(m);
+      __builtin_amdgcn_wave_barrier();
+      remaining &= ~m;
+    }
+  }
+}
+
+// Exclusive scan of the padded counts by the first wave: start[e] for every e and
+// *total_out = sum of padded counts.  cnt[e] must be final.
+__device__ inline void scan_padded(const int* __restrict__ cnt, int E, int bm,
+                                   int* __restrict__ start, int* __restrict__ total_out) {
+  if (wave_id() != 0) return;
+  const int lane = lane_id();
+  int carry = 0;
+  for (int e0 = 0; e0 < E; e0 += kWave) {
+    const int e = e0 + lane;
+    const int n = e < E ? cnt[e] : 0;
+    const int padded = (n + bm - 1) & -bm;
+    const int incl = wave_incl_scan(padded);
+    if (e < E) start[e] = carry + incl - padded;
+    carry += read_lane(incl, kWave - 1);
+  }
+  if (lane == 0) *total_out = carry;
+}
+
+// expert_ids: thread e writes the tiles of expert e ([start_e, start_e + padded_e) / bm);
+// the rest of the first cap/bm entries gets -1.
+__device__ inline void fill_expert_ids(const int* __restrict__ cnt, const int* __restrict__ start,
+                                       int E, int bm, int total, int64_t cap,
+                                       int32_t* __restrict__ expert_ids) {
+  const int lg = log2_pow2(bm);
+  for (int e = threadIdx.x; e < E; e += blockDim.x) {
+    const int n = cnt[e];
+    const int s = start[e];
+    const int p1 = (s + n + bm - 1) >> lg;
+    for (int p = s >> lg; p < p1; ++p) expert_ids[p] = e;
+  }
+  const int ntiles_cap = static_cast<int>(cap >> lg);
+  for (int p = (total >> lg) + threadIdx.x; p < ntiles_cap; p += blockDim.x) expert_ids[p] = -1;
+}
+
+// ---------------------------------------------------------------- single work-group path
+// The whole table in one work-group of kAlignThreads threads (ids may live in LDS).
+// sorted_ids is first filled with the sentinel R, then the scatter overwrites the
+// routed rows (the barrier between the two waits for the stores to complete).
+__device__ inline void align_small_body(const int32_t* ids, int R, int E, int bm, int64_t cap,
+                                        int32_t* __restrict__ sorted_ids,
+                                        int32_t* __restrict__ expert_ids,
+                                        int32_t* __restrict__ ntpp, int32_t* __restrict__ counts) {
+  __shared__ int hist[kAlignWaves][kMaxE];   // per-wave segment histogram, later run cursors
+  __shared__ int cnt[kMaxE], start[kMaxE];
+  __shared__ int total_s;
+  const int w = wave_id();
+  // contiguous segments, one per wave, in ascending row order
+  const int per = (R + kAlignWaves - 1) / kAlignWaves;
+  const int r0 = min(R, w * per), r1 = min(R, r0 + per);
+  for (int i = threadIdx.x; i < kAlignWaves * kMaxE; i += blockDim.x) {
+    if ((i & (kMaxE - 1)) < E) (&hist[0][0])[i] = 0;
+  }
+  for (int64_t p = threadIdx.x; p < cap; p += blockDim.x) sorted_ids[p] = R;
+  __syncthreads();
+  segment_histogram(ids, r0, r1, hist[w]);
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += blockDim.x) {
+    int s = 0;
+#pragma unroll
+    for (int q = 0; q < kAlignWaves; ++q) s += hist[q][e];
+    cnt[e] = s;
+  }
+  __syncthreads();
+  scan_padded(cnt, E, bm, start, &total_s);
+  __syncthreads();
+  const int total = total_s;
+  // per-wave run cursors: start_e + rows of expert e in earlier segments
+  for (int e = threadIdx.x; e < E; e += blockDim.x) {
+    int run = start[e];
+#pragma unroll
+    for (int q = 0; q < kAlignWaves; ++q) {
+      const int c = hist[q][e];
+      hist[q][e] = run;
+      run += c;
+    }
+    if (counts) counts[e] = cnt[e];
+  }
+  if (threadIdx.x == 0) *ntpp = total;
+  fill_expert_ids(cnt, start, E, bm, total, cap, expert_ids);
+  __syncthreads();
+  segment_scatter(ids, r0, r1, hist[w], sorted_ids);
+}
+
+}  // namespace alignd
+}  // namespace moe

@@ -42,4 +42,48 @@ __device__ __forceinline__ void wave_sync() {
 template <typename T>
 __device__ __forceinline__ T wave_shfl(T v, int src) { return __shfl(v, src, kWave); }
 
+// ---------------------------------------------------------------- DPP lane moves
+// Data-parallel-primitive moves stay in the VALU (no LDS round trip, unlike the
+// ds_bpermute behind __shfl).  gfx9 control codes; every call must run with the
+// whole wave active.
+namespace dpp {
+constexpr int kQuadXor1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kQuadXor2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kRowHalfMirror = 0x141;  // lane i <- lane 7-i within each 8 lanes
+constexpr int kRowMirror = 0x140;      // lane i <- lane 15-i within each 16-lane row
+constexpr int kRowShr = 0x110;         // + n: lane i <- lane i-n of the same row
+constexpr int kRowBcast15 = 0x142;     // lane 15 of row r -> every lane of row r+1
+constexpr int kRowBcast31 = 0x143;     // lane 31 -> every lane of rows 2 and 3
+}  // namespace dpp
+
+// Lanes not written by the move (no source lane, or row masked off) return 0.
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ int dpp_move(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, ROW_MASK, 0xF, false);
+}
+
+// Inclusive prefix sum over the 64 lanes.
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  v += dpp_move<dpp::kRowShr + 1>(v);
+  v += dpp_move<dpp::kRowShr + 2>(v);
+  v += dpp_move<dpp::kRowShr + 4>(v);
+  v += dpp_move<dpp::kRowShr + 8>(v);
+  v += dpp_move<dpp::kRowBcast15, 0xA>(v);
+  v += dpp_move<dpp::kRowBcast31, 0xC>(v);
+  return v;
+}
+
+__device__ __forceinline__ int read_lane(int v, int lane) {
+  return __builtin_amdgcn_readlane(v, lane);
+}
+__device__ __forceinline__ float read_lane(float v, int lane) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
+}
+__device__ __forceinline__ double read_lane(double v, int lane) {
+  const uint64_t b = __builtin_bit_cast(uint64_t, v);
+  const uint32_t lo = __builtin_amdgcn_readlane(static_cast<int>(b & 0xffffffffu), lane);
+  const uint32_t hi = __builtin_amdgcn_readlane(static_cast<int>(b >> 32), lane);
+  return __builtin_bit_cast(double, (static_cast<uint64_t>(hi) << 32) | lo);
+}
+
 }  // namespace moe

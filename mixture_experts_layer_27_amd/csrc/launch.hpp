@@ -16,10 +16,20 @@ struct RouteArgs {
 };
 
 // router
+// bf16 logits at decode batch sizes are produced as router_slabs(T,H) partial slabs
+// [nz][T][E] that the top-k stage adds in ascending order (nz == 1: plain logits).
+int router_slabs(int T, int H, bool bf16);
 hipError_t launch_router_logits(const void* x, const void* wg, int T, int H, int E, bool bf16,
                                 float* logits, hipStream_t s);
-hipError_t launch_topk(const float* logits, int T, int E, int k, const RouteArgs& a,
-                       int32_t* ids, float* w, hipStream_t s);
+// logits_out (nullable) receives the summed logits when nz > 1
+hipError_t launch_topk(const float* logits, int nz, float* logits_out, int T, int E, int k,
+                       const RouteArgs& a, int32_t* ids, float* w, hipStream_t s);
+// top-k of every token and the align table in one single-work-group launch
+bool route_align_fusable(int T, int k, int E);
+hipError_t launch_route_align_small(const float* logits, int nz, float* logits_out, int T, int E,
+                                    int k, const RouteArgs& a, int32_t* ids, float* w, int bm,
+                                    int64_t cap, int32_t* sorted_ids, int32_t* expert_ids,
+                                    int32_t* ntpp, int32_t* counts, hipStream_t s);
 
 // align
 size_t align_ws_bytes(int R, int E);

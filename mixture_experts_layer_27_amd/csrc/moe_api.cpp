@@ -177,9 +177,10 @@ const char* moe_status_string(int status) {
 const char* moe_last_error(void) { return g_err.c_str(); }
 
 // ------------------------------------------------------------------------------ route
-size_t moe_route_workspace_size(int T, int E) {
-  if (T <= 0 || E <= 0) return 0;
-  return round_up(static_cast<size_t>(T) * E * sizeof(float));
+size_t moe_route_workspace_size(int T, int H, int E, moe_dtype dt) {
+  if (T <= 0 || H <= 0 || E <= 0 || !valid_dt(dt)) return 0;
+  const size_t nz = static_cast<size_t>(moe::router_slabs(T, H, dt == MOE_BF16));
+  return round_up(nz * static_cast<size_t>(T) * E * sizeof(float));
 }
 
 moe_status moe_route(const void* x, const void* wg, int T, int H, int E, int k, moe_dtype dt,
@@ -196,17 +197,14 @@ moe_status moe_route(const void* x, const void* wg, int T, int H, int E, int k, 
     if (H % 64) return fail(MOE_ERR_UNSUPPORTED, "bf16 router needs H %% 64 == 0 (H=%d)", H);
     if (!aligned16(x) || !aligned16(wg)) return fail(MOE_ERR_INVALID_ARG, "x/Wg not 16-byte aligned");
   }
-  float* logits = logits_out;
-  if (!logits) {
-    if (!ws || ws_bytes < moe_route_workspace_size(T, E))
-      return fail(MOE_ERR_WORKSPACE, "route workspace needs %zu bytes",
-                  moe_route_workspace_size(T, E));
-    logits = static_cast<float*>(ws);
-  }
+  const size_t need = moe_route_workspace_size(T, H, E, dt);
+  if (!ws || ws_bytes < need) return fail(MOE_ERR_WORKSPACE, "route workspace needs %zu bytes", need);
+  float* slabs = static_cast<float*>(ws);
+  const int nz = moe::router_slabs(T, H, dt == MOE_BF16);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = moe::launch_router_logits(x, wg, T, H, E, dt == MOE_BF16, logits, s);
+  hipError_t e = moe::launch_router_logits(x, wg, T, H, E, dt == MOE_BF16, slabs, s);
   if (e != hipSuccess) return hip_status(e, "router logits");
-  e = moe::launch_topk(logits, T, E, k, route_args(cfg), topk_ids, topk_w, s);
+  e = moe::launch_topk(slabs, nz, logits_out, T, E, k, route_args(cfg), topk_ids, topk_w, s);
   return hip_status(e, "top-k");
 }
 
@@ -218,7 +216,7 @@ moe_status moe_route_from_logits(const float* logits, int T, int E, int k,
   if ((st = check_route_cfg(cfg, E, k)) != MOE_OK) return st;
   if (T == 0) return ok();
   if (!logits || !topk_ids || !topk_w) return fail(MOE_ERR_INVALID_ARG, "NULL tensor pointer");
-  hipError_t e = moe::launch_topk(logits, T, E, k, route_args(cfg), topk_ids, topk_w,
+  hipError_t e = moe::launch_topk(logits, 1, nullptr, T, E, k, route_args(cfg), topk_ids, topk_w,
                                   static_cast<hipStream_t>(stream));
   return hip_status(e, "top-k");
 }
@@ -358,7 +356,8 @@ moe_status moe_forward(const void* x, const void* w13, const void* w2, const flo
 // ------------------------------------------------------------------------------ layer
 namespace {
 struct LayerPlan {
-  int bm;
+  int bm, nz;
+  bool fused_route_align;
   int64_t cap;
   size_t off_logits, off_ids, off_w, off_sorted, off_eids, off_ntpp, off_counts, off_align,
       off_fwd, total;
@@ -370,7 +369,9 @@ LayerPlan plan_layer(int T, int H, int I, int E, int k, moe_dtype dt) {
   p.cap = capacity(T, k, E, p.bm);
   const size_t R = static_cast<size_t>(T) * k;
   size_t off = 0;
-  p.off_logits = off; off += round_up(static_cast<size_t>(T) * E * sizeof(float));
+  p.nz = moe::router_slabs(T, H, dt == MOE_BF16);
+  p.fused_route_align = moe::route_align_fusable(T, k, E);
+  p.off_logits = off; off += round_up(static_cast<size_t>(p.nz) * T * E * sizeof(float));
   p.off_ids = off; off += round_up(R * sizeof(int32_t));
   p.off_w = off; off += round_up(R * sizeof(float));
   p.off_sorted = off; off += round_up(static_cast<size_t>(p.cap) * sizeof(int32_t));
@@ -415,11 +416,17 @@ moe_status moe_layer(const void* x, const void* wg, const void* w13, const void*
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = moe::launch_router_logits(x, wg, T, H, E, dt == MOE_BF16, logits, s);
   if (e != hipSuccess) return hip_status(e, "router logits");
-  e = moe::launch_topk(logits, T, E, k, route_args(cfg), ids, tw, s);
-  if (e != hipSuccess) return hip_status(e, "top-k");
-  e = moe::launch_align(ids, T * k, E, p.bm, p.cap, sorted, eids, ntpp, counts,
-                        reinterpret_cast<int32_t*>(b + p.off_align), s);
-  if (e != hipSuccess) return hip_status(e, "align");
+  if (p.fused_route_align) {
+    e = moe::launch_route_align_small(logits, p.nz, nullptr, T, E, k, route_args(cfg), ids, tw,
+                                      p.bm, p.cap, sorted, eids, ntpp, counts, s);
+    if (e != hipSuccess) return hip_status(e, "route+align");
+  } else {
+    e = moe::launch_topk(logits, p.nz, nullptr, T, E, k, route_args(cfg), ids, tw, s);
+    if (e != hipSuccess) return hip_status(e, "top-k");
+    e = moe::launch_align(ids, T * k, E, p.bm, p.cap, sorted, eids, ntpp, counts,
+                          reinterpret_cast<int32_t*>(b + p.off_align), s);
+    if (e != hipSuccess) return hip_status(e, "align");
+  }
   return moe_forward(x, w13, w2, tw, sorted, eids, ntpp, T, H, I, E, k, p.bm, dt,
                      MOE_VARIANT_AUTO, out, b + p.off_fwd, forward_ws(T, H, I, k, dt), stream);
 }

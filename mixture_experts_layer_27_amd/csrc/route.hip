@@ -3,14 +3,20 @@
 // model table, section 3 `route`, section 4 grouped sigmoid router).
 //
 // Logits (bf16): MFMA 16x16x32 bf16 with operands read straight from global memory
-// in MFMA register layout (each lane owns one row of A or B and 32 contiguous bytes
-// of K; the same k permutation is applied to both operands, so the dot products are
-// unchanged).  A work-group covers 16 tokens x 16*(4/KSPLIT) experts; KSPLIT waves
-// split K and reduce through LDS, which spreads the Wg stream over more CUs when T
-// is small (decode).
+// in MFMA register layout: lane group g = lane>>4 of a row reads elements g*8..g*8+7
+// of each 32-element half of a 64-element chunk, so the k order is the natural one and
+// one load instruction covers 64 contiguous bytes of each of 16 rows.  A work-group
+// covers 16 tokens x 16*(4/KSPLIT) experts; KSPLIT waves split its K range and reduce
+// through LDS.  At decode batch sizes the K range is further split over NZ work-groups
+// (slabs), each writing partial logits [NZ][T][E]; the top-k stage adds the slabs in
+// ascending slab order, so the result does not depend on scheduling.  This spreads
+// the Wg stream (3.7 MB for E=256, H=7168) over a few hundred work-groups.
 //
 // Top-k: one wave per token; lane l owns experts l, l+64, ...; each of the k
-// selections is a wave arg-max on (value desc, index asc).
+// selections is a wave arg-max on (value desc, index asc).  For small batches a
+// single work-group routes every token and then builds the align table in the same
+// launch (the ids never leave LDS before the align step reads them).
+#include "align_dev.hpp"
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -18,30 +24,31 @@ namespace moe {
 
 namespace {
 
-constexpr int kMaxPerLane = 8;   // E <= 512
+constexpr int kMaxSlabs = 16;
 
 template <int KSPLIT>
 __global__ void __launch_bounds__(256)
 router_logits_bf16_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ wg,
-                          int T, int H, int E, float* __restrict__ logits) {
+                          int T, int H, int E, int kz, float* __restrict__ logits) {
   constexpr int kExpWaves = 4 / KSPLIT;            // expert sub-blocks per WG
   __shared__ f32x4 red[4][kWave];
   const int lane = lane_id(), w = wave_id();
   const int eblk = w / KSPLIT, ks = w % KSPLIT;
   const int t0 = blockIdx.x * 16;
   const int e0 = (blockIdx.y * kExpWaves + eblk) * 16;
+  const int z = blockIdx.z;                         // K slab of this work-group
   const int row = lane & 15, grp = lane >> 4;
   const int t = min(t0 + row, T - 1);
   const int e = min(e0 + row, E - 1);
-  const uint16_t* xa = x + static_cast<int64_t>(t) * H + grp * 16;
-  const uint16_t* wb = wg + static_cast<int64_t>(e) * H + grp * 16;
-  const int kper = H / KSPLIT;                      // H % (64*KSPLIT) == 0 (host-checked)
+  const uint16_t* xa = x + static_cast<int64_t>(t) * H + grp * 8;
+  const uint16_t* wb = wg + static_cast<int64_t>(e) * H + grp * 8;
+  const int klo = z * kz, khi = min(H, klo + kz);   // kz and H are multiples of 64
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  for (int k0 = ks * kper; k0 < (ks + 1) * kper; k0 += 64) {
+  for (int k0 = klo + ks * 64; k0 < khi; k0 += 64 * KSPLIT) {
     const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(xa + k0);
-    const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(xa + k0 + 8);
+    const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(xa + k0 + 32);
     const bf16x8 b0 = *reinterpret_cast<const bf16x8*>(wb + k0);
-    const bf16x8 b1 = *reinterpret_cast<const bf16x8*>(wb + k0 + 8);
+    const bf16x8 b1 = *reinterpret_cast<const bf16x8*>(wb + k0 + 32);
     acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, b0, acc, 0, 0, 0);
     acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, b1, acc, 0, 0, 0);
   }
@@ -57,9 +64,10 @@ router_logits_bf16_kernel(const uint16_t* __restrict__ x, const uint16_t* __rest
   // D layout (16x16): lane holds column (lane & 15) = expert, rows 4*(lane>>4)+v = tokens
   const int ec = e0 + (lane & 15);
   if (ec >= E) return;
+  float* slab = logits + static_cast<int64_t>(z) * T * E;
   for (int v = 0; v < 4; ++v) {
     const int tr = t0 + 4 * (lane >> 4) + v;
-    if (tr < T) logits[static_cast<int64_t>(tr) * E + ec] = acc[v];
+    if (tr < T) slab[static_cast<int64_t>(tr) * E + ec] = acc[v];
   }
 }
 
@@ -77,11 +85,50 @@ router_logits_f32_kernel(const float* __restrict__ x, const float* __restrict__ 
 }
 
 // (value, index) arg-max across the wave: better = larger value, then smaller index.
+// Indices are distinct, so the order is total and the combining order does not matter.
+__device__ __forceinline__ void argmax_merge(float& v, int& idx, float ov, int oi) {
+  const bool take = (ov > v) | ((ov == v) & (oi < idx));   // no short-circuit branches
+  v = take ? ov : v;
+  idx = take ? oi : idx;
+}
+
+template <int CTRL>
+__device__ __forceinline__ void argmax_step(float& v, int& idx) {
+  const float ov = __int_as_float(dpp_move<CTRL>(__float_as_int(v)));
+  const int oi = dpp_move<CTRL>(idx);
+  argmax_merge(v, idx, ov, oi);
+}
+
+// Every lane returns the wave's best: DPP within each 16-lane row, then the four row
+// winners read as uniform values.
 __device__ __forceinline__ void wave_argmax(float& v, int& idx) {
-  for (int d = 32; d >= 1; d >>= 1) {
-    const float ov = __shfl_xor(v, d, kWave);
-    const int oi = __shfl_xor(idx, d, kWave);
-    if (ov > v || (ov == v && oi < idx)) { v = ov; idx = oi; }
+  argmax_step<dpp::kQuadXor1>(v, idx);
+  argmax_step<dpp::kQuadXor2>(v, idx);
+  argmax_step<dpp::kRowHalfMirror>(v, idx);
+  argmax_step<dpp::kRowMirror>(v, idx);
+  float b = read_lane(v, 0);
+  int bi = read_lane(idx, 0);
+  argmax_merge(b, bi, read_lane(v, 16), read_lane(idx, 16));
+  argmax_merge(b, bi, read_lane(v, 32), read_lane(idx, 32));
+  argmax_merge(b, bi, read_lane(v, 48), read_lane(idx, 48));
+  v = b;
+  idx = bi;
+}
+
+// (m1, m2) <- the two largest of {m1, m2, o1, o2}, given m1 >= m2 and o1 >= o2
+__device__ __forceinline__ void top2_merge(float& m1, float& m2, float o1, float o2) {
+  const float n2 = fmaxf(fminf(m1, o1), fmaxf(m2, o2));
+  m1 = fmaxf(m1, o1);
+  m2 = n2;
+}
+
+template <int CTRL, int NSLOT>
+__device__ __forceinline__ void top2_steps(float (&m1)[NSLOT], float (&m2)[NSLOT]) {
+#pragma unroll
+  for (int i = 0; i < NSLOT; ++i) {
+    const float o1 = __int_as_float(dpp_move<CTRL>(__float_as_int(m1[i])));
+    const float o2 = __int_as_float(dpp_move<CTRL>(__float_as_int(m2[i])));
+    top2_merge(m1[i], m2[i], o1, o2);
   }
 }
 
@@ -90,119 +137,245 @@ __device__ __forceinline__ float sigmoid_rn(float l) {
   return static_cast<float>(1.0 / (1.0 + exp(-static_cast<double>(l))));
 }
 
-__global__ void __launch_bounds__(256)
-topk_kernel(const float* __restrict__ logits, int T, int E, int k, int mode,
-            const float* __restrict__ offset, const float* __restrict__ bias, int n_group,
-            int topk_group, float scaling, int32_t* __restrict__ ids, float* __restrict__ wout) {
-  __shared__ float cval[4][512];
-  __shared__ int keep_grp[4][64];
-  __shared__ int chosen_id[4][16];
-  __shared__ float chosen_src[4][16];
-  const int lane = lane_id(), w = wave_id();
-  const int t = blockIdx.x * 4 + w;
-  if (t >= T) return;                              // whole wave leaves together
-  const float* lrow = logits + static_cast<int64_t>(t) * E;
+struct TopkParams {
+  const float* logits;     // nz slabs of [T][E] (nz == 1: the logits themselves)
+  int nz;
+  float* logits_out;       // [T][E] or null: receives the summed logits (nz > 1)
+  int T, E, k, mode;
+  const float* offset;
+  const float* bias;
+  int n_group, topk_group;
+  float scaling;
+  int32_t* ids;
+  float* w;
+};
+
+// LDS of one wave's top-k (group segment pairs)
+struct TopkLds {
+  float cval[512];
+};
+
+// Routes token t with the calling wave: writes ids/w (and logits_out) of t, and the
+// ids into ids_lds when given.  NSLOT = experts per lane (E <= 64*NSLOT); ZC = logit
+// slabs loaded per round trip (bounded by the registers the launch allows).
+template <int NSLOT, int ZC>
+__device__ void topk_token(const TopkParams& p, int t, TopkLds& sh, int32_t* ids_lds) {
+  const int lane = lane_id();
+  const int E = p.E, k = p.k, mode = p.mode;
   const float kNegInf = -__builtin_inff();
-  float sel[kMaxPerLane];    // selection value (-inf = not eligible / taken)
-  float wsrc[kMaxPerLane];   // weight source: logit (modes 0,1) or unbiased sigmoid (2)
+  // every load first, at clamped indices, so that all of them are in flight together;
+  // slabs are added in ascending order
+  float lv[NSLOT], ov[NSLOT], bv[NSLOT];
+  const float* lrow = p.logits + static_cast<int64_t>(t) * E;
+  const int64_t slab = static_cast<int64_t>(p.T) * E;
 #pragma unroll
-  for (int i = 0; i < kMaxPerLane; ++i) {
+  for (int i = 0; i < NSLOT; ++i) {
+    const int ec = min(lane + kWave * i, E - 1);
+    lv[i] = lrow[ec];
+    ov[i] = p.offset ? p.offset[ec] : 0.f;
+    bv[i] = p.bias ? p.bias[ec] : 0.f;
+  }
+  if (p.nz > 1) {
+    for (int z0 = 1; z0 < p.nz; z0 += ZC) {
+      float part[ZC][NSLOT];
+#pragma unroll
+      for (int q = 0; q < ZC; ++q) {
+        const int zc = min(z0 + q, p.nz - 1);
+#pragma unroll
+        for (int i = 0; i < NSLOT; ++i)
+          part[q][i] = lrow[zc * slab + min(lane + kWave * i, E - 1)];
+      }
+#pragma unroll
+      for (int q = 0; q < ZC; ++q) {
+#pragma unroll
+        for (int i = 0; i < NSLOT; ++i) lv[i] = z0 + q < p.nz ? lv[i] + part[q][i] : lv[i];
+      }
+    }
+  }
+  float sel[NSLOT];    // selection value (-inf = not eligible / taken)
+  float wsrc[NSLOT];   // weight source: logit (modes 0,1) or unbiased sigmoid (2)
+#pragma unroll
+  for (int i = 0; i < NSLOT; ++i) {
     const int e = lane + kWave * i;
-    float v = kNegInf, ws = 0.f;
-    if (e < E) {
-      float l = lrow[e];
-      if (offset) l = l + offset[e];
-      if (mode == 2) {
-        const float s = sigmoid_rn(l);
-        v = bias ? s + bias[e] : s;
-        ws = s;
-      } else {
-        v = l;
-        ws = l;
+    if (p.logits_out && e < E) p.logits_out[static_cast<int64_t>(t) * E + e] = lv[i];
+    float l = lv[i];
+    if (p.offset) l = l + ov[i];
+    float v, ws;
+    if (mode == 2) {
+      const float s = sigmoid_rn(l);
+      v = p.bias ? s + bv[i] : s;
+      ws = s;
+    } else {
+      v = l;
+      ws = l;
+    }
+    sel[i] = e < E ? v : kNegInf;
+    wsrc[i] = e < E ? ws : 0.f;
+  }
+  if (mode == 2 && p.n_group > 0 && p.topk_group > 0) {
+    // group score = sum of the two largest biased scores of a contiguous group of
+    // gsz = E / n_group experts.  Top-2 pairs are first merged across aligned lane
+    // segments of `sub` lanes (sub = the largest power of two <= 16 dividing gsz) with
+    // DPP moves; lane g then merges the gsz/sub segment pairs of group g from LDS.
+    // Only values enter the score, so the merge order does not change it.
+    const int gsz = E / p.n_group;
+    const int sub = min(16, gsz & -gsz);
+    float m1[NSLOT], m2[NSLOT];
+#pragma unroll
+    for (int i = 0; i < NSLOT; ++i) { m1[i] = sel[i]; m2[i] = kNegInf; }
+    if (sub >= 2) top2_steps<dpp::kQuadXor1, NSLOT>(m1, m2);
+    if (sub >= 4) top2_steps<dpp::kQuadXor2, NSLOT>(m1, m2);
+    if (sub >= 8) top2_steps<dpp::kRowHalfMirror, NSLOT>(m1, m2);
+    if (sub >= 16) top2_steps<dpp::kRowMirror, NSLOT>(m1, m2);
+    // segment pairs: first value at cval[s], second at cval[256 + s] (sub >= 2 leaves at
+    // most 256 segments; with sub == 1 every second value is -inf and not stored)
+#pragma unroll
+    for (int i = 0; i < NSLOT; ++i) {
+      const int e = lane + kWave * i;
+      if (e < E && (lane & (sub - 1)) == 0) {
+        const int sg = e / sub;
+        sh.cval[sg] = m1[i];
+        if (sub > 1) sh.cval[256 + sg] = m2[i];
       }
     }
-    sel[i] = v;
-    wsrc[i] = ws;
-  }
-  if (mode == 2 && n_group > 0 && topk_group > 0) {
-    // group scores: sum of the two largest biased scores of each contiguous group
-#pragma unroll
-    for (int i = 0; i < kMaxPerLane; ++i) {
-      const int e = lane + kWave * i;
-      if (e < E) cval[w][e] = sel[i];
-    }
     wave_sync();
-    const int gsz = E / n_group;
-    float gscore = kNegInf;
-    int gidx = lane;
-    if (lane < n_group) {
-      float m1 = kNegInf, m2 = kNegInf;
-      for (int q = 0; q < gsz; ++q) {              // ascending index: ties keep the first
-        const float c = cval[w][lane * gsz + q];
-        if (c > m1) { m2 = m1; m1 = c; } else if (c > m2) { m2 = c; }
-      }
-      gscore = m1 + m2;
+    float gs = kNegInf;
+    if (lane < p.n_group) {
+      const int nps = gsz / sub;
+      const int s0 = lane * nps;
+      float g1 = sh.cval[s0];
+      float g2 = sub > 1 ? sh.cval[256 + s0] : kNegInf;
+      for (int q = 1; q < nps; ++q)
+        top2_merge(g1, g2, sh.cval[s0 + q], sub > 1 ? sh.cval[256 + s0 + q] : kNegInf);
+      gs = g1 + g2;
     }
-    keep_grp[w][lane] = 0;
-    wave_sync();
-    for (int j = 0; j < topk_group; ++j) {
-      float v = gscore;
-      int idx = gidx;
-      if (lane >= n_group) { v = kNegInf; idx = 0x7fffffff; }
-      wave_argmax(v, idx);
-      if (lane == idx) { keep_grp[w][lane] = 1; gscore = kNegInf; gidx = 0x7fffffff; }
-      wave_sync();
+    // keep the topk_group groups of highest score (ties to the lower group index):
+    // group g is kept when fewer than topk_group groups beat it
+    int beaten_by = 0;
+    for (int h = 0; h < p.n_group; ++h) {
+      const float o = read_lane(gs, h);
+      beaten_by += ((o > gs) | ((o == gs) & (h < lane))) ? 1 : 0;
     }
+    const uint64_t keep = __ballot(lane < p.n_group && beaten_by < p.topk_group);
 #pragma unroll
-    for (int i = 0; i < kMaxPerLane; ++i) {
-      const int e = lane + kWave * i;
-      if (e < E && !keep_grp[w][e / gsz]) sel[i] = kNegInf;
+    for (int i = 0; i < NSLOT; ++i) {
+      const int e = min(lane + kWave * i, E - 1);
+      sel[i] = (keep >> (e / gsz)) & 1ull ? sel[i] : kNegInf;
     }
+    wave_sync();                                   // cval is reused by the next token
   }
-  // k selections; lane 0 keeps the chosen (id, weight source) pairs in LDS
+  // k selections; lane j keeps the j-th chosen (id, weight source) pair.  Branch-free:
+  // invalid, masked and taken slots hold -inf and never win (at least k finite
+  // candidates exist), and within a lane a larger slot is a larger index, so a strict
+  // comparison keeps the lower index on ties.
+  int my_id = 0;
+  float my_src = 0.f;
   for (int j = 0; j < k; ++j) {
-    float bv = kNegInf;
-    int bi = 0x7fffffff;
+    float best = sel[0];
+    int bi = lane;
 #pragma unroll
-    for (int i = 0; i < kMaxPerLane; ++i) {       // within a lane, larger i = larger index
-      const int e = lane + kWave * i;
-      if (e < E && (sel[i] > bv || (sel[i] == bv && e < bi))) {
-        bv = sel[i];
-        bi = e;
-      }
+    for (int i = 1; i < NSLOT; ++i) {
+      const bool better = sel[i] > best;
+      best = better ? sel[i] : best;
+      bi = better ? lane + kWave * i : bi;
     }
-    wave_argmax(bv, bi);
+    wave_argmax(best, bi);
     float src = 0.f;
 #pragma unroll
-    for (int i = 0; i < kMaxPerLane; ++i) {
-      if (lane + kWave * i == bi) { src = wsrc[i]; sel[i] = kNegInf; }
+    for (int i = 0; i < NSLOT; ++i) {
+      const bool hit = lane + kWave * i == bi;
+      src = hit ? wsrc[i] : src;
+      sel[i] = hit ? kNegInf : sel[i];
     }
-    src = __shfl(src, bi & (kWave - 1), kWave);   // the owner lane broadcasts
-    if (lane == 0) {
-      chosen_id[w][j] = bi;
-      chosen_src[w][j] = src;
-    }
+    src = read_lane(src, bi & (kWave - 1));        // the owner lane broadcasts
+    my_id = lane == j ? bi : my_id;
+    my_src = lane == j ? src : my_src;
   }
-  wave_sync();
-  if (lane == 0) {
-    double sum = 0.0;
-    const double l0 = chosen_src[w][0];
-    for (int j = 0; j < k; ++j) {
-      const double v = mode == 2 ? static_cast<double>(chosen_src[w][j])
-                                 : exp(static_cast<double>(chosen_src[w][j]) - l0);
-      sum += v;
-    }
-    for (int j = 0; j < k; ++j) {
-      const double v = mode == 2 ? static_cast<double>(chosen_src[w][j])
-                                 : exp(static_cast<double>(chosen_src[w][j]) - l0);
-      const double wt = mode == 2 ? static_cast<double>(scaling) * v / sum : v / sum;
-      ids[static_cast<int64_t>(t) * k + j] = chosen_id[w][j];
-      wout[static_cast<int64_t>(t) * k + j] = static_cast<float>(wt);
-    }
+  // weights in double: modes 0/1 exp(l_j - l_0) / sum, mode 2 scale * s_j / sum; the
+  // sum runs over j = 0..k-1 in order
+  const double l0 = static_cast<double>(read_lane(my_src, 0));
+  const double myv = mode == 2 ? static_cast<double>(my_src)
+                               : exp(static_cast<double>(my_src) - l0);
+  double sum = 0.0;
+  for (int j = 0; j < k; ++j) sum += read_lane(myv, j);
+  if (lane < k) {
+    const double wt = mode == 2 ? static_cast<double>(p.scaling) * myv / sum : myv / sum;
+    p.ids[static_cast<int64_t>(t) * k + lane] = my_id;
+    p.w[static_cast<int64_t>(t) * k + lane] = static_cast<float>(wt);
+    if (ids_lds) ids_lds[t * k + lane] = my_id;
   }
 }
 
+template <int NSLOT>
+__global__ void __launch_bounds__(256)
+topk_kernel(TopkParams p) {
+  __shared__ TopkLds sh[4];
+  const int w = wave_id();
+  const int t = blockIdx.x * 4 + w;
+  if (t >= p.T) return;                            // whole wave leaves together
+  topk_token<NSLOT, 60 / NSLOT>(p, t, sh[w], nullptr);
+}
+
+// Small batches: one work-group of 1024 threads routes all T tokens (wave w takes
+// tokens w, w+16, ...) and then builds the align table from the ids held in LDS.
+constexpr int kFusedMaxT = 32;
+constexpr int kFusedMaxRows = kFusedMaxT * 16;
+static_assert(alignd::kAlignThreads == 1024, "fused kernel runs the align body with 1024 threads");
+
+template <int NSLOT>
+__global__ void __launch_bounds__(1024)
+route_align_small_kernel(TopkParams p, int bm, int64_t cap, int32_t* __restrict__ sorted_ids,
+                         int32_t* __restrict__ expert_ids, int32_t* __restrict__ ntpp,
+                         int32_t* __restrict__ counts) {
+  __shared__ TopkLds sh[16];
+  __shared__ int32_t ids_lds[kFusedMaxRows];
+  const int w = wave_id();
+  for (int t = w; t < p.T; t += 16) topk_token<NSLOT, 28 / NSLOT>(p, t, sh[w], ids_lds);
+  __syncthreads();
+  alignd::align_small_body(ids_lds, p.T * p.k, p.E, bm, cap, sorted_ids, expert_ids, ntpp,
+                           counts);
+}
+
+// K slabs of the bf16 logits: at decode batch sizes enough work-groups to stream Wg
+// from many CUs, each slab a multiple of 256 columns (64 per wave).
+int slab_cols(int T, int H) {
+  if (T > 64 || H % 256) return H;
+  int nz = H / 512;
+  nz = nz < 1 ? 1 : (nz > kMaxSlabs ? kMaxSlabs : nz);
+  return (H / nz + 255) / 256 * 256;
+}
+
+TopkParams topk_params(const float* logits, int nz, float* logits_out, int T, int E, int k,
+                       const RouteArgs& a, int32_t* ids, float* w) {
+  TopkParams p;
+  p.logits = logits;
+  p.nz = nz;
+  p.logits_out = logits_out;
+  p.T = T;
+  p.E = E;
+  p.k = k;
+  p.mode = a.mode;
+  p.offset = a.offset;
+  p.bias = a.bias;
+  p.n_group = a.n_group;
+  p.topk_group = a.topk_group;
+  p.scaling = a.scaling;
+  p.ids = ids;
+  p.w = w;
+  return p;
+}
+
 }  // namespace
+
+int router_slabs(int T, int H, bool bf16) {
+  if (!bf16 || T <= 0) return 1;
+  const int kz = slab_cols(T, H);
+  return (H + kz - 1) / kz;
+}
+
+bool route_align_fusable(int T, int k, int E) {
+  return T <= kFusedMaxT && T * k <= kFusedMaxRows && E <= 4 * kWave;
+}
 
 hipError_t launch_router_logits(const void* x, const void* wg, int T, int H, int E, bool bf16,
                                 float* logits, hipStream_t s) {
@@ -215,24 +388,39 @@ hipError_t launch_router_logits(const void* x, const void* wg, int T, int H, int
     return hipGetLastError();
   }
   const unsigned tb = static_cast<unsigned>((T + 15) / 16);
+  const int nz = router_slabs(T, H, true);
   if (T <= 64 && H % 256 == 0) {
-    // decode: 16 experts per WG, K split over 4 waves
-    hipLaunchKernelGGL(router_logits_bf16_kernel<4>, dim3(tb, (E + 15) / 16), dim3(256), 0, s,
-                       static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(wg), T, H,
-                       E, logits);
+    // decode: 16 experts per work-group, each slab's K range split over 4 waves
+    hipLaunchKernelGGL(router_logits_bf16_kernel<4>, dim3(tb, (E + 15) / 16, nz), dim3(256), 0,
+                       s, static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(wg), T, H,
+                       E, slab_cols(T, H), logits);
   } else {
-    hipLaunchKernelGGL(router_logits_bf16_kernel<1>, dim3(tb, (E + 63) / 64), dim3(256), 0, s,
+    hipLaunchKernelGGL(router_logits_bf16_kernel<1>, dim3(tb, (E + 63) / 64, 1), dim3(256), 0, s,
                        static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(wg), T, H,
-                       E, logits);
+                       E, H, logits);
   }
   return hipGetLastError();
 }
 
-hipError_t launch_topk(const float* logits, int T, int E, int k, const RouteArgs& a,
-                       int32_t* ids, float* w, hipStream_t s) {
+hipError_t launch_topk(const float* logits, int nz, float* logits_out, int T, int E, int k,
+                       const RouteArgs& a, int32_t* ids, float* w, hipStream_t s) {
   if (T == 0) return hipSuccess;
-  hipLaunchKernelGGL(topk_kernel, dim3((T + 3) / 4), dim3(256), 0, s, logits, T, E, k, a.mode,
-                     a.offset, a.bias, a.n_group, a.topk_group, a.scaling, ids, w);
+  const TopkParams p = topk_params(logits, nz, logits_out, T, E, k, a, ids, w);
+  if (E <= 4 * kWave)
+    hipLaunchKernelGGL(topk_kernel<4>, dim3((T + 3) / 4), dim3(256), 0, s, p);
+  else
+    hipLaunchKernelGGL(topk_kernel<8>, dim3((T + 3) / 4), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_route_align_small(const float* logits, int nz, float* logits_out, int T, int E,
+                                    int k, const RouteArgs& a, int32_t* ids, float* w, int bm,
+                                    int64_t cap, int32_t* sorted_ids, int32_t* expert_ids,
+                                    int32_t* ntpp, int32_t* counts, hipStream_t s) {
+  // E <= 256 (route_align_fusable): four experts per lane
+  const TopkParams p = topk_params(logits, nz, logits_out, T, E, k, a, ids, w);
+  hipLaunchKernelGGL(route_align_small_kernel<4>, dim3(1), dim3(1024), 0, s, p, bm, cap,
+                     sorted_ids, expert_ids, ntpp, counts);
   return hipGetLastError();
 }
 

@@ -91,6 +91,24 @@ def test_route_validation(L):
     assert b"k=" in L.lib.moe_last_error() or L.lib.moe_last_error() == b""
 
 
+def test_route_workspace_size(L):
+    """Slabbed router at decode batch sizes: the partial logits of every K slab live in
+    the workspace (H=7168 splits into 14 slabs of 512 columns); fp32 and large T keep
+    one [T,E] buffer.  The workspace is required even when logits_out is given."""
+    sz = L.lib.moe_route_workspace_size
+    assert sz(1, 7168, 256, 1) == 14 * 256 * 4
+    assert sz(64, 7168, 256, 1) == 14 * 64 * 256 * 4
+    assert sz(65, 7168, 256, 1) == 65 * 256 * 4
+    assert sz(1, 7168, 256, 0) == 256 * 4
+    assert sz(4, 64, 8, 1) == 256          # one slab, rounded up to 256 bytes
+    assert sz(0, 64, 8, 1) == 0
+    c = cfg(L)
+    need = sz(16, 4096, 128, 1)
+    assert need == 8 * 16 * 128 * 4
+    assert L.lib.moe_route(FAKE, FAKE, 16, 4096, 128, 8, 1, ctypes.byref(c), FAKE, FAKE, FAKE,
+                           FAKE, need - 1, None) == WORKSPACE
+
+
 def test_align_validation(L):
     f = L.lib.moe_align
     assert f(FAKE, 4, 2, 8, 3, FAKE, FAKE, FAKE, None, FAKE, 1 << 20, None) == INVALID

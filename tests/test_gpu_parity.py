@@ -97,7 +97,12 @@ def test_route_from_logits_softmax(lib, T, E, k, mode):
 
 
 @pytest.mark.parametrize("T,E,k,ng,tg", [(64, 256, 8, 8, 4), (300, 256, 8, 8, 4), (17, 16, 4, 4, 2),
-                                         (40, 64, 6, 0, 0), (33, 512, 8, 64, 3)])
+                                         (40, 64, 6, 0, 0), (33, 512, 8, 64, 3),
+                                         # group sizes 3, 12, 128, 2 (odd, non power of
+                                         # two, several 16-lane rows, pairs)
+                                         (20, 96, 4, 32, 8), (20, 96, 6, 8, 3),
+                                         (20, 256, 8, 2, 1), (5, 384, 8, 3, 2),
+                                         (9, 40, 4, 20, 5), (3, 128, 8, 64, 8)])
 def test_route_from_logits_grouped(lib, T, E, k, ng, tg):
     rng = np.random.default_rng(T + E)
     l32 = rng.standard_normal((T, E)).astype(np.float32)
@@ -273,7 +278,10 @@ def test_layer_tiny(lib):
 
 @pytest.mark.parametrize("name,T,scale", [("mixtral", 96, 16), ("qwen3_skewed", 64, 8),
                                           ("deepseek_decode", 16, 8), ("gptoss", 128, 8),
-                                          ("qwen3_balanced", 40, 8)])
+                                          ("qwen3_balanced", 40, 8),
+                                          # K-split router slabs + one-launch route/align
+                                          ("deepseek_decode", 8, 4), ("qwen3_skewed", 3, 4),
+                                          ("deepseek_decode", 32, 4), ("deepseek_decode", 48, 4)])
 def test_layer_reduced(lib, name, T, scale):
     base = S.WORKLOADS[name]
     wl = base.scaled(T=T, H=base.H // scale // 64 * 64 or 64, I=base.I // scale // 64 * 64 or 64)
@@ -281,10 +289,12 @@ def test_layer_reduced(lib, name, T, scale):
     _layer_vs_oracle(lib, wl, lay)
 
 
-def test_layer_hip_graph_replays(lib):
+@pytest.mark.parametrize("T,H", [(96, 256), (8, 1024)])
+def test_layer_hip_graph_replays(lib, T, H):
     """The whole layer captured once in a HIP graph; replays with new activations (so the
-    routing changes) match eager runs."""
-    wl = S.WORKLOADS["qwen3_skewed"].scaled(T=96, H=256, I=128)
+    routing changes) match eager runs.  T=8 takes the small-batch launches (router K
+    slabs, one-launch route + align)."""
+    wl = S.WORKLOADS["qwen3_skewed"].scaled(T=T, H=H, I=128)
     lay = S.make_layer(wl, device=DEV, seed=5)
     cfg = lib_cfg(lib, wl, lay)
     x = lay.x.clone()
