@@ -17,7 +17,7 @@ LIB = os.path.join(PKG, "libmoe_mi355x.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = ["align.hip", "route.hip", "gemm.hip", "gemm_pipe.hip", "decode.hip", "moe_api.cpp"]
-HEADERS = ["common.hpp", "launch.hpp"]
+HEADERS = ["common.hpp", "launch.hpp", "align_dev.hpp", "dma.hpp"]
 
 # -packed-fp32-ops is off: no v_pk_{add,mul,fma}_f32 anywhere in the device code.
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",

@@ -3,163 +3,290 @@
 // tiles) and section 8 (FLOP per weight byte ~ n_e: bandwidth-bound below hundreds of
 // rows per expert)).
 //
-// Operand swap: the weights are the MFMA "A" side (16 weight rows per v_mfma_f32_16x16x32_bf16)
-// and the few routed token rows are the "B" side (16 tokens per MFMA), so a tile with a
-// single routed row still feeds whole MFMAs from the weight stream.  Weights go straight
-// from HBM to registers: lane l owns weight row (l & 15); in each K step of 32*CH elements
-// the four lanes of a row read 64 contiguous bytes per load instruction (16 rows per
-// instruction), in the natural MFMA k order, and the token rows are read the same way.
+// Operand swap: the weights are the MFMA "A" side (16 weight rows per
+// v_mfma_f32_16x16x32_bf16) and up to 16 routed token rows the "B" side, so a tile with
+// a single routed row still feeds whole MFMAs from the weight stream.
 //
-// Work item = (align tile of block_m <= 64 rows, block of weight rows).  GEMM1 items hold
-// 16 gate rows + the 16 matching up rows (16 output columns of a, SwiGLU in the epilogue);
-// GEMM2 items hold 32 rows of W2 (32 output columns of y, router weight in the epilogue).
-// The four waves of a work-group take K steps round-robin (adjacent 64*CH-byte pieces of the
-// same rows at the same time) and reduce through LDS.  The grid is persistent: the item
-// count comes from the device-side padded total, so no work-group is launched for padding.
+// Every wave is an independent streaming unit (one-wave work-groups, persistent grid).
+// Work item = (sub-tile of 16 routed rows, block of RB weight rows of its expert).
+// For each K step of STEP elements the wave copies the item's RB weight rows and the 16
+// token rows into a slot of its own LDS ring with global_load_lds: one load instruction
+// moves 1 KB made of whole 256-byte (STEP 128) or 128-byte (STEP 64) row segments,
+// the access pattern HBM serves fastest, and the MFMA register layout is recovered by
+// the LDS reads.  The XOR swizzle that keeps those reads conflict-free is applied on the
+// global side (lane i of a DMA fetches the chunk that belongs at LDS position i).
+// P ring slots: while step g is consumed, steps g+1 .. g+P-1 are in flight, across
+// item boundaries.  All loads of the loop are these DMAs (routing ids come through
+// scalar loads), so a fixed s_waitcnt vmcnt tells exactly when step g has landed.
 #include <algorithm>
 
 #include "common.hpp"
+#include "dma.hpp"
 #include "launch.hpp"
 
 namespace moe {
 
 namespace {
 
-constexpr int kDecWaves = 4;
-constexpr int kMaxTG = 4;   // token groups of 16 per pass (64 rows)
-
 struct DArgs {
   const uint16_t* A;      // weights: W13 [E,2I,H] or W2 [E,H,I]
   const uint16_t* X;      // token rows: x [T,H] (GEMM1) or a [R,I] (GEMM2)
   void* C;                // a [R,I] bf16 or y [R,H] f32
-  const float* topk_w;
-  const int32_t* sorted_ids;
-  const int32_t* expert_ids;
-  const int32_t* ntpp;
   int R, gather_div, K, I, H;
   int64_t a_expert_stride;
-  int block_m;
+  int block_m;            // >= 16: a tile holds block_m / 16 sub-tiles of 16 rows
   int nblk;               // weight-row blocks per expert
 };
 
-template <int MODE, int CH>
-__global__ void __launch_bounds__(256)
-moe_decode_kernel(DArgs p) {
-  __shared__ f32x4 red[kDecWaves][kMaxTG][2][kWave];
-  __shared__ int rows_s[64];
-  const int lane = lane_id(), w = wave_id();
-  const int total = *p.ntpp;
-  const int ntiles = total / p.block_m;
-  const int nitems = ntiles * p.nblk;
-  const int row16 = lane & 15, g = lane >> 4;
-  const int K = p.K;
-  constexpr int STEP = 32 * CH;            // K elements per step
-  const int nsteps = K / STEP;
+template <int STEP>
+struct DStep {
+  static constexpr int CPR = STEP / 8;      // 16-byte chunks per row per step
+  static constexpr int ROWB = STEP * 2;     // bytes per row per step
+  static constexpr int RPI = kWave / CPR;   // rows per DMA instruction (1 KB)
+  static constexpr int KSUB = STEP / 32;    // MFMA k-substeps per step
+  static_assert(STEP == 64 || STEP == 128, "step");
+};
 
-  for (int item = blockIdx.x; item < nitems; item += gridDim.x) {
-    const int tile = item / p.nblk, blk = item % p.nblk;
-    const int e = p.expert_ids[tile];
-    // weight rows of the two 16-row fragments
-    int wrow0, wrow1;
-    if (MODE == 1) { wrow0 = blk * 16 + row16; wrow1 = p.I + blk * 16 + row16; }
-    else { wrow0 = blk * 32 + row16; wrow1 = blk * 32 + 16 + row16; }
+// LDS position of logical 16-byte chunk c of row r: rows r..r+15 at one logical chunk
+// land on 16 distinct 16-byte bank groups (256-byte rows: c ^ r; 128-byte rows: two
+// rows share a bank window, so the low row bit selects the half and r>>1 the XOR)
+template <int CPR>
+__device__ __forceinline__ int dsw(int r, int c) {
+  return CPR == 16 ? (c ^ (r & 15)) : (c ^ ((r >> 1) & 7));
+}
+
+// the SUB routed rows of sub-tile u (uniform scalar loads); R marks an empty slot
+template <int SUB>
+__device__ __forceinline__ void load_ids(const int32_t* __restrict__ sorted_ids, int u,
+                                         int (&ids)[SUB]) {
+  const int32_t* sp = sorted_ids + static_cast<int64_t>(u) * SUB;
+#pragma unroll
+  for (int t = 0; t < SUB; ++t) ids[t] = sp[t];
+}
+
+// v[t] for a per-lane t in [0, N <= 64) of N wave-uniform values: lane q receives v[q]
+// (v_writelane), then the lane crossbar (ds_bpermute) reads lane t.  (A select chain
+// over constant indices gets turned into a private-memory table lookup, whose loads
+// would disturb the DMA wait counts.)
+template <int N>
+__device__ __forceinline__ int pick(const int (&v)[N], int t) {
+  static_assert(N <= kWave, "one value per lane");
+  int lanes = 0;
+#pragma unroll
+  for (int q = 0; q < N; ++q)
+    asm volatile("v_writelane_b32 %0, %1, %2" : "+v"(lanes) : "s"(v[q]), "n"(q));
+  return __shfl(lanes, t, kWave);
+}
+
+// DMA sources of one work item: RB weight rows of one expert and the SUB = 16*NTG
+// token rows of one sub-tile
+template <int MODE, int RB, int NTG, int STEP, bool NT>
+struct Stream {
+  using S = DStep<STEP>;
+  static constexpr int SUB = 16 * NTG;
+  static constexpr int NW = RB / S::RPI;        // weight DMAs per step
+  static constexpr int NX = SUB / S::RPI;       // token-row DMAs per step
+
+  // per-lane sources of an item's DMAs at k offset 0
+  static __device__ __forceinline__ void setup(const DArgs& p,
+                                               const int32_t* __restrict__ sorted_ids,
+                                               const int32_t* __restrict__ expert_ids, int item,
+                                               const uint16_t* (&wp)[NW],
+                                               const uint16_t* (&xp)[NX]) {
+    const int lane = lane_id();
+    const int u = item / p.nblk, blk = item - u * p.nblk;
+    const int e = expert_ids[(u * SUB) / p.block_m];
+    int ids[SUB];
+    load_ids<SUB>(sorted_ids, u, ids);
     const uint16_t* wb = p.A + static_cast<int64_t>(e) * p.a_expert_stride;
-    // step layout: MFMA substep c (k32 slice c of the step) takes, in lane group g, the
-    // 8 elements at c*32 + g*8, so one load instruction reads 64 contiguous bytes of each
-    // of the 16 rows (four lanes per row)
-    const uint16_t* w0 = wb + static_cast<int64_t>(wrow0) * K + g * 8;
-    const uint16_t* w1 = wb + static_cast<int64_t>(wrow1) * K + g * 8;
-
-    for (int m0 = 0; m0 < p.block_m; m0 += 16 * kMaxTG) {
-      // rows of this pass (up to 64) and how many 16-row groups hold a routed row
-      __syncthreads();
-      if (threadIdx.x < 64) {
-        const int m = m0 + threadIdx.x;
-        rows_s[threadIdx.x] = m < p.block_m ? p.sorted_ids[static_cast<int64_t>(tile) * p.block_m + m]
-                                            : p.R;
-      }
-      __syncthreads();
-      int ntg = 0;
+    const int rl = lane / S::CPR, ch = lane % S::CPR;
 #pragma unroll
-      for (int q = 0; q < kMaxTG; ++q)
-        if (rows_s[q * 16] < p.R) ntg = q + 1;   // valid rows come first in a tile
-      if (ntg == 0) break;
-
-      const uint16_t* xr[kMaxTG];
+    for (int j = 0; j < NW; ++j) {
+      const int row = j * S::RPI + rl;
+      int wrow;
+      if (MODE == 1)   // first half gate rows W1, second half the matching up rows W3
+        wrow = row < RB / 2 ? blk * (RB / 2) + row : p.I + blk * (RB / 2) + (row - RB / 2);
+      else
+        wrow = blk * RB + row;
+      wp[j] = wb + static_cast<int64_t>(wrow) * p.K + dsw<S::CPR>(row, ch) * 8;
+    }
+    // empty slots re-read the sub-tile's first row (row 0 if the whole sub-tile is
+    // padding, which happens only when block_m > SUB)
+    const int fb = ids[0] < p.R ? ids[0] : 0;
 #pragma unroll
-      for (int q = 0; q < kMaxTG; ++q) {
-        const int r = rows_s[q * 16 + row16];
-        const int xrow = r < p.R ? r / p.gather_div : 0;
-        xr[q] = p.X + static_cast<int64_t>(xrow) * K + g * 8;
-      }
-      f32x4 acc[kMaxTG][2];
-#pragma unroll
-      for (int q = 0; q < kMaxTG; ++q)
-#pragma unroll
-        for (int f = 0; f < 2; ++f) acc[q][f] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-      for (int s = w; s < nsteps; s += kDecWaves) {
-        const int k0 = s * STEP;
-        bf16x8 a0[CH], a1[CH];
-#pragma unroll
-        for (int c = 0; c < CH; ++c) {
-          a0[c] = __builtin_nontemporal_load(reinterpret_cast<const bf16x8*>(w0 + k0 + c * 32));
-          a1[c] = __builtin_nontemporal_load(reinterpret_cast<const bf16x8*>(w1 + k0 + c * 32));
-        }
-#pragma unroll
-        for (int q = 0; q < kMaxTG; ++q) {
-          if (q < ntg) {
-            bf16x8 b[CH];
-#pragma unroll
-            for (int c = 0; c < CH; ++c) b[c] = *reinterpret_cast<const bf16x8*>(xr[q] + k0 + c * 32);
-#pragma unroll
-            for (int c = 0; c < CH; ++c) {
-              acc[q][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0[c], b[c], acc[q][0], 0, 0, 0);
-              acc[q][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1[c], b[c], acc[q][1], 0, 0, 0);
-            }
-          }
-        }
-      }
-      // cross-wave reduction; wave q finishes token group q
-#pragma unroll
-      for (int q = 0; q < kMaxTG; ++q) {
-        if (q < ntg) {
-          red[w][q][0][lane] = acc[q][0];
-          red[w][q][1][lane] = acc[q][1];
-        }
-      }
-      __syncthreads();
-      if (w < ntg) {
-        const int q = w;
-        f32x4 s0 = red[0][q][0][lane], s1 = red[0][q][1][lane];
-#pragma unroll
-        for (int ww = 1; ww < kDecWaves; ++ww) {
-          const f32x4 o0 = red[ww][q][0][lane], o1 = red[ww][q][1][lane];
-#pragma unroll
-          for (int v = 0; v < 4; ++v) { s0[v] += o0[v]; s1[v] += o1[v]; }
-        }
-        // D layout (16x16): lane holds token column (lane & 15), weight rows 4*(lane>>4)+v
-        const int r = rows_s[q * 16 + row16];
-        if (r < p.R) {
-          if (MODE == 1) {
-            uint32_t pk[2];
-#pragma unroll
-            for (int v = 0; v < 4; v += 2) {
-              const float ga = s0[v], ua = s1[v], gb = s0[v + 1], ub = s1[v + 1];
-              pk[v / 2] = pack_bf16x2(ga / (1.f + __expf(-ga)) * ua, gb / (1.f + __expf(-gb)) * ub);
-            }
-            uint16_t* out = static_cast<uint16_t*>(p.C) + static_cast<int64_t>(r) * p.I + blk * 16 + 4 * g;
-            *reinterpret_cast<uint2*>(out) = make_uint2(pk[0], pk[1]);
-          } else {
-            const float wr = p.topk_w[r];
-            float* out = static_cast<float*>(p.C) + static_cast<int64_t>(r) * p.H + blk * 32 + 4 * g;
-            *reinterpret_cast<float4*>(out) = make_float4(wr * s0[0], wr * s0[1], wr * s0[2], wr * s0[3]);
-            *reinterpret_cast<float4*>(out + 16) = make_float4(wr * s1[0], wr * s1[1], wr * s1[2], wr * s1[3]);
-          }
-        }
-      }
+    for (int j = 0; j < NX; ++j) {
+      const int t = j * S::RPI + rl;
+      int r = pick(ids, t);
+      r = r < p.R ? r : fb;
+      const int xrow = r / p.gather_div;
+      xp[j] = p.X + static_cast<int64_t>(xrow) * p.K + dsw<S::CPR>(t & 15, ch) * 8;
     }
   }
+
+  static __device__ __forceinline__ void issue(const uint16_t* const (&wp)[NW],
+                                               const uint16_t* const (&xp)[NX], int k0,
+                                               MOE_LDS uint8_t* slot) {
+#pragma unroll
+    for (int j = 0; j < NW; ++j) {
+      if (NT) dma16_nt(wp[j] + k0, slot + j * 1024);    // weights read once
+      else dma16(wp[j] + k0, slot + j * 1024);
+    }
+#pragma unroll
+    for (int j = 0; j < NX; ++j) dma16(xp[j] + k0, slot + RB * S::ROWB + j * 1024);
+  }
+};
+
+// The routing tables are separate __restrict__ arguments: with them the compiler may
+// read the (wave-uniform) entries with scalar loads, which count on lgkmcnt and leave
+// the vmcnt accounting of the DMA ring untouched.
+template <int MODE, int RB, int NTG, int STEP, int P, bool NT>
+__global__ void __launch_bounds__(64)
+moe_decode_kernel(DArgs p, const int32_t* __restrict__ sorted_ids,
+                  const int32_t* __restrict__ expert_ids, const int32_t* __restrict__ ntpp,
+                  const float* __restrict__ topk_w) {
+  using S = DStep<STEP>;
+  using St = Stream<MODE, RB, NTG, STEP, NT>;
+  constexpr int SUB = St::SUB;
+  constexpr int NF = RB / 16;                   // 16-row weight fragments per item
+  constexpr int NI = St::NW + St::NX;           // DMAs per step
+  constexpr int SLOT = (RB + SUB) * S::ROWB;
+  static_assert(P >= 3 && (P - 2) * NI < 64, "ring depth");
+  static_assert(MODE != 1 || NF % 2 == 0, "gate/up fragment pairs");
+  __shared__ __attribute__((aligned(1024))) uint8_t ring[P * SLOT];
+
+  const int lane = lane_id();
+  const int total = *ntpp;
+  const int nitems = (total / SUB) * p.nblk;
+  if (nitems == 0) return;
+  // as many waves as give every wave the same number of items (the fewest waves that
+  // reach the smallest per-wave count): a wave streams at a bounded rate, so a tail of
+  // waves with one item more would run at a fraction of the bandwidth
+  const int per = (nitems + gridDim.x - 1) / gridDim.x;
+  const int G = per > 0 ? (nitems + per - 1) / per : 1;
+  const int first = blockIdx.x;
+  if (first >= G) return;
+  const int nsteps = p.K / STEP;
+  const int gtot = ((nitems - 1 - first) / G + 1) * nsteps;   // this wave's steps
+
+  // issue cursor: the step the next DMA batch belongs to (it stays on the last step
+  // once everything is issued, so the ring tail re-reads it into unused slots)
+  MOE_LDS uint8_t* lring = (MOE_LDS uint8_t*)ring;
+  const uint16_t* wp[St::NW];
+  const uint16_t* xp[St::NX];
+  St::setup(p, sorted_ids, expert_ids, first, wp, xp);
+  int gi = 0, iss_s = 0, iss_item = first;
+#define MOE_DECODE_ISSUE_NEXT()                                                 \
+  do {                                                                          \
+    St::issue(wp, xp, iss_s * STEP, lring + (gi % P) * SLOT);                   \
+    ++gi;                                                                       \
+    if (gi < gtot && ++iss_s == nsteps) {                                       \
+      iss_s = 0;                                                                \
+      iss_item += G;                                                            \
+      St::setup(p, sorted_ids, expert_ids, iss_item, wp, xp);                   \
+    }                                                                           \
+  } while (0)
+#pragma unroll
+  for (int q = 0; q < P - 1; ++q) MOE_DECODE_ISSUE_NEXT();
+
+  f32x4 acc[NTG][NF];
+  int cs = 0, cmp_item = first;
+  const int tr = lane & 15;
+  for (int g = 0; g < gtot; ++g) {
+    wait_vm_c<(P - 2) * NI>();                  // step g's batch has landed in LDS
+    asm volatile("" ::: "memory");
+    MOE_DECODE_ISSUE_NEXT();                    // into the slot step g-1 used
+    if (cs == 0) {
+#pragma unroll
+      for (int q = 0; q < NTG; ++q)
+#pragma unroll
+        for (int f = 0; f < NF; ++f) acc[q][f] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    const uint8_t* slot = ring + (g % P) * SLOT;
+#pragma unroll
+    for (int ks = 0; ks < S::KSUB; ++ks) {
+      const int c = ks * 4 + (lane >> 4);       // 8 k-elements of lane group lane>>4
+      bf16x8 b[NTG];
+#pragma unroll
+      for (int q = 0; q < NTG; ++q)
+        b[q] = *reinterpret_cast<const bf16x8*>(slot + (RB + 16 * q + tr) * S::ROWB +
+                                                dsw<S::CPR>(tr, c) * 16);
+#pragma unroll
+      for (int f = 0; f < NF; ++f) {
+        const int row = 16 * f + tr;
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(slot + row * S::ROWB +
+                                                          dsw<S::CPR>(row, c) * 16);
+#pragma unroll
+        for (int q = 0; q < NTG; ++q)
+          acc[q][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b[q], acc[q][f], 0, 0, 0);
+      }
+    }
+    if (++cs == nsteps) {
+      // epilogue.  D layout (16x16): lane holds token column (lane & 15), weight rows
+      // 4*(lane>>4)+v of each fragment
+      cs = 0;
+      const int u = cmp_item / p.nblk, blk = cmp_item - u * p.nblk;
+      int ids[SUB];
+      load_ids<SUB>(sorted_ids, u, ids);
+      int wts[SUB];                             // GEMM2 router weights (uniform loads)
+      if (MODE == 2) {
+#pragma unroll
+        for (int t = 0; t < SUB; ++t) wts[t] = __float_as_int(topk_w[ids[t] < p.R ? ids[t] : 0]);
+      }
+#pragma unroll
+      for (int q = 0; q < NTG; ++q) {
+        const int r = pick(ids, 16 * q + tr);
+        const float wr = MODE == 2 ? __int_as_float(pick(wts, 16 * q + tr)) : 0.f;
+        if (r < p.R) {
+          if (MODE == 1) {
+#pragma unroll
+            for (int f = 0; f < NF / 2; ++f) {
+              const f32x4 gt = acc[q][f], up = acc[q][f + NF / 2];
+              uint32_t pk[2];
+#pragma unroll
+              for (int v = 0; v < 4; v += 2)
+                pk[v / 2] = pack_bf16x2(gt[v] / (1.f + __expf(-gt[v])) * up[v],
+                                        gt[v + 1] / (1.f + __expf(-gt[v + 1])) * up[v + 1]);
+              uint16_t* out = static_cast<uint16_t*>(p.C) + static_cast<int64_t>(r) * p.I +
+                              blk * (RB / 2) + 16 * f + 4 * (lane >> 4);
+              *reinterpret_cast<uint2*>(out) = make_uint2(pk[0], pk[1]);
+            }
+          } else {
+#pragma unroll
+            for (int f = 0; f < NF; ++f) {
+              float* out = static_cast<float*>(p.C) + static_cast<int64_t>(r) * p.H +
+                           blk * RB + 16 * f + 4 * (lane >> 4);
+              *reinterpret_cast<float4*>(out) = make_float4(
+                  wr * acc[q][f][0], wr * acc[q][f][1], wr * acc[q][f][2], wr * acc[q][f][3]);
+            }
+          }
+        }
+      }
+      cmp_item += G;
+    }
+  }
+  wait_vm_c<0>();                                // no DMA may land after the wave exits
+#undef MOE_DECODE_ISSUE_NEXT
+}
+
+constexpr int kDecodeRB = 64;   // weight rows per work item
+
+int decode_ntg(int block_m, int R, int E) {
+  // 32-row sub-tiles once experts average several rows (fewer weight re-reads by the
+  // sub-tiles of one expert); never more than one align tile
+  const int want = R >= 4 * E ? 2 : 1;
+  return std::min(want, block_m / 16);
+}
+
+template <int MODE, int NTG, int STEP, bool NT>
+hipError_t launch_decode(const DArgs& p, const GemmArgs& g, hipStream_t s) {
+  constexpr int P = NTG == 1 ? 4 : 3;
+  constexpr int kLds = P * (kDecodeRB + 16 * NTG) * DStep<STEP>::ROWB;
+  constexpr int kPerCU = std::max(1, (160 * 1024) / kLds);
+  const int64_t max_items = (g.cap / (16 * NTG)) * p.nblk;
+  const unsigned grid = static_cast<unsigned>(std::min<int64_t>(max_items, 256 * kPerCU));
+  hipLaunchKernelGGL((moe_decode_kernel<MODE, kDecodeRB, NTG, STEP, P, NT>), dim3(grid), dim3(64),
+                     0, s, p, g.sorted_ids, g.expert_ids, g.ntpp, g.topk_w);
+  return hipGetLastError();
 }
 
 template <int MODE>
@@ -169,10 +296,6 @@ hipError_t run_decode(const GemmArgs& g, hipStream_t s) {
   p.A = static_cast<const uint16_t*>(g.B);
   p.X = static_cast<const uint16_t*>(g.A);
   p.C = g.C;
-  p.topk_w = g.topk_w;
-  p.sorted_ids = g.sorted_ids;
-  p.expert_ids = g.expert_ids;
-  p.ntpp = g.ntpp;
   p.R = g.T * g.k;
   p.gather_div = g1 ? g.k : 1;
   p.K = g1 ? g.H : g.I;
@@ -180,18 +303,27 @@ hipError_t run_decode(const GemmArgs& g, hipStream_t s) {
   p.H = g.H;
   p.a_expert_stride = g1 ? static_cast<int64_t>(2) * g.I * g.H : static_cast<int64_t>(g.H) * g.I;
   p.block_m = g.block_m;
-  p.nblk = g1 ? g.I / 16 : g.H / 32;
-  const int64_t max_items = (g.cap / g.block_m) * p.nblk;
-  if (max_items == 0) return hipSuccess;
-  const unsigned grid = static_cast<unsigned>(std::min<int64_t>(max_items, 256 * 8));
-  if (p.K % 128 == 0)
-    hipLaunchKernelGGL((moe_decode_kernel<MODE, 4>), dim3(grid), dim3(256), 0, s, p);
-  else
-    hipLaunchKernelGGL((moe_decode_kernel<MODE, 2>), dim3(grid), dim3(256), 0, s, p);
-  return hipGetLastError();
+  const int N = g1 ? 2 * g.I : g.H;             // weight rows per expert
+  p.nblk = N / kDecodeRB;
+  if (g.cap == 0) return hipSuccess;
+  const int ntg = decode_ntg(g.block_m, p.R, g.E);
+  const bool s128 = p.K % 128 == 0;
+  if (ntg == 2)
+    return s128 ? launch_decode<MODE, 2, 128, false>(p, g, s)
+                : launch_decode<MODE, 2, 64, false>(p, g, s);
+  // non-temporal weight stream while experts average at most two routed rows, so that
+  // almost every expert block is read by a single sub-tile; otherwise the sub-tiles of
+  // one expert re-read its weights, and those re-reads should hit in L2
+  if (p.R <= 2 * g.E)
+    return s128 ? launch_decode<MODE, 1, 128, true>(p, g, s)
+                : launch_decode<MODE, 1, 64, true>(p, g, s);
+  return s128 ? launch_decode<MODE, 1, 128, false>(p, g, s)
+              : launch_decode<MODE, 1, 64, false>(p, g, s);
 }
 
 }  // namespace
+
+int decode_block_m(int R, int E) { return 16 * decode_ntg(256, R, E); }
 
 hipError_t launch_decode_gemm1(const GemmArgs& g, hipStream_t s) { return run_decode<1>(g, s); }
 hipError_t launch_decode_gemm2(const GemmArgs& g, hipStream_t s) { return run_decode<2>(g, s); }

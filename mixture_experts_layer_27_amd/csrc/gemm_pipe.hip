@@ -16,9 +16,8 @@
 #include <type_traits>
 
 #include "common.hpp"
+#include "dma.hpp"
 #include "launch.hpp"
-
-#define MOE_LDS __attribute__((address_space(3)))
 
 namespace moe {
 
@@ -104,64 +103,6 @@ __device__ __forceinline__ bool grouped_slot(int bid, int mtiles, int nblocks, b
   return mt < mtiles && nb < nblocks;
 }
 constexpr int kGroupM = 4, kGroupN = 8;
-
-// 16-byte global -> LDS DMA (global_load_lds_dwordx4): lane i writes lds_base + 16*i.
-// Issued from inline assembly so that the compiler's wait-count insertion does not treat
-// it as an LDS store that every later LDS read must wait for (which would force
-// vmcnt(0) before each stage and collapse the ring); completion of this wave's DMAs is
-// awaited explicitly with wait_vm() before the barrier that publishes a stage.
-__device__ __forceinline__ void dma16(const void* gptr, const MOE_LDS void* lds_base) {
-  const uint32_t l = __builtin_amdgcn_readfirstlane(
-      static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds_base)));   // wave-uniform
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(gptr), "s"(l) : "memory", "m0");
-}
-
-// 4-byte global -> LDS DMA used as an L2 prefetch: each lane touches one cache line;
-// the bytes land in a scratch LDS slot nobody reads.
-__device__ __forceinline__ void prefetch_line(const void* gptr, const MOE_LDS void* lds_base) {
-  const uint32_t l = __builtin_amdgcn_readfirstlane(
-      static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds_base)));
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" : : "v"(gptr), "s"(l) : "memory", "m0");
-}
-
-// work-group barrier that also keeps the compiler from moving LDS accesses across it,
-// without the vmcnt(0) that __syncthreads() implies (the DMA ring stays in flight)
-__device__ __forceinline__ void barrier_keep_vm() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
-// s_waitcnt immediate for gfx9: vmcnt[3:0] | expcnt(7)<<4 | lgkmcnt(15)<<8 | vmcnt[5:4]<<14
-#define MOE_VMW(N) __builtin_amdgcn_s_waitcnt(((N) & 15) | (7 << 4) | (15 << 8) | (((N) >> 4) << 14))
-// wait until at most n of this wave's vector-memory ops are outstanding
-__device__ __forceinline__ void wait_vm(int n) {
-  switch (n) {
-    case 0: MOE_VMW(0); break;
-    case 1: MOE_VMW(1); break;
-    case 2: MOE_VMW(2); break;
-    case 3: MOE_VMW(3); break;
-    case 4: MOE_VMW(4); break;
-    case 5: MOE_VMW(5); break;
-    case 6: MOE_VMW(6); break;
-    case 7: MOE_VMW(7); break;
-    case 8: MOE_VMW(8); break;
-    case 10: MOE_VMW(10); break;
-    case 12: MOE_VMW(12); break;
-    case 14: MOE_VMW(14); break;
-    case 16: MOE_VMW(16); break;
-    case 20: MOE_VMW(20); break;
-    case 24: MOE_VMW(24); break;
-    case 32: MOE_VMW(32); break;
-    default: MOE_VMW(0); break;      // conservative: everything done
-  }
-}
-
-template <int N>
-__device__ __forceinline__ void wait_vm_c() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
-}
 
 template <int MODE, int BM, int BN, int WM, int WN, int BK, int NSTAGE, int PFD>
 __global__ void __launch_bounds__(WM * WN * 64)

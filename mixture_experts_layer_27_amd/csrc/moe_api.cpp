@@ -109,7 +109,8 @@ int auto_variant(int T, int H, int I, int E, int k, moe_dtype dt) {
 
 int preferred_bm(int T, int H, int I, int E, int k, moe_dtype dt) {
   if (dt != MOE_BF16) return 16;
-  if (auto_variant(T, H, I, E, k, dt) == MOE_VARIANT_DECODE) return 64;
+  if (auto_variant(T, H, I, E, k, dt) == MOE_VARIANT_DECODE)
+    return moe::decode_block_m(static_cast<int>(static_cast<int64_t>(T) * k), E);
   // 256-row MFMA tiles once the average expert fills several of them (the padding of
   // each expert's last tile is then a small fraction); 128-row tiles otherwise
   const int64_t avg = static_cast<int64_t>(T) * k / E;
@@ -135,6 +136,8 @@ moe_status check_gemm_common(int T, int H, int I, int E, int k, int block_m, int
     const int v = resolve_variant(variant, T, H, I, E, k, static_cast<moe_dtype>(dt));
     if (v == MOE_VARIANT_PREFILL && moe::prefill_tile_m(block_m) == 0)
       return fail(MOE_ERR_UNSUPPORTED, "bf16 prefill tiles need block_m >= 32 (got %d)", block_m);
+    if (v == MOE_VARIANT_DECODE && block_m < 16)
+      return fail(MOE_ERR_UNSUPPORTED, "bf16 decode tiles need block_m >= 16 (got %d)", block_m);
   }
   if (static_cast<int64_t>(T) * k * std::max(H, I) >= (int64_t(1) << 40))
     return fail(MOE_ERR_UNSUPPORTED, "tensor too large");

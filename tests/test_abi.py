@@ -132,6 +132,7 @@ def test_forward_validation(L):
                  a["bm"], a["dt"], a["var"], FAKE, FAKE, a["ws"], None)
 
     assert call(bm=16, var=1) == UNSUPPORTED   # bf16 MFMA prefill tiles need block_m >= 32
+    assert call(bm=8, var=2) == UNSUPPORTED    # bf16 decode sub-tiles are 16 rows
     assert call(bm=48) == INVALID
     assert call(I=96) == UNSUPPORTED           # bf16 needs I % 64 == 0
     assert call(dt=5) == INVALID

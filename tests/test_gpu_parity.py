@@ -216,7 +216,8 @@ BF16_SHAPES = [
 
 
 @pytest.mark.parametrize("shape", BF16_SHAPES)
-@pytest.mark.parametrize("bm,variant", [(32, 1), (64, 1), (128, 1), (256, 1), (32, 2), (64, 2)])
+@pytest.mark.parametrize("bm,variant", [(32, 1), (64, 1), (128, 1), (256, 1), (16, 2), (32, 2),
+                                        (64, 2)])
 def test_forward_bf16(lib, shape, bm, variant):
     T, H, I, E, k, mode, skew = shape
     g = torch.Generator(device="cpu").manual_seed(T * 7 + H + I + E)
