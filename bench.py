@@ -47,7 +47,7 @@ def parse():
     return ap.parse_args()
 
 
-KERNEL_SOURCES = ("gemm_pipe.hip", "decode.hip", "gemm.hip", "common.hpp")
+KERNEL_SOURCES = ("gemm_pipe.hip", "decode.hip", "gemm.hip", "common.hpp", "dma.hpp")
 
 
 def kernel_digest() -> str:
