@@ -45,27 +45,24 @@ __device__ __forceinline__ void barrier_keep_vm() {
 
 // s_waitcnt immediate for gfx9: vmcnt[3:0] | expcnt(7)<<4 | lgkmcnt(15)<<8 | vmcnt[5:4]<<14
 #define MOE_VMW(N) __builtin_amdgcn_s_waitcnt(((N) & 15) | (7 << 4) | (15 << 8) | (((N) >> 4) << 14))
-// wait until at most n of this wave's vector-memory ops are outstanding
+// wait until at most n of this wave's vector-memory ops are outstanding (n in [0, 48];
+// larger values wait for everything, which is always correct)
 __device__ __forceinline__ void wait_vm(int n) {
+#define MOE_VMW_CASE(N) case N: MOE_VMW(N); break;
   switch (n) {
-    case 0: MOE_VMW(0); break;
-    case 1: MOE_VMW(1); break;
-    case 2: MOE_VMW(2); break;
-    case 3: MOE_VMW(3); break;
-    case 4: MOE_VMW(4); break;
-    case 5: MOE_VMW(5); break;
-    case 6: MOE_VMW(6); break;
-    case 7: MOE_VMW(7); break;
-    case 8: MOE_VMW(8); break;
-    case 10: MOE_VMW(10); break;
-    case 12: MOE_VMW(12); break;
-    case 14: MOE_VMW(14); break;
-    case 16: MOE_VMW(16); break;
-    case 20: MOE_VMW(20); break;
-    case 24: MOE_VMW(24); break;
-    case 32: MOE_VMW(32); break;
+    MOE_VMW_CASE(0) MOE_VMW_CASE(1) MOE_VMW_CASE(2) MOE_VMW_CASE(3) MOE_VMW_CASE(4)
+    MOE_VMW_CASE(5) MOE_VMW_CASE(6) MOE_VMW_CASE(7) MOE_VMW_CASE(8) MOE_VMW_CASE(9)
+    MOE_VMW_CASE(10) MOE_VMW_CASE(11) MOE_VMW_CASE(12) MOE_VMW_CASE(13) MOE_VMW_CASE(14)
+    MOE_VMW_CASE(15) MOE_VMW_CASE(16) MOE_VMW_CASE(17) MOE_VMW_CASE(18) MOE_VMW_CASE(19)
+    MOE_VMW_CASE(20) MOE_VMW_CASE(21) MOE_VMW_CASE(22) MOE_VMW_CASE(23) MOE_VMW_CASE(24)
+    MOE_VMW_CASE(25) MOE_VMW_CASE(26) MOE_VMW_CASE(27) MOE_VMW_CASE(28) MOE_VMW_CASE(29)
+    MOE_VMW_CASE(30) MOE_VMW_CASE(31) MOE_VMW_CASE(32) MOE_VMW_CASE(33) MOE_VMW_CASE(34)
+    MOE_VMW_CASE(35) MOE_VMW_CASE(36) MOE_VMW_CASE(37) MOE_VMW_CASE(38) MOE_VMW_CASE(39)
+    MOE_VMW_CASE(40) MOE_VMW_CASE(41) MOE_VMW_CASE(42) MOE_VMW_CASE(43) MOE_VMW_CASE(44)
+    MOE_VMW_CASE(45) MOE_VMW_CASE(46) MOE_VMW_CASE(47) MOE_VMW_CASE(48)
     default: MOE_VMW(0); break;      // conservative: everything done
   }
+#undef MOE_VMW_CASE
 }
 
 template <int N>

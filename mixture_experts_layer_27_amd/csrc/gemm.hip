@@ -20,6 +20,8 @@
 // each XCD (work-groups are dealt round-robin over 8 XCDs) receives a contiguous
 // range of slots, m-tile fastest: the tiles that share an expert's weight block run
 // at the same time on the same XCD and share its L2.
+#include <algorithm>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -265,6 +267,39 @@ gemm2_f32_kernel(const float* __restrict__ a, const float* __restrict__ w2,
 }
 
 // ------------------------------------------------------------------ combine
+// out[t, h] = sum_j y[t*k + j, h] in slot order, one rounding.
+// Vector path: 8 consecutive h per thread (two 16-byte loads per source row, one 16-byte
+// bf16 or two 16-byte fp32 stores), token rows on grid.y.
+template <bool BF16>
+__global__ void __launch_bounds__(256)
+combine_vec_kernel(const float* __restrict__ y, int T, int H, int k, void* __restrict__ out) {
+  const int h0 = (blockIdx.x * 256 + threadIdx.x) * 8;
+  if (h0 >= H) return;
+  for (int t = blockIdx.y; t < T; t += gridDim.y) {
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < k; ++j) {
+      const float* row = y + (static_cast<int64_t>(t) * k + j) * H + h0;
+      const float4 a = *reinterpret_cast<const float4*>(row);
+      const float4 b = *reinterpret_cast<const float4*>(row + 4);
+      acc[0] += a.x; acc[1] += a.y; acc[2] += a.z; acc[3] += a.w;
+      acc[4] += b.x; acc[5] += b.y; acc[6] += b.z; acc[7] += b.w;
+    }
+    if (BF16) {
+      u32x4 v;
+      v[0] = pack_bf16x2(acc[0], acc[1]);
+      v[1] = pack_bf16x2(acc[2], acc[3]);
+      v[2] = pack_bf16x2(acc[4], acc[5]);
+      v[3] = pack_bf16x2(acc[6], acc[7]);
+      *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(out) + static_cast<int64_t>(t) * H + h0) = v;
+    } else {
+      float* o = static_cast<float*>(out) + static_cast<int64_t>(t) * H + h0;
+      *reinterpret_cast<float4*>(o) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+      *reinterpret_cast<float4*>(o + 4) = make_float4(acc[4], acc[5], acc[6], acc[7]);
+    }
+  }
+}
+
+// any H or alignment: one element per thread
 template <bool BF16>
 __global__ void __launch_bounds__(256)
 combine_kernel(const float* __restrict__ y, int T, int H, int k, void* __restrict__ out) {
@@ -351,6 +386,15 @@ hipError_t launch_combine(const float* y, int T, int H, int k, bool bf16, void* 
                           hipStream_t s) {
   const int64_t n = static_cast<int64_t>(T) * H;
   if (n == 0) return hipSuccess;
+  const bool vec = H % 8 == 0 && (reinterpret_cast<uintptr_t>(y) & 15) == 0 &&
+                   (reinterpret_cast<uintptr_t>(out) & 15) == 0;
+  if (vec) {
+    const dim3 grid(static_cast<unsigned>((H / 8 + 255) / 256),
+                    static_cast<unsigned>(std::min(T, 65535)));
+    if (bf16) hipLaunchKernelGGL(combine_vec_kernel<true>, grid, dim3(256), 0, s, y, T, H, k, out);
+    else hipLaunchKernelGGL(combine_vec_kernel<false>, grid, dim3(256), 0, s, y, T, H, k, out);
+    return hipGetLastError();
+  }
   const dim3 grid(static_cast<unsigned>((n + 255) / 256));
   if (bf16) hipLaunchKernelGGL(combine_kernel<true>, grid, dim3(256), 0, s, y, T, H, k, out);
   else hipLaunchKernelGGL(combine_kernel<false>, grid, dim3(256), 0, s, y, T, H, k, out);

@@ -110,6 +110,7 @@ moe_gemm_pipe_kernel(PArgs p) {
   using C = PCfg<MODE, BM, BN, WM, WN, BK, NSTAGE>;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[NSTAGE * C::STAGE];
   __shared__ int srow[BM];
+  __shared__ float swt[MODE == 2 ? BM : 1];       // GEMM2: router weight of each tile row
   __shared__ __attribute__((aligned(256))) uint8_t pf_sink[PFD > 0 ? 256 : 4];
 
   int mt, nb;
@@ -121,8 +122,13 @@ moe_gemm_pipe_kernel(PArgs p) {
   const int tid = threadIdx.x, lane = lane_id(), w = wave_id();
   const int K = p.K;
 
-  // rows of the tile (sentinels read row 0 and are never stored)
-  for (int m = tid; m < BM; m += C::NT) srow[m] = p.sorted_ids[static_cast<int64_t>(mt) * BM + m];
+  // rows of the tile (sentinels read row 0 and are never stored); GEMM2 also stages the
+  // router weights here, so its epilogue issues no dependent global loads
+  for (int m = tid; m < BM; m += C::NT) {
+    const int r = p.sorted_ids[static_cast<int64_t>(mt) * BM + m];
+    srow[m] = r;
+    if (MODE == 2) swt[m] = r < p.R ? p.topk_w[r] : 0.f;
+  }
   __syncthreads();
 
   // DMA sources: instruction j of wave w fills tile rows RPI*(w + NW*j) .. +RPI (1 KB);
@@ -353,7 +359,7 @@ moe_gemm_pipe_kernel(PArgs p) {
         const int m = wm * C::WTM + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
         const int r = srow[m];
         if (r >= p.R) continue;
-        const float wr = p.topk_w[r];
+        const float wr = swt[m];
 #pragma unroll
         for (int j = 0; j < C::FN; ++j) {
           const int col = nb * BN + wn * C::WTN + j * 32 + (lane & 31);

@@ -56,6 +56,7 @@ hipError_t launch_gemm2(const GemmArgs& g, bool bf16, int variant, hipStream_t s
 hipError_t launch_combine(const float* y, int T, int H, int k, bool bf16, void* out,
                           hipStream_t s);
 
+
 // small-M weight-streaming variant (decode.hip); block_m >= 16.  decode_block_m: the
 // block_m whose tiles match the kernel's sub-tile height for R routed rows over E experts
 int decode_block_m(int R, int E);

@@ -389,15 +389,22 @@ hipError_t launch_router_logits(const void* x, const void* wg, int T, int H, int
   }
   const unsigned tb = static_cast<unsigned>((T + 15) / 16);
   const int nz = router_slabs(T, H, true);
+  const uint16_t* xb = static_cast<const uint16_t*>(x);
+  const uint16_t* wb = static_cast<const uint16_t*>(wg);
   if (T <= 64 && H % 256 == 0) {
     // decode: 16 experts per work-group, each slab's K range split over 4 waves
     hipLaunchKernelGGL(router_logits_bf16_kernel<4>, dim3(tb, (E + 15) / 16, nz), dim3(256), 0,
-                       s, static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(wg), T, H,
-                       E, slab_cols(T, H), logits);
+                       s, xb, wb, T, H, E, slab_cols(T, H), logits);
+  } else if (E <= 16) {
+    // few experts: one 16-expert block per work-group, K split over its 4 waves
+    hipLaunchKernelGGL(router_logits_bf16_kernel<4>, dim3(tb, 1, 1), dim3(256), 0, s, xb, wb, T,
+                       H, E, H, logits);
+  } else if (E <= 32) {
+    hipLaunchKernelGGL(router_logits_bf16_kernel<2>, dim3(tb, 1, 1), dim3(256), 0, s, xb, wb, T,
+                       H, E, H, logits);
   } else {
     hipLaunchKernelGGL(router_logits_bf16_kernel<1>, dim3(tb, (E + 63) / 64, 1), dim3(256), 0, s,
-                       static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(wg), T, H,
-                       E, H, logits);
+                       xb, wb, T, H, E, H, logits);
   }
   return hipGetLastError();
 }

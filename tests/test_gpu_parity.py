@@ -119,7 +119,9 @@ def test_route_grouped_page_example(lib):
 
 @pytest.mark.parametrize("T,H,E,k,mode", [(300, 512, 8, 2, 0), (64, 1024, 128, 8, 0),
                                           (16, 7168 // 4, 256, 8, 2), (1, 2048, 256, 8, 2),
-                                          (200, 2880, 128, 4, 1)])
+                                          (200, 2880, 128, 4, 1),
+                                          # few experts: K split over the waves of a block
+                                          (100, 640, 24, 4, 0), (90, 320, 16, 2, 1)])
 def test_route_fused_logits(lib, T, H, E, k, mode):
     """moe_route: fp32-accumulated logits within their error bound of the float64 ones;
     ids identical to the oracle's on every token whose selection margin exceeds twice that
@@ -176,18 +178,23 @@ def _forward_case(lib, x, wg, w13, w2, k, mode, bm, variant, offset=None, bias=N
     lib.moe_gemm2_weighted(a, d2, dw, sorted_ids, expert_ids, ntpp, T, k, bm, variant, y=y)
     out = lib.moe_combine(y, T, k, x.dtype)
     out_fwd = lib.moe_forward(dx, d13, d2, dw, sorted_ids, expert_ids, ntpp, k, bm, variant)
+    out_fwd2 = lib.moe_forward(dx, d13, d2, dw, sorted_ids, expert_ids, ntpp, k, bm, variant)
     _sync()
     if check_rows:
         assert not torch.isnan(a[:R]).any() and not torch.isnan(y[:R]).any()
         assert torch.isnan(a[R:]).all() and torch.isnan(y[R:]).all()     # nothing past row R
+    # moe_forward is deterministic and runs the same kernels as the single calls
+    assert torch.equal(out_fwd, out_fwd2)
     assert torch.equal(out, out_fwd)
-    got = np64(out)
-    if dt_bf16:
-        r = bf16_tol_check(got, ref)
-        # the GPU mirrors the oracle's rounding points: errors are ~ one bf16 ulp of out
-        assert np.mean(np.abs(got - ref)) / np.sqrt(np.mean(ref ** 2)) < 2e-3
-        return r
-    return f32_tol_check(got, ref)
+    for o in (out, out_fwd):
+        got = np64(o)
+        if dt_bf16:
+            r = bf16_tol_check(got, ref)
+            # the GPU mirrors the oracle's rounding points: errors are ~ one bf16 ulp of out
+            assert np.mean(np.abs(got - ref)) / np.sqrt(np.mean(ref ** 2)) < 2e-3
+        else:
+            r = f32_tol_check(got, ref)
+    return r
 
 
 def test_forward_fp32_tiny_layer(lib):
