@@ -329,8 +329,29 @@ route_align_small_kernel(TopkParams p, int bm, int64_t cap, int32_t* __restrict_
                          int32_t* __restrict__ counts) {
   __shared__ TopkLds sh[16];
   __shared__ int32_t ids_lds[kFusedMaxRows];
+  __shared__ float lg[kFusedMaxT * 4 * kWave];   // summed logits [T][E], E <= 256
   const int w = wave_id();
-  for (int t = w; t < p.T; t += 16) topk_token<NSLOT, 28 / NSLOT>(p, t, sh[w], ids_lds);
+  // every thread sums the K slabs of some (token, expert) pairs, all slab loads in flight
+  // at once (slabs added in ascending order, as in the one-wave path), so the per-token
+  // selection below reads its logits from LDS instead of waiting on global round trips
+  const int TE = p.T * p.E;
+  const int64_t slab = static_cast<int64_t>(TE);
+  for (int i = threadIdx.x; i < TE; i += blockDim.x) {
+    float part[kMaxSlabs];
+#pragma unroll
+    for (int z = 0; z < kMaxSlabs; ++z) part[z] = p.logits[min(z, p.nz - 1) * slab + i];
+    float l = part[0];
+#pragma unroll
+    for (int z = 1; z < kMaxSlabs; ++z) l = z < p.nz ? l + part[z] : l;
+    lg[i] = l;
+    if (p.logits_out) p.logits_out[i] = l;
+  }
+  __syncthreads();
+  TopkParams q = p;
+  q.logits = lg;
+  q.nz = 1;
+  q.logits_out = nullptr;
+  for (int t = w; t < p.T; t += 16) topk_token<NSLOT, 1>(q, t, sh[w], ids_lds);
   __syncthreads();
   alignd::align_small_body(ids_lds, p.T * p.k, p.E, bm, cap, sorted_ids, expert_ids, ntpp,
                            counts);
