@@ -32,6 +32,13 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
 }
 
+// SiLU(g) * u for the bf16 SwiGLU epilogues: x * (1 / (1 + e^-x)) with the hardware
+// reciprocal (v_rcp_f32, about 1 ulp), ample for a result rounded to bf16 next.
+// e^-x overflowing to +inf gives rcp = 0 and SiLU = -0 for large negative x.
+__device__ __forceinline__ float silu_mul_bf16path(float g, float u) {
+  return g * __builtin_amdgcn_rcpf(1.f + __expf(-g)) * u;
+}
+
 // Orders LDS traffic between the lanes of one wave (no work-group barrier).
 __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");

@@ -244,8 +244,8 @@ moe_decode_kernel(DArgs p, const int32_t* __restrict__ sorted_ids,
               uint32_t pk[2];
 #pragma unroll
               for (int v = 0; v < 4; v += 2)
-                pk[v / 2] = pack_bf16x2(gt[v] / (1.f + __expf(-gt[v])) * up[v],
-                                        gt[v + 1] / (1.f + __expf(-gt[v + 1])) * up[v + 1]);
+                pk[v / 2] = pack_bf16x2(silu_mul_bf16path(gt[v], up[v]),
+                                        silu_mul_bf16path(gt[v + 1], up[v + 1]));
               uint16_t* out = static_cast<uint16_t*>(p.C) + static_cast<int64_t>(r) * p.I +
                               blk * (RB / 2) + 16 * f + 4 * (lane >> 4);
               *reinterpret_cast<uint2*>(out) = make_uint2(pk[0], pk[1]);

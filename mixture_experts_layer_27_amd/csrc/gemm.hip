@@ -196,7 +196,7 @@ moe_gemm_bf16_kernel(KArgs p) {
           const int r = srow[m];
           if (r >= p.R) continue;
           const float g = acc[i][2 * q][v], u = acc[i][2 * q + 1][v];
-          const float a = g / (1.f + __expf(-g)) * u;
+          const float a = silu_mul_bf16path(g, u);
           out[static_cast<int64_t>(r) * p.N + col] = f32_to_bf16(a);
         }
       }

@@ -335,7 +335,7 @@ moe_gemm_pipe_kernel(PArgs p) {
         for (int v = 0; v < 16; ++v) {
           const int m = wm * C::WTM + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
           const float g = acc[i][2 * q][v], u = acc[i][2 * q + 1][v];
-          *reinterpret_cast<uint16_t*>(smem + m * ROWS + lc * 2) = f32_to_bf16(g / (1.f + __expf(-g)) * u);
+          *reinterpret_cast<uint16_t*>(smem + m * ROWS + lc * 2) = f32_to_bf16(silu_mul_bf16path(g, u));
         }
       }
     }
