@@ -219,6 +219,7 @@ BF16_SHAPES = [
     (64, 256, 128, 32, 4, 1, "zipf"),
     (24, 512, 256, 64, 8, 2, None),
     (1, 1024, 256, 256, 8, 2, None),
+    (5, 320, 192, 16, 4, 0, None),          # H and I = 64 mod 128: 64-column decode steps
 ]
 
 
@@ -294,6 +295,16 @@ def test_layer_reduced(lib, name, T, scale):
     base = S.WORKLOADS[name]
     wl = base.scaled(T=T, H=base.H // scale // 64 * 64 or 64, I=base.I // scale // 64 * 64 or 64)
     lay = S.make_layer(wl, device=DEV, seed=3)
+    _layer_vs_oracle(lib, wl, lay)
+
+
+@pytest.mark.parametrize("T", [8, 300])
+def test_layer_widest_routing(lib, T):
+    """E = 512 experts, k = 16 slots (the limits of the routing kernels): eight experts
+    per lane in top-k and no fused route+align at decode sizes."""
+    base = S.WORKLOADS["qwen3_balanced"]
+    wl = base.scaled(T=T, H=256, I=128, E=512, k=16)
+    lay = S.make_layer(wl, device=DEV, seed=11)
     _layer_vs_oracle(lib, wl, lay)
 
 
