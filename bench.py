@@ -2,8 +2,10 @@
 
 One step = one moe_layer call through the C ABI (route -> align -> GEMM1+SwiGLU -> GEMM2 x
 weight -> combine) over one batch of seeded synthetic input already resident in HBM, on
-the current HIP stream.  Prints ONE JSON line.  The GEMM1 launch duration for the
-roofline is taken in separate eager steps that call the stages one by one.
+the current HIP stream.  Prints ONE JSON line.  `config` also carries the spread of single
+steps (p10/p50/p90) and per-stage durations: K calls of one stage captured in one HIP graph
+whose replay is timed between HIP events; the GEMM1 duration for the roofline comes from
+there.
 
   python bench.py [--steps K] [--warmup W] [--workload mixtral|deepseek_decode|...] [--T n]
 
@@ -150,22 +152,33 @@ def main():
     stream = torch.cuda.current_stream()
     staged = args.block_m is not None
 
-    def launch_staged(i, sp, g1_events=None):
-        """route -> align -> GEMM1+SwiGLU -> GEMM2 x weight -> combine, one call each."""
+    def launch_staged(i, sp, marks=None, only=None):
+        """route -> align -> GEMM1+SwiGLU -> GEMM2 x weight -> combine, one call each; with
+        `marks` (6 events) the boundaries between the stages are recorded on the stream;
+        `only` = j runs stage j alone."""
         x = xs[i % nx]
-        m.check(lib.moe_route(P(x), P(lay.wg), T, H, E, k, dt, ctypes.byref(cfg), P(ids), P(w),
-                              None, P(rws), rws.numel(), sp), "route")
-        m.check(lib.moe_align(P(ids), T, k, E, bm, P(sorted_ids), P(expert_ids), P(ntpp), P(counts),
-                              P(aws), aws.numel(), sp), "align")
-        if g1_events:
-            g1_events[0].record(torch.cuda.current_stream())
-        m.check(lib.moe_gemm1_swiglu(P(x), P(lay.w13), P(sorted_ids), P(expert_ids), P(ntpp), T, H, I,
-                                     E, k, bm, dt, variant, P(a), sp), "gemm1")
-        if g1_events:
-            g1_events[1].record(torch.cuda.current_stream())
-        m.check(lib.moe_gemm2_weighted(P(a), P(lay.w2), P(w), P(sorted_ids), P(expert_ids), P(ntpp),
-                                       T, H, I, E, k, bm, dt, variant, P(y), sp), "gemm2")
-        m.check(lib.moe_combine(P(y), T, H, k, dt, P(out), sp), "combine")
+        mark = (lambda j: marks[j].record(torch.cuda.current_stream())) if marks else (lambda j: None)
+        run = lambda j: only is None or only == j
+        mark(0)
+        if run(0):
+            m.check(lib.moe_route(P(x), P(lay.wg), T, H, E, k, dt, ctypes.byref(cfg), P(ids), P(w),
+                                  None, P(rws), rws.numel(), sp), "route")
+        mark(1)
+        if run(1):
+            m.check(lib.moe_align(P(ids), T, k, E, bm, P(sorted_ids), P(expert_ids), P(ntpp),
+                                  P(counts), P(aws), aws.numel(), sp), "align")
+        mark(2)
+        if run(2):
+            m.check(lib.moe_gemm1_swiglu(P(x), P(lay.w13), P(sorted_ids), P(expert_ids), P(ntpp), T,
+                                         H, I, E, k, bm, dt, variant, P(a), sp), "gemm1")
+        mark(3)
+        if run(3):
+            m.check(lib.moe_gemm2_weighted(P(a), P(lay.w2), P(w), P(sorted_ids), P(expert_ids),
+                                           P(ntpp), T, H, I, E, k, bm, dt, variant, P(y), sp), "gemm2")
+        mark(4)
+        if run(4):
+            m.check(lib.moe_combine(P(y), T, H, k, dt, P(out), sp), "combine")
+        mark(5)
 
     def launch(i, sp):
         """One step: the whole layer in one library call."""
@@ -216,13 +229,52 @@ def main():
     torch.cuda.synchronize()
     ms = t_start.elapsed_time(t_end) / args.steps
 
-    # GEMM1 launch duration: HIP events bracketing the kernel on its own stream, K eager steps
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(args.steps)]
+    # spread of single steps (one event pair per replay, same work as above)
+    per = []
     for i in range(args.steps):
-        launch_staged(i, cur_sp(), ev[i])
+        a_ev, b_ev = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a_ev.record(stream)
+        if graphs:
+            graphs[i % nx].replay()
+        else:
+            launch(i, cur_sp())
+        b_ev.record(stream)
+        per.append((a_ev, b_ev))
     torch.cuda.synchronize()
-    g1_ms = sum(s_.elapsed_time(e_) for s_, e_ in ev) / args.steps
+    per_ms = sorted(a_.elapsed_time(b_) for a_, b_ in per)
+    pct = lambda q: per_ms[min(len(per_ms) - 1, int(round(q * (len(per_ms) - 1))))]
+
+    # per-stage durations (GEMM1 among them): K calls of one stage captured back to back in
+    # one HIP graph, one replay timed between two HIP events on the replay stream, so that
+    # neither host nor graph launch latency enters (the stages read what the previous full
+    # step left in the buffers)
+    stage_names = ("route", "align", "gemm1", "gemm2", "combine")
+    stages_ms = {}
+    if args.eager:
+        marks = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+        for i in range(args.steps):
+            launch_staged(i, cur_sp(), marks[i])
+        torch.cuda.synchronize()
+        for j, nm in enumerate(stage_names):
+            stages_ms[nm] = sum(mk[j].elapsed_time(mk[j + 1]) for mk in marks) / args.steps
+    else:
+        launch_staged(0, cur_sp())
+        torch.cuda.synchronize()
+        for j, nm in enumerate(stage_names):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=cs):
+                for _ in range(args.steps):
+                    launch_staged(0, cur_sp(), only=j)
+            g.replay()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record(stream)
+            g.replay()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            stages_ms[nm] = e0.elapsed_time(e1) / args.steps
+            del g
+    g1_ms = stages_ms["gemm1"]
     flops = wl.flops
     g1_flops = 2 * R * 2 * I * H
     decode = T <= 256
@@ -254,6 +306,10 @@ def main():
                       "route_mode": wl.mode, "block_m": bm, "variant": variant,
                       "timing": "eager" if args.eager else "hip-graph replay",
                       "step": "stage-by-stage calls" if staged else "moe_layer",
+                      "step_ms_p10_p50_p90": [pct(0.1), pct(0.5), pct(0.9)],
+                      "stages_ms": {nm: round(v, 4) for nm, v in stages_ms.items()},
+                      "route_align_combine_share": (stages_ms["route"] + stages_ms["align"] +
+                                                    stages_ms["combine"]) / sum(stages_ms.values()),
                       "parallelism": "single-gpu"},
            "roofline": roof}
     if decode:
