@@ -39,7 +39,12 @@ Readings where the pages leave a step open (each also listed in the design doc):
 5. sentinel = T*k; buffer tails past the padded total hold the sentinel in
    sorted_ids and -1 in expert_ids;
 6. for bf16 layers the SwiGLU activation a (GEMM2's input) is rounded to bf16
-   (round-to-nearest-even); all other intermediates stay in float64 here.
+   (round-to-nearest-even); all other intermediates stay in float64 here;
+7. "FP8 weights" ([MKR] section 8 prices an expert's weights at one byte per
+   element; section 9 lists FP8 weight variants of the fused kernel) are read as
+   the OCP 8-bit E4M3 format with one float32 scale per weight row (output
+   channel) of each expert: W = decode(code) * scale[e, row].  Activations, the
+   router and the output keep the bf16 layer's types.
 """
 from __future__ import annotations
 
@@ -66,6 +71,34 @@ def bf16_round(a) -> np.ndarray:
 
 def f32(a) -> np.ndarray:
     return np.asarray(a, dtype=np.float32)
+
+
+# --------------------------------------------------------------------------- FP8 weights (reading 7)
+
+def fp8_e4m3_value(code: int) -> float:
+    """Value of one OCP E4M3 byte: sign bit, 4 exponent bits with bias 7, 3 mantissa
+    bits.  Exponent field 0 holds the subnormals m/8 * 2^-6; the all-ones exponent
+    with mantissa 7 is NaN (there is no infinity), so the largest value is 448."""
+    sign = -1.0 if code & 0x80 else 1.0
+    e = (code >> 3) & 0xF
+    m = code & 0x7
+    if e == 0xF and m == 0x7:
+        return math.nan
+    if e == 0:
+        return sign * (m / 8.0) * 2.0 ** -6
+    return sign * (1.0 + m / 8.0) * 2.0 ** (e - 7)
+
+
+def fp8_e4m3_decode(codes) -> np.ndarray:
+    """Decode an array of E4M3 bytes (any integer dtype) to float64."""
+    table = np.array([fp8_e4m3_value(c) for c in range(256)], np.float64)
+    return table[np.asarray(codes).astype(np.int64) & 0xFF]
+
+
+def dequant_rows(codes, scale) -> np.ndarray:
+    """Expert weights from E4M3 codes [E, N, K] and per-row scales [E, N]:
+    W[e, n, :] = decode(codes[e, n, :]) * scale[e, n]  (float64)."""
+    return fp8_e4m3_decode(codes) * np.asarray(scale, np.float64)[..., None]
 
 
 # --------------------------------------------------------------------------- routing ([MKR] s3, s4)
@@ -315,6 +348,17 @@ def moe_layer(x, wg, w13, w2, k, mode, offset=None, bias=None, n_group=0, topk_g
     ids, w = route(logits32, k, mode, offset, bias, n_group, topk_group, scaling)
     out = moe_loop(x, w13, w2, ids, w, round_a=round_a)
     return out, ids, w, logits32
+
+
+def moe_layer_fp8(x, wg, w13_codes, w13_scale, w2_codes, w2_scale, k, mode, offset=None,
+                  bias=None, n_group=0, topk_group=0, scaling=1.0):
+    """The bf16 layer with FP8 expert weights (reading 7): the expert weights are the
+    decoded codes times their row scales; everything else as ``moe_layer`` with the
+    SwiGLU activation rounded to bf16."""
+    w13 = dequant_rows(w13_codes, w13_scale)
+    w2 = dequant_rows(w2_codes, w2_scale)
+    return moe_layer(x, wg, w13, w2, k, mode, offset, bias, n_group, topk_group, scaling,
+                     round_a=True)
 
 
 def expert_flops(T, k, H, I) -> int:

@@ -22,6 +22,13 @@ Routing, Permutation, and Grouped GEMM", section 1):
 * ``gptoss``          T=16384, H=2880, I=2880, E=128, k=4, bf16, top-4 then softmax,
                        per-expert logit offset 0.5*ln(Zipf(s=1.2) rank weight).
 
+* ``deepseek_decode_fp8`` / ``mixtral_fp8``: the same layers with FP8 expert
+                       weights (dtype "bf16_fp8w"): each expert weight row drawn in
+                       fp32 as for bf16, divided by its scale amax(|row|)/448 and
+                       converted to OCP E4M3 by torch (round to nearest even); the
+                       codes and the fp32 scales are the inputs.  x, Wg and out stay
+                       bf16.
+
 Every floating-point input is an fp32 normal draw; bf16 workloads round it
 to bf16 (round-to-nearest-even, torch's conversion).  Weights follow
 N(0, 1/fan_in): std 1/sqrt(H) for Wg, W1, W3 and 1/sqrt(I) for W2.
@@ -48,7 +55,7 @@ class Workload:
     I: int
     E: int
     k: int
-    dtype: str                      # "f32" or "bf16"
+    dtype: str                      # "f32", "bf16" or "bf16_fp8w" (bf16, FP8 expert weights)
     mode: int
     n_group: int = 0
     topk_group: int = 0
@@ -86,10 +93,28 @@ WORKLOADS = {
                                 scaling=2.5, bias_std=math.sqrt(0.1)),
     "gptoss": Workload("gptoss", 16384, 2880, 2880, 128, 4, "bf16",
                        ROUTE_TOPK_THEN_SOFTMAX, offset="zipf"),
+    "deepseek_decode_fp8": Workload("deepseek_decode_fp8", 1, 7168, 2048, 256, 8, "bf16_fp8w",
+                                    ROUTE_SIGMOID_BIAS_GROUPED, n_group=8, topk_group=4,
+                                    scaling=2.5, bias_std=math.sqrt(0.1)),
+    "mixtral_fp8": Workload("mixtral_fp8", 4096, 4096, 14336, 8, 2, "bf16_fp8w",
+                            ROUTE_SOFTMAX_TOPK_RENORM),
 }
+
+FP8_MAX = 448.0     # largest finite OCP E4M3 value
+
+
+def quantize_fp8_rows(w: torch.Tensor):
+    """Input recipe for FP8 expert weights: per row (last dim) scale = amax/448 in fp32,
+    codes = torch's E4M3 conversion of w / scale, returned as uint8.  Returns
+    (codes uint8 [..., N, K], scale fp32 [..., N])."""
+    w = w.to(torch.float32)
+    scale = (w.abs().amax(dim=-1) / FP8_MAX).clamp_min(2.0 ** -120)
+    codes = (w / scale[..., None]).to(torch.float8_e4m3fn).view(torch.uint8)
+    return codes, scale
 
 
 def _torch_dtype(dt: str) -> torch.dtype:
+    """Type of x, Wg and out (FP8-weight layers keep them bf16)."""
     return torch.float32 if dt == "f32" else torch.bfloat16
 
 
@@ -133,6 +158,8 @@ class Layer:
     w2: torch.Tensor         # [E, H, I]
     offset: torch.Tensor | None = None   # [E] f32
     bias: torch.Tensor | None = None     # [E] f32
+    w13_scale: torch.Tensor | None = None  # [E, 2I] f32 (FP8 weights: w13 holds uint8 codes)
+    w2_scale: torch.Tensor | None = None   # [E, H] f32 (FP8 weights: w2 holds uint8 codes)
     extra: dict = field(default_factory=dict)
 
 
@@ -157,17 +184,29 @@ def make_layer(wl: Workload, device="cpu", seed: int = 0, x_seed: int | None = N
         g = _gen(device, seed)
         x = torch.randn(T, H, generator=g, device=device).to(dt)
         wg = (torch.randn(E, H, generator=g, device=device) / math.sqrt(H)).to(dt)
-        w13 = torch.empty(E, 2 * I, H, dtype=dt, device=device)
-        w2 = torch.empty(E, H, I, dtype=dt, device=device)
+        fp8 = wl.dtype == "bf16_fp8w"
+        wdt = torch.uint8 if fp8 else dt
+        w13 = torch.empty(E, 2 * I, H, dtype=wdt, device=device)
+        w2 = torch.empty(E, H, I, dtype=wdt, device=device)
+        s13 = torch.empty(E, 2 * I, dtype=torch.float32, device=device) if fp8 else None
+        s2 = torch.empty(E, H, dtype=torch.float32, device=device) if fp8 else None
+
+        def put(dst, sdst, e, rows, w):
+            if fp8:
+                dst[e, rows], sdst[e, rows] = quantize_fp8_rows(w)
+            else:
+                dst[e, rows] = w.to(dt)
+
         # per expert, to bound the fp32 staging memory at the large shapes
         for e in range(E):
-            w13[e, :I] = (torch.randn(I, H, generator=g, device=device) / math.sqrt(H)).to(dt)
-            w13[e, I:] = (torch.randn(I, H, generator=g, device=device) / math.sqrt(H)).to(dt)
-            w2[e] = (torch.randn(H, I, generator=g, device=device) / math.sqrt(I)).to(dt)
+            put(w13, s13, e, slice(0, I), torch.randn(I, H, generator=g, device=device) / math.sqrt(H))
+            put(w13, s13, e, slice(I, 2 * I),
+                torch.randn(I, H, generator=g, device=device) / math.sqrt(H))
+            put(w2, s2, e, slice(0, H), torch.randn(H, I, generator=g, device=device) / math.sqrt(I))
         if x_seed is not None:
             gx = _gen(device, x_seed)
             x = torch.randn(T, H, generator=gx, device=device).to(dt)
-        lay = Layer(wl, x, wg, w13, w2)
+        lay = Layer(wl, x, wg, w13, w2, w13_scale=s13, w2_scale=s2)
     off = logit_offset(wl, seed)
     bias = selection_bias(wl, seed)
     lay.offset = None if off is None else off.to(device)

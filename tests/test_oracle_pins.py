@@ -389,3 +389,67 @@ def test_identical_experts_sum_of_weights():
 def test_selection_margin():
     l32 = np.array([[1.0, 0.5, 0.25, 0.0]], np.float32)
     assert O.selection_margin(l32, 2, 0)[0] == pytest.approx(0.25)
+
+
+# ----------------------------------------------------------------------------- FP8 weights
+
+def _torch_e4m3(codes):
+    """torch's own E4M3 decoding (the library routine, independent of the oracle's)."""
+    c = torch.as_tensor(np.asarray(codes, np.uint8))
+    return c.view(torch.float8_e4m3fn).to(torch.float64).numpy()
+
+
+def test_fp8_decode_all_codes_match_library():
+    codes = np.arange(256)
+    ours = O.fp8_e4m3_decode(codes)
+    ref = _torch_e4m3(codes)
+    assert np.array_equal(np.isnan(ours), np.isnan(ref))
+    fin = ~np.isnan(ref)
+    assert np.array_equal(ours[fin], ref[fin])
+    assert np.array_equal(np.signbit(ours[fin]), np.signbit(ref[fin]))
+
+
+def test_fp8_decode_closed_forms():
+    # OCP 8-bit floating point, E4M3: bias 7, no infinities, one NaN mantissa pattern
+    v = O.fp8_e4m3_value
+    assert v(0x7E) == 448.0 and v(0xFE) == -448.0              # largest finite
+    assert v(0x01) == 2.0 ** -9 and v(0x07) == 7 * 2.0 ** -9   # subnormals m/8 * 2^-6
+    assert v(0x08) == 2.0 ** -6                                # smallest normal
+    assert v(0x38) == 1.0 and v(0xB8) == -1.0 and v(0x3C) == 1.5
+    assert v(0x00) == 0.0 and math.copysign(1.0, v(0x80)) == -1.0
+    nan = [c for c in range(256) if math.isnan(v(c))]
+    assert nan == [0x7F, 0xFF]
+    pos = [v(c) for c in range(0x7F)]
+    assert all(b > a for a, b in zip(pos, pos[1:]))              # codes order the values
+    assert all(v(c | 0x80) == -v(c) for c in range(0x7F))
+
+
+def test_fp8_row_quantisation_error_bound():
+    """Decoded codes times the row scale recover each weight to E4M3's rounding bound:
+    half an ulp (2^-4 relative) in the normal range, half the subnormal step (2^-10 of
+    the scale) below it.  A scale applied along the wrong axis breaks the bound."""
+    g = torch.Generator().manual_seed(5)
+    w = torch.randn(3, 40, 24, generator=g) * torch.rand(3, 40, 1, generator=g) * 4
+    codes, scale = S.quantize_fp8_rows(w)
+    deq = O.dequant_rows(codes.numpy(), scale.numpy())
+    wn = w.double().numpy()
+    sc = scale.double().numpy()[..., None]
+    bound = np.maximum(2.0 ** -4 * np.abs(wn), 2.0 ** -10 * sc) * (1 + 1e-6) + 1e-30
+    assert np.all(np.abs(deq - wn) <= bound)
+    # the row maximum maps onto the largest code
+    assert np.all(np.abs(deq).max(axis=-1) == pytest.approx(np.abs(wn).max(axis=-1), rel=1e-6))
+
+
+def test_fp8_layer_matches_bruteforce():
+    wl = S.WORKLOADS["deepseek_decode_fp8"].scaled(T=3, H=16, I=12, E=32, n_group=8,
+                                                   topk_group=4)
+    lay = S.make_layer(wl, seed=3)
+    x = lay.x.double().numpy()
+    out, ids, w, _ = O.moe_layer_fp8(x, lay.wg.double().numpy(), lay.w13.numpy(),
+                                     lay.w13_scale.numpy(), lay.w2.numpy(), lay.w2_scale.numpy(),
+                                     wl.k, wl.mode, None, lay.bias.numpy(), wl.n_group,
+                                     wl.topk_group, wl.scaling)
+    w13 = _torch_e4m3(lay.w13.numpy()) * lay.w13_scale.double().numpy()[..., None]
+    w2 = _torch_e4m3(lay.w2.numpy()) * lay.w2_scale.double().numpy()[..., None]
+    ref = O.moe_bruteforce(x, w13, w2, ids, w, round_a=True)
+    assert np.allclose(out, ref, rtol=1e-12, atol=1e-12)
