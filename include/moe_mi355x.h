@@ -36,8 +36,17 @@
  * - Element types: MOE_BF16 means x, Wg, W13, W2 and out are bf16 and the SwiGLU
  *   activation a is stored as bf16 (it is GEMM2's input); MOE_F32 means all of
  *   them are fp32.  Accumulation is fp32 in both; logits, topk_w and y are fp32.
+ *   MOE_BF16_FP8W is MOE_BF16 with FP8 expert weights (the *_fp8 entry points):
+ *   W13 and W2 hold one OCP E4M3 byte per weight (sign, 4 exponent bits with bias
+ *   7, 3 mantissa bits; no infinities; 0x7F/0xFF are NaN) and come with fp32
+ *   per-row scales W13_scale [E,2I] and W2_scale [E,H]; the weight used is
+ *   decode(code[e,n,:]) * scale[e,n] (section 8 of the routing/grouped GEMM page
+ *   prices an expert's weights at one byte each; section 9 lists FP8 weight
+ *   variants).  The decoded values are exact in bf16, the products are accumulated
+ *   in fp32 and the row scale multiplies the accumulator.
  * - Limits: 1 <= k <= 16, k <= E <= 512, T >= 0, T*k < 2^31; for MOE_BF16, H and I
- *   are multiples of 64; x, W13, W2, out, a and y 16-byte aligned.
+ *   are multiples of 64 (128 for MOE_BF16_FP8W); x, W13, W2, out, a and y 16-byte
+ *   aligned.
  */
 #ifndef MOE_MI355X_H
 #define MOE_MI355X_H
@@ -57,7 +66,7 @@ typedef enum {
   MOE_ERR_HIP = -4            /* a HIP call failed (launch error)                     */
 } moe_status;
 
-typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_BF16_FP8W = 2 } moe_dtype;
 
 /* Routing rules ("Mixture-of-Experts Kernels: Routing, Permutation, and Grouped GEMM",
  * section 1 model table, section 3 `route`, section 4 grouped router). */
@@ -138,7 +147,8 @@ moe_status moe_align(const int32_t* topk_ids, int T, int k, int E, int block_m,
 /* Variant of the expert GEMMs: 0 = automatic (from T, k, E, H, I on the host),
  * 1 = prefill (MFMA tiles staged through LDS), 2 = decode (weight streaming, small M).
  * bf16 block_m limits: prefill >= 32, decode >= 16 (MOE_ERR_UNSUPPORTED otherwise);
- * fp32 takes any block_m. */
+ * fp32 takes any block_m.  FP8 weights run on the decode variant (block_m >= 16) at
+ * every T: automatic resolves to it and prefill is MOE_ERR_UNSUPPORTED. */
 enum { MOE_VARIANT_AUTO = 0, MOE_VARIANT_PREFILL = 1, MOE_VARIANT_DECODE = 2 };
 
 /* block_m that moe_forward's automatic variant wants moe_align to use. */
@@ -160,6 +170,20 @@ moe_status moe_gemm2_weighted(const void* a, const void* w2, const float* topk_w
                               int E, int k, int block_m, moe_dtype dt, int variant, float* y,
                               void* stream);
 
+/* The same two GEMMs with FP8 expert weights (dtype MOE_BF16_FP8W: x and a bf16).
+ * w13 / w2: E4M3 bytes [E,2I,H] / [E,H,I]; w13_scale [E,2I], w2_scale [E,H] fp32
+ * (device, 4-byte aligned; a NULL scale is MOE_ERR_INVALID_ARG).  block_m >= 16. */
+moe_status moe_gemm1_swiglu_fp8(const void* x, const uint8_t* w13, const float* w13_scale,
+                                const int32_t* sorted_ids, const int32_t* expert_ids,
+                                const int32_t* num_tokens_post_padded, int T, int H, int I,
+                                int E, int k, int block_m, int variant, void* a, void* stream);
+moe_status moe_gemm2_weighted_fp8(const void* a, const uint8_t* w2, const float* w2_scale,
+                                  const float* topk_w, const int32_t* sorted_ids,
+                                  const int32_t* expert_ids,
+                                  const int32_t* num_tokens_post_padded, int T, int H, int I,
+                                  int E, int k, int block_m, int variant, float* y,
+                                  void* stream);
+
 /* Combine: out[t, :] = sum_{j<k} y[t*k + j, :] in slot order (fp32), rounded once to
  * dt.  Every routed row of y must have been written. */
 moe_status moe_combine(const float* y, int T, int H, int k, moe_dtype dt, void* out,
@@ -174,6 +198,15 @@ moe_status moe_forward(const void* x, const void* w13, const void* w2, const flo
                        int k, int block_m, moe_dtype dt, int variant, void* out, void* ws,
                        size_t ws_bytes, void* stream);
 
+/* moe_forward with FP8 expert weights (workspace: moe_forward_workspace_size with
+ * MOE_BF16_FP8W). */
+moe_status moe_forward_fp8(const void* x, const uint8_t* w13, const float* w13_scale,
+                           const uint8_t* w2, const float* w2_scale, const float* topk_w,
+                           const int32_t* sorted_ids, const int32_t* expert_ids,
+                           const int32_t* num_tokens_post_padded, int T, int H, int I, int E,
+                           int k, int block_m, int variant, void* out, void* ws,
+                           size_t ws_bytes, void* stream);
+
 /* ---------------------------------------------------------------------------------- */
 /* The whole layer: route -> align (block_m = moe_preferred_block_m) -> forward.
  * topk_ids_out / topk_w_out ([T,k]) optionally receive the routing; when NULL the
@@ -183,6 +216,14 @@ moe_status moe_layer(const void* x, const void* wg, const void* w13, const void*
                      const moe_route_cfg* cfg, int T, int H, int I, int E, int k, moe_dtype dt,
                      void* out, int32_t* topk_ids_out, float* topk_w_out, void* ws,
                      size_t ws_bytes, void* stream);
+/* moe_layer with FP8 expert weights: x, Wg and out bf16; w13/w2 E4M3 bytes with their
+ * per-row scales (as for moe_forward_fp8).  ws: moe_layer_workspace_size(...,
+ * MOE_BF16_FP8W) bytes. */
+moe_status moe_layer_fp8(const void* x, const void* wg, const uint8_t* w13,
+                         const float* w13_scale, const uint8_t* w2, const float* w2_scale,
+                         const moe_route_cfg* cfg, int T, int H, int I, int E, int k, void* out,
+                         int32_t* topk_ids_out, float* topk_w_out, void* ws, size_t ws_bytes,
+                         void* stream);
 
 /* ---------------------------------------------------------------------------------- */
 const char* moe_status_string(int status);

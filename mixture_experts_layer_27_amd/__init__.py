@@ -15,13 +15,14 @@ import torch
 
 from ._lib import lib, LIB_PATH, MoeError, RouteCfg, check  # noqa: F401
 
-F32, BF16 = 0, 1
+F32, BF16, BF16_FP8W = 0, 1, 2
 ROUTE_SOFTMAX_TOPK_RENORM, ROUTE_TOPK_THEN_SOFTMAX, ROUTE_SIGMOID_BIAS_GROUPED = 0, 1, 2
 VARIANT_AUTO, VARIANT_PREFILL, VARIANT_DECODE = 0, 1, 2
 
 __all__ = [
     "moe_route", "moe_route_from_logits", "moe_align", "moe_align_capacity",
     "moe_gemm1_swiglu", "moe_gemm2_weighted", "moe_combine", "moe_forward", "moe_layer",
+    "moe_gemm1_swiglu_fp8", "moe_gemm2_weighted_fp8", "moe_forward_fp8", "moe_layer_fp8",
     "moe_preferred_block_m", "moe_auto_variant", "moe_layer_workspace_size",
     "moe_forward_workspace_size", "moe_align_workspace_size", "moe_route_workspace_size",
     "route_cfg", "MoeError", "LIB_PATH",
@@ -44,6 +45,16 @@ def _p(t):
     if not t.is_contiguous():
         raise ValueError("tensors must be contiguous")
     return ctypes.c_void_p(t.data_ptr())
+
+
+def _fp8(w, scale, rows):
+    """Check an FP8 expert weight (uint8 E4M3 codes [E, N, K]) and its fp32 row scales
+    [E, N]."""
+    if w.dtype != torch.uint8:
+        raise TypeError("FP8 weights are uint8 tensors of E4M3 codes")
+    if scale is None or scale.dtype != torch.float32 or tuple(scale.shape) != (w.shape[0], rows):
+        raise ValueError(f"scale must be fp32 [{w.shape[0]}, {rows}]")
+    return _p(w), _p(scale)
 
 
 def _stream():
@@ -198,4 +209,67 @@ def moe_layer(x, wg, w13, w2, k, cfg: RouteCfg, out=None, ws=None, topk_ids_out=
     check(lib.moe_layer(_p(x), _p(wg), _p(w13), _p(w2), ctypes.byref(cfg), T, H, I, E, k, _dt(x),
                         _p(out), _p(topk_ids_out), _p(topk_w_out), _p(ws), ws.numel(),
                         _stream()), "moe_layer")
+    return out
+
+
+# ----------------------------------------------------------------- FP8 expert weights
+
+def moe_gemm1_swiglu_fp8(x, w13, w13_scale, sorted_ids, expert_ids, ntpp, k, block_m,
+                         variant=0, a=None):
+    T, H = x.shape
+    E, I2, _ = w13.shape
+    I = I2 // 2
+    pw, ps = _fp8(w13, w13_scale, I2)
+    if a is None:
+        a = torch.zeros(T * k, I, dtype=x.dtype, device=x.device)
+    check(lib.moe_gemm1_swiglu_fp8(_p(x), pw, ps, _p(sorted_ids), _p(expert_ids), _p(ntpp), T, H,
+                                   I, E, k, block_m, variant, _p(a), _stream()),
+          "moe_gemm1_swiglu_fp8")
+    return a
+
+
+def moe_gemm2_weighted_fp8(a, w2, w2_scale, topk_w, sorted_ids, expert_ids, ntpp, T, k, block_m,
+                           variant=0, y=None):
+    E, H, I = w2.shape
+    pw, ps = _fp8(w2, w2_scale, H)
+    if y is None:
+        y = torch.zeros(T * k, H, dtype=torch.float32, device=a.device)
+    check(lib.moe_gemm2_weighted_fp8(_p(a), pw, ps, _p(topk_w), _p(sorted_ids), _p(expert_ids),
+                                     _p(ntpp), T, H, I, E, k, block_m, variant, _p(y), _stream()),
+          "moe_gemm2_weighted_fp8")
+    return y
+
+
+def moe_forward_fp8(x, w13, w13_scale, w2, w2_scale, topk_w, sorted_ids, expert_ids, ntpp, k,
+                    block_m, variant=0, out=None, ws=None):
+    T, H = x.shape
+    E, I2, _ = w13.shape
+    I = I2 // 2
+    p13, s13 = _fp8(w13, w13_scale, I2)
+    p2, s2 = _fp8(w2, w2_scale, H)
+    if out is None:
+        out = torch.empty(T, H, dtype=x.dtype, device=x.device)
+    if ws is None:
+        ws = _ws(lib.moe_forward_workspace_size(T, H, I, E, k, BF16_FP8W), x.device)
+    check(lib.moe_forward_fp8(_p(x), p13, s13, p2, s2, _p(topk_w), _p(sorted_ids),
+                              _p(expert_ids), _p(ntpp), T, H, I, E, k, block_m, variant, _p(out),
+                              _p(ws), ws.numel(), _stream()), "moe_forward_fp8")
+    return out
+
+
+def moe_layer_fp8(x, wg, w13, w13_scale, w2, w2_scale, k, cfg: RouteCfg, out=None, ws=None,
+                  topk_ids_out=None, topk_w_out=None):
+    """moe_layer with FP8 expert weights (uint8 E4M3 codes + fp32 row scales)."""
+    T, H = x.shape
+    E, I2, _ = w13.shape
+    I = I2 // 2
+    p13, s13 = _fp8(w13, w13_scale, I2)
+    p2, s2 = _fp8(w2, w2_scale, H)
+    if out is None:
+        out = torch.empty(T, H, dtype=x.dtype, device=x.device)
+    if ws is None:
+        ws = _ws(lib.moe_layer_workspace_size(T, H, I, E, k, BF16_FP8W), x.device)
+    check(lib.moe_layer_fp8(_p(x), _p(wg), p13, s13, p2, s2, ctypes.byref(cfg), T, H, I, E, k,
+                            _p(out), _p(topk_ids_out), _p(topk_w_out), _p(ws), ws.numel(),
+                            _stream()), "moe_layer_fp8")
     return out

@@ -36,11 +36,18 @@ _SIGS = {
     "moe_auto_variant": (_i, [_i, _i, _i, _i, _i, _i]),
     "moe_gemm1_swiglu": (_i, [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _i, _p, _p]),
     "moe_gemm2_weighted": (_i, [_p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _i, _p, _p]),
+    "moe_gemm1_swiglu_fp8": (_i, [_p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _p, _p]),
+    "moe_gemm2_weighted_fp8": (_i, [_p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _p,
+                                    _p]),
     "moe_combine": (_i, [_p, _i, _i, _i, _i, _p, _p]),
     "moe_forward_workspace_size": (_sz, [_i, _i, _i, _i, _i, _i]),
     "moe_forward": (_i, [_p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _i, _p, _p, _sz,
                          _p]),
+    "moe_forward_fp8": (_i, [_p, _p, _p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _p,
+                             _p, _sz, _p]),
     "moe_layer_workspace_size": (_sz, [_i, _i, _i, _i, _i, _i]),
+    "moe_layer_fp8": (_i, [_p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _p, _p, _p, _p, _sz,
+                           _p]),
     "moe_layer": (_i, [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _p, _p, _p, _p, _sz, _p]),
     "moe_status_string": (ctypes.c_char_p, [_i]),
     "moe_last_error": (ctypes.c_char_p, []),

@@ -7,6 +7,12 @@
 // v_mfma_f32_16x16x32_bf16) and up to 16 routed token rows the "B" side, so a tile with
 // a single routed row still feeds whole MFMAs from the weight stream.
 //
+// Weights are bf16, or OCP E4M3 bytes with one fp32 scale per weight row (FP8 weights:
+// section 8 of the same page prices an expert at one byte per weight).  FP8 rows are
+// streamed as bytes, expanded to bf16 after the LDS read (exact: every E4M3 value is a
+// bf16 value) and fed to the same bf16 MFMA; the row scale multiplies the fp32
+// accumulator in the epilogue.
+//
 // Every wave is an independent streaming unit (one-wave work-groups, persistent grid).
 // Work item = (sub-tile of 16 routed rows, block of RB weight rows of its expert).
 // For each K step of STEP elements the wave copies the item's RB weight rows and the 16
@@ -29,30 +35,36 @@ namespace moe {
 namespace {
 
 struct DArgs {
-  const uint16_t* A;      // weights: W13 [E,2I,H] or W2 [E,H,I]
+  const uint8_t* A;       // weights: W13 [E,2I,H] or W2 [E,H,I] (bf16 or E4M3 bytes)
   const uint16_t* X;      // token rows: x [T,H] (GEMM1) or a [R,I] (GEMM2)
   void* C;                // a [R,I] bf16 or y [R,H] f32
   int R, gather_div, K, I, H;
-  int64_t a_expert_stride;
+  int64_t a_expert_stride;   // weight elements per expert
   int block_m;            // >= 16: a tile holds block_m / 16 sub-tiles of 16 rows
   int nblk;               // weight-row blocks per expert
 };
 
-template <int STEP>
+// One K step of STEP elements: weight rows of WB bytes per element, token rows bf16.
+template <int STEP, int WB>
 struct DStep {
-  static constexpr int CPR = STEP / 8;      // 16-byte chunks per row per step
-  static constexpr int ROWB = STEP * 2;     // bytes per row per step
-  static constexpr int RPI = kWave / CPR;   // rows per DMA instruction (1 KB)
+  static constexpr int WROWB = STEP * WB;   // weight bytes per row per step
+  static constexpr int XROWB = STEP * 2;    // token bytes per row per step
+  static constexpr int WCPR = WROWB / 16;   // 16-byte chunks per weight row
+  static constexpr int XCPR = XROWB / 16;
+  static constexpr int WRPI = kWave / WCPR; // weight rows per DMA instruction (1 KB)
+  static constexpr int XRPI = kWave / XCPR;
   static constexpr int KSUB = STEP / 32;    // MFMA k-substeps per step
-  static_assert(STEP == 64 || STEP == 128, "step");
+  static_assert(WROWB == 128 || WROWB == 256, "weight row segment");
+  static_assert(XROWB >= 128 && XROWB <= 512, "token row segment");
 };
 
 // LDS position of logical 16-byte chunk c of row r: rows r..r+15 at one logical chunk
-// land on 16 distinct 16-byte bank groups (256-byte rows: c ^ r; 128-byte rows: two
-// rows share a bank window, so the low row bit selects the half and r>>1 the XOR)
+// land on 16 distinct 16-byte bank groups (rows of 256 bytes or more: c ^ r inside each
+// 256-byte half; 128-byte rows: two rows share a bank window, so the low row bit
+// selects the half and r>>1 the XOR)
 template <int CPR>
 __device__ __forceinline__ int dsw(int r, int c) {
-  return CPR == 16 ? (c ^ (r & 15)) : (c ^ ((r >> 1) & 7));
+  return CPR >= 16 ? (c ^ (r & 15)) : (c ^ ((r >> 1) & 7));
 }
 
 // the SUB routed rows of sub-tile u (uniform scalar loads); R marks an empty slot
@@ -69,87 +81,107 @@ __device__ __forceinline__ void load_ids(const int32_t* __restrict__ sorted_ids,
 // over constant indices gets turned into a private-memory table lookup, whose loads
 // would disturb the DMA wait counts.)
 template <int N>
-__device__ __forceinline__ int pick(const int (&v)[N], int t) {
+__device__ __forceinline__ int spread(const int (&v)[N]) {
   static_assert(N <= kWave, "one value per lane");
   int lanes = 0;
 #pragma unroll
   for (int q = 0; q < N; ++q)
     asm volatile("v_writelane_b32 %0, %1, %2" : "+v"(lanes) : "s"(v[q]), "n"(q));
-  return __shfl(lanes, t, kWave);
+  return lanes;
+}
+template <int N>
+__device__ __forceinline__ int pick(const int (&v)[N], int t) {
+  return __shfl(spread(v), t, kWave);
+}
+
+// 16 E4M3 bytes -> two runs of 8 bf16 (bytes 0..7, bytes 8..15), exact
+__device__ __forceinline__ void fp8x16_to_bf16(const u32x4 q, bf16x8& lo, bf16x8& hi) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  bf16x2 p[8];
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    p[2 * d] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(q[d], 1.0f, false);
+    p[2 * d + 1] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(q[d], 1.0f, true);
+  }
+  lo = bf16x8{p[0][0], p[0][1], p[1][0], p[1][1], p[2][0], p[2][1], p[3][0], p[3][1]};
+  hi = bf16x8{p[4][0], p[4][1], p[5][0], p[5][1], p[6][0], p[6][1], p[7][0], p[7][1]};
 }
 
 // DMA sources of one work item: RB weight rows of one expert and the SUB = 16*NTG
 // token rows of one sub-tile
-template <int MODE, int RB, int NTG, int STEP, bool NT>
+template <int MODE, int RB, int NTG, int STEP, bool NT, int WB>
 struct Stream {
-  using S = DStep<STEP>;
+  using S = DStep<STEP, WB>;
   static constexpr int SUB = 16 * NTG;
-  static constexpr int NW = RB / S::RPI;        // weight DMAs per step
-  static constexpr int NX = SUB / S::RPI;       // token-row DMAs per step
+  static constexpr int NW = RB / S::WRPI;       // weight DMAs per step
+  static constexpr int NX = SUB / S::XRPI;      // token-row DMAs per step
 
   // per-lane sources of an item's DMAs at k offset 0
   static __device__ __forceinline__ void setup(const DArgs& p,
                                                const int32_t* __restrict__ sorted_ids,
                                                const int32_t* __restrict__ expert_ids, int item,
-                                               const uint16_t* (&wp)[NW],
+                                               const uint8_t* (&wp)[NW],
                                                const uint16_t* (&xp)[NX]) {
     const int lane = lane_id();
     const int u = item / p.nblk, blk = item - u * p.nblk;
     const int e = expert_ids[(u * SUB) / p.block_m];
     int ids[SUB];
     load_ids<SUB>(sorted_ids, u, ids);
-    const uint16_t* wb = p.A + static_cast<int64_t>(e) * p.a_expert_stride;
-    const int rl = lane / S::CPR, ch = lane % S::CPR;
+    const uint8_t* wb = p.A + static_cast<int64_t>(e) * p.a_expert_stride * WB;
+    const int rl = lane / S::WCPR, ch = lane % S::WCPR;
 #pragma unroll
     for (int j = 0; j < NW; ++j) {
-      const int row = j * S::RPI + rl;
+      const int row = j * S::WRPI + rl;
       int wrow;
       if (MODE == 1)   // first half gate rows W1, second half the matching up rows W3
         wrow = row < RB / 2 ? blk * (RB / 2) + row : p.I + blk * (RB / 2) + (row - RB / 2);
       else
         wrow = blk * RB + row;
-      wp[j] = wb + static_cast<int64_t>(wrow) * p.K + dsw<S::CPR>(row, ch) * 8;
+      wp[j] = wb + static_cast<int64_t>(wrow) * p.K * WB + dsw<S::WCPR>(row, ch) * 16;
     }
     // empty slots re-read the sub-tile's first row (row 0 if the whole sub-tile is
     // padding, which happens only when block_m > SUB)
     const int fb = ids[0] < p.R ? ids[0] : 0;
+    const int xl = lane / S::XCPR, xch = lane % S::XCPR;
 #pragma unroll
     for (int j = 0; j < NX; ++j) {
-      const int t = j * S::RPI + rl;
+      const int t = j * S::XRPI + xl;
       int r = pick(ids, t);
       r = r < p.R ? r : fb;
       const int xrow = r / p.gather_div;
-      xp[j] = p.X + static_cast<int64_t>(xrow) * p.K + dsw<S::CPR>(t & 15, ch) * 8;
+      xp[j] = p.X + static_cast<int64_t>(xrow) * p.K + dsw<S::XCPR>(t & 15, xch) * 8;
     }
   }
 
-  static __device__ __forceinline__ void issue(const uint16_t* const (&wp)[NW],
+  // k0: element offset of the step
+  static __device__ __forceinline__ void issue(const uint8_t* const (&wp)[NW],
                                                const uint16_t* const (&xp)[NX], int k0,
                                                MOE_LDS uint8_t* slot) {
 #pragma unroll
     for (int j = 0; j < NW; ++j) {
-      if (NT) dma16_nt(wp[j] + k0, slot + j * 1024);    // weights read once
-      else dma16(wp[j] + k0, slot + j * 1024);
+      if (NT) dma16_nt(wp[j] + k0 * WB, slot + j * 1024);    // weights read once
+      else dma16(wp[j] + k0 * WB, slot + j * 1024);
     }
 #pragma unroll
-    for (int j = 0; j < NX; ++j) dma16(xp[j] + k0, slot + RB * S::ROWB + j * 1024);
+    for (int j = 0; j < NX; ++j) dma16(xp[j] + k0, slot + RB * S::WROWB + j * 1024);
   }
 };
 
 // The routing tables are separate __restrict__ arguments: with them the compiler may
 // read the (wave-uniform) entries with scalar loads, which count on lgkmcnt and leave
 // the vmcnt accounting of the DMA ring untouched.
-template <int MODE, int RB, int NTG, int STEP, int P, bool NT>
+template <int MODE, int RB, int NTG, int STEP, int P, bool NT, int WB>
 __global__ void __launch_bounds__(64)
 moe_decode_kernel(DArgs p, const int32_t* __restrict__ sorted_ids,
                   const int32_t* __restrict__ expert_ids, const int32_t* __restrict__ ntpp,
-                  const float* __restrict__ topk_w) {
-  using S = DStep<STEP>;
-  using St = Stream<MODE, RB, NTG, STEP, NT>;
+                  const float* __restrict__ topk_w, const float* __restrict__ wscale) {
+  using S = DStep<STEP, WB>;
+  using St = Stream<MODE, RB, NTG, STEP, NT, WB>;
   constexpr int SUB = St::SUB;
   constexpr int NF = RB / 16;                   // 16-row weight fragments per item
   constexpr int NI = St::NW + St::NX;           // DMAs per step
-  constexpr int SLOT = (RB + SUB) * S::ROWB;
+  constexpr int SLOT = RB * S::WROWB + SUB * S::XROWB;
+  static_assert(RB <= kWave, "one scale per lane");
   static_assert(P >= 3 && (P - 2) * NI < 64, "ring depth");
   static_assert(MODE != 1 || NF % 2 == 0, "gate/up fragment pairs");
   __shared__ __attribute__((aligned(1024))) uint8_t ring[P * SLOT];
@@ -171,7 +203,7 @@ moe_decode_kernel(DArgs p, const int32_t* __restrict__ sorted_ids,
   // issue cursor: the step the next DMA batch belongs to (it stays on the last step
   // once everything is issued, so the ring tail re-reads it into unused slots)
   MOE_LDS uint8_t* lring = (MOE_LDS uint8_t*)ring;
-  const uint16_t* wp[St::NW];
+  const uint8_t* wp[St::NW];
   const uint16_t* xp[St::NX];
   St::setup(p, sorted_ids, expert_ids, first, wp, xp);
   int gi = 0, iss_s = 0, iss_item = first;
@@ -202,22 +234,56 @@ moe_decode_kernel(DArgs p, const int32_t* __restrict__ sorted_ids,
         for (int f = 0; f < NF; ++f) acc[q][f] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
     const uint8_t* slot = ring + (g % P) * SLOT;
+    const uint8_t* xs = slot + RB * S::WROWB;   // token rows of the step
+    if (WB == 2) {
 #pragma unroll
-    for (int ks = 0; ks < S::KSUB; ++ks) {
-      const int c = ks * 4 + (lane >> 4);       // 8 k-elements of lane group lane>>4
-      bf16x8 b[NTG];
-#pragma unroll
-      for (int q = 0; q < NTG; ++q)
-        b[q] = *reinterpret_cast<const bf16x8*>(slot + (RB + 16 * q + tr) * S::ROWB +
-                                                dsw<S::CPR>(tr, c) * 16);
-#pragma unroll
-      for (int f = 0; f < NF; ++f) {
-        const int row = 16 * f + tr;
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(slot + row * S::ROWB +
-                                                          dsw<S::CPR>(row, c) * 16);
+      for (int ks = 0; ks < S::KSUB; ++ks) {
+        const int c = ks * 4 + (lane >> 4);     // 8 k-elements of lane group lane>>4
+        bf16x8 b[NTG];
 #pragma unroll
         for (int q = 0; q < NTG; ++q)
-          acc[q][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b[q], acc[q][f], 0, 0, 0);
+          b[q] = *reinterpret_cast<const bf16x8*>(xs + (16 * q + tr) * S::XROWB +
+                                                  dsw<S::XCPR>(tr, c) * 16);
+#pragma unroll
+        for (int f = 0; f < NF; ++f) {
+          const int row = 16 * f + tr;
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(slot + row * S::WROWB +
+                                                            dsw<S::WCPR>(row, c) * 16);
+#pragma unroll
+          for (int q = 0; q < NTG; ++q)
+            acc[q][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b[q], acc[q][f], 0, 0, 0);
+        }
+      }
+    } else {
+      // Two MFMAs per 64 k-elements.  The sum over k does not depend on how k is dealt
+      // to lane groups, so lane group gq takes the 16 consecutive k-elements
+      // 16*gq .. 16*gq+15 of the 64: one 16-byte chunk of each weight row (expanded to
+      // two bf16x8), and the two matching bf16 chunks of each token row.
+#pragma unroll
+      for (int kp = 0; kp < S::KSUB / 2; ++kp) {
+        const int gq = lane >> 4;
+        const int cw = kp * 4 + gq;             // weight chunk (16 E4M3 values)
+        const int cx = kp * 8 + 2 * gq;         // first of two token chunks
+        bf16x8 b0[NTG], b1[NTG];
+#pragma unroll
+        for (int q = 0; q < NTG; ++q) {
+          const uint8_t* xr = xs + (16 * q + tr) * S::XROWB;
+          b0[q] = *reinterpret_cast<const bf16x8*>(xr + dsw<S::XCPR>(tr, cx) * 16);
+          b1[q] = *reinterpret_cast<const bf16x8*>(xr + dsw<S::XCPR>(tr, cx + 1) * 16);
+        }
+#pragma unroll
+        for (int f = 0; f < NF; ++f) {
+          const int row = 16 * f + tr;
+          const u32x4 wq = *reinterpret_cast<const u32x4*>(slot + row * S::WROWB +
+                                                           dsw<S::WCPR>(row, cw) * 16);
+          bf16x8 a0, a1;
+          fp8x16_to_bf16(wq, a0, a1);
+#pragma unroll
+          for (int q = 0; q < NTG; ++q) {
+            acc[q][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, b0[q], acc[q][f], 0, 0, 0);
+            acc[q][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, b1[q], acc[q][f], 0, 0, 0);
+          }
+        }
       }
     }
     if (++cs == nsteps) {
@@ -227,6 +293,30 @@ moe_decode_kernel(DArgs p, const int32_t* __restrict__ sorted_ids,
       const int u = cmp_item / p.nblk, blk = cmp_item - u * p.nblk;
       int ids[SUB];
       load_ids<SUB>(sorted_ids, u, ids);
+      // FP8 weights: the row scales of this lane's accumulator rows 16f + 4(lane>>4) + v.
+      // Lane j of stab holds the scale of the item's weight row j (uniform loads, in the
+      // order of the DMA rows: gate rows then up rows for GEMM1); the lane-crossbar reads
+      // run here, with the whole wave active (an inactive source lane reads as 0).
+      float rs[NF][4];
+      if (WB == 1) {
+        const int e = expert_ids[(u * SUB) / p.block_m];
+        const int nrows = MODE == 1 ? 2 * p.I : p.H;
+        const float* sp = wscale + static_cast<int64_t>(e) * nrows;
+        int sv[RB];
+#pragma unroll
+        for (int j = 0; j < RB; ++j) {
+          const int wrow = MODE == 1 ? (j < RB / 2 ? blk * (RB / 2) + j
+                                                   : p.I + blk * (RB / 2) + (j - RB / 2))
+                                     : blk * RB + j;
+          sv[j] = __float_as_int(sp[wrow]);
+        }
+        const int stab = spread(sv);
+#pragma unroll
+        for (int f = 0; f < NF; ++f)
+#pragma unroll
+          for (int v = 0; v < 4; ++v)
+            rs[f][v] = __int_as_float(__shfl(stab, 16 * f + 4 * (lane >> 4) + v, kWave));
+      }
       int wts[SUB];                             // GEMM2 router weights (uniform loads)
       if (MODE == 2) {
 #pragma unroll
@@ -240,7 +330,14 @@ moe_decode_kernel(DArgs p, const int32_t* __restrict__ sorted_ids,
           if (MODE == 1) {
 #pragma unroll
             for (int f = 0; f < NF / 2; ++f) {
-              const f32x4 gt = acc[q][f], up = acc[q][f + NF / 2];
+              f32x4 gt = acc[q][f], up = acc[q][f + NF / 2];
+              if (WB == 1) {
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                  gt[v] *= rs[f][v];
+                  up[v] *= rs[f + NF / 2][v];
+                }
+              }
               uint32_t pk[2];
 #pragma unroll
               for (int v = 0; v < 4; v += 2)
@@ -253,10 +350,15 @@ moe_decode_kernel(DArgs p, const int32_t* __restrict__ sorted_ids,
           } else {
 #pragma unroll
             for (int f = 0; f < NF; ++f) {
+              f32x4 v4 = acc[q][f];
+              if (WB == 1) {
+#pragma unroll
+                for (int v = 0; v < 4; ++v) v4[v] *= rs[f][v];
+              }
               float* out = static_cast<float*>(p.C) + static_cast<int64_t>(r) * p.H +
                            blk * RB + 16 * f + 4 * (lane >> 4);
-              *reinterpret_cast<float4*>(out) = make_float4(
-                  wr * acc[q][f][0], wr * acc[q][f][1], wr * acc[q][f][2], wr * acc[q][f][3]);
+              *reinterpret_cast<float4*>(out) =
+                  make_float4(wr * v4[0], wr * v4[1], wr * v4[2], wr * v4[3]);
             }
           }
         }
@@ -278,23 +380,45 @@ int decode_ntg(int block_m, int R, int E) {
   return std::min(want, block_m / 16);
 }
 
-template <int MODE, int NTG, int STEP, bool NT>
+template <int MODE, int NTG, int STEP, bool NT, int WB, int P>
 hipError_t launch_decode(const DArgs& p, const GemmArgs& g, hipStream_t s) {
-  constexpr int P = NTG == 1 ? 4 : 3;
-  constexpr int kLds = P * (kDecodeRB + 16 * NTG) * DStep<STEP>::ROWB;
+  using S = DStep<STEP, WB>;
+  constexpr int kLds = P * (kDecodeRB * S::WROWB + 16 * NTG * S::XROWB);
   constexpr int kPerCU = std::max(1, (160 * 1024) / kLds);
   const int64_t max_items = (g.cap / (16 * NTG)) * p.nblk;
   const unsigned grid = static_cast<unsigned>(std::min<int64_t>(max_items, 256 * kPerCU));
-  hipLaunchKernelGGL((moe_decode_kernel<MODE, kDecodeRB, NTG, STEP, P, NT>), dim3(grid), dim3(64),
-                     0, s, p, g.sorted_ids, g.expert_ids, g.ntpp, g.topk_w);
+  hipLaunchKernelGGL((moe_decode_kernel<MODE, kDecodeRB, NTG, STEP, P, NT, WB>), dim3(grid),
+                     dim3(64), 0, s, p, g.sorted_ids, g.expert_ids, g.ntpp, g.topk_w, g.w_scale);
   return hipGetLastError();
+}
+
+// bf16 weights: 128-element steps (256-byte weight rows) when K allows, else 64
+template <int MODE, int NTG, bool NT>
+hipError_t launch_decode_bf16(const DArgs& p, const GemmArgs& g, hipStream_t s) {
+  constexpr int P = NTG == 1 ? 4 : 3;
+  return p.K % 128 == 0 ? launch_decode<MODE, NTG, 128, NT, 2, P>(p, g, s)
+                        : launch_decode<MODE, NTG, 64, NT, 2, P>(p, g, s);
+}
+
+// FP8 weights: 256-element steps (256-byte weight rows, 512-byte token rows) when K
+// allows, else 128 (K % 128 == 0 is checked by the caller)
+template <int MODE, int NTG, bool NT>
+hipError_t launch_decode_fp8(const DArgs& p, const GemmArgs& g, hipStream_t s) {
+  return p.K % 256 == 0 ? launch_decode<MODE, NTG, 256, NT, 1, 3>(p, g, s)
+                        : launch_decode<MODE, NTG, 128, NT, 1, 4>(p, g, s);
+}
+
+template <int MODE, int NTG, bool NT>
+hipError_t launch_decode_w(const DArgs& p, const GemmArgs& g, hipStream_t s) {
+  return g.w_scale ? launch_decode_fp8<MODE, NTG, NT>(p, g, s)
+                   : launch_decode_bf16<MODE, NTG, NT>(p, g, s);
 }
 
 template <int MODE>
 hipError_t run_decode(const GemmArgs& g, hipStream_t s) {
   DArgs p{};
   const bool g1 = MODE == 1;
-  p.A = static_cast<const uint16_t*>(g.B);
+  p.A = static_cast<const uint8_t*>(g.B);
   p.X = static_cast<const uint16_t*>(g.A);
   p.C = g.C;
   p.R = g.T * g.k;
@@ -308,22 +432,14 @@ hipError_t run_decode(const GemmArgs& g, hipStream_t s) {
   p.nblk = N / kDecodeRB;
   if (g.cap == 0) return hipSuccess;
   const int ntg = decode_ntg(g.block_m, p.R, g.E);
-  const bool s128 = p.K % 128 == 0;
   // non-temporal weight stream while almost every expert fits one sub-tile (each weight
   // block read once); otherwise the sub-tiles of one expert re-read its weights, and
   // those re-reads should hit in L2
-  if (ntg == 2) {
-    if (p.R <= 4 * g.E)
-      return s128 ? launch_decode<MODE, 2, 128, true>(p, g, s)
-                  : launch_decode<MODE, 2, 64, true>(p, g, s);
-    return s128 ? launch_decode<MODE, 2, 128, false>(p, g, s)
-                : launch_decode<MODE, 2, 64, false>(p, g, s);
-  }
-  if (p.R <= 2 * g.E)
-    return s128 ? launch_decode<MODE, 1, 128, true>(p, g, s)
-                : launch_decode<MODE, 1, 64, true>(p, g, s);
-  return s128 ? launch_decode<MODE, 1, 128, false>(p, g, s)
-              : launch_decode<MODE, 1, 64, false>(p, g, s);
+  if (ntg == 2)
+    return p.R <= 4 * g.E ? launch_decode_w<MODE, 2, true>(p, g, s)
+                          : launch_decode_w<MODE, 2, false>(p, g, s);
+  return p.R <= 2 * g.E ? launch_decode_w<MODE, 1, true>(p, g, s)
+                        : launch_decode_w<MODE, 1, false>(p, g, s);
 }
 
 }  // namespace

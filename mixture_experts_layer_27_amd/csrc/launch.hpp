@@ -43,6 +43,7 @@ struct GemmArgs {
   const void* B;             // GEMM1: W13 [E,2I,H]; GEMM2: W2 [E,H,I]
   void* C;                   // GEMM1: a [R,I] (bf16/f32); GEMM2: y [R,H] f32
   const float* topk_w;       // GEMM2 only
+  const float* w_scale;      // FP8 weights: per-row scales of B ([E,2I] or [E,H]); else null
   const int32_t* sorted_ids;
   const int32_t* expert_ids;
   const int32_t* ntpp;

@@ -36,8 +36,12 @@ moe_status hip_status(hipError_t e, const char* what) {
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+// activation types of the router and the combine (x, Wg, out)
 bool valid_dt(int dt) { return dt == MOE_F32 || dt == MOE_BF16; }
-size_t esize(moe_dtype dt) { return dt == MOE_BF16 ? 2 : 4; }
+// expert GEMMs and the layer also take bf16 activations with FP8 expert weights
+bool valid_expert_dt(int dt) { return valid_dt(dt) || dt == MOE_BF16_FP8W; }
+bool bf16_acts(int dt) { return dt == MOE_BF16 || dt == MOE_BF16_FP8W; }
+size_t esize(moe_dtype dt) { return bf16_acts(dt) ? 2 : 4; }
 size_t round_up(size_t v) { return (v + 255) & ~static_cast<size_t>(255); }
 bool is_pow2(int v) { return v > 0 && (v & (v - 1)) == 0; }
 
@@ -101,6 +105,7 @@ moe::RouteArgs route_args(const moe_route_cfg* cfg) {
 
 int auto_variant(int T, int H, int I, int E, int k, moe_dtype dt) {
   (void)H; (void)I;
+  if (dt == MOE_BF16_FP8W) return MOE_VARIANT_DECODE;   // the FP8-weight kernels
   if (dt != MOE_BF16) return MOE_VARIANT_PREFILL;
   const int64_t R = static_cast<int64_t>(T) * k;
   // decode when the average expert holds at most 8 routed rows
@@ -108,7 +113,7 @@ int auto_variant(int T, int H, int I, int E, int k, moe_dtype dt) {
 }
 
 int preferred_bm(int T, int H, int I, int E, int k, moe_dtype dt) {
-  if (dt != MOE_BF16) return 16;
+  if (dt == MOE_F32) return 16;
   if (auto_variant(T, H, I, E, k, dt) == MOE_VARIANT_DECODE)
     return moe::decode_block_m(static_cast<int>(static_cast<int64_t>(T) * k), E);
   // 256-row MFMA tiles once the average expert fills several of them (the padding of
@@ -125,7 +130,7 @@ moe_status check_gemm_common(int T, int H, int I, int E, int k, int block_m, int
                              int variant) {
   moe_status st = check_tke(T, k, E);
   if (st != MOE_OK) return st;
-  if (!valid_dt(dt)) return fail(MOE_ERR_INVALID_ARG, "dtype=%d", dt);
+  if (!valid_expert_dt(dt)) return fail(MOE_ERR_INVALID_ARG, "dtype=%d", dt);
   if (H <= 0 || I <= 0) return fail(MOE_ERR_INVALID_ARG, "H=%d I=%d must be > 0", H, I);
   if (!is_pow2(block_m) || block_m > 256)
     return fail(MOE_ERR_INVALID_ARG, "block_m=%d must be a power of two <= 256", block_m);
@@ -139,16 +144,26 @@ moe_status check_gemm_common(int T, int H, int I, int E, int k, int block_m, int
     if (v == MOE_VARIANT_DECODE && block_m < 16)
       return fail(MOE_ERR_UNSUPPORTED, "bf16 decode tiles need block_m >= 16 (got %d)", block_m);
   }
+  if (dt == MOE_BF16_FP8W) {
+    if (H % 128 || I % 128)
+      return fail(MOE_ERR_UNSUPPORTED, "FP8 weights need H, I multiples of 128 (H=%d I=%d)", H, I);
+    const int v = resolve_variant(variant, T, H, I, E, k, static_cast<moe_dtype>(dt));
+    if (v != MOE_VARIANT_DECODE)
+      return fail(MOE_ERR_UNSUPPORTED, "FP8 weights run on the weight-streaming kernels only");
+    if (block_m < 16)
+      return fail(MOE_ERR_UNSUPPORTED, "FP8-weight tiles need block_m >= 16 (got %d)", block_m);
+  }
   if (static_cast<int64_t>(T) * k * std::max(H, I) >= (int64_t(1) << 40))
     return fail(MOE_ERR_UNSUPPORTED, "tensor too large");
   return MOE_OK;
 }
 
-moe::GemmArgs gemm_args(const void* A, const void* B, void* C, const float* topk_w,
-                        const int32_t* sorted_ids, const int32_t* expert_ids,
-                        const int32_t* ntpp, int T, int H, int I, int E, int k, int block_m) {
+moe::GemmArgs gemm_args(const void* A, const void* B, const float* B_scale, void* C,
+                        const float* topk_w, const int32_t* sorted_ids,
+                        const int32_t* expert_ids, const int32_t* ntpp, int T, int H, int I,
+                        int E, int k, int block_m) {
   moe::GemmArgs g;
-  g.A = A; g.B = B; g.C = C; g.topk_w = topk_w;
+  g.A = A; g.B = B; g.w_scale = B_scale; g.C = C; g.topk_w = topk_w;
   g.sorted_ids = sorted_ids; g.expert_ids = expert_ids; g.ntpp = ntpp;
   g.T = T; g.H = H; g.I = I; g.E = E; g.k = k; g.block_m = block_m;
   g.cap = capacity(T, k, E, block_m);
@@ -268,22 +283,78 @@ int moe_preferred_block_m(int T, int H, int I, int E, int k, moe_dtype dt) {
   return preferred_bm(T, H, I, E, k, dt);
 }
 
-moe_status moe_gemm1_swiglu(const void* x, const void* w13, const int32_t* sorted_ids,
-                            const int32_t* expert_ids, const int32_t* num_tokens_post_padded,
-                            int T, int H, int I, int E, int k, int block_m, moe_dtype dt,
-                            int variant, void* a, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// FP8 weights need both scale arrays (the *_fp8 entry points); other weights take none
+moe_status check_scales(int dt, const float* s13, const float* s2) {
+  if (dt == MOE_BF16_FP8W) {
+    if (!s13 || !s2)
+      return fail(MOE_ERR_INVALID_ARG, "FP8 weights need their per-row scales (the *_fp8 entry points)");
+  } else if (s13 || s2) {
+    return fail(MOE_ERR_INVALID_ARG, "weight scales are only taken with FP8 weights");
+  }
+  return MOE_OK;
+}
+
+moe_status gemm1_impl(const void* x, const void* w13, const float* w13_scale,
+                      const int32_t* sorted_ids, const int32_t* expert_ids,
+                      const int32_t* num_tokens_post_padded, int T, int H, int I, int E, int k,
+                      int block_m, moe_dtype dt, int variant, void* a, void* stream) {
   moe_status st = check_gemm_common(T, H, I, E, k, block_m, dt, variant);
   if (st != MOE_OK) return st;
+  if ((st = check_scales(dt, w13_scale, w13_scale)) != MOE_OK) return st;
   if (T == 0) return ok();
   if (!x || !w13 || !sorted_ids || !expert_ids || !num_tokens_post_padded || !a)
     return fail(MOE_ERR_INVALID_ARG, "NULL tensor pointer");
   if (!aligned16(x) || !aligned16(w13) || !aligned16(a))
     return fail(MOE_ERR_INVALID_ARG, "x/W13/a not 16-byte aligned");
   const int v = resolve_variant(variant, T, H, I, E, k, dt);
-  moe::GemmArgs g = gemm_args(x, w13, a, nullptr, sorted_ids, expert_ids,
+  moe::GemmArgs g = gemm_args(x, w13, w13_scale, a, nullptr, sorted_ids, expert_ids,
                               num_tokens_post_padded, T, H, I, E, k, block_m);
-  return hip_status(moe::launch_gemm1(g, dt == MOE_BF16, v, static_cast<hipStream_t>(stream)),
+  return hip_status(moe::launch_gemm1(g, bf16_acts(dt), v, static_cast<hipStream_t>(stream)),
                     "gemm1");
+}
+
+moe_status gemm2_impl(const void* a, const void* w2, const float* w2_scale, const float* topk_w,
+                      const int32_t* sorted_ids, const int32_t* expert_ids,
+                      const int32_t* num_tokens_post_padded, int T, int H, int I, int E, int k,
+                      int block_m, moe_dtype dt, int variant, float* y, void* stream) {
+  moe_status st = check_gemm_common(T, H, I, E, k, block_m, dt, variant);
+  if (st != MOE_OK) return st;
+  if ((st = check_scales(dt, w2_scale, w2_scale)) != MOE_OK) return st;
+  if (T == 0) return ok();
+  if (!a || !w2 || !topk_w || !sorted_ids || !expert_ids || !num_tokens_post_padded || !y)
+    return fail(MOE_ERR_INVALID_ARG, "NULL tensor pointer");
+  if (!aligned16(a) || !aligned16(w2) || !aligned16(y))
+    return fail(MOE_ERR_INVALID_ARG, "a/W2/y not 16-byte aligned");
+  const int v = resolve_variant(variant, T, H, I, E, k, dt);
+  moe::GemmArgs g = gemm_args(a, w2, w2_scale, y, topk_w, sorted_ids, expert_ids,
+                              num_tokens_post_padded, T, H, I, E, k, block_m);
+  return hip_status(moe::launch_gemm2(g, bf16_acts(dt), v, static_cast<hipStream_t>(stream)),
+                    "gemm2");
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status moe_gemm1_swiglu(const void* x, const void* w13, const int32_t* sorted_ids,
+                            const int32_t* expert_ids, const int32_t* num_tokens_post_padded,
+                            int T, int H, int I, int E, int k, int block_m, moe_dtype dt,
+                            int variant, void* a, void* stream) {
+  return gemm1_impl(x, w13, nullptr, sorted_ids, expert_ids, num_tokens_post_padded, T, H, I, E,
+                    k, block_m, dt, variant, a, stream);
+}
+
+moe_status moe_gemm1_swiglu_fp8(const void* x, const uint8_t* w13, const float* w13_scale,
+                                const int32_t* sorted_ids, const int32_t* expert_ids,
+                                const int32_t* num_tokens_post_padded, int T, int H, int I,
+                                int E, int k, int block_m, int variant, void* a, void* stream) {
+  if (!w13_scale) return fail(MOE_ERR_INVALID_ARG, "w13_scale is NULL");
+  return gemm1_impl(x, w13, w13_scale, sorted_ids, expert_ids, num_tokens_post_padded, T, H, I,
+                    E, k, block_m, MOE_BF16_FP8W, variant, a, stream);
 }
 
 moe_status moe_gemm2_weighted(const void* a, const void* w2, const float* topk_w,
@@ -291,18 +362,19 @@ moe_status moe_gemm2_weighted(const void* a, const void* w2, const float* topk_w
                               const int32_t* num_tokens_post_padded, int T, int H, int I,
                               int E, int k, int block_m, moe_dtype dt, int variant, float* y,
                               void* stream) {
-  moe_status st = check_gemm_common(T, H, I, E, k, block_m, dt, variant);
-  if (st != MOE_OK) return st;
-  if (T == 0) return ok();
-  if (!a || !w2 || !topk_w || !sorted_ids || !expert_ids || !num_tokens_post_padded || !y)
-    return fail(MOE_ERR_INVALID_ARG, "NULL tensor pointer");
-  if (!aligned16(a) || !aligned16(w2) || !aligned16(y))
-    return fail(MOE_ERR_INVALID_ARG, "a/W2/y not 16-byte aligned");
-  const int v = resolve_variant(variant, T, H, I, E, k, dt);
-  moe::GemmArgs g = gemm_args(a, w2, y, topk_w, sorted_ids, expert_ids, num_tokens_post_padded,
-                              T, H, I, E, k, block_m);
-  return hip_status(moe::launch_gemm2(g, dt == MOE_BF16, v, static_cast<hipStream_t>(stream)),
-                    "gemm2");
+  return gemm2_impl(a, w2, nullptr, topk_w, sorted_ids, expert_ids, num_tokens_post_padded, T, H,
+                    I, E, k, block_m, dt, variant, y, stream);
+}
+
+moe_status moe_gemm2_weighted_fp8(const void* a, const uint8_t* w2, const float* w2_scale,
+                                  const float* topk_w, const int32_t* sorted_ids,
+                                  const int32_t* expert_ids,
+                                  const int32_t* num_tokens_post_padded, int T, int H, int I,
+                                  int E, int k, int block_m, int variant, float* y,
+                                  void* stream) {
+  if (!w2_scale) return fail(MOE_ERR_INVALID_ARG, "w2_scale is NULL");
+  return gemm2_impl(a, w2, w2_scale, topk_w, sorted_ids, expert_ids, num_tokens_post_padded, T,
+                    H, I, E, k, block_m, MOE_BF16_FP8W, variant, y, stream);
 }
 
 moe_status moe_combine(const float* y, int T, int H, int k, moe_dtype dt, void* out,
@@ -318,17 +390,22 @@ moe_status moe_combine(const float* y, int T, int H, int k, moe_dtype dt, void* 
 
 size_t moe_forward_workspace_size(int T, int H, int I, int E, int k, moe_dtype dt) {
   (void)E;
-  if (T <= 0 || H <= 0 || I <= 0 || k < 1 || !valid_dt(dt)) return 0;
+  if (T <= 0 || H <= 0 || I <= 0 || k < 1 || !valid_expert_dt(dt)) return 0;
   return forward_ws(T, H, I, k, dt);
 }
 
-moe_status moe_forward(const void* x, const void* w13, const void* w2, const float* topk_w,
-                       const int32_t* sorted_ids, const int32_t* expert_ids,
-                       const int32_t* num_tokens_post_padded, int T, int H, int I, int E,
-                       int k, int block_m, moe_dtype dt, int variant, void* out, void* ws,
-                       size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+moe_status forward_impl(const void* x, const void* w13, const float* w13_scale, const void* w2,
+                        const float* w2_scale, const float* topk_w, const int32_t* sorted_ids,
+                        const int32_t* expert_ids, const int32_t* num_tokens_post_padded, int T,
+                        int H, int I, int E, int k, int block_m, moe_dtype dt, int variant,
+                        void* out, void* ws, size_t ws_bytes, void* stream) {
   moe_status st = check_gemm_common(T, H, I, E, k, block_m, dt, variant);
   if (st != MOE_OK) return st;
+  if ((st = check_scales(dt, w13_scale, w2_scale)) != MOE_OK) return st;
   if (T == 0) return ok();
   if (!x || !w13 || !w2 || !topk_w || !sorted_ids || !expert_ids || !num_tokens_post_padded ||
       !out)
@@ -344,16 +421,42 @@ moe_status moe_forward(const void* x, const void* w13, const void* w2, const flo
   float* y = reinterpret_cast<float*>(base + round_up(R * I * esize(dt)));
   const int v = resolve_variant(variant, T, H, I, E, k, dt);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const bool bf = dt == MOE_BF16;
-  moe::GemmArgs g1 = gemm_args(x, w13, a, nullptr, sorted_ids, expert_ids,
+  const bool bf = bf16_acts(dt);
+  moe::GemmArgs g1 = gemm_args(x, w13, w13_scale, a, nullptr, sorted_ids, expert_ids,
                                num_tokens_post_padded, T, H, I, E, k, block_m);
   hipError_t e = moe::launch_gemm1(g1, bf, v, s);
   if (e != hipSuccess) return hip_status(e, "gemm1");
-  moe::GemmArgs g2 = gemm_args(a, w2, y, topk_w, sorted_ids, expert_ids, num_tokens_post_padded,
-                               T, H, I, E, k, block_m);
+  moe::GemmArgs g2 = gemm_args(a, w2, w2_scale, y, topk_w, sorted_ids, expert_ids,
+                               num_tokens_post_padded, T, H, I, E, k, block_m);
   e = moe::launch_gemm2(g2, bf, v, s);
   if (e != hipSuccess) return hip_status(e, "gemm2");
   return hip_status(moe::launch_combine(y, T, H, k, bf, out, s), "combine");
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status moe_forward(const void* x, const void* w13, const void* w2, const float* topk_w,
+                       const int32_t* sorted_ids, const int32_t* expert_ids,
+                       const int32_t* num_tokens_post_padded, int T, int H, int I, int E,
+                       int k, int block_m, moe_dtype dt, int variant, void* out, void* ws,
+                       size_t ws_bytes, void* stream) {
+  return forward_impl(x, w13, nullptr, w2, nullptr, topk_w, sorted_ids, expert_ids,
+                      num_tokens_post_padded, T, H, I, E, k, block_m, dt, variant, out, ws,
+                      ws_bytes, stream);
+}
+
+moe_status moe_forward_fp8(const void* x, const uint8_t* w13, const float* w13_scale,
+                           const uint8_t* w2, const float* w2_scale, const float* topk_w,
+                           const int32_t* sorted_ids, const int32_t* expert_ids,
+                           const int32_t* num_tokens_post_padded, int T, int H, int I, int E,
+                           int k, int block_m, int variant, void* out, void* ws,
+                           size_t ws_bytes, void* stream) {
+  if (!w13_scale || !w2_scale) return fail(MOE_ERR_INVALID_ARG, "NULL scale pointer");
+  return forward_impl(x, w13, w13_scale, w2, w2_scale, topk_w, sorted_ids, expert_ids,
+                      num_tokens_post_padded, T, H, I, E, k, block_m, MOE_BF16_FP8W, variant,
+                      out, ws, ws_bytes, stream);
 }
 
 // ------------------------------------------------------------------------------ layer
@@ -372,7 +475,7 @@ LayerPlan plan_layer(int T, int H, int I, int E, int k, moe_dtype dt) {
   p.cap = capacity(T, k, E, p.bm);
   const size_t R = static_cast<size_t>(T) * k;
   size_t off = 0;
-  p.nz = moe::router_slabs(T, H, dt == MOE_BF16);
+  p.nz = moe::router_slabs(T, H, bf16_acts(dt));
   p.fused_route_align = moe::route_align_fusable(T, k, E);
   p.off_logits = off; off += round_up(static_cast<size_t>(p.nz) * T * E * sizeof(float));
   p.off_ids = off; off += round_up(R * sizeof(int32_t));
@@ -389,21 +492,26 @@ LayerPlan plan_layer(int T, int H, int I, int E, int k, moe_dtype dt) {
 }  // namespace
 
 size_t moe_layer_workspace_size(int T, int H, int I, int E, int k, moe_dtype dt) {
-  if (T <= 0 || H <= 0 || I <= 0 || E <= 0 || k < 1 || !valid_dt(dt)) return 0;
+  if (T <= 0 || H <= 0 || I <= 0 || E <= 0 || k < 1 || !valid_expert_dt(dt)) return 0;
   return plan_layer(T, H, I, E, k, dt).total;
 }
 
-moe_status moe_layer(const void* x, const void* wg, const void* w13, const void* w2,
-                     const moe_route_cfg* cfg, int T, int H, int I, int E, int k, moe_dtype dt,
-                     void* out, int32_t* topk_ids_out, float* topk_w_out, void* ws,
-                     size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+moe_status layer_impl(const void* x, const void* wg, const void* w13, const float* w13_scale,
+                      const void* w2, const float* w2_scale, const moe_route_cfg* cfg, int T,
+                      int H, int I, int E, int k, moe_dtype dt, void* out, int32_t* topk_ids_out,
+                      float* topk_w_out, void* ws, size_t ws_bytes, void* stream) {
   moe_status st = check_gemm_common(T, H, I, E, k, 32, dt, MOE_VARIANT_AUTO);
   if (st != MOE_OK) return st;
   if ((st = check_route_cfg(cfg, E, k)) != MOE_OK) return st;
+  if ((st = check_scales(dt, w13_scale, w2_scale)) != MOE_OK) return st;
   if (T == 0) return ok();
   if (!x || !wg || !w13 || !w2 || !out) return fail(MOE_ERR_INVALID_ARG, "NULL tensor pointer");
-  if (dt == MOE_BF16 && (!aligned16(x) || !aligned16(wg) || !aligned16(w13) || !aligned16(w2) ||
-                         !aligned16(out)))
+  if (bf16_acts(dt) && (!aligned16(x) || !aligned16(wg) || !aligned16(w13) || !aligned16(w2) ||
+                        !aligned16(out)))
     return fail(MOE_ERR_INVALID_ARG, "tensor not 16-byte aligned");
   const LayerPlan p = plan_layer(T, H, I, E, k, dt);
   if (!ws || ws_bytes < p.total) return fail(MOE_ERR_WORKSPACE, "layer workspace needs %zu bytes", p.total);
@@ -417,7 +525,7 @@ moe_status moe_layer(const void* x, const void* wg, const void* w13, const void*
   int32_t* ntpp = reinterpret_cast<int32_t*>(b + p.off_ntpp);
   int32_t* counts = reinterpret_cast<int32_t*>(b + p.off_counts);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = moe::launch_router_logits(x, wg, T, H, E, dt == MOE_BF16, logits, s);
+  hipError_t e = moe::launch_router_logits(x, wg, T, H, E, bf16_acts(dt), logits, s);
   if (e != hipSuccess) return hip_status(e, "router logits");
   if (p.fused_route_align) {
     e = moe::launch_route_align_small(logits, p.nz, nullptr, T, E, k, route_args(cfg), ids, tw,
@@ -430,8 +538,31 @@ moe_status moe_layer(const void* x, const void* wg, const void* w13, const void*
                           reinterpret_cast<int32_t*>(b + p.off_align), s);
     if (e != hipSuccess) return hip_status(e, "align");
   }
-  return moe_forward(x, w13, w2, tw, sorted, eids, ntpp, T, H, I, E, k, p.bm, dt,
-                     MOE_VARIANT_AUTO, out, b + p.off_fwd, forward_ws(T, H, I, k, dt), stream);
+  return forward_impl(x, w13, w13_scale, w2, w2_scale, tw, sorted, eids, ntpp, T, H, I, E, k,
+                      p.bm, dt, MOE_VARIANT_AUTO, out, b + p.off_fwd, forward_ws(T, H, I, k, dt),
+                      stream);
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status moe_layer(const void* x, const void* wg, const void* w13, const void* w2,
+                     const moe_route_cfg* cfg, int T, int H, int I, int E, int k, moe_dtype dt,
+                     void* out, int32_t* topk_ids_out, float* topk_w_out, void* ws,
+                     size_t ws_bytes, void* stream) {
+  return layer_impl(x, wg, w13, nullptr, w2, nullptr, cfg, T, H, I, E, k, dt, out, topk_ids_out,
+                    topk_w_out, ws, ws_bytes, stream);
+}
+
+moe_status moe_layer_fp8(const void* x, const void* wg, const uint8_t* w13,
+                         const float* w13_scale, const uint8_t* w2, const float* w2_scale,
+                         const moe_route_cfg* cfg, int T, int H, int I, int E, int k, void* out,
+                         int32_t* topk_ids_out, float* topk_w_out, void* ws, size_t ws_bytes,
+                         void* stream) {
+  if (!w13_scale || !w2_scale) return fail(MOE_ERR_INVALID_ARG, "NULL scale pointer");
+  return layer_impl(x, wg, w13, w13_scale, w2, w2_scale, cfg, T, H, I, E, k, MOE_BF16_FP8W, out,
+                    topk_ids_out, topk_w_out, ws, ws_bytes, stream);
 }
 
 }  // extern "C"

@@ -57,3 +57,36 @@ def compact_experts(ids: np.ndarray, w13, w2):
     w13c = np.stack([np64(w13[e]) for e in used])
     w2c = np.stack([np64(w2[e]) for e in used])
     return ids_c, w13c, w2c
+
+
+DTYPE_CODE = {"f32": 0, "bf16": 1, "bf16_fp8w": 2}
+
+
+def bf16_layer(wl) -> bool:
+    """bf16 activations (bf16 weights, or FP8 weights with bf16 activations)."""
+    return wl.dtype in ("bf16", "bf16_fp8w")
+
+
+def run_layer(lib, lay, k, cfg, **kw):
+    """moe_layer, or moe_layer_fp8 when the layer's expert weights are E4M3 codes."""
+    if lay.w13_scale is not None:
+        return lib.moe_layer_fp8(lay.x, lay.wg, lay.w13, lay.w13_scale, lay.w2, lay.w2_scale, k,
+                                 cfg, **kw)
+    return lib.moe_layer(lay.x, lay.wg, lay.w13, lay.w2, k, cfg, **kw)
+
+
+def expert_weights64(lay, experts=None):
+    """Host float64 expert weights (decoded and scaled for FP8 layers), optionally only
+    the listed experts, in that order."""
+    if lay.w13_scale is None:
+        if experts is None:
+            return np64(lay.w13), np64(lay.w2)
+        return (np.stack([np64(lay.w13[e]) for e in experts]),
+                np.stack([np64(lay.w2[e]) for e in experts]))
+    idx = torch.tensor(list(range(lay.w13.shape[0])) if experts is None else list(experts),
+                       device=lay.w13.device)
+    w13 = O.dequant_rows(lay.w13.index_select(0, idx).cpu().numpy(),
+                         lay.w13_scale.index_select(0, idx).cpu().numpy())
+    w2 = O.dequant_rows(lay.w2.index_select(0, idx).cpu().numpy(),
+                        lay.w2_scale.index_select(0, idx).cpu().numpy())
+    return w13, w2

@@ -160,3 +160,44 @@ def test_layer_workspace_and_variants(L):
         st = lib.moe_layer(FAKE, FAKE, FAKE, FAKE, ctypes.byref(c), T, H, I, E, k, dt, FAKE, None,
                            None, FAKE, ws - 1, None)
         assert st == WORKSPACE
+
+
+def test_fp8_weight_entry_points_validate(L):
+    """FP8 expert weights: scales are required, the plain entry points refuse the FP8
+    dtype (they have no scale argument), H and I must be multiples of 128, and only the
+    weight-streaming variant (block_m >= 16) takes them."""
+    lib = L.lib
+    FP8 = 2
+
+    def fwd(s13=FAKE, s2=FAKE, H=256, I=256, bm=16, var=0, ws=1 << 24):
+        return lib.moe_forward_fp8(FAKE, FAKE, s13, FAKE, s2, FAKE, FAKE, FAKE, FAKE, 4, H, I, 8,
+                                   2, bm, var, FAKE, FAKE, ws, None)
+
+    assert fwd(s13=None) == INVALID
+    assert fwd(s2=None) == INVALID
+    assert fwd(H=192) == UNSUPPORTED
+    assert fwd(I=320) == UNSUPPORTED
+    assert fwd(bm=8) == UNSUPPORTED
+    assert fwd(var=1) == UNSUPPORTED
+    assert fwd(ws=100) == WORKSPACE
+    need = lib.moe_forward_workspace_size(4, 256, 256, 8, 2, FP8)
+    assert need == lib.moe_forward_workspace_size(4, 256, 256, 8, 2, 1)   # a bf16, y fp32
+    assert fwd(ws=need - 1) == WORKSPACE
+    # the plain forward has no scales: FP8 weights are refused there
+    assert lib.moe_forward(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 256, 256, 8, 2, 16, FP8, 0,
+                           FAKE, FAKE, 1 << 24, None) == INVALID
+    assert lib.moe_gemm1_swiglu_fp8(FAKE, FAKE, None, FAKE, FAKE, FAKE, 4, 256, 256, 8, 2, 16, 0,
+                                    FAKE, None) == INVALID
+    assert lib.moe_gemm2_weighted_fp8(FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, 4, 256, 256, 8, 2,
+                                      16, 0, FAKE, None) == INVALID
+    assert lib.moe_auto_variant(4096, 4096, 14336, 8, 2, FP8) == 2
+    assert lib.moe_preferred_block_m(1, 7168, 2048, 256, 8, FP8) == 16
+    c = cfg(L, 2, ng=8, tg=4, scale=2.5)
+    ws = lib.moe_layer_workspace_size(1, 7168, 2048, 256, 8, FP8)
+    assert ws > 0
+    assert lib.moe_layer_fp8(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ctypes.byref(c), 1, 7168, 2048,
+                             256, 8, FAKE, None, None, FAKE, ws - 1, None) == WORKSPACE
+    assert lib.moe_layer_fp8(FAKE, FAKE, FAKE, None, FAKE, FAKE, ctypes.byref(c), 1, 7168, 2048,
+                             256, 8, FAKE, None, None, FAKE, ws, None) == INVALID
+    # the router and the combine take activation types only
+    assert lib.moe_combine(FAKE, 4, 256, 2, FP8, FAKE, None) == INVALID

@@ -12,8 +12,9 @@ import torch
 
 from oracle import moe_oracle as O
 from synth import inputs as S
-from tests.gpu_util import (bf16_tol_check, compact_experts, f32_tol_check, lib_cfg,
-                            logit_error_bound, np64, route_kwargs)
+from tests.gpu_util import (DTYPE_CODE, bf16_layer, bf16_tol_check, expert_weights64,
+                            f32_tol_check, lib_cfg, logit_error_bound, np64, route_kwargs,
+                            run_layer)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -25,7 +26,7 @@ def _check_layer(lib, wl, lay, n_sample, seed=0):
     cfg = lib_cfg(lib, wl, lay)
     ids = torch.empty(T, k, dtype=torch.int32, device=DEV)
     w = torch.empty(T, k, dtype=torch.float32, device=DEV)
-    out = lib.moe_layer(lay.x, lay.wg, lay.w13, lay.w2, k, cfg, topk_ids_out=ids, topk_w_out=w)
+    out = run_layer(lib, lay, k, cfg, topk_ids_out=ids, topk_w_out=w)
     torch.cuda.synchronize()
     gids = ids.cpu().numpy()
     gw = w.cpu().numpy().astype(np.float64)
@@ -41,7 +42,7 @@ def _check_layer(lib, wl, lay, n_sample, seed=0):
     logits = O.router_logits(x64, wg64)
     kw = route_kwargs(wl, lay)
     rid, rw = O.route(logits.astype(np.float32), k, wl.mode, **kw)
-    bm = lib.moe_preferred_block_m(T, wl.H, wl.I, E, k, 1 if wl.dtype == "bf16" else 0)
+    bm = lib.moe_preferred_block_m(T, wl.H, wl.I, E, k, DTYPE_CODE[wl.dtype])
     sorted_ids, expert_ids, ntpp, counts = lib.moe_align(torch.from_numpy(rid).to(DEV), E, bm)
     cap = O.align_capacity(T, k, E, bm)
     ref_al = O.align_argsort(rid, E, bm, cap)
@@ -63,10 +64,12 @@ def _check_layer(lib, wl, lay, n_sample, seed=0):
     cand = np.nonzero(same)[0]
     pick = np.unique(np.concatenate([cand[:1], cand[-1:], rng.choice(cand, min(n_sample, cand.size),
                                                                      replace=False)]))
-    ids_c, w13c, w2c = compact_experts(rid[pick], lay.w13, lay.w2)
-    ref = O.moe_loop(x64[pick], w13c, w2c, ids_c, rw[pick], round_a=wl.dtype == "bf16")
+    used = sorted(set(int(v) for v in rid[pick].reshape(-1)))
+    ids_c = np.searchsorted(np.array(used), rid[pick]).astype(np.int32)
+    w13c, w2c = expert_weights64(lay, used)
+    ref = O.moe_loop(x64[pick], w13c, w2c, ids_c, rw[pick], round_a=bf16_layer(wl))
     got = np64(out[torch.from_numpy(pick).to(DEV)])
-    if wl.dtype == "bf16":
+    if bf16_layer(wl):
         r, rel = bf16_tol_check(got, ref)
     else:
         r = f32_tol_check(got, ref)
@@ -115,6 +118,21 @@ def test_fullsize_deepseek_decode():
         wl = base.with_T(T)
         x = S.make_x(wl, device=DEV, seed=77 + T)
         sub = S.Layer(wl, x, lay.wg, lay.w13, lay.w2, lay.offset, lay.bias)
+        _check_layer(lib, wl, sub, n)
+    del lay
+    torch.cuda.empty_cache()
+
+
+def test_fullsize_deepseek_decode_fp8():
+    """DeepSeek-V3-shaped layer with FP8 (E4M3, per-row scale) expert weights."""
+    import mixture_experts_layer_27_amd as lib
+    base = S.WORKLOADS["deepseek_decode_fp8"].with_T(64)
+    lay = S.make_layer(base, device=DEV)
+    for T, n in ((1, 1), (16, 3), (64, 3)):
+        wl = base.with_T(T)
+        x = S.make_x(wl, device=DEV, seed=77 + T)
+        sub = S.Layer(wl, x, lay.wg, lay.w13, lay.w2, lay.offset, lay.bias,
+                      w13_scale=lay.w13_scale, w2_scale=lay.w2_scale)
         _check_layer(lib, wl, sub, n)
     del lay
     torch.cuda.empty_cache()

@@ -9,8 +9,8 @@ import torch
 
 from oracle import moe_oracle as O
 from synth import inputs as S
-from tests.gpu_util import (bf16_tol_check, compact_experts, f32_tol_check, lib_cfg,
-                            logit_error_bound, np64, route_kwargs)
+from tests.gpu_util import (bf16_layer, bf16_tol_check, expert_weights64, f32_tol_check,
+                            lib_cfg, logit_error_bound, np64, route_kwargs, run_layer)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -244,6 +244,74 @@ def test_forward_bf16(lib, shape, bm, variant):
     _forward_case(lib, x, wg, w13, w2, k, mode, bm, variant, off, bias, ng, tg, sc)
 
 
+# ------------------------------------------------------------------------------ FP8 weights
+
+def _fp8_weights(g, E, N, K, spread):
+    """E4M3 codes + row scales of N(0, 1/K) weights.  With ``spread`` the rows are further
+    scaled by 2^u, u uniform in {-1, 0, 1}, so a scale read for the wrong row shows.
+    Only W13 gets the spread: spread rows of W2 would make the output columns unequal
+    and its largest elements carry more than the bf16 tolerance in output rounding
+    alone; W2's amax scales still differ by tens of percent from row to row."""
+    w = torch.randn(E, N, K, generator=g) / K ** 0.5
+    if spread:
+        w = w * torch.pow(2.0, torch.randint(-1, 2, (E, N, 1), generator=g).float())
+    return S.quantize_fp8_rows(w)
+
+
+def _forward_fp8_case(lib, T, H, I, E, k, mode, bm, seed, offset=None):
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    x = torch.randn(T, H, generator=g).to(torch.bfloat16)
+    wg = (torch.randn(E, H, generator=g) / H ** 0.5).to(torch.bfloat16)
+    c13, s13 = _fp8_weights(g, E, 2 * I, H, True)
+    c2, s2 = _fp8_weights(g, E, H, I, False)
+    bias = (torch.randn(E, generator=g) * 0.3).numpy().astype(np.float32) if mode == 2 else None
+    ng, tg, sc = ((8, 4, 2.5) if E >= 64 else (4, 2, 2.5)) if mode == 2 else (0, 0, 1.0)
+    x64, wg64 = np64(x), np64(wg)
+    l32 = O.router_logits(x64, wg64).astype(np.float32)
+    ids, w = O.route(l32, k, mode, offset, bias, ng, tg, sc)
+    w32 = w.astype(np.float32)
+    ref = O.moe_loop(x64, O.dequant_rows(c13.numpy(), s13.numpy()),
+                     O.dequant_rows(c2.numpy(), s2.numpy()), ids, w32.astype(np.float64),
+                     round_a=True)
+    dx, d13, ds13, d2, ds2 = (t.to(DEV) for t in (x, c13, s13, c2, s2))
+    dids = torch.from_numpy(ids).to(DEV)
+    dw = torch.from_numpy(w32).to(DEV)
+    sorted_ids, expert_ids, ntpp, _ = lib.moe_align(dids, E, bm)
+    R = T * k
+    a = torch.full((R + 8, I), float("nan"), dtype=torch.bfloat16, device=DEV)
+    y = torch.full((R + 8, H), float("nan"), dtype=torch.float32, device=DEV)
+    lib.moe_gemm1_swiglu_fp8(dx, d13, ds13, sorted_ids, expert_ids, ntpp, k, bm, 0, a=a)
+    lib.moe_gemm2_weighted_fp8(a, d2, ds2, dw, sorted_ids, expert_ids, ntpp, T, k, bm, 0, y=y)
+    out = lib.moe_combine(y, T, k, torch.bfloat16)
+    out_fwd = lib.moe_forward_fp8(dx, d13, ds13, d2, ds2, dw, sorted_ids, expert_ids, ntpp, k, bm)
+    _sync()
+    assert not torch.isnan(a[:R]).any() and not torch.isnan(y[:R]).any()
+    assert torch.isnan(a[R:]).all() and torch.isnan(y[R:]).all()
+    assert torch.equal(out, out_fwd)
+    got = np64(out)
+    r = bf16_tol_check(got, ref)
+    assert np.mean(np.abs(got - ref)) / np.sqrt(np.mean(ref ** 2)) < 2e-3
+    return r
+
+
+FP8_SHAPES = [
+    # T, H, I, E, k, mode: K = 256-multiples take 256-element steps, the others 128
+    (1, 1024, 256, 256, 8, 2),
+    (200, 256, 256, 8, 2, 0),              # many rows per expert: sub-tiles re-read weights
+    (37, 384, 128, 16, 1, 0),              # 128-element steps in both GEMMs
+    (64, 512, 384, 32, 4, 1),
+    (24, 768, 256, 64, 8, 2),
+    (5, 640, 640, 16, 4, 0),               # K = 640: 128-element steps, 5 of them
+]
+
+
+@pytest.mark.parametrize("shape", FP8_SHAPES)
+@pytest.mark.parametrize("bm", [16, 32, 64])
+def test_forward_fp8_weights(lib, shape, bm):
+    T, H, I, E, k, mode = shape
+    _forward_fp8_case(lib, T, H, I, E, k, mode, bm, seed=T + H + I + E + bm)
+
+
 # ------------------------------------------------------------------------------ whole layer
 
 def _layer_vs_oracle(lib, wl, lay):
@@ -251,7 +319,7 @@ def _layer_vs_oracle(lib, wl, lay):
     T, k = wl.T, wl.k
     ids = torch.empty(T, k, dtype=torch.int32, device=DEV)
     w = torch.empty(T, k, dtype=torch.float32, device=DEV)
-    out = lib.moe_layer(lay.x, lay.wg, lay.w13, lay.w2, k, cfg, topk_ids_out=ids, topk_w_out=w)
+    out = run_layer(lib, lay, k, cfg, topk_ids_out=ids, topk_w_out=w)
     _sync()
     x64, wg64 = np64(lay.x), np64(lay.wg)
     ref_logits = O.router_logits(x64, wg64)
@@ -266,10 +334,10 @@ def _layer_vs_oracle(lib, wl, lay):
     assert same.mean() > 0.5
     # the reference output uses the oracle's own routing; tokens routed differently (near
     # ties within the logits' error bound) are left out of the element-wise comparison
-    ref = O.moe_loop(x64[same], np64(lay.w13), np64(lay.w2), rid[same], rw[same],
-                     round_a=wl.dtype == "bf16")
+    w13_64, w2_64 = expert_weights64(lay)
+    ref = O.moe_loop(x64[same], w13_64, w2_64, rid[same], rw[same], round_a=bf16_layer(wl))
     got = np64(out)[same]
-    if wl.dtype == "bf16":
+    if bf16_layer(wl):
         return bf16_tol_check(got, ref)
     return f32_tol_check(got, ref)
 
@@ -295,6 +363,17 @@ def test_layer_reduced(lib, name, T, scale):
     base = S.WORKLOADS[name]
     wl = base.scaled(T=T, H=base.H // scale // 64 * 64 or 64, I=base.I // scale // 64 * 64 or 64)
     lay = S.make_layer(wl, device=DEV, seed=3)
+    _layer_vs_oracle(lib, wl, lay)
+
+
+@pytest.mark.parametrize("name,T,scale", [("deepseek_decode_fp8", 1, 4),
+                                          ("deepseek_decode_fp8", 8, 4),
+                                          ("deepseek_decode_fp8", 64, 4),
+                                          ("mixtral_fp8", 96, 16)])
+def test_layer_fp8_reduced(lib, name, T, scale):
+    base = S.WORKLOADS[name]
+    wl = base.scaled(T=T, H=base.H // scale // 128 * 128, I=base.I // scale // 128 * 128)
+    lay = S.make_layer(wl, device=DEV, seed=4)
     _layer_vs_oracle(lib, wl, lay)
 
 
