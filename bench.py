@@ -11,7 +11,8 @@ there.
 
 Default workload: the Mixtral-8x7B-shaped prefill layer (T=4096, H=4096, I=14336, E=8,
 k=2, bf16), metric = useful TFLOPS = 2*T*k*3*H*I / step time.  Decode workloads report
-weight GB/s = active experts * 3*H*I*2 B / step time.
+weight GB/s = active experts * 3*H*I*2 B / step time (FP8 weights: 1 B per weight plus the
+active experts' fp32 row scales, (2I + H)*4 B each).
 """
 from __future__ import annotations
 
@@ -76,6 +77,14 @@ def measured_traffic(key: str):
     return rec["traffic_bytes_per_launch"]
 
 
+def expert_bytes(wl) -> int:
+    """Weight bytes of one expert: 3*H*I weights (2 B in bf16; 1 B in FP8 plus the fp32
+    scales of its 2I + H rows)."""
+    if wl.dtype == "bf16_fp8w":
+        return 3 * wl.H * wl.I + (2 * wl.I + wl.H) * 4
+    return 3 * wl.H * wl.I * (4 if wl.dtype == "f32" else 2)
+
+
 def cpu_baseline(wl, lay, sample_T):
     """Time the CPU oracle (routing + per-expert loop) on the first sample_T tokens."""
     import numpy as np
@@ -87,19 +96,25 @@ def cpu_baseline(wl, lay, sample_T):
         cores = os.cpu_count() or 1
     x = lay.x[:sample_T].float().cpu().numpy()
     wg = lay.wg.float().cpu().numpy()
-    w13 = lay.w13.float().cpu().numpy()
-    w2 = lay.w2.float().cpu().numpy()
     kw = dict(offset=None if lay.offset is None else lay.offset.cpu().numpy(),
               bias=None if lay.bias is None else lay.bias.cpu().numpy(),
-              n_group=wl.n_group, topk_group=wl.topk_group, scaling=wl.scaling,
-              round_a=wl.dtype == "bf16")
-    t0 = time.perf_counter()
-    out, ids, _, _ = O.moe_layer(x, wg, w13, w2, wl.k, wl.mode, **kw)
+              n_group=wl.n_group, topk_group=wl.topk_group, scaling=wl.scaling)
+    if lay.w13_scale is not None:
+        c13, s13 = lay.w13.cpu().numpy(), lay.w13_scale.cpu().numpy()
+        c2, s2 = lay.w2.cpu().numpy(), lay.w2_scale.cpu().numpy()
+        t0 = time.perf_counter()
+        out, ids, _, _ = O.moe_layer_fp8(x, wg, c13, s13, c2, s2, wl.k, wl.mode, **kw)
+    else:
+        w13 = lay.w13.float().cpu().numpy()
+        w2 = lay.w2.float().cpu().numpy()
+        t0 = time.perf_counter()
+        out, ids, _, _ = O.moe_layer(x, wg, w13, w2, wl.k, wl.mode, round_a=wl.dtype == "bf16",
+                                     **kw)
     dt = time.perf_counter() - t0
     flops = 2 * sample_T * wl.k * 3 * wl.H * wl.I
     if wl.T <= 256:  # decode: weight bytes of the experts the sample activates
         active = len(set(ids.reshape(-1).tolist()))
-        value, unit = active * 3 * wl.H * wl.I * 2 / dt / 1e9, "GB/s"
+        value, unit = active * expert_bytes(wl) / dt / 1e9, "GB/s"
     else:
         value, unit = flops / dt / 1e12, "TFLOPS"
     return {"value": value, "unit": unit, "cores": int(cores), "kind": "oracle",
@@ -124,7 +139,9 @@ def main():
     dev = "cuda"
     lay = S.make_layer(wl, device=dev, seed=0)
     T, H, I, E, k = wl.T, wl.H, wl.I, wl.E, wl.k
-    dt = m.BF16 if wl.dtype == "bf16" else m.F32
+    fp8 = wl.dtype == "bf16_fp8w"
+    dt = {"bf16": m.BF16, "f32": m.F32, "bf16_fp8w": m.BF16_FP8W}[wl.dtype]
+    dta = m.BF16 if fp8 else dt      # activation type (router, combine)
     cfg = m.route_cfg(wl.mode, lay.offset, lay.bias, wl.n_group, wl.topk_group, wl.scaling)
     bm = args.block_m or m.moe_preferred_block_m(T, H, I, E, k, dt)
     variant = m.moe_auto_variant(T, H, I, E, k, dt)
@@ -136,7 +153,7 @@ def main():
     i32 = dict(dtype=torch.int32, device=dev)
     ids = torch.empty(T, k, **i32)
     w = torch.empty(T, k, dtype=torch.float32, device=dev)
-    rws = torch.empty(max(16, m.moe_route_workspace_size(T, H, E, dt)), dtype=torch.uint8, device=dev)
+    rws = torch.empty(max(16, m.moe_route_workspace_size(T, H, E, dta)), dtype=torch.uint8, device=dev)
     sorted_ids = torch.empty(cap, **i32)
     expert_ids = torch.empty(cap // bm, **i32)
     ntpp = torch.empty(1, **i32)
@@ -161,23 +178,31 @@ def main():
         run = lambda j: only is None or only == j
         mark(0)
         if run(0):
-            m.check(lib.moe_route(P(x), P(lay.wg), T, H, E, k, dt, ctypes.byref(cfg), P(ids), P(w),
+            m.check(lib.moe_route(P(x), P(lay.wg), T, H, E, k, dta, ctypes.byref(cfg), P(ids), P(w),
                                   None, P(rws), rws.numel(), sp), "route")
         mark(1)
         if run(1):
             m.check(lib.moe_align(P(ids), T, k, E, bm, P(sorted_ids), P(expert_ids), P(ntpp),
                                   P(counts), P(aws), aws.numel(), sp), "align")
         mark(2)
-        if run(2):
+        if run(2) and fp8:
+            m.check(lib.moe_gemm1_swiglu_fp8(P(x), P(lay.w13), P(lay.w13_scale), P(sorted_ids),
+                                             P(expert_ids), P(ntpp), T, H, I, E, k, bm, variant,
+                                             P(a), sp), "gemm1")
+        elif run(2):
             m.check(lib.moe_gemm1_swiglu(P(x), P(lay.w13), P(sorted_ids), P(expert_ids), P(ntpp), T,
                                          H, I, E, k, bm, dt, variant, P(a), sp), "gemm1")
         mark(3)
-        if run(3):
+        if run(3) and fp8:
+            m.check(lib.moe_gemm2_weighted_fp8(P(a), P(lay.w2), P(lay.w2_scale), P(w),
+                                               P(sorted_ids), P(expert_ids), P(ntpp), T, H, I, E,
+                                               k, bm, variant, P(y), sp), "gemm2")
+        elif run(3):
             m.check(lib.moe_gemm2_weighted(P(a), P(lay.w2), P(w), P(sorted_ids), P(expert_ids),
                                            P(ntpp), T, H, I, E, k, bm, dt, variant, P(y), sp), "gemm2")
         mark(4)
         if run(4):
-            m.check(lib.moe_combine(P(y), T, H, k, dt, P(out), sp), "combine")
+            m.check(lib.moe_combine(P(y), T, H, k, dta, P(out), sp), "combine")
         mark(5)
 
     def launch(i, sp):
@@ -185,6 +210,11 @@ def main():
         if staged:
             return launch_staged(i, sp)
         x = xs[i % nx]
+        if fp8:
+            m.check(lib.moe_layer_fp8(P(x), P(lay.wg), P(lay.w13), P(lay.w13_scale), P(lay.w2),
+                                      P(lay.w2_scale), ctypes.byref(cfg), T, H, I, E, k, P(out),
+                                      P(ids), P(w), P(lws), lws.numel(), sp), "layer")
+            return
         m.check(lib.moe_layer(P(x), P(lay.wg), P(lay.w13), P(lay.w2), ctypes.byref(cfg), T, H, I, E,
                               k, dt, P(out), P(ids), P(w), P(lws), lws.numel(), sp), "layer")
 
@@ -285,9 +315,10 @@ def main():
             launch(i, cur_sp())
             act.append(int(torch.unique(ids).numel()))
         n_act = sum(act) / len(act)
-        wbytes = n_act * 3 * H * I * 2
+        wbytes = n_act * expert_bytes(wl)
         value, unit = wbytes / (ms * 1e-3) / 1e9, "GB/s"
-        g1_bytes = n_act * 2 * I * H * 2
+        # GEMM1 streams W13: 2I*H weights (+ 2I row scales with FP8 weights)
+        g1_bytes = n_act * (2 * I * H + 2 * I * 4 if fp8 else 2 * I * H * 2)
         roof = {"bound": "hbm", "achieved": g1_bytes / (g1_ms * 1e-3) / 1e9, "peak": PEAK_HBM_GBS,
                 "unit": "GB/s", "traffic": measured_traffic(f"{wl.name}_T{T}")}
     else:

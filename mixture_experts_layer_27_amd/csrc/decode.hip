@@ -400,12 +400,13 @@ hipError_t launch_decode_bf16(const DArgs& p, const GemmArgs& g, hipStream_t s) 
                         : launch_decode<MODE, NTG, 64, NT, 2, P>(p, g, s);
 }
 
-// FP8 weights: 256-element steps (256-byte weight rows, 512-byte token rows) when K
-// allows, else 128 (K % 128 == 0 is checked by the caller)
+// FP8 weights: 128-element steps (128-byte weight rows, 256-byte token rows; K % 128 == 0
+// is checked by the caller).  Measured on the DeepSeek-V3 layer: a 4-slot ring at three
+// waves per CU streams faster than 256-element steps (which fit one or two waves per CU)
+// at every batch size; 32-row sub-tiles need the 3-slot ring to keep three waves.
 template <int MODE, int NTG, bool NT>
 hipError_t launch_decode_fp8(const DArgs& p, const GemmArgs& g, hipStream_t s) {
-  return p.K % 256 == 0 ? launch_decode<MODE, NTG, 256, NT, 1, 3>(p, g, s)
-                        : launch_decode<MODE, NTG, 128, NT, 1, 4>(p, g, s);
+  return launch_decode<MODE, NTG, 128, NT, 1, NTG == 1 ? 4 : 3>(p, g, s);
 }
 
 template <int MODE, int NTG, bool NT>

@@ -295,13 +295,13 @@ def _forward_fp8_case(lib, T, H, I, E, k, mode, bm, seed, offset=None):
 
 
 FP8_SHAPES = [
-    # T, H, I, E, k, mode: K = 256-multiples take 256-element steps, the others 128
+    # T, H, I, E, k, mode (128-element K steps: K = 128 is a single step)
     (1, 1024, 256, 256, 8, 2),
     (200, 256, 256, 8, 2, 0),              # many rows per expert: sub-tiles re-read weights
-    (37, 384, 128, 16, 1, 0),              # 128-element steps in both GEMMs
+    (37, 384, 128, 16, 1, 0),              # GEMM2 K = 128: one step per item
     (64, 512, 384, 32, 4, 1),
     (24, 768, 256, 64, 8, 2),
-    (5, 640, 640, 16, 4, 0),               # K = 640: 128-element steps, 5 of them
+    (5, 640, 640, 16, 4, 0),               # K = 640: 5 steps
 ]
 
 
