@@ -147,13 +147,14 @@ moe_status moe_align(const int32_t* topk_ids, int T, int k, int E, int block_m,
 /* Variant of the expert GEMMs: 0 = automatic (from T, k, E, H, I on the host),
  * 1 = prefill (MFMA tiles staged through LDS), 2 = decode (weight streaming, small M).
  * bf16 block_m limits: prefill >= 32, decode >= 16 (MOE_ERR_UNSUPPORTED otherwise);
- * fp32 takes any block_m.  FP8 weights run on the decode variant (block_m >= 16) at
- * every T: automatic resolves to it and prefill is MOE_ERR_UNSUPPORTED. */
+ * fp32 takes any block_m.  FP8 weights: prefill block_m >= 128, decode >= 16. */
 enum { MOE_VARIANT_AUTO = 0, MOE_VARIANT_PREFILL = 1, MOE_VARIANT_DECODE = 2 };
 
-/* block_m that moe_forward's automatic variant wants moe_align to use. */
+/* block_m that moe_forward's automatic variant wants moe_align to use (0 when T < 0,
+ * E < 1, k < 1 or dt is not a moe_dtype). */
 int moe_preferred_block_m(int T, int H, int I, int E, int k, moe_dtype dt);
-/* The variant moe_forward will run for these sizes (1 or 2). */
+/* The variant moe_forward will run for these sizes (1 or 2; 0 for invalid sizes as
+ * above). */
 int moe_auto_variant(int T, int H, int I, int E, int k, moe_dtype dt);
 
 /* GEMM1 + SwiGLU: a[r, :] (dtype dt, [T*k, I]) for every non-sentinel row r of the
@@ -172,7 +173,8 @@ moe_status moe_gemm2_weighted(const void* a, const void* w2, const float* topk_w
 
 /* The same two GEMMs with FP8 expert weights (dtype MOE_BF16_FP8W: x and a bf16).
  * w13 / w2: E4M3 bytes [E,2I,H] / [E,H,I]; w13_scale [E,2I], w2_scale [E,H] fp32
- * (device, 4-byte aligned; a NULL scale is MOE_ERR_INVALID_ARG).  block_m >= 16. */
+ * (device, 4-byte aligned; a NULL scale is MOE_ERR_INVALID_ARG).  block_m limits as
+ * above (prefill >= 128, decode >= 16). */
 moe_status moe_gemm1_swiglu_fp8(const void* x, const uint8_t* w13, const float* w13_scale,
                                 const int32_t* sorted_ids, const int32_t* expert_ids,
                                 const int32_t* num_tokens_post_padded, int T, int H, int I,

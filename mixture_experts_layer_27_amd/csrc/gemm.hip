@@ -344,7 +344,7 @@ template <int MODE>
 hipError_t dispatch_bf16(const GemmArgs& g, int variant, hipStream_t s) {
   const int bm = g.block_m;
   if (variant == 2) return MODE == 1 ? launch_decode_gemm1(g, s) : launch_decode_gemm2(g, s);
-  if (g.w_scale) return hipErrorInvalidValue;     // FP8 weights: weight-streaming kernels only
+  if (g.w_scale && bm % 128 != 0) return hipErrorInvalidValue;   // FP8: pipelined tiles only
   if (bm % 256 == 0) return MODE == 1 ? launch_pipe_gemm1(g, 256, s) : launch_pipe_gemm2(g, 256, s);
   if (bm % 128 == 0) return MODE == 1 ? launch_pipe_gemm1(g, 128, s) : launch_pipe_gemm2(g, 128, s);
   if (bm % 64 == 0) return run_bf16<MODE, 64, 128, 1, 2>(g, s);

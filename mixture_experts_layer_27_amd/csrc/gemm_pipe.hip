@@ -13,6 +13,12 @@
 //   fp32 accumulator tile (up to 128 x 128 = 256 AGPRs); LDS fragments are double-buffered
 //   in registers so the MFMAs of one k16 step overlap the LDS reads of the next; GEMM1 B tiles interleave 32-row gate and up blocks so that SwiGLU
 //   runs in registers.
+// * FP8 expert weights (OCP E4M3 bytes, one fp32 scale per weight row; section 8 of the
+//   same page prices an expert at one byte per weight): the B tile is staged as bytes
+//   (64-byte LDS rows per 64-element stage, half the bf16 tile, so the 256-row tile fits
+//   a 3-stage ring), each 16-byte chunk is expanded to bf16 after the LDS read (exact)
+//   and feeds two bf16 MFMAs, and the row scales (staged in LDS with the tile's rows)
+//   multiply the fp32 accumulators in the epilogue.
 #include <type_traits>
 
 #include "common.hpp"
@@ -25,7 +31,8 @@ namespace {
 
 struct PArgs {
   const uint16_t* A;
-  const uint16_t* B;
+  const uint8_t* B;        // bf16 or E4M3 bytes
+  const float* B_scale;    // FP8 weights: per-row scales [E, 2I] or [E, H]
   void* C;
   const float* topk_w;
   const int32_t* sorted_ids;
@@ -38,39 +45,70 @@ struct PArgs {
   int n_outer;             // raster order of the tile groups (see grouped_slot)
 };
 
-template <int MODE, int BM, int BN, int WM, int WN, int BK_, int NSTAGE>
+template <int MODE, int BM, int BN, int WM, int WN, int BK_, int NSTAGE, int WB = 2>
 struct PCfg {
   static constexpr int NW = WM * WN;
   static constexpr int NT = NW * kWave;
   static constexpr int BK = BK_;                      // K elements per stage (32 or 64)
-  static constexpr int ROWB = BK * 2;                 // bytes per LDS row
-  static constexpr int CPR = BK / 8;                  // 16-byte chunks per row
-  static constexpr int RPI = kWave / CPR;             // rows per DMA instruction (1 KB)
+  static constexpr int ROWA = BK * 2;                 // bytes per LDS row of A (bf16)
+  static constexpr int ROWB = BK * WB;                // bytes per LDS row of B (bf16 / E4M3)
+  static constexpr int CPRA = ROWA / 16, CPRB = ROWB / 16;   // 16-byte chunks per row
+  static constexpr int RPIA = kWave / CPRA;           // rows per DMA instruction (1 KB)
+  static constexpr int RPIB = kWave / CPRB;
   static constexpr int KS = BK / 16;                  // k16 MFMA steps per stage
   static constexpr int WTM = BM / WM, WTN = BN / WN;
   static constexpr int FM = WTM / 32, FN = WTN / 32;
-  static constexpr int LA = BM / RPI / NW;            // DMA instructions per wave per stage (A)
-  static constexpr int LB = BN / RPI / NW;            // (B)
+  static constexpr int LA = BM / RPIA / NW;           // DMA instructions per wave per stage (A)
+  static constexpr int LB = BN / RPIB / NW;           // (B)
   static constexpr int L = LA + LB;
-  static constexpr int SA = BM * ROWB, SB = BN * ROWB;
+  static constexpr int SA = BM * ROWA, SB = BN * ROWB;
   static constexpr int STAGE = SA + SB;
+  static constexpr int EXTRA = BM * 4 + (MODE == 2 ? BM * 4 : 0) + (WB == 1 ? BN * 4 : 0);
   static_assert(BK == 32 || BK == 64, "stage depth");
-  static_assert(BM % (RPI * NW) == 0 && BN % (RPI * NW) == 0, "DMA rows per wave");
+  static_assert(WB == 2 || BK == 64, "FP8 tiles: 64-element stages (64-byte B rows)");
+  static_assert(BM % (RPIA * NW) == 0 && BN % (RPIB * NW) == 0, "DMA rows per wave");
   static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile");
   static_assert(MODE != 1 || WTN % 64 == 0, "GEMM1 wave tile holds gate/up pairs");
-  static_assert(NSTAGE >= 2 && NSTAGE * STAGE <= 160 * 1024 - BM * 4, "LDS");
+  static_assert(NSTAGE >= 2 && NSTAGE * STAGE + EXTRA <= 160 * 1024, "LDS");
 };
 
 // LDS swizzles (chunk c of row m lives at physical chunk c ^ sw(m)).  64-byte rows:
 // sw = ((m >> 1) ^ (m >> 3)) & 3; 128-byte rows: sw = (m >> 1) & 7.  Both spread the
 // MFMA operand reads (rows m..m+31 at one logical chunk) over all banks.
 __device__ __forceinline__ int sw4(int row) { return ((row >> 1) ^ (row >> 3)) & 3; }
-template <int BK>
-__device__ __forceinline__ int swz(int row) { return BK == 32 ? sw4(row) : ((row >> 1) & 7); }
-template <int BK>
+template <int ROWB>
+__device__ __forceinline__ int swz(int row) { return ROWB == 64 ? sw4(row) : ((row >> 1) & 7); }
+template <int ROWB>
 __device__ __forceinline__ int pswz(int row, int chunk) {
-  return row * (BK * 2) + ((chunk ^ swz<BK>(row)) << 4);
+  return row * ROWB + ((chunk ^ swz<ROWB>(row)) << 4);
 }
+
+// 16 E4M3 bytes -> two runs of 8 bf16 (bytes 0..7, bytes 8..15), exact
+__device__ __forceinline__ void fp8x16_to_bf16x2(const u32x4 q, bf16x8& lo, bf16x8& hi) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  bf16x2 h[8];
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    h[2 * d] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(q[d], 1.0f, false);
+    h[2 * d + 1] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(q[d], 1.0f, true);
+  }
+  lo = bf16x8{h[0][0], h[0][1], h[1][0], h[1][1], h[2][0], h[2][1], h[3][0], h[3][1]};
+  hi = bf16x8{h[4][0], h[4][1], h[5][0], h[5][1], h[6][0], h[6][1], h[7][0], h[7][1]};
+}
+
+// Register fragments of one MFMA step group: bf16 weights use one k16 step (A and B
+// chunk per lane); FP8 weights use two k16 steps per B chunk (16 E4M3 values per lane).
+template <int FM, int FN, int WB>
+struct Frags;
+template <int FM, int FN>
+struct Frags<FM, FN, 2> {
+  bf16x8 a[FM], b[FN];
+};
+template <int FM, int FN>
+struct Frags<FM, FN, 1> {
+  bf16x8 a0[FM], a1[FM];
+  u32x4 q[FN];
+};
 
 // Work-group -> (m-tile, n-block).  Work-groups are dealt round-robin over the 8 XCDs
 // (bid % 8) and each XCD runs its share in bid order, so bid = 8*j + xcd is the j-th
@@ -104,13 +142,14 @@ __device__ __forceinline__ bool grouped_slot(int bid, int mtiles, int nblocks, b
 }
 constexpr int kGroupM = 4, kGroupN = 8;
 
-template <int MODE, int BM, int BN, int WM, int WN, int BK, int NSTAGE, int PFD>
+template <int MODE, int BM, int BN, int WM, int WN, int BK, int NSTAGE, int PFD, int WB>
 __global__ void __launch_bounds__(WM * WN * 64)
 moe_gemm_pipe_kernel(PArgs p) {
-  using C = PCfg<MODE, BM, BN, WM, WN, BK, NSTAGE>;
+  using C = PCfg<MODE, BM, BN, WM, WN, BK, NSTAGE, WB>;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[NSTAGE * C::STAGE];
   __shared__ int srow[BM];
   __shared__ float swt[MODE == 2 ? BM : 1];       // GEMM2: router weight of each tile row
+  __shared__ float sscale[WB == 1 ? BN : 1];      // FP8: scale of each B tile row
   __shared__ __attribute__((aligned(256))) uint8_t pf_sink[PFD > 0 ? 256 : 4];
 
   int mt, nb;
@@ -129,64 +168,63 @@ moe_gemm_pipe_kernel(PArgs p) {
     srow[m] = r;
     if (MODE == 2) swt[m] = r < p.R ? p.topk_w[r] : 0.f;
   }
-  __syncthreads();
-
-  // DMA sources: instruction j of wave w fills tile rows RPI*(w + NW*j) .. +RPI (1 KB);
-  // lane -> row lane / CPR, physical chunk lane % CPR, logical chunk pch ^ swz(row)
-  const int lrow = lane / C::CPR, pch = lane % C::CPR;
-  const uint16_t* a_src[C::LA];
-#pragma unroll
-  for (int j = 0; j < C::LA; ++j) {
-    const int m = C::RPI * (w + C::NW * j) + lrow;
-    const int r = srow[m];
-    const int arow = r < p.R ? r / p.gather_div : 0;
-    a_src[j] = p.A + static_cast<int64_t>(arow) * K + ((pch ^ swz<BK>(m)) << 3);
-  }
-  const uint16_t* b_base = p.B + static_cast<int64_t>(e) * p.b_expert_stride;
-  const uint16_t* b_src[C::LB];
-#pragma unroll
-  for (int j = 0; j < C::LB; ++j) {
-    const int n = C::RPI * (w + C::NW * j) + lrow;
-    int brow;
+  // B tile row n -> weight row of the expert (GEMM1: 32-row gate and up blocks
+  // interleaved, so each wave's accumulators hold matching gate/up pairs); columns past
+  // N read row 0 and are never stored
+  auto b_row = [&](int n) {
     if (MODE == 1) {
       const int blk = n >> 5;
       int col = nb * (BN / 2) + (blk >> 1) * 32 + (n & 31);
       if (col >= p.N) col = 0;
-      brow = (blk & 1) ? p.I + col : col;
-    } else {
-      int col = nb * BN + n;
-      if (col >= p.N) col = 0;
-      brow = col;
+      return (blk & 1) ? p.I + col : col;
     }
-    b_src[j] = b_base + static_cast<int64_t>(brow) * K + ((pch ^ swz<BK>(n)) << 3);
+    int col = nb * BN + n;
+    if (col >= p.N) col = 0;
+    return col;
+  };
+  if (WB == 1) {
+    const int nrows = MODE == 1 ? 2 * p.I : p.N;
+    for (int n = tid; n < BN; n += C::NT)
+      sscale[n] = p.B_scale[static_cast<int64_t>(e) * nrows + b_row(n)];
+  }
+  __syncthreads();
+
+  // DMA sources: instruction j of wave w fills tile rows RPI*(w + NW*j) .. +RPI (1 KB);
+  // lane -> row lane / CPR, physical chunk lane % CPR, logical chunk pch ^ swz(row)
+  const int lrow = lane / C::CPRA, pch = lane % C::CPRA;
+  const uint16_t* a_src[C::LA];
+#pragma unroll
+  for (int j = 0; j < C::LA; ++j) {
+    const int m = C::RPIA * (w + C::NW * j) + lrow;
+    const int r = srow[m];
+    const int arow = r < p.R ? r / p.gather_div : 0;
+    a_src[j] = p.A + static_cast<int64_t>(arow) * K + ((pch ^ swz<C::ROWA>(m)) << 3);
+  }
+  const uint8_t* b_base = p.B + static_cast<int64_t>(e) * p.b_expert_stride * WB;
+  const uint8_t* b_src[C::LB];
+  const int lrowb = lane / C::CPRB, pchb = lane % C::CPRB;
+#pragma unroll
+  for (int j = 0; j < C::LB; ++j) {
+    const int n = C::RPIB * (w + C::NW * j) + lrowb;
+    b_src[j] = b_base + static_cast<int64_t>(b_row(n)) * K * WB +
+               ((pchb ^ swz<C::ROWB>(n)) << 4);
   }
 
   // L2 prefetch of stage kt+PFD: lane l of wave w touches A row and B row
   // (BM/NW)*w + l (rows wrap when a wave has fewer than 64 of them)
   const uint16_t* pfa = nullptr;
-  const uint16_t* pfb = nullptr;
+  const uint8_t* pfb = nullptr;
   if constexpr (PFD > 0) {
     const int m = (BM / C::NW) * w + lane % (BM / C::NW);
     const int r = srow[m];
     pfa = p.A + static_cast<int64_t>(r < p.R ? r / p.gather_div : 0) * K;
     const int n = (BN / C::NW) * w + lane % (BN / C::NW);
-    int brow;
-    if (MODE == 1) {
-      const int blk = n >> 5;
-      int col = nb * (BN / 2) + (blk >> 1) * 32 + (n & 31);
-      if (col >= p.N) col = 0;
-      brow = (blk & 1) ? p.I + col : col;
-    } else {
-      int col = nb * BN + n;
-      if (col >= p.N) col = 0;
-      brow = col;
-    }
-    pfb = b_base + static_cast<int64_t>(brow) * K;
+    pfb = b_base + static_cast<int64_t>(b_row(n)) * K * WB;
   }
   auto prefetch = [&](int kt) {
     if constexpr (PFD > 0) {
       prefetch_line(pfa + kt * C::BK, (MOE_LDS void*)pf_sink);
-      prefetch_line(pfb + kt * C::BK, (MOE_LDS void*)pf_sink);
+      prefetch_line(pfb + kt * C::BK * WB, (MOE_LDS void*)pf_sink);
     }
   };
   constexpr int P = PFD > 0 ? 2 : 0;      // prefetch instructions per wave per stage
@@ -199,7 +237,7 @@ moe_gemm_pipe_kernel(PArgs p) {
       dma16(a_src[j] + k0, (MOE_LDS void*)(st + 1024 * (w + C::NW * j)));
 #pragma unroll
     for (int j = 0; j < C::LB; ++j)
-      dma16(b_src[j] + k0, (MOE_LDS void*)(st + C::SA + 1024 * (w + C::NW * j)));
+      dma16(b_src[j] + k0 * WB, (MOE_LDS void*)(st + C::SA + 1024 * (w + C::NW * j)));
   };
 
   const int wm = w / WN, wn = w % WN;
@@ -212,35 +250,69 @@ moe_gemm_pipe_kernel(PArgs p) {
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
   const int nk = K / C::BK;
-  // Fragments of k16 step ks of stage kt: A rows of this wave's M slice, B rows of its
-  // N slice; lanes 0-31 take logical chunk 2*ks, lanes 32-63 chunk 2*ks+1 of each row.
-  auto read_frags = [&](int kt, int ks, bf16x8 (&fa)[C::FM], bf16x8 (&fb)[C::FN]) {
+  // Fragments of step ks of stage kt: A rows of this wave's M slice, B rows of its N
+  // slice.  bf16 weights: one k16 step per ks, lanes 0-31 take logical chunk 2*ks,
+  // lanes 32-63 chunk 2*ks+1 of each row.  FP8 weights: two k16 steps per ks (32
+  // k-elements); the sum over k does not depend on how k is dealt to the lanes, so lane
+  // half h takes the 16 consecutive k-elements 32*ks + 16h .. +15: B chunk 2*ks + h (16
+  // E4M3 values) and A chunks 4*ks + 2h (first MFMA) and 4*ks + 2h + 1 (second).
+  constexpr int NSTEP = WB == 2 ? C::KS : C::KS / 2;
+  using Fr = Frags<C::FM, C::FN, WB>;
+  auto read_frags = [&](int kt, int ks, Fr& f) {
     const uint8_t* sa = smem + (kt % NSTAGE) * C::STAGE;
     const uint8_t* sb = sa + C::SA;
-    const int ch = 2 * ks + (lane >> 5);
+    if constexpr (WB == 2) {
+      const int ch = 2 * ks + (lane >> 5);
 #pragma unroll
-    for (int i = 0; i < C::FM; ++i) {
-      const int row = wm * C::WTM + i * 32 + (lane & 31);
-      fa[i] = *reinterpret_cast<const bf16x8*>(sa + pswz<BK>(row, ch));
-    }
+      for (int i = 0; i < C::FM; ++i) {
+        const int row = wm * C::WTM + i * 32 + (lane & 31);
+        f.a[i] = *reinterpret_cast<const bf16x8*>(sa + pswz<C::ROWA>(row, ch));
+      }
 #pragma unroll
-    for (int j = 0; j < C::FN; ++j) {
-      const int row = wn * C::WTN + j * 32 + (lane & 31);
-      fb[j] = *reinterpret_cast<const bf16x8*>(sb + pswz<BK>(row, ch));
+      for (int j = 0; j < C::FN; ++j) {
+        const int row = wn * C::WTN + j * 32 + (lane & 31);
+        f.b[j] = *reinterpret_cast<const bf16x8*>(sb + pswz<C::ROWB>(row, ch));
+      }
+    } else {
+      const int h = lane >> 5;
+#pragma unroll
+      for (int i = 0; i < C::FM; ++i) {
+        const int row = wm * C::WTM + i * 32 + (lane & 31);
+        f.a0[i] = *reinterpret_cast<const bf16x8*>(sa + pswz<C::ROWA>(row, 4 * ks + 2 * h));
+        f.a1[i] = *reinterpret_cast<const bf16x8*>(sa + pswz<C::ROWA>(row, 4 * ks + 2 * h + 1));
+      }
+#pragma unroll
+      for (int j = 0; j < C::FN; ++j) {
+        const int row = wn * C::WTN + j * 32 + (lane & 31);
+        f.q[j] = *reinterpret_cast<const u32x4*>(sb + pswz<C::ROWB>(row, 2 * ks + h));
+      }
     }
   };
-  auto mfma_all = [&](const bf16x8 (&fa)[C::FM], const bf16x8 (&fb)[C::FN]) {
+  auto mfma_all = [&](const Fr& f) {
+    if constexpr (WB == 2) {
 #pragma unroll
-    for (int i = 0; i < C::FM; ++i)
+      for (int i = 0; i < C::FM; ++i)
 #pragma unroll
-      for (int j = 0; j < C::FN; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+        for (int j = 0; j < C::FN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
+    } else {
+#pragma unroll
+      for (int j = 0; j < C::FN; ++j) {
+        bf16x8 b0, b1;
+        fp8x16_to_bf16x2(f.q[j], b0, b1);
+#pragma unroll
+        for (int i = 0; i < C::FM; ++i) {
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a0[i], b0, acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a1[i], b1, acc[i][j], 0, 0, 0);
+        }
+      }
+    }
   };
 
   // Fragments are double-buffered in registers: the reads of k16 step q+1 are issued
   // before the MFMAs of step q.  sched_barrier(0) pins each group in place so the
   // scheduler does not sink the reads next to their first use (exposing LDS latency).
-  bf16x8 fa[2][C::FM], fb[2][C::FN];
+  Fr fr[2];
   using T_ = std::true_type;
   using F_ = std::false_type;
 
@@ -255,9 +327,9 @@ moe_gemm_pipe_kernel(PArgs p) {
     //   last   (kt = nk-1): no barrier.
     auto stage = [&](auto has_next, auto refill, int kt, int vm_allowed) {
 #pragma unroll
-      for (int ks = 0; ks < C::KS; ++ks) {
-        if (ks + 1 < C::KS) {
-          read_frags(kt, ks + 1, fa[(ks + 1) & 1], fb[(ks + 1) & 1]);
+      for (int ks = 0; ks < NSTEP; ++ks) {
+        if (ks + 1 < NSTEP) {
+          read_frags(kt, ks + 1, fr[(ks + 1) & 1]);
         } else if constexpr (decltype(has_next)::value) {
           // issued so far: stages 0 .. kt+NSTAGE-2; stage kt+1 must be complete, so
           // only the NSTAGE-3 stages after it may still be in flight
@@ -265,10 +337,10 @@ moe_gemm_pipe_kernel(PArgs p) {
           else wait_vm(vm_allowed);
           barrier_keep_vm();
           if constexpr (decltype(refill)::value) issue(kt + NSTAGE - 1);
-          read_frags(kt + 1, 0, fa[0], fb[0]);
+          read_frags(kt + 1, 0, fr[0]);
         }
         __builtin_amdgcn_sched_barrier(0);
-        mfma_all(fa[ks & 1], fb[ks & 1]);
+        mfma_all(fr[ks & 1]);
         __builtin_amdgcn_sched_barrier(0);
       }
     };
@@ -277,7 +349,7 @@ moe_gemm_pipe_kernel(PArgs p) {
       if (s < nk) issue(s);
     wait_vm(min(NSTAGE - 2, nk - 1) * C::L);
     barrier_keep_vm();
-    read_frags(0, 0, fa[0], fb[0]);
+    read_frags(0, 0, fr[0]);
     int kt = 0;
     for (; kt + NSTAGE <= nk; ++kt) stage(T_{}, T_{}, kt, 0);
     for (; kt + 1 < nk; ++kt) stage(T_{}, F_{}, kt, (min(kt + NSTAGE - 2, nk - 1) - (kt + 1)) * C::L);
@@ -296,12 +368,12 @@ moe_gemm_pipe_kernel(PArgs p) {
         issue(kt + 1);
         if (kt + 1 + PFD < nk) prefetch(kt + 1 + PFD);
       }
-      read_frags(kt, 0, fa[0], fb[0]);
+      read_frags(kt, 0, fr[0]);
 #pragma unroll
-      for (int ks = 0; ks < C::KS; ++ks) {
-        if (ks + 1 < C::KS) read_frags(kt, ks + 1, fa[(ks + 1) & 1], fb[(ks + 1) & 1]);
+      for (int ks = 0; ks < NSTEP; ++ks) {
+        if (ks + 1 < NSTEP) read_frags(kt, ks + 1, fr[(ks + 1) & 1]);
         __builtin_amdgcn_sched_barrier(0);
-        mfma_all(fa[ks & 1], fb[ks & 1]);
+        mfma_all(fr[ks & 1]);
         __builtin_amdgcn_sched_barrier(0);
       }
     };
@@ -331,10 +403,18 @@ moe_gemm_pipe_kernel(PArgs p) {
 #pragma unroll
       for (int q = 0; q < C::FN / 2; ++q) {
         const int lc = (wn * C::WTN) / 2 + q * 32 + (lane & 31);
+        // FP8: scales of this lane's gate and up weight rows (tile rows of fragments 2q
+        // and 2q+1)
+        const float sg = WB == 1 ? sscale[wn * C::WTN + 2 * q * 32 + (lane & 31)] : 1.f;
+        const float su = WB == 1 ? sscale[wn * C::WTN + (2 * q + 1) * 32 + (lane & 31)] : 1.f;
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const int m = wm * C::WTM + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-          const float g = acc[i][2 * q][v], u = acc[i][2 * q + 1][v];
+          float g = acc[i][2 * q][v], u = acc[i][2 * q + 1][v];
+          if (WB == 1) {
+            g *= sg;
+            u *= su;
+          }
           *reinterpret_cast<uint16_t*>(smem + m * ROWS + lc * 2) = f32_to_bf16(silu_mul_bf16path(g, u));
         }
       }
@@ -363,19 +443,22 @@ moe_gemm_pipe_kernel(PArgs p) {
 #pragma unroll
         for (int j = 0; j < C::FN; ++j) {
           const int col = nb * BN + wn * C::WTN + j * 32 + (lane & 31);
-          if (col < p.N) out[static_cast<int64_t>(r) * p.N + col] = wr * acc[i][j][v];
+          const float a = WB == 1 ? acc[i][j][v] * sscale[wn * C::WTN + j * 32 + (lane & 31)]
+                                  : acc[i][j][v];
+          if (col < p.N) out[static_cast<int64_t>(r) * p.N + col] = wr * a;
         }
       }
     }
   }
 }
 
-template <int MODE, int BM, int BN, int WM, int WN, int BK, int NSTAGE, int PFD>
+template <int MODE, int BM, int BN, int WM, int WN, int BK, int NSTAGE, int PFD, int WB = 2>
 hipError_t run_pipe(const GemmArgs& g, hipStream_t s) {
   PArgs p{};
   const bool g1 = MODE == 1;
   p.A = static_cast<const uint16_t*>(g.A);
-  p.B = static_cast<const uint16_t*>(g.B);
+  p.B = static_cast<const uint8_t*>(g.B);
+  p.B_scale = g.w_scale;
   p.C = g.C;
   p.topk_w = g.topk_w;
   p.sorted_ids = g.sorted_ids;
@@ -397,7 +480,7 @@ hipError_t run_pipe(const GemmArgs& g, hipStream_t s) {
                          ((p.nblocks + kGroupN - 1) / kGroupN);
   const int64_t G = (groups + 7) / 8 * 8 * kGroupM * kGroupN;
   if (G == 0) return hipSuccess;
-  hipLaunchKernelGGL((moe_gemm_pipe_kernel<MODE, BM, BN, WM, WN, BK, NSTAGE, PFD>),
+  hipLaunchKernelGGL((moe_gemm_pipe_kernel<MODE, BM, BN, WM, WN, BK, NSTAGE, PFD, WB>),
                      dim3(static_cast<unsigned>(G)), dim3(WM * WN * 64), 0, s, p);
   return hipGetLastError();
 }
@@ -407,12 +490,22 @@ hipError_t run_pipe(const GemmArgs& g, hipStream_t s) {
 // Tile choice for the pipelined prefill kernels; returns hipErrorInvalidValue when
 // block_m does not allow a 128/256-row tile (callers fall back to gemm.hip's tiles).
 hipError_t launch_pipe_gemm1(const GemmArgs& g, int tile_m, hipStream_t s) {
+  if (g.w_scale) {     // FP8 weights: the half-size B tile leaves room for a deeper ring
+    if (tile_m == 256) return run_pipe<1, 256, 256, 2, 2, 64, 3, 0, 1>(g, s);
+    if (tile_m == 128) return run_pipe<1, 128, 256, 2, 2, 64, 4, 0, 1>(g, s);
+    return hipErrorInvalidValue;
+  }
   if (tile_m == 256) return run_pipe<1, 256, 256, 2, 2, 64, 2, 0>(g, s);
   if (tile_m == 128) return run_pipe<1, 128, 256, 2, 2, 64, 3, 0>(g, s);
   return hipErrorInvalidValue;
 }
 
 hipError_t launch_pipe_gemm2(const GemmArgs& g, int tile_m, hipStream_t s) {
+  if (g.w_scale) {
+    if (tile_m == 256) return run_pipe<2, 256, 256, 2, 2, 64, 3, 0, 1>(g, s);
+    if (tile_m == 128) return run_pipe<2, 128, 256, 2, 2, 64, 4, 0, 1>(g, s);
+    return hipErrorInvalidValue;
+  }
   if (tile_m == 256) return run_pipe<2, 256, 256, 2, 2, 64, 2, 2>(g, s);
   if (tile_m == 128) return run_pipe<2, 128, 256, 2, 2, 64, 3, 0>(g, s);
   return hipErrorInvalidValue;

@@ -105,8 +105,7 @@ moe::RouteArgs route_args(const moe_route_cfg* cfg) {
 
 int auto_variant(int T, int H, int I, int E, int k, moe_dtype dt) {
   (void)H; (void)I;
-  if (dt == MOE_BF16_FP8W) return MOE_VARIANT_DECODE;   // the FP8-weight kernels
-  if (dt != MOE_BF16) return MOE_VARIANT_PREFILL;
+  if (dt == MOE_F32) return MOE_VARIANT_PREFILL;
   const int64_t R = static_cast<int64_t>(T) * k;
   // decode when the average expert holds at most 8 routed rows
   return R <= 8 * static_cast<int64_t>(E) ? MOE_VARIANT_DECODE : MOE_VARIANT_PREFILL;
@@ -148,10 +147,10 @@ moe_status check_gemm_common(int T, int H, int I, int E, int k, int block_m, int
     if (H % 128 || I % 128)
       return fail(MOE_ERR_UNSUPPORTED, "FP8 weights need H, I multiples of 128 (H=%d I=%d)", H, I);
     const int v = resolve_variant(variant, T, H, I, E, k, static_cast<moe_dtype>(dt));
-    if (v != MOE_VARIANT_DECODE)
-      return fail(MOE_ERR_UNSUPPORTED, "FP8 weights run on the weight-streaming kernels only");
-    if (block_m < 16)
-      return fail(MOE_ERR_UNSUPPORTED, "FP8-weight tiles need block_m >= 16 (got %d)", block_m);
+    if (v == MOE_VARIANT_PREFILL && block_m < 128)
+      return fail(MOE_ERR_UNSUPPORTED, "FP8-weight prefill tiles need block_m >= 128 (got %d)", block_m);
+    if (v == MOE_VARIANT_DECODE && block_m < 16)
+      return fail(MOE_ERR_UNSUPPORTED, "FP8-weight decode tiles need block_m >= 16 (got %d)", block_m);
   }
   if (static_cast<int64_t>(T) * k * std::max(H, I) >= (int64_t(1) << 40))
     return fail(MOE_ERR_UNSUPPORTED, "tensor too large");
@@ -276,10 +275,12 @@ moe_status moe_align(const int32_t* topk_ids, int T, int k, int E, int block_m,
 
 // ------------------------------------------------------------------------------ forward
 int moe_auto_variant(int T, int H, int I, int E, int k, moe_dtype dt) {
+  if (T < 0 || E < 1 || k < 1 || !valid_expert_dt(dt)) return 0;
   return auto_variant(T, H, I, E, k, dt);
 }
 
 int moe_preferred_block_m(int T, int H, int I, int E, int k, moe_dtype dt) {
+  if (T < 0 || E < 1 || k < 1 || !valid_expert_dt(dt)) return 0;
   return preferred_bm(T, H, I, E, k, dt);
 }
 
@@ -504,7 +505,11 @@ moe_status layer_impl(const void* x, const void* wg, const void* w13, const floa
                       const void* w2, const float* w2_scale, const moe_route_cfg* cfg, int T,
                       int H, int I, int E, int k, moe_dtype dt, void* out, int32_t* topk_ids_out,
                       float* topk_w_out, void* ws, size_t ws_bytes, void* stream) {
-  moe_status st = check_gemm_common(T, H, I, E, k, 32, dt, MOE_VARIANT_AUTO);
+  moe_status st = check_tke(T, k, E);
+  if (st != MOE_OK) return st;
+  if (!valid_expert_dt(dt)) return fail(MOE_ERR_INVALID_ARG, "dtype=%d", dt);
+  // the sizes must suit the block_m this layer aligns with
+  st = check_gemm_common(T, H, I, E, k, preferred_bm(T, H, I, E, k, dt), dt, MOE_VARIANT_AUTO);
   if (st != MOE_OK) return st;
   if ((st = check_route_cfg(cfg, E, k)) != MOE_OK) return st;
   if ((st = check_scales(dt, w13_scale, w2_scale)) != MOE_OK) return st;

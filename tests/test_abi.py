@@ -178,7 +178,8 @@ def test_fp8_weight_entry_points_validate(L):
     assert fwd(H=192) == UNSUPPORTED
     assert fwd(I=320) == UNSUPPORTED
     assert fwd(bm=8) == UNSUPPORTED
-    assert fwd(var=1) == UNSUPPORTED
+    assert fwd(var=1) == UNSUPPORTED          # prefill tiles need block_m >= 128
+    assert fwd(var=1, bm=64) == UNSUPPORTED
     assert fwd(ws=100) == WORKSPACE
     need = lib.moe_forward_workspace_size(4, 256, 256, 8, 2, FP8)
     assert need == lib.moe_forward_workspace_size(4, 256, 256, 8, 2, 1)   # a bf16, y fp32
@@ -190,8 +191,13 @@ def test_fp8_weight_entry_points_validate(L):
                                     FAKE, None) == INVALID
     assert lib.moe_gemm2_weighted_fp8(FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, 4, 256, 256, 8, 2,
                                       16, 0, FAKE, None) == INVALID
-    assert lib.moe_auto_variant(4096, 4096, 14336, 8, 2, FP8) == 2
+    assert lib.moe_auto_variant(4096, 4096, 14336, 8, 2, FP8) == 1
+    assert lib.moe_auto_variant(1, 7168, 2048, 256, 8, FP8) == 2
     assert lib.moe_preferred_block_m(1, 7168, 2048, 256, 8, FP8) == 16
+    assert lib.moe_preferred_block_m(4096, 4096, 14336, 8, 2, FP8) == 256
+    # size queries reject sizes they cannot plan for instead of dividing by E = 0
+    assert lib.moe_preferred_block_m(4, 64, 64, 0, 2, 1) == 0
+    assert lib.moe_auto_variant(4, 64, 64, 8, 0, 1) == 0
     c = cfg(L, 2, ng=8, tg=4, scale=2.5)
     ws = lib.moe_layer_workspace_size(1, 7168, 2048, 256, 8, FP8)
     assert ws > 0

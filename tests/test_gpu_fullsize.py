@@ -86,7 +86,7 @@ def test_fullsize_tiny():
 
 
 @pytest.mark.parametrize("name,n", [("mixtral", 12), ("qwen3_balanced", 6), ("qwen3_skewed", 6),
-                                    ("gptoss", 6)])
+                                    ("gptoss", 6), ("mixtral_fp8", 12)])
 def test_fullsize_prefill(name, n):
     import mixture_experts_layer_27_amd as lib
     wl = S.WORKLOADS[name]

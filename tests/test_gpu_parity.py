@@ -246,24 +246,24 @@ def test_forward_bf16(lib, shape, bm, variant):
 
 # ------------------------------------------------------------------------------ FP8 weights
 
-def _fp8_weights(g, E, N, K, spread):
-    """E4M3 codes + row scales of N(0, 1/K) weights.  With ``spread`` the rows are further
-    scaled by 2^u, u uniform in {-1, 0, 1}, so a scale read for the wrong row shows.
-    Only W13 gets the spread: spread rows of W2 would make the output columns unequal
-    and its largest elements carry more than the bf16 tolerance in output rounding
-    alone; W2's amax scales still differ by tens of percent from row to row."""
+def _fp8_weights(g, E, N, K):
+    """E4M3 codes + row scales of N(0, 1/K) weights.  Each row's scale is amax/448 times
+    2^u, u uniform in {0, 1, 2}: the codes of a row span 448, 224 or 112, so a scale
+    applied to the wrong row is off by up to 4x, while the weights themselves (codes
+    times scale) keep one distribution, as do the outputs."""
     w = torch.randn(E, N, K, generator=g) / K ** 0.5
-    if spread:
-        w = w * torch.pow(2.0, torch.randint(-1, 2, (E, N, 1), generator=g).float())
-    return S.quantize_fp8_rows(w)
+    u = torch.randint(0, 3, (E, N), generator=g).float()
+    scale = w.abs().amax(dim=-1) / S.FP8_MAX * torch.pow(2.0, u)
+    codes = (w / scale[..., None]).to(torch.float8_e4m3fn).view(torch.uint8)
+    return codes, scale
 
 
-def _forward_fp8_case(lib, T, H, I, E, k, mode, bm, seed, offset=None):
+def _forward_fp8_case(lib, T, H, I, E, k, mode, bm, seed, offset=None, variant=0):
     g = torch.Generator(device="cpu").manual_seed(seed)
     x = torch.randn(T, H, generator=g).to(torch.bfloat16)
     wg = (torch.randn(E, H, generator=g) / H ** 0.5).to(torch.bfloat16)
-    c13, s13 = _fp8_weights(g, E, 2 * I, H, True)
-    c2, s2 = _fp8_weights(g, E, H, I, False)
+    c13, s13 = _fp8_weights(g, E, 2 * I, H)
+    c2, s2 = _fp8_weights(g, E, H, I)
     bias = (torch.randn(E, generator=g) * 0.3).numpy().astype(np.float32) if mode == 2 else None
     ng, tg, sc = ((8, 4, 2.5) if E >= 64 else (4, 2, 2.5)) if mode == 2 else (0, 0, 1.0)
     x64, wg64 = np64(x), np64(wg)
@@ -280,10 +280,11 @@ def _forward_fp8_case(lib, T, H, I, E, k, mode, bm, seed, offset=None):
     R = T * k
     a = torch.full((R + 8, I), float("nan"), dtype=torch.bfloat16, device=DEV)
     y = torch.full((R + 8, H), float("nan"), dtype=torch.float32, device=DEV)
-    lib.moe_gemm1_swiglu_fp8(dx, d13, ds13, sorted_ids, expert_ids, ntpp, k, bm, 0, a=a)
-    lib.moe_gemm2_weighted_fp8(a, d2, ds2, dw, sorted_ids, expert_ids, ntpp, T, k, bm, 0, y=y)
+    lib.moe_gemm1_swiglu_fp8(dx, d13, ds13, sorted_ids, expert_ids, ntpp, k, bm, variant, a=a)
+    lib.moe_gemm2_weighted_fp8(a, d2, ds2, dw, sorted_ids, expert_ids, ntpp, T, k, bm, variant, y=y)
     out = lib.moe_combine(y, T, k, torch.bfloat16)
-    out_fwd = lib.moe_forward_fp8(dx, d13, ds13, d2, ds2, dw, sorted_ids, expert_ids, ntpp, k, bm)
+    out_fwd = lib.moe_forward_fp8(dx, d13, ds13, d2, ds2, dw, sorted_ids, expert_ids, ntpp, k, bm,
+                                  variant)
     _sync()
     assert not torch.isnan(a[:R]).any() and not torch.isnan(y[:R]).any()
     assert torch.isnan(a[R:]).all() and torch.isnan(y[R:]).all()
@@ -306,10 +307,18 @@ FP8_SHAPES = [
 
 
 @pytest.mark.parametrize("shape", FP8_SHAPES)
-@pytest.mark.parametrize("bm", [16, 32, 64])
-def test_forward_fp8_weights(lib, shape, bm):
+@pytest.mark.parametrize("bm,variant", [(16, 2), (32, 2), (64, 2), (128, 1), (256, 1)])
+def test_forward_fp8_weights(lib, shape, bm, variant):
+    """Weight-streaming (variant 2) and pipelined MFMA tiles (variant 1) on FP8 weights."""
     T, H, I, E, k, mode = shape
-    _forward_fp8_case(lib, T, H, I, E, k, mode, bm, seed=T + H + I + E + bm)
+    _forward_fp8_case(lib, T, H, I, E, k, mode, bm, seed=T + H + I + E + bm, variant=variant)
+
+
+@pytest.mark.parametrize("bm", [128, 256])
+def test_forward_fp8_prefill_many_tiles(lib, bm):
+    """Several m-tiles per expert, ragged last tiles, N = 2I over several 128-column
+    blocks plus a tail (I = 640), K = 1152 (18 stages of 64)."""
+    _forward_fp8_case(lib, 700, 1152, 640, 8, 2, 0, bm, seed=bm, variant=1)
 
 
 # ------------------------------------------------------------------------------ whole layer
@@ -369,7 +378,7 @@ def test_layer_reduced(lib, name, T, scale):
 @pytest.mark.parametrize("name,T,scale", [("deepseek_decode_fp8", 1, 4),
                                           ("deepseek_decode_fp8", 8, 4),
                                           ("deepseek_decode_fp8", 64, 4),
-                                          ("mixtral_fp8", 96, 16)])
+                                          ("mixtral_fp8", 96, 16), ("mixtral_fp8", 1024, 16)])
 def test_layer_fp8_reduced(lib, name, T, scale):
     base = S.WORKLOADS[name]
     wl = base.scaled(T=T, H=base.H // scale // 128 * 128, I=base.I // scale // 128 * 128)
