@@ -20,7 +20,8 @@ Source pages (cited by title and section):
   (sigmoid + selection-bias + group-limited routing), section 5 (the
   sorted_ids / expert_ids / padded-total contract), section 6 (GEMM1 gathers
   x rows r//k against W13[e] = [W1;W3], GEMM2 multiplies by the router weight
-  and stores at row r, combine sums the k slots), section 10 (test matrix).
+  and stores at row r, combine sums the k slots), section 10 (test matrix),
+  section 11 (exercises: counting align, expert_map for expert parallelism).
 * [CKM] "Custom Kernels for Mixture-of-Experts": device-resident dispatch
   metadata (grouped GEMM section).
 * [FMK] "fused-moe-kernel" skill page: padding ids must be >= the number of
@@ -359,6 +360,52 @@ def moe_layer_fp8(x, wg, w13_codes, w13_scale, w2_codes, w2_scale, k, mode, offs
     w2 = dequant_rows(w2_codes, w2_scale)
     return moe_layer(x, wg, w13, w2, k, mode, offset, bias, n_group, topk_group, scaling,
                      round_a=True)
+
+
+# --------------------------------------------------------------------------- expert parallelism ([MKR] s11)
+
+def align_ep(topk_ids, E, block_m, expert_map, cap=None):
+    """The align table of one GPU under expert parallelism ([MKR] s11 exercise: experts
+    not on this GPU get expert_ids = -1, and the GEMMs skip those tiles).  The table of
+    all E experts (same sorted_ids, total and counts as ``align_argsort``) with each
+    tile's owner e replaced by expert_map[e]: its index among this GPU's experts, or -1."""
+    r = align_argsort(topk_ids, E, block_m, cap)
+    emap = np.asarray(expert_map, np.int64)
+    eids = r["expert_ids"].astype(np.int64)
+    owned = eids >= 0
+    eids[owned] = emap[eids[owned]]
+    r["expert_ids"] = eids.astype(np.int32)
+    return r
+
+
+def moe_loop_ep(x, w13_local, w2_local, ids, w, expert_map, round_a=False):
+    """One GPU's share of the layer under expert parallelism: the per-expert loop over
+    the experts this GPU holds (local index l = expert_map[e], weights w13_local[l],
+    w2_local[l]); slots routed to other GPUs' experts add nothing here.  Summing the
+    shares of GPUs whose maps partition the experts gives the whole layer."""
+    x = np.asarray(x, np.float64)
+    w2_local = np.asarray(w2_local, np.float64)
+    W1, W3 = _split_w13(w13_local)
+    T, H = x.shape
+    ids = np.asarray(ids)
+    k = ids.shape[1]
+    emap = np.asarray(expert_map, np.int64)
+    flat_local = emap[ids.reshape(-1)]
+    flat_w = np.asarray(w, np.float64).reshape(-1)
+    y = np.zeros((T * k, H))
+    for l in range(W1.shape[0]):
+        rows = np.nonzero(flat_local == l)[0]
+        if rows.size == 0:
+            continue
+        xe = x[rows // k]
+        a = silu(xe @ W1[l].T) * (xe @ W3[l].T)
+        if round_a:
+            a = bf16_round(a)
+        y[rows] = flat_w[rows, None] * (a @ w2_local[l].T)
+    out = np.zeros((T, H))
+    for j in range(k):
+        out += y[j::k]
+    return out
 
 
 def expert_flops(T, k, H, I) -> int:

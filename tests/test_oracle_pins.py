@@ -453,3 +453,67 @@ def test_fp8_layer_matches_bruteforce():
     w2 = _torch_e4m3(lay.w2.numpy()) * lay.w2_scale.double().numpy()[..., None]
     ref = O.moe_bruteforce(x, w13, w2, ids, w, round_a=True)
     assert np.allclose(out, ref, rtol=1e-12, atol=1e-12)
+
+
+# ----------------------------------------------------------------------------- expert parallelism
+
+def _half_maps(E, seed):
+    """Two expert maps that split the E experts between two GPUs at random."""
+    perm = np.random.default_rng(seed).permutation(E)
+    owner = np.zeros(E, np.int64)
+    owner[perm[E // 2:]] = 1
+    maps = []
+    for g in range(2):
+        m = np.full(E, -1, np.int32)
+        mine = np.nonzero(owner == g)[0]
+        m[mine] = np.arange(mine.size)
+        maps.append(m)
+    return maps
+
+
+def test_ep_shares_sum_to_the_layer():
+    """[MKR] s11 exercise, 'half the experts remote': the two GPUs' shares add up to the
+    whole layer, and a map that keeps every expert local is the layer itself."""
+    x, wg, w1, w3, w2, k = S.page_test_case("skewed")
+    w13 = torch.cat([w1, w3], dim=1).double().numpy()
+    w2 = w2.double().numpy()
+    x = x.double().numpy()
+    l32 = O.router_logits(x, wg.double().numpy()).astype(np.float32)
+    ids, w = O.route(l32, k, O.SOFTMAX_TOPK_RENORM)
+    full = O.moe_loop(x, w13, w2, ids, w)
+    E = w13.shape[0]
+    parts = []
+    for m in _half_maps(E, 4):
+        mine = np.nonzero(m >= 0)[0]
+        order = np.argsort(m[mine])
+        parts.append(O.moe_loop_ep(x, w13[mine[order]], w2[mine[order]], ids, w, m))
+        # each share alone misses the other half's experts
+        assert np.abs(parts[-1] - full).max() > 1e-3
+    assert np.allclose(parts[0] + parts[1], full, rtol=1e-12, atol=1e-12)
+    ident = np.arange(E, dtype=np.int32)
+    assert np.allclose(O.moe_loop_ep(x, w13, w2, ids, w, ident), full, rtol=1e-13, atol=1e-13)
+    none = np.full(E, -1, np.int32)
+    assert np.all(O.moe_loop_ep(x, w13[:0], w2[:0], ids, w, none) == 0.0)
+
+
+def test_ep_align_marks_remote_tiles():
+    """The EP table keeps the global sorted_ids and total; tiles of remote experts carry -1,
+    local ones the local index, the cap tail stays -1."""
+    ids = S.random_topk_ids(300, 8, 64, seed=3, skew=0.8).numpy()
+    for bm in (16, 64):
+        cap = O.align_capacity(300, 8, 64, bm)
+        ref = O.align_argsort(ids, 64, bm, cap)
+        for m in _half_maps(64, bm):
+            r = O.align_ep(ids, 64, bm, m, cap)
+            assert np.array_equal(r["sorted_ids"], ref["sorted_ids"])
+            assert r["total"] == ref["total"]
+            nt = ref["total"] // bm
+            for p in range(cap // bm):
+                e = ref["expert_ids"][p]
+                assert r["expert_ids"][p] == (m[e] if p < nt else -1)
+            # every routed row of a local expert sits in a tile marked with its local index
+            for p in range(nt):
+                rows = r["sorted_ids"][p * bm:(p + 1) * bm]
+                rows = rows[rows < ids.size]
+                owner = m[ids.reshape(-1)[rows]]
+                assert np.all(owner == r["expert_ids"][p])
