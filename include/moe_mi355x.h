@@ -138,11 +138,28 @@ moe_status moe_align(const int32_t* topk_ids, int T, int k, int E, int block_m,
                      int32_t* num_tokens_post_padded, int32_t* expert_counts,
                      void* ws, size_t ws_bytes, void* stream);
 
+/* Align for one GPU of an expert-parallel layer (section 11 exercise of the routing/
+ * grouped GEMM page: experts not on this GPU get expert_ids = -1 and the GEMMs skip
+ * their tiles).  expert_map [E] int32 (device, not NULL): expert_map[e] is e's index
+ * among this GPU's experts, or -1 when another GPU holds it.  The table is moe_align's
+ * (same sorted_ids, total and counts) with each tile's owner e replaced by
+ * expert_map[e].  Precondition (not checked on the device): the values are -1 or in
+ * [0, E_local), E_local being the number of experts in the weights the GEMMs get. */
+moe_status moe_align_ep(const int32_t* topk_ids, int T, int k, int E, int block_m,
+                        const int32_t* expert_map, int32_t* sorted_ids, int32_t* expert_ids,
+                        int32_t* num_tokens_post_padded, int32_t* expert_counts, void* ws,
+                        size_t ws_bytes, void* stream);
+
 /* ---------------------------------------------------------------------------------- */
 /* Expert computation ("Mixture-of-Experts Kernels: ...", section 6).
  * Tiles past the device-side padded total exit at once; sentinel rows are never
  * stored; tiles of an expert with no rows do not exist, so its weights are never
- * read. */
+ * read.  E is the expert count the table was built for (it sizes the grids through
+ * the table's capacity).  Weights are indexed by the table's expert ids: with a
+ * moe_align_ep table E is the global count while the weights hold this GPU's experts
+ * only ([E_local, ...]); tiles marked -1 are skipped by GEMM1
+ * and GEMM2 writes zeros into their rows of y, so the combine yields this GPU's share
+ * (the shares of GPUs whose maps partition the experts add up to the layer). */
 
 /* Variant of the expert GEMMs: 0 = automatic (from T, k, E, H, I on the host),
  * 1 = prefill (MFMA tiles staged through LDS), 2 = decode (weight streaming, small M).
@@ -226,6 +243,18 @@ moe_status moe_layer_fp8(const void* x, const void* wg, const uint8_t* w13,
                          const moe_route_cfg* cfg, int T, int H, int I, int E, int k, void* out,
                          int32_t* topk_ids_out, float* topk_w_out, void* ws, size_t ws_bytes,
                          void* stream);
+
+/* One GPU's share of an expert-parallel layer: route over all E experts (Wg [E,H] is
+ * global), moe_align_ep with expert_map, then the expert GEMMs on this GPU's experts
+ * (w13 [E_local,2I,H], w2 [E_local,H,I]) and the combine; out = the sum over the slots
+ * whose experts are local.  dt: MOE_F32, MOE_BF16 (scales NULL) or MOE_BF16_FP8W (E4M3
+ * weights with their row scales [E_local,2I] / [E_local,H]).  ws: moe_layer_workspace_size
+ * (T,H,I,E,k,dt) bytes. */
+moe_status moe_layer_ep(const void* x, const void* wg, const void* w13, const float* w13_scale,
+                        const void* w2, const float* w2_scale, const int32_t* expert_map,
+                        const moe_route_cfg* cfg, int T, int H, int I, int E, int k,
+                        moe_dtype dt, void* out, int32_t* topk_ids_out, float* topk_w_out,
+                        void* ws, size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------------- */
 const char* moe_status_string(int status);

@@ -23,6 +23,7 @@ __all__ = [
     "moe_route", "moe_route_from_logits", "moe_align", "moe_align_capacity",
     "moe_gemm1_swiglu", "moe_gemm2_weighted", "moe_combine", "moe_forward", "moe_layer",
     "moe_gemm1_swiglu_fp8", "moe_gemm2_weighted_fp8", "moe_forward_fp8", "moe_layer_fp8",
+    "moe_align_ep", "moe_layer_ep",
     "moe_preferred_block_m", "moe_auto_variant", "moe_layer_workspace_size",
     "moe_forward_workspace_size", "moe_align_workspace_size", "moe_route_workspace_size",
     "route_cfg", "MoeError", "LIB_PATH",
@@ -134,6 +135,28 @@ def moe_align(topk_ids, E: int, block_m: int, out=None):
     return sorted_ids, expert_ids, ntpp, counts
 
 
+def moe_align_ep(topk_ids, E: int, block_m: int, expert_map, out=None):
+    """moe_align for one GPU of an expert-parallel layer: tiles carry expert_map[e] (the
+    expert's local index, -1 when another GPU holds it).  Returns the same four tensors."""
+    T, k = topk_ids.shape
+    cap = lib.moe_align_capacity(T, k, E, block_m)
+    dev = topk_ids.device
+    if expert_map.dtype != torch.int32 or expert_map.numel() != E:
+        raise ValueError("expert_map must be int32 [E]")
+    if out is None:
+        sorted_ids = torch.empty(max(cap, 1), dtype=torch.int32, device=dev)[:cap]
+        expert_ids = torch.empty(max(cap // block_m, 1), dtype=torch.int32, device=dev)[:cap // block_m]
+        ntpp = torch.empty(1, dtype=torch.int32, device=dev)
+        counts = torch.empty(E, dtype=torch.int32, device=dev)
+    else:
+        sorted_ids, expert_ids, ntpp, counts = out
+    ws = _ws(lib.moe_align_workspace_size(T, k, E, block_m), dev)
+    check(lib.moe_align_ep(_p(topk_ids), T, k, E, block_m, _p(expert_map), _p(sorted_ids),
+                           _p(expert_ids), _p(ntpp), _p(counts), _p(ws), ws.numel(), _stream()),
+          "moe_align_ep")
+    return sorted_ids, expert_ids, ntpp, counts
+
+
 def moe_preferred_block_m(T, H, I, E, k, dtype) -> int:
     return lib.moe_preferred_block_m(T, H, I, E, k, dtype)
 
@@ -142,9 +165,12 @@ def moe_auto_variant(T, H, I, E, k, dtype) -> int:
     return lib.moe_auto_variant(T, H, I, E, k, dtype)
 
 
-def moe_gemm1_swiglu(x, w13, sorted_ids, expert_ids, ntpp, k, block_m, variant=0, a=None):
+def moe_gemm1_swiglu(x, w13, sorted_ids, expert_ids, ntpp, k, block_m, variant=0, a=None, E=None):
+    """E: experts the align table was built for (default: w13's; under expert parallelism
+    the global count, while w13 holds this GPU's experts)."""
     T, H = x.shape
-    E, I2, _ = w13.shape
+    El, I2, _ = w13.shape
+    E = El if E is None else E
     I = I2 // 2
     if a is None:
         a = torch.zeros(T * k, I, dtype=x.dtype, device=x.device)
@@ -155,8 +181,9 @@ def moe_gemm1_swiglu(x, w13, sorted_ids, expert_ids, ntpp, k, block_m, variant=0
 
 
 def moe_gemm2_weighted(a, w2, topk_w, sorted_ids, expert_ids, ntpp, T, k, block_m, variant=0,
-                       y=None):
-    E, H, I = w2.shape
+                       y=None, E=None):
+    El, H, I = w2.shape
+    E = El if E is None else E
     if y is None:
         y = torch.zeros(T * k, H, dtype=torch.float32, device=a.device)
     check(lib.moe_gemm2_weighted(_p(a), _p(w2), _p(topk_w), _p(sorted_ids), _p(expert_ids),
@@ -178,9 +205,12 @@ def moe_forward_workspace_size(T, H, I, E, k, dtype) -> int:
 
 
 def moe_forward(x, w13, w2, topk_w, sorted_ids, expert_ids, ntpp, k, block_m, variant=0,
-                out=None, ws=None):
+                out=None, ws=None, E=None):
+    """E: experts the align table was built for (default: w13's; the global count under
+    expert parallelism)."""
     T, H = x.shape
-    E, I2, _ = w13.shape
+    El, I2, _ = w13.shape
+    E = El if E is None else E
     I = I2 // 2
     if out is None:
         out = torch.empty(T, H, dtype=x.dtype, device=x.device)
@@ -215,9 +245,10 @@ def moe_layer(x, wg, w13, w2, k, cfg: RouteCfg, out=None, ws=None, topk_ids_out=
 # ----------------------------------------------------------------- FP8 expert weights
 
 def moe_gemm1_swiglu_fp8(x, w13, w13_scale, sorted_ids, expert_ids, ntpp, k, block_m,
-                         variant=0, a=None):
+                         variant=0, a=None, E=None):
     T, H = x.shape
-    E, I2, _ = w13.shape
+    El, I2, _ = w13.shape
+    E = El if E is None else E
     I = I2 // 2
     pw, ps = _fp8(w13, w13_scale, I2)
     if a is None:
@@ -229,8 +260,9 @@ def moe_gemm1_swiglu_fp8(x, w13, w13_scale, sorted_ids, expert_ids, ntpp, k, blo
 
 
 def moe_gemm2_weighted_fp8(a, w2, w2_scale, topk_w, sorted_ids, expert_ids, ntpp, T, k, block_m,
-                           variant=0, y=None):
-    E, H, I = w2.shape
+                           variant=0, y=None, E=None):
+    El, H, I = w2.shape
+    E = El if E is None else E
     pw, ps = _fp8(w2, w2_scale, H)
     if y is None:
         y = torch.zeros(T * k, H, dtype=torch.float32, device=a.device)
@@ -241,9 +273,10 @@ def moe_gemm2_weighted_fp8(a, w2, w2_scale, topk_w, sorted_ids, expert_ids, ntpp
 
 
 def moe_forward_fp8(x, w13, w13_scale, w2, w2_scale, topk_w, sorted_ids, expert_ids, ntpp, k,
-                    block_m, variant=0, out=None, ws=None):
+                    block_m, variant=0, out=None, ws=None, E=None):
     T, H = x.shape
-    E, I2, _ = w13.shape
+    El, I2, _ = w13.shape
+    E = El if E is None else E
     I = I2 // 2
     p13, s13 = _fp8(w13, w13_scale, I2)
     p2, s2 = _fp8(w2, w2_scale, H)
@@ -272,4 +305,31 @@ def moe_layer_fp8(x, wg, w13, w13_scale, w2, w2_scale, k, cfg: RouteCfg, out=Non
     check(lib.moe_layer_fp8(_p(x), _p(wg), p13, s13, p2, s2, ctypes.byref(cfg), T, H, I, E, k,
                             _p(out), _p(topk_ids_out), _p(topk_w_out), _p(ws), ws.numel(),
                             _stream()), "moe_layer_fp8")
+    return out
+
+
+def moe_layer_ep(x, wg, w13, w2, k, cfg: RouteCfg, expert_map, w13_scale=None, w2_scale=None,
+                 out=None, ws=None, topk_ids_out=None, topk_w_out=None):
+    """One GPU's share of an expert-parallel layer: Wg covers all E experts, w13/w2 (and
+    the row scales, for FP8 weights) hold this GPU's experts in local index order."""
+    T, H = x.shape
+    E = wg.shape[0]
+    El, I2, _ = w13.shape
+    I = I2 // 2
+    if expert_map.dtype != torch.int32 or expert_map.numel() != E:
+        raise ValueError("expert_map must be int32 [E]")
+    if w13.dtype == torch.uint8:
+        dt = BF16_FP8W
+        p13, s13 = _fp8(w13, w13_scale, I2)
+        p2, s2 = _fp8(w2, w2_scale, H)
+    else:
+        dt = _dt(x)
+        p13, s13, p2, s2 = _p(w13), None, _p(w2), None
+    if out is None:
+        out = torch.empty(T, H, dtype=x.dtype, device=x.device)
+    if ws is None:
+        ws = _ws(lib.moe_layer_workspace_size(T, H, I, E, k, dt), x.device)
+    check(lib.moe_layer_ep(_p(x), _p(wg), p13, s13, p2, s2, _p(expert_map), ctypes.byref(cfg), T,
+                           H, I, E, k, dt, _p(out), _p(topk_ids_out), _p(topk_w_out), _p(ws),
+                           ws.numel(), _stream()), "moe_layer_ep")
     return out

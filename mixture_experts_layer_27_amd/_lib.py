@@ -10,7 +10,7 @@ import os
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_mi355x.so")
 
 if not os.path.exists(LIB_PATH):
-    raise ImportError(f"{LIB_PATH} is not built; run `python -m mixture_experts_layer_27_amd.build`"
+    raise ImportError(f"{LIB_PATH} is not built; run `python mixture_experts_layer_27_amd/build.py`"
                       " (or __graft_entry__.build()) first")
 
 lib = ctypes.CDLL(LIB_PATH)
@@ -32,6 +32,7 @@ _SIGS = {
     "moe_align_capacity": (ctypes.c_int64, [_i, _i, _i, _i]),
     "moe_align_workspace_size": (_sz, [_i, _i, _i, _i]),
     "moe_align": (_i, [_p, _i, _i, _i, _i, _p, _p, _p, _p, _p, _sz, _p]),
+    "moe_align_ep": (_i, [_p, _i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _sz, _p]),
     "moe_preferred_block_m": (_i, [_i, _i, _i, _i, _i, _i]),
     "moe_auto_variant": (_i, [_i, _i, _i, _i, _i, _i]),
     "moe_gemm1_swiglu": (_i, [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _i, _p, _p]),
@@ -49,6 +50,8 @@ _SIGS = {
     "moe_layer_fp8": (_i, [_p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _p, _p, _p, _p, _sz,
                            _p]),
     "moe_layer": (_i, [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _p, _p, _p, _p, _sz, _p]),
+    "moe_layer_ep": (_i, [_p, _p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _p, _p, _p, _p,
+                          _sz, _p]),
     "moe_status_string": (ctypes.c_char_p, [_i]),
     "moe_last_error": (ctypes.c_char_p, []),
     "moe_version": (ctypes.c_char_p, []),

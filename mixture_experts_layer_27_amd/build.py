@@ -1,6 +1,8 @@
 """Build libmoe_mi355x.so in-tree with hipcc for gfx950.
 
-    python -m mixture_experts_layer_27_amd.build [-v]
+    python mixture_experts_layer_27_amd/build.py [-v]
+
+(Run it by path: importing the package loads the library it is about to rebuild.)
 """
 from __future__ import annotations
 

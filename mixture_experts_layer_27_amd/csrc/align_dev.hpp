@@ -70,17 +70,21 @@ __device__ inline void scan_padded(const int* __restrict__ cnt, int E, int bm,
   if (lane == 0) *total_out = carry;
 }
 
-// expert_ids: thread e writes the tiles of expert e ([start_e, start_e + padded_e) / bm);
-// the rest of the first cap/bm entries gets -1.
+// expert_ids: thread e writes the tiles of expert e ([start_e, start_e + padded_e) / bm)
+// with its owner: e, or emap[e] when an expert map is given (expert parallelism: the
+// expert's index among this GPU's experts, -1 for an expert held elsewhere); the rest
+// of the first cap/bm entries gets -1.
 __device__ inline void fill_expert_ids(const int* __restrict__ cnt, const int* __restrict__ start,
                                        int E, int bm, int total, int64_t cap,
-                                       int32_t* __restrict__ expert_ids) {
+                                       int32_t* __restrict__ expert_ids,
+                                       const int32_t* __restrict__ emap) {
   const int lg = log2_pow2(bm);
   for (int e = threadIdx.x; e < E; e += blockDim.x) {
     const int n = cnt[e];
     const int s = start[e];
     const int p1 = (s + n + bm - 1) >> lg;
-    for (int p = s >> lg; p < p1; ++p) expert_ids[p] = e;
+    const int owner = emap ? emap[e] : e;
+    for (int p = s >> lg; p < p1; ++p) expert_ids[p] = owner;
   }
   const int ntiles_cap = static_cast<int>(cap >> lg);
   for (int p = (total >> lg) + threadIdx.x; p < ntiles_cap; p += blockDim.x) expert_ids[p] = -1;
@@ -93,7 +97,8 @@ __device__ inline void fill_expert_ids(const int* __restrict__ cnt, const int* _
 __device__ inline void align_small_body(const int32_t* ids, int R, int E, int bm, int64_t cap,
                                         int32_t* __restrict__ sorted_ids,
                                         int32_t* __restrict__ expert_ids,
-                                        int32_t* __restrict__ ntpp, int32_t* __restrict__ counts) {
+                                        int32_t* __restrict__ ntpp, int32_t* __restrict__ counts,
+                                        const int32_t* __restrict__ emap) {
   __shared__ int hist[kAlignWaves][kMaxE];   // per-wave segment histogram, later run cursors
   __shared__ int cnt[kMaxE], start[kMaxE];
   __shared__ int total_s;
@@ -130,7 +135,7 @@ __device__ inline void align_small_body(const int32_t* ids, int R, int E, int bm
     if (counts) counts[e] = cnt[e];
   }
   if (threadIdx.x == 0) *ntpp = total;
-  fill_expert_ids(cnt, start, E, bm, total, cap, expert_ids);
+  fill_expert_ids(cnt, start, E, bm, total, cap, expert_ids, emap);
   __syncthreads();
   segment_scatter(ids, r0, r1, hist[w], sorted_ids);
 }

@@ -117,14 +117,13 @@ struct Stream {
   static constexpr int NX = SUB / S::XRPI;      // token-row DMAs per step
 
   // per-lane sources of an item's DMAs at k offset 0
+  // e: the item's expert (index into the weights), >= 0
   static __device__ __forceinline__ void setup(const DArgs& p,
-                                               const int32_t* __restrict__ sorted_ids,
-                                               const int32_t* __restrict__ expert_ids, int item,
-                                               const uint8_t* (&wp)[NW],
+                                               const int32_t* __restrict__ sorted_ids, int item,
+                                               int e, const uint8_t* (&wp)[NW],
                                                const uint16_t* (&xp)[NX]) {
     const int lane = lane_id();
     const int u = item / p.nblk, blk = item - u * p.nblk;
-    const int e = expert_ids[(u * SUB) / p.block_m];
     int ids[SUB];
     load_ids<SUB>(sorted_ids, u, ids);
     const uint8_t* wb = p.A + static_cast<int64_t>(e) * p.a_expert_stride * WB;
@@ -167,6 +166,43 @@ struct Stream {
   }
 };
 
+// Expert parallelism: a tile whose expert is held by another GPU has expert_ids = -1.
+// Its items are skipped; GEMM2 writes zeros into its rows' slice of y (plain stores:
+// they only make the ring's later vmcnt waits stricter, never looser) so the combine
+// adds nothing for them.
+template <int MODE, int RB, int SUB>
+__device__ __forceinline__ void zero_item(const DArgs& p, const int32_t* __restrict__ sorted_ids,
+                                          int item) {
+  if (MODE != 2) return;
+  const int lane = lane_id();
+  const int u = item / p.nblk, blk = item - u * p.nblk;
+  int ids[SUB];
+  load_ids<SUB>(sorted_ids, u, ids);
+  static_assert(RB == 64, "16 lanes x 4 floats per row");
+#pragma unroll
+  for (int t0 = 0; t0 < SUB; t0 += 4) {
+    const int r = pick(ids, t0 + (lane >> 4));
+    if (r < p.R)
+      *reinterpret_cast<float4*>(static_cast<float*>(p.C) + static_cast<int64_t>(r) * p.H +
+                                 blk * RB + 4 * (lane & 15)) = make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+}
+
+// The first item at or after `item` (stepping by G) whose tile has an expert on this GPU;
+// its expert in e.  Returns >= nitems when there is none.  ZERO: zero-fill the skipped
+// items (done by the issue cursor, which walks every item of the wave first).
+template <int MODE, int RB, int SUB, bool ZERO>
+__device__ __forceinline__ int next_local(const DArgs& p, const int32_t* __restrict__ sorted_ids,
+                                          const int32_t* __restrict__ expert_ids, int item,
+                                          int G, int nitems, int& e) {
+  for (; item < nitems; item += G) {
+    e = expert_ids[((item / p.nblk) * SUB) / p.block_m];
+    if (e >= 0) break;
+    if (ZERO) zero_item<MODE, RB, SUB>(p, sorted_ids, item);
+  }
+  return item;
+}
+
 // The routing tables are separate __restrict__ arguments: with them the compiler may
 // read the (wave-uniform) entries with scalar loads, which count on lgkmcnt and leave
 // the vmcnt accounting of the DMA ring untouched.
@@ -198,32 +234,45 @@ moe_decode_kernel(DArgs p, const int32_t* __restrict__ sorted_ids,
   const int first = blockIdx.x;
   if (first >= G) return;
   const int nsteps = p.K / STEP;
-  const int gtot = ((nitems - 1 - first) / G + 1) * nsteps;   // this wave's steps
 
-  // issue cursor: the step the next DMA batch belongs to (it stays on the last step
-  // once everything is issued, so the ring tail re-reads it into unused slots)
+  // issue cursor: the step the next DMA batch belongs to.  Once the wave's last local
+  // item is fully issued it stays on that item's last step, so the ring tail re-reads
+  // it into slots nobody consumes.
   MOE_LDS uint8_t* lring = (MOE_LDS uint8_t*)ring;
   const uint8_t* wp[St::NW];
   const uint16_t* xp[St::NX];
-  St::setup(p, sorted_ids, expert_ids, first, wp, xp);
-  int gi = 0, iss_s = 0, iss_item = first;
-#define MOE_DECODE_ISSUE_NEXT()                                                 \
-  do {                                                                          \
-    St::issue(wp, xp, iss_s * STEP, lring + (gi % P) * SLOT);                   \
-    ++gi;                                                                       \
-    if (gi < gtot && ++iss_s == nsteps) {                                       \
-      iss_s = 0;                                                                \
-      iss_item += G;                                                            \
-      St::setup(p, sorted_ids, expert_ids, iss_item, wp, xp);                   \
-    }                                                                           \
+  int e0 = 0;
+  const int first_local = next_local<MODE, RB, SUB, true>(p, sorted_ids, expert_ids, first, G,
+                                                          nitems, e0);
+  if (first_local >= nitems) return;            // every item of this wave is remote
+  St::setup(p, sorted_ids, first_local, e0, wp, xp);
+  int gi = 0, iss_s = 0, iss_item = first_local;
+  bool iss_done = false;
+#define MOE_DECODE_ISSUE_NEXT()                                                        \
+  do {                                                                                 \
+    St::issue(wp, xp, iss_s * STEP, lring + (gi % P) * SLOT);                          \
+    ++gi;                                                                              \
+    if (!iss_done && ++iss_s == nsteps) {                                              \
+      int e_ = 0;                                                                      \
+      const int nxt = next_local<MODE, RB, SUB, true>(p, sorted_ids, expert_ids,       \
+                                                      iss_item + G, G, nitems, e_);    \
+      if (nxt >= nitems) {                                                             \
+        iss_done = true;                                                               \
+        iss_s = nsteps - 1;                                                            \
+      } else {                                                                         \
+        iss_s = 0;                                                                     \
+        iss_item = nxt;                                                                \
+        St::setup(p, sorted_ids, iss_item, e_, wp, xp);                                \
+      }                                                                                \
+    }                                                                                  \
   } while (0)
 #pragma unroll
   for (int q = 0; q < P - 1; ++q) MOE_DECODE_ISSUE_NEXT();
 
   f32x4 acc[NTG][NF];
-  int cs = 0, cmp_item = first;
+  int cs = 0, cmp_item = first_local, cmp_e = e0;
   const int tr = lane & 15;
-  for (int g = 0; g < gtot; ++g) {
+  for (int g = 0;; ++g) {
     wait_vm_c<(P - 2) * NI>();                  // step g's batch has landed in LDS
     asm volatile("" ::: "memory");
     MOE_DECODE_ISSUE_NEXT();                    // into the slot step g-1 used
@@ -299,9 +348,8 @@ moe_decode_kernel(DArgs p, const int32_t* __restrict__ sorted_ids,
       // run here, with the whole wave active (an inactive source lane reads as 0).
       float rs[NF][4];
       if (WB == 1) {
-        const int e = expert_ids[(u * SUB) / p.block_m];
         const int nrows = MODE == 1 ? 2 * p.I : p.H;
-        const float* sp = wscale + static_cast<int64_t>(e) * nrows;
+        const float* sp = wscale + static_cast<int64_t>(cmp_e) * nrows;
         int sv[RB];
 #pragma unroll
         for (int j = 0; j < RB; ++j) {
@@ -363,7 +411,9 @@ moe_decode_kernel(DArgs p, const int32_t* __restrict__ sorted_ids,
           }
         }
       }
-      cmp_item += G;
+      cmp_item = next_local<MODE, RB, SUB, false>(p, sorted_ids, expert_ids, cmp_item + G, G,
+                                                  nitems, cmp_e);
+      if (cmp_item >= nitems) break;            // the wave's last local item is done
     }
   }
   wait_vm_c<0>();                                // no DMA may land after the wave exits

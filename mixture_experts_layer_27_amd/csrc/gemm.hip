@@ -81,6 +81,19 @@ moe_gemm_bf16_kernel(KArgs p) {
   const int total = *p.ntpp;
   if (mt * BM >= total) return;
   const int e = p.expert_ids[(mt * BM) / p.block_m];
+  if (e < 0) {
+    // expert held by another GPU: GEMM1 skips the tile, GEMM2 writes zeros into its
+    // slice of y so the combine adds nothing for these rows
+    if (MODE == 2) {
+      float* out = static_cast<float*>(p.C);
+      for (int idx = threadIdx.x; idx < BM * BN; idx += blockDim.x) {
+        const int r = p.sorted_ids[static_cast<int64_t>(mt) * BM + idx / BN];
+        const int col = nb * BN + idx % BN;
+        if (r < p.R && col < p.N) out[static_cast<int64_t>(r) * p.N + col] = 0.f;
+      }
+    }
+    return;
+  }
 
   const int tid = threadIdx.x, lane = lane_id(), w = wave_id();
   const int kc = tid & 7;
@@ -235,6 +248,7 @@ gemm1_f32_kernel(const float* __restrict__ x, const float* __restrict__ w13,
   const int r = sorted_ids[pos];
   if (r >= R) return;
   const int e = expert_ids[pos / block_m];
+  if (e < 0) return;                              // expert held by another GPU
   const float* xr = x + static_cast<int64_t>(r / k) * H;
   const float* wgate = w13 + (static_cast<int64_t>(e) * 2 * I + n) * H;
   const float* wup = w13 + (static_cast<int64_t>(e) * 2 * I + I + n) * H;
@@ -259,6 +273,10 @@ gemm2_f32_kernel(const float* __restrict__ a, const float* __restrict__ w2,
   const int r = sorted_ids[pos];
   if (r >= R) return;
   const int e = expert_ids[pos / block_m];
+  if (e < 0) {                                    // expert held by another GPU
+    y[static_cast<int64_t>(r) * H + n] = 0.f;
+    return;
+  }
   const float* ar = a + static_cast<int64_t>(r) * I;
   const float* wr = w2 + (static_cast<int64_t>(e) * H + n) * I;
   float acc = 0.f;

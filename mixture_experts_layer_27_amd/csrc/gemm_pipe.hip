@@ -157,6 +157,7 @@ moe_gemm_pipe_kernel(PArgs p) {
   const int total = *p.ntpp;
   if (mt * BM >= total) return;
   const int e = p.expert_ids[(mt * BM) / p.block_m];
+  if (MODE == 1 && e < 0) return;       // expert held by another GPU: nothing to compute
 
   const int tid = threadIdx.x, lane = lane_id(), w = wave_id();
   const int K = p.K;
@@ -167,6 +168,20 @@ moe_gemm_pipe_kernel(PArgs p) {
     const int r = p.sorted_ids[static_cast<int64_t>(mt) * BM + m];
     srow[m] = r;
     if (MODE == 2) swt[m] = r < p.R ? p.topk_w[r] : 0.f;
+  }
+  if (MODE == 2 && e < 0) {
+    // expert held by another GPU: zeros in this tile's slice of y, so the combine adds
+    // nothing for these rows
+    __syncthreads();
+    float* out = static_cast<float*>(p.C);
+    for (int idx = tid; idx < BM * (BN / 4); idx += C::NT) {
+      const int m = idx / (BN / 4), col = nb * BN + (idx % (BN / 4)) * 4;
+      const int r = srow[m];
+      if (r < p.R && col < p.N)
+        *reinterpret_cast<float4*>(out + static_cast<int64_t>(r) * p.N + col) =
+            make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    return;
   }
   // B tile row n -> weight row of the expert (GEMM1: 32-row gate and up blocks
   // interleaved, so each wave's accumulators hold matching gate/up pairs); columns past

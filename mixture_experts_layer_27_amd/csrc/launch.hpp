@@ -29,13 +29,14 @@ bool route_align_fusable(int T, int k, int E);
 hipError_t launch_route_align_small(const float* logits, int nz, float* logits_out, int T, int E,
                                     int k, const RouteArgs& a, int32_t* ids, float* w, int bm,
                                     int64_t cap, int32_t* sorted_ids, int32_t* expert_ids,
-                                    int32_t* ntpp, int32_t* counts, hipStream_t s);
+                                    int32_t* ntpp, int32_t* counts, const int32_t* emap,
+                                    hipStream_t s);
 
-// align
+// align; emap (nullable, [E]): expert parallelism, tiles carry emap[e] (-1: remote)
 size_t align_ws_bytes(int R, int E);
 hipError_t launch_align(const int32_t* ids, int R, int E, int bm, int64_t cap,
                         int32_t* sorted_ids, int32_t* expert_ids, int32_t* ntpp,
-                        int32_t* counts, int32_t* ws_hist, hipStream_t s);
+                        int32_t* counts, int32_t* ws_hist, const int32_t* emap, hipStream_t s);
 
 // expert GEMMs
 struct GemmArgs {
@@ -45,7 +46,7 @@ struct GemmArgs {
   const float* topk_w;       // GEMM2 only
   const float* w_scale;      // FP8 weights: per-row scales of B ([E,2I] or [E,H]); else null
   const int32_t* sorted_ids;
-  const int32_t* expert_ids;
+  const int32_t* expert_ids;     // owner of each tile; -1: skipped (GEMM2 zero-fills its rows)
   const int32_t* ntpp;
   int T, H, I, E, k, block_m;
   int64_t cap;               // capacity of sorted_ids

@@ -250,10 +250,14 @@ size_t moe_align_workspace_size(int T, int k, int E, int block_m) {
   return round_up(moe::align_ws_bytes(T * k, E));
 }
 
-moe_status moe_align(const int32_t* topk_ids, int T, int k, int E, int block_m,
-                     int32_t* sorted_ids, int32_t* expert_ids,
-                     int32_t* num_tokens_post_padded, int32_t* expert_counts, void* ws,
-                     size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+moe_status align_impl(const int32_t* topk_ids, int T, int k, int E, int block_m,
+                      const int32_t* expert_map, int32_t* sorted_ids, int32_t* expert_ids,
+                      int32_t* num_tokens_post_padded, int32_t* expert_counts, void* ws,
+                      size_t ws_bytes, void* stream) {
   moe_status st = check_tke(T, k, E);
   if (st != MOE_OK) return st;
   if (!is_pow2(block_m) || block_m > 256)
@@ -269,8 +273,30 @@ moe_status moe_align(const int32_t* topk_ids, int T, int k, int E, int block_m,
     return fail(MOE_ERR_WORKSPACE, "align workspace needs %zu bytes", need);
   hipError_t e = moe::launch_align(topk_ids, T * k, E, block_m, cap, sorted_ids, expert_ids,
                                    num_tokens_post_padded, expert_counts,
-                                   static_cast<int32_t*>(ws), static_cast<hipStream_t>(stream));
+                                   static_cast<int32_t*>(ws), expert_map,
+                                   static_cast<hipStream_t>(stream));
   return hip_status(e, "align");
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status moe_align(const int32_t* topk_ids, int T, int k, int E, int block_m,
+                     int32_t* sorted_ids, int32_t* expert_ids,
+                     int32_t* num_tokens_post_padded, int32_t* expert_counts, void* ws,
+                     size_t ws_bytes, void* stream) {
+  return align_impl(topk_ids, T, k, E, block_m, nullptr, sorted_ids, expert_ids,
+                    num_tokens_post_padded, expert_counts, ws, ws_bytes, stream);
+}
+
+moe_status moe_align_ep(const int32_t* topk_ids, int T, int k, int E, int block_m,
+                        const int32_t* expert_map, int32_t* sorted_ids, int32_t* expert_ids,
+                        int32_t* num_tokens_post_padded, int32_t* expert_counts, void* ws,
+                        size_t ws_bytes, void* stream) {
+  if (!expert_map) return fail(MOE_ERR_INVALID_ARG, "expert_map is NULL");
+  return align_impl(topk_ids, T, k, E, block_m, expert_map, sorted_ids, expert_ids,
+                    num_tokens_post_padded, expert_counts, ws, ws_bytes, stream);
 }
 
 // ------------------------------------------------------------------------------ forward
@@ -502,7 +528,8 @@ size_t moe_layer_workspace_size(int T, int H, int I, int E, int k, moe_dtype dt)
 namespace {
 
 moe_status layer_impl(const void* x, const void* wg, const void* w13, const float* w13_scale,
-                      const void* w2, const float* w2_scale, const moe_route_cfg* cfg, int T,
+                      const void* w2, const float* w2_scale, const int32_t* expert_map,
+                      const moe_route_cfg* cfg, int T,
                       int H, int I, int E, int k, moe_dtype dt, void* out, int32_t* topk_ids_out,
                       float* topk_w_out, void* ws, size_t ws_bytes, void* stream) {
   moe_status st = check_tke(T, k, E);
@@ -534,13 +561,13 @@ moe_status layer_impl(const void* x, const void* wg, const void* w13, const floa
   if (e != hipSuccess) return hip_status(e, "router logits");
   if (p.fused_route_align) {
     e = moe::launch_route_align_small(logits, p.nz, nullptr, T, E, k, route_args(cfg), ids, tw,
-                                      p.bm, p.cap, sorted, eids, ntpp, counts, s);
+                                      p.bm, p.cap, sorted, eids, ntpp, counts, expert_map, s);
     if (e != hipSuccess) return hip_status(e, "route+align");
   } else {
     e = moe::launch_topk(logits, p.nz, nullptr, T, E, k, route_args(cfg), ids, tw, s);
     if (e != hipSuccess) return hip_status(e, "top-k");
     e = moe::launch_align(ids, T * k, E, p.bm, p.cap, sorted, eids, ntpp, counts,
-                          reinterpret_cast<int32_t*>(b + p.off_align), s);
+                          reinterpret_cast<int32_t*>(b + p.off_align), expert_map, s);
     if (e != hipSuccess) return hip_status(e, "align");
   }
   return forward_impl(x, w13, w13_scale, w2, w2_scale, tw, sorted, eids, ntpp, T, H, I, E, k,
@@ -556,8 +583,8 @@ moe_status moe_layer(const void* x, const void* wg, const void* w13, const void*
                      const moe_route_cfg* cfg, int T, int H, int I, int E, int k, moe_dtype dt,
                      void* out, int32_t* topk_ids_out, float* topk_w_out, void* ws,
                      size_t ws_bytes, void* stream) {
-  return layer_impl(x, wg, w13, nullptr, w2, nullptr, cfg, T, H, I, E, k, dt, out, topk_ids_out,
-                    topk_w_out, ws, ws_bytes, stream);
+  return layer_impl(x, wg, w13, nullptr, w2, nullptr, nullptr, cfg, T, H, I, E, k, dt, out,
+                    topk_ids_out, topk_w_out, ws, ws_bytes, stream);
 }
 
 moe_status moe_layer_fp8(const void* x, const void* wg, const uint8_t* w13,
@@ -566,7 +593,17 @@ moe_status moe_layer_fp8(const void* x, const void* wg, const uint8_t* w13,
                          int32_t* topk_ids_out, float* topk_w_out, void* ws, size_t ws_bytes,
                          void* stream) {
   if (!w13_scale || !w2_scale) return fail(MOE_ERR_INVALID_ARG, "NULL scale pointer");
-  return layer_impl(x, wg, w13, w13_scale, w2, w2_scale, cfg, T, H, I, E, k, MOE_BF16_FP8W, out,
+  return layer_impl(x, wg, w13, w13_scale, w2, w2_scale, nullptr, cfg, T, H, I, E, k,
+                    MOE_BF16_FP8W, out, topk_ids_out, topk_w_out, ws, ws_bytes, stream);
+}
+
+moe_status moe_layer_ep(const void* x, const void* wg, const void* w13, const float* w13_scale,
+                        const void* w2, const float* w2_scale, const int32_t* expert_map,
+                        const moe_route_cfg* cfg, int T, int H, int I, int E, int k,
+                        moe_dtype dt, void* out, int32_t* topk_ids_out, float* topk_w_out,
+                        void* ws, size_t ws_bytes, void* stream) {
+  if (!expert_map) return fail(MOE_ERR_INVALID_ARG, "expert_map is NULL");
+  return layer_impl(x, wg, w13, w13_scale, w2, w2_scale, expert_map, cfg, T, H, I, E, k, dt, out,
                     topk_ids_out, topk_w_out, ws, ws_bytes, stream);
 }
 

@@ -326,7 +326,7 @@ template <int NSLOT>
 __global__ void __launch_bounds__(1024)
 route_align_small_kernel(TopkParams p, int bm, int64_t cap, int32_t* __restrict__ sorted_ids,
                          int32_t* __restrict__ expert_ids, int32_t* __restrict__ ntpp,
-                         int32_t* __restrict__ counts) {
+                         int32_t* __restrict__ counts, const int32_t* __restrict__ emap) {
   __shared__ TopkLds sh[16];
   __shared__ int32_t ids_lds[kFusedMaxRows];
   __shared__ float lg[kFusedMaxT * 4 * kWave];   // summed logits [T][E], E <= 256
@@ -354,7 +354,7 @@ route_align_small_kernel(TopkParams p, int bm, int64_t cap, int32_t* __restrict_
   for (int t = w; t < p.T; t += 16) topk_token<NSLOT, 1>(q, t, sh[w], ids_lds);
   __syncthreads();
   alignd::align_small_body(ids_lds, p.T * p.k, p.E, bm, cap, sorted_ids, expert_ids, ntpp,
-                           counts);
+                           counts, emap);
 }
 
 // K slabs of the bf16 logits: at decode batch sizes enough work-groups to stream Wg
@@ -444,11 +444,12 @@ hipError_t launch_topk(const float* logits, int nz, float* logits_out, int T, in
 hipError_t launch_route_align_small(const float* logits, int nz, float* logits_out, int T, int E,
                                     int k, const RouteArgs& a, int32_t* ids, float* w, int bm,
                                     int64_t cap, int32_t* sorted_ids, int32_t* expert_ids,
-                                    int32_t* ntpp, int32_t* counts, hipStream_t s) {
+                                    int32_t* ntpp, int32_t* counts, const int32_t* emap,
+                                    hipStream_t s) {
   // E <= 256 (route_align_fusable): four experts per lane
   const TopkParams p = topk_params(logits, nz, logits_out, T, E, k, a, ids, w);
   hipLaunchKernelGGL(route_align_small_kernel<4>, dim3(1), dim3(1024), 0, s, p, bm, cap,
-                     sorted_ids, expert_ids, ntpp, counts);
+                     sorted_ids, expert_ids, ntpp, counts, emap);
   return hipGetLastError();
 }
 

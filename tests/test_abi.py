@@ -207,3 +207,23 @@ def test_fp8_weight_entry_points_validate(L):
                              256, 8, FAKE, None, None, FAKE, ws, None) == INVALID
     # the router and the combine take activation types only
     assert lib.moe_combine(FAKE, 4, 256, 2, FP8, FAKE, None) == INVALID
+
+
+def test_expert_parallel_entry_points_validate(L):
+    lib = L.lib
+    assert lib.moe_align_ep(FAKE, 4, 2, 8, 16, None, FAKE, FAKE, FAKE, None, FAKE, 1 << 20,
+                            None) == INVALID                       # the map is required
+    assert lib.moe_align_ep(FAKE, 4, 2, 8, 3, FAKE, FAKE, FAKE, FAKE, None, FAKE, 1 << 20,
+                            None) == INVALID                       # block_m not a power of two
+    c = cfg(L)
+    ws = lib.moe_layer_workspace_size(4, 64, 64, 8, 2, 1)
+    assert lib.moe_layer_ep(FAKE, FAKE, FAKE, None, FAKE, None, None, ctypes.byref(c), 4, 64, 64,
+                            8, 2, 1, FAKE, None, None, FAKE, ws, None) == INVALID
+    assert lib.moe_layer_ep(FAKE, FAKE, FAKE, None, FAKE, None, FAKE, ctypes.byref(c), 4, 64, 64,
+                            8, 2, 1, FAKE, None, None, FAKE, ws - 1, None) == WORKSPACE
+    # FP8 weights need their scales here too; bf16 weights take none
+    ws8 = lib.moe_layer_workspace_size(4, 128, 128, 8, 2, 2)
+    assert lib.moe_layer_ep(FAKE, FAKE, FAKE, None, FAKE, None, FAKE, ctypes.byref(c), 4, 128, 128,
+                            8, 2, 2, FAKE, None, None, FAKE, ws8, None) == INVALID
+    assert lib.moe_layer_ep(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ctypes.byref(c), 4, 64, 64,
+                            8, 2, 1, FAKE, None, None, FAKE, ws, None) == INVALID

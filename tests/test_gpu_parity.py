@@ -426,3 +426,141 @@ def test_layer_hip_graph_replays(lib, T, H):
         ref = lib.moe_layer(xn, lay.wg, lay.w13, lay.w2, wl.k, cfg)
         _sync()
         assert torch.equal(got, ref)
+
+
+# ------------------------------------------------------------------------------ expert parallelism
+
+def _half_map(E, seed):
+    """expert_map of one GPU holding a random half of the E experts (local indices in
+    ascending expert order), and the list of those experts."""
+    perm = np.random.default_rng(seed).permutation(E)
+    mine = np.sort(perm[: E // 2])
+    m = np.full(E, -1, np.int32)
+    m[mine] = np.arange(mine.size, dtype=np.int32)
+    return m, mine
+
+
+@pytest.mark.parametrize("bm", [16, 64, 256])
+@pytest.mark.parametrize("T,k,E,skew", [(1, 8, 256, 0.0), (64, 8, 256, 0.5), (3000, 4, 16, 1.0),
+                                        (2048, 8, 256, 0.0)])
+def test_align_ep_bitexact(lib, bm, T, k, E, skew):
+    """The page's exercise: half the experts remote; tiles carry local indices or -1."""
+    ids_np = S.random_topk_ids(T, k, E, seed=T + E + bm, skew=skew).numpy()
+    m, _ = _half_map(E, bm + T)
+    ids = torch.from_numpy(ids_np).to(DEV)
+    sorted_ids, expert_ids, ntpp, counts = lib.moe_align_ep(ids, E, bm, torch.from_numpy(m).to(DEV))
+    _sync()
+    cap = O.align_capacity(T, k, E, bm)
+    ref = O.align_ep(ids_np, E, bm, m, cap)
+    assert int(ntpp.item()) == ref["total"]
+    assert np.array_equal(counts.cpu().numpy(), ref["counts"])
+    assert np.array_equal(expert_ids.cpu().numpy(), ref["expert_ids"])
+    assert np.array_equal(sorted_ids.cpu().numpy(), ref["sorted_ids"])
+
+
+def _forward_ep_case(lib, T, H, I, E, k, bm, variant, dtype, seed):
+    """Oracle routing -> GPU align_ep + forward on this GPU's half of the experts ->
+    compare with the oracle's share; then the other half, and the two shares' sum
+    against the whole layer."""
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    x = torch.randn(T, H, generator=g)
+    wg = torch.randn(E, H, generator=g) / H ** 0.5
+    if dtype == "fp8":
+        c13, s13 = _fp8_weights(g, E, 2 * I, H)
+        c2, s2 = _fp8_weights(g, E, H, I)
+        w13_64 = O.dequant_rows(c13.numpy(), s13.numpy())
+        w2_64 = O.dequant_rows(c2.numpy(), s2.numpy())
+        x = x.to(torch.bfloat16)
+    else:
+        dt = torch.bfloat16 if dtype == "bf16" else torch.float32
+        x = x.to(dt)
+        w13 = (torch.randn(E, 2 * I, H, generator=g) / H ** 0.5).to(dt)
+        w2 = (torch.randn(E, H, I, generator=g) / I ** 0.5).to(dt)
+        w13_64, w2_64 = np64(w13), np64(w2)
+    x64 = np64(x)
+    l32 = O.router_logits(x64, np64(wg)).astype(np.float32)
+    ids, w = O.route(l32, k, O.SOFTMAX_TOPK_RENORM)
+    w32 = w.astype(np.float32)
+    round_a = dtype != "f32"
+    full = O.moe_loop(x64, w13_64, w2_64, ids, w32.astype(np.float64), round_a=round_a)
+    dx = x.to(DEV)
+    dids = torch.from_numpy(ids).to(DEV)
+    dw = torch.from_numpy(w32).to(DEV)
+    m0, mine = _half_map(E, seed)
+    rest = np.setdiff1d(np.arange(E), mine)
+    m1 = np.full(E, -1, np.int32)
+    m1[rest] = np.arange(rest.size, dtype=np.int32)
+    outs = []
+    for emap, loc in ((m0, mine), (m1, rest)):
+        ref = O.moe_loop_ep(x64, w13_64[loc], w2_64[loc], ids, w32.astype(np.float64), emap,
+                            round_a=round_a)
+        sorted_ids, expert_ids, ntpp, _ = lib.moe_align_ep(dids, E, bm,
+                                                           torch.from_numpy(emap).to(DEV))
+        sel = torch.from_numpy(loc).long()
+        if dtype == "fp8":
+            out = lib.moe_forward_fp8(dx, c13[sel].contiguous().to(DEV), s13[sel].contiguous().to(DEV),
+                                      c2[sel].contiguous().to(DEV), s2[sel].contiguous().to(DEV), dw,
+                                      sorted_ids, expert_ids, ntpp, k, bm, variant, E=E)
+        else:
+            out = lib.moe_forward(dx, w13[sel].contiguous().to(DEV), w2[sel].contiguous().to(DEV), dw,
+                                  sorted_ids, expert_ids, ntpp, k, bm, variant, E=E)
+        _sync()
+        got = np64(out)
+        if dtype == "f32":
+            # the share alone can be small where the other half dominates: compare against
+            # the whole layer's scale
+            r = np.abs(got - ref).max() / np.abs(full).max()
+            assert r <= 1e-5, f"share error {r:.3e}"
+        else:
+            rms = np.sqrt(np.mean(full ** 2))
+            r = np.abs(got - ref).max() / rms
+            assert r <= 2e-2, f"share max|d|/RMS(layer) {r:.3e}"
+        outs.append(got)
+    tot = outs[0] + outs[1]
+    if dtype == "f32":
+        f32_tol_check(tot, full)
+    else:
+        bf16_tol_check(tot, full, tol=4e-2)     # two shares, each rounded to bf16 once
+
+
+@pytest.mark.parametrize("dtype,bm,variant", [("bf16", 128, 1), ("bf16", 256, 1), ("bf16", 32, 1),
+                                              ("bf16", 16, 2), ("bf16", 32, 2), ("fp8", 128, 1),
+                                              ("fp8", 16, 2), ("fp8", 32, 2), ("f32", 16, 0)])
+@pytest.mark.parametrize("T,H,I,E,k", [(300, 256, 256, 8, 2), (24, 512, 256, 64, 8),
+                                       (1, 1024, 256, 256, 8)])
+def test_forward_ep_half_remote(lib, dtype, bm, variant, T, H, I, E, k):
+    _forward_ep_case(lib, T, H, I, E, k, bm, variant, dtype, seed=T + E + bm + variant)
+
+
+@pytest.mark.parametrize("name,T,scale", [("deepseek_decode", 8, 4), ("deepseek_decode", 64, 4),
+                                          ("mixtral", 512, 16), ("deepseek_decode_fp8", 16, 4)])
+def test_layer_ep(lib, name, T, scale):
+    """moe_layer_ep (global routing, this GPU's half of the experts) against the oracle's
+    share on tokens whose routing agrees."""
+    base = S.WORKLOADS[name]
+    q = 128 if base.dtype == "bf16_fp8w" else 64
+    wl = base.scaled(T=T, H=base.H // scale // q * q, I=base.I // scale // q * q)
+    lay = S.make_layer(wl, device=DEV, seed=6)
+    m, mine = _half_map(wl.E, T)
+    sel = torch.from_numpy(mine).long().to(DEV)
+    cfg = lib_cfg(lib, wl, lay)
+    ids = torch.empty(T, wl.k, dtype=torch.int32, device=DEV)
+    w = torch.empty(T, wl.k, dtype=torch.float32, device=DEV)
+    kw = {}
+    if lay.w13_scale is not None:
+        kw = dict(w13_scale=lay.w13_scale[sel].contiguous(), w2_scale=lay.w2_scale[sel].contiguous())
+    out = lib.moe_layer_ep(lay.x, lay.wg, lay.w13[sel].contiguous(), lay.w2[sel].contiguous(), wl.k,
+                           cfg, torch.from_numpy(m).to(DEV), topk_ids_out=ids, topk_w_out=w, **kw)
+    _sync()
+    x64, wg64 = np64(lay.x), np64(lay.wg)
+    logits = O.router_logits(x64, wg64)
+    rkw = route_kwargs(wl, lay)
+    rid, rw = O.route(logits.astype(np.float32), wl.k, wl.mode, **rkw)
+    same = np.all(ids.cpu().numpy() == rid, axis=1)
+    assert same.mean() > 0.5
+    w13_64, w2_64 = expert_weights64(lay, list(mine))
+    full13, full2 = expert_weights64(lay)
+    ref = O.moe_loop_ep(x64[same], w13_64, w2_64, rid[same], rw[same], m, round_a=True)
+    full = O.moe_loop(x64[same], full13, full2, rid[same], rw[same], round_a=True)
+    r = np.abs(np64(out)[same] - ref).max() / np.sqrt(np.mean(full ** 2))
+    assert r <= 2e-2, f"share max|d|/RMS(layer) {r:.3e}"
