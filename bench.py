@@ -44,6 +44,10 @@ def parse():
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB first (a known-size "
                          "kernel that calibrates HBM byte counters)")
+    ap.add_argument("--ep", type=int, default=1,
+                    help="expert-parallel degree: this GPU holds every ep-th expert (e %% ep "
+                         "== 0) and computes the share of the layer those experts give "
+                         "(moe_layer_ep); value counts the local experts only")
     ap.add_argument("--block-m", type=int, default=None,
                     help="align block_m (the expert GEMM tile height follows it); times the "
                          "stage-by-stage calls instead of moe_layer")
@@ -139,6 +143,18 @@ def main():
     dev = "cuda"
     lay = S.make_layer(wl, device=dev, seed=0)
     T, H, I, E, k = wl.T, wl.H, wl.I, wl.E, wl.k
+    # expert weights this GPU holds (all of them unless --ep)
+    ep = args.ep
+    emap = None
+    w13, w2, s13, s2 = lay.w13, lay.w2, lay.w13_scale, lay.w2_scale
+    if ep > 1:
+        local = torch.arange(0, E, ep, device=dev)
+        emap = torch.full((E,), -1, dtype=torch.int32, device=dev)
+        emap[local] = torch.arange(local.numel(), dtype=torch.int32, device=dev)
+        w13, w2 = w13[local].contiguous(), w2[local].contiguous()
+        if s13 is not None:
+            s13, s2 = s13[local].contiguous(), s2[local].contiguous()
+        torch.cuda.empty_cache()
     fp8 = wl.dtype == "bf16_fp8w"
     dt = {"bf16": m.BF16, "f32": m.F32, "bf16_fp8w": m.BF16_FP8W}[wl.dtype]
     dta = m.BF16 if fp8 else dt      # activation type (router, combine)
@@ -181,24 +197,27 @@ def main():
             m.check(lib.moe_route(P(x), P(lay.wg), T, H, E, k, dta, ctypes.byref(cfg), P(ids), P(w),
                                   None, P(rws), rws.numel(), sp), "route")
         mark(1)
-        if run(1):
+        if run(1) and emap is not None:
+            m.check(lib.moe_align_ep(P(ids), T, k, E, bm, P(emap), P(sorted_ids), P(expert_ids),
+                                     P(ntpp), P(counts), P(aws), aws.numel(), sp), "align")
+        elif run(1):
             m.check(lib.moe_align(P(ids), T, k, E, bm, P(sorted_ids), P(expert_ids), P(ntpp),
                                   P(counts), P(aws), aws.numel(), sp), "align")
         mark(2)
         if run(2) and fp8:
-            m.check(lib.moe_gemm1_swiglu_fp8(P(x), P(lay.w13), P(lay.w13_scale), P(sorted_ids),
+            m.check(lib.moe_gemm1_swiglu_fp8(P(x), P(w13), P(s13), P(sorted_ids),
                                              P(expert_ids), P(ntpp), T, H, I, E, k, bm, variant,
                                              P(a), sp), "gemm1")
         elif run(2):
-            m.check(lib.moe_gemm1_swiglu(P(x), P(lay.w13), P(sorted_ids), P(expert_ids), P(ntpp), T,
+            m.check(lib.moe_gemm1_swiglu(P(x), P(w13), P(sorted_ids), P(expert_ids), P(ntpp), T,
                                          H, I, E, k, bm, dt, variant, P(a), sp), "gemm1")
         mark(3)
         if run(3) and fp8:
-            m.check(lib.moe_gemm2_weighted_fp8(P(a), P(lay.w2), P(lay.w2_scale), P(w),
+            m.check(lib.moe_gemm2_weighted_fp8(P(a), P(w2), P(s2), P(w),
                                                P(sorted_ids), P(expert_ids), P(ntpp), T, H, I, E,
                                                k, bm, variant, P(y), sp), "gemm2")
         elif run(3):
-            m.check(lib.moe_gemm2_weighted(P(a), P(lay.w2), P(w), P(sorted_ids), P(expert_ids),
+            m.check(lib.moe_gemm2_weighted(P(a), P(w2), P(w), P(sorted_ids), P(expert_ids),
                                            P(ntpp), T, H, I, E, k, bm, dt, variant, P(y), sp), "gemm2")
         mark(4)
         if run(4):
@@ -210,6 +229,12 @@ def main():
         if staged:
             return launch_staged(i, sp)
         x = xs[i % nx]
+        if emap is not None:
+            m.check(lib.moe_layer_ep(P(x), P(lay.wg), P(w13), P(s13) if fp8 else None, P(w2),
+                                     P(s2) if fp8 else None, P(emap), ctypes.byref(cfg), T, H, I,
+                                     E, k, dt, P(out), P(ids), P(w), P(lws), lws.numel(), sp),
+                    "layer")
+            return
         if fp8:
             m.check(lib.moe_layer_fp8(P(x), P(lay.wg), P(lay.w13), P(lay.w13_scale), P(lay.w2),
                                       P(lay.w2_scale), ctypes.byref(cfg), T, H, I, E, k, P(out),
@@ -313,7 +338,8 @@ def main():
         act = []
         for i in range(args.steps):
             launch(i, cur_sp())
-            act.append(int(torch.unique(ids).numel()))
+            u = torch.unique(ids)
+            act.append(int(u.numel() if emap is None else (emap[u.long()] >= 0).sum()))
         n_act = sum(act) / len(act)
         wbytes = n_act * expert_bytes(wl)
         value, unit = wbytes / (ms * 1e-3) / 1e9, "GB/s"
@@ -345,7 +371,11 @@ def main():
            "roofline": roof}
     if decode:
         rec["config"]["active_experts"] = n_act
-    if not args.no_cpu_baseline:
+    if ep > 1:
+        rec["config"]["expert_parallel"] = {"degree": ep, "local_experts": int(w13.shape[0]),
+                                            "held": "experts e with e % degree == 0",
+                                            "value_counts": "local experts only"}
+    if not args.no_cpu_baseline and ep == 1:
         st = args.cpu_sample_tokens or T
         rec["cpu_baseline"] = cpu_baseline(wl, lay, st)
     print(json.dumps(rec), flush=True)

@@ -117,13 +117,13 @@ struct Stream {
   static constexpr int NX = SUB / S::XRPI;      // token-row DMAs per step
 
   // per-lane sources of an item's DMAs at k offset 0
-  // e: the item's expert (index into the weights), >= 0
+  // item = (sub-tile u of the align table, weight-row block blk); e: its expert
+  // (index into the weights), >= 0
   static __device__ __forceinline__ void setup(const DArgs& p,
-                                               const int32_t* __restrict__ sorted_ids, int item,
-                                               int e, const uint8_t* (&wp)[NW],
+                                               const int32_t* __restrict__ sorted_ids, int u,
+                                               int blk, int e, const uint8_t* (&wp)[NW],
                                                const uint16_t* (&xp)[NX]) {
     const int lane = lane_id();
-    const int u = item / p.nblk, blk = item - u * p.nblk;
     int ids[SUB];
     load_ids<SUB>(sorted_ids, u, ids);
     const uint8_t* wb = p.A + static_cast<int64_t>(e) * p.a_expert_stride * WB;
@@ -167,40 +167,112 @@ struct Stream {
 };
 
 // Expert parallelism: a tile whose expert is held by another GPU has expert_ids = -1.
-// Its items are skipped; GEMM2 writes zeros into its rows' slice of y (plain stores:
-// they only make the ring's later vmcnt waits stricter, never looser) so the combine
-// adds nothing for them.
-template <int MODE, int RB, int SUB>
-__device__ __forceinline__ void zero_item(const DArgs& p, const int32_t* __restrict__ sorted_ids,
-                                          int item) {
-  if (MODE != 2) return;
+// The persistent loop deals out the items of local sub-tiles only (so the waves stay
+// balanced however the local experts are spread over the table); GEMM2 writes zeros
+// into the rows of the other sub-tiles so the combine adds nothing for them.
+//
+// Local sub-tile table, held in lanes: lane l covers sub-tiles [l*B, l*B + B) (B <= 64,
+// so at most 4096 sub-tiles): (lo, hi) = bitmask of its local ones, pre = number of
+// local sub-tiles in lower lanes' blocks.  The q-th local sub-tile is found with one
+// ballot and scalar bit arithmetic, no memory access.
+struct LocalSubtiles {
+  uint32_t lo, hi;
+  int pre;
+  int B;
+  int count;       // local sub-tiles in the table
+};
+
+template <int SUB>
+__device__ __forceinline__ LocalSubtiles local_subtiles(const int32_t* __restrict__ expert_ids,
+                                                        int nsub, int block_m) {
   const int lane = lane_id();
-  const int u = item / p.nblk, blk = item - u * p.nblk;
-  int ids[SUB];
-  load_ids<SUB>(sorted_ids, u, ids);
-  static_assert(RB == 64, "16 lanes x 4 floats per row");
+  LocalSubtiles t;
+  t.B = (nsub + kWave - 1) / kWave;
+  uint64_t fl = 0;
+  int cnt = 0;
+  // per-lane loads, issued 8 at a time (before any DMA of the ring is in flight)
+  for (int i0 = 0; i0 < t.B; i0 += 8) {
+    int ow[8];
 #pragma unroll
-  for (int t0 = 0; t0 < SUB; t0 += 4) {
-    const int r = pick(ids, t0 + (lane >> 4));
-    if (r < p.R)
-      *reinterpret_cast<float4*>(static_cast<float*>(p.C) + static_cast<int64_t>(r) * p.H +
-                                 blk * RB + 4 * (lane & 15)) = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int i = 0; i < 8; ++i) {
+      const int u = min(lane * t.B + i0 + i, nsub - 1);
+      ow[i] = expert_ids[(u * SUB) / block_m];
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const bool in = i0 + i < t.B && lane * t.B + i0 + i < nsub;
+      if (in && ow[i] >= 0) {
+        fl |= 1ull << (i0 + i);
+        ++cnt;
+      }
+    }
   }
+  const int incl = wave_incl_scan(cnt);
+  t.pre = incl - cnt;
+  t.count = read_lane(incl, kWave - 1);
+  t.lo = static_cast<uint32_t>(fl);
+  t.hi = static_cast<uint32_t>(fl >> 32);
+  return t;
 }
 
-// The first item at or after `item` (stepping by G) whose tile has an expert on this GPU;
-// its expert in e.  Returns >= nitems when there is none.  ZERO: zero-fill the skipped
-// items (done by the issue cursor, which walks every item of the wave first).
-template <int MODE, int RB, int SUB, bool ZERO>
-__device__ __forceinline__ int next_local(const DArgs& p, const int32_t* __restrict__ sorted_ids,
-                                          const int32_t* __restrict__ expert_ids, int item,
-                                          int G, int nitems, int& e) {
-  for (; item < nitems; item += G) {
-    e = expert_ids[((item / p.nblk) * SUB) / p.block_m];
-    if (e >= 0) break;
-    if (ZERO) zero_item<MODE, RB, SUB>(p, sorted_ids, item);
+// position of the n-th (from 0) set bit of m (m has more than n set bits)
+__device__ __forceinline__ int nth_set_bit(uint64_t m, int n) {
+  int pos = 0;
+#pragma unroll
+  for (int w = 32; w >= 1; w >>= 1) {
+    const int c = __popcll(m & ((1ull << w) - 1));
+    if (n >= c) {
+      n -= c;
+      m >>= w;
+      pos += w;
+    }
   }
-  return item;
+  return pos;
+}
+
+// sub-tile index of the q-th local sub-tile (q < count; whole wave active)
+__device__ __forceinline__ int local_subtile(const LocalSubtiles& t, int q) {
+  const uint64_t below = __ballot(t.pre <= q);
+  const int l = 63 - __clzll(static_cast<long long>(below));
+  const uint64_t m = (static_cast<uint64_t>(static_cast<uint32_t>(read_lane(static_cast<int>(t.hi), l))) << 32) |
+                     static_cast<uint32_t>(read_lane(static_cast<int>(t.lo), l));
+  return l * t.B + nth_set_bit(m, q - read_lane(t.pre, l));
+}
+
+__device__ __forceinline__ bool is_local(const LocalSubtiles& t, int u) {
+  const int l = u / t.B, b = u - l * t.B;
+  const uint32_t w = static_cast<uint32_t>(read_lane(static_cast<int>(b < 32 ? t.lo : t.hi), l));
+  return (w >> (b & 31)) & 1u;
+}
+
+// GEMM2: zeros in y for the remote items among [i0, i1) of all nsub*nblk items
+// (item = sub-tile * nblk + block).  Lane group lane>>4 takes one of four rows, its 16
+// lanes the 64 floats of the block.
+template <int RB, int SUB>
+__device__ __forceinline__ void zero_range(const DArgs& p, const int32_t* __restrict__ sorted_ids,
+                                           const LocalSubtiles& lt, int i0, int i1) {
+  static_assert(RB == 64, "16 lanes x 4 floats per row");
+  const int lane = lane_id();
+  int it = i0;
+  while (it < i1) {
+    const int u = it / p.nblk;
+    const int end = min(i1, (u + 1) * p.nblk);
+    if (!is_local(lt, u)) {
+      int ids[SUB];
+      load_ids<SUB>(sorted_ids, u, ids);
+#pragma unroll
+      for (int t0 = 0; t0 < SUB; t0 += 4) {
+        const int r = pick(ids, t0 + (lane >> 4));
+        if (r < p.R) {
+          float* row = static_cast<float*>(p.C) + static_cast<int64_t>(r) * p.H;
+          for (int b = it - u * p.nblk; b < end - u * p.nblk; ++b)
+            *reinterpret_cast<float4*>(row + b * RB + 4 * (lane & 15)) =
+                make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+      }
+    }
+    it = end;
+  }
 }
 
 // The routing tables are separate __restrict__ arguments: with them the compiler may
@@ -224,55 +296,69 @@ moe_decode_kernel(DArgs p, const int32_t* __restrict__ sorted_ids,
 
   const int lane = lane_id();
   const int total = *ntpp;
-  const int nitems = (total / SUB) * p.nblk;
-  if (nitems == 0) return;
+  const int nsub = total / SUB;
+  if (nsub == 0) return;
+  const LocalSubtiles lt = local_subtiles<SUB>(expert_ids, nsub, p.block_m);
+  const int nitems = lt.count * p.nblk;         // items of local sub-tiles
   // as many waves as give every wave the same number of items (the fewest waves that
   // reach the smallest per-wave count): a wave streams at a bounded rate, so a tail of
   // waves with one item more would run at a fraction of the bandwidth
   const int per = (nitems + gridDim.x - 1) / gridDim.x;
-  const int G = per > 0 ? (nitems + per - 1) / per : 1;
+  const int G = per > 0 ? (nitems + per - 1) / per : 0;
   const int first = blockIdx.x;
+  if (MODE == 2 && lt.count < nsub) {
+    // zeros for the rows of remote sub-tiles: the waves left without local items share
+    // them in contiguous ranges (the sub-tile's row ids are loaded once per sub-tile);
+    // when every wave streams, each adds an equal share after its own items
+    const int64_t nz = static_cast<int64_t>(nsub) * p.nblk;
+    const int idle = gridDim.x - G;
+    if (idle > 0 && first >= G) {
+      const int w = first - G;
+      zero_range<RB, SUB>(p, sorted_ids, lt, static_cast<int>(nz * w / idle),
+                          static_cast<int>(nz * (w + 1) / idle));
+      return;
+    }
+  }
   if (first >= G) return;
   const int nsteps = p.K / STEP;
+  const int gtot = ((nitems - 1 - first) / G + 1) * nsteps;   // this wave's steps
 
-  // issue cursor: the step the next DMA batch belongs to.  Once the wave's last local
-  // item is fully issued it stays on that item's last step, so the ring tail re-reads
-  // it into slots nobody consumes.
+  // local item j -> (sub-tile, block, expert)
+#define MOE_DECODE_ITEM(j, u, blk, e)                                                 \
+  do {                                                                                \
+    const int q_ = (j) / p.nblk;                                                      \
+    blk = (j) - q_ * p.nblk;                                                          \
+    u = lt.count == nsub ? q_ : local_subtile(lt, q_);                                \
+    e = expert_ids[(u * SUB) / p.block_m];                                            \
+  } while (0)
+
+  // issue cursor: the step the next DMA batch belongs to (it stays on the last step
+  // once everything is issued, so the ring tail re-reads it into unused slots)
   MOE_LDS uint8_t* lring = (MOE_LDS uint8_t*)ring;
   const uint8_t* wp[St::NW];
   const uint16_t* xp[St::NX];
-  int e0 = 0;
-  const int first_local = next_local<MODE, RB, SUB, true>(p, sorted_ids, expert_ids, first, G,
-                                                          nitems, e0);
-  if (first_local >= nitems) return;            // every item of this wave is remote
-  St::setup(p, sorted_ids, first_local, e0, wp, xp);
-  int gi = 0, iss_s = 0, iss_item = first_local;
-  bool iss_done = false;
-#define MOE_DECODE_ISSUE_NEXT()                                                        \
-  do {                                                                                 \
-    St::issue(wp, xp, iss_s * STEP, lring + (gi % P) * SLOT);                          \
-    ++gi;                                                                              \
-    if (!iss_done && ++iss_s == nsteps) {                                              \
-      int e_ = 0;                                                                      \
-      const int nxt = next_local<MODE, RB, SUB, true>(p, sorted_ids, expert_ids,       \
-                                                      iss_item + G, G, nitems, e_);    \
-      if (nxt >= nitems) {                                                             \
-        iss_done = true;                                                               \
-        iss_s = nsteps - 1;                                                            \
-      } else {                                                                         \
-        iss_s = 0;                                                                     \
-        iss_item = nxt;                                                                \
-        St::setup(p, sorted_ids, iss_item, e_, wp, xp);                                \
-      }                                                                                \
-    }                                                                                  \
+  int iu, ib, ie;
+  MOE_DECODE_ITEM(first, iu, ib, ie);
+  St::setup(p, sorted_ids, iu, ib, ie, wp, xp);
+  int gi = 0, iss_s = 0, iss_item = first;
+#define MOE_DECODE_ISSUE_NEXT()                                                       \
+  do {                                                                                \
+    St::issue(wp, xp, iss_s * STEP, lring + (gi % P) * SLOT);                         \
+    ++gi;                                                                             \
+    if (gi < gtot && ++iss_s == nsteps) {                                             \
+      iss_s = 0;                                                                      \
+      iss_item += G;                                                                  \
+      MOE_DECODE_ITEM(iss_item, iu, ib, ie);                                          \
+      St::setup(p, sorted_ids, iu, ib, ie, wp, xp);                                   \
+    }                                                                                 \
   } while (0)
 #pragma unroll
   for (int q = 0; q < P - 1; ++q) MOE_DECODE_ISSUE_NEXT();
 
   f32x4 acc[NTG][NF];
-  int cs = 0, cmp_item = first_local, cmp_e = e0;
+  int cs = 0, cmp_item = first;
   const int tr = lane & 15;
-  for (int g = 0;; ++g) {
+  for (int g = 0; g < gtot; ++g) {
     wait_vm_c<(P - 2) * NI>();                  // step g's batch has landed in LDS
     asm volatile("" ::: "memory");
     MOE_DECODE_ISSUE_NEXT();                    // into the slot step g-1 used
@@ -339,7 +425,8 @@ moe_decode_kernel(DArgs p, const int32_t* __restrict__ sorted_ids,
       // epilogue.  D layout (16x16): lane holds token column (lane & 15), weight rows
       // 4*(lane>>4)+v of each fragment
       cs = 0;
-      const int u = cmp_item / p.nblk, blk = cmp_item - u * p.nblk;
+      int u, blk, cmp_e;
+      MOE_DECODE_ITEM(cmp_item, u, blk, cmp_e);
       int ids[SUB];
       load_ids<SUB>(sorted_ids, u, ids);
       // FP8 weights: the row scales of this lane's accumulator rows 16f + 4(lane>>4) + v.
@@ -411,13 +498,17 @@ moe_decode_kernel(DArgs p, const int32_t* __restrict__ sorted_ids,
           }
         }
       }
-      cmp_item = next_local<MODE, RB, SUB, false>(p, sorted_ids, expert_ids, cmp_item + G, G,
-                                                  nitems, cmp_e);
-      if (cmp_item >= nitems) break;            // the wave's last local item is done
+      cmp_item += G;
     }
+  }
+  if (MODE == 2 && lt.count < nsub && G == static_cast<int>(gridDim.x)) {
+    const int64_t nz = static_cast<int64_t>(nsub) * p.nblk;
+    zero_range<RB, SUB>(p, sorted_ids, lt, static_cast<int>(nz * first / G),
+                        static_cast<int>(nz * (first + 1) / G));
   }
   wait_vm_c<0>();                                // no DMA may land after the wave exits
 #undef MOE_DECODE_ISSUE_NEXT
+#undef MOE_DECODE_ITEM
 }
 
 constexpr int kDecodeRB = 64;   // weight rows per work item

@@ -47,6 +47,8 @@ bool is_pow2(int v) { return v > 0 && (v & (v - 1)) == 0; }
 
 constexpr int kMaxE = 512;
 constexpr int kMaxK = 16;
+// the weight-streaming kernels keep a table of up to 4096 16-row sub-tiles in lanes
+constexpr int64_t kMaxDecodeRows = 4096 * 16;
 
 moe_status check_tke(int T, int k, int E) {
   if (T < 0) return fail(MOE_ERR_INVALID_ARG, "T=%d must be >= 0", T);
@@ -152,6 +154,11 @@ moe_status check_gemm_common(int T, int H, int I, int E, int k, int block_m, int
     if (v == MOE_VARIANT_DECODE && block_m < 16)
       return fail(MOE_ERR_UNSUPPORTED, "FP8-weight decode tiles need block_m >= 16 (got %d)", block_m);
   }
+  if (bf16_acts(dt) &&
+      resolve_variant(variant, T, H, I, E, k, static_cast<moe_dtype>(dt)) == MOE_VARIANT_DECODE &&
+      capacity(T, k, E, block_m) > kMaxDecodeRows)
+    return fail(MOE_ERR_UNSUPPORTED, "the decode variant takes at most %d padded rows (use prefill)",
+                kMaxDecodeRows);
   if (static_cast<int64_t>(T) * k * std::max(H, I) >= (int64_t(1) << 40))
     return fail(MOE_ERR_UNSUPPORTED, "tensor too large");
   return MOE_OK;
