@@ -333,6 +333,7 @@ def main():
     flops = wl.flops
     g1_flops = 2 * R * 2 * I * H
     decode = T <= 256
+    traffic_key = f"{wl.name}_T{T}" + (f"_ep{ep}" if ep > 1 else "")
     if decode:
         # active experts of each timed step, recomputed outside the timed region
         act = []
@@ -346,12 +347,12 @@ def main():
         # GEMM1 streams W13: 2I*H weights (+ 2I row scales with FP8 weights)
         g1_bytes = n_act * (2 * I * H + 2 * I * 4 if fp8 else 2 * I * H * 2)
         roof = {"bound": "hbm", "achieved": g1_bytes / (g1_ms * 1e-3) / 1e9, "peak": PEAK_HBM_GBS,
-                "unit": "GB/s", "traffic": measured_traffic(f"{wl.name}_T{T}")}
+                "unit": "GB/s", "traffic": measured_traffic(traffic_key)}
     else:
         value, unit = flops / (ms * 1e-3) / 1e12, "TFLOPS"
         roof = {"bound": "mfma", "achieved": g1_flops / (g1_ms * 1e-3) / 1e12,
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "traffic": measured_traffic(f"{wl.name}_T{T}")}
+                "traffic": measured_traffic(traffic_key)}
     roof["frac"] = roof["achieved"] / roof["peak"]
     roof["kernel"] = ("moe_decode_kernel<GEMM1+SwiGLU>" if variant == m.VARIANT_DECODE
                       else "moe_gemm_pipe_kernel<GEMM1+SwiGLU>")
