@@ -45,7 +45,11 @@ Readings where the pages leave a step open (each also listed in the design doc):
    element; section 9 lists FP8 weight variants of the fused kernel) are read as
    the OCP 8-bit E4M3 format with one float32 scale per weight row (output
    channel) of each expert: W = decode(code) * scale[e, row].  Activations, the
-   router and the output keep the bf16 layer's types.
+   router and the output keep the bf16 layer's types;
+8. the shared expert of DeepSeek-V3 / Kimi K2 ([MKR] section 1 table, "+1
+   shared") is an always-on SwiGLU expert of the routed experts' shape: every token
+   adds its output with weight 1; here it is expert E, reached through one more
+   routing slot j = k.
 """
 from __future__ import annotations
 
@@ -406,6 +410,32 @@ def moe_loop_ep(x, w13_local, w2_local, ids, w, expert_map, round_a=False):
     for j in range(k):
         out += y[j::k]
     return out
+
+
+# --------------------------------------------------------------------------- shared expert ([MKR] s1 table)
+
+def add_shared_slot(ids, w, E):
+    """Routing with the shared expert (reading 17): every token gets one more slot, j = k,
+    holding expert E (the shared one) with weight 1."""
+    ids = np.asarray(ids)
+    T = ids.shape[0]
+    ids_s = np.concatenate([ids, np.full((T, 1), E, ids.dtype)], axis=1)
+    w_s = np.concatenate([np.asarray(w, np.float64), np.ones((T, 1))], axis=1)
+    return ids_s, w_s
+
+
+def moe_layer_shared(x, wg, w13, w2, k, mode, offset=None, bias=None, n_group=0, topk_group=0,
+                     scaling=1.0, round_a=False):
+    """Layer with one shared expert ([MKR] s1 table: DeepSeek-V3 and Kimi K2 have routed
+    experts '+1 shared'): routing over the E routed experts (Wg has E rows), then the
+    per-expert loop over the k routed slots plus the shared slot (expert E of w13 / w2,
+    weight 1)."""
+    E = np.asarray(wg).shape[0]
+    logits32 = router_logits(x, wg).astype(np.float32)
+    ids, w = route(logits32, k, mode, offset, bias, n_group, topk_group, scaling)
+    ids_s, w_s = add_shared_slot(ids, w, E)
+    out = moe_loop(x, w13, w2, ids_s, w_s, round_a=round_a)
+    return out, ids_s, w_s, logits32
 
 
 def expert_flops(T, k, H, I) -> int:

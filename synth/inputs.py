@@ -22,6 +22,10 @@ Routing, Permutation, and Grouped GEMM", section 1):
 * ``gptoss``          T=16384, H=2880, I=2880, E=128, k=4, bf16, top-4 then softmax,
                        per-expert logit offset 0.5*ln(Zipf(s=1.2) rank weight).
 
+* ``kimi_k2_decode``  T in {1,16,64}, H=7168, I=2048, E=384 routed + 1 shared, k=8, bf16,
+                       sigmoid + selection bias ~ N(0, variance 0.1), no groups, no
+                       weight scale (the page gives none for this model); the shared
+                       expert's W13/W2 follow the routed ones (index E), Wg has E rows.
 * ``deepseek_decode_fp8`` / ``mixtral_fp8``: the same layers with FP8 expert
                        weights (dtype "bf16_fp8w"): each expert weight row drawn in
                        fp32 as for bf16, divided by its scale amax(|row|)/448 and
@@ -63,6 +67,7 @@ class Workload:
     offset: str | None = None       # None, "hot8", "zipf"
     bias_std: float | None = None   # selection bias std (sigmoid router)
     recipe: str = "device"          # "page_tiny" or "device"
+    shared: int = 0                 # shared experts (0 or 1): expert E of W13/W2
 
     @property
     def R(self) -> int:
@@ -98,6 +103,8 @@ WORKLOADS = {
                                     scaling=2.5, bias_std=math.sqrt(0.1)),
     "mixtral_fp8": Workload("mixtral_fp8", 4096, 4096, 14336, 8, 2, "bf16_fp8w",
                             ROUTE_SOFTMAX_TOPK_RENORM),
+    "kimi_k2_decode": Workload("kimi_k2_decode", 1, 7168, 2048, 384, 8, "bf16",
+                               ROUTE_SIGMOID_BIAS_GROUPED, bias_std=math.sqrt(0.1), shared=1),
 }
 
 FP8_MAX = 448.0     # largest finite OCP E4M3 value
@@ -154,8 +161,8 @@ class Layer:
     wl: Workload
     x: torch.Tensor          # [T, H]
     wg: torch.Tensor         # [E, H]
-    w13: torch.Tensor        # [E, 2I, H]
-    w2: torch.Tensor         # [E, H, I]
+    w13: torch.Tensor        # [E (+1 shared), 2I, H]
+    w2: torch.Tensor         # [E (+1 shared), H, I]
     offset: torch.Tensor | None = None   # [E] f32
     bias: torch.Tensor | None = None     # [E] f32
     w13_scale: torch.Tensor | None = None  # [E, 2I] f32 (FP8 weights: w13 holds uint8 codes)
@@ -186,10 +193,11 @@ def make_layer(wl: Workload, device="cpu", seed: int = 0, x_seed: int | None = N
         wg = (torch.randn(E, H, generator=g, device=device) / math.sqrt(H)).to(dt)
         fp8 = wl.dtype == "bf16_fp8w"
         wdt = torch.uint8 if fp8 else dt
-        w13 = torch.empty(E, 2 * I, H, dtype=wdt, device=device)
-        w2 = torch.empty(E, H, I, dtype=wdt, device=device)
-        s13 = torch.empty(E, 2 * I, dtype=torch.float32, device=device) if fp8 else None
-        s2 = torch.empty(E, H, dtype=torch.float32, device=device) if fp8 else None
+        EW = E + wl.shared                 # expert weights drawn: routed, then shared
+        w13 = torch.empty(EW, 2 * I, H, dtype=wdt, device=device)
+        w2 = torch.empty(EW, H, I, dtype=wdt, device=device)
+        s13 = torch.empty(EW, 2 * I, dtype=torch.float32, device=device) if fp8 else None
+        s2 = torch.empty(EW, H, dtype=torch.float32, device=device) if fp8 else None
 
         def put(dst, sdst, e, rows, w):
             if fp8:
@@ -198,7 +206,7 @@ def make_layer(wl: Workload, device="cpu", seed: int = 0, x_seed: int | None = N
                 dst[e, rows] = w.to(dt)
 
         # per expert, to bound the fp32 staging memory at the large shapes
-        for e in range(E):
+        for e in range(EW):
             put(w13, s13, e, slice(0, I), torch.randn(I, H, generator=g, device=device) / math.sqrt(H))
             put(w13, s13, e, slice(I, 2 * I),
                 torch.randn(I, H, generator=g, device=device) / math.sqrt(H))

@@ -517,3 +517,33 @@ def test_ep_align_marks_remote_tiles():
                 rows = rows[rows < ids.size]
                 owner = m[ids.reshape(-1)[rows]]
                 assert np.all(owner == r["expert_ids"][p])
+
+
+# ----------------------------------------------------------------------------- shared expert
+
+def test_shared_expert_adds_a_dense_swiglu_ffn():
+    """The shared slot adds exactly the dense SwiGLU FFN of expert E to every token (no
+    router weight); zero shared weights give the routed layer; the routing itself is the
+    routed experts' (Wg has E rows)."""
+    rng = np.random.default_rng(7)
+    T, H, I, E, k = 9, 12, 10, 6, 2
+    x = rng.standard_normal((T, H))
+    wg = rng.standard_normal((E, H)) / H ** 0.5
+    w13 = rng.standard_normal((E + 1, 2 * I, H)) / H ** 0.5
+    w2 = rng.standard_normal((E + 1, H, I)) / I ** 0.5
+    out, ids_s, w_s, l32 = O.moe_layer_shared(x, wg, w13, w2, k, O.SOFTMAX_TOPK_RENORM)
+    routed, ids, w, _ = O.moe_layer(x, wg, w13[:E], w2[:E], k, O.SOFTMAX_TOPK_RENORM)
+    assert np.array_equal(ids_s[:, :k], ids) and np.all(ids_s[:, k] == E)
+    assert np.all(w_s[:, k] == 1.0) and np.allclose(w_s[:, :k], w)
+    g = x @ w13[E, :I].T
+    u = x @ w13[E, I:].T
+    dense = (g / (1 + np.exp(-g)) * u) @ w2[E].T
+    assert np.allclose(out - routed, dense, rtol=1e-11, atol=1e-12)
+    z13, z2 = w13.copy(), w2.copy()
+    z13[E] = 0.0
+    z2[E] = 0.0
+    out0, _, _, _ = O.moe_layer_shared(x, wg, z13, z2, k, O.SOFTMAX_TOPK_RENORM)
+    assert np.allclose(out0, routed, rtol=1e-13, atol=1e-13)
+    # brute force with the extra slot
+    bf = O.moe_bruteforce(x, w13, w2, ids_s, w_s)
+    assert np.allclose(out, bf, rtol=1e-12, atol=1e-12)
