@@ -246,6 +246,22 @@ moe_status moe_layer_fp8(const void* x, const void* wg, const uint8_t* w13,
                          int32_t* topk_ids_out, float* topk_w_out, void* ws, size_t ws_bytes,
                          void* stream);
 
+/* The layer with one shared expert (DeepSeek-V3, Kimi K2: routed experts "+1 shared",
+ * section 1 table of the routing/grouped GEMM page): an always-on SwiGLU expert of the
+ * routed experts' shape whose output every token adds with weight 1.  Wg [E,H] routes
+ * over the E routed experts; w13 [E+1,2I,H] and w2 [E+1,H,I] hold the routed experts
+ * followed by the shared one (index E; FP8 weights and scales [E+1,...] likewise).  The
+ * shared expert is one more routing slot, so topk_ids_out / topk_w_out are [T, k+1]
+ * with column k = (E, 1.0), the flat row is r = t*(k+1) + j, and align, the GEMMs and
+ * the combine run on k+1 slots over E+1 experts.  k <= 15, E+1 <= 512.
+ * ws: moe_layer_shared_workspace_size(T,H,I,E,k,dt) bytes. */
+size_t moe_layer_shared_workspace_size(int T, int H, int I, int E, int k, moe_dtype dt);
+moe_status moe_layer_shared(const void* x, const void* wg, const void* w13,
+                            const float* w13_scale, const void* w2, const float* w2_scale,
+                            const moe_route_cfg* cfg, int T, int H, int I, int E, int k,
+                            moe_dtype dt, void* out, int32_t* topk_ids_out, float* topk_w_out,
+                            void* ws, size_t ws_bytes, void* stream);
+
 /* One GPU's share of an expert-parallel layer: route over all E experts (Wg [E,H] is
  * global), moe_align_ep with expert_map, then the expert GEMMs on this GPU's experts
  * (w13 [E_local,2I,H], w2 [E_local,H,I]) and the combine; out = the sum over the slots

@@ -23,7 +23,7 @@ __all__ = [
     "moe_route", "moe_route_from_logits", "moe_align", "moe_align_capacity",
     "moe_gemm1_swiglu", "moe_gemm2_weighted", "moe_combine", "moe_forward", "moe_layer",
     "moe_gemm1_swiglu_fp8", "moe_gemm2_weighted_fp8", "moe_forward_fp8", "moe_layer_fp8",
-    "moe_align_ep", "moe_layer_ep",
+    "moe_align_ep", "moe_layer_ep", "moe_layer_shared",
     "moe_preferred_block_m", "moe_auto_variant", "moe_layer_workspace_size",
     "moe_forward_workspace_size", "moe_align_workspace_size", "moe_route_workspace_size",
     "route_cfg", "MoeError", "LIB_PATH",
@@ -332,4 +332,31 @@ def moe_layer_ep(x, wg, w13, w2, k, cfg: RouteCfg, expert_map, w13_scale=None, w
     check(lib.moe_layer_ep(_p(x), _p(wg), p13, s13, p2, s2, _p(expert_map), ctypes.byref(cfg), T,
                            H, I, E, k, dt, _p(out), _p(topk_ids_out), _p(topk_w_out), _p(ws),
                            ws.numel(), _stream()), "moe_layer_ep")
+    return out
+
+
+def moe_layer_shared(x, wg, w13, w2, k, cfg: RouteCfg, w13_scale=None, w2_scale=None, out=None,
+                     ws=None, topk_ids_out=None, topk_w_out=None):
+    """The layer with one shared expert: w13 / w2 hold the E routed experts followed by the
+    shared one (index E); the routing outputs, if given, are [T, k+1]."""
+    T, H = x.shape
+    E = wg.shape[0]
+    EW, I2, _ = w13.shape
+    if EW != E + 1:
+        raise ValueError("w13 must hold E routed experts + 1 shared")
+    I = I2 // 2
+    if w13.dtype == torch.uint8:
+        dt = BF16_FP8W
+        p13, s13 = _fp8(w13, w13_scale, I2)
+        p2, s2 = _fp8(w2, w2_scale, H)
+    else:
+        dt = _dt(x)
+        p13, s13, p2, s2 = _p(w13), None, _p(w2), None
+    if out is None:
+        out = torch.empty(T, H, dtype=x.dtype, device=x.device)
+    if ws is None:
+        ws = _ws(lib.moe_layer_shared_workspace_size(T, H, I, E, k, dt), x.device)
+    check(lib.moe_layer_shared(_p(x), _p(wg), p13, s13, p2, s2, ctypes.byref(cfg), T, H, I, E, k,
+                               dt, _p(out), _p(topk_ids_out), _p(topk_w_out), _p(ws), ws.numel(),
+                               _stream()), "moe_layer_shared")
     return out

@@ -13,6 +13,7 @@ struct RouteArgs {
   const float* bias;     // [E] or null
   int n_group, topk_group;
   float scaling;
+  int shared;            // 1: the routing gets slot k = shared expert E with weight 1
 };
 
 // router
@@ -21,11 +22,12 @@ struct RouteArgs {
 int router_slabs(int T, int H, bool bf16);
 hipError_t launch_router_logits(const void* x, const void* wg, int T, int H, int E, bool bf16,
                                 float* logits, hipStream_t s);
-// logits_out (nullable) receives the summed logits when nz > 1
+// logits_out (nullable) receives the summed logits when nz > 1; ids / w are [T][k + a.shared]
 hipError_t launch_topk(const float* logits, int nz, float* logits_out, int T, int E, int k,
                        const RouteArgs& a, int32_t* ids, float* w, hipStream_t s);
-// top-k of every token and the align table in one single-work-group launch
-bool route_align_fusable(int T, int k, int E);
+// top-k of every token and the align table in one single-work-group launch (k routed
+// slots over E experts, plus the shared slot when shared = 1)
+bool route_align_fusable(int T, int k, int E, int shared);
 hipError_t launch_route_align_small(const float* logits, int nz, float* logits_out, int T, int E,
                                     int k, const RouteArgs& a, int32_t* ids, float* w, int bm,
                                     int64_t cap, int32_t* sorted_ids, int32_t* expert_ids,

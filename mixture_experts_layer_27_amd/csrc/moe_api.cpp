@@ -102,6 +102,7 @@ moe::RouteArgs route_args(const moe_route_cfg* cfg) {
   a.n_group = cfg->mode == 2 ? cfg->n_group : 0;
   a.topk_group = cfg->mode == 2 ? cfg->topk_group : 0;
   a.scaling = cfg->mode == 2 ? cfg->routed_scaling : 1.f;
+  a.shared = 0;
   return a;
 }
 
@@ -503,23 +504,26 @@ struct LayerPlan {
       off_fwd, total;
 };
 
-LayerPlan plan_layer(int T, int H, int I, int E, int k, moe_dtype dt) {
+// shared = 1: the routing gets one more slot (the shared expert, index E), so the table,
+// the GEMMs and the combine see k + 1 slots over E + 1 experts
+LayerPlan plan_layer(int T, int H, int I, int E, int k, moe_dtype dt, int shared = 0) {
   LayerPlan p;
-  p.bm = preferred_bm(T, H, I, E, k, dt);
-  p.cap = capacity(T, k, E, p.bm);
-  const size_t R = static_cast<size_t>(T) * k;
+  const int ES = E + shared, KS = k + shared;
+  p.bm = preferred_bm(T, H, I, ES, KS, dt);
+  p.cap = capacity(T, KS, ES, p.bm);
+  const size_t R = static_cast<size_t>(T) * KS;
   size_t off = 0;
   p.nz = moe::router_slabs(T, H, bf16_acts(dt));
-  p.fused_route_align = moe::route_align_fusable(T, k, E);
+  p.fused_route_align = moe::route_align_fusable(T, k, E, shared);
   p.off_logits = off; off += round_up(static_cast<size_t>(p.nz) * T * E * sizeof(float));
   p.off_ids = off; off += round_up(R * sizeof(int32_t));
   p.off_w = off; off += round_up(R * sizeof(float));
   p.off_sorted = off; off += round_up(static_cast<size_t>(p.cap) * sizeof(int32_t));
   p.off_eids = off; off += round_up(static_cast<size_t>(p.cap / p.bm) * sizeof(int32_t));
   p.off_ntpp = off; off += round_up(sizeof(int32_t));
-  p.off_counts = off; off += round_up(static_cast<size_t>(E) * sizeof(int32_t));
-  p.off_align = off; off += round_up(moe::align_ws_bytes(static_cast<int>(R), E));
-  p.off_fwd = off; off += forward_ws(T, H, I, k, dt);
+  p.off_counts = off; off += round_up(static_cast<size_t>(ES) * sizeof(int32_t));
+  p.off_align = off; off += round_up(moe::align_ws_bytes(static_cast<int>(R), ES));
+  p.off_fwd = off; off += forward_ws(T, H, I, KS, dt);
   p.total = off;
   return p;
 }
@@ -538,12 +542,18 @@ moe_status layer_impl(const void* x, const void* wg, const void* w13, const floa
                       const void* w2, const float* w2_scale, const int32_t* expert_map,
                       const moe_route_cfg* cfg, int T,
                       int H, int I, int E, int k, moe_dtype dt, void* out, int32_t* topk_ids_out,
-                      float* topk_w_out, void* ws, size_t ws_bytes, void* stream) {
+                      float* topk_w_out, void* ws, size_t ws_bytes, void* stream,
+                      int shared = 0) {
   moe_status st = check_tke(T, k, E);
   if (st != MOE_OK) return st;
+  const int ES = E + shared, KS = k + shared;
+  if (shared && (st = check_tke(T, KS, ES)) != MOE_OK) return st;
+  if (shared && expert_map)
+    return fail(MOE_ERR_UNSUPPORTED, "a shared expert with an expert map is not supported");
   if (!valid_expert_dt(dt)) return fail(MOE_ERR_INVALID_ARG, "dtype=%d", dt);
   // the sizes must suit the block_m this layer aligns with
-  st = check_gemm_common(T, H, I, E, k, preferred_bm(T, H, I, E, k, dt), dt, MOE_VARIANT_AUTO);
+  st = check_gemm_common(T, H, I, ES, KS, preferred_bm(T, H, I, ES, KS, dt), dt,
+                         MOE_VARIANT_AUTO);
   if (st != MOE_OK) return st;
   if ((st = check_route_cfg(cfg, E, k)) != MOE_OK) return st;
   if ((st = check_scales(dt, w13_scale, w2_scale)) != MOE_OK) return st;
@@ -552,7 +562,7 @@ moe_status layer_impl(const void* x, const void* wg, const void* w13, const floa
   if (bf16_acts(dt) && (!aligned16(x) || !aligned16(wg) || !aligned16(w13) || !aligned16(w2) ||
                         !aligned16(out)))
     return fail(MOE_ERR_INVALID_ARG, "tensor not 16-byte aligned");
-  const LayerPlan p = plan_layer(T, H, I, E, k, dt);
+  const LayerPlan p = plan_layer(T, H, I, E, k, dt, shared);
   if (!ws || ws_bytes < p.total) return fail(MOE_ERR_WORKSPACE, "layer workspace needs %zu bytes", p.total);
   if (!aligned16(ws)) return fail(MOE_ERR_INVALID_ARG, "workspace not 16-byte aligned");
   uint8_t* b = static_cast<uint8_t*>(ws);
@@ -566,19 +576,21 @@ moe_status layer_impl(const void* x, const void* wg, const void* w13, const floa
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = moe::launch_router_logits(x, wg, T, H, E, bf16_acts(dt), logits, s);
   if (e != hipSuccess) return hip_status(e, "router logits");
+  moe::RouteArgs ra = route_args(cfg);
+  ra.shared = shared;
   if (p.fused_route_align) {
-    e = moe::launch_route_align_small(logits, p.nz, nullptr, T, E, k, route_args(cfg), ids, tw,
-                                      p.bm, p.cap, sorted, eids, ntpp, counts, expert_map, s);
+    e = moe::launch_route_align_small(logits, p.nz, nullptr, T, E, k, ra, ids, tw, p.bm, p.cap,
+                                      sorted, eids, ntpp, counts, expert_map, s);
     if (e != hipSuccess) return hip_status(e, "route+align");
   } else {
-    e = moe::launch_topk(logits, p.nz, nullptr, T, E, k, route_args(cfg), ids, tw, s);
+    e = moe::launch_topk(logits, p.nz, nullptr, T, E, k, ra, ids, tw, s);
     if (e != hipSuccess) return hip_status(e, "top-k");
-    e = moe::launch_align(ids, T * k, E, p.bm, p.cap, sorted, eids, ntpp, counts,
+    e = moe::launch_align(ids, T * KS, ES, p.bm, p.cap, sorted, eids, ntpp, counts,
                           reinterpret_cast<int32_t*>(b + p.off_align), expert_map, s);
     if (e != hipSuccess) return hip_status(e, "align");
   }
-  return forward_impl(x, w13, w13_scale, w2, w2_scale, tw, sorted, eids, ntpp, T, H, I, E, k,
-                      p.bm, dt, MOE_VARIANT_AUTO, out, b + p.off_fwd, forward_ws(T, H, I, k, dt),
+  return forward_impl(x, w13, w13_scale, w2, w2_scale, tw, sorted, eids, ntpp, T, H, I, ES, KS,
+                      p.bm, dt, MOE_VARIANT_AUTO, out, b + p.off_fwd, forward_ws(T, H, I, KS, dt),
                       stream);
 }
 
@@ -602,6 +614,20 @@ moe_status moe_layer_fp8(const void* x, const void* wg, const uint8_t* w13,
   if (!w13_scale || !w2_scale) return fail(MOE_ERR_INVALID_ARG, "NULL scale pointer");
   return layer_impl(x, wg, w13, w13_scale, w2, w2_scale, nullptr, cfg, T, H, I, E, k,
                     MOE_BF16_FP8W, out, topk_ids_out, topk_w_out, ws, ws_bytes, stream);
+}
+
+size_t moe_layer_shared_workspace_size(int T, int H, int I, int E, int k, moe_dtype dt) {
+  if (T <= 0 || H <= 0 || I <= 0 || E <= 0 || k < 1 || !valid_expert_dt(dt)) return 0;
+  return plan_layer(T, H, I, E, k, dt, 1).total;
+}
+
+moe_status moe_layer_shared(const void* x, const void* wg, const void* w13,
+                            const float* w13_scale, const void* w2, const float* w2_scale,
+                            const moe_route_cfg* cfg, int T, int H, int I, int E, int k,
+                            moe_dtype dt, void* out, int32_t* topk_ids_out, float* topk_w_out,
+                            void* ws, size_t ws_bytes, void* stream) {
+  return layer_impl(x, wg, w13, w13_scale, w2, w2_scale, nullptr, cfg, T, H, I, E, k, dt, out,
+                    topk_ids_out, topk_w_out, ws, ws_bytes, stream, 1);
 }
 
 moe_status moe_layer_ep(const void* x, const void* wg, const void* w13, const float* w13_scale,

@@ -146,8 +146,9 @@ struct TopkParams {
   const float* bias;
   int n_group, topk_group;
   float scaling;
-  int32_t* ids;
+  int32_t* ids;            // [T][k + shared]
   float* w;
+  int shared;              // 1: slot k is the shared expert (id E, weight 1)
 };
 
 // LDS of one wave's top-k (group segment pairs)
@@ -298,11 +299,17 @@ __device__ void topk_token(const TopkParams& p, int t, TopkLds& sh, int32_t* ids
                                : exp(static_cast<double>(my_src) - l0);
   double sum = 0.0;
   for (int j = 0; j < k; ++j) sum += read_lane(myv, j);
+  // rows of k + shared slots; the shared expert takes slot k with weight 1
+  const int ko = k + p.shared;
   if (lane < k) {
     const double wt = mode == 2 ? static_cast<double>(p.scaling) * myv / sum : myv / sum;
-    p.ids[static_cast<int64_t>(t) * k + lane] = my_id;
-    p.w[static_cast<int64_t>(t) * k + lane] = static_cast<float>(wt);
-    if (ids_lds) ids_lds[t * k + lane] = my_id;
+    p.ids[static_cast<int64_t>(t) * ko + lane] = my_id;
+    p.w[static_cast<int64_t>(t) * ko + lane] = static_cast<float>(wt);
+    if (ids_lds) ids_lds[t * ko + lane] = my_id;
+  } else if (lane < ko) {
+    p.ids[static_cast<int64_t>(t) * ko + lane] = p.E;
+    p.w[static_cast<int64_t>(t) * ko + lane] = 1.f;
+    if (ids_lds) ids_lds[t * ko + lane] = p.E;
   }
 }
 
@@ -353,8 +360,8 @@ route_align_small_kernel(TopkParams p, int bm, int64_t cap, int32_t* __restrict_
   q.logits_out = nullptr;
   for (int t = w; t < p.T; t += 16) topk_token<NSLOT, 1>(q, t, sh[w], ids_lds);
   __syncthreads();
-  alignd::align_small_body(ids_lds, p.T * p.k, p.E, bm, cap, sorted_ids, expert_ids, ntpp,
-                           counts, emap);
+  alignd::align_small_body(ids_lds, p.T * (p.k + p.shared), p.E + p.shared, bm, cap, sorted_ids,
+                           expert_ids, ntpp, counts, emap);
 }
 
 // K slabs of the bf16 logits: at decode batch sizes enough work-groups to stream Wg
@@ -383,6 +390,7 @@ TopkParams topk_params(const float* logits, int nz, float* logits_out, int T, in
   p.scaling = a.scaling;
   p.ids = ids;
   p.w = w;
+  p.shared = a.shared;
   return p;
 }
 
@@ -394,8 +402,8 @@ int router_slabs(int T, int H, bool bf16) {
   return (H + kz - 1) / kz;
 }
 
-bool route_align_fusable(int T, int k, int E) {
-  return T <= kFusedMaxT && T * k <= kFusedMaxRows && E <= 4 * kWave;
+bool route_align_fusable(int T, int k, int E, int shared) {
+  return T <= kFusedMaxT && T * (k + shared) <= kFusedMaxRows && E <= 4 * kWave;
 }
 
 hipError_t launch_router_logits(const void* x, const void* wg, int T, int H, int E, bool bf16,

@@ -227,3 +227,19 @@ def test_expert_parallel_entry_points_validate(L):
                             8, 2, 2, FAKE, None, None, FAKE, ws8, None) == INVALID
     assert lib.moe_layer_ep(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ctypes.byref(c), 4, 64, 64,
                             8, 2, 1, FAKE, None, None, FAKE, ws, None) == INVALID
+
+
+def test_shared_expert_layer_validates(L):
+    lib = L.lib
+    c = cfg(L, 2)
+    ws = lib.moe_layer_shared_workspace_size(4, 256, 256, 384, 8, 1)
+    assert ws > lib.moe_layer_workspace_size(4, 256, 256, 384, 8, 1)   # one more slot per token
+    assert lib.moe_layer_shared(FAKE, FAKE, FAKE, None, FAKE, None, ctypes.byref(c), 4, 256, 256,
+                                384, 8, 1, FAKE, None, None, FAKE, ws - 1, None) == WORKSPACE
+    # k routed slots + the shared one must fit the 16-slot limit; E + 1 the 512-expert one
+    big = lib.moe_layer_shared_workspace_size(4, 256, 256, 64, 16, 1)
+    assert lib.moe_layer_shared(FAKE, FAKE, FAKE, None, FAKE, None, ctypes.byref(cfg(L)), 4, 256,
+                                256, 64, 16, 1, FAKE, None, None, FAKE, big, None) == UNSUPPORTED
+    big = lib.moe_layer_shared_workspace_size(4, 256, 256, 512, 8, 1)
+    assert lib.moe_layer_shared(FAKE, FAKE, FAKE, None, FAKE, None, ctypes.byref(cfg(L)), 4, 256,
+                                256, 512, 8, 1, FAKE, None, None, FAKE, big, None) == UNSUPPORTED

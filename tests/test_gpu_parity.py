@@ -564,3 +564,42 @@ def test_layer_ep(lib, name, T, scale):
     full = O.moe_loop(x64[same], full13, full2, rid[same], rw[same], round_a=True)
     r = np.abs(np64(out)[same] - ref).max() / np.sqrt(np.mean(full ** 2))
     assert r <= 2e-2, f"share max|d|/RMS(layer) {r:.3e}"
+
+
+# ------------------------------------------------------------------------------ shared expert
+
+@pytest.mark.parametrize("name,T,scale", [("kimi_k2_decode", 1, 4), ("kimi_k2_decode", 8, 4),
+                                          ("kimi_k2_decode", 64, 4), ("kimi_k2_decode", 600, 8),
+                                          ("deepseek_decode", 16, 4), ("mixtral", 512, 16),
+                                          ("deepseek_decode_fp8", 8, 4)])
+def test_layer_shared_expert(lib, name, T, scale):
+    """moe_layer_shared: the routing's extra column is the shared expert (E, weight 1) and
+    the output matches the oracle's per-expert loop over k routed slots + the shared
+    slot on tokens whose routing agrees."""
+    base = S.WORKLOADS[name].scaled(shared=1)
+    q = 128 if base.dtype == "bf16_fp8w" else 64
+    wl = base.scaled(T=T, H=base.H // scale // q * q, I=base.I // scale // q * q)
+    lay = S.make_layer(wl, device=DEV, seed=8)
+    cfg = lib_cfg(lib, wl, lay)
+    k, E = wl.k, wl.E
+    ids = torch.empty(T, k + 1, dtype=torch.int32, device=DEV)
+    w = torch.empty(T, k + 1, dtype=torch.float32, device=DEV)
+    kw = {} if lay.w13_scale is None else dict(w13_scale=lay.w13_scale, w2_scale=lay.w2_scale)
+    out = lib.moe_layer_shared(lay.x, lay.wg, lay.w13, lay.w2, k, cfg, topk_ids_out=ids,
+                               topk_w_out=w, **kw)
+    _sync()
+    gids, gw = ids.cpu().numpy(), w.cpu().numpy()
+    assert np.all(gids[:, k] == E) and np.all(gw[:, k] == 1.0)
+    x64, wg64 = np64(lay.x), np64(lay.wg)
+    logits = O.router_logits(x64, wg64)
+    rkw = route_kwargs(wl, lay)
+    rid, rw = O.route(logits.astype(np.float32), k, wl.mode, **rkw)
+    same = np.all(gids[:, :k] == rid, axis=1)
+    margin = O.selection_margin(logits.astype(np.float32), k, wl.mode, rkw["offset"], rkw["bias"],
+                                wl.n_group, wl.topk_group)
+    assert np.all(same | (margin <= 2 * logit_error_bound(x64, wg64)))
+    assert same.mean() > 0.5
+    ids_s, w_s = O.add_shared_slot(rid, rw, E)
+    w13_64, w2_64 = expert_weights64(lay)
+    ref = O.moe_loop(x64[same], w13_64, w2_64, ids_s[same], w_s[same], round_a=True)
+    bf16_tol_check(np64(out)[same], ref)
