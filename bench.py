@@ -111,11 +111,11 @@ def cpu_baseline(wl, lay, sample_T):
     else:
         w13 = lay.w13.float().cpu().numpy()
         w2 = lay.w2.float().cpu().numpy()
+        layer = O.moe_layer_shared if wl.shared else O.moe_layer
         t0 = time.perf_counter()
-        out, ids, _, _ = O.moe_layer(x, wg, w13, w2, wl.k, wl.mode, round_a=wl.dtype == "bf16",
-                                     **kw)
+        out, ids, _, _ = layer(x, wg, w13, w2, wl.k, wl.mode, round_a=wl.dtype == "bf16", **kw)
     dt = time.perf_counter() - t0
-    flops = 2 * sample_T * wl.k * 3 * wl.H * wl.I
+    flops = 2 * sample_T * (wl.k + wl.shared) * 3 * wl.H * wl.I
     if wl.T <= 256:  # decode: weight bytes of the experts the sample activates
         active = len(set(ids.reshape(-1).tolist()))
         value, unit = active * expert_bytes(wl) / dt / 1e9, "GB/s"
@@ -143,11 +143,17 @@ def main():
     dev = "cuda"
     lay = S.make_layer(wl, device=dev, seed=0)
     T, H, I, E, k = wl.T, wl.H, wl.I, wl.E, wl.k
+    # a shared expert is one more routing slot (expert E, weight 1): the table, the GEMMs
+    # and the combine see K1 = k + 1 slots over ES = E + 1 experts
+    shared = wl.shared
+    K1, ES = k + shared, E + shared
     # expert weights this GPU holds (all of them unless --ep)
     ep = args.ep
     emap = None
     w13, w2, s13, s2 = lay.w13, lay.w2, lay.w13_scale, lay.w2_scale
     if ep > 1:
+        if shared:
+            raise SystemExit("--ep with a shared expert is not supported")
         local = torch.arange(0, E, ep, device=dev)
         emap = torch.full((E,), -1, dtype=torch.int32, device=dev)
         emap[local] = torch.arange(local.numel(), dtype=torch.int32, device=dev)
@@ -159,23 +165,28 @@ def main():
     dt = {"bf16": m.BF16, "f32": m.F32, "bf16_fp8w": m.BF16_FP8W}[wl.dtype]
     dta = m.BF16 if fp8 else dt      # activation type (router, combine)
     cfg = m.route_cfg(wl.mode, lay.offset, lay.bias, wl.n_group, wl.topk_group, wl.scaling)
-    bm = args.block_m or m.moe_preferred_block_m(T, H, I, E, k, dt)
-    variant = m.moe_auto_variant(T, H, I, E, k, dt)
-    cap = m.moe_align_capacity(T, k, E, bm)
-    R = T * k
+    bm = args.block_m or m.moe_preferred_block_m(T, H, I, ES, K1, dt)
+    variant = m.moe_auto_variant(T, H, I, ES, K1, dt)
+    cap = m.moe_align_capacity(T, K1, ES, bm)
+    R = T * K1
     # rotate activation batches for decode so successive steps route differently
     nx = 8 if T <= 256 else 1
     xs = [lay.x] + [S.make_x(wl, device=dev, seed=1000 + i) for i in range(nx - 1)]
     i32 = dict(dtype=torch.int32, device=dev)
-    ids = torch.empty(T, k, **i32)
-    w = torch.empty(T, k, dtype=torch.float32, device=dev)
+    ids = torch.empty(T, K1, **i32)
+    w = torch.empty(T, K1, dtype=torch.float32, device=dev)
+    # the route stage alone writes the k routed slots (the full step fills ids / w)
+    ids_r = torch.empty(T, k, **i32) if shared else ids
+    w_r = torch.empty(T, k, dtype=torch.float32, device=dev) if shared else w
     rws = torch.empty(max(16, m.moe_route_workspace_size(T, H, E, dta)), dtype=torch.uint8, device=dev)
     sorted_ids = torch.empty(cap, **i32)
     expert_ids = torch.empty(cap // bm, **i32)
     ntpp = torch.empty(1, **i32)
-    counts = torch.empty(E, **i32)
-    aws = torch.empty(max(16, m.moe_align_workspace_size(T, k, E, bm)), dtype=torch.uint8, device=dev)
-    lws = torch.empty(m.moe_layer_workspace_size(T, H, I, E, k, dt), dtype=torch.uint8, device=dev)
+    counts = torch.empty(ES, **i32)
+    aws = torch.empty(max(16, m.moe_align_workspace_size(T, K1, ES, bm)), dtype=torch.uint8, device=dev)
+    lws_n = (m.lib.moe_layer_shared_workspace_size if shared else m.moe_layer_workspace_size)(
+        T, H, I, E, k, dt)
+    lws = torch.empty(lws_n, dtype=torch.uint8, device=dev)
     a = torch.empty(R, I, dtype=lay.x.dtype, device=dev)
     y = torch.empty(R, H, dtype=torch.float32, device=dev)
     out = torch.empty(T, H, dtype=lay.x.dtype, device=dev)
@@ -194,34 +205,35 @@ def main():
         run = lambda j: only is None or only == j
         mark(0)
         if run(0):
-            m.check(lib.moe_route(P(x), P(lay.wg), T, H, E, k, dta, ctypes.byref(cfg), P(ids), P(w),
-                                  None, P(rws), rws.numel(), sp), "route")
+            m.check(lib.moe_route(P(x), P(lay.wg), T, H, E, k, dta, ctypes.byref(cfg), P(ids_r),
+                                  P(w_r), None, P(rws), rws.numel(), sp), "route")
         mark(1)
         if run(1) and emap is not None:
             m.check(lib.moe_align_ep(P(ids), T, k, E, bm, P(emap), P(sorted_ids), P(expert_ids),
                                      P(ntpp), P(counts), P(aws), aws.numel(), sp), "align")
         elif run(1):
-            m.check(lib.moe_align(P(ids), T, k, E, bm, P(sorted_ids), P(expert_ids), P(ntpp),
+            m.check(lib.moe_align(P(ids), T, K1, ES, bm, P(sorted_ids), P(expert_ids), P(ntpp),
                                   P(counts), P(aws), aws.numel(), sp), "align")
         mark(2)
         if run(2) and fp8:
             m.check(lib.moe_gemm1_swiglu_fp8(P(x), P(w13), P(s13), P(sorted_ids),
-                                             P(expert_ids), P(ntpp), T, H, I, E, k, bm, variant,
+                                             P(expert_ids), P(ntpp), T, H, I, ES, K1, bm, variant,
                                              P(a), sp), "gemm1")
         elif run(2):
             m.check(lib.moe_gemm1_swiglu(P(x), P(w13), P(sorted_ids), P(expert_ids), P(ntpp), T,
-                                         H, I, E, k, bm, dt, variant, P(a), sp), "gemm1")
+                                         H, I, ES, K1, bm, dt, variant, P(a), sp), "gemm1")
         mark(3)
         if run(3) and fp8:
             m.check(lib.moe_gemm2_weighted_fp8(P(a), P(w2), P(s2), P(w),
-                                               P(sorted_ids), P(expert_ids), P(ntpp), T, H, I, E,
-                                               k, bm, variant, P(y), sp), "gemm2")
+                                               P(sorted_ids), P(expert_ids), P(ntpp), T, H, I, ES,
+                                               K1, bm, variant, P(y), sp), "gemm2")
         elif run(3):
             m.check(lib.moe_gemm2_weighted(P(a), P(w2), P(w), P(sorted_ids), P(expert_ids),
-                                           P(ntpp), T, H, I, E, k, bm, dt, variant, P(y), sp), "gemm2")
+                                           P(ntpp), T, H, I, ES, K1, bm, dt, variant, P(y), sp),
+                    "gemm2")
         mark(4)
         if run(4):
-            m.check(lib.moe_combine(P(y), T, H, k, dta, P(out), sp), "combine")
+            m.check(lib.moe_combine(P(y), T, H, K1, dta, P(out), sp), "combine")
         mark(5)
 
     def launch(i, sp):
@@ -229,6 +241,12 @@ def main():
         if staged:
             return launch_staged(i, sp)
         x = xs[i % nx]
+        if shared:
+            m.check(lib.moe_layer_shared(P(x), P(lay.wg), P(w13), P(s13) if fp8 else None, P(w2),
+                                         P(s2) if fp8 else None, ctypes.byref(cfg), T, H, I, E, k,
+                                         dt, P(out), P(ids), P(w), P(lws), lws.numel(), sp),
+                    "layer")
+            return
         if emap is not None:
             m.check(lib.moe_layer_ep(P(x), P(lay.wg), P(w13), P(s13) if fp8 else None, P(w2),
                                      P(s2) if fp8 else None, P(emap), ctypes.byref(cfg), T, H, I,
@@ -330,7 +348,7 @@ def main():
             stages_ms[nm] = e0.elapsed_time(e1) / args.steps
             del g
     g1_ms = stages_ms["gemm1"]
-    flops = wl.flops
+    flops = 2 * T * K1 * 3 * H * I        # useful expert FLOPs (the shared slot included)
     g1_flops = 2 * R * 2 * I * H
     decode = T <= 256
     traffic_key = f"{wl.name}_T{T}" + (f"_ep{ep}" if ep > 1 else "")
@@ -357,11 +375,14 @@ def main():
     roof["kernel"] = ("moe_decode_kernel<GEMM1+SwiGLU>" if variant == m.VARIANT_DECODE
                       else "moe_gemm_pipe_kernel<GEMM1+SwiGLU>")
     roof["kernel_ms"] = g1_ms
+    if shared:
+        roof["kernel"] += " (k+1 slots: the shared expert is slot k)"
     rec = {"metric": METRIC, "value": value, "unit": unit, "n_gpus": 1, "steps": args.steps,
            "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
            "vs_baseline": None, "dtype": wl.dtype, "data": "synthetic",
            "config": {"workload": f"{wl.name}", "T": T, "H": H, "I": I, "E": E, "k": k,
-                      "route_mode": wl.mode, "block_m": bm, "variant": variant,
+                      "route_mode": wl.mode, "shared_experts": shared, "block_m": bm,
+                      "variant": variant,
                       "timing": "eager" if args.eager else "hip-graph replay",
                       "step": "stage-by-stage calls" if staged else "moe_layer",
                       "step_ms_p10_p50_p90": [pct(0.1), pct(0.5), pct(0.9)],

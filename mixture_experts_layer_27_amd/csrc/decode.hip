@@ -246,12 +246,13 @@ __device__ __forceinline__ bool is_local(const LocalSubtiles& t, int u) {
 }
 
 // GEMM2: zeros in y for the remote items among [i0, i1) of all nsub*nblk items
-// (item = sub-tile * nblk + block).  Lane group lane>>4 takes one of four rows, its 16
-// lanes the 64 floats of the block.
+// (item = sub-tile * nblk + block).  RB/4 lanes write the RB floats of one row's block,
+// 64/(RB/4) rows at a time.
 template <int RB, int SUB>
 __device__ __forceinline__ void zero_range(const DArgs& p, const int32_t* __restrict__ sorted_ids,
                                            const LocalSubtiles& lt, int i0, int i1) {
-  static_assert(RB == 64, "16 lanes x 4 floats per row");
+  constexpr int LPR = RB / 4, RPP = kWave / LPR;
+  static_assert(RB % 4 == 0 && kWave % LPR == 0 && SUB % RPP == 0, "row split");
   const int lane = lane_id();
   int it = i0;
   while (it < i1) {
@@ -261,12 +262,12 @@ __device__ __forceinline__ void zero_range(const DArgs& p, const int32_t* __rest
       int ids[SUB];
       load_ids<SUB>(sorted_ids, u, ids);
 #pragma unroll
-      for (int t0 = 0; t0 < SUB; t0 += 4) {
-        const int r = pick(ids, t0 + (lane >> 4));
+      for (int t0 = 0; t0 < SUB; t0 += RPP) {
+        const int r = pick(ids, t0 + lane / LPR);
         if (r < p.R) {
           float* row = static_cast<float*>(p.C) + static_cast<int64_t>(r) * p.H;
           for (int b = it - u * p.nblk; b < end - u * p.nblk; ++b)
-            *reinterpret_cast<float4*>(row + b * RB + 4 * (lane & 15)) =
+            *reinterpret_cast<float4*>(row + b * RB + 4 * (lane % LPR)) =
                 make_float4(0.f, 0.f, 0.f, 0.f);
         }
       }
@@ -511,7 +512,7 @@ moe_decode_kernel(DArgs p, const int32_t* __restrict__ sorted_ids,
 #undef MOE_DECODE_ITEM
 }
 
-constexpr int kDecodeRB = 64;   // weight rows per work item
+constexpr int kDecodeRB = 64;   // weight rows per work item (32 for bf16 16-row sub-tiles)
 
 int decode_ntg(int block_m, int R, int E) {
   // 32-row sub-tiles once experts average more than one row: the popular experts then
@@ -521,24 +522,31 @@ int decode_ntg(int block_m, int R, int E) {
   return std::min(want, block_m / 16);
 }
 
-template <int MODE, int NTG, int STEP, bool NT, int WB, int P>
-hipError_t launch_decode(const DArgs& p, const GemmArgs& g, hipStream_t s) {
+template <int MODE, int NTG, int STEP, bool NT, int WB, int P, int RB = kDecodeRB>
+hipError_t launch_decode(const DArgs& p0, const GemmArgs& g, hipStream_t s) {
   using S = DStep<STEP, WB>;
-  constexpr int kLds = P * (kDecodeRB * S::WROWB + 16 * NTG * S::XROWB);
+  DArgs p = p0;
+  p.nblk = (MODE == 1 ? 2 * p.I : p.H) / RB;
+  constexpr int kLds = P * (RB * S::WROWB + 16 * NTG * S::XROWB);
   constexpr int kPerCU = std::max(1, (160 * 1024) / kLds);
   const int64_t max_items = (g.cap / (16 * NTG)) * p.nblk;
   const unsigned grid = static_cast<unsigned>(std::min<int64_t>(max_items, 256 * kPerCU));
-  hipLaunchKernelGGL((moe_decode_kernel<MODE, kDecodeRB, NTG, STEP, P, NT, WB>), dim3(grid),
-                     dim3(64), 0, s, p, g.sorted_ids, g.expert_ids, g.ntpp, g.topk_w, g.w_scale);
+  hipLaunchKernelGGL((moe_decode_kernel<MODE, RB, NTG, STEP, P, NT, WB>), dim3(grid), dim3(64), 0,
+                     s, p, g.sorted_ids, g.expert_ids, g.ntpp, g.topk_w, g.w_scale);
   return hipGetLastError();
 }
 
-// bf16 weights: 128-element steps (256-byte weight rows) when K allows, else 64
+// bf16 weights, 128-element steps (K % 128 != 0: 64).  GEMM1 with 16-row sub-tiles:
+// 32-row work items with a 6-slot ring (two waves per CU); against 64-row items and a
+// 4-slot ring it measured level at the DeepSeek-V3 shape's T = 1 and 20 % faster when
+// the items just exceed the waves (Kimi K2 at T = 1: 9 experts, 576 items of 64 rows
+// for 512 waves).  GEMM2 measured no better that way and keeps 64-row items; 32-row
+// sub-tiles keep 64-row items and a 3-slot ring.
 template <int MODE, int NTG, bool NT>
 hipError_t launch_decode_bf16(const DArgs& p, const GemmArgs& g, hipStream_t s) {
-  constexpr int P = NTG == 1 ? 4 : 3;
-  return p.K % 128 == 0 ? launch_decode<MODE, NTG, 128, NT, 2, P>(p, g, s)
-                        : launch_decode<MODE, NTG, 64, NT, 2, P>(p, g, s);
+  if (p.K % 128 != 0) return launch_decode<MODE, NTG, 64, NT, 2, NTG == 1 ? 4 : 3>(p, g, s);
+  if constexpr (NTG == 1 && MODE == 1) return launch_decode<MODE, NTG, 128, NT, 2, 6, 32>(p, g, s);
+  else return launch_decode<MODE, NTG, 128, NT, 2, NTG == 1 ? 4 : 3>(p, g, s);
 }
 
 // FP8 weights: 128-element steps (128-byte weight rows, 256-byte token rows; K % 128 == 0
@@ -570,8 +578,6 @@ hipError_t run_decode(const GemmArgs& g, hipStream_t s) {
   p.H = g.H;
   p.a_expert_stride = g1 ? static_cast<int64_t>(2) * g.I * g.H : static_cast<int64_t>(g.H) * g.I;
   p.block_m = g.block_m;
-  const int N = g1 ? 2 * g.I : g.H;             // weight rows per expert
-  p.nblk = N / kDecodeRB;
   if (g.cap == 0) return hipSuccess;
   const int ntg = decode_ntg(g.block_m, p.R, g.E);
   // non-temporal weight stream while almost every expert fits one sub-tile (each weight
