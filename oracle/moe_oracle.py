@@ -320,6 +320,38 @@ def moe_dense(x, w13, w2, ids, w, round_a=False):
     return out
 
 
+def moe_permute_grouped(x, w13, w2, ids, w, round_a=False):
+    """Third implementation ([MKR] s2 'permute, then grouped GEMM'; s10 'three
+    implementations'): physically reorder the routed rows so each expert's rows are
+    contiguous (stable order by expert), run one GEMM per contiguous segment given by
+    the per-expert offsets, scale by the router weight, then un-permute by adding each
+    row into its token's output.  Shares no indexing code with ``moe_loop``."""
+    x = np.asarray(x, np.float64)
+    w2 = np.asarray(w2, np.float64)
+    W1, W3 = _split_w13(w13)
+    T, H = x.shape
+    ids = np.asarray(ids)
+    k = ids.shape[1]
+    flat = ids.reshape(-1)
+    order = np.argsort(flat, kind="stable")               # routed rows grouped by expert
+    xs = x[order // k]                                    # the permuted copy
+    ends = np.cumsum(np.bincount(flat, minlength=W1.shape[0]))
+    ys = np.zeros((flat.size, H))
+    start = 0
+    for e, end in enumerate(ends):
+        if end > start:
+            seg = xs[start:end]
+            h = silu(seg @ W1[e].T) * (seg @ W3[e].T)
+            if round_a:
+                h = bf16_round(h)
+            ys[start:end] = h @ w2[e].T
+        start = end
+    ys *= np.asarray(w, np.float64).reshape(-1)[order, None]
+    out = np.zeros((T, H))
+    np.add.at(out, order // k, ys)                        # un-permute + combine
+    return out
+
+
 def moe_bruteforce(x, w13, w2, ids, w, round_a=False):
     """Scalar Python loops per (token, slot, output element); tiny inputs only."""
     x = np.asarray(x, np.float64).tolist()

@@ -209,6 +209,15 @@ def test_forward_page_test_matrix(lib, case):
     w13 = torch.cat([w1, w3], dim=1)
     r = _forward_case(lib, x, wg, w13, w2, k, 0, 16, 0)
     assert r <= 1e-5
+    # the page's third opinion: permute -> grouped GEMM per expert segment -> un-permute
+    x64, w13_64, w2_64 = np64(x), np64(w13), np64(w2)
+    ids, w = O.route(O.router_logits(x64, np64(wg)).astype(np.float32), k, 0)
+    w32 = w.astype(np.float32)
+    sorted_ids, expert_ids, ntpp, _ = lib.moe_align(torch.from_numpy(ids).to(DEV), w13.shape[0], 16)
+    out = lib.moe_forward(x.to(DEV), w13.to(DEV), w2.to(DEV), torch.from_numpy(w32).to(DEV),
+                          sorted_ids, expert_ids, ntpp, k, 16)
+    _sync()
+    f32_tol_check(np64(out), O.moe_permute_grouped(x64, w13_64, w2_64, ids, w32.astype(np.float64)))
 
 
 BF16_SHAPES = [

@@ -547,3 +547,37 @@ def test_shared_expert_adds_a_dense_swiglu_ffn():
     # brute force with the extra slot
     bf = O.moe_bruteforce(x, w13, w2, ids_s, w_s)
     assert np.allclose(out, bf, rtol=1e-12, atol=1e-12)
+
+
+# ----------------------------------------------------------------------------- third implementation
+
+@pytest.mark.parametrize("case", ["uniform", "skewed", "decode", "top1"])
+def test_permute_grouped_matches_loop_and_library_grouped_mm(case):
+    """[MKR] s10: loop, fused kernel and F.grouped_mm with explicit permute / un-permute.
+    The oracle's permute path agrees with the per-expert loop (float64), and torch's own
+    grouped GEMM on the same permuted layout (fp32, library routine) agrees with both."""
+    import torch.nn.functional as F
+    x, wg, w1, w3, w2, k = S.page_test_case(case)
+    w13 = torch.cat([w1, w3], dim=1)
+    x64, w13_64, w2_64 = x.double().numpy(), w13.double().numpy(), w2.double().numpy()
+    l32 = O.router_logits(x64, wg.double().numpy()).astype(np.float32)
+    ids, w = O.route(l32, k, O.SOFTMAX_TOPK_RENORM)
+    loop = O.moe_loop(x64, w13_64, w2_64, ids, w)
+    perm = O.moe_permute_grouped(x64, w13_64, w2_64, ids, w)
+    assert np.allclose(perm, loop, rtol=1e-12, atol=1e-12)
+    assert np.allclose(O.moe_permute_grouped(x64, w13_64, w2_64, ids, w, round_a=True),
+                       O.moe_loop(x64, w13_64, w2_64, ids, w, round_a=True), rtol=1e-12, atol=1e-12)
+    # torch.nn.functional.grouped_mm (fp32 on the CPU) on the permuted rows
+    E = w13.shape[0]
+    I = w13.shape[1] // 2
+    flat = torch.from_numpy(ids.reshape(-1).astype(np.int64))
+    order = torch.argsort(flat, stable=True)
+    xs = x[order // k].contiguous()
+    offs = torch.cumsum(torch.bincount(flat, minlength=E), 0).to(torch.int32)
+    g = F.grouped_mm(xs, w13[:, :I].transpose(-2, -1).contiguous(), offs=offs)
+    u = F.grouped_mm(xs, w13[:, I:].transpose(-2, -1).contiguous(), offs=offs)
+    h = (F.silu(g) * u).contiguous()
+    ys = F.grouped_mm(h, w2.transpose(-2, -1).contiguous(), offs=offs)
+    ys = ys * torch.from_numpy(w.reshape(-1).astype(np.float32))[order, None]
+    lib = torch.zeros(x.shape[0], x.shape[1]).index_add_(0, order // k, ys).double().numpy()
+    assert np.abs(lib - loop).max() / np.abs(loop).max() < 1e-5
