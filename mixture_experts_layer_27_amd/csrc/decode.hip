@@ -42,6 +42,8 @@ struct DArgs {
   int64_t a_expert_stride;   // weight elements per expert
   int block_m;            // >= 16: a tile holds block_m / 16 sub-tiles of 16 rows
   int nblk;               // weight-row blocks per expert
+  int nsub_cap;           // sub-tiles in the table's capacity (cap / (16 * NTG))
+  int bm_shift;           // log2(block_m): sub-tile u lies in align tile (u * SUB) >> bm_shift
 };
 
 // One K step of STEP elements: weight rows of WB bytes per element, token rows bf16.
@@ -117,15 +119,13 @@ struct Stream {
   static constexpr int NX = SUB / S::XRPI;      // token-row DMAs per step
 
   // per-lane sources of an item's DMAs at k offset 0
-  // item = (sub-tile u of the align table, weight-row block blk); e: its expert
-  // (index into the weights), >= 0
-  static __device__ __forceinline__ void setup(const DArgs& p,
-                                               const int32_t* __restrict__ sorted_ids, int u,
-                                               int blk, int e, const uint8_t* (&wp)[NW],
+  // item = (sub-tile of the align table, weight-row block blk); idsv: its routed row ids
+  // held in lanes (lane t: row t of the sub-tile); e: its expert (index into the
+  // weights), >= 0
+  static __device__ __forceinline__ void setup(const DArgs& p, int idsv, int blk, int e,
+                                               const uint8_t* (&wp)[NW],
                                                const uint16_t* (&xp)[NX]) {
     const int lane = lane_id();
-    int ids[SUB];
-    load_ids<SUB>(sorted_ids, u, ids);
     const uint8_t* wb = p.A + static_cast<int64_t>(e) * p.a_expert_stride * WB;
     const int rl = lane / S::WCPR, ch = lane % S::WCPR;
 #pragma unroll
@@ -140,12 +140,13 @@ struct Stream {
     }
     // empty slots re-read the sub-tile's first row (row 0 if the whole sub-tile is
     // padding, which happens only when block_m > SUB)
-    const int fb = ids[0] < p.R ? ids[0] : 0;
+    const int id0 = read_lane(idsv, 0);
+    const int fb = id0 < p.R ? id0 : 0;
     const int xl = lane / S::XCPR, xch = lane % S::XCPR;
 #pragma unroll
     for (int j = 0; j < NX; ++j) {
       const int t = j * S::XRPI + xl;
-      int r = pick(ids, t);
+      int r = __shfl(idsv, t, kWave);
       r = r < p.R ? r : fb;
       const int xrow = r / p.gather_div;
       xp[j] = p.X + static_cast<int64_t>(xrow) * p.K + dsw<S::XCPR>(t & 15, xch) * 8;
@@ -182,31 +183,31 @@ struct LocalSubtiles {
   int count;       // local sub-tiles in the table
 };
 
+// The blocks cover the table's capacity (ncap sub-tiles), so the owner loads do not wait
+// for the padded total; sub-tiles at or past nsub (the total's) count as not local.
 template <int SUB>
 __device__ __forceinline__ LocalSubtiles local_subtiles(const int32_t* __restrict__ expert_ids,
-                                                        int nsub, int block_m) {
+                                                        int ncap, int nsub, int bm_shift) {
   const int lane = lane_id();
   LocalSubtiles t;
-  t.B = (nsub + kWave - 1) / kWave;
+  t.B = (ncap + kWave - 1) / kWave;
   uint64_t fl = 0;
-  int cnt = 0;
-  // per-lane loads, issued 8 at a time (before any DMA of the ring is in flight)
+  // per-lane loads, issued 8 at a time (before any DMA of the ring is in flight); they do
+  // not depend on nsub, whose limit is applied to the bits afterwards
   for (int i0 = 0; i0 < t.B; i0 += 8) {
     int ow[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const int u = min(lane * t.B + i0 + i, nsub - 1);
-      ow[i] = expert_ids[(u * SUB) / block_m];
+      const int u = min(lane * t.B + i0 + i, ncap - 1);
+      ow[i] = expert_ids[(u * SUB) >> bm_shift];
     }
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const bool in = i0 + i < t.B && lane * t.B + i0 + i < nsub;
-      if (in && ow[i] >= 0) {
-        fl |= 1ull << (i0 + i);
-        ++cnt;
-      }
-    }
+    for (int i = 0; i < 8; ++i)
+      if (i0 + i < t.B && ow[i] >= 0) fl |= 1ull << (i0 + i);
   }
+  const int lim = nsub - lane * t.B;            // bits at or past lim are past the total
+  fl &= lim >= 64 ? ~0ull : (lim <= 0 ? 0ull : (1ull << lim) - 1);
+  const int cnt = __popcll(fl);
   const int incl = wave_incl_scan(cnt);
   t.pre = incl - cnt;
   t.count = read_lane(incl, kWave - 1);
@@ -279,7 +280,18 @@ __device__ __forceinline__ void zero_range(const DArgs& p, const int32_t* __rest
 // The routing tables are separate __restrict__ arguments: with them the compiler may
 // read the (wave-uniform) entries with scalar loads, which count on lgkmcnt and leave
 // the vmcnt accounting of the DMA ring untouched.
-template <int MODE, int RB, int NTG, int STEP, int P, bool NT, int WB>
+//
+// Latency outside the stream.  Every wave starts at once, so the memory round trips
+// before the first weight DMA and after the last MFMA are dead time for the whole GPU
+// (at one token they are a sizeable part of the launch).  The prologue therefore issues
+// every load that does not depend on another before the first wait: the padded total,
+// the owners of the table's whole capacity, and the routing ids and owner of the
+// sub-tile that the wave's first item has when every sub-tile is local.
+// CACHED (K / STEP >= P: the issue cursor is at most one item ahead of the compute): an
+// item's routing ids (and GEMM2's router weights) are kept from its setup for its
+// epilogue, and the next item's ids and owner are loaded one item ahead, so neither the
+// item boundaries of the DMA stream nor the epilogues wait on the routing tables.
+template <int MODE, int RB, int NTG, int STEP, int P, bool NT, int WB, bool CACHED>
 __global__ void __launch_bounds__(64)
 moe_decode_kernel(DArgs p, const int32_t* __restrict__ sorted_ids,
                   const int32_t* __restrict__ expert_ids, const int32_t* __restrict__ ntpp,
@@ -296,18 +308,25 @@ moe_decode_kernel(DArgs p, const int32_t* __restrict__ sorted_ids,
   __shared__ __attribute__((aligned(1024))) uint8_t ring[P * SLOT];
 
   const int lane = lane_id();
-  const int total = *ntpp;
-  const int nsub = total / SUB;
+  const int first = blockIdx.x;
+  // independent loads first (see above); u0 < nsub_cap keeps them inside the table
+  // (per-lane vector loads: no DMA is in flight yet, so their waits cost nothing, and the
+  // compiler keeps them in one batch with the owner loads)
+  const int u0 = min(first / p.nblk, p.nsub_cap - 1);
+  const int ids0v = sorted_ids[static_cast<int64_t>(u0) * SUB + min(lane, SUB - 1)];
+  const int e0v = expert_ids[(u0 * SUB) >> p.bm_shift];
+  const int totalv = *ntpp;
+  const LocalSubtiles lt = local_subtiles<SUB>(expert_ids, p.nsub_cap, totalv / SUB, p.bm_shift);
+  const int nsub = read_lane(totalv, 0) / SUB;
   if (nsub == 0) return;
-  const LocalSubtiles lt = local_subtiles<SUB>(expert_ids, nsub, p.block_m);
   const int nitems = lt.count * p.nblk;         // items of local sub-tiles
+  const bool all_local = lt.count == nsub;
   // as many waves as give every wave the same number of items (the fewest waves that
   // reach the smallest per-wave count): a wave streams at a bounded rate, so a tail of
   // waves with one item more would run at a fraction of the bandwidth
   const int per = (nitems + gridDim.x - 1) / gridDim.x;
   const int G = per > 0 ? (nitems + per - 1) / per : 0;
-  const int first = blockIdx.x;
-  if (MODE == 2 && lt.count < nsub) {
+  if (MODE == 2 && !all_local) {
     // zeros for the rows of remote sub-tiles: the waves left without local items share
     // them in contiguous ranges (the sub-tile's row ids are loaded once per sub-tile);
     // when every wave streams, each adds an equal share after its own items
@@ -324,37 +343,97 @@ moe_decode_kernel(DArgs p, const int32_t* __restrict__ sorted_ids,
   const int nsteps = p.K / STEP;
   const int gtot = ((nitems - 1 - first) / G + 1) * nsteps;   // this wave's steps
 
-  // local item j -> (sub-tile, block, expert)
-#define MOE_DECODE_ITEM(j, u, blk, e)                                                 \
-  do {                                                                                \
-    const int q_ = (j) / p.nblk;                                                      \
-    blk = (j) - q_ * p.nblk;                                                          \
-    u = lt.count == nsub ? q_ : local_subtile(lt, q_);                                \
-    e = expert_ids[(u * SUB) / p.block_m];                                            \
-  } while (0)
+  // local item j -> (sub-tile u, weight-row block blk)
+  auto item_at = [&](int j, int& u, int& blk) {
+    const int q = j / p.nblk;
+    blk = j - q * p.nblk;
+    u = all_local ? q : local_subtile(lt, q);
+  };
+  auto owner = [&](int u) { return expert_ids[(u * SUB) >> p.bm_shift]; };
+
+  // issue item: routing ids (in lanes), block, expert
+  int iidsv, ib, ie;
+  if (all_local) {
+    ib = first - u0 * p.nblk;
+    ie = read_lane(e0v, 0);
+    iidsv = ids0v;
+  } else {
+    int iu;
+    item_at(first, iu, ib);
+    ie = owner(iu);
+    int ids[SUB];
+    load_ids<SUB>(sorted_ids, iu, ids);
+    iidsv = spread(ids);
+  }
+  // CACHED: the next issue item (loaded one item ahead), the issue item's ids held in
+  // lanes and its GEMM2 router weights (loads in flight), the compute item's ones
+  int nids[SUB], nb = 0, ne = 0;
+  int bw[SUB];
+  int c_idsv = 0, c_wv = 0, cb = 0, ce = 0;
+  auto prefetch_next = [&](int j) {
+    if (j < nitems) {
+      int nu;
+      item_at(j, nu, nb);
+      ne = owner(nu);
+      load_ids<SUB>(sorted_ids, nu, nids);
+    }
+  };
+  // GEMM2: the router weights of the issue item's rows (uniform loads)
+  auto load_issue_weights = [&]() {
+    if (MODE == 2) {
+#pragma unroll
+      for (int t = 0; t < SUB; ++t) {
+        const int r = read_lane(iidsv, t);
+        bw[t] = __float_as_int(topk_w[r < p.R ? r : 0]);
+      }
+    }
+  };
 
   // issue cursor: the step the next DMA batch belongs to (it stays on the last step
   // once everything is issued, so the ring tail re-reads it into unused slots)
   MOE_LDS uint8_t* lring = (MOE_LDS uint8_t*)ring;
   const uint8_t* wp[St::NW];
   const uint16_t* xp[St::NX];
-  int iu, ib, ie;
-  MOE_DECODE_ITEM(first, iu, ib, ie);
-  St::setup(p, sorted_ids, iu, ib, ie, wp, xp);
+  St::setup(p, iidsv, ib, ie, wp, xp);
+  if (CACHED) {
+    load_issue_weights();
+    prefetch_next(first + G);
+  }
   int gi = 0, iss_s = 0, iss_item = first;
-#define MOE_DECODE_ISSUE_NEXT()                                                       \
-  do {                                                                                \
-    St::issue(wp, xp, iss_s * STEP, lring + (gi % P) * SLOT);                         \
-    ++gi;                                                                             \
-    if (gi < gtot && ++iss_s == nsteps) {                                             \
-      iss_s = 0;                                                                      \
-      iss_item += G;                                                                  \
-      MOE_DECODE_ITEM(iss_item, iu, ib, ie);                                          \
-      St::setup(p, sorted_ids, iu, ib, ie, wp, xp);                                   \
-    }                                                                                 \
-  } while (0)
+  auto issue_next = [&]() {
+    St::issue(wp, xp, iss_s * STEP, lring + (gi % P) * SLOT);
+    ++gi;
+    if (gi < gtot && ++iss_s == nsteps) {
+      iss_s = 0;
+      iss_item += G;
+      if (CACHED) {
+        ib = nb;
+        ie = ne;
+        iidsv = spread(nids);
+        St::setup(p, iidsv, ib, ie, wp, xp);
+        load_issue_weights();
+        prefetch_next(iss_item + G);
+      } else {
+        int iu;
+        item_at(iss_item, iu, ib);
+        ie = owner(iu);
+        int ids[SUB];
+        load_ids<SUB>(sorted_ids, iu, ids);
+        iidsv = spread(ids);
+        St::setup(p, iidsv, ib, ie, wp, xp);
+      }
+    }
+  };
 #pragma unroll
-  for (int q = 0; q < P - 1; ++q) MOE_DECODE_ISSUE_NEXT();
+  for (int q = 0; q < P - 1; ++q) issue_next();
+  // CACHED: K / STEP >= P, so the prologue stayed inside the first item
+  auto take_issue_item = [&]() {
+    c_idsv = iidsv;
+    if (MODE == 2) c_wv = spread(bw);
+    cb = ib;
+    ce = ie;
+  };
+  if (CACHED) take_issue_item();
 
   f32x4 acc[NTG][NF];
   int cs = 0, cmp_item = first;
@@ -362,7 +441,7 @@ moe_decode_kernel(DArgs p, const int32_t* __restrict__ sorted_ids,
   for (int g = 0; g < gtot; ++g) {
     wait_vm_c<(P - 2) * NI>();                  // step g's batch has landed in LDS
     asm volatile("" ::: "memory");
-    MOE_DECODE_ISSUE_NEXT();                    // into the slot step g-1 used
+    issue_next();                               // into the slot step g-1 used
     if (cs == 0) {
 #pragma unroll
       for (int q = 0; q < NTG; ++q)
@@ -426,10 +505,27 @@ moe_decode_kernel(DArgs p, const int32_t* __restrict__ sorted_ids,
       // epilogue.  D layout (16x16): lane holds token column (lane & 15), weight rows
       // 4*(lane>>4)+v of each fragment
       cs = 0;
-      int u, blk, cmp_e;
-      MOE_DECODE_ITEM(cmp_item, u, blk, cmp_e);
-      int ids[SUB];
-      load_ids<SUB>(sorted_ids, u, ids);
+      int blk, cmp_e, idsv, wv = 0;
+      if (CACHED) {
+        blk = cb;
+        cmp_e = ce;
+        idsv = c_idsv;
+        wv = c_wv;
+      } else {
+        int u;
+        item_at(cmp_item, u, blk);
+        cmp_e = owner(u);
+        int ids[SUB];
+        load_ids<SUB>(sorted_ids, u, ids);
+        idsv = spread(ids);
+        if (MODE == 2) {
+          int wts[SUB];                         // router weights (uniform loads)
+#pragma unroll
+          for (int t = 0; t < SUB; ++t)
+            wts[t] = __float_as_int(topk_w[ids[t] < p.R ? ids[t] : 0]);
+          wv = spread(wts);
+        }
+      }
       // FP8 weights: the row scales of this lane's accumulator rows 16f + 4(lane>>4) + v.
       // Lane j of stab holds the scale of the item's weight row j (uniform loads, in the
       // order of the DMA rows: gate rows then up rows for GEMM1); the lane-crossbar reads
@@ -453,15 +549,10 @@ moe_decode_kernel(DArgs p, const int32_t* __restrict__ sorted_ids,
           for (int v = 0; v < 4; ++v)
             rs[f][v] = __int_as_float(__shfl(stab, 16 * f + 4 * (lane >> 4) + v, kWave));
       }
-      int wts[SUB];                             // GEMM2 router weights (uniform loads)
-      if (MODE == 2) {
-#pragma unroll
-        for (int t = 0; t < SUB; ++t) wts[t] = __float_as_int(topk_w[ids[t] < p.R ? ids[t] : 0]);
-      }
 #pragma unroll
       for (int q = 0; q < NTG; ++q) {
-        const int r = pick(ids, 16 * q + tr);
-        const float wr = MODE == 2 ? __int_as_float(pick(wts, 16 * q + tr)) : 0.f;
+        const int r = __shfl(idsv, 16 * q + tr, kWave);
+        const float wr = MODE == 2 ? __int_as_float(__shfl(wv, 16 * q + tr, kWave)) : 0.f;
         if (r < p.R) {
           if (MODE == 1) {
 #pragma unroll
@@ -500,16 +591,16 @@ moe_decode_kernel(DArgs p, const int32_t* __restrict__ sorted_ids,
         }
       }
       cmp_item += G;
+      // the issue cursor is on the next item by now (or still on this one, the last)
+      if (CACHED) take_issue_item();
     }
   }
-  if (MODE == 2 && lt.count < nsub && G == static_cast<int>(gridDim.x)) {
+  if (MODE == 2 && !all_local && G == static_cast<int>(gridDim.x)) {
     const int64_t nz = static_cast<int64_t>(nsub) * p.nblk;
     zero_range<RB, SUB>(p, sorted_ids, lt, static_cast<int>(nz * first / G),
                         static_cast<int>(nz * (first + 1) / G));
   }
   wait_vm_c<0>();                                // no DMA may land after the wave exits
-#undef MOE_DECODE_ISSUE_NEXT
-#undef MOE_DECODE_ITEM
 }
 
 constexpr int kDecodeRB = 64;   // weight rows per work item (32 for bf16 16-row sub-tiles)
@@ -529,10 +620,17 @@ hipError_t launch_decode(const DArgs& p0, const GemmArgs& g, hipStream_t s) {
   p.nblk = (MODE == 1 ? 2 * p.I : p.H) / RB;
   constexpr int kLds = P * (RB * S::WROWB + 16 * NTG * S::XROWB);
   constexpr int kPerCU = std::max(1, (160 * 1024) / kLds);
-  const int64_t max_items = (g.cap / (16 * NTG)) * p.nblk;
+  p.nsub_cap = static_cast<int>(g.cap / (16 * NTG));
+  p.bm_shift = __builtin_ctz(static_cast<unsigned>(p.block_m));   // block_m: a power of two
+  if (p.nsub_cap == 0) return hipSuccess;
+  const int64_t max_items = static_cast<int64_t>(p.nsub_cap) * p.nblk;
   const unsigned grid = static_cast<unsigned>(std::min<int64_t>(max_items, 256 * kPerCU));
-  hipLaunchKernelGGL((moe_decode_kernel<MODE, RB, NTG, STEP, P, NT, WB>), dim3(grid), dim3(64), 0,
-                     s, p, g.sorted_ids, g.expert_ids, g.ntpp, g.topk_w, g.w_scale);
+  if (p.K / STEP >= P)
+    hipLaunchKernelGGL((moe_decode_kernel<MODE, RB, NTG, STEP, P, NT, WB, true>), dim3(grid),
+                       dim3(64), 0, s, p, g.sorted_ids, g.expert_ids, g.ntpp, g.topk_w, g.w_scale);
+  else
+    hipLaunchKernelGGL((moe_decode_kernel<MODE, RB, NTG, STEP, P, NT, WB, false>), dim3(grid),
+                       dim3(64), 0, s, p, g.sorted_ids, g.expert_ids, g.ntpp, g.topk_w, g.w_scale);
   return hipGetLastError();
 }
 

@@ -384,6 +384,21 @@ def test_layer_reduced(lib, name, T, scale):
     _layer_vs_oracle(lib, wl, lay)
 
 
+@pytest.mark.parametrize("name,T", [("deepseek_decode", 1), ("deepseek_decode", 3),
+                                    ("deepseek_decode", 8), ("deepseek_decode_fp8", 2),
+                                    ("qwen3_skewed", 5)])
+def test_layer_small_batch_repeated(lib, name, T):
+    """Small decode batches (one-launch route + align, weight-streaming GEMMs): three calls
+    in a row on the same buffers with new activations (so the experts change), each against
+    the oracle."""
+    base = S.WORKLOADS[name]
+    q = 128 if name.endswith("fp8") else 64
+    wl = base.scaled(T=T, H=base.H // 4 // q * q, I=base.I // 4 // q * q)
+    for rep in range(3):
+        lay = S.make_layer(wl, device=DEV, seed=9, x_seed=100 + rep)
+        _layer_vs_oracle(lib, wl, lay)
+
+
 @pytest.mark.parametrize("name,T,scale", [("deepseek_decode_fp8", 1, 4),
                                           ("deepseek_decode_fp8", 8, 4),
                                           ("deepseek_decode_fp8", 64, 4),
