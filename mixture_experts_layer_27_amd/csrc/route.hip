@@ -84,37 +84,6 @@ router_logits_f32_kernel(const float* __restrict__ x, const float* __restrict__ 
   logits[i] = acc;
 }
 
-// (value, index) arg-max across the wave: better = larger value, then smaller index.
-// Indices are distinct, so the order is total and the combining order does not matter.
-__device__ __forceinline__ void argmax_merge(float& v, int& idx, float ov, int oi) {
-  const bool take = (ov > v) | ((ov == v) & (oi < idx));   // no short-circuit branches
-  v = take ? ov : v;
-  idx = take ? oi : idx;
-}
-
-template <int CTRL>
-__device__ __forceinline__ void argmax_step(float& v, int& idx) {
-  const float ov = __int_as_float(dpp_move<CTRL>(__float_as_int(v)));
-  const int oi = dpp_move<CTRL>(idx);
-  argmax_merge(v, idx, ov, oi);
-}
-
-// Every lane returns the wave's best: DPP within each 16-lane row, then the four row
-// winners read as uniform values.
-__device__ __forceinline__ void wave_argmax(float& v, int& idx) {
-  argmax_step<dpp::kQuadXor1>(v, idx);
-  argmax_step<dpp::kQuadXor2>(v, idx);
-  argmax_step<dpp::kRowHalfMirror>(v, idx);
-  argmax_step<dpp::kRowMirror>(v, idx);
-  float b = read_lane(v, 0);
-  int bi = read_lane(idx, 0);
-  argmax_merge(b, bi, read_lane(v, 16), read_lane(idx, 16));
-  argmax_merge(b, bi, read_lane(v, 32), read_lane(idx, 32));
-  argmax_merge(b, bi, read_lane(v, 48), read_lane(idx, 48));
-  v = b;
-  idx = bi;
-}
-
 // (m1, m2) <- the two largest of {m1, m2, o1, o2}, given m1 >= m2 and o1 >= o2
 __device__ __forceinline__ void top2_merge(float& m1, float& m2, float o1, float o2) {
   const float n2 = fmaxf(fminf(m1, o1), fmaxf(m2, o2));
@@ -130,6 +99,30 @@ __device__ __forceinline__ void top2_steps(float (&m1)[NSLOT], float (&m2)[NSLOT
     const float o2 = __int_as_float(dpp_move<CTRL>(__float_as_int(m2[i])));
     top2_merge(m1[i], m2[i], o1, o2);
   }
+}
+
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ uint64_t key_max_step(uint64_t v) {
+  const uint32_t lo = static_cast<uint32_t>(dpp_move<CTRL, ROW_MASK>(static_cast<int>(v)));
+  const uint32_t hi = static_cast<uint32_t>(dpp_move<CTRL, ROW_MASK>(static_cast<int>(v >> 32)));
+  const uint64_t o = (static_cast<uint64_t>(hi) << 32) | lo;
+  return o > v ? o : v;
+}
+
+// Maximum of an unsigned 64-bit key over the wave (0 is the identity: lanes a DPP move
+// does not write read 0).  Within each 16-lane row by four moves, then row 0 into row 1
+// and row 2 into row 3 (row_bcast:15), then row 1 into rows 2 and 3 (row_bcast:31): lane
+// 63 ends with the maximum, which every lane reads.
+__device__ __forceinline__ uint64_t wave_max_key(uint64_t v) {
+  v = key_max_step<dpp::kQuadXor1>(v);
+  v = key_max_step<dpp::kQuadXor2>(v);
+  v = key_max_step<dpp::kRowHalfMirror>(v);
+  v = key_max_step<dpp::kRowMirror>(v);
+  v = key_max_step<dpp::kRowBcast15, 0xA>(v);
+  v = key_max_step<dpp::kRowBcast31, 0xC>(v);
+  const uint32_t lo = static_cast<uint32_t>(read_lane(static_cast<int>(v), kWave - 1));
+  const uint32_t hi = static_cast<uint32_t>(read_lane(static_cast<int>(v >> 32), kWave - 1));
+  return (static_cast<uint64_t>(hi) << 32) | lo;
 }
 
 __device__ __forceinline__ float sigmoid_rn(float l) {
@@ -265,30 +258,39 @@ __device__ void topk_token(const TopkParams& p, int t, TopkLds& sh, int32_t* ids
     }
     wave_sync();                                   // cval is reused by the next token
   }
-  // k selections; lane j keeps the j-th chosen (id, weight source) pair.  Branch-free:
-  // invalid, masked and taken slots hold -inf and never win (at least k finite
-  // candidates exist), and within a lane a larger slot is a larger index, so a strict
-  // comparison keeps the lower index on ties.
+  // k selections; lane j keeps the j-th chosen (id, weight source) pair.  Each candidate
+  // is one 64-bit key: the selection value's bits mapped to an unsigned order (-0 folded
+  // into +0, so equal values give equal high words) above the complemented expert index,
+  // so the largest key is the largest value and, among equal values, the lower index.
+  // Invalid, masked and taken candidates hold key 0, below every eligible key (at least
+  // k eligible candidates exist).  A pick is a wave maximum of the lanes' best keys.
+  uint64_t key[NSLOT];
+#pragma unroll
+  for (int i = 0; i < NSLOT; ++i) {
+    const uint32_t b = __float_as_uint(sel[i] + 0.f);
+    const uint32_t ord = b ^ (static_cast<uint32_t>(static_cast<int32_t>(b) >> 31) | 0x80000000u);
+    key[i] = sel[i] == kNegInf ? 0ull
+                               : (static_cast<uint64_t>(ord) << 32) |
+                                     static_cast<uint32_t>(~(lane + kWave * i));
+  }
+  uint64_t lbest = key[0];
+#pragma unroll
+  for (int i = 1; i < NSLOT; ++i) lbest = key[i] > lbest ? key[i] : lbest;
   int my_id = 0;
   float my_src = 0.f;
   for (int j = 0; j < k; ++j) {
-    float best = sel[0];
-    int bi = lane;
+    const uint64_t best = wave_max_key(lbest);
+    const int bi = static_cast<int>(~static_cast<uint32_t>(best));
+    const int slot = bi / kWave;                    // uniform
+    float src = wsrc[0];
 #pragma unroll
-    for (int i = 1; i < NSLOT; ++i) {
-      const bool better = sel[i] > best;
-      best = better ? sel[i] : best;
-      bi = better ? lane + kWave * i : bi;
-    }
-    wave_argmax(best, bi);
-    float src = 0.f;
+    for (int i = 1; i < NSLOT; ++i) src = slot == i ? wsrc[i] : src;
+    src = read_lane(src, bi & (kWave - 1));         // the owner lane's weight source
 #pragma unroll
-    for (int i = 0; i < NSLOT; ++i) {
-      const bool hit = lane + kWave * i == bi;
-      src = hit ? wsrc[i] : src;
-      sel[i] = hit ? kNegInf : sel[i];
-    }
-    src = read_lane(src, bi & (kWave - 1));        // the owner lane broadcasts
+    for (int i = 0; i < NSLOT; ++i) key[i] = key[i] == best ? 0ull : key[i];
+    lbest = key[0];
+#pragma unroll
+    for (int i = 1; i < NSLOT; ++i) lbest = key[i] > lbest ? key[i] : lbest;
     my_id = lane == j ? bi : my_id;
     my_src = lane == j ? src : my_src;
   }
@@ -337,7 +339,14 @@ route_align_small_kernel(TopkParams p, int bm, int64_t cap, int32_t* __restrict_
   __shared__ TopkLds sh[16];
   __shared__ int32_t ids_lds[kFusedMaxRows];
   __shared__ float lg[kFusedMaxT * 4 * kWave];   // summed logits [T][E], E <= 256
+  __shared__ float soff[4 * kWave], sbias[4 * kWave];
   const int w = wave_id();
+  // the per-expert offsets and biases are staged in LDS beside the logits, their loads in
+  // flight together with the slab loads below
+  for (int i = threadIdx.x; i < p.E; i += blockDim.x) {
+    if (p.offset) soff[i] = p.offset[i];
+    if (p.bias) sbias[i] = p.bias[i];
+  }
   // every thread sums the K slabs of some (token, expert) pairs, all slab loads in flight
   // at once (slabs added in ascending order, as in the one-wave path), so the per-token
   // selection below reads its logits from LDS instead of waiting on global round trips
@@ -358,6 +367,8 @@ route_align_small_kernel(TopkParams p, int bm, int64_t cap, int32_t* __restrict_
   q.logits = lg;
   q.nz = 1;
   q.logits_out = nullptr;
+  q.offset = p.offset ? soff : nullptr;
+  q.bias = p.bias ? sbias : nullptr;
   for (int t = w; t < p.T; t += 16) topk_token<NSLOT, 1>(q, t, sh[w], ids_lds);
   __syncthreads();
   alignd::align_small_body(ids_lds, p.T * (p.k + p.shared), p.E + p.shared, bm, cap, sorted_ids,
