@@ -56,31 +56,67 @@ align_hist_kernel(const int32_t* __restrict__ ids, int R, int E, int nseg, int64
 }
 
 // Phase 2 (one work-group): totals, scan, expert_ids; hist[seg][e] becomes the run
-// base of expert e in segment seg.
+// base of expert e in segment seg.  The [nseg x E] matrix is walked by every thread:
+// thread (g, e) owns expert e and the contiguous segments [q0, q1) of group g (G groups,
+// threads of one group read adjacent experts, so each row of hist is read coalesced), with
+// loads issued eight at a time; the groups' partial counts are combined in LDS.
 __global__ void __launch_bounds__(kAlignThreads)
 align_scan_kernel(int R, int E, int bm, int64_t cap, int nseg, int32_t* __restrict__ hist,
                   int32_t* __restrict__ expert_ids, int32_t* __restrict__ ntpp,
                   int32_t* __restrict__ counts, const int32_t* __restrict__ emap) {
+  constexpr int kB = 8;                         // loads in flight per thread
+  __shared__ int part[kAlignThreads];           // [g][e]: count, then the group's base
   __shared__ int cnt[kMaxE], start[kMaxE];
   __shared__ int total_s;
-  for (int e = threadIdx.x; e < E; e += blockDim.x) {
-    int s = 0;
-    for (int q = 0; q < nseg; ++q) s += hist[static_cast<int64_t>(q) * E + e];
-    cnt[e] = s;
+  int ep = 1;                                   // E rounded up to a power of two
+  while (ep < E) ep <<= 1;
+  const int G = kAlignThreads / ep;             // >= 2 (E <= 512)
+  const int e = threadIdx.x % ep, g = threadIdx.x / ep;
+  const int per = (nseg + G - 1) / G;
+  const int q0 = min(nseg, g * per), q1 = min(nseg, q0 + per);
+  const bool mine = e < E;
+  int s = 0;
+  if (mine) {
+    for (int q = q0; q < q1; q += kB) {
+      int v[kB];
+#pragma unroll
+      for (int b = 0; b < kB; ++b)
+        v[b] = q + b < q1 ? hist[static_cast<int64_t>(q + b) * E + e] : 0;
+#pragma unroll
+      for (int b = 0; b < kB; ++b) s += v[b];
+    }
+  }
+  part[threadIdx.x] = s;
+  __syncthreads();
+  // per expert: total count, and each group's base inside the expert's run (groups in
+  // ascending segment order)
+  if (g == 0 && mine) {
+    int run = 0;
+    for (int h = 0; h < G; ++h) {
+      const int c = part[h * ep + e];
+      part[h * ep + e] = run;
+      run += c;
+    }
+    cnt[e] = run;
   }
   __syncthreads();
   scan_padded(cnt, E, bm, start, &total_s);
   __syncthreads();
   const int total = total_s;
-  for (int e = threadIdx.x; e < E; e += blockDim.x) {
-    int run = start[e];
-    for (int q = 0; q < nseg; ++q) {
-      const int64_t i = static_cast<int64_t>(q) * E + e;
-      const int c = hist[i];
-      hist[i] = run;
-      run += c;
+  if (mine) {
+    int run = start[e] + part[threadIdx.x];
+    for (int q = q0; q < q1; q += kB) {
+      int v[kB];
+#pragma unroll
+      for (int b = 0; b < kB; ++b)
+        v[b] = q + b < q1 ? hist[static_cast<int64_t>(q + b) * E + e] : 0;
+#pragma unroll
+      for (int b = 0; b < kB; ++b) {
+        if (q + b < q1) hist[static_cast<int64_t>(q + b) * E + e] = run;
+        run += v[b];
+      }
     }
-    if (counts) counts[e] = cnt[e];
+    if (counts && g == 0) counts[e] = cnt[e];
   }
   if (threadIdx.x == 0) *ntpp = total;
   fill_expert_ids(cnt, start, E, bm, total, cap, expert_ids, emap);
