@@ -71,6 +71,103 @@ router_logits_bf16_kernel(const uint16_t* __restrict__ x, const uint16_t* __rest
   }
 }
 
+// Large batches (many experts): a work-group computes a 64-token x 64-expert tile, its
+// 4 waves 32 x 32 each (2 x 2 MFMA 16x16 blocks).  Per 64-element K chunk the x and Wg
+// tiles (8 KB each) are staged in LDS, double-buffered, with the next chunk's global
+// loads in flight during the current chunk's MFMAs; every wave then reads its fragments
+// from LDS instead of from global memory, which cuts the L2 traffic per logit about
+// fourfold against one-wave 16 x 16 tiles.  LDS rows are 128 bytes; 16-byte chunk c of
+// row r sits at c ^ ((r >> 1) & 7), so the 16 rows an MFMA operand read touches at one
+// logical chunk land on distinct bank groups.  The MFMAs run over k in ascending order,
+// as in the kernels above.
+constexpr int kRt = 64;                            // tile rows (tokens) and columns (experts)
+
+__global__ void __launch_bounds__(256)
+router_logits_tile_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ wg, int T,
+                          int H, int E, float* __restrict__ logits) {
+  __shared__ __attribute__((aligned(16))) uint8_t sm[2][2][kRt * 128];   // [buf][x|wg]
+  const int tid = threadIdx.x, lane = lane_id(), w = wave_id();
+  const int t0 = blockIdx.x * kRt, e0 = blockIdx.y * kRt;
+  // staging: thread tid moves 16-byte chunks (row, c) = (tid / 8 + 32 * h, tid % 8), h = 0, 1
+  const int sr = tid / 8, sc = tid % 8;
+  const uint16_t* xs[2];
+  const uint16_t* ws[2];
+  int so[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int r = sr + 32 * h;
+    xs[h] = x + static_cast<int64_t>(min(t0 + r, T - 1)) * H + sc * 8;
+    ws[h] = wg + static_cast<int64_t>(min(e0 + r, E - 1)) * H + sc * 8;
+    so[h] = r * 128 + ((sc ^ ((r >> 1) & 7)) * 16);
+  }
+  const int wt = (w >> 1) * 32, we = (w & 1) * 32;   // this wave's 32 x 32 sub-tile
+  const int fr = lane & 15, fg = lane >> 4;          // MFMA operand row, k group
+  f32x4 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  u32x4 px[2], pw[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    px[h] = *reinterpret_cast<const u32x4*>(xs[h]);
+    pw[h] = *reinterpret_cast<const u32x4*>(ws[h]);
+  }
+  const int nchunk = H / 64;
+  for (int c = 0; c < nchunk; ++c) {
+    uint8_t* bx = sm[c & 1][0];
+    uint8_t* bw = sm[c & 1][1];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      *reinterpret_cast<u32x4*>(bx + so[h]) = px[h];
+      *reinterpret_cast<u32x4*>(bw + so[h]) = pw[h];
+    }
+    __syncthreads();
+    if (c + 1 < nchunk) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        px[h] = *reinterpret_cast<const u32x4*>(xs[h] + (c + 1) * 64);
+        pw[h] = *reinterpret_cast<const u32x4*>(ws[h] + (c + 1) * 64);
+      }
+    }
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const int ch = ks * 4 + fg;                    // logical 16-byte chunk of the row
+      bf16x8 a[2], b[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int r = wt + 16 * i + fr;
+        a[i] = *reinterpret_cast<const bf16x8*>(bx + r * 128 + ((ch ^ ((r >> 1) & 7)) * 16));
+      }
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int r = we + 16 * j + fr;
+        b[j] = *reinterpret_cast<const bf16x8*>(bw + r * 128 + ((ch ^ ((r >> 1) & 7)) * 16));
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+    }
+    // the buffer written next iteration (the other one) was last read one iteration ago,
+    // before this iteration's barrier: no second barrier needed
+  }
+  // D layout (16x16): lane holds column (lane & 15) = expert, rows 4*(lane>>4)+v = tokens
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int ec = e0 + we + 16 * j + (lane & 15);
+    if (ec >= E) continue;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int tr = t0 + wt + 16 * i + 4 * (lane >> 4) + v;
+        if (tr < T) logits[static_cast<int64_t>(tr) * E + ec] = acc[i][j][v];
+      }
+  }
+}
+
 __global__ void __launch_bounds__(256)
 router_logits_f32_kernel(const float* __restrict__ x, const float* __restrict__ wg, int T,
                          int H, int E, float* __restrict__ logits) {
@@ -443,8 +540,9 @@ hipError_t launch_router_logits(const void* x, const void* wg, int T, int H, int
     hipLaunchKernelGGL(router_logits_bf16_kernel<2>, dim3(tb, 1, 1), dim3(256), 0, s, xb, wb, T,
                        H, E, H, logits);
   } else {
-    hipLaunchKernelGGL(router_logits_bf16_kernel<1>, dim3(tb, (E + 63) / 64, 1), dim3(256), 0, s,
-                       xb, wb, T, H, E, H, logits);
+    hipLaunchKernelGGL(router_logits_tile_kernel,
+                       dim3(static_cast<unsigned>((T + kRt - 1) / kRt), (E + kRt - 1) / kRt),
+                       dim3(256), 0, s, xb, wb, T, H, E, logits);
   }
   return hipGetLastError();
 }
