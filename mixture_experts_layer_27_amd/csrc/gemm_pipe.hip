@@ -19,6 +19,8 @@
 //   a 3-stage ring), each 16-byte chunk is expanded to bf16 after the LDS read (exact)
 //   and feeds two bf16 MFMAs, and the row scales (staged in LDS with the tile's rows)
 //   multiply the fp32 accumulators in the epilogue.
+#include <algorithm>
+#include <atomic>
 #include <type_traits>
 
 #include "common.hpp"
@@ -43,6 +45,10 @@ struct PArgs {
   int block_m;
   int mtiles, nblocks;
   int n_outer;             // raster order of the tile groups (see grouped_slot)
+  // GEMM2, bf16 weights: split of the last partial round (see split_plan); 1 = off
+  int split_max;
+  int ncu;                 // compute units: one round = ncu tiles (one work-group per CU)
+  float* partial;          // [ncu][BM][BN] fp32 partial sums of the split tiles
 };
 
 template <int MODE, int BM, int BN, int WM, int WN, int BK_, int NSTAGE, int WB = 2>
@@ -142,6 +148,50 @@ __device__ __forceinline__ bool grouped_slot(int bid, int mtiles, int nblocks, b
 }
 constexpr int kGroupM = 4, kGroupN = 8;
 
+// GEMM2 (bf16 weights): balanced rounds with a split last round.  GEMM2's tiles are few
+// and long (K = I), so the rounds of ncu tiles (one work-group per CU) quantise: at the
+// Mixtral-8x7B shape 592 tiles make 2.3 rounds but take 3, with the grouped raster above
+// dealing 96 tiles to some XCDs and 64 to others.  Here the real tile count N (from the
+// padded total on the device) is split into N - rem whole tiles, rem = N mod ncu, and the
+// rem tiles of the last round, each cut into `parts` K ranges (parts <= split_max, parts *
+// rem <= ncu), so the last round is a few partial-sum work-groups spread over every CU.
+// Whole tiles: XCD x (= bid % 8) takes the contiguous tile range [x N'/8, (x+1) N'/8) in
+// order; tiles are ordered in strips of 8 n-blocks with the m-tiles inside, so the 32
+// tiles an XCD runs at once are 4 m-tiles x 8 n-blocks, as with the grouped raster.  Split
+// parts write raw fp32 sums to `partial`; a fix-up launch adds them in part order and
+// applies the router weight.  When the plan splits nothing (rem = 0, or too many tiles
+// left over for a short round) the grouped raster above is kept.
+struct SplitPlan {
+  int mreal, full, rem, parts;
+};
+__device__ __forceinline__ SplitPlan split_plan(int total, int bm, int nblocks, int ncu,
+                                                int split_max, int nk) {
+  SplitPlan s;
+  s.mreal = total / bm;
+  const int nreal = s.mreal * nblocks;
+  s.rem = nreal % ncu;
+  s.parts = s.rem > 0 ? min(min(split_max, ncu / s.rem), nk) : 1;
+  if (s.parts < 2) {
+    s.rem = 0;
+    s.parts = 1;
+  }
+  s.full = nreal - s.rem;
+  return s;
+}
+// tile q of the strip order -> (m-tile, n-block)
+__device__ __forceinline__ void strip_tile(int q, int mreal, int nblocks, int& mt, int& nb) {
+  const int nfs = nblocks / 8, span = mreal * 8;
+  if (q < nfs * span) {
+    const int st = q / span, r = q - st * span;
+    mt = r / 8;
+    nb = st * 8 + r % 8;
+  } else {
+    const int wl = nblocks - nfs * 8, r = q - nfs * span;
+    mt = r / wl;
+    nb = nfs * 8 + r % wl;
+  }
+}
+
 template <int MODE, int BM, int BN, int WM, int WN, int BK, int NSTAGE, int PFD, int WB>
 __global__ void __launch_bounds__(WM * WN * 64)
 moe_gemm_pipe_kernel(PArgs p) {
@@ -153,7 +203,34 @@ moe_gemm_pipe_kernel(PArgs p) {
   __shared__ __attribute__((aligned(256))) uint8_t pf_sink[PFD > 0 ? 256 : 4];
 
   int mt, nb;
-  if (!grouped_slot<kGroupM, kGroupN>(blockIdx.x, p.mtiles, p.nblocks, p.n_outer, mt, nb)) return;
+  int kb = 0, ke = p.K / C::BK;   // the K stages of this work-group
+  int unit = -1;                  // >= 0: a K range of a split tile (writes partial sums)
+  SplitPlan sp{0, 0, 0, 1};
+  if (MODE == 2 && p.split_max > 1)
+    sp = split_plan(*p.ntpp, BM, p.nblocks, p.ncu, p.split_max, ke);
+  if (sp.parts > 1) {
+    const int xcd = blockIdx.x & 7, j = blockIdx.x >> 3;
+    const int x0 = static_cast<int>(static_cast<int64_t>(sp.full) * xcd / 8);
+    const int x1 = static_cast<int>(static_cast<int64_t>(sp.full) * (xcd + 1) / 8);
+    const int jmax = (sp.full + 7) / 8;
+    int q;
+    if (j < x1 - x0) {
+      q = x0 + j;
+    } else if (j >= jmax) {
+      const int v = (j - jmax) * 8 + xcd;
+      if (v >= sp.rem * sp.parts) return;
+      q = sp.full + v / sp.parts;
+      const int part = v % sp.parts, nk0 = ke;
+      unit = v;
+      kb = part * nk0 / sp.parts;
+      ke = (part + 1) * nk0 / sp.parts;
+    } else {
+      return;
+    }
+    strip_tile(q, sp.mreal, p.nblocks, mt, nb);
+  } else if (!grouped_slot<kGroupM, kGroupN>(blockIdx.x, p.mtiles, p.nblocks, p.n_outer, mt, nb)) {
+    return;
+  }
   const int total = *p.ntpp;
   if (mt * BM >= total) return;
   const int e = p.expert_ids[(mt * BM) / p.block_m];
@@ -171,7 +248,8 @@ moe_gemm_pipe_kernel(PArgs p) {
   }
   if (MODE == 2 && e < 0) {
     // expert held by another GPU: zeros in this tile's slice of y, so the combine adds
-    // nothing for these rows
+    // nothing for these rows (the fix-up writes them for a split tile)
+    if (unit >= 0) return;
     __syncthreads();
     float* out = static_cast<float*>(p.C);
     for (int idx = tid; idx < BM * (BN / 4); idx += C::NT) {
@@ -213,7 +291,7 @@ moe_gemm_pipe_kernel(PArgs p) {
     const int m = C::RPIA * (w + C::NW * j) + lrow;
     const int r = srow[m];
     const int arow = r < p.R ? r / p.gather_div : 0;
-    a_src[j] = p.A + static_cast<int64_t>(arow) * K + ((pch ^ swz<C::ROWA>(m)) << 3);
+    a_src[j] = p.A + static_cast<int64_t>(arow) * K + kb * C::BK + ((pch ^ swz<C::ROWA>(m)) << 3);
   }
   const uint8_t* b_base = p.B + static_cast<int64_t>(e) * p.b_expert_stride * WB;
   const uint8_t* b_src[C::LB];
@@ -221,7 +299,7 @@ moe_gemm_pipe_kernel(PArgs p) {
 #pragma unroll
   for (int j = 0; j < C::LB; ++j) {
     const int n = C::RPIB * (w + C::NW * j) + lrowb;
-    b_src[j] = b_base + static_cast<int64_t>(b_row(n)) * K * WB +
+    b_src[j] = b_base + static_cast<int64_t>(b_row(n)) * K * WB + kb * C::BK * WB +
                ((pchb ^ swz<C::ROWB>(n)) << 4);
   }
 
@@ -232,9 +310,9 @@ moe_gemm_pipe_kernel(PArgs p) {
   if constexpr (PFD > 0) {
     const int m = (BM / C::NW) * w + lane % (BM / C::NW);
     const int r = srow[m];
-    pfa = p.A + static_cast<int64_t>(r < p.R ? r / p.gather_div : 0) * K;
+    pfa = p.A + static_cast<int64_t>(r < p.R ? r / p.gather_div : 0) * K + kb * C::BK;
     const int n = (BN / C::NW) * w + lane % (BN / C::NW);
-    pfb = b_base + static_cast<int64_t>(b_row(n)) * K * WB;
+    pfb = b_base + static_cast<int64_t>(b_row(n)) * K * WB + kb * C::BK * WB;
   }
   auto prefetch = [&](int kt) {
     if constexpr (PFD > 0) {
@@ -264,7 +342,7 @@ moe_gemm_pipe_kernel(PArgs p) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
-  const int nk = K / C::BK;
+  const int nk = ke - kb;
   // Fragments of step ks of stage kt: A rows of this wave's M slice, B rows of its N
   // slice.  bf16 weights: one k16 step per ks, lanes 0-31 take logical chunk 2*ks,
   // lanes 32-63 chunk 2*ks+1 of each row.  FP8 weights: two k16 steps per ks (32
@@ -445,6 +523,18 @@ moe_gemm_pipe_kernel(PArgs p) {
       *reinterpret_cast<u32x4*>(out + static_cast<int64_t>(r) * p.N + col) =
           *reinterpret_cast<const u32x4*>(smem + m * ROWS + c * 16);
     }
+  } else if (unit >= 0) {
+    // split tile: raw fp32 sums of this K range, [BM][BN] per part
+    float* part = p.partial + static_cast<int64_t>(unit) * BM * BN;
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int m = wm * C::WTM + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+#pragma unroll
+        for (int j = 0; j < C::FN; ++j)
+          part[m * BN + wn * C::WTN + j * 32 + (lane & 31)] = acc[i][j][v];
+      }
   } else {
     float* out = static_cast<float*>(p.C);
 #pragma unroll
@@ -465,6 +555,51 @@ moe_gemm_pipe_kernel(PArgs p) {
       }
     }
   }
+}
+
+// Fix-up of the split GEMM2 tiles: y = w * (sum of the parts in part order); rows of a
+// tile whose expert is held by another GPU get zeros.  Block (i, b): split tile i,
+// elements 1024 b .. 1024 b + 1023 of its BM x BN slice, four per thread.
+template <int BM, int BN, int BK>
+__global__ void __launch_bounds__(256)
+gemm2_split_fixup_kernel(PArgs p) {
+  const int total = *p.ntpp;
+  const SplitPlan sp = split_plan(total, BM, p.nblocks, p.ncu, p.split_max, p.K / BK);
+  const int i = blockIdx.x;
+  if (i >= sp.rem) return;
+  int mt, nb;
+  strip_tile(sp.full + i, sp.mreal, p.nblocks, mt, nb);
+  const int idx = (blockIdx.y * 256 + threadIdx.x) * 4;
+  if (idx >= BM * BN) return;
+  const int m = idx / BN, c = idx % BN;
+  const int r = p.sorted_ids[static_cast<int64_t>(mt) * BM + m];
+  const int col = nb * BN + c;
+  if (r >= p.R || col >= p.N) return;                // N % 4 == 0: the 4 columns are in
+  float* out = static_cast<float*>(p.C) + static_cast<int64_t>(r) * p.N + col;
+  if (p.expert_ids[(mt * BM) / p.block_m] < 0) {
+    *reinterpret_cast<float4*>(out) = make_float4(0.f, 0.f, 0.f, 0.f);
+    return;
+  }
+  const float* src = p.partial + static_cast<int64_t>(i) * sp.parts * BM * BN + idx;
+  float4 a = *reinterpret_cast<const float4*>(src);
+  for (int q = 1; q < sp.parts; ++q) {
+    const float4 b = *reinterpret_cast<const float4*>(src + static_cast<int64_t>(q) * BM * BN);
+    a.x += b.x; a.y += b.y; a.z += b.z; a.w += b.w;
+  }
+  const float wr = p.topk_w[r];
+  *reinterpret_cast<float4*>(out) = make_float4(wr * a.x, wr * a.y, wr * a.z, wr * a.w);
+}
+
+int device_cu_count() {
+  static std::atomic<int> cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  int v = cached[dev].load(std::memory_order_relaxed);
+  if (v == 0) {
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    cached[dev].store(v, std::memory_order_relaxed);
+  }
+  return v;
 }
 
 template <int MODE, int BM, int BN, int WM, int WN, int BK, int NSTAGE, int PFD, int WB = 2>
@@ -493,10 +628,25 @@ hipError_t run_pipe(const GemmArgs& g, hipStream_t s) {
   // every (group, position) slot: ceil over groups of kGroupM x kGroupN, 8 XCDs at a time
   const int64_t groups = static_cast<int64_t>((p.mtiles + kGroupM - 1) / kGroupM) *
                          ((p.nblocks + kGroupN - 1) / kGroupN);
-  const int64_t G = (groups + 7) / 8 * 8 * kGroupM * kGroupN;
+  int64_t G = (groups + 7) / 8 * 8 * kGroupM * kGroupN;
   if (G == 0) return hipSuccess;
+  p.split_max = 1;
+  if (MODE == 2 && WB == 2 && g.split_ws) {
+    const int ncu = device_cu_count();
+    if (ncu > 0 && g.split_ws_bytes >= static_cast<size_t>(ncu) * BM * BN * sizeof(float)) {
+      p.split_max = 4;
+      p.ncu = ncu;
+      p.partial = g.split_ws;
+      // whole tiles (<= every real tile) + one round of parts + the XCD rounding, or the
+      // grouped raster's slots when the plan does not split
+      G = std::max<int64_t>(G, (static_cast<int64_t>(p.mtiles) * p.nblocks + ncu + 16 + 7) / 8 * 8);
+    }
+  }
   hipLaunchKernelGGL((moe_gemm_pipe_kernel<MODE, BM, BN, WM, WN, BK, NSTAGE, PFD, WB>),
                      dim3(static_cast<unsigned>(G)), dim3(WM * WN * 64), 0, s, p);
+  if (MODE == 2 && p.split_max > 1)
+    hipLaunchKernelGGL((gemm2_split_fixup_kernel<BM, BN, BK>),
+                       dim3(static_cast<unsigned>(p.ncu), (BM * BN) / 1024), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 

@@ -52,7 +52,15 @@ struct GemmArgs {
   const int32_t* ntpp;
   int T, H, I, E, k, block_m;
   int64_t cap;               // capacity of sorted_ids
+  // GEMM2 prefill, bf16 weights: room for the partial sums of a split last round of
+  // tiles (used when it holds one [256 x 256] fp32 tile per compute unit; else unsplit)
+  float* split_ws = nullptr;
+  size_t split_ws_bytes = 0;
 };
+
+// workspace the split last round of GEMM2 may use (one 256 x 256 fp32 tile per CU, for up
+// to 256 CUs)
+constexpr size_t kSplitWsBytes = static_cast<size_t>(256) * 256 * 256 * sizeof(float);
 
 // variant: 1 prefill, 2 decode
 hipError_t launch_gemm1(const GemmArgs& g, bool bf16, int variant, hipStream_t s);

@@ -182,6 +182,13 @@ size_t forward_ws(int T, int H, int I, int k, moe_dtype dt) {
   return round_up(R * I * esize(dt)) + round_up(R * H * sizeof(float));
 }
 
+// the forward workspace with room for GEMM2's split last round when the layer's automatic
+// variant is prefill with bf16 weights (the GEMM runs unsplit in a smaller workspace)
+size_t forward_ws_full(int T, int H, int I, int E, int k, moe_dtype dt) {
+  const bool split = dt == MOE_BF16 && auto_variant(T, H, I, E, k, dt) == MOE_VARIANT_PREFILL;
+  return forward_ws(T, H, I, k, dt) + (split ? moe::kSplitWsBytes : 0);
+}
+
 }  // namespace
 
 extern "C" {
@@ -424,9 +431,8 @@ moe_status moe_combine(const float* y, int T, int H, int k, moe_dtype dt, void* 
 }
 
 size_t moe_forward_workspace_size(int T, int H, int I, int E, int k, moe_dtype dt) {
-  (void)E;
-  if (T <= 0 || H <= 0 || I <= 0 || k < 1 || !valid_expert_dt(dt)) return 0;
-  return forward_ws(T, H, I, k, dt);
+  if (T <= 0 || H <= 0 || I <= 0 || E <= 0 || k < 1 || !valid_expert_dt(dt)) return 0;
+  return forward_ws_full(T, H, I, E, k, dt);
 }
 
 }  // extern "C"
@@ -463,6 +469,10 @@ moe_status forward_impl(const void* x, const void* w13, const float* w13_scale, 
   if (e != hipSuccess) return hip_status(e, "gemm1");
   moe::GemmArgs g2 = gemm_args(a, w2, w2_scale, y, topk_w, sorted_ids, expert_ids,
                                num_tokens_post_padded, T, H, I, E, k, block_m);
+  if (dt == MOE_BF16 && v == MOE_VARIANT_PREFILL && ws_bytes >= need + moe::kSplitWsBytes) {
+    g2.split_ws = reinterpret_cast<float*>(base + need);
+    g2.split_ws_bytes = moe::kSplitWsBytes;
+  }
   e = moe::launch_gemm2(g2, bf, v, s);
   if (e != hipSuccess) return hip_status(e, "gemm2");
   return hip_status(moe::launch_combine(y, T, H, k, bf, out, s), "combine");
@@ -523,7 +533,7 @@ LayerPlan plan_layer(int T, int H, int I, int E, int k, moe_dtype dt, int shared
   p.off_ntpp = off; off += round_up(sizeof(int32_t));
   p.off_counts = off; off += round_up(static_cast<size_t>(ES) * sizeof(int32_t));
   p.off_align = off; off += round_up(moe::align_ws_bytes(static_cast<int>(R), ES));
-  p.off_fwd = off; off += forward_ws(T, H, I, KS, dt);
+  p.off_fwd = off; off += forward_ws_full(T, H, I, ES, KS, dt);
   p.total = off;
   return p;
 }
@@ -590,7 +600,8 @@ moe_status layer_impl(const void* x, const void* wg, const void* w13, const floa
     if (e != hipSuccess) return hip_status(e, "align");
   }
   return forward_impl(x, w13, w13_scale, w2, w2_scale, tw, sorted, eids, ntpp, T, H, I, ES, KS,
-                      p.bm, dt, MOE_VARIANT_AUTO, out, b + p.off_fwd, forward_ws(T, H, I, KS, dt),
+                      p.bm, dt, MOE_VARIANT_AUTO, out, b + p.off_fwd,
+                      forward_ws_full(T, H, I, ES, KS, dt),
                       stream);
 }
 

@@ -183,9 +183,13 @@ def _forward_case(lib, x, wg, w13, w2, k, mode, bm, variant, offset=None, bias=N
     if check_rows:
         assert not torch.isnan(a[:R]).any() and not torch.isnan(y[:R]).any()
         assert torch.isnan(a[R:]).all() and torch.isnan(y[R:]).all()     # nothing past row R
-    # moe_forward is deterministic and runs the same kernels as the single calls
+    # moe_forward is deterministic.  It runs the same kernels as the single calls, except
+    # that with bf16 weights at prefill its workspace lets GEMM2 split the last round of
+    # tiles in K (the fp32 sums are then added in another order); that result is checked
+    # against the oracle below like the other
     assert torch.equal(out_fwd, out_fwd2)
-    assert torch.equal(out, out_fwd)
+    if not (dt_bf16 and variant in (0, 1)):
+        assert torch.equal(out, out_fwd)
     for o in (out, out_fwd):
         got = np64(o)
         if dt_bf16:
