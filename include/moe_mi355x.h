@@ -211,7 +211,7 @@ moe_status moe_combine(const float* y, int T, int H, int k, moe_dtype dt, void* 
                        void* stream);
 
 /* GEMM1+SwiGLU, GEMM2 x weight and combine.  ws: moe_forward_workspace_size bytes
- * (holds a and y; when the automatic variant is prefill with bf16 weights, also 64 MiB of
+ * (holds a and y; when the automatic variant is prefill, also 64 MiB of
  * partial sums for GEMM2's split last round of tiles).  A workspace that holds a and y
  * but not the partial sums is accepted: GEMM2 then runs its tiles unsplit. */
 size_t moe_forward_workspace_size(int T, int H, int I, int E, int k, moe_dtype dt);

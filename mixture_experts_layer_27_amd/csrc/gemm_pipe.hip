@@ -45,7 +45,7 @@ struct PArgs {
   int block_m;
   int mtiles, nblocks;
   int n_outer;             // raster order of the tile groups (see grouped_slot)
-  // GEMM2, bf16 weights: split of the last partial round (see split_plan); 1 = off
+  // GEMM2: split of the last partial round (see split_plan); 1 = off
   int split_max;
   int ncu;                 // compute units: one round = ncu tiles (one work-group per CU)
   float* partial;          // [ncu][BM][BN] fp32 partial sums of the split tiles
@@ -148,7 +148,7 @@ __device__ __forceinline__ bool grouped_slot(int bid, int mtiles, int nblocks, b
 }
 constexpr int kGroupM = 4, kGroupN = 8;
 
-// GEMM2 (bf16 weights): balanced rounds with a split last round.  GEMM2's tiles are few
+// GEMM2: balanced rounds with a split last round.  GEMM2's tiles are few
 // and long (K = I), so the rounds of ncu tiles (one work-group per CU) quantise: at the
 // Mixtral-8x7B shape 592 tiles make 2.3 rounds but take 3, with the grouped raster above
 // dealing 96 tiles to some XCDs and 64 to others.  Here the real tile count N (from the
@@ -159,7 +159,7 @@ constexpr int kGroupM = 4, kGroupN = 8;
 // order; tiles are ordered in strips of 8 n-blocks with the m-tiles inside, so the 32
 // tiles an XCD runs at once are 4 m-tiles x 8 n-blocks, as with the grouped raster.  Split
 // parts write raw fp32 sums to `partial`; a fix-up launch adds them in part order and
-// applies the router weight.  When the plan splits nothing (rem = 0, or too many tiles
+// applies the row scale (FP8 weights) and the router weight.  When the plan splits nothing (rem = 0, or too many tiles
 // left over for a short round) the grouped raster above is kept.
 struct SplitPlan {
   int mreal, full, rem, parts;
@@ -576,7 +576,8 @@ gemm2_split_fixup_kernel(PArgs p) {
   const int col = nb * BN + c;
   if (r >= p.R || col >= p.N) return;                // N % 4 == 0: the 4 columns are in
   float* out = static_cast<float*>(p.C) + static_cast<int64_t>(r) * p.N + col;
-  if (p.expert_ids[(mt * BM) / p.block_m] < 0) {
+  const int e = p.expert_ids[(mt * BM) / p.block_m];
+  if (e < 0) {
     *reinterpret_cast<float4*>(out) = make_float4(0.f, 0.f, 0.f, 0.f);
     return;
   }
@@ -585,6 +586,10 @@ gemm2_split_fixup_kernel(PArgs p) {
   for (int q = 1; q < sp.parts; ++q) {
     const float4 b = *reinterpret_cast<const float4*>(src + static_cast<int64_t>(q) * BM * BN);
     a.x += b.x; a.y += b.y; a.z += b.z; a.w += b.w;
+  }
+  if (p.B_scale) {   // FP8 weights: the row scale of each output column, as the epilogue
+    const float4 sc = *reinterpret_cast<const float4*>(p.B_scale + static_cast<int64_t>(e) * p.N + col);
+    a.x *= sc.x; a.y *= sc.y; a.z *= sc.z; a.w *= sc.w;
   }
   const float wr = p.topk_w[r];
   *reinterpret_cast<float4*>(out) = make_float4(wr * a.x, wr * a.y, wr * a.z, wr * a.w);
@@ -631,7 +636,7 @@ hipError_t run_pipe(const GemmArgs& g, hipStream_t s) {
   int64_t G = (groups + 7) / 8 * 8 * kGroupM * kGroupN;
   if (G == 0) return hipSuccess;
   p.split_max = 1;
-  if (MODE == 2 && WB == 2 && g.split_ws) {
+  if (MODE == 2 && g.split_ws) {
     const int ncu = device_cu_count();
     if (ncu > 0 && g.split_ws_bytes >= static_cast<size_t>(ncu) * BM * BN * sizeof(float)) {
       p.split_max = 4;

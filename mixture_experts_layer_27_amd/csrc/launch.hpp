@@ -52,7 +52,7 @@ struct GemmArgs {
   const int32_t* ntpp;
   int T, H, I, E, k, block_m;
   int64_t cap;               // capacity of sorted_ids
-  // GEMM2 prefill, bf16 weights: room for the partial sums of a split last round of
+  // GEMM2 prefill: room for the partial sums of a split last round of
   // tiles (used when it holds one [256 x 256] fp32 tile per compute unit; else unsplit)
   float* split_ws = nullptr;
   size_t split_ws_bytes = 0;

@@ -183,9 +183,9 @@ size_t forward_ws(int T, int H, int I, int k, moe_dtype dt) {
 }
 
 // the forward workspace with room for GEMM2's split last round when the layer's automatic
-// variant is prefill with bf16 weights (the GEMM runs unsplit in a smaller workspace)
+// variant is prefill (the GEMM runs unsplit in a smaller workspace)
 size_t forward_ws_full(int T, int H, int I, int E, int k, moe_dtype dt) {
-  const bool split = dt == MOE_BF16 && auto_variant(T, H, I, E, k, dt) == MOE_VARIANT_PREFILL;
+  const bool split = bf16_acts(dt) && auto_variant(T, H, I, E, k, dt) == MOE_VARIANT_PREFILL;
   return forward_ws(T, H, I, k, dt) + (split ? moe::kSplitWsBytes : 0);
 }
 
@@ -469,7 +469,7 @@ moe_status forward_impl(const void* x, const void* w13, const float* w13_scale, 
   if (e != hipSuccess) return hip_status(e, "gemm1");
   moe::GemmArgs g2 = gemm_args(a, w2, w2_scale, y, topk_w, sorted_ids, expert_ids,
                                num_tokens_post_padded, T, H, I, E, k, block_m);
-  if (dt == MOE_BF16 && v == MOE_VARIANT_PREFILL && ws_bytes >= need + moe::kSplitWsBytes) {
+  if (bf && v == MOE_VARIANT_PREFILL && ws_bytes >= need + moe::kSplitWsBytes) {
     g2.split_ws = reinterpret_cast<float*>(base + need);
     g2.split_ws_bytes = moe::kSplitWsBytes;
   }

@@ -184,7 +184,7 @@ def _forward_case(lib, x, wg, w13, w2, k, mode, bm, variant, offset=None, bias=N
         assert not torch.isnan(a[:R]).any() and not torch.isnan(y[:R]).any()
         assert torch.isnan(a[R:]).all() and torch.isnan(y[R:]).all()     # nothing past row R
     # moe_forward is deterministic.  It runs the same kernels as the single calls, except
-    # that with bf16 weights at prefill its workspace lets GEMM2 split the last round of
+    # that at prefill its workspace lets GEMM2 split the last round of
     # tiles in K (the fp32 sums are then added in another order); that result is checked
     # against the oracle below like the other
     assert torch.equal(out_fwd, out_fwd2)
@@ -301,7 +301,9 @@ def _forward_fp8_case(lib, T, H, I, E, k, mode, bm, seed, offset=None, variant=0
     _sync()
     assert not torch.isnan(a[:R]).any() and not torch.isnan(y[:R]).any()
     assert torch.isnan(a[R:]).all() and torch.isnan(y[R:]).all()
-    assert torch.equal(out, out_fwd)
+    # moe_forward_fp8 may split GEMM2's last round at prefill (see the bf16 case)
+    if variant not in (0, 1):
+        assert torch.equal(out, out_fwd)
     got = np64(out)
     r = bf16_tol_check(got, ref)
     assert np.mean(np.abs(got - ref)) / np.sqrt(np.mean(ref ** 2)) < 2e-3
