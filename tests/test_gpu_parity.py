@@ -405,6 +405,18 @@ def test_layer_small_batch_repeated(lib, name, T):
         _layer_vs_oracle(lib, wl, lay)
 
 
+@pytest.mark.parametrize("name", ["qwen3_balanced", "qwen3_balanced_fp8"])
+def test_layer_prefill_split_round(lib, name):
+    """Prefill with more tiles than compute units and a short last round: 384 GEMM2 tiles of
+    128 x 256 on a 256-CU part are one round of whole tiles (contiguous per-XCD ranges) and
+    128 tiles split in two K ranges, against the oracle."""
+    wl = S.WORKLOADS["qwen3_balanced"].scaled(T=512, H=768, I=128)
+    if name.endswith("fp8"):
+        wl = wl.scaled(dtype="bf16_fp8w")
+    lay = S.make_layer(wl, device=DEV, seed=5)
+    _layer_vs_oracle(lib, wl, lay)
+
+
 @pytest.mark.parametrize("name,T,scale", [("deepseek_decode_fp8", 1, 4),
                                           ("deepseek_decode_fp8", 8, 4),
                                           ("deepseek_decode_fp8", 64, 4),
@@ -426,11 +438,12 @@ def test_layer_widest_routing(lib, T):
     _layer_vs_oracle(lib, wl, lay)
 
 
-@pytest.mark.parametrize("T,H", [(96, 256), (8, 1024)])
+@pytest.mark.parametrize("T,H", [(96, 256), (8, 1024), (512, 1024)])
 def test_layer_hip_graph_replays(lib, T, H):
     """The whole layer captured once in a HIP graph; replays with new activations (so the
     routing changes) match eager runs.  T=8 takes the small-batch launches (router K
-    slabs, one-launch route + align)."""
+    slabs, one-launch route + align); T=512 the prefill tiles, with GEMM2's last round of
+    tiles split in K (partial sums in the workspace, fix-up launch)."""
     wl = S.WORKLOADS["qwen3_skewed"].scaled(T=T, H=H, I=128)
     lay = S.make_layer(wl, device=DEV, seed=5)
     cfg = lib_cfg(lib, wl, lay)
