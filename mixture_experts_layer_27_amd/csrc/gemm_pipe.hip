@@ -192,8 +192,10 @@ __device__ __forceinline__ void strip_tile(int q, int mreal, int nblocks, int& m
   }
 }
 
+// 32-element stages leave room for two work-groups per CU: their register budget is held
+// to two waves per SIMD
 template <int MODE, int BM, int BN, int WM, int WN, int BK, int NSTAGE, int PFD, int WB>
-__global__ void __launch_bounds__(WM * WN * 64)
+__global__ void __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(BK == 32 ? 2 : 1)))
 moe_gemm_pipe_kernel(PArgs p) {
   using C = PCfg<MODE, BM, BN, WM, WN, BK, NSTAGE, WB>;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[NSTAGE * C::STAGE];
@@ -666,7 +668,7 @@ hipError_t launch_pipe_gemm1(const GemmArgs& g, int tile_m, hipStream_t s) {
     return hipErrorInvalidValue;
   }
   if (tile_m == 256) return run_pipe<1, 256, 256, 2, 2, 64, 2, 0>(g, s);
-  if (tile_m == 128) return run_pipe<1, 128, 256, 2, 2, 64, 3, 0>(g, s);
+  if (tile_m == 128) return run_pipe<1, 128, 256, 2, 2, 32, 3, 0>(g, s);
   return hipErrorInvalidValue;
 }
 
@@ -677,7 +679,7 @@ hipError_t launch_pipe_gemm2(const GemmArgs& g, int tile_m, hipStream_t s) {
     return hipErrorInvalidValue;
   }
   if (tile_m == 256) return run_pipe<2, 256, 256, 2, 2, 64, 2, 2>(g, s);
-  if (tile_m == 128) return run_pipe<2, 128, 256, 2, 2, 64, 3, 0>(g, s);
+  if (tile_m == 128) return run_pipe<2, 128, 256, 2, 2, 32, 3, 0>(g, s);
   return hipErrorInvalidValue;
 }
 
