@@ -47,7 +47,7 @@ struct PArgs {
   int n_outer;             // raster order of the tile groups (see grouped_slot)
   // GEMM2: split of the last partial round (see split_plan); 1 = off
   int split_max;
-  int ncu;                 // compute units: one round = ncu tiles (one work-group per CU)
+  int ncu;                 // work-groups in flight: one round = ncu tiles (CUs x work-groups per CU)
   float* partial;          // [ncu][BM][BN] fp32 partial sums of the split tiles
 };
 
@@ -149,7 +149,7 @@ __device__ __forceinline__ bool grouped_slot(int bid, int mtiles, int nblocks, b
 constexpr int kGroupM = 4, kGroupN = 8;
 
 // GEMM2: balanced rounds with a split last round.  GEMM2's tiles are few
-// and long (K = I), so the rounds of ncu tiles (one work-group per CU) quantise: at the
+// and long (K = I), so the rounds of ncu tiles (the work-groups in flight) quantise: at the
 // Mixtral-8x7B shape 592 tiles make 2.3 rounds but take 3, with the grouped raster above
 // dealing 96 tiles to some XCDs and 64 to others.  Here the real tile count N (from the
 // padded total on the device) is split into N - rem whole tiles, rem = N mod ncu, and the
@@ -639,7 +639,8 @@ hipError_t run_pipe(const GemmArgs& g, hipStream_t s) {
   if (G == 0) return hipSuccess;
   p.split_max = 1;
   if (MODE == 2 && g.split_ws) {
-    const int ncu = device_cu_count();
+    // 32-element stages run two work-groups per CU (see the kernel's register budget)
+    const int ncu = device_cu_count() * (BK == 32 ? 2 : 1);
     if (ncu > 0 && g.split_ws_bytes >= static_cast<size_t>(ncu) * BM * BN * sizeof(float)) {
       p.split_max = 4;
       p.ncu = ncu;
