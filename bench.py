@@ -367,6 +367,16 @@ def main():
         roof = {"bound": "hbm", "achieved": g1_bytes / (g1_ms * 1e-3) / 1e9, "peak": PEAK_HBM_GBS,
                 "unit": "GB/s", "traffic": measured_traffic(traffic_key)}
     else:
+        if emap is not None:
+            # expert parallelism: only the routed rows of this GPU's experts are computed;
+            # count them for each timed step, outside the timed region
+            loc = []
+            for i in range(args.steps):
+                launch(i, cur_sp())
+                loc.append(int((emap[ids.reshape(-1).long()] >= 0).sum()))
+            r_local = sum(loc) / len(loc)
+            flops = 2 * r_local * 3 * H * I
+            g1_flops = 2 * r_local * 2 * I * H
         value, unit = flops / (ms * 1e-3) / 1e12, "TFLOPS"
         roof = {"bound": "mfma", "achieved": g1_flops / (g1_ms * 1e-3) / 1e12,
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
