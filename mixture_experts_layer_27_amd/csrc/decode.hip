@@ -282,15 +282,16 @@ __device__ __forceinline__ void zero_range(const DArgs& p, const int32_t* __rest
 // the vmcnt accounting of the DMA ring untouched.
 //
 // Latency outside the stream.  Every wave starts at once, so the memory round trips
-// before the first weight DMA and after the last MFMA are dead time for the whole GPU
-// (at one token they are a sizeable part of the launch).  The prologue therefore issues
-// every load that does not depend on another before the first wait: the padded total,
-// the owners of the table's whole capacity, and the routing ids and owner of the
-// sub-tile that the wave's first item has when every sub-tile is local.
-// CACHED (K / STEP >= P: the issue cursor is at most one item ahead of the compute): an
-// item's routing ids (and GEMM2's router weights) are kept from its setup for its
-// epilogue, and the next item's ids and owner are loaded one item ahead, so neither the
-// item boundaries of the DMA stream nor the epilogues wait on the routing tables.
+// before the first weight DMA and after the last MFMA are dead time for the whole GPU.
+// The prologue therefore issues every load that does not depend on another before the
+// first wait: the padded total, the owners of the table's whole capacity, and the routing
+// ids and owner of the sub-tile that the wave's first item has when every sub-tile is
+// local (one round trip to the first DMA instead of four; about 1 us of a one-token
+// step).  CACHED (K / STEP >= P: the issue cursor is at most one item ahead of the
+// compute): an item's routing ids (and GEMM2's router weights) are kept from its setup for
+// its epilogue, and the next item's ids and owner are loaded one item ahead, so the item
+// boundaries of the DMA stream and the epilogues do not wait on the routing tables (the
+// FP8 epilogue still loads its row scales).
 template <int MODE, int RB, int NTG, int STEP, int P, bool NT, int WB, bool CACHED>
 __global__ void __launch_bounds__(64)
 moe_decode_kernel(DArgs p, const int32_t* __restrict__ sorted_ids,

@@ -5,14 +5,18 @@
 // * Global -> LDS without registers: global_load_lds_dwordx4 writes each lane's 16 bytes
 //   at (wave base + 16 * lane), so the LDS swizzle is applied on the global side: lane i
 //   of an instruction fetches the logical chunk that belongs at physical slot i.
-// * NSTAGE-deep ring of BK=32 stages (64-byte LDS rows; chunk c of row m lives at
-//   c ^ sw4(m), conflict-free for both the 16-row DMA writes and the 32-row MFMA
-//   operand reads).  Stage kt+NSTAGE-1 is issued while stage kt is consumed; one
-//   barrier per stage, preceded by an explicit vmcnt wait for this wave's own loads.
-// * v_mfma_f32_32x32x16_bf16, 2 x 2 waves (one per SIMD), each holding a (BM/2) x (BN/2)
-//   fp32 accumulator tile (up to 128 x 128 = 256 AGPRs); LDS fragments are double-buffered
-//   in registers so the MFMAs of one k16 step overlap the LDS reads of the next; GEMM1 B tiles interleave 32-row gate and up blocks so that SwiGLU
-//   runs in registers.
+// * NSTAGE-deep ring of BK-element stages: BK = 64 (128-byte LDS rows, chunk c of row m
+//   at c ^ ((m >> 1) & 7)) for 256-row tiles, BK = 32 (64-byte rows, c ^ sw4(m)) for
+//   128-row tiles, whose 73 KB ring lets two work-groups share a CU; both swizzles are
+//   conflict-free for the DMA writes and the 32-row MFMA operand reads.  Stage
+//   kt+NSTAGE-1 is issued while stage kt is consumed; one barrier per stage, preceded by
+//   an explicit vmcnt wait for this wave's own loads.
+// * v_mfma_f32_32x32x16_bf16, WM x WN waves each holding a (BM/WM) x (BN/WN) fp32
+//   accumulator tile: 2 x 2 (one wave per SIMD, up to 128 x 128), or 2 x 4 for GEMM1's
+//   256-row tile (two waves per SIMD, 128 x 64 each); LDS fragments are double-buffered in
+//   registers so the MFMAs of one k16 step overlap the LDS reads of the next; GEMM1 B
+//   tiles interleave 32-row gate and up blocks so that SwiGLU runs in registers.
+// * GEMM2 splits a short last round of tiles in K over every CU (see split_plan).
 // * FP8 expert weights (OCP E4M3 bytes, one fp32 scale per weight row; section 8 of the
 //   same page prices an expert at one byte per weight): the B tile is staged as bytes
 //   (64-byte LDS rows per 64-element stage, half the bf16 tile, so the 256-row tile fits

@@ -10,10 +10,13 @@
 // through LDS.  At decode batch sizes the K range is further split over NZ work-groups
 // (slabs), each writing partial logits [NZ][T][E]; the top-k stage adds the slabs in
 // ascending slab order, so the result does not depend on scheduling.  This spreads
-// the Wg stream (3.7 MB for E=256, H=7168) over a few hundred work-groups.
+// the Wg stream (3.7 MB for E=256, H=7168) over a few hundred work-groups.  Larger
+// batches with more than 32 experts use 64 x 64 work-group tiles staged in LDS
+// (router_logits_tile_kernel).
 //
 // Top-k: one wave per token; lane l owns experts l, l+64, ...; each of the k
-// selections is a wave arg-max on (value desc, index asc).  For small batches a
+// selections is a wave arg-max on (value desc, index asc), taken as one maximum of
+// 64-bit keys.  For small batches a
 // single work-group routes every token and then builds the align table in the same
 // launch (the ids never leave LDS before the align step reads them).
 #include "align_dev.hpp"
