@@ -403,6 +403,12 @@ def main():
            "roofline": roof}
     if decode:
         rec["config"]["active_experts"] = n_act
+    if not decode and not staged:
+        # the per-stage GEMM2 call has no workspace and runs every tile whole; inside the
+        # layer step GEMM2 may split a short last round of tiles (partial sums + fix-up)
+        rec["config"]["stage_note"] = ("stages_ms.gemm2 is the standalone GEMM2 call (tiles "
+                                       "whole); the layer step's GEMM2 may split its last "
+                                       "round of tiles in K")
     if ep > 1:
         rec["config"]["expert_parallel"] = {"degree": ep, "local_experts": int(w13.shape[0]),
                                             "held": "experts e with e % degree == 0",
