@@ -26,7 +26,8 @@
  *   error nothing is enqueued, outputs are untouched, and moe_last_error()
  *   returns a thread-local message.  A failed kernel launch returns MOE_ERR_HIP.
  * - Not checked on the device (preconditions): topk_ids values lie in [0, E)
- *   and each token's k ids are distinct (both hold for ids from moe_route);
+ *   (moe_align skips, and counts nowhere, any that do not; see there) and each
+ *   token's k ids are distinct (both hold for ids from moe_route);
  *   sorted_ids / expert_ids / num_tokens_post_padded come from moe_align with the
  *   same T, k, E, block_m.
  * - Layouts (row-major, "nn.Linear" [out, in] weights, section 11 of the
@@ -130,7 +131,12 @@ moe_status moe_route_from_logits(const float* logits, int T, int E, int k,
  *                           cap/block_m).
  * Buffers are sized for the worst case cap = moe_align_capacity(T,k,E,block_m), so the
  * call is graph-capturable; the result is bit-exact and deterministic.
- * block_m: a power of two in [1, 256].  ws: moe_align_workspace_size(...) bytes. */
+ * block_m: a power of two in [1, 256].  ws: moe_align_workspace_size(...) bytes.
+ * Ids outside [0, E) (possible only for caller-supplied ids) are skipped on the device:
+ * such a row is counted for no expert and appears in no tile, the rest of the table is
+ * built as if it were absent, and no memory outside the buffers is touched; the host
+ * detects it afterwards as sum(expert_counts) < T*k (the expert GEMMs then leave that
+ * row of a/y unwritten, so its token's output is not defined). */
 int64_t moe_align_capacity(int T, int k, int E, int block_m);
 size_t moe_align_workspace_size(int T, int k, int E, int block_m);
 moe_status moe_align(const int32_t* topk_ids, int T, int k, int E, int block_m,

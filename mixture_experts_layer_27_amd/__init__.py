@@ -116,9 +116,20 @@ def moe_align_workspace_size(T: int, k: int, E: int, block_m: int) -> int:
     return lib.moe_align_workspace_size(T, k, E, block_m)
 
 
-def moe_align(topk_ids, E: int, block_m: int, out=None):
+def _reject_bad_ids(counts, T: int, k: int, strict: bool):
+    """The library skips ids outside [0, E) and counts them for no expert: with ``strict``
+    (outside HIP-graph capture) read the counts back and raise when rows are missing."""
+    if not strict or torch.cuda.is_current_stream_capturing():
+        return
+    got = int(counts.cpu().sum())
+    if got != T * k:
+        raise ValueError(f"moe_align: {T * k - got} topk_ids outside [0, E) were skipped")
+
+
+def moe_align(topk_ids, E: int, block_m: int, out=None, strict: bool = True):
     """-> (sorted_ids [cap], expert_ids [cap/block_m], num_tokens_post_padded [1],
-    expert_counts [E]), all int32 on the GPU.  ``out`` may supply those four buffers."""
+    expert_counts [E]), all int32 on the GPU.  ``out`` may supply those four buffers.
+    ``strict`` raises ValueError when some ids were outside [0, E) (it waits for the call)."""
     T, k = topk_ids.shape
     cap = lib.moe_align_capacity(T, k, E, block_m)
     dev = topk_ids.device
@@ -132,10 +143,11 @@ def moe_align(topk_ids, E: int, block_m: int, out=None):
     ws = _ws(lib.moe_align_workspace_size(T, k, E, block_m), dev)
     check(lib.moe_align(_p(topk_ids), T, k, E, block_m, _p(sorted_ids), _p(expert_ids), _p(ntpp),
                         _p(counts), _p(ws), ws.numel(), _stream()), "moe_align")
+    _reject_bad_ids(counts, T, k, strict)
     return sorted_ids, expert_ids, ntpp, counts
 
 
-def moe_align_ep(topk_ids, E: int, block_m: int, expert_map, out=None):
+def moe_align_ep(topk_ids, E: int, block_m: int, expert_map, out=None, strict: bool = True):
     """moe_align for one GPU of an expert-parallel layer: tiles carry expert_map[e] (the
     expert's local index, -1 when another GPU holds it).  Returns the same four tensors."""
     T, k = topk_ids.shape
@@ -154,6 +166,7 @@ def moe_align_ep(topk_ids, E: int, block_m: int, expert_map, out=None):
     check(lib.moe_align_ep(_p(topk_ids), T, k, E, block_m, _p(expert_map), _p(sorted_ids),
                            _p(expert_ids), _p(ntpp), _p(counts), _p(ws), ws.numel(), _stream()),
           "moe_align_ep")
+    _reject_bad_ids(counts, T, k, strict)
     return sorted_ids, expert_ids, ntpp, counts
 
 

@@ -49,7 +49,7 @@ align_hist_kernel(const int32_t* __restrict__ ids, int R, int E, int nseg, int64
   __builtin_amdgcn_wave_barrier();
   if (seg < nseg) {
     const int r0 = seg * kSegRows, r1 = min(R, r0 + kSegRows);
-    segment_histogram(ids, r0, r1, cnt[w]);
+    segment_histogram(ids, r0, r1, E, cnt[w]);
     __builtin_amdgcn_wave_barrier();
     for (int e = lane_id(); e < E; e += kWave) hist[static_cast<int64_t>(seg) * E + e] = cnt[w][e];
   }
@@ -133,7 +133,7 @@ align_scatter_kernel(const int32_t* __restrict__ ids, int R, int E, int nseg,
   for (int e = lane_id(); e < E; e += kWave) run[w][e] = hist[static_cast<int64_t>(seg) * E + e];
   __builtin_amdgcn_wave_barrier();
   const int r0 = seg * kSegRows, r1 = min(R, r0 + kSegRows);
-  segment_scatter(ids, r0, r1, run[w], sorted_ids);
+  segment_scatter(ids, r0, r1, E, run[w], sorted_ids);
 }
 
 }  // namespace

@@ -19,24 +19,31 @@ constexpr int kMaxE = 512;
 
 __device__ __forceinline__ int log2_pow2(int v) { return __builtin_ctz(static_cast<unsigned>(v)); }
 
-// Histogram of rows [r0, r1) into lds_cnt[0..E) (LDS atomics).
-__device__ inline void segment_histogram(const int32_t* __restrict__ ids, int r0, int r1,
+// Histogram of rows [r0, r1) into lds_cnt[0..E) (LDS atomics).  An id outside [0, E)
+// (possible only for ids the caller supplies) is skipped: it is counted nowhere, so the
+// table stays consistent for the other rows and the counts sum to less than the rows.
+__device__ inline void segment_histogram(const int32_t* __restrict__ ids, int r0, int r1, int E,
                                          int* __restrict__ lds_cnt) {
   const int lane = lane_id();
-  for (int r = r0 + lane; r < r1; r += kWave) atomicAdd(&lds_cnt[ids[r]], 1);
+  for (int r = r0 + lane; r < r1; r += kWave) {
+    const int e = ids[r];
+    if (static_cast<unsigned>(e) < static_cast<unsigned>(E)) atomicAdd(&lds_cnt[e], 1);
+  }
 }
 
 // Stable scatter of rows [r0, r1) by the calling wave; run[e] holds the next free
 // position of expert e for this segment (LDS, owned by this wave).  Rows of equal
-// expert inside a 64-row chunk are ranked with a ballot match loop.
-__device__ inline void segment_scatter(const int32_t* __restrict__ ids, int r0, int r1,
+// expert inside a 64-row chunk are ranked with a ballot match loop.  Rows whose id is
+// outside [0, E) are skipped, as in the histogram.
+__device__ inline void segment_scatter(const int32_t* __restrict__ ids, int r0, int r1, int E,
                                        int* __restrict__ run, int32_t* __restrict__ sorted_ids) {
   const int lane = lane_id();
   const uint64_t lt = lanemask_lt();
   for (int base = r0; base < r1; base += kWave) {
     const int r = base + lane;
-    const bool valid = r < r1;
-    const int e = valid ? ids[r] : -1;
+    const int id = r < r1 ? ids[r] : -1;
+    const bool valid = static_cast<unsigned>(id) < static_cast<unsigned>(E);
+    const int e = valid ? id : -1;
     uint64_t remaining = __ballot(valid);
     while (remaining) {
       const int leader = __ffsll(static_cast<unsigned long long>(remaining)) - 1;
@@ -111,7 +118,7 @@ __device__ inline void align_small_body(const int32_t* ids, int R, int E, int bm
   }
   for (int64_t p = threadIdx.x; p < cap; p += blockDim.x) sorted_ids[p] = R;
   __syncthreads();
-  segment_histogram(ids, r0, r1, hist[w]);
+  segment_histogram(ids, r0, r1, E, hist[w]);
   __syncthreads();
   for (int e = threadIdx.x; e < E; e += blockDim.x) {
     int s = 0;
@@ -137,7 +144,7 @@ __device__ inline void align_small_body(const int32_t* ids, int R, int E, int bm
   if (threadIdx.x == 0) *ntpp = total;
   fill_expert_ids(cnt, start, E, bm, total, cap, expert_ids, emap);
   __syncthreads();
-  segment_scatter(ids, r0, r1, hist[w], sorted_ids);
+  segment_scatter(ids, r0, r1, E, hist[w], sorted_ids);
 }
 
 }  // namespace alignd

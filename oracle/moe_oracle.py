@@ -196,30 +196,41 @@ def align_capacity(T, k, E, block_m) -> int:
     return (bound // block_m) * block_m
 
 
-def align_argsort(topk_ids, E, block_m, cap=None):
-    """Histogram, pad to block_m, exclusive scan, scatter; rows grouped by a stable sort.
+def align_runs(topk_ids, E, block_m, cap=None):
+    """The align table ([MKR] s5) built one expert run at a time.
+
+    Walking the experts in ascending order, expert e owns a run of ceil(n_e / block_m)
+    whole tiles that starts where the previous expert's run ended.  The run's first n_e
+    slots hold the flat rows routed to e in ascending row order (the stable order the
+    page calls a choice that makes the output deterministic); its remaining slots hold
+    the sentinel R = T*k, and each of its tiles records e in expert_ids.  Slots past the
+    last run (up to ``cap``) keep the sentinel and their tiles -1 (reading 5).
 
     Returns dict(sorted_ids, expert_ids, total, counts) with buffers of length ``cap``
     (default: the padded total) and cap // block_m.
     """
     flat = np.asarray(topk_ids, np.int64).reshape(-1)
-    R = flat.size
-    counts = np.bincount(flat, minlength=E)
-    padded = (counts + block_m - 1) // block_m * block_m
-    starts = np.cumsum(padded) - padded
-    total = int(padded.sum())
+    sentinel = flat.size
+    runs, owners, counts = [], [], np.zeros(E, np.int32)
+    for e in range(E):
+        mine = np.flatnonzero(flat == e)             # ascending flat rows of expert e
+        counts[e] = mine.size
+        if mine.size == 0:
+            continue                                 # an empty expert owns no tile
+        ntiles = -(-mine.size // block_m)
+        run = np.full(ntiles * block_m, sentinel, np.int64)
+        run[: mine.size] = mine
+        runs.append(run)
+        owners.extend([e] * ntiles)
+    table = np.concatenate(runs) if runs else np.zeros(0, np.int64)
+    total = int(table.size)
     if cap is None:
         cap = total
-    sorted_ids = np.full(cap, R, np.int32)
-    order = np.argsort(flat, kind="stable")
-    first_of = np.cumsum(counts) - counts                 # unpadded run start per expert
-    rank = np.arange(R) - first_of[flat[order]]
-    sorted_ids[starts[flat[order]] + rank] = order
+    sorted_ids = np.full(cap, sentinel, np.int32)
+    sorted_ids[:total] = table
     expert_ids = np.full(cap // block_m, -1, np.int32)
-    tiles = np.repeat(np.arange(E, dtype=np.int32), padded // block_m)
-    expert_ids[: tiles.size] = tiles
-    return dict(sorted_ids=sorted_ids, expert_ids=expert_ids, total=total,
-                counts=counts.astype(np.int32))
+    expert_ids[: len(owners)] = owners
+    return dict(sorted_ids=sorted_ids, expert_ids=expert_ids, total=total, counts=counts)
 
 
 def align_counting(topk_ids, E, block_m, cap=None):
@@ -297,6 +308,41 @@ def moe_loop(x, w13, w2, ids, w, round_a=False, return_rows=False):
     return (out, y) if return_rows else out
 
 
+def swiglu_rows(x, w13, ids):
+    """GEMM1 + SwiGLU of every routed row ([MKR] s6: flat row r = t*k + j gathers token
+    r // k and multiplies it by W13[e] = [W1[e]; W3[e]] of its expert e = ids[t, j]):
+    a[r] = silu(x[t] W1[e]^T) * (x[t] W3[e]^T), float64, not rounded.  Slots whose id is
+    outside [0, E) (an expert this call does not hold) are left zero."""
+    x = np.asarray(x, np.float64)
+    W1, W3 = _split_w13(w13)
+    ids = np.asarray(ids)
+    T, k = ids.shape
+    a = np.zeros((T * k, W1.shape[1]))
+    for e in range(W1.shape[0]):
+        tt, jj = np.nonzero(ids == e)               # the slots routed to expert e
+        if tt.size:
+            xe = x[tt]
+            a[tt * k + jj] = silu(xe @ W1[e].T) * (xe @ W3[e].T)
+    return a
+
+
+def down_and_combine(a, w2, ids, w):
+    """GEMM2 x router weight and the combine ([MKR] s6) from given activations a [T*k, I]:
+    out[t] = sum_j w[t, j] * (a[t*k + j] W2[e]^T), e = ids[t, j], float64.  Slots whose id
+    is outside [0, E) add nothing."""
+    a = np.asarray(a, np.float64)
+    w2 = np.asarray(w2, np.float64)
+    ids = np.asarray(ids)
+    wv = np.asarray(w, np.float64)
+    T, k = ids.shape
+    out = np.zeros((T, w2.shape[1]))
+    for e in range(w2.shape[0]):
+        tt, jj = np.nonzero(ids == e)                # one slot per token: ids of a token differ
+        if tt.size:
+            out[tt] += wv[tt, jj, None] * (a[tt * k + jj] @ w2[e].T)
+    return out
+
+
 def moe_dense(x, w13, w2, ids, w, round_a=False):
     """Dense version ([MKR] s3 ``moe_dense``): run every expert on every token, then
     weight by a [T, E] gate matrix holding the k routed weights per token."""
@@ -322,34 +368,47 @@ def moe_dense(x, w13, w2, ids, w, round_a=False):
 
 def moe_permute_grouped(x, w13, w2, ids, w, round_a=False):
     """Third implementation ([MKR] s2 'permute, then grouped GEMM'; s10 'three
-    implementations'): physically reorder the routed rows so each expert's rows are
-    contiguous (stable order by expert), run one GEMM per contiguous segment given by
-    the per-expert offsets, scale by the router weight, then un-permute by adding each
-    row into its token's output.  Shares no indexing code with ``moe_loop``."""
+    implementations'), written as matrix algebra.
+
+    The routed (token, slot) pairs are listed expert by expert (ascending expert, and
+    within an expert ascending token, then slot), so each expert's pairs form one
+    contiguous segment of the list.  The permutation is a 0/1 gather matrix P [R, T]
+    whose row i selects the token of pair i, so P @ x is the permuted activation copy;
+    each segment goes through its expert's SwiGLU FFN as one dense GEMM chain; the
+    un-permute and the weighted combine are a single matrix Q [T, R] with Q[t, i] =
+    (router weight of pair i) when pair i belongs to token t, so out = Q @ Y.
+    Shares no indexing code with ``moe_loop`` (no flat row numbers, no slot-order sum).
+    """
     x = np.asarray(x, np.float64)
     w2 = np.asarray(w2, np.float64)
     W1, W3 = _split_w13(w13)
     T, H = x.shape
+    E = W1.shape[0]
     ids = np.asarray(ids)
-    k = ids.shape[1]
-    flat = ids.reshape(-1)
-    order = np.argsort(flat, kind="stable")               # routed rows grouped by expert
-    xs = x[order // k]                                    # the permuted copy
-    ends = np.cumsum(np.bincount(flat, minlength=W1.shape[0]))
-    ys = np.zeros((flat.size, H))
-    start = 0
-    for e, end in enumerate(ends):
-        if end > start:
-            seg = xs[start:end]
-            h = silu(seg @ W1[e].T) * (seg @ W3[e].T)
+    wv = np.asarray(w, np.float64)
+    pairs, seg_len = [], []
+    for e in range(E):
+        mine = [(t, j) for t in range(T) for j in range(ids.shape[1]) if ids[t, j] == e]
+        pairs.extend(mine)
+        seg_len.append(len(mine))
+    R = len(pairs)
+    P = np.zeros((R, T))
+    Q = np.zeros((T, R))
+    for i, (t, j) in enumerate(pairs):
+        P[i, t] = 1.0
+        Q[t, i] = wv[t, j]
+    xp = P @ x                                        # permuted activations
+    Y = np.zeros((R, H))
+    lo = 0
+    for e, n in enumerate(seg_len):                   # grouped GEMM: one segment per expert
+        if n:
+            seg = xp[lo:lo + n]
+            a = silu(seg @ W1[e].T) * (seg @ W3[e].T)
             if round_a:
-                h = bf16_round(h)
-            ys[start:end] = h @ w2[e].T
-        start = end
-    ys *= np.asarray(w, np.float64).reshape(-1)[order, None]
-    out = np.zeros((T, H))
-    np.add.at(out, order // k, ys)                        # un-permute + combine
-    return out
+                a = bf16_round(a)
+            Y[lo:lo + n] = a @ w2[e].T
+        lo += n
+    return Q @ Y                                      # un-permute and combine
 
 
 def moe_bruteforce(x, w13, w2, ids, w, round_a=False):
@@ -403,9 +462,9 @@ def moe_layer_fp8(x, wg, w13_codes, w13_scale, w2_codes, w2_scale, k, mode, offs
 def align_ep(topk_ids, E, block_m, expert_map, cap=None):
     """The align table of one GPU under expert parallelism ([MKR] s11 exercise: experts
     not on this GPU get expert_ids = -1, and the GEMMs skip those tiles).  The table of
-    all E experts (same sorted_ids, total and counts as ``align_argsort``) with each
+    all E experts (same sorted_ids, total and counts as ``align_runs``) with each
     tile's owner e replaced by expert_map[e]: its index among this GPU's experts, or -1."""
-    r = align_argsort(topk_ids, E, block_m, cap)
+    r = align_runs(topk_ids, E, block_m, cap)
     emap = np.asarray(expert_map, np.int64)
     eids = r["expert_ids"].astype(np.int64)
     owned = eids >= 0
@@ -477,35 +536,70 @@ def expert_flops(T, k, H, I) -> int:
 
 # --------------------------------------------------------------------------- routing margins
 
-def selection_margin(logits32, k, mode, offset=None, bias=None, n_group=0, topk_group=0):
-    """Per token, the smallest gap between a selected score and the best unselected one
-    (and, for the grouped router, between the last kept and first dropped group score),
-    measured on the float32 selection scores.  A token whose margin is below the error
-    bound of its logits may be routed either way by a correct implementation."""
+def selection_scores(logits32, mode, offset=None, bias=None) -> np.ndarray:
+    """The float32 scores the router compares (float64 copy): logits (+ offset) for the
+    softmax rules, sigmoid(logit) + bias for the grouped sigmoid rule ([MKR] s4)."""
     l = f32(logits32)
-    T, E = l.shape
     if offset is not None:
         l = (l + f32(offset)[None, :]).astype(np.float32)
     if mode == SIGMOID_BIAS_GROUPED:
-        s = sigmoid_f32(l)
-        b = np.zeros(E, np.float32) if bias is None else f32(bias)
-        sc = (s + b[None, :]).astype(np.float32).astype(np.float64)
-    else:
-        sc = l.astype(np.float64)
-    m = np.full(T, np.inf)
+        b = np.zeros(l.shape[1], np.float32) if bias is None else f32(bias)
+        return (sigmoid_f32(l) + b[None, :]).astype(np.float32).astype(np.float64)
+    return l.astype(np.float64)
+
+
+def selection_margin(logits32, k, mode, offset=None, bias=None, n_group=0, topk_group=0):
+    """Per token, a radius rho in selection-score units: every perturbation of the scores
+    that moves no score by rho or more leaves the SET of selected experts unchanged (slot
+    order may still swap between near-equal selected experts).  A token whose scores are
+    known only to within rho may be routed either way by a correct implementation.
+
+    Derivation (scores c; S = selected set, c_k = its smallest score):
+    * plain top-k (the softmax rules, or the sigmoid rule without group limit): S changes
+      only if a selected and an unselected score cross, each moving at most rho, so
+      rho = (c_k - best unselected) / 2;
+    * group-limited top-k ([MKR] s4): a group score is the sum of the group's two largest
+      scores, so it moves by at most 2 rho.  Within the kept groups' candidates the
+      k-th / (k+1)-th gap gives (gap) / 2 as above.  A kept group A can be displaced by a
+      dropped group B only when G_A - G_B < 4 rho; that changes S if A holds a selected
+      expert, and otherwise only if an expert of B then beats c_k, which needs
+      (c_k - max c_B) < 2 rho.  So each (A, B) pair bounds rho by (G_A - G_B) / 4, or by
+      the larger of that and (c_k - max c_B) / 2 when A holds no selected expert.
+    rho is the minimum over these events: a sound lower bound of the true radius (exact
+    when groups have two experts, where each event's perturbation is attained, up to the
+    float32 rounding of the group sums, which the group events subtract)."""
+    sc = selection_scores(logits32, mode, offset, bias)
+    T, E = sc.shape
+    rho = np.full(T, np.inf)
+    grouped = mode == SIGMOID_BIAS_GROUPED and n_group and topk_group and topk_group < n_group
     for t in range(T):
-        o = order_first(sc[t])
-        if k < E:
-            m[t] = sc[t, o[k - 1]] - sc[t, o[k]]
-        if mode == SIGMOID_BIAS_GROUPED and n_group and topk_group and topk_group < n_group:
-            gsz = E // n_group
-            g = np.array([np.sort(sc[t, i * gsz:(i + 1) * gsz])[-2:].sum() for i in range(n_group)])
-            go = np.sort(g)[::-1]
-            m[t] = min(m[t], go[topk_group - 1] - go[topk_group])
-            # within the kept groups, the k-th vs (k+1)-th candidate
-            kept = order_first(g.astype(np.float64))[:topk_group]
-            cand = np.concatenate([np.arange(i * gsz, (i + 1) * gsz) for i in kept])
-            oc = order_first(sc[t], cand)
-            if len(oc) > k:
-                m[t] = min(m[t], sc[t, oc[k - 1]] - sc[t, oc[k]])
-    return m
+        c = sc[t]
+        if not grouped:
+            o = order_first(c)
+            if k < E:
+                rho[t] = (c[o[k - 1]] - c[o[k]]) / 2
+            continue
+        gsz = E // n_group
+        members = [np.arange(g * gsz, (g + 1) * gsz) for g in range(n_group)]
+        # group scores as the router forms them (a float32 sum of the two largest)
+        G = np.array([np.float32(np.sort(c[m])[-1]) + np.float32(np.sort(c[m])[-2])
+                      for m in members], np.float32)
+        kept = order_first(G)[:topk_group]
+        dropped = [g for g in range(n_group) if g not in set(kept.tolist())]
+        cand = np.concatenate([members[g] for g in kept])
+        oc = order_first(c, cand)
+        sel = set(oc[:k].tolist())
+        ck = c[oc[k - 1]]
+        r = (ck - c[oc[k]]) / 2 if oc.size > k else np.inf
+        for A in kept:
+            holds = any(e in sel for e in members[A].tolist())
+            for B in dropped:
+                # the float32 rounding of each perturbed group sum may add half an
+                # ulp on either side of the pair
+                ulp = float(np.spacing(np.float32(max(abs(G[A]), abs(G[B])))))
+                eps = (float(G[A]) - float(G[B]) - 2 * ulp) / 4
+                if not holds:
+                    eps = max(eps, (ck - c[members[B]].max()) / 2)
+                r = min(r, eps)
+        rho[t] = max(r, 0.0)
+    return rho

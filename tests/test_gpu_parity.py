@@ -10,7 +10,9 @@ import torch
 from oracle import moe_oracle as O
 from synth import inputs as S
 from tests.gpu_util import (bf16_layer, bf16_tol_check, expert_weights64, f32_tol_check,
-                            lib_cfg, logit_error_bound, np64, route_kwargs, run_layer)
+                            layer_check, layer_reference, lib_cfg, logit_error_bound, np64,
+                            routing_vs_oracle, run_layer, same_set, score_error_bound,
+                            swiglu_flip_check)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -28,7 +30,7 @@ def _align_case(lib, ids_np, E, bm):
     sorted_ids, expert_ids, ntpp, counts = lib.moe_align(ids, E, bm)
     _sync()
     cap = O.align_capacity(T, k, E, bm)
-    ref = O.align_argsort(ids_np, E, bm, cap)
+    ref = O.align_runs(ids_np, E, bm, cap)
     assert sorted_ids.numel() == cap
     assert int(ntpp.item()) == ref["total"]
     assert np.array_equal(counts.cpu().numpy(), ref["counts"])
@@ -65,6 +67,31 @@ def test_align_edge_counts(lib, bm):
     hot = S.random_topk_ids(3000, 4, 16, seed=2, hot=5).numpy()     # one expert gets every token
     _align_case(lib, hot, 16, bm)
     _align_case(lib, S.random_topk_ids(1, 1, 8, seed=0).numpy(), 8, bm)
+
+
+@pytest.mark.parametrize("T,k,E", [(50, 4, 16), (4097, 2, 8)])
+def test_align_skips_out_of_range_ids(lib, T, k, E):
+    """Caller-supplied ids outside [0, E) are skipped on the device (single work-group and
+    multi-launch paths): the table equals the oracle's for the valid rows alone, the counts
+    fall short of T*k, and the binding rejects the call unless told not to."""
+    ids = S.random_topk_ids(T, k, E, seed=T).numpy()
+    rng = np.random.default_rng(T)
+    bad = rng.choice(T * k, size=7, replace=False)
+    vals = np.array([-1, E, E + 100, 2 ** 31 - 1, -(2 ** 31), 3 * E, -7], np.int32)
+    ids.reshape(-1)[bad] = vals
+    d = torch.from_numpy(ids).to(DEV)
+    for bm in (16, 64):
+        sorted_ids, expert_ids, ntpp, counts = lib.moe_align(d, E, bm, strict=False)
+        _sync()
+        cap = O.align_capacity(T, k, E, bm)
+        ref = O.align_runs(ids, E, bm, cap)
+        assert int(counts.sum()) == T * k - bad.size
+        assert int(ntpp.item()) == ref["total"]
+        assert np.array_equal(counts.cpu().numpy(), ref["counts"])
+        assert np.array_equal(expert_ids.cpu().numpy(), ref["expert_ids"])
+        assert np.array_equal(sorted_ids.cpu().numpy(), ref["sorted_ids"])
+        with pytest.raises(ValueError):
+            lib.moe_align(d, E, bm)
 
 
 # ------------------------------------------------------------------------------ routing
@@ -143,14 +170,17 @@ def test_route_fused_logits(lib, T, H, E, k, mode):
     bn = None if bias is None else bias.numpy()
     rid, _ = O.route(ref.astype(np.float32), k, mode, None, bn, ng, tg, sc)
     margin = O.selection_margin(ref.astype(np.float32), k, mode, None, bn, ng, tg)
-    clear = margin > 2 * bound
+    clear = margin > score_error_bound(bound, mode, ref.astype(np.float32), None, bn)
     if T >= 16:
         assert clear.mean() > 0.5
-    assert np.array_equal(ids.cpu().numpy()[clear], rid[clear])
+    assert np.all(same_set(ids.cpu().numpy()[clear], rid[clear]))
     # weights move with the logits: |dw| <= w * (|dl_j| + |dl_0|) for the softmax rules
     _, rw = O.route(ref.astype(np.float32), k, mode, None, bn, ng, tg, sc)
     tol = 4 * bound[clear, None] * (sc if mode == 2 else 1.0) + 1e-6
-    assert np.all(np.abs(w.cpu().numpy()[clear] - rw[clear]) <= tol)
+    # compare weights slot by slot once both sides list the experts in the same order
+    gi = ids.cpu().numpy()[clear]
+    ordered = np.all(gi == rid[clear], axis=1)
+    assert np.all(np.abs(w.cpu().numpy()[clear][ordered] - rw[clear][ordered]) <= tol[ordered])
 
 
 # ------------------------------------------------------------------------------ expert GEMMs
@@ -190,10 +220,16 @@ def _forward_case(lib, x, wg, w13, w2, k, mode, bm, variant, offset=None, bias=N
     assert torch.equal(out_fwd, out_fwd2)
     if not (dt_bf16 and variant in (0, 1)):
         assert torch.equal(out, out_fwd)
+    kref = None
+    if dt_bf16:
+        # GEMM1's activations against the exact SwiGLU values, and the oracle's GEMM2 x
+        # weight + combine on the GPU's own activations for the kernel check
+        swiglu_flip_check(np64(a[:R]), O.swiglu_rows(x64, w13_64, ids), np.arange(R))
+        kref = O.down_and_combine(np64(a[:R]), w2_64, ids, w32.astype(np.float64))
     for o in (out, out_fwd):
         got = np64(o)
         if dt_bf16:
-            r = bf16_tol_check(got, ref)
+            r = bf16_tol_check(got, ref, kernel_ref=kref)
             # the GPU mirrors the oracle's rounding points: errors are ~ one bf16 ulp of out
             assert np.mean(np.abs(got - ref)) / np.sqrt(np.mean(ref ** 2)) < 2e-3
         else:
@@ -304,9 +340,14 @@ def _forward_fp8_case(lib, T, H, I, E, k, mode, bm, seed, offset=None, variant=0
     # moe_forward_fp8 may split GEMM2's last round at prefill (see the bf16 case)
     if variant not in (0, 1):
         assert torch.equal(out, out_fwd)
-    got = np64(out)
-    r = bf16_tol_check(got, ref)
-    assert np.mean(np.abs(got - ref)) / np.sqrt(np.mean(ref ** 2)) < 2e-3
+    w13_64 = O.dequant_rows(c13.numpy(), s13.numpy())
+    w2_64 = O.dequant_rows(c2.numpy(), s2.numpy())
+    swiglu_flip_check(np64(a[:R]), O.swiglu_rows(x64, w13_64, ids), np.arange(R))
+    kref = O.down_and_combine(np64(a[:R]), w2_64, ids, w32.astype(np.float64))
+    for o in (out, out_fwd):
+        got = np64(o)
+        r = bf16_tol_check(got, ref, kernel_ref=kref)
+        assert np.mean(np.abs(got - ref)) / np.sqrt(np.mean(ref ** 2)) < 2e-3
     return r
 
 
@@ -336,34 +377,120 @@ def test_forward_fp8_prefill_many_tiles(lib, bm):
     _forward_fp8_case(lib, 700, 1152, 640, 8, 2, 0, bm, seed=bm, variant=1)
 
 
+# ------------------------------------------------------------------------------ tile-boundary loads
+
+def _forward_given_routing(lib, x, w13, w2, ids, w32, bm, variant, scales=None):
+    """Given routing (ids, weights) -> GPU align + GEMM1 + GEMM2 + combine, both as stage
+    calls and as moe_forward, against the oracle's per-expert loop on every element."""
+    T, H = x.shape
+    k = ids.shape[1]
+    E = w13.shape[0]
+    I = w13.shape[1] // 2
+    R = T * k
+    dx, d13, d2 = x.to(DEV), w13.to(DEV), w2.to(DEV)
+    dw = torch.from_numpy(w32).to(DEV)
+    sorted_ids, expert_ids, ntpp, counts = lib.moe_align(torch.from_numpy(ids).to(DEV), E, bm)
+    a = torch.full((R + 8, I), float("nan"), dtype=torch.bfloat16, device=DEV)
+    y = torch.full((R + 8, H), float("nan"), dtype=torch.float32, device=DEV)
+    if scales is None:
+        lib.moe_gemm1_swiglu(dx, d13, sorted_ids, expert_ids, ntpp, k, bm, variant, a=a)
+        lib.moe_gemm2_weighted(a, d2, dw, sorted_ids, expert_ids, ntpp, T, k, bm, variant, y=y)
+        fwd = lib.moe_forward(dx, d13, d2, dw, sorted_ids, expert_ids, ntpp, k, bm, variant)
+        w13_64, w2_64 = np64(w13), np64(w2)
+    else:
+        s13, s2 = (t.to(DEV) for t in scales)
+        lib.moe_gemm1_swiglu_fp8(dx, d13, s13, sorted_ids, expert_ids, ntpp, k, bm, variant, a=a)
+        lib.moe_gemm2_weighted_fp8(a, d2, s2, dw, sorted_ids, expert_ids, ntpp, T, k, bm, variant,
+                                   y=y)
+        fwd = lib.moe_forward_fp8(dx, d13, s13, d2, s2, dw, sorted_ids, expert_ids, ntpp, k, bm,
+                                  variant)
+        w13_64 = O.dequant_rows(w13.numpy(), scales[0].numpy())
+        w2_64 = O.dequant_rows(w2.numpy(), scales[1].numpy())
+    out = lib.moe_combine(y, T, k, torch.bfloat16)
+    _sync()
+    assert np.array_equal(counts.cpu().numpy(), np.bincount(ids.reshape(-1), minlength=E))
+    assert not torch.isnan(a[:R]).any() and not torch.isnan(y[:R]).any()
+    assert torch.isnan(a[R:]).all() and torch.isnan(y[R:]).all()
+    ref = O.moe_loop(np64(x), w13_64, w2_64, ids, w32.astype(np.float64), round_a=True)
+    swiglu_flip_check(np64(a[:R]), O.swiglu_rows(np64(x), w13_64, ids), np.arange(R))
+    kref = O.down_and_combine(np64(a[:R]), w2_64, ids, w32.astype(np.float64))
+    for o in (out, fwd):
+        bf16_tol_check(np64(o), ref, kernel_ref=kref)
+
+
+def _routing_weights(T, k, seed):
+    rng = np.random.default_rng(seed)
+    w = rng.uniform(0.1, 1.0, (T, k))
+    return (w / w.sum(1, keepdims=True)).astype(np.float32)
+
+
+EDGE_CASES = [(16, 2), (32, 2), (32, 1), (64, 1), (128, 1), (256, 1)]
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+@pytest.mark.parametrize("bm,variant", EDGE_CASES)
+def test_forward_tile_boundary_loads(lib, bm, variant, fp8):
+    """[MKR] s10 functional table: experts with 0, 1, BLOCK_M-1, BLOCK_M, BLOCK_M+1 and
+    2*BLOCK_M rows (plus a second empty expert and a small one) through the expert GEMMs
+    at the tile heights the decode and prefill kernels use."""
+    if fp8 and (bm, variant) in ((32, 1), (64, 1)):
+        pytest.skip("FP8 weights run on the 16/32-row streaming and 128/256-row pipelined tiles")
+    loads = [0, 1, bm - 1, bm, bm + 1, 2 * bm, 0, 3]
+    k = 2
+    ids = S.ids_with_counts(loads, k, seed=bm + variant).numpy()
+    T = ids.shape[0]
+    E = len(loads)
+    H, I = (256, 256) if fp8 else (256, 192)
+    g = torch.Generator(device="cpu").manual_seed(bm * 10 + variant + fp8)
+    x = torch.randn(T, H, generator=g).to(torch.bfloat16)
+    w32 = _routing_weights(T, k, bm)
+    if fp8:
+        c13, s13 = _fp8_weights(g, E, 2 * I, H)
+        c2, s2 = _fp8_weights(g, E, H, I)
+        _forward_given_routing(lib, x, c13, c2, ids, w32, bm, variant, scales=(s13, s2))
+    else:
+        w13 = (torch.randn(E, 2 * I, H, generator=g) / H ** 0.5).to(torch.bfloat16)
+        w2 = (torch.randn(E, H, I, generator=g) / I ** 0.5).to(torch.bfloat16)
+        _forward_given_routing(lib, x, w13, w2, ids, w32, bm, variant)
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+@pytest.mark.parametrize("bm,variant", EDGE_CASES)
+def test_forward_one_expert_takes_every_token(lib, bm, variant, fp8):
+    """[MKR] s10 functional table: one expert receives every token (slot 0 of all 300
+    tokens), the other slot spread over the rest."""
+    if fp8 and (bm, variant) in ((32, 1), (64, 1)):
+        pytest.skip("FP8 weights run on the 16/32-row streaming and 128/256-row pipelined tiles")
+    T, k, E = 300, 2, 8
+    ids = S.random_topk_ids(T, k, E, seed=bm, hot=5).numpy()
+    H, I = (256, 256) if fp8 else (256, 192)
+    g = torch.Generator(device="cpu").manual_seed(bm + variant + 7 * fp8)
+    x = torch.randn(T, H, generator=g).to(torch.bfloat16)
+    w32 = _routing_weights(T, k, bm + 1)
+    if fp8:
+        c13, s13 = _fp8_weights(g, E, 2 * I, H)
+        c2, s2 = _fp8_weights(g, E, H, I)
+        _forward_given_routing(lib, x, c13, c2, ids, w32, bm, variant, scales=(s13, s2))
+    else:
+        w13 = (torch.randn(E, 2 * I, H, generator=g) / H ** 0.5).to(torch.bfloat16)
+        w2 = (torch.randn(E, H, I, generator=g) / I ** 0.5).to(torch.bfloat16)
+        _forward_given_routing(lib, x, w13, w2, ids, w32, bm, variant)
+
+
 # ------------------------------------------------------------------------------ whole layer
 
 def _layer_vs_oracle(lib, wl, lay):
+    """moe_layer against the oracle on every output element (see layer_check): routing
+    within the selection margin, the spec tolerance against the oracle's per-expert
+    math, and GEMM1 / GEMM2 + combine each against the oracle fed the GPU's inputs."""
     cfg = lib_cfg(lib, wl, lay)
     T, k = wl.T, wl.k
     ids = torch.empty(T, k, dtype=torch.int32, device=DEV)
     w = torch.empty(T, k, dtype=torch.float32, device=DEV)
     out = run_layer(lib, lay, k, cfg, topk_ids_out=ids, topk_w_out=w)
     _sync()
-    x64, wg64 = np64(lay.x), np64(lay.wg)
-    ref_logits = O.router_logits(x64, wg64)
-    kw = route_kwargs(wl, lay)
-    rid, rw = O.route(ref_logits.astype(np.float32), k, wl.mode, **kw)
-    margin = O.selection_margin(ref_logits.astype(np.float32), k, wl.mode, kw["offset"], kw["bias"],
-                                wl.n_group, wl.topk_group)
-    bound = logit_error_bound(x64, wg64)
-    gids = ids.cpu().numpy()
-    same = np.all(gids == rid, axis=1)
-    assert np.all(same | (margin <= 2 * bound)), "routing differs on a token with a clear margin"
-    assert same.mean() > 0.5
-    # the reference output uses the oracle's own routing; tokens routed differently (near
-    # ties within the logits' error bound) are left out of the element-wise comparison
-    w13_64, w2_64 = expert_weights64(lay)
-    ref = O.moe_loop(x64[same], w13_64, w2_64, rid[same], rw[same], round_a=bf16_layer(wl))
-    got = np64(out)[same]
-    if bf16_layer(wl):
-        return bf16_tol_check(got, ref)
-    return f32_tol_check(got, ref)
+    r, agree, _ = layer_check(lib, wl, lay, out, ids.cpu().numpy(), w.cpu().numpy().astype(np.float64))
+    return r
 
 
 def test_layer_tiny(lib):
@@ -405,17 +532,19 @@ def test_layer_small_batch_repeated(lib, name, T):
         _layer_vs_oracle(lib, wl, lay)
 
 
+@pytest.mark.parametrize("seed", [5, 13, 21])
 @pytest.mark.parametrize("name", ["qwen3_balanced", "qwen3_balanced_fp8"])
-def test_layer_prefill_split_round(lib, name):
+def test_layer_prefill_split_round(lib, name, seed):
     """Prefill with more tiles than work-groups in flight and a short last round: 640 GEMM2
     tiles of 128 x 256 on a 256-CU part (two work-groups per CU) are one round of whole tiles
-    (contiguous per-XCD ranges) and 128 tiles split in four K ranges, against the oracle.
-    (Seed 13 keeps the largest output within 6 RMS: the bf16 tolerance is absolute in RMS
-    units, and the rounding of a larger outlier alone can approach it.)"""
+    (contiguous per-XCD ranges) and 128 tiles split in four K ranges, against the oracle on
+    several seeds.  Outputs reach 6-7 RMS here, where the bf16 rounding of the output alone
+    takes up to 0.017 RMS of the 0.02 tolerance; the kernel-error check of bf16_tol_check
+    bounds what the split sums and the fix-up add beyond that rounding."""
     wl = S.WORKLOADS["qwen3_balanced"].scaled(T=512, H=1280, I=128)
     if name.endswith("fp8"):
         wl = wl.scaled(dtype="bf16_fp8w")
-    lay = S.make_layer(wl, device=DEV, seed=13)
+    lay = S.make_layer(wl, device=DEV, seed=seed)
     _layer_vs_oracle(lib, wl, lay)
 
 
@@ -581,7 +710,7 @@ def test_forward_ep_half_remote(lib, dtype, bm, variant, T, H, I, E, k):
                                           ("mixtral", 512, 16), ("deepseek_decode_fp8", 16, 4)])
 def test_layer_ep(lib, name, T, scale):
     """moe_layer_ep (global routing, this GPU's half of the experts) against the oracle's
-    share on tokens whose routing agrees."""
+    share on every token (near-tie tokens the GPU routed differently use its routing)."""
     base = S.WORKLOADS[name]
     q = 128 if base.dtype == "bf16_fp8w" else 64
     wl = base.scaled(T=T, H=base.H // scale // q * q, I=base.I // scale // q * q)
@@ -597,17 +726,16 @@ def test_layer_ep(lib, name, T, scale):
     out = lib.moe_layer_ep(lay.x, lay.wg, lay.w13[sel].contiguous(), lay.w2[sel].contiguous(), wl.k,
                            cfg, torch.from_numpy(m).to(DEV), topk_ids_out=ids, topk_w_out=w, **kw)
     _sync()
-    x64, wg64 = np64(lay.x), np64(lay.wg)
-    logits = O.router_logits(x64, wg64)
-    rkw = route_kwargs(wl, lay)
-    rid, rw = O.route(logits.astype(np.float32), wl.k, wl.mode, **rkw)
-    same = np.all(ids.cpu().numpy() == rid, axis=1)
+    gids, gw = ids.cpu().numpy(), w.cpu().numpy().astype(np.float64)
+    rid, rw, same = routing_vs_oracle(wl, lay, gids)
     assert same.mean() > 0.5
+    ref_ids = np.where(same[:, None], rid, gids)
+    ref_w = np.where(same[:, None], rw, gw)
+    x64 = np64(lay.x)
     w13_64, w2_64 = expert_weights64(lay, list(mine))
-    full13, full2 = expert_weights64(lay)
-    ref = O.moe_loop_ep(x64[same], w13_64, w2_64, rid[same], rw[same], m, round_a=True)
-    full = O.moe_loop(x64[same], full13, full2, rid[same], rw[same], round_a=True)
-    r = np.abs(np64(out)[same] - ref).max() / np.sqrt(np.mean(full ** 2))
+    ref = O.moe_loop_ep(x64, w13_64, w2_64, ref_ids, ref_w, m, round_a=True)
+    full = layer_reference(lay, ref_ids, ref_w, round_a=True)
+    r = np.abs(np64(out) - ref).max() / np.sqrt(np.mean(full ** 2))
     assert r <= 2e-2, f"share max|d|/RMS(layer) {r:.3e}"
 
 
@@ -620,7 +748,7 @@ def test_layer_ep(lib, name, T, scale):
 def test_layer_shared_expert(lib, name, T, scale):
     """moe_layer_shared: the routing's extra column is the shared expert (E, weight 1) and
     the output matches the oracle's per-expert loop over k routed slots + the shared
-    slot on tokens whose routing agrees."""
+    slot on every token (near-tie tokens the GPU routed differently use its routing)."""
     base = S.WORKLOADS[name].scaled(shared=1)
     q = 128 if base.dtype == "bf16_fp8w" else 64
     wl = base.scaled(T=T, H=base.H // scale // q * q, I=base.I // scale // q * q)
@@ -633,18 +761,6 @@ def test_layer_shared_expert(lib, name, T, scale):
     out = lib.moe_layer_shared(lay.x, lay.wg, lay.w13, lay.w2, k, cfg, topk_ids_out=ids,
                                topk_w_out=w, **kw)
     _sync()
-    gids, gw = ids.cpu().numpy(), w.cpu().numpy()
+    gids, gw = ids.cpu().numpy(), w.cpu().numpy().astype(np.float64)
     assert np.all(gids[:, k] == E) and np.all(gw[:, k] == 1.0)
-    x64, wg64 = np64(lay.x), np64(lay.wg)
-    logits = O.router_logits(x64, wg64)
-    rkw = route_kwargs(wl, lay)
-    rid, rw = O.route(logits.astype(np.float32), k, wl.mode, **rkw)
-    same = np.all(gids[:, :k] == rid, axis=1)
-    margin = O.selection_margin(logits.astype(np.float32), k, wl.mode, rkw["offset"], rkw["bias"],
-                                wl.n_group, wl.topk_group)
-    assert np.all(same | (margin <= 2 * logit_error_bound(x64, wg64)))
-    assert same.mean() > 0.5
-    ids_s, w_s = O.add_shared_slot(rid, rw, E)
-    w13_64, w2_64 = expert_weights64(lay)
-    ref = O.moe_loop(x64[same], w13_64, w2_64, ids_s[same], w_s[same], round_a=True)
-    bf16_tol_check(np64(out)[same], ref)
+    layer_check(lib, wl, lay, out, gids, gw)

@@ -28,7 +28,7 @@ def test_align_worked_example_both_implementations():
     g = gold("align_worked_example.json")
     ids = np.array(g["topk_ids"], np.int32)
     assert ids.reshape(-1).tolist() == g["flat"]
-    for impl in (O.align_argsort, O.align_counting):
+    for impl in (O.align_runs, O.align_counting):
         r = impl(ids, g["num_experts"], g["block_m"])
         assert r["sorted_ids"].tolist() == g["sorted_ids"]
         assert r["expert_ids"].tolist() == g["expert_ids"]
@@ -42,7 +42,7 @@ def test_align_padded_totals_match_printed_test_matrix():
     for name, c in g["cases"].items():
         ids = S.ids_with_counts(c["loads"], c["k"], seed=3).numpy()
         assert ids.shape == (c["T"], c["k"])
-        for impl in (O.align_argsort, O.align_counting):
+        for impl in (O.align_runs, O.align_counting):
             r = impl(ids, c["E"], bm)
             assert r["total"] == c["padded"], name
             assert r["counts"].tolist() == c["loads"]
@@ -80,7 +80,7 @@ def _check_align_invariants(ids, E, bm, r, cap):
 def test_align_invariants_and_implementations_agree(bm, T, k, E, skew):
     ids = S.random_topk_ids(T, k, E, seed=T + E, skew=skew).numpy()
     cap = O.align_capacity(T, k, E, bm)
-    a = O.align_argsort(ids, E, bm, cap)
+    a = O.align_runs(ids, E, bm, cap)
     b = O.align_counting(ids, E, bm, cap)
     for key in ("sorted_ids", "expert_ids", "counts"):
         assert np.array_equal(a[key], b[key]), key
@@ -97,7 +97,7 @@ def test_align_edge_counts():
     loads[-1] += pad
     ids = S.ids_with_counts(loads, k, seed=5).numpy()
     cap = O.align_capacity(ids.shape[0], k, len(loads), bm)
-    r = O.align_argsort(ids, len(loads), bm, cap)
+    r = O.align_runs(ids, len(loads), bm, cap)
     _check_align_invariants(ids, len(loads), bm, r, cap)
     assert r["total"] == sum(-(-c // bm) * bm for c in loads)
     hot = S.random_topk_ids(100, 4, 16, seed=1, hot=3).numpy()
@@ -112,7 +112,7 @@ def test_align_capacity_is_tight_bound():
     T, k, E, bm = 8, 2, 4, 4
     loads = [5, 5, 1, 5]
     ids = S.ids_with_counts(loads, k).numpy()
-    r = O.align_argsort(ids, E, bm)
+    r = O.align_runs(ids, E, bm)
     assert r["total"] == 8 + 8 + 4 + 8 == 28
     assert O.align_capacity(T, k, E, bm) >= r["total"]
     assert O.align_capacity(1, 8, 256, 64) == 8 * 64
@@ -142,7 +142,7 @@ def test_test_matrix_loads():
         logits32 = O.router_logits(x.numpy(), wg.numpy()).astype(np.float32)
         ids, _ = O.route(logits32, k, O.SOFTMAX_TOPK_RENORM)
         assert np.bincount(ids.reshape(-1), minlength=c["E"]).tolist() == c["loads"], name
-        assert O.align_argsort(ids, c["E"], g["block_m"])["total"] == c["padded"]
+        assert O.align_runs(ids, c["E"], g["block_m"])["total"] == c["padded"]
 
 
 def test_grouped_router_worked_example():
@@ -322,6 +322,34 @@ def test_loop_dense_bruteforce_agree(mode):
     assert np.abs(ar - a).max() > 0                   # the bf16 rounding point is real
 
 
+@pytest.mark.parametrize("mode", [0, 2])
+def test_stage_functions_compose_to_the_layer(mode):
+    """GEMM1+SwiGLU rows, the bf16 rounding of a, then GEMM2 x weight + combine give the
+    per-expert loop and the scalar brute force; slots of experts outside [0, E) add
+    nothing (the two halves of a split of the experts add up to the layer)."""
+    rng = np.random.default_rng(mode + 40)
+    T, H, I, E, k = 9, 12, 10, 6, 3
+    x = rng.standard_normal((T, H))
+    w13 = rng.standard_normal((E, 2 * I, H)) / np.sqrt(H)
+    w2 = rng.standard_normal((E, H, I)) / np.sqrt(I)
+    l32 = rng.standard_normal((T, E)).astype(np.float32)
+    kw = dict(n_group=3, topk_group=2, scaling=2.5) if mode == 2 else {}
+    ids, w = O.route(l32, k, mode, **kw)
+    for rnd in (False, True):
+        a = O.swiglu_rows(x, w13, ids)
+        out = O.down_and_combine(O.bf16_round(a) if rnd else a, w2, ids, w)
+        assert np.allclose(out, O.moe_loop(x, w13, w2, ids, w, round_a=rnd), rtol=1e-12, atol=1e-13)
+        assert np.allclose(out, O.moe_bruteforce(x, w13, w2, ids, w, round_a=rnd), rtol=1e-11,
+                           atol=1e-12)
+    half = np.where(ids < 3, ids, -1)
+    other = np.where(ids >= 3, ids - 3, -1)
+    a0 = O.swiglu_rows(x, w13[:3], half)
+    a1 = O.swiglu_rows(x, w13[3:], other)
+    assert np.allclose(a0 + a1, O.swiglu_rows(x, w13, ids), rtol=0, atol=0)
+    both = O.down_and_combine(a0, w2[:3], half, w) + O.down_and_combine(a1, w2[3:], other, w)
+    assert np.allclose(both, O.moe_loop(x, w13, w2, ids, w), rtol=1e-12, atol=1e-13)
+
+
 def test_loop_vs_dense_tiny_layer():
     g = gold("tiny_layer.json")
     lay = S.make_layer(S.WORKLOADS["tiny"])
@@ -386,9 +414,111 @@ def test_identical_experts_sum_of_weights():
     assert np.allclose(out, 2.5 * ref, rtol=1e-13)
 
 
-def test_selection_margin():
+def _bias_route_set(c_target, k, ng, tg):
+    """Selected set of the grouped sigmoid router when every logit is 0 (sigmoid = 1/2
+    exactly) and the bias carries the scores: c = fl32(1/2 + bias)."""
+    b = (np.asarray(c_target, np.float64) - 0.5).astype(np.float32)
+    ids, _ = O.route(np.zeros((1, b.size), np.float32), k, O.SIGMOID_BIAS_GROUPED, bias=b,
+                     n_group=ng, topk_group=tg)
+    return frozenset(ids[0].tolist())
+
+
+def _bias_margin(c_target, k, ng, tg):
+    b = (np.asarray(c_target, np.float64) - 0.5).astype(np.float32)
+    return float(O.selection_margin(np.zeros((1, b.size), np.float32), k, O.SIGMOID_BIAS_GROUPED,
+                                    bias=b, n_group=ng, topk_group=tg)[0])
+
+
+def test_selection_margin_plain_topk_closed_form():
+    """Plain top-k: half the gap between the k-th and (k+1)-th score (each side may move
+    by the radius)."""
     l32 = np.array([[1.0, 0.5, 0.25, 0.0]], np.float32)
-    assert O.selection_margin(l32, 2, 0)[0] == pytest.approx(0.25)
+    assert O.selection_margin(l32, 2, 0)[0] == 0.125
+    assert O.selection_margin(l32, 2, 1)[0] == 0.125
+    # the offset is part of the selection score
+    off = np.array([0.0, 0.0, 0.5, 0.0], np.float32)
+    assert O.selection_margin(l32, 2, 0, offset=off)[0] == 0.125      # 0.75 vs 0.5
+    assert O.selection_margin(l32, 4, 0)[0] == np.inf                 # k = E: nothing to swap
+
+
+def test_selection_margin_grouped_closed_forms():
+    """[MKR] s4 group-limited routing, scores set exactly through the bias (4 groups of 2,
+    keep 2, top-2)."""
+    # three groups tied at 1.5: the tie rule keeps groups 0 and 1, group 1 holds a selected
+    # expert, so no perturbation is safe
+    c = [0.9, 0.6, 0.8, 0.7, 0.75, 0.75, 0.5, 0.5]
+    assert _bias_route_set(c, 2, 4, 2) == {0, 2}
+    assert _bias_margin(c, 2, 4, 2) == 0.0
+    # the kept/dropped group gap binds: G1 = 1.30 vs G2 = 1.28 -> about 0.02 / 4
+    c = [0.95, 0.60, 0.90, 0.40, 0.66, 0.62, 0.1, 0.1]
+    m = _bias_margin(c, 2, 4, 2)
+    c32 = (np.float32(0.5) + (np.asarray(c) - 0.5).astype(np.float32)).astype(np.float64)
+    g1 = float(np.float32(c32[2]) + np.float32(c32[3]))
+    g2 = float(np.float32(c32[4]) + np.float32(c32[5]))
+    assert m == pytest.approx((g1 - g2) / 4, abs=1e-6)
+    # the last kept group holds no selected expert and the dropped group's best expert is
+    # far below the k-th: the group swap cannot change the set, the expert gap binds
+    c = [0.95, 0.90, 0.60, 0.59, 0.58, 0.57, 0.1, 0.1]
+    assert _bias_route_set(c, 2, 4, 2) == {0, 1}
+    c32 = (np.float32(0.5) + (np.asarray(c) - 0.5).astype(np.float32)).astype(np.float64)
+    assert _bias_margin(c, 2, 4, 2) == pytest.approx((c32[1] - c32[2]) / 2, abs=1e-7)
+
+
+def _grouped_instance(rng, E, ng, tg, k):
+    """Scores for the bias-carried router: well separated values (no exact ties)."""
+    return np.round(rng.uniform(0.0, 1.0, E), 4)
+
+
+@pytest.mark.parametrize("E,ng,tg,k", [(8, 4, 2, 2), (8, 4, 1, 2), (8, 4, 3, 3), (8, 2, 1, 1),
+                                       (6, 3, 1, 2)])
+def test_selection_margin_grouped_brute_force(E, ng, tg, k):
+    """Brute force over every perturbation with components in {-eps, 0, +eps} (3^E of
+    them): below the reported radius the selected set never changes; just above it some
+    perturbation changes it (groups of two experts, where the bound is exact).  Plus
+    random perturbations inside the radius."""
+    rng = np.random.default_rng(E * 100 + ng * 10 + tg + k)
+    corners = np.array(list(itertools.product((-1.0, 0.0, 1.0), repeat=E)))
+    exact = E // ng == 2
+    checked = 0
+    for trial in range(40):
+        c = _grouped_instance(rng, E, ng, tg, k)
+        m = _bias_margin(c, k, ng, tg)
+        if not (1e-4 < m < 0.2):
+            continue
+        base = _bias_route_set(c, k, ng, tg)
+        below = 0.999 * m
+        for d in corners:
+            assert _bias_route_set(c + below * d, k, ng, tg) == base
+        for _ in range(200):
+            d = rng.uniform(-below, below, E)
+            assert _bias_route_set(c + d, k, ng, tg) == base
+        if exact:
+            above = 1.002 * m
+            assert any(_bias_route_set(c + above * d, k, ng, tg) != base for d in corners), \
+                f"radius {m} is not attained: the bound is loose on {c}"
+        checked += 1
+        if checked == 4:
+            break
+    assert checked >= 2
+
+
+@pytest.mark.parametrize("mode", [0, 1])
+def test_selection_margin_plain_brute_force(mode):
+    """Softmax rules: perturbing the logits by just under the radius never changes the
+    selected set; moving the k-th down and the (k+1)-th up by just over it does."""
+    rng = np.random.default_rng(5 + mode)
+    E, k = 7, 3
+    for _ in range(30):
+        l = rng.standard_normal((1, E)).astype(np.float32)
+        m = float(O.selection_margin(l, k, mode)[0])
+        base = set(O.route(l, k, mode)[0][0].tolist())
+        for _ in range(300):
+            d = rng.uniform(-0.999 * m, 0.999 * m, E).astype(np.float32)
+            assert set(O.route((l + d).astype(np.float32), k, mode)[0][0].tolist()) == base
+        o = np.argsort(-l[0].astype(np.float64), kind="stable")
+        d = np.zeros(E, np.float32)
+        d[o[k - 1]], d[o[k]] = -1.002 * m, 1.002 * m
+        assert set(O.route((l + d[None]).astype(np.float32), k, mode)[0][0].tolist()) != base
 
 
 # ----------------------------------------------------------------------------- FP8 weights
@@ -502,7 +632,7 @@ def test_ep_align_marks_remote_tiles():
     ids = S.random_topk_ids(300, 8, 64, seed=3, skew=0.8).numpy()
     for bm in (16, 64):
         cap = O.align_capacity(300, 8, 64, bm)
-        ref = O.align_argsort(ids, 64, bm, cap)
+        ref = O.align_runs(ids, 64, bm, cap)
         for m in _half_maps(64, bm):
             r = O.align_ep(ids, 64, bm, m, cap)
             assert np.array_equal(r["sorted_ids"], ref["sorted_ids"])
@@ -567,17 +697,23 @@ def test_permute_grouped_matches_loop_and_library_grouped_mm(case):
     assert np.allclose(perm, loop, rtol=1e-12, atol=1e-12)
     assert np.allclose(O.moe_permute_grouped(x64, w13_64, w2_64, ids, w, round_a=True),
                        O.moe_loop(x64, w13_64, w2_64, ids, w, round_a=True), rtol=1e-12, atol=1e-12)
-    # torch.nn.functional.grouped_mm (fp32 on the CPU) on the permuted rows
-    E = w13.shape[0]
-    I = w13.shape[1] // 2
-    flat = torch.from_numpy(ids.reshape(-1).astype(np.int64))
-    order = torch.argsort(flat, stable=True)
-    xs = x[order // k].contiguous()
-    offs = torch.cumsum(torch.bincount(flat, minlength=E), 0).to(torch.int32)
-    g = F.grouped_mm(xs, w13[:, :I].transpose(-2, -1).contiguous(), offs=offs)
-    u = F.grouped_mm(xs, w13[:, I:].transpose(-2, -1).contiguous(), offs=offs)
-    h = (F.silu(g) * u).contiguous()
-    ys = F.grouped_mm(h, w2.transpose(-2, -1).contiguous(), offs=offs)
-    ys = ys * torch.from_numpy(w.reshape(-1).astype(np.float32))[order, None]
-    lib = torch.zeros(x.shape[0], x.shape[1]).index_add_(0, order // k, ys).double().numpy()
+    # torch's grouped GEMM (F.grouped_mm, fp32 on the CPU) as the library leg.  Its
+    # contract: rows [ends[g-1], ends[g]) of the left operand multiply the g-th matrix of
+    # the right one.  Routed (token, slot) pairs are ranked by the key expert * T*k +
+    # (pair index), so each expert's pairs are one contiguous run; the runs' ends come
+    # from where each expert's keys stop.
+    E, I, T = w13.shape[0], w13.shape[1] // 2, x.shape[0]
+    R = T * k
+    eid = torch.from_numpy(ids.astype(np.int64)).reshape(-1)
+    key, rank = torch.sort(eid * R + torch.arange(R))
+    tok = rank // k
+    ends = torch.searchsorted(key, (torch.arange(E) + 1) * R).to(torch.int32)
+    lhs = x.index_select(0, tok)
+    gate = F.grouped_mm(lhs, w13[:, :I].permute(0, 2, 1).contiguous(), offs=ends)
+    up = F.grouped_mm(lhs, w13[:, I:].permute(0, 2, 1).contiguous(), offs=ends)
+    act = (gate * torch.sigmoid(gate) * up).contiguous()
+    rows = F.grouped_mm(act, w2.permute(0, 2, 1).contiguous(), offs=ends)
+    wt = torch.from_numpy(w.astype(np.float32)).reshape(-1).index_select(0, rank)
+    lib = torch.zeros(T, x.shape[1]).scatter_add_(
+        0, tok[:, None].expand(-1, x.shape[1]), rows * wt[:, None]).double().numpy()
     assert np.abs(lib - loop).max() / np.abs(loop).max() < 1e-5
