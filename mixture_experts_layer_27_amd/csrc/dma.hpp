@@ -65,6 +65,9 @@ __device__ __forceinline__ void wait_vm(int n) {
 #undef MOE_VMW_CASE
 }
 
+// wait until this wave's LDS reads (and other LDS / scalar-memory ops) have returned
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
 template <int N>
 __device__ __forceinline__ void wait_vm_c() {
   static_assert(N >= 0 && N < 64, "vmcnt range");

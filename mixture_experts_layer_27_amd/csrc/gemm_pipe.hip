@@ -8,9 +8,12 @@
 // * NSTAGE-deep ring of BK-element stages: BK = 64 (128-byte LDS rows, chunk c of row m
 //   at c ^ ((m >> 1) & 7)) for 256-row tiles, BK = 32 (64-byte rows, c ^ sw4(m)) for
 //   128-row tiles, whose 73 KB ring lets two work-groups share a CU; both swizzles are
-//   conflict-free for the DMA writes and the 32-row MFMA operand reads.  Stage
-//   kt+NSTAGE-1 is issued while stage kt is consumed; one barrier per stage, preceded by
-//   an explicit vmcnt wait for this wave's own loads.
+//   conflict-free for the DMA writes and the 32-row MFMA operand reads.  One barrier per
+//   stage, preceded by an explicit vmcnt wait for this wave's own loads, placed before
+//   the stage's last k16 step so that it and the next stage's first fragment reads sit in
+//   the shadow of the MFMAs already issued.  With two 64-element stages (bf16 256-row
+//   tiles) the slot just read is refilled right after that barrier, one DMA instruction
+//   between each two MFMAs; deeper rings refill the slot read one stage earlier.
 // * v_mfma_f32_32x32x16_bf16, WM x WN waves each holding a (BM/WM) x (BN/WN) fp32
 //   accumulator tile: 2 x 2 (one wave per SIMD, up to 128 x 128), or 2 x 4 for GEMM1's
 //   256-row tile (two waves per SIMD, 128 x 64 each); LDS fragments are double-buffered in
@@ -150,7 +153,7 @@ __device__ __forceinline__ bool grouped_slot(int bid, int mtiles, int nblocks, b
   nb = gn * GN + pos / GM;
   return mt < mtiles && nb < nblocks;
 }
-constexpr int kGroupM = 4, kGroupN = 8;
+constexpr int kGroupM = 4, kGroupN = 4;
 
 // GEMM2: balanced rounds with a split last round.  GEMM2's tiles are few
 // and long (K = I), so the rounds of ncu tiles (the work-groups in flight) quantise: at the
@@ -410,6 +413,30 @@ moe_gemm_pipe_kernel(PArgs p) {
     }
   };
 
+  // The MFMAs of one k16 step with stage kt's DMA instructions spread between them (bf16
+  // two-stage ring): one DMA after each MFMA while both last.
+  auto mfma_issue_interleaved = [&](const auto& f, int kt) {
+    static_assert(WB == 2, "bf16 weights");
+    uint8_t* st = smem + (kt % NSTAGE) * C::STAGE;
+    const int k0 = kt * C::BK;
+    constexpr int NM = C::FM * C::FN;
+#pragma unroll
+    for (int q = 0; q < NM; ++q) {
+      const int i = q / C::FN, j = q % C::FN;
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
+#pragma unroll
+      for (int d = q * C::L / NM; d < (q + 1) * C::L / NM; ++d) {
+        if (d < C::LA) dma16(a_src[d] + k0, (MOE_LDS void*)(st + 1024 * (w + C::NW * d)));
+        else dma16(b_src[d - C::LA] + k0 * WB, (MOE_LDS void*)(st + C::SA + 1024 * (w + C::NW * (d - C::LA))));
+      }
+    }
+#pragma unroll
+    for (int d = (NM >= C::L ? C::L : NM * (C::L / NM)); d < C::L; ++d) {
+      if (d < C::LA) dma16(a_src[d] + k0, (MOE_LDS void*)(st + 1024 * (w + C::NW * d)));
+      else dma16(b_src[d - C::LA] + k0 * WB, (MOE_LDS void*)(st + C::SA + 1024 * (w + C::NW * (d - C::LA))));
+    }
+  };
+
   // Fragments are double-buffered in registers: the reads of k16 step q+1 are issued
   // before the MFMAs of step q.  sched_barrier(0) pins each group in place so the
   // scheduler does not sink the reads next to their first use (exposing LDS latency).
@@ -456,37 +483,54 @@ moe_gemm_pipe_kernel(PArgs p) {
     for (; kt + 1 < nk; ++kt) stage(T_{}, F_{}, kt, (min(kt + NSTAGE - 2, nk - 1) - (kt + 1)) * C::L);
     stage(F_{}, F_{}, kt, 0);
   } else {
-    // Two stages: stage kt+1 is loaded while stage kt computes.  The barrier at the
-    // start of each stage both publishes it (after this wave's own wait) and frees the
-    // other slot, which held stage kt-1.
-    // With PFD > 0, stage kt+1+PFD is also touched into L2 right after stage kt+1's DMA,
-    // so the DMA of each stage finds its lines resident; the wait below lets those
-    // prefetches stay in flight.
-    auto stage = [&](auto refill, int kt, int vm_allowed) {
-      wait_vm(vm_allowed);
-      barrier_keep_vm();
-      if constexpr (decltype(refill)::value) {
-        issue(kt + 1);
-        if (kt + 1 + PFD < nk) prefetch(kt + 1 + PFD);
-      }
-      read_frags(kt, 0, fr[0]);
+    // Two stages.  Stage kt+1 is published at a barrier placed before the last k16 step of
+    // stage kt, so the barrier and the first fragment reads of stage kt+1 sit in the shadow
+    // of the MFMAs already issued; every wave has read all of stage kt by then (its LDS
+    // reads are awaited before the barrier), so the slot of stage kt is refilled with stage
+    // kt+2 right after it, one DMA instruction after each MFMA of that last step so the
+    // MFMA pipe keeps running while the DMAs issue.  With PFD > 0, stage kt+2+PFD is also
+    // touched into L2 after that refill; the waits leave those prefetches in flight.
+    int npf = 0;                                  // prefetch instructions issued, not yet covered
+    issue(0);
+    if (nk > 1) issue(1);
+    if constexpr (PFD > 0) {
+      for (int d = 2; d < 2 + PFD && d < nk; ++d, npf += P) prefetch(d);
+    }
+    wait_vm((nk > 1 ? C::L : 0) + npf);
+    barrier_keep_vm();
+    read_frags(0, 0, fr[0]);
+    // pf: prefetch instructions issued after stage kt+1's DMAs (they may stay in flight)
+    auto stage = [&](auto refill, int kt, int pf) {
 #pragma unroll
       for (int ks = 0; ks < NSTEP; ++ks) {
-        if (ks + 1 < NSTEP) read_frags(kt, ks + 1, fr[(ks + 1) & 1]);
+        if (ks + 1 < NSTEP) {
+          read_frags(kt, ks + 1, fr[(ks + 1) & 1]);
+          __builtin_amdgcn_sched_barrier(0);
+          mfma_all(fr[ks & 1]);
+          __builtin_amdgcn_sched_barrier(0);
+          continue;
+        }
+        if (kt + 1 < nk) {
+          wait_lgkm0();
+          wait_vm(pf);
+          barrier_keep_vm();
+          read_frags(kt + 1, 0, fr[0]);
+        }
         __builtin_amdgcn_sched_barrier(0);
-        mfma_all(fr[ks & 1]);
+        if constexpr (decltype(refill)::value) {
+          mfma_issue_interleaved(fr[ks & 1], kt + 2);
+          if (kt + 2 + PFD < nk) prefetch(kt + 2 + PFD);
+        } else {
+          mfma_all(fr[ks & 1]);
+        }
         __builtin_amdgcn_sched_barrier(0);
       }
     };
-    issue(0);
-    int npf = 0;
-    for (int d = 1; d <= PFD && d < nk; ++d, ++npf) prefetch(d);
     int kt = 0;
-    // stage 0 waits behind the warm-up prefetches; stage kt >= 1 behind PF(kt+PFD) only
-    for (; kt + 1 < nk; ++kt) {
-      stage(T_{}, kt, kt == 0 ? npf * P : (kt + PFD < nk ? P : 0));
-    }
-    stage(F_{}, kt, kt == 0 ? npf * P : (kt + PFD < nk ? P : 0));
+    // prefetch instructions issued after the refill of stage kt+1 (at stage kt-1)
+    for (; kt + 2 < nk; ++kt) stage(T_{}, kt, (kt >= 1 && kt + 1 + PFD < nk) ? P : (kt == 0 ? npf : 0));
+    for (; kt < nk; ++kt) stage(F_{}, kt, (kt >= 1 && kt + 1 + PFD < nk) ? P : (kt == 0 ? npf : 0));
+    wait_vm_c<0>();
   }
 
   // ---- epilogue.  D layout (32x32): lane holds column (lane & 31),
