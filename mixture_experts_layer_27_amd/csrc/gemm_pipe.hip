@@ -252,10 +252,13 @@ moe_gemm_pipe_kernel(PArgs p) {
 
   // rows of the tile (sentinels read row 0 and are never stored); GEMM2 also stages the
   // router weights here, so its epilogue issues no dependent global loads
+  static_assert(C::NT >= BM, "one tile row per thread");
+  int valid = 0;
   for (int m = tid; m < BM; m += C::NT) {
     const int r = p.sorted_ids[static_cast<int64_t>(mt) * BM + m];
     srow[m] = r;
     if (MODE == 2) swt[m] = r < p.R ? p.topk_w[r] : 0.f;
+    valid = r < p.R;
   }
   if (MODE == 2 && e < 0) {
     // expert held by another GPU: zeros in this tile's slice of y, so the combine adds
@@ -291,7 +294,8 @@ moe_gemm_pipe_kernel(PArgs p) {
     for (int n = tid; n < BN; n += C::NT)
       sscale[n] = p.B_scale[static_cast<int64_t>(e) * nrows + b_row(n)];
   }
-  __syncthreads();
+  // routed rows of the tile: a prefix (an expert's padding rows end its last tile)
+  const int nv = __syncthreads_count(valid);
 
   // DMA sources: instruction j of wave w fills tile rows RPI*(w + NW*j) .. +RPI (1 KB);
   // lane -> row lane / CPR, physical chunk lane % CPR, logical chunk pch ^ swz(row)
@@ -345,6 +349,9 @@ moe_gemm_pipe_kernel(PArgs p) {
   };
 
   const int wm = w / WN, wn = w % WN;
+  // 32-row fragments of this wave holding routed rows; the rest of the tile is padding,
+  // whose MFMAs and A-operand reads are skipped
+  const int na = __builtin_amdgcn_readfirstlane(min(C::FM, max(0, (nv - wm * C::WTM + 31) >> 5)));
   f32x16 acc[C::FM][C::FN];
 #pragma unroll
   for (int i = 0; i < C::FM; ++i)
@@ -362,7 +369,7 @@ moe_gemm_pipe_kernel(PArgs p) {
   // E4M3 values) and A chunks 4*ks + 2h (first MFMA) and 4*ks + 2h + 1 (second).
   constexpr int NSTEP = WB == 2 ? C::KS : C::KS / 2;
   using Fr = Frags<C::FM, C::FN, WB>;
-  auto read_frags = [&](int kt, int ks, Fr& f) {
+  auto read_frags = [&](auto full, int kt, int ks, Fr& f) {
     const uint8_t* sa = smem + (kt % NSTAGE) * C::STAGE;
     const uint8_t* sb = sa + C::SA;
     if constexpr (WB == 2) {
@@ -370,7 +377,7 @@ moe_gemm_pipe_kernel(PArgs p) {
 #pragma unroll
       for (int i = 0; i < C::FM; ++i) {
         const int row = wm * C::WTM + i * 32 + (lane & 31);
-        f.a[i] = *reinterpret_cast<const bf16x8*>(sa + pswz<C::ROWA>(row, ch));
+        if (decltype(full)::value || i < na) f.a[i] = *reinterpret_cast<const bf16x8*>(sa + pswz<C::ROWA>(row, ch));
       }
 #pragma unroll
       for (int j = 0; j < C::FN; ++j) {
@@ -382,8 +389,10 @@ moe_gemm_pipe_kernel(PArgs p) {
 #pragma unroll
       for (int i = 0; i < C::FM; ++i) {
         const int row = wm * C::WTM + i * 32 + (lane & 31);
-        f.a0[i] = *reinterpret_cast<const bf16x8*>(sa + pswz<C::ROWA>(row, 4 * ks + 2 * h));
-        f.a1[i] = *reinterpret_cast<const bf16x8*>(sa + pswz<C::ROWA>(row, 4 * ks + 2 * h + 1));
+        if (decltype(full)::value || i < na) {
+          f.a0[i] = *reinterpret_cast<const bf16x8*>(sa + pswz<C::ROWA>(row, 4 * ks + 2 * h));
+          f.a1[i] = *reinterpret_cast<const bf16x8*>(sa + pswz<C::ROWA>(row, 4 * ks + 2 * h + 1));
+        }
       }
 #pragma unroll
       for (int j = 0; j < C::FN; ++j) {
@@ -392,13 +401,13 @@ moe_gemm_pipe_kernel(PArgs p) {
       }
     }
   };
-  auto mfma_all = [&](const Fr& f) {
+  auto mfma_all = [&](auto full, const Fr& f) {
     if constexpr (WB == 2) {
 #pragma unroll
       for (int i = 0; i < C::FM; ++i)
 #pragma unroll
         for (int j = 0; j < C::FN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
+          if (decltype(full)::value || i < na) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
     } else {
 #pragma unroll
       for (int j = 0; j < C::FN; ++j) {
@@ -406,8 +415,10 @@ moe_gemm_pipe_kernel(PArgs p) {
         fp8x16_to_bf16x2(f.q[j], b0, b1);
 #pragma unroll
         for (int i = 0; i < C::FM; ++i) {
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a0[i], b0, acc[i][j], 0, 0, 0);
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a1[i], b1, acc[i][j], 0, 0, 0);
+          if (decltype(full)::value || i < na) {
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a0[i], b0, acc[i][j], 0, 0, 0);
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a1[i], b1, acc[i][j], 0, 0, 0);
+          }
         }
       }
     }
@@ -415,7 +426,7 @@ moe_gemm_pipe_kernel(PArgs p) {
 
   // The MFMAs of one k16 step with stage kt's DMA instructions spread between them (bf16
   // two-stage ring): one DMA after each MFMA while both last.
-  auto mfma_issue_interleaved = [&](const auto& f, int kt) {
+  auto mfma_issue_interleaved = [&](auto full, const auto& f, int kt) {
     static_assert(WB == 2, "bf16 weights");
     uint8_t* st = smem + (kt % NSTAGE) * C::STAGE;
     const int k0 = kt * C::BK;
@@ -423,7 +434,7 @@ moe_gemm_pipe_kernel(PArgs p) {
 #pragma unroll
     for (int q = 0; q < NM; ++q) {
       const int i = q / C::FN, j = q % C::FN;
-      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
+      if (decltype(full)::value || i < na) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
 #pragma unroll
       for (int d = q * C::L / NM; d < (q + 1) * C::L / NM; ++d) {
         if (d < C::LA) dma16(a_src[d] + k0, (MOE_LDS void*)(st + 1024 * (w + C::NW * d)));
@@ -444,6 +455,9 @@ moe_gemm_pipe_kernel(PArgs p) {
   using T_ = std::true_type;
   using F_ = std::false_type;
 
+  // The K loop, instantiated for full tiles and for a tile whose last fragments are padding
+  auto kloop = [&](auto full) {
+
   if constexpr (NSTAGE >= 3) {
     // Ring of NSTAGE stages, NSTAGE-1 in flight.  The barrier that publishes stage kt+1
     // sits before the last k16 step of stage kt, so the first fragments of kt+1 are read
@@ -457,7 +471,7 @@ moe_gemm_pipe_kernel(PArgs p) {
 #pragma unroll
       for (int ks = 0; ks < NSTEP; ++ks) {
         if (ks + 1 < NSTEP) {
-          read_frags(kt, ks + 1, fr[(ks + 1) & 1]);
+          read_frags(full, kt, ks + 1, fr[(ks + 1) & 1]);
         } else if constexpr (decltype(has_next)::value) {
           // issued so far: stages 0 .. kt+NSTAGE-2; stage kt+1 must be complete, so
           // only the NSTAGE-3 stages after it may still be in flight
@@ -465,10 +479,10 @@ moe_gemm_pipe_kernel(PArgs p) {
           else wait_vm(vm_allowed);
           barrier_keep_vm();
           if constexpr (decltype(refill)::value) issue(kt + NSTAGE - 1);
-          read_frags(kt + 1, 0, fr[0]);
+          read_frags(full, kt + 1, 0, fr[0]);
         }
         __builtin_amdgcn_sched_barrier(0);
-        mfma_all(fr[ks & 1]);
+        mfma_all(full, fr[ks & 1]);
         __builtin_amdgcn_sched_barrier(0);
       }
     };
@@ -477,7 +491,7 @@ moe_gemm_pipe_kernel(PArgs p) {
       if (s < nk) issue(s);
     wait_vm(min(NSTAGE - 2, nk - 1) * C::L);
     barrier_keep_vm();
-    read_frags(0, 0, fr[0]);
+    read_frags(full, 0, 0, fr[0]);
     int kt = 0;
     for (; kt + NSTAGE <= nk; ++kt) stage(T_{}, T_{}, kt, 0);
     for (; kt + 1 < nk; ++kt) stage(T_{}, F_{}, kt, (min(kt + NSTAGE - 2, nk - 1) - (kt + 1)) * C::L);
@@ -498,15 +512,15 @@ moe_gemm_pipe_kernel(PArgs p) {
     }
     wait_vm((nk > 1 ? C::L : 0) + npf);
     barrier_keep_vm();
-    read_frags(0, 0, fr[0]);
+    read_frags(full, 0, 0, fr[0]);
     // pf: prefetch instructions issued after stage kt+1's DMAs (they may stay in flight)
     auto stage = [&](auto refill, int kt, int pf) {
 #pragma unroll
       for (int ks = 0; ks < NSTEP; ++ks) {
         if (ks + 1 < NSTEP) {
-          read_frags(kt, ks + 1, fr[(ks + 1) & 1]);
+          read_frags(full, kt, ks + 1, fr[(ks + 1) & 1]);
           __builtin_amdgcn_sched_barrier(0);
-          mfma_all(fr[ks & 1]);
+          mfma_all(full, fr[ks & 1]);
           __builtin_amdgcn_sched_barrier(0);
           continue;
         }
@@ -514,14 +528,14 @@ moe_gemm_pipe_kernel(PArgs p) {
           wait_lgkm0();
           wait_vm(pf);
           barrier_keep_vm();
-          read_frags(kt + 1, 0, fr[0]);
+          read_frags(full, kt + 1, 0, fr[0]);
         }
         __builtin_amdgcn_sched_barrier(0);
         if constexpr (decltype(refill)::value) {
-          mfma_issue_interleaved(fr[ks & 1], kt + 2);
+          mfma_issue_interleaved(full, fr[ks & 1], kt + 2);
           if (kt + 2 + PFD < nk) prefetch(kt + 2 + PFD);
         } else {
-          mfma_all(fr[ks & 1]);
+          mfma_all(full, fr[ks & 1]);
         }
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -532,6 +546,11 @@ moe_gemm_pipe_kernel(PArgs p) {
     for (; kt < nk; ++kt) stage(F_{}, kt, (kt >= 1 && kt + 1 + PFD < nk) ? P : (kt == 0 ? npf : 0));
     wait_vm_c<0>();
   }
+
+  };
+  // (FP8 tiles always run the full-tile loop: the second instance would not fit their registers)
+  if (WB == 1 || na == C::FM) kloop(T_{});
+  else kloop(F_{});
 
   // ---- epilogue.  D layout (32x32): lane holds column (lane & 31),
   //      rows 8*(v/4) + 4*(lane/32) + (v%4), v = 0..15.
