@@ -431,6 +431,7 @@ moe_gemm_pipe_kernel(PArgs p) {
     uint8_t* st = smem + (kt % NSTAGE) * C::STAGE;
     const int k0 = kt * C::BK;
     constexpr int NM = C::FM * C::FN;
+    if constexpr (C::NW == 8) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int q = 0; q < NM; ++q) {
       const int i = q / C::FN, j = q % C::FN;
@@ -441,11 +442,39 @@ moe_gemm_pipe_kernel(PArgs p) {
         else dma16(b_src[d - C::LA] + k0 * WB, (MOE_LDS void*)(st + C::SA + 1024 * (w + C::NW * (d - C::LA))));
       }
     }
+    if constexpr (C::NW == 8) __builtin_amdgcn_s_setprio(0);
 #pragma unroll
     for (int d = (NM >= C::L ? C::L : NM * (C::L / NM)); d < C::L; ++d) {
       if (d < C::LA) dma16(a_src[d] + k0, (MOE_LDS void*)(st + 1024 * (w + C::NW * d)));
       else dma16(b_src[d - C::LA] + k0 * WB, (MOE_LDS void*)(st + C::SA + 1024 * (w + C::NW * (d - C::LA))));
     }
+  };
+
+  // The MFMAs of fragments f (bf16 weights) with the LDS reads of the next k16 step's
+  // fragments g spread between them, so the operand reads of the waves sharing a SIMD do
+  // not arrive at the LDS in one burst; with two waves per SIMD the MFMA cluster runs at
+  // raised issue priority.
+  auto mfma_reads = [&](auto full, const auto& f, int kt, int ks, auto& g) {
+    static_assert(WB == 2, "bf16 weights");
+    const uint8_t* sa = smem + (kt % NSTAGE) * C::STAGE;
+    const uint8_t* sb = sa + C::SA;
+    const int ch = 2 * ks + (lane >> 5);
+    constexpr int NM = C::FM * C::FN;
+    if constexpr (C::NW == 8) __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+    for (int q = 0; q < NM; ++q) {
+      const int i = q / C::FN, j = q % C::FN;
+      if (decltype(full)::value || i < na)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
+      if (q < C::FM) {
+        if (decltype(full)::value || q < na)
+          g.a[q] = *reinterpret_cast<const bf16x8*>(sa + pswz<C::ROWA>(wm * C::WTM + q * 32 + (lane & 31), ch));
+      } else if (q < C::FM + C::FN) {
+        g.b[q - C::FM] = *reinterpret_cast<const bf16x8*>(
+            sb + pswz<C::ROWB>(wn * C::WTN + (q - C::FM) * 32 + (lane & 31), ch));
+      }
+    }
+    if constexpr (C::NW == 8) __builtin_amdgcn_s_setprio(0);
   };
 
   // Fragments are double-buffered in registers: the reads of k16 step q+1 are issued
@@ -470,6 +499,11 @@ moe_gemm_pipe_kernel(PArgs p) {
     auto stage = [&](auto has_next, auto refill, int kt, int vm_allowed) {
 #pragma unroll
       for (int ks = 0; ks < NSTEP; ++ks) {
+        if (WB == 2 && ks + 1 < NSTEP) {
+          if constexpr (WB == 2) mfma_reads(full, fr[ks & 1], kt, ks + 1, fr[(ks + 1) & 1]);
+          __builtin_amdgcn_sched_barrier(0);
+          continue;
+        }
         if (ks + 1 < NSTEP) {
           read_frags(full, kt, ks + 1, fr[(ks + 1) & 1]);
         } else if constexpr (decltype(has_next)::value) {
@@ -518,9 +552,7 @@ moe_gemm_pipe_kernel(PArgs p) {
 #pragma unroll
       for (int ks = 0; ks < NSTEP; ++ks) {
         if (ks + 1 < NSTEP) {
-          read_frags(full, kt, ks + 1, fr[(ks + 1) & 1]);
-          __builtin_amdgcn_sched_barrier(0);
-          mfma_all(full, fr[ks & 1]);
+          mfma_reads(full, fr[ks & 1], kt, ks + 1, fr[(ks + 1) & 1]);
           __builtin_amdgcn_sched_barrier(0);
           continue;
         }
