@@ -15,10 +15,11 @@
 //   tiles) the slot just read is refilled right after that barrier, one DMA instruction
 //   between each two MFMAs; deeper rings refill the slot read one stage earlier.
 // * v_mfma_f32_32x32x16_bf16, WM x WN waves each holding a (BM/WM) x (BN/WN) fp32
-//   accumulator tile: 2 x 2 (one wave per SIMD, up to 128 x 128), or 2 x 4 for GEMM1's
-//   256-row tile (two waves per SIMD, 128 x 64 each); LDS fragments are double-buffered in
-//   registers so the MFMAs of one k16 step overlap the LDS reads of the next; GEMM1 B
-//   tiles interleave 32-row gate and up blocks so that SwiGLU runs in registers.
+//   accumulator tile: 2 x 2 (one wave per SIMD, up to 128 x 128), or 2 x 4 for the bf16
+//   256-row tiles (two waves per SIMD, 128 x 64 each); LDS fragments are double-buffered in
+//   registers and the reads of the next k16 step are spread between the MFMAs of this
+//   one; GEMM1 B tiles interleave 32-row gate and up blocks so that SwiGLU runs in
+//   registers.
 // * GEMM2 splits a short last round of tiles in K over every CU (see split_plan).
 // * FP8 expert weights (OCP E4M3 bytes, one fp32 scale per weight row; section 8 of the
 //   same page prices an expert at one byte per weight): the B tile is staged as bytes
@@ -769,8 +770,8 @@ hipError_t launch_pipe_gemm1(const GemmArgs& g, int tile_m, hipStream_t s) {
     if (tile_m == 128) return run_pipe<1, 128, 256, 2, 2, 64, 4, 0, 1>(g, s);
     return hipErrorInvalidValue;
   }
-  // 8 waves (2 x 4) for the 256-row tile: measured 1.97 -> 1.92 ms on the Mixtral-8x7B
-  // shape; GEMM2 measured slower that way and keeps 4
+  // 8 waves (2 x 4, two per SIMD) for the 256-row tile: with the operand reads spread
+  // between the MFMAs they measure faster than 4 (Mixtral-8x7B shape: 1.84 vs 1.88 ms)
   if (tile_m == 256) return run_pipe<1, 256, 256, 2, 4, 64, 2, 0>(g, s);
   if (tile_m == 128) return run_pipe<1, 128, 256, 2, 2, 32, 3, 0>(g, s);
   return hipErrorInvalidValue;
@@ -782,7 +783,9 @@ hipError_t launch_pipe_gemm2(const GemmArgs& g, int tile_m, hipStream_t s) {
     if (tile_m == 128) return run_pipe<2, 128, 256, 2, 2, 64, 4, 0, 1>(g, s);
     return hipErrorInvalidValue;
   }
-  if (tile_m == 256) return run_pipe<2, 256, 256, 2, 2, 64, 2, 2>(g, s);
+  // 8 waves as GEMM1; no L2 prefetch (Mixtral-8x7B shape: 1.08 ms against 1.15 ms for 4
+  // waves with a prefetch two stages ahead)
+  if (tile_m == 256) return run_pipe<2, 256, 256, 2, 4, 64, 2, 0>(g, s);
   if (tile_m == 128) return run_pipe<2, 128, 256, 2, 2, 32, 3, 0>(g, s);
   return hipErrorInvalidValue;
 }
