@@ -10,7 +10,11 @@ there.
   python bench.py [--steps K] [--warmup W] [--workload mixtral|deepseek_decode|...] [--T n]
 
 Default workload: the Mixtral-8x7B-shaped prefill layer (T=4096, H=4096, I=14336, E=8,
-k=2, bf16), metric = useful TFLOPS = 2*T*k*3*H*I / step time.  Decode workloads report
+k=2, bf16), metric = useful TFLOPS = 2*T*k*3*H*I / step time.  The default run also
+carries, measured in the same process: `decode` (the DeepSeek-V3-shaped layer at T = 1,
+16 and 64: weight GB/s and fraction of HBM, stage times), `calibration` (a dense bf16 GEMM
+of the same total size through torch, the comparison point the pages name for prefill),
+and `cpu_baseline` (the oracle on the host cores, plus its timings on the tiny layer).  Decode workloads report
 weight GB/s = active experts * 3*H*I*2 B / step time (FP8 weights: 1 B per weight plus the
 active experts' fp32 row scales, (2I + H)*4 B each).
 """
@@ -38,6 +42,9 @@ def parse():
     ap.add_argument("--workload", default="mixtral")
     ap.add_argument("--T", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true",
+                    help="default Mixtral run: skip the DeepSeek decode sub-record and the "
+                         "dense-GEMM calibration")
     ap.add_argument("--eager", action="store_true",
                     help="time eager launches instead of HIP-graph replays of the step")
     ap.add_argument("--cpu-sample-tokens", type=int, default=None)
@@ -123,23 +130,64 @@ def cpu_baseline(wl, lay, sample_T):
         value, unit = flops / dt / 1e12, "TFLOPS"
     return {"value": value, "unit": unit, "cores": int(cores), "kind": "oracle",
             "sample": f"{sample_T} of {wl.T} tokens of the same layer (numpy float64 oracle, "
-                      f"route + per-expert loop), {dt:.2f} s"}
+                      f"route + per-expert loop), {dt:.2f} s",
+            "cpu_model": cpu_model(), "os_cpu_count": os.cpu_count(),
+            "threads_note": "cores = the BLAS threads numpy's matrix products ran on"}
 
 
-def main():
-    args = parse()
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU: this layer's benchmark runs on a single MI355X "
-              "(no sharding); run it with --gpus 1", file=sys.stderr)
-        sys.exit(2)
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
+
+def tiny_oracle_timings(reps=20):
+    """The oracle on the tiny fp32 layer (T=64, H=64, I=96, E=8, k=2): routing + per-expert
+    loop with all BLAS threads and with one, and the dense run-every-expert version."""
+    import numpy as np
+    from oracle import moe_oracle as O
+    from synth import inputs as S
+    wl = S.WORKLOADS["tiny"]
+    lay = S.make_layer(wl)
+    x = lay.x.double().numpy()
+    wg, w13, w2 = lay.wg.double().numpy(), lay.w13.double().numpy(), lay.w2.double().numpy()
+    logits32 = O.router_logits(x, wg).astype(np.float32)
+    ids, w = O.route(logits32, wl.k, wl.mode)
+
+    def best(fn):
+        ts = []
+        for _ in range(reps):
+            t0 = time.perf_counter()
+            fn()
+            ts.append(time.perf_counter() - t0)
+        return min(ts) * 1e3
+
+    out = {"loop_ms": best(lambda: O.moe_layer(x, wg, w13, w2, wl.k, wl.mode)),
+           "dense_ms": best(lambda: O.moe_dense(x, w13, w2, ids, w))}
+    try:
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(limits=1):
+            out["loop_1thread_ms"] = best(lambda: O.moe_layer(x, wg, w13, w2, wl.k, wl.mode))
+    except Exception:
+        out["loop_1thread_ms"] = None
+    out["note"] = "best of %d runs; loop includes routing, dense is the expert math alone" % reps
+    return out
+
+
+def measure(args, workload: str, T_override=None, with_cpu=True):
+    """Time one workload's layer step (and its stages); returns the JSON record."""
     import torch
     import mixture_experts_layer_27_amd as m
     from synth import inputs as S
 
-    wl = S.WORKLOADS[args.workload]
-    if args.T is not None:
-        wl = wl.with_T(args.T)
+    wl = S.WORKLOADS[workload]
+    if T_override is not None:
+        wl = wl.with_T(T_override)
     dev = "cuda"
     lay = S.make_layer(wl, device=dev, seed=0)
     T, H, I, E, k = wl.T, wl.H, wl.I, wl.E, wl.k
@@ -413,9 +461,78 @@ def main():
         rec["config"]["expert_parallel"] = {"degree": ep, "local_experts": int(w13.shape[0]),
                                             "held": "experts e with e % degree == 0",
                                             "value_counts": "local experts only"}
-    if not args.no_cpu_baseline and ep == 1:
+    if wl.offset == "hot8":
+        # share of the routed rows that the +3.0 logit offset sends to experts 0..7
+        rec["config"]["hot_block_share"] = float((ids[:, :k] < 8).float().mean())
+    if with_cpu and not args.no_cpu_baseline and ep == 1:
         st = args.cpu_sample_tokens or T
         rec["cpu_baseline"] = cpu_baseline(wl, lay, st)
+    del lay, xs, graphs
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return rec
+
+
+def dense_calibration(T, H, I, k, steps):
+    """The pages' comparison point for prefill: a dense bf16 GEMM of the same total size
+    (the T*k routed rows against one expert's weights), timed through torch (hipBLASLt)."""
+    import torch
+    R = T * k
+    g = torch.Generator(device="cuda").manual_seed(0)
+    out = {}
+    for name, (M, K, N) in (("gemm1", (R, H, 2 * I)), ("gemm2", (R, I, H))):
+        a = torch.randn(M, K, device="cuda", generator=g).to(torch.bfloat16)
+        w = (torch.randn(N, K, device="cuda", generator=g) / K ** 0.5).to(torch.bfloat16)
+        for _ in range(3):
+            torch.nn.functional.linear(a, w)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            torch.nn.functional.linear(a, w)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        out[name + "_ms"] = ms
+        out[name + "_tflops"] = 2 * M * K * N / (ms * 1e-3) / 1e12
+        del a, w
+    out["layer_gemms_ms"] = out["gemm1_ms"] + out["gemm2_ms"]
+    out["note"] = ("torch.nn.functional.linear (hipBLASLt) on dense bf16 [T*k, H] x [H, 2I] "
+                   "and [T*k, I] x [I, H]: the same total GEMM size as the layer's expert "
+                   "GEMMs, with no gather, padding or expert boundaries")
+    torch.cuda.empty_cache()
+    return out
+
+
+def decode_summary(rec):
+    """The figures of a decode record kept in the headline line's decode sub-record."""
+    c = rec["config"]
+    return {"T": c["T"], "weight_GBps": rec["value"], "frac_of_hbm": rec["value"] / PEAK_HBM_GBS,
+            "ms_per_step": rec["ms_per_step"], "active_experts": c.get("active_experts"),
+            "stages_ms": c["stages_ms"], "step_ms_p10_p50_p90": c["step_ms_p10_p50_p90"],
+            "gemm1_weight_GBps": rec["roofline"]["achieved"],
+            "gemm1_frac_of_hbm": rec["roofline"]["frac"]}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: this layer's benchmark runs on a single MI355X "
+              "(no sharding); run it with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    rec = measure(args, args.workload, args.T)
+    if args.workload == "mixtral" and args.T is None and args.block_m is None and args.ep == 1 \
+            and not args.no_decode:
+        # the second headline target, measured in the same run: DeepSeek-V3-shaped decode
+        c = rec["config"]
+        rec["calibration"] = dense_calibration(c["T"], c["H"], c["I"], c["k"], args.steps)
+        rec["decode"] = {"workload": "deepseek_decode (E=256, k=8, H=7168, I=2048, bf16, "
+                                     "sigmoid + bias grouped routing)"}
+        for T in (1, 16, 64):
+            rec["decode"][f"T{T}"] = decode_summary(measure(args, "deepseek_decode", T,
+                                                            with_cpu=False))
+        if "cpu_baseline" in rec:
+            rec["cpu_baseline"]["tiny_layer"] = tiny_oracle_timings()
     print(json.dumps(rec), flush=True)
 
 

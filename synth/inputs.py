@@ -19,6 +19,8 @@ Routing, Permutation, and Grouped GEMM", section 1):
 * ``deepseek_decode`` T in {1,16,64,256}, H=7168, I=2048, E=256, k=8, bf16,
                        sigmoid + selection bias ~ N(0, variance 0.1), 8 groups,
                        keep 4 groups, weights x2.5.
+* ``deepseek_decode_bias01``  the same with the selection bias drawn with standard
+                       deviation 0.1 (the other reading of "N(0, 0.1)").
 * ``gptoss``          T=16384, H=2880, I=2880, E=128, k=4, bf16, top-4 then softmax,
                        per-expert logit offset 0.5*ln(Zipf(s=1.2) rank weight).
 
@@ -96,6 +98,10 @@ WORKLOADS = {
     "deepseek_decode": Workload("deepseek_decode", 1, 7168, 2048, 256, 8, "bf16",
                                 ROUTE_SIGMOID_BIAS_GROUPED, n_group=8, topk_group=4,
                                 scaling=2.5, bias_std=math.sqrt(0.1)),
+    # the bias read as standard deviation 0.1 instead of variance 0.1 (secondary sweep)
+    "deepseek_decode_bias01": Workload("deepseek_decode_bias01", 1, 7168, 2048, 256, 8, "bf16",
+                                       ROUTE_SIGMOID_BIAS_GROUPED, n_group=8, topk_group=4,
+                                       scaling=2.5, bias_std=0.1),
     "gptoss": Workload("gptoss", 16384, 2880, 2880, 128, 4, "bf16",
                        ROUTE_TOPK_THEN_SOFTMAX, offset="zipf"),
     "deepseek_decode_fp8": Workload("deepseek_decode_fp8", 1, 7168, 2048, 256, 8, "bf16_fp8w",
