@@ -245,6 +245,19 @@ moe_status moe_layer(const void* x, const void* wg, const void* w13, const void*
                      const moe_route_cfg* cfg, int T, int H, int I, int E, int k, moe_dtype dt,
                      void* out, int32_t* topk_ids_out, float* topk_w_out, void* ws,
                      size_t ws_bytes, void* stream);
+/* moe_layer for callers that cannot allocate memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid it): the same launches, with the workspace taken
+ * from a static device array of the library (96 MiB per GPU, held until the process ends;
+ * enough for the DeepSeek-V3-shaped decode layer up to T = 256).  x, wg, w13, w2, out and
+ * the optional routing outputs are as for moe_layer (bf16 or fp32; no FP8 weights).
+ * Returns MOE_ERR_WORKSPACE, enqueuing nothing, when moe_layer_workspace_size(...) exceeds
+ * 96 MiB.  Calls no allocating routine.  Every call on one GPU uses that GPU's one array,
+ * so calls that overlap on a GPU (other streams, other threads) race; no kernel of the
+ * layer reads workspace it has not written in the same call, so nothing is cleared. */
+moe_status moe_layer_noalloc(const void* x, const void* wg, const void* w13, const void* w2,
+                             const moe_route_cfg* cfg, int T, int H, int I, int E, int k,
+                             moe_dtype dt, void* out, int32_t* topk_ids_out, float* topk_w_out,
+                             void* stream);
 /* moe_layer with FP8 expert weights: x, Wg and out bf16; w13/w2 E4M3 bytes with their
  * per-row scales (as for moe_forward_fp8).  ws: moe_layer_workspace_size(...,
  * MOE_BF16_FP8W) bytes. */

@@ -23,7 +23,7 @@ __all__ = [
     "moe_route", "moe_route_from_logits", "moe_align", "moe_align_capacity",
     "moe_gemm1_swiglu", "moe_gemm2_weighted", "moe_combine", "moe_forward", "moe_layer",
     "moe_gemm1_swiglu_fp8", "moe_gemm2_weighted_fp8", "moe_forward_fp8", "moe_layer_fp8",
-    "moe_align_ep", "moe_layer_ep", "moe_layer_shared",
+    "moe_align_ep", "moe_layer_ep", "moe_layer_shared", "moe_layer_noalloc",
     "moe_preferred_block_m", "moe_auto_variant", "moe_layer_workspace_size",
     "moe_forward_workspace_size", "moe_align_workspace_size", "moe_route_workspace_size",
     "route_cfg", "MoeError", "LIB_PATH",
@@ -252,6 +252,21 @@ def moe_layer(x, wg, w13, w2, k, cfg: RouteCfg, out=None, ws=None, topk_ids_out=
     check(lib.moe_layer(_p(x), _p(wg), _p(w13), _p(w2), ctypes.byref(cfg), T, H, I, E, k, _dt(x),
                         _p(out), _p(topk_ids_out), _p(topk_w_out), _p(ws), ws.numel(),
                         _stream()), "moe_layer")
+    return out
+
+
+def moe_layer_noalloc(x, wg, w13, w2, k, cfg: RouteCfg, out=None, topk_ids_out=None,
+                      topk_w_out=None):
+    """moe_layer with the workspace in the library's static device scratch (no workspace
+    argument; see the C declaration for the size limit)."""
+    T, H = x.shape
+    E, I2, _ = w13.shape
+    I = I2 // 2
+    if out is None:
+        out = torch.empty(T, H, dtype=x.dtype, device=x.device)
+    check(lib.moe_layer_noalloc(_p(x), _p(wg), _p(w13), _p(w2), ctypes.byref(cfg), T, H, I, E, k,
+                                _dt(x), _p(out), _p(topk_ids_out), _p(topk_w_out), _stream()),
+          "moe_layer_noalloc")
     return out
 
 

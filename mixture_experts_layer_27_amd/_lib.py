@@ -50,6 +50,7 @@ _SIGS = {
     "moe_layer_fp8": (_i, [_p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _p, _p, _p, _p, _sz,
                            _p]),
     "moe_layer": (_i, [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _p, _p, _p, _p, _sz, _p]),
+    "moe_layer_noalloc": (_i, [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _p, _p, _p, _p]),
     "moe_layer_shared_workspace_size": (_sz, [_i, _i, _i, _i, _i, _i]),
     "moe_layer_shared": (_i, [_p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _p, _p, _p, _p,
                               _sz, _p]),

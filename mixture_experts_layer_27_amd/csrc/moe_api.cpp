@@ -6,6 +6,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 
 #include "../../include/moe_mi355x.h"
@@ -649,6 +650,64 @@ moe_status moe_layer_ep(const void* x, const void* wg, const void* w13, const fl
   if (!expert_map) return fail(MOE_ERR_INVALID_ARG, "expert_map is NULL");
   return layer_impl(x, wg, w13, w13_scale, w2, w2_scale, expert_map, cfg, T, H, I, E, k, dt, out,
                     topk_ids_out, topk_w_out, ws, ws_bytes, stream);
+}
+
+}  // extern "C"
+
+// ------------------------------------------------------------------ allocation-free layer
+// The workspace of moe_layer_noalloc: a device array of the library, one per GPU (each
+// device that runs the entry point holds its copy until the process ends).  Its name is
+// a host-side stand-in; the device address of the current device's copy comes from
+// hipGetSymbolAddress, taken once per device on that device's first call.
+constexpr size_t kNoallocScratchBytes = static_cast<size_t>(96) << 20;
+static __device__ __align__(256) uint8_t scratch[kNoallocScratchBytes];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+moe_status scratch_of_current_device(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(MOE_ERR_UNSUPPORTED, "device %d", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e, "hipGetSymbolAddress(scratch)");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status moe_layer_noalloc(const void* x, const void* wg, const void* w13, const void* w2,
+                             const moe_route_cfg* cfg, int T, int H, int I, int E, int k,
+                             moe_dtype dt, void* out, int32_t* topk_ids_out, float* topk_w_out,
+                             void* stream) {
+  if (dt == MOE_BF16_FP8W)
+    return fail(MOE_ERR_UNSUPPORTED, "moe_layer_noalloc takes bf16 or fp32 expert weights");
+  const size_t need = moe_layer_workspace_size(T, H, I, E, k, dt);
+  if (T > 0 && need == 0) return fail(MOE_ERR_INVALID_ARG, "invalid sizes or dtype");
+  if (need > kNoallocScratchBytes)
+    return fail(MOE_ERR_WORKSPACE,
+                "moe_layer_noalloc: this layer needs %zu bytes of workspace, above the %zu-byte "
+                "static scratch (use moe_layer with a caller workspace)",
+                need, kNoallocScratchBytes);
+  void* ws = nullptr;
+  if (T > 0) {
+    const moe_status st = scratch_of_current_device(&ws);
+    if (st != MOE_OK) return st;
+  }
+  return layer_impl(x, wg, w13, nullptr, w2, nullptr, nullptr, cfg, T, H, I, E, k, dt, out,
+                    topk_ids_out, topk_w_out, ws, kNoallocScratchBytes, stream);
 }
 
 }  // extern "C"

@@ -243,3 +243,18 @@ def test_shared_expert_layer_validates(L):
     big = lib.moe_layer_shared_workspace_size(4, 256, 256, 512, 8, 1)
     assert lib.moe_layer_shared(FAKE, FAKE, FAKE, None, FAKE, None, ctypes.byref(cfg(L)), 4, 256,
                                 256, 512, 8, 1, FAKE, None, None, FAKE, big, None) == UNSUPPORTED
+
+
+def test_noalloc_layer_rejects_on_the_host(L):
+    """moe_layer_noalloc: a layer whose workspace exceeds the static scratch, FP8 weights and
+    invalid sizes fail before anything touches the device."""
+    lib = L.lib
+    c = cfg(L)
+    # Mixtral-shaped prefill at T=4096: a [8192, 14336] bf16 + y [8192, 4096] fp32 >> 96 MiB
+    assert lib.moe_layer_noalloc(FAKE, FAKE, FAKE, FAKE, ctypes.byref(c), 4096, 4096, 14336, 8,
+                                 2, 1, FAKE, None, None, None) == WORKSPACE
+    assert b"static scratch" in lib.moe_last_error()
+    assert lib.moe_layer_noalloc(FAKE, FAKE, FAKE, FAKE, ctypes.byref(c), 4, 256, 256, 8, 2, 2,
+                                 FAKE, None, None, None) == UNSUPPORTED
+    assert lib.moe_layer_noalloc(FAKE, FAKE, FAKE, FAKE, ctypes.byref(c), 4, 256, 256, 8, 0, 1,
+                                 FAKE, None, None, None) == INVALID
