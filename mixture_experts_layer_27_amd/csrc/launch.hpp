@@ -25,6 +25,11 @@ hipError_t launch_router_logits(const void* x, const void* wg, int T, int H, int
 // logits_out (nullable) receives the summed logits when nz > 1; ids / w are [T][k + a.shared]
 hipError_t launch_topk(const float* logits, int nz, float* logits_out, int T, int E, int k,
                        const RouteArgs& a, int32_t* ids, float* w, hipStream_t s);
+// prefill with up to 32 experts: logits and top-k in one launch (16 tokens per work-group)
+bool route_fused_ok(int T, int H, int E, bool bf16);
+hipError_t launch_route_fused(const void* x, const void* wg, int T, int H, int E, int k,
+                              const RouteArgs& a, int32_t* ids, float* w, float* logits_out,
+                              hipStream_t s);
 // top-k of every token and the align table in one single-work-group launch (k routed
 // slots over E experts, plus the shared slot when shared = 1)
 bool route_align_fusable(int T, int k, int E, int shared);

@@ -235,6 +235,10 @@ moe_status moe_route(const void* x, const void* wg, int T, int H, int E, int k, 
   float* slabs = static_cast<float*>(ws);
   const int nz = moe::router_slabs(T, H, dt == MOE_BF16);
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (moe::route_fused_ok(T, H, E, dt == MOE_BF16))   // prefill: logits and top-k in one launch
+    return hip_status(moe::launch_route_fused(x, wg, T, H, E, k, route_args(cfg), topk_ids, topk_w,
+                                              logits_out, s),
+                      "router");
   hipError_t e = moe::launch_router_logits(x, wg, T, H, E, dt == MOE_BF16, slabs, s);
   if (e != hipSuccess) return hip_status(e, "router logits");
   e = moe::launch_topk(slabs, nz, logits_out, T, E, k, route_args(cfg), topk_ids, topk_w, s);
@@ -585,10 +589,22 @@ moe_status layer_impl(const void* x, const void* wg, const void* w13, const floa
   int32_t* ntpp = reinterpret_cast<int32_t*>(b + p.off_ntpp);
   int32_t* counts = reinterpret_cast<int32_t*>(b + p.off_counts);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = moe::launch_router_logits(x, wg, T, H, E, bf16_acts(dt), logits, s);
-  if (e != hipSuccess) return hip_status(e, "router logits");
   moe::RouteArgs ra = route_args(cfg);
   ra.shared = shared;
+  hipError_t e = hipSuccess;
+  if (!p.fused_route_align && moe::route_fused_ok(T, H, E, bf16_acts(dt))) {
+    // prefill: logits and top-k in one launch, then the align table
+    e = moe::launch_route_fused(x, wg, T, H, E, k, ra, ids, tw, nullptr, s);
+    if (e != hipSuccess) return hip_status(e, "router");
+    e = moe::launch_align(ids, T * KS, ES, p.bm, p.cap, sorted, eids, ntpp, counts,
+                          reinterpret_cast<int32_t*>(b + p.off_align), expert_map, s);
+    if (e != hipSuccess) return hip_status(e, "align");
+    return forward_impl(x, w13, w13_scale, w2, w2_scale, tw, sorted, eids, ntpp, T, H, I, ES, KS,
+                        p.bm, dt, MOE_VARIANT_AUTO, out, b + p.off_fwd,
+                        forward_ws_full(T, H, I, ES, KS, dt), stream);
+  }
+  e = moe::launch_router_logits(x, wg, T, H, E, bf16_acts(dt), logits, s);
+  if (e != hipSuccess) return hip_status(e, "router logits");
   if (p.fused_route_align) {
     e = moe::launch_route_align_small(logits, p.nz, nullptr, T, E, k, ra, ids, tw, p.bm, p.cap,
                                       sorted, eids, ntpp, counts, expert_map, s);

@@ -231,7 +231,9 @@ __device__ __forceinline__ float sigmoid_rn(float l) {
 }
 
 struct TopkParams {
-  const float* logits;     // nz slabs of [T][E] (nz == 1: the logits themselves)
+  const float* logits;     // nz slabs of [T][E] (nz == 1: the logits themselves); row t of
+                           // a slab is token t0 + t
+  int t0;
   int nz;
   float* logits_out;       // [T][E] or null: receives the summed logits (nz > 1)
   int T, E, k, mode;
@@ -260,7 +262,7 @@ __device__ void topk_token(const TopkParams& p, int t, TopkLds& sh, int32_t* ids
   // every load first, at clamped indices, so that all of them are in flight together;
   // slabs are added in ascending order
   float lv[NSLOT], ov[NSLOT], bv[NSLOT];
-  const float* lrow = p.logits + static_cast<int64_t>(t) * E;
+  const float* lrow = p.logits + static_cast<int64_t>(t - p.t0) * E;
   const int64_t slab = static_cast<int64_t>(p.T) * E;
 #pragma unroll
   for (int i = 0; i < NSLOT; ++i) {
@@ -475,6 +477,78 @@ route_align_small_kernel(TopkParams p, int bm, int64_t cap, int32_t* __restrict_
                            expert_ids, ntpp, counts, emap);
 }
 
+// Prefill with few experts (E <= 32), one launch: a work-group of 16 waves routes 16
+// tokens.  The 16 x E logits are computed with MFMA 16x16x32 (operands read from global
+// memory in MFMA register layout, as in router_logits_bf16_kernel): each wave takes a
+// (16-expert block, K slice) pair, KS = 16 / blocks slices per block, and the KS partial
+// sums of a block are added in slice order through LDS.  The logits stay in LDS and each
+// wave then routes one token with the same per-token selection as topk_kernel.  With many
+// experts the gate matrix a work-group reads would outgrow the 16 tokens' activations
+// (at E = 128 eight times over), so those keep the two-launch path.
+template <int KS>
+__global__ void __launch_bounds__(1024)
+route_fused_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ wg, int H,
+                   TopkParams p) {
+  constexpr int kSlots = 4;                        // topk_token's slots per lane (E <= 256)
+  __shared__ TopkLds sh[16];
+  __shared__ float lg[16 * 32];
+  __shared__ f32x4 red[16][kWave];
+  const int lane = lane_id(), w = __builtin_amdgcn_readfirstlane(wave_id());
+  const int T = p.T, E = p.E;
+  const int t0 = blockIdx.x * 16;
+  const int row = lane & 15, grp = lane >> 4;
+  const uint16_t* xa = x + static_cast<int64_t>(min(t0 + row, T - 1)) * H + grp * 8;
+  const int blk = w / KS, ks = w % KS;
+  const uint16_t* wb = wg + static_cast<int64_t>(min(blk * 16 + row, E - 1)) * H + grp * 8;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  // this wave's 64-element chunks k0 = ks*64 + c*64*KS, c < nc; the operands of D chunks
+  // are in flight at once (the first window may load the last chunk again in place of
+  // chunks past the end; those are not used)
+  constexpr int D = 4;
+  const int nc = (H / 64 - ks + KS - 1) / KS;
+  const int klast = H - 64;
+  bf16x8 fa[D][2], fb[D][2];
+  auto load = [&](int d, int c) {
+    const int k0 = min(ks * 64 + c * 64 * KS, klast);
+    fa[d][0] = *reinterpret_cast<const bf16x8*>(xa + k0);
+    fa[d][1] = *reinterpret_cast<const bf16x8*>(xa + k0 + 32);
+    fb[d][0] = *reinterpret_cast<const bf16x8*>(wb + k0);
+    fb[d][1] = *reinterpret_cast<const bf16x8*>(wb + k0 + 32);
+  };
+#pragma unroll
+  for (int d = 0; d < D; ++d) load(d, d);
+  for (int c = 0; c < nc; c += D) {                // nc is wave-uniform: no masked MFMA
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      if (c + d < nc) {
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[d][0], fb[d][0], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[d][1], fb[d][1], acc, 0, 0, 0);
+      }
+      if (c + d + D < nc) load(d, c + d + D);
+    }
+  }
+  red[w][lane] = acc;
+  __syncthreads();
+  // D layout (16x16): lane holds column (lane & 15) = expert, rows 4*(lane>>4)+v = tokens
+  if (ks == 0) {
+    for (int q = 1; q < KS; ++q) {
+      const f32x4 o = red[w + q][lane];
+      acc[0] += o[0]; acc[1] += o[1]; acc[2] += o[2]; acc[3] += o[3];
+    }
+    const int ec = blk * 16 + (lane & 15);
+    if (ec < E)
+      for (int v = 0; v < 4; ++v) lg[(4 * (lane >> 4) + v) * E + ec] = acc[v];
+  }
+  __syncthreads();
+  if (t0 + w < T) {
+    TopkParams q = p;
+    q.logits = lg;
+    q.t0 = t0;
+    q.nz = 1;
+    topk_token<kSlots, 1>(q, t0 + w, sh[w], nullptr);
+  }
+}
+
 // K slabs of the bf16 logits: at decode batch sizes enough work-groups to stream Wg
 // from many CUs, each slab a multiple of 256 columns (64 per wave).
 int slab_cols(int T, int H) {
@@ -488,6 +562,7 @@ TopkParams topk_params(const float* logits, int nz, float* logits_out, int T, in
                        const RouteArgs& a, int32_t* ids, float* w) {
   TopkParams p;
   p.logits = logits;
+  p.t0 = 0;
   p.nz = nz;
   p.logits_out = logits_out;
   p.T = T;
@@ -558,6 +633,27 @@ hipError_t launch_topk(const float* logits, int nz, float* logits_out, int T, in
     hipLaunchKernelGGL(topk_kernel<4>, dim3((T + 3) / 4), dim3(256), 0, s, p);
   else
     hipLaunchKernelGGL(topk_kernel<8>, dim3((T + 3) / 4), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+bool route_fused_ok(int T, int H, int E, bool bf16) {
+  return bf16 && T > 64 && H % 64 == 0 && E <= 32;
+}
+
+hipError_t launch_route_fused(const void* x, const void* wg, int T, int H, int E, int k,
+                              const RouteArgs& a, int32_t* ids, float* w, float* logits_out,
+                              hipStream_t s) {
+  const TopkParams p = topk_params(nullptr, 1, logits_out, T, E, k, a, ids, w);
+  const dim3 grid(static_cast<unsigned>((T + 15) / 16));
+  const uint16_t* xb = static_cast<const uint16_t*>(x);
+  const uint16_t* wb = static_cast<const uint16_t*>(wg);
+  // 16 waves over (expert block, K slice) pairs, 16 / blocks slices per block
+  if (E <= 16)
+    hipLaunchKernelGGL(route_fused_kernel<16>, grid, dim3(1024), 0, s, xb, wb, H, p);
+  else if (E <= 32)
+    hipLaunchKernelGGL(route_fused_kernel<8>, grid, dim3(1024), 0, s, xb, wb, H, p);
+  else
+    return hipErrorInvalidValue;
   return hipGetLastError();
 }
 

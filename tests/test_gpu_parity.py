@@ -148,7 +148,12 @@ def test_route_grouped_page_example(lib):
                                           (16, 7168 // 4, 256, 8, 2), (1, 2048, 256, 8, 2),
                                           (200, 2880, 128, 4, 1),
                                           # few experts: K split over the waves of a block
-                                          (100, 640, 24, 4, 0), (90, 320, 16, 2, 1)])
+                                          (100, 640, 24, 4, 0), (90, 320, 16, 2, 1),
+                                          # prefill sizes: one launch up to 32 experts
+                                          # (16-token work-groups), two beyond
+                                          (4100, 4096, 8, 2, 0), (4111, 1024, 32, 4, 1),
+                                          (4096, 256, 128, 8, 0), (4100, 192, 512, 16, 1),
+                                          (4099, 448, 256, 8, 2), (4096, 2880, 128, 4, 1)])
 def test_route_fused_logits(lib, T, H, E, k, mode):
     """moe_route: fp32-accumulated logits within their error bound of the float64 ones;
     ids identical to the oracle's on every token whose selection margin exceeds twice that
