@@ -29,6 +29,7 @@
 #include "common.hpp"
 #include "dma.hpp"
 #include "launch.hpp"
+#include "route_dev.hpp"
 
 namespace moe {
 
@@ -109,14 +110,18 @@ __device__ __forceinline__ void fp8x16_to_bf16(const u32x4 q, bf16x8& lo, bf16x8
   hi = bf16x8{p[4][0], p[4][1], p[5][0], p[5][1], p[6][0], p[6][1], p[7][0], p[7][1]};
 }
 
-// DMA sources of one work item: RB weight rows of one expert and the SUB = 16*NTG
-// token rows of one sub-tile
-template <int MODE, int RB, int NTG, int STEP, bool NT, int WB>
+// DMA sources of one work item: RB weight rows of one expert and the first XR of the
+// SUB = 16*NTG token rows of one sub-tile.  XR < SUB when no expert can hold more than
+// XR routed rows (T <= XR: top-k experts are distinct, so an expert holds at most one
+// row per token, at the head of its table tile); the MFMA columns of the rows past XR
+// then read rows of the XR (their results are padding and never stored).
+template <int MODE, int RB, int NTG, int STEP, bool NT, int WB, int XR>
 struct Stream {
   using S = DStep<STEP, WB>;
   static constexpr int SUB = 16 * NTG;
   static constexpr int NW = RB / S::WRPI;       // weight DMAs per step
-  static constexpr int NX = SUB / S::XRPI;      // token-row DMAs per step
+  static constexpr int NX = XR / S::XRPI;       // token-row DMAs per step
+  static_assert(XR % S::XRPI == 0 && XR <= SUB && (XR == SUB || NTG == 1), "token rows");
 
   // per-lane sources of an item's DMAs at k offset 0
   // item = (sub-tile of the align table, weight-row block blk); idsv: its routed row ids
@@ -277,6 +282,63 @@ __device__ __forceinline__ void zero_range(const DArgs& p, const int32_t* __rest
   }
 }
 
+// Single-token decode with the routing folded into GEMM1 (ROUTE).  Every wave selects
+// the token's experts itself (rdev::topk_select on the router's logit slabs) and ranks
+// them by expert index, so that sub-tile u holds the one row of the u-th smallest selected
+// expert: the table moe_align builds for these rows with block_m = 16, known to each wave
+// without a launch in between.  Work-group 0 also writes the routing (ids, weights) and
+// that table for GEMM2.  Ids outside [0, ES) (only where fewer than k experts are
+// eligible) get no sub-tile, as in moe_align.
+struct DRoute {
+  rdev::TopkParams tp;     // T = 1; tp.ids / tp.w: the k + shared slots
+  int32_t* sorted_ids;     // [cap]
+  int32_t* expert_ids;     // [cap / 16]
+  int32_t* ntpp;
+  int32_t* counts;         // [ES] or null
+  int ES;                  // experts of the table (E + shared)
+  int cap;                 // 16 * (k + shared)
+};
+
+// lane u < nvalid returns sub-tile u's expert (e_sorted) and row (j_sorted)
+__device__ __forceinline__ void route_single_token(const DRoute& r, rdev::TopkLds& tsh,
+                                                   bool writer, int& e_sorted, int& j_sorted,
+                                                   int& nvalid) {
+  const int lane = lane_id();
+  int id;
+  float w;
+  rdev::topk_select<4, 15>(r.tp, 0, tsh, id, w);
+  const int K1 = r.tp.k + r.tp.shared;
+  const bool valid = lane < K1 && static_cast<unsigned>(id) < static_cast<unsigned>(r.ES);
+  const uint64_t vm = __ballot(valid);
+  nvalid = __popcll(vm);
+  // the selected experts are distinct: rank = number of smaller valid ones
+  int rank = 0;
+  for (int i = 0; i < K1; ++i) rank += (((vm >> i) & 1) && read_lane(id, i) < id) ? 1 : 0;
+  const int dst = valid ? rank : kWave - 1;       // K1 < 64: lane 63 takes the rest
+  e_sorted = __builtin_amdgcn_ds_permute(dst * 4, id);
+  j_sorted = __builtin_amdgcn_ds_permute(dst * 4, lane);
+  if (!writer) return;
+  if (lane < K1) {
+    r.tp.ids[lane] = id;
+    r.tp.w[lane] = w;
+  }
+  // sorted_ids: the first entry of tile u is its row, the rest the sentinel K1
+  for (int q0 = 0; q0 < r.cap; q0 += kWave) {
+    const int q = q0 + lane, u = min(q >> 4, kWave - 1);
+    const int ju = __shfl(j_sorted, u, kWave);
+    if (q < r.cap) r.sorted_ids[q] = ((q & 15) == 0 && u < nvalid) ? ju : K1;
+  }
+  if (lane < (r.cap >> 4)) r.expert_ids[lane] = lane < nvalid ? e_sorted : -1;
+  if (lane == 0) *r.ntpp = 16 * nvalid;
+  if (r.counts) {
+    for (int e = lane; e < r.ES; e += kWave) {
+      int c = 0;
+      for (int i = 0; i < K1; ++i) c += (((vm >> i) & 1) && read_lane(id, i) == e) ? 1 : 0;
+      r.counts[e] = c;
+    }
+  }
+}
+
 // The routing tables are separate __restrict__ arguments: with them the compiler may
 // read the (wave-uniform) entries with scalar loads, which count on lgkmcnt and leave
 // the vmcnt accounting of the DMA ring untouched.
@@ -292,20 +354,23 @@ __device__ __forceinline__ void zero_range(const DArgs& p, const int32_t* __rest
 // its epilogue, and the next item's ids and owner are loaded one item ahead, so the item
 // boundaries of the DMA stream and the epilogues do not wait on the routing tables (the
 // FP8 epilogue still loads its row scales).
-template <int MODE, int RB, int NTG, int STEP, int P, bool NT, int WB, bool CACHED>
+template <int MODE, int RB, int NTG, int STEP, int P, bool NT, int WB, bool CACHED, int XR,
+          bool ROUTE = false>
 __global__ void __launch_bounds__(64)
 moe_decode_kernel(DArgs p, const int32_t* __restrict__ sorted_ids,
                   const int32_t* __restrict__ expert_ids, const int32_t* __restrict__ ntpp,
-                  const float* __restrict__ topk_w, const float* __restrict__ wscale) {
+                  const float* __restrict__ topk_w, const float* __restrict__ wscale,
+                  DRoute rt) {
   using S = DStep<STEP, WB>;
-  using St = Stream<MODE, RB, NTG, STEP, NT, WB>;
+  using St = Stream<MODE, RB, NTG, STEP, NT, WB, XR>;
   constexpr int SUB = St::SUB;
   constexpr int NF = RB / 16;                   // 16-row weight fragments per item
   constexpr int NI = St::NW + St::NX;           // DMAs per step
-  constexpr int SLOT = RB * S::WROWB + SUB * S::XROWB;
+  constexpr int SLOT = RB * S::WROWB + XR * S::XROWB;
   static_assert(RB <= kWave, "one scale per lane");
   static_assert(P >= 3 && (P - 2) * NI < 64, "ring depth");
   static_assert(MODE != 1 || NF % 2 == 0, "gate/up fragment pairs");
+  static_assert(!ROUTE || (MODE == 1 && NTG == 1), "routing folds into single-token GEMM1");
   __shared__ __attribute__((aligned(1024))) uint8_t ring[P * SLOT];
 
   const int lane = lane_id();
@@ -314,11 +379,25 @@ moe_decode_kernel(DArgs p, const int32_t* __restrict__ sorted_ids,
   // (per-lane vector loads: no DMA is in flight yet, so their waits cost nothing, and the
   // compiler keeps them in one batch with the owner loads)
   const int u0 = min(first / p.nblk, p.nsub_cap - 1);
-  const int ids0v = sorted_ids[static_cast<int64_t>(u0) * SUB + min(lane, SUB - 1)];
-  const int e0v = expert_ids[(u0 * SUB) >> p.bm_shift];
-  const int totalv = *ntpp;
-  const LocalSubtiles lt = local_subtiles<SUB>(expert_ids, p.nsub_cap, totalv / SUB, p.bm_shift);
-  const int nsub = read_lane(totalv, 0) / SUB;
+  int ids0v, e0v, nsub;
+  LocalSubtiles lt;
+  int re_sorted = 0, rj_sorted = 0;             // ROUTE: sub-tile (lane) -> expert, row
+  if constexpr (ROUTE) {
+    __shared__ rdev::TopkLds tsh;
+    int nvalid;
+    route_single_token(rt, tsh, first == 0, re_sorted, rj_sorted, nvalid);
+    const int j0 = __shfl(rj_sorted, u0, kWave);
+    ids0v = lane == 0 ? j0 : p.R;
+    e0v = __shfl(re_sorted, u0, kWave);
+    nsub = nvalid;
+    lt.count = nsub;
+  } else {
+    ids0v = sorted_ids[static_cast<int64_t>(u0) * SUB + min(lane, SUB - 1)];
+    e0v = expert_ids[(u0 * SUB) >> p.bm_shift];
+    const int totalv = *ntpp;
+    lt = local_subtiles<SUB>(expert_ids, p.nsub_cap, totalv / SUB, p.bm_shift);
+    nsub = read_lane(totalv, 0) / SUB;
+  }
   if (nsub == 0) return;
   const int nitems = lt.count * p.nblk;         // items of local sub-tiles
   const bool all_local = lt.count == nsub;
@@ -350,7 +429,20 @@ moe_decode_kernel(DArgs p, const int32_t* __restrict__ sorted_ids,
     blk = j - q * p.nblk;
     u = all_local ? q : local_subtile(lt, q);
   };
-  auto owner = [&](int u) { return expert_ids[(u * SUB) >> p.bm_shift]; };
+  auto owner = [&](int u) {
+    if constexpr (ROUTE) return read_lane(re_sorted, u);
+    else return expert_ids[(u * SUB) >> p.bm_shift];
+  };
+  // the SUB routed rows of sub-tile u
+  auto fetch_ids = [&](int u, int (&ids)[SUB]) {
+    if constexpr (ROUTE) {
+      ids[0] = read_lane(rj_sorted, u);
+#pragma unroll
+      for (int t = 1; t < SUB; ++t) ids[t] = p.R;
+    } else {
+      load_ids<SUB>(sorted_ids, u, ids);
+    }
+  };
 
   // issue item: routing ids (in lanes), block, expert
   int iidsv, ib, ie;
@@ -363,7 +455,7 @@ moe_decode_kernel(DArgs p, const int32_t* __restrict__ sorted_ids,
     item_at(first, iu, ib);
     ie = owner(iu);
     int ids[SUB];
-    load_ids<SUB>(sorted_ids, iu, ids);
+    fetch_ids(iu, ids);
     iidsv = spread(ids);
   }
   // CACHED: the next issue item (loaded one item ahead), the issue item's ids held in
@@ -376,7 +468,7 @@ moe_decode_kernel(DArgs p, const int32_t* __restrict__ sorted_ids,
       int nu;
       item_at(j, nu, nb);
       ne = owner(nu);
-      load_ids<SUB>(sorted_ids, nu, nids);
+      fetch_ids(nu, nids);
     }
   };
   // GEMM2: the router weights of the issue item's rows (uniform loads)
@@ -419,7 +511,7 @@ moe_decode_kernel(DArgs p, const int32_t* __restrict__ sorted_ids,
         item_at(iss_item, iu, ib);
         ie = owner(iu);
         int ids[SUB];
-        load_ids<SUB>(sorted_ids, iu, ids);
+        fetch_ids(iu, ids);
         iidsv = spread(ids);
         St::setup(p, iidsv, ib, ie, wp, xp);
       }
@@ -439,6 +531,7 @@ moe_decode_kernel(DArgs p, const int32_t* __restrict__ sorted_ids,
   f32x4 acc[NTG][NF];
   int cs = 0, cmp_item = first;
   const int tr = lane & 15;
+  const int xrow = XR < 16 ? (tr & (XR - 1)) : tr;   // token row the lane's column reads
   for (int g = 0; g < gtot; ++g) {
     wait_vm_c<(P - 2) * NI>();                  // step g's batch has landed in LDS
     asm volatile("" ::: "memory");
@@ -458,8 +551,8 @@ moe_decode_kernel(DArgs p, const int32_t* __restrict__ sorted_ids,
         bf16x8 b[NTG];
 #pragma unroll
         for (int q = 0; q < NTG; ++q)
-          b[q] = *reinterpret_cast<const bf16x8*>(xs + (16 * q + tr) * S::XROWB +
-                                                  dsw<S::XCPR>(tr, c) * 16);
+          b[q] = *reinterpret_cast<const bf16x8*>(xs + (16 * q + xrow) * S::XROWB +
+                                                  dsw<S::XCPR>(xrow, c) * 16);
 #pragma unroll
         for (int f = 0; f < NF; ++f) {
           const int row = 16 * f + tr;
@@ -483,9 +576,9 @@ moe_decode_kernel(DArgs p, const int32_t* __restrict__ sorted_ids,
         bf16x8 b0[NTG], b1[NTG];
 #pragma unroll
         for (int q = 0; q < NTG; ++q) {
-          const uint8_t* xr = xs + (16 * q + tr) * S::XROWB;
-          b0[q] = *reinterpret_cast<const bf16x8*>(xr + dsw<S::XCPR>(tr, cx) * 16);
-          b1[q] = *reinterpret_cast<const bf16x8*>(xr + dsw<S::XCPR>(tr, cx + 1) * 16);
+          const uint8_t* xr = xs + (16 * q + xrow) * S::XROWB;
+          b0[q] = *reinterpret_cast<const bf16x8*>(xr + dsw<S::XCPR>(xrow, cx) * 16);
+          b1[q] = *reinterpret_cast<const bf16x8*>(xr + dsw<S::XCPR>(xrow, cx + 1) * 16);
         }
 #pragma unroll
         for (int f = 0; f < NF; ++f) {
@@ -517,7 +610,7 @@ moe_decode_kernel(DArgs p, const int32_t* __restrict__ sorted_ids,
         item_at(cmp_item, u, blk);
         cmp_e = owner(u);
         int ids[SUB];
-        load_ids<SUB>(sorted_ids, u, ids);
+        fetch_ids(u, ids);
         idsv = spread(ids);
         if (MODE == 2) {
           int wts[SUB];                         // router weights (uniform loads)
@@ -614,25 +707,54 @@ int decode_ntg(int block_m, int R, int E) {
   return std::min(want, block_m / 16);
 }
 
-template <int MODE, int NTG, int STEP, bool NT, int WB, int P, int RB = kDecodeRB>
-hipError_t launch_decode(const DArgs& p0, const GemmArgs& g, hipStream_t s) {
+template <int MODE, int NTG, int STEP, bool NT, int WB, int P, int RB, int XR>
+hipError_t launch_decode_x(const DArgs& p0, const GemmArgs& g, hipStream_t s, const DRoute* rt) {
   using S = DStep<STEP, WB>;
   DArgs p = p0;
   p.nblk = (MODE == 1 ? 2 * p.I : p.H) / RB;
-  constexpr int kLds = P * (RB * S::WROWB + 16 * NTG * S::XROWB);
+  constexpr int kLds = P * (RB * S::WROWB + XR * S::XROWB);
   constexpr int kPerCU = std::max(1, (160 * 1024) / kLds);
   p.nsub_cap = static_cast<int>(g.cap / (16 * NTG));
   p.bm_shift = __builtin_ctz(static_cast<unsigned>(p.block_m));   // block_m: a power of two
   if (p.nsub_cap == 0) return hipSuccess;
   const int64_t max_items = static_cast<int64_t>(p.nsub_cap) * p.nblk;
   const unsigned grid = static_cast<unsigned>(std::min<int64_t>(max_items, 256 * kPerCU));
+  if constexpr (MODE == 1 && NTG == 1 && NT && XR < 16) {
+    if (rt) {
+      if (p.K / STEP >= P)
+        hipLaunchKernelGGL((moe_decode_kernel<MODE, RB, NTG, STEP, P, NT, WB, true, XR, true>),
+                           dim3(grid), dim3(64), 0, s, p, g.sorted_ids, g.expert_ids, g.ntpp,
+                           g.topk_w, g.w_scale, *rt);
+      else
+        hipLaunchKernelGGL((moe_decode_kernel<MODE, RB, NTG, STEP, P, NT, WB, false, XR, true>),
+                           dim3(grid), dim3(64), 0, s, p, g.sorted_ids, g.expert_ids, g.ntpp,
+                           g.topk_w, g.w_scale, *rt);
+      return hipGetLastError();
+    }
+  }
+  if (rt) return hipErrorInvalidValue;          // routing folds into single-token GEMM1 only
+  const DRoute none{};
   if (p.K / STEP >= P)
-    hipLaunchKernelGGL((moe_decode_kernel<MODE, RB, NTG, STEP, P, NT, WB, true>), dim3(grid),
-                       dim3(64), 0, s, p, g.sorted_ids, g.expert_ids, g.ntpp, g.topk_w, g.w_scale);
+    hipLaunchKernelGGL((moe_decode_kernel<MODE, RB, NTG, STEP, P, NT, WB, true, XR>),
+                       dim3(grid), dim3(64), 0, s, p, g.sorted_ids, g.expert_ids, g.ntpp,
+                       g.topk_w, g.w_scale, none);
   else
-    hipLaunchKernelGGL((moe_decode_kernel<MODE, RB, NTG, STEP, P, NT, WB, false>), dim3(grid),
-                       dim3(64), 0, s, p, g.sorted_ids, g.expert_ids, g.ntpp, g.topk_w, g.w_scale);
+    hipLaunchKernelGGL((moe_decode_kernel<MODE, RB, NTG, STEP, P, NT, WB, false, XR>),
+                       dim3(grid), dim3(64), 0, s, p, g.sorted_ids, g.expert_ids, g.ntpp,
+                       g.topk_w, g.w_scale, none);
   return hipGetLastError();
+}
+
+// token rows per sub-tile that are streamed: one DMA's worth when no expert holds more
+// rows than that (16-row sub-tiles only), else all of them
+template <int MODE, int NTG, int STEP, bool NT, int WB, int P, int RB = kDecodeRB,
+          int PF = P, int RBF = RB>
+hipError_t launch_decode(const DArgs& p, const GemmArgs& g, hipStream_t s, const DRoute* rt) {
+  constexpr int XRPI = DStep<STEP, WB>::XRPI;
+  const int64_t bound = g.max_rows > 0 ? g.max_rows : static_cast<int64_t>(g.T) * g.k;
+  if constexpr (NTG == 1)
+    if (bound <= XRPI) return launch_decode_x<MODE, NTG, STEP, NT, WB, PF, RBF, XRPI>(p, g, s, rt);
+  return launch_decode_x<MODE, NTG, STEP, NT, WB, P, RB, 16 * NTG>(p, g, s, rt);
 }
 
 // bf16 weights, 128-element steps (K % 128 != 0: 64).  GEMM1 with 16-row sub-tiles:
@@ -642,10 +764,11 @@ hipError_t launch_decode(const DArgs& p0, const GemmArgs& g, hipStream_t s) {
 // for 512 waves).  GEMM2 measured no better that way and keeps 64-row items; 32-row
 // sub-tiles keep 64-row items and a 3-slot ring.
 template <int MODE, int NTG, bool NT>
-hipError_t launch_decode_bf16(const DArgs& p, const GemmArgs& g, hipStream_t s) {
-  if (p.K % 128 != 0) return launch_decode<MODE, NTG, 64, NT, 2, NTG == 1 ? 4 : 3>(p, g, s);
-  if constexpr (NTG == 1 && MODE == 1) return launch_decode<MODE, NTG, 128, NT, 2, 6, 32>(p, g, s);
-  else return launch_decode<MODE, NTG, 128, NT, 2, NTG == 1 ? 4 : 3>(p, g, s);
+hipError_t launch_decode_bf16(const DArgs& p, const GemmArgs& g, hipStream_t s,
+                              const DRoute* rt) {
+  if (p.K % 128 != 0) return launch_decode<MODE, NTG, 64, NT, 2, NTG == 1 ? 4 : 3>(p, g, s, rt);
+  if constexpr (NTG == 1 && MODE == 1) return launch_decode<MODE, NTG, 128, NT, 2, 6, 32>(p, g, s, rt);
+  else return launch_decode<MODE, NTG, 128, NT, 2, NTG == 1 ? 4 : 3>(p, g, s, rt);
 }
 
 // FP8 weights: 128-element steps (128-byte weight rows, 256-byte token rows; K % 128 == 0
@@ -653,18 +776,19 @@ hipError_t launch_decode_bf16(const DArgs& p, const GemmArgs& g, hipStream_t s) 
 // waves per CU streams faster than 256-element steps (which fit one or two waves per CU)
 // at every batch size; 32-row sub-tiles need the 3-slot ring to keep three waves.
 template <int MODE, int NTG, bool NT>
-hipError_t launch_decode_fp8(const DArgs& p, const GemmArgs& g, hipStream_t s) {
-  return launch_decode<MODE, NTG, 128, NT, 1, NTG == 1 ? 4 : 3>(p, g, s);
+hipError_t launch_decode_fp8(const DArgs& p, const GemmArgs& g, hipStream_t s,
+                              const DRoute* rt) {
+  return launch_decode<MODE, NTG, 128, NT, 1, NTG == 1 ? 4 : 3>(p, g, s, rt);
 }
 
 template <int MODE, int NTG, bool NT>
-hipError_t launch_decode_w(const DArgs& p, const GemmArgs& g, hipStream_t s) {
-  return g.w_scale ? launch_decode_fp8<MODE, NTG, NT>(p, g, s)
-                   : launch_decode_bf16<MODE, NTG, NT>(p, g, s);
+hipError_t launch_decode_w(const DArgs& p, const GemmArgs& g, hipStream_t s, const DRoute* rt) {
+  return g.w_scale ? launch_decode_fp8<MODE, NTG, NT>(p, g, s, rt)
+                   : launch_decode_bf16<MODE, NTG, NT>(p, g, s, rt);
 }
 
 template <int MODE>
-hipError_t run_decode(const GemmArgs& g, hipStream_t s) {
+hipError_t run_decode(const GemmArgs& g, hipStream_t s, const DRoute* rt = nullptr) {
   DArgs p{};
   const bool g1 = MODE == 1;
   p.A = static_cast<const uint8_t*>(g.B);
@@ -683,10 +807,10 @@ hipError_t run_decode(const GemmArgs& g, hipStream_t s) {
   // block read once); otherwise the sub-tiles of one expert re-read its weights, and
   // those re-reads should hit in L2
   if (ntg == 2)
-    return p.R <= 4 * g.E ? launch_decode_w<MODE, 2, true>(p, g, s)
-                          : launch_decode_w<MODE, 2, false>(p, g, s);
-  return p.R <= 2 * g.E ? launch_decode_w<MODE, 1, true>(p, g, s)
-                        : launch_decode_w<MODE, 1, false>(p, g, s);
+    return p.R <= 4 * g.E ? launch_decode_w<MODE, 2, true>(p, g, s, rt)
+                          : launch_decode_w<MODE, 2, false>(p, g, s, rt);
+  return p.R <= 2 * g.E ? launch_decode_w<MODE, 1, true>(p, g, s, rt)
+                        : launch_decode_w<MODE, 1, false>(p, g, s, rt);
 }
 
 }  // namespace
@@ -694,6 +818,44 @@ hipError_t run_decode(const GemmArgs& g, hipStream_t s) {
 int decode_block_m(int R, int E) { return 16 * decode_ntg(256, R, E); }
 
 hipError_t launch_decode_gemm1(const GemmArgs& g, hipStream_t s) { return run_decode<1>(g, s); }
+
+bool decode_route_ok(int T, int E, int k, int shared) {
+  return T == 1 && E <= 4 * kWave && k + shared < kWave;
+}
+
+hipError_t launch_decode_gemm1_routed(const GemmArgs& g, const float* logits, int nz,
+                                      const RouteArgs& a, int E, int k, int32_t* ids, float* w,
+                                      int32_t* counts, hipStream_t s) {
+  if (!decode_route_ok(g.T, E, k, a.shared) || g.k != k + a.shared || g.block_m != 16 ||
+      g.cap != 16 * g.k)
+    return hipErrorInvalidValue;
+  DRoute r{};
+  r.tp.logits = logits;
+  r.tp.t0 = 0;
+  r.tp.nz = nz;
+  r.tp.logits_out = nullptr;
+  r.tp.T = 1;
+  r.tp.E = E;
+  r.tp.k = k;
+  r.tp.mode = a.mode;
+  r.tp.offset = a.offset;
+  r.tp.bias = a.bias;
+  r.tp.n_group = a.n_group;
+  r.tp.topk_group = a.topk_group;
+  r.tp.scaling = a.scaling;
+  r.tp.ids = ids;
+  r.tp.w = w;
+  r.tp.shared = a.shared;
+  r.sorted_ids = const_cast<int32_t*>(g.sorted_ids);
+  r.expert_ids = const_cast<int32_t*>(g.expert_ids);
+  r.ntpp = const_cast<int32_t*>(g.ntpp);
+  r.counts = counts;
+  r.ES = g.E;
+  r.cap = static_cast<int>(g.cap);
+  GemmArgs g1 = g;
+  g1.max_rows = 1;
+  return run_decode<1>(g1, s, &r);
+}
 hipError_t launch_decode_gemm2(const GemmArgs& g, hipStream_t s) { return run_decode<2>(g, s); }
 
 }  // namespace moe

@@ -57,6 +57,9 @@ struct GemmArgs {
   const int32_t* ntpp;
   int T, H, I, E, k, block_m;
   int64_t cap;               // capacity of sorted_ids
+  // bound on the routed rows any one expert holds (0: T * k).  The layer passes T: its
+  // router picks k distinct experts per token.
+  int max_rows = 0;
   // GEMM2 prefill: room for the partial sums of a split last round of
   // tiles (used when it holds one [256 x 256] fp32 tile per compute unit; else unsplit)
   float* split_ws = nullptr;
@@ -78,6 +81,14 @@ hipError_t launch_combine(const float* y, int T, int H, int k, bool bf16, void* 
 // block_m whose tiles match the kernel's sub-tile height for R routed rows over E experts
 int decode_block_m(int R, int E);
 hipError_t launch_decode_gemm1(const GemmArgs& g, hipStream_t s);
+// one token (T = 1, E <= 256): GEMM1 that first routes the token from the router's nz
+// logit slabs ([nz][1][E]) with the rules of `a`, writes ids / w (k + shared slots) and
+// the align table of g (block_m 16, cap 16 * g.k) and counts ([g.E]), then streams the
+// selected experts
+bool decode_route_ok(int T, int E, int k, int shared);
+hipError_t launch_decode_gemm1_routed(const GemmArgs& g, const float* logits, int nz,
+                                      const RouteArgs& a, int E, int k, int32_t* ids, float* w,
+                                      int32_t* counts, hipStream_t s);
 hipError_t launch_decode_gemm2(const GemmArgs& g, hipStream_t s);
 
 // pipelined large-tile prefill kernels (gemm_pipe.hip); tile_m 128 or 256

@@ -448,7 +448,8 @@ moe_status forward_impl(const void* x, const void* w13, const float* w13_scale, 
                         const float* w2_scale, const float* topk_w, const int32_t* sorted_ids,
                         const int32_t* expert_ids, const int32_t* num_tokens_post_padded, int T,
                         int H, int I, int E, int k, int block_m, moe_dtype dt, int variant,
-                        void* out, void* ws, size_t ws_bytes, void* stream) {
+                        void* out, void* ws, size_t ws_bytes, void* stream,
+                        int max_rows = 0) {
   moe_status st = check_gemm_common(T, H, I, E, k, block_m, dt, variant);
   if (st != MOE_OK) return st;
   if ((st = check_scales(dt, w13_scale, w2_scale)) != MOE_OK) return st;
@@ -470,10 +471,12 @@ moe_status forward_impl(const void* x, const void* w13, const float* w13_scale, 
   const bool bf = bf16_acts(dt);
   moe::GemmArgs g1 = gemm_args(x, w13, w13_scale, a, nullptr, sorted_ids, expert_ids,
                                num_tokens_post_padded, T, H, I, E, k, block_m);
+  g1.max_rows = max_rows;
   hipError_t e = moe::launch_gemm1(g1, bf, v, s);
   if (e != hipSuccess) return hip_status(e, "gemm1");
   moe::GemmArgs g2 = gemm_args(a, w2, w2_scale, y, topk_w, sorted_ids, expert_ids,
                                num_tokens_post_padded, T, H, I, E, k, block_m);
+  g2.max_rows = max_rows;
   if (bf && v == MOE_VARIANT_PREFILL && ws_bytes >= need + moe::kSplitWsBytes) {
     g2.split_ws = reinterpret_cast<float*>(base + need);
     g2.split_ws_bytes = moe::kSplitWsBytes;
@@ -514,6 +517,7 @@ namespace {
 struct LayerPlan {
   int bm, nz;
   bool fused_route_align;
+  bool route_in_gemm1;     // one token: GEMM1 selects the experts from the logit slabs
   int64_t cap;
   size_t off_logits, off_ids, off_w, off_sorted, off_eids, off_ntpp, off_counts, off_align,
       off_fwd, total;
@@ -530,6 +534,9 @@ LayerPlan plan_layer(int T, int H, int I, int E, int k, moe_dtype dt, int shared
   size_t off = 0;
   p.nz = moe::router_slabs(T, H, bf16_acts(dt));
   p.fused_route_align = moe::route_align_fusable(T, k, E, shared);
+  p.route_in_gemm1 = bf16_acts(dt) && moe::decode_route_ok(T, E, k, shared) &&
+                     auto_variant(T, H, I, ES, KS, dt) == MOE_VARIANT_DECODE && p.bm == 16 &&
+                     p.cap == 16 * KS;
   p.off_logits = off; off += round_up(static_cast<size_t>(p.nz) * T * E * sizeof(float));
   p.off_ids = off; off += round_up(R * sizeof(int32_t));
   p.off_w = off; off += round_up(R * sizeof(float));
@@ -592,6 +599,26 @@ moe_status layer_impl(const void* x, const void* wg, const void* w13, const floa
   moe::RouteArgs ra = route_args(cfg);
   ra.shared = shared;
   hipError_t e = hipSuccess;
+  if (p.route_in_gemm1 && !expert_map) {
+    // one token: the router's logit slabs, then GEMM1 routes the token itself (every wave
+    // selects and ranks the experts; work-group 0 writes the routing and the table),
+    // GEMM2, the combine
+    e = moe::launch_router_logits(x, wg, T, H, E, true, logits, s);
+    if (e != hipSuccess) return hip_status(e, "router logits");
+    uint8_t* fw = b + p.off_fwd;
+    void* a = fw;
+    float* y = reinterpret_cast<float*>(fw + round_up(static_cast<size_t>(KS) * I * esize(dt)));
+    moe::GemmArgs g1 = gemm_args(x, w13, w13_scale, a, nullptr, sorted, eids, ntpp, T, H, I, ES,
+                                 KS, p.bm);
+    e = moe::launch_decode_gemm1_routed(g1, logits, p.nz, ra, E, k, ids, tw, counts, s);
+    if (e != hipSuccess) return hip_status(e, "gemm1 (routed)");
+    moe::GemmArgs g2 = gemm_args(a, w2, w2_scale, y, tw, sorted, eids, ntpp, T, H, I, ES, KS,
+                                 p.bm);
+    g2.max_rows = 1;
+    e = moe::launch_gemm2(g2, true, MOE_VARIANT_DECODE, s);
+    if (e != hipSuccess) return hip_status(e, "gemm2");
+    return hip_status(moe::launch_combine(y, T, H, KS, true, out, s), "combine");
+  }
   if (!p.fused_route_align && moe::route_fused_ok(T, H, E, bf16_acts(dt))) {
     // prefill: logits and top-k in one launch, then the align table
     e = moe::launch_route_fused(x, wg, T, H, E, k, ra, ids, tw, nullptr, s);
@@ -601,7 +628,7 @@ moe_status layer_impl(const void* x, const void* wg, const void* w13, const floa
     if (e != hipSuccess) return hip_status(e, "align");
     return forward_impl(x, w13, w13_scale, w2, w2_scale, tw, sorted, eids, ntpp, T, H, I, ES, KS,
                         p.bm, dt, MOE_VARIANT_AUTO, out, b + p.off_fwd,
-                        forward_ws_full(T, H, I, ES, KS, dt), stream);
+                        forward_ws_full(T, H, I, ES, KS, dt), stream, T);
   }
   e = moe::launch_router_logits(x, wg, T, H, E, bf16_acts(dt), logits, s);
   if (e != hipSuccess) return hip_status(e, "router logits");
@@ -618,8 +645,8 @@ moe_status layer_impl(const void* x, const void* wg, const void* w13, const floa
   }
   return forward_impl(x, w13, w13_scale, w2, w2_scale, tw, sorted, eids, ntpp, T, H, I, ES, KS,
                       p.bm, dt, MOE_VARIANT_AUTO, out, b + p.off_fwd,
-                      forward_ws_full(T, H, I, ES, KS, dt),
-                      stream);
+                      forward_ws_full(T, H, I, ES, KS, dt), stream,
+                      T);   // the router's k experts of a token are distinct
 }
 
 }  // namespace

@@ -15,17 +15,20 @@
 // (router_logits_tile_kernel).
 //
 // Top-k: one wave per token; lane l owns experts l, l+64, ...; each of the k
-// selections is a wave arg-max on (value desc, index asc), taken as one maximum of
-// 64-bit keys.  For small batches a
+// selections is a wave arg-max on (value desc, index asc) over the heads of per-lane
+// sorted candidate lists.  For small batches a
 // single work-group routes every token and then builds the align table in the same
 // launch (the ids never leave LDS before the align step reads them).
 #include "align_dev.hpp"
 #include "common.hpp"
 #include "launch.hpp"
+#include "route_dev.hpp"
 
 namespace moe {
 
 namespace {
+
+using namespace rdev;
 
 constexpr int kMaxSlabs = 16;
 
@@ -182,239 +185,6 @@ router_logits_f32_kernel(const float* __restrict__ x, const float* __restrict__ 
   float acc = 0.f;
   for (int h = 0; h < H; ++h) acc = fmaf(xr[h], wr[h], acc);
   logits[i] = acc;
-}
-
-// (m1, m2) <- the two largest of {m1, m2, o1, o2}, given m1 >= m2 and o1 >= o2
-__device__ __forceinline__ void top2_merge(float& m1, float& m2, float o1, float o2) {
-  const float n2 = fmaxf(fminf(m1, o1), fmaxf(m2, o2));
-  m1 = fmaxf(m1, o1);
-  m2 = n2;
-}
-
-template <int CTRL, int NSLOT>
-__device__ __forceinline__ void top2_steps(float (&m1)[NSLOT], float (&m2)[NSLOT]) {
-#pragma unroll
-  for (int i = 0; i < NSLOT; ++i) {
-    const float o1 = __int_as_float(dpp_move<CTRL>(__float_as_int(m1[i])));
-    const float o2 = __int_as_float(dpp_move<CTRL>(__float_as_int(m2[i])));
-    top2_merge(m1[i], m2[i], o1, o2);
-  }
-}
-
-template <int CTRL, int ROW_MASK = 0xF>
-__device__ __forceinline__ uint64_t key_max_step(uint64_t v) {
-  const uint32_t lo = static_cast<uint32_t>(dpp_move<CTRL, ROW_MASK>(static_cast<int>(v)));
-  const uint32_t hi = static_cast<uint32_t>(dpp_move<CTRL, ROW_MASK>(static_cast<int>(v >> 32)));
-  const uint64_t o = (static_cast<uint64_t>(hi) << 32) | lo;
-  return o > v ? o : v;
-}
-
-// Maximum of an unsigned 64-bit key over the wave (0 is the identity: lanes a DPP move
-// does not write read 0).  Within each 16-lane row by four moves, then row 0 into row 1
-// and row 2 into row 3 (row_bcast:15), then row 1 into rows 2 and 3 (row_bcast:31): lane
-// 63 ends with the maximum, which every lane reads.
-__device__ __forceinline__ uint64_t wave_max_key(uint64_t v) {
-  v = key_max_step<dpp::kQuadXor1>(v);
-  v = key_max_step<dpp::kQuadXor2>(v);
-  v = key_max_step<dpp::kRowHalfMirror>(v);
-  v = key_max_step<dpp::kRowMirror>(v);
-  v = key_max_step<dpp::kRowBcast15, 0xA>(v);
-  v = key_max_step<dpp::kRowBcast31, 0xC>(v);
-  const uint32_t lo = static_cast<uint32_t>(read_lane(static_cast<int>(v), kWave - 1));
-  const uint32_t hi = static_cast<uint32_t>(read_lane(static_cast<int>(v >> 32), kWave - 1));
-  return (static_cast<uint64_t>(hi) << 32) | lo;
-}
-
-__device__ __forceinline__ float sigmoid_rn(float l) {
-  // sigma(l) evaluated in double and rounded once to the nearest float
-  return static_cast<float>(1.0 / (1.0 + exp(-static_cast<double>(l))));
-}
-
-struct TopkParams {
-  const float* logits;     // nz slabs of [T][E] (nz == 1: the logits themselves); row t of
-                           // a slab is token t0 + t
-  int t0;
-  int nz;
-  float* logits_out;       // [T][E] or null: receives the summed logits (nz > 1)
-  int T, E, k, mode;
-  const float* offset;
-  const float* bias;
-  int n_group, topk_group;
-  float scaling;
-  int32_t* ids;            // [T][k + shared]
-  float* w;
-  int shared;              // 1: slot k is the shared expert (id E, weight 1)
-};
-
-// LDS of one wave's top-k (group segment pairs)
-struct TopkLds {
-  float cval[512];
-};
-
-// Routes token t with the calling wave: writes ids/w (and logits_out) of t, and the
-// ids into ids_lds when given.  NSLOT = experts per lane (E <= 64*NSLOT); ZC = logit
-// slabs loaded per round trip (bounded by the registers the launch allows).
-template <int NSLOT, int ZC>
-__device__ void topk_token(const TopkParams& p, int t, TopkLds& sh, int32_t* ids_lds) {
-  const int lane = lane_id();
-  const int E = p.E, k = p.k, mode = p.mode;
-  const float kNegInf = -__builtin_inff();
-  // every load first, at clamped indices, so that all of them are in flight together;
-  // slabs are added in ascending order
-  float lv[NSLOT], ov[NSLOT], bv[NSLOT];
-  const float* lrow = p.logits + static_cast<int64_t>(t - p.t0) * E;
-  const int64_t slab = static_cast<int64_t>(p.T) * E;
-#pragma unroll
-  for (int i = 0; i < NSLOT; ++i) {
-    const int ec = min(lane + kWave * i, E - 1);
-    lv[i] = lrow[ec];
-    ov[i] = p.offset ? p.offset[ec] : 0.f;
-    bv[i] = p.bias ? p.bias[ec] : 0.f;
-  }
-  if (p.nz > 1) {
-    for (int z0 = 1; z0 < p.nz; z0 += ZC) {
-      float part[ZC][NSLOT];
-#pragma unroll
-      for (int q = 0; q < ZC; ++q) {
-        const int zc = min(z0 + q, p.nz - 1);
-#pragma unroll
-        for (int i = 0; i < NSLOT; ++i)
-          part[q][i] = lrow[zc * slab + min(lane + kWave * i, E - 1)];
-      }
-#pragma unroll
-      for (int q = 0; q < ZC; ++q) {
-#pragma unroll
-        for (int i = 0; i < NSLOT; ++i) lv[i] = z0 + q < p.nz ? lv[i] + part[q][i] : lv[i];
-      }
-    }
-  }
-  float sel[NSLOT];    // selection value (-inf = not eligible / taken)
-  float wsrc[NSLOT];   // weight source: logit (modes 0,1) or unbiased sigmoid (2)
-#pragma unroll
-  for (int i = 0; i < NSLOT; ++i) {
-    const int e = lane + kWave * i;
-    if (p.logits_out && e < E) p.logits_out[static_cast<int64_t>(t) * E + e] = lv[i];
-    float l = lv[i];
-    if (p.offset) l = l + ov[i];
-    float v, ws;
-    if (mode == 2) {
-      const float s = sigmoid_rn(l);
-      v = p.bias ? s + bv[i] : s;
-      ws = s;
-    } else {
-      v = l;
-      ws = l;
-    }
-    sel[i] = e < E ? v : kNegInf;
-    wsrc[i] = e < E ? ws : 0.f;
-  }
-  if (mode == 2 && p.n_group > 0 && p.topk_group > 0) {
-    // group score = sum of the two largest biased scores of a contiguous group of
-    // gsz = E / n_group experts.  Top-2 pairs are first merged across aligned lane
-    // segments of `sub` lanes (sub = the largest power of two <= 16 dividing gsz) with
-    // DPP moves; lane g then merges the gsz/sub segment pairs of group g from LDS.
-    // Only values enter the score, so the merge order does not change it.
-    const int gsz = E / p.n_group;
-    const int sub = min(16, gsz & -gsz);
-    float m1[NSLOT], m2[NSLOT];
-#pragma unroll
-    for (int i = 0; i < NSLOT; ++i) { m1[i] = sel[i]; m2[i] = kNegInf; }
-    if (sub >= 2) top2_steps<dpp::kQuadXor1, NSLOT>(m1, m2);
-    if (sub >= 4) top2_steps<dpp::kQuadXor2, NSLOT>(m1, m2);
-    if (sub >= 8) top2_steps<dpp::kRowHalfMirror, NSLOT>(m1, m2);
-    if (sub >= 16) top2_steps<dpp::kRowMirror, NSLOT>(m1, m2);
-    // segment pairs: first value at cval[s], second at cval[256 + s] (sub >= 2 leaves at
-    // most 256 segments; with sub == 1 every second value is -inf and not stored)
-#pragma unroll
-    for (int i = 0; i < NSLOT; ++i) {
-      const int e = lane + kWave * i;
-      if (e < E && (lane & (sub - 1)) == 0) {
-        const int sg = e / sub;
-        sh.cval[sg] = m1[i];
-        if (sub > 1) sh.cval[256 + sg] = m2[i];
-      }
-    }
-    wave_sync();
-    float gs = kNegInf;
-    if (lane < p.n_group) {
-      const int nps = gsz / sub;
-      const int s0 = lane * nps;
-      float g1 = sh.cval[s0];
-      float g2 = sub > 1 ? sh.cval[256 + s0] : kNegInf;
-      for (int q = 1; q < nps; ++q)
-        top2_merge(g1, g2, sh.cval[s0 + q], sub > 1 ? sh.cval[256 + s0 + q] : kNegInf);
-      gs = g1 + g2;
-    }
-    // keep the topk_group groups of highest score (ties to the lower group index):
-    // group g is kept when fewer than topk_group groups beat it
-    int beaten_by = 0;
-    for (int h = 0; h < p.n_group; ++h) {
-      const float o = read_lane(gs, h);
-      beaten_by += ((o > gs) | ((o == gs) & (h < lane))) ? 1 : 0;
-    }
-    const uint64_t keep = __ballot(lane < p.n_group && beaten_by < p.topk_group);
-#pragma unroll
-    for (int i = 0; i < NSLOT; ++i) {
-      const int e = min(lane + kWave * i, E - 1);
-      sel[i] = (keep >> (e / gsz)) & 1ull ? sel[i] : kNegInf;
-    }
-    wave_sync();                                   // cval is reused by the next token
-  }
-  // k selections; lane j keeps the j-th chosen (id, weight source) pair.  Each candidate
-  // is one 64-bit key: the selection value's bits mapped to an unsigned order (-0 folded
-  // into +0, so equal values give equal high words) above the complemented expert index,
-  // so the largest key is the largest value and, among equal values, the lower index.
-  // Invalid, masked and taken candidates hold key 0, below every eligible key (at least
-  // k eligible candidates exist).  A pick is a wave maximum of the lanes' best keys.
-  uint64_t key[NSLOT];
-#pragma unroll
-  for (int i = 0; i < NSLOT; ++i) {
-    const uint32_t b = __float_as_uint(sel[i] + 0.f);
-    const uint32_t ord = b ^ (static_cast<uint32_t>(static_cast<int32_t>(b) >> 31) | 0x80000000u);
-    key[i] = sel[i] == kNegInf ? 0ull
-                               : (static_cast<uint64_t>(ord) << 32) |
-                                     static_cast<uint32_t>(~(lane + kWave * i));
-  }
-  uint64_t lbest = key[0];
-#pragma unroll
-  for (int i = 1; i < NSLOT; ++i) lbest = key[i] > lbest ? key[i] : lbest;
-  int my_id = 0;
-  float my_src = 0.f;
-  for (int j = 0; j < k; ++j) {
-    const uint64_t best = wave_max_key(lbest);
-    const int bi = static_cast<int>(~static_cast<uint32_t>(best));
-    const int slot = bi / kWave;                    // uniform
-    float src = wsrc[0];
-#pragma unroll
-    for (int i = 1; i < NSLOT; ++i) src = slot == i ? wsrc[i] : src;
-    src = read_lane(src, bi & (kWave - 1));         // the owner lane's weight source
-#pragma unroll
-    for (int i = 0; i < NSLOT; ++i) key[i] = key[i] == best ? 0ull : key[i];
-    lbest = key[0];
-#pragma unroll
-    for (int i = 1; i < NSLOT; ++i) lbest = key[i] > lbest ? key[i] : lbest;
-    my_id = lane == j ? bi : my_id;
-    my_src = lane == j ? src : my_src;
-  }
-  // weights in double: modes 0/1 exp(l_j - l_0) / sum, mode 2 scale * s_j / sum; the
-  // sum runs over j = 0..k-1 in order
-  const double l0 = static_cast<double>(read_lane(my_src, 0));
-  const double myv = mode == 2 ? static_cast<double>(my_src)
-                               : exp(static_cast<double>(my_src) - l0);
-  double sum = 0.0;
-  for (int j = 0; j < k; ++j) sum += read_lane(myv, j);
-  // rows of k + shared slots; the shared expert takes slot k with weight 1
-  const int ko = k + p.shared;
-  if (lane < k) {
-    const double wt = mode == 2 ? static_cast<double>(p.scaling) * myv / sum : myv / sum;
-    p.ids[static_cast<int64_t>(t) * ko + lane] = my_id;
-    p.w[static_cast<int64_t>(t) * ko + lane] = static_cast<float>(wt);
-    if (ids_lds) ids_lds[t * ko + lane] = my_id;
-  } else if (lane < ko) {
-    p.ids[static_cast<int64_t>(t) * ko + lane] = p.E;
-    p.w[static_cast<int64_t>(t) * ko + lane] = 1.f;
-    if (ids_lds) ids_lds[t * ko + lane] = p.E;
-  }
 }
 
 template <int NSLOT>

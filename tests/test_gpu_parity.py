@@ -524,11 +524,13 @@ def test_layer_reduced(lib, name, T, scale):
 
 @pytest.mark.parametrize("name,T", [("deepseek_decode", 1), ("deepseek_decode", 3),
                                     ("deepseek_decode", 8), ("deepseek_decode_fp8", 2),
-                                    ("qwen3_skewed", 5)])
+                                    ("qwen3_skewed", 5), ("mixtral", 4), ("mixtral_fp8", 3),
+                                    ("deepseek_decode", 4)])
 def test_layer_small_batch_repeated(lib, name, T):
     """Small decode batches (one-launch route + align, weight-streaming GEMMs): three calls
     in a row on the same buffers with new activations (so the experts change), each against
-    the oracle."""
+    the oracle.  Up to T = 4 the GEMMs stream only the first four token rows of a sub-tile
+    (an expert holds at most T rows); Mixtral's 8 experts at T = 4 fill all four."""
     base = S.WORKLOADS[name]
     q = 128 if name.endswith("fp8") else 64
     wl = base.scaled(T=T, H=base.H // 4 // q * q, I=base.I // 4 // q * q)
