@@ -37,7 +37,7 @@ PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=24)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="mixtral")
     ap.add_argument("--T", type=int, default=None)
@@ -322,8 +322,12 @@ def measure(args, workload: str, T_override=None, with_cpu=True):
     torch.cuda.synchronize()
 
     # the step as HIP graphs (one per activation batch): the library only enqueues work,
-    # so a whole layer is capturable and replays without host launch gaps
+    # so a whole layer is capturable and replays without host launch gaps.  A model step
+    # replays its layers from one graph, so the timed loop replays `chunk`, the nx steps
+    # (activation batches in turn) captured in one graph, and single-step graphs only for
+    # the remainder: no graph launch sits between the steps of a chunk.
     graphs = []
+    chunk = None
     if not args.eager:
         cs = torch.cuda.Stream()
         cs.wait_stream(stream)
@@ -332,16 +336,27 @@ def measure(args, workload: str, T_override=None, with_cpu=True):
             with torch.cuda.graph(g, stream=cs):
                 launch(i, cur_sp())
             graphs.append(g)
+        if nx > 1:
+            chunk = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(chunk, stream=cs):
+                for i in range(nx):
+                    launch(i, cur_sp())
         torch.cuda.synchronize()
         for i in range(args.warmup):
             graphs[i % nx].replay()
+        if chunk is not None:
+            chunk.replay()
         torch.cuda.synchronize()
 
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_start.record(stream)
-    for i in range(args.steps):
+    i = 0
+    while chunk is not None and i + nx <= args.steps:
+        chunk.replay()
+        i += nx
+    for i in range(i, args.steps):
         if graphs:
             graphs[i % nx].replay()
         else:

@@ -295,12 +295,23 @@ combine_vec_kernel(const float* __restrict__ y, int T, int H, int k, void* __res
   if (h0 >= H) return;
   for (int t = blockIdx.y; t < T; t += gridDim.y) {
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int j = 0; j < k; ++j) {
-      const float* row = y + (static_cast<int64_t>(t) * k + j) * H + h0;
-      const float4 a = *reinterpret_cast<const float4*>(row);
-      const float4 b = *reinterpret_cast<const float4*>(row + 4);
-      acc[0] += a.x; acc[1] += a.y; acc[2] += a.z; acc[3] += a.w;
-      acc[4] += b.x; acc[5] += b.y; acc[6] += b.z; acc[7] += b.w;
+    // the rows of up to 8 slots are loaded before any is added (one round trip per 8
+    // slots; slots past k re-read slot k-1 and are not added), then added in slot order
+    for (int j0 = 0; j0 < k; j0 += 8) {
+      float4 a[8], b[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const float* row = y + (static_cast<int64_t>(t) * k + min(j0 + q, k - 1)) * H + h0;
+        a[q] = *reinterpret_cast<const float4*>(row);
+        b[q] = *reinterpret_cast<const float4*>(row + 4);
+      }
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        if (j0 + q < k) {
+          acc[0] += a[q].x; acc[1] += a[q].y; acc[2] += a[q].z; acc[3] += a[q].w;
+          acc[4] += b[q].x; acc[5] += b[q].y; acc[6] += b[q].z; acc[7] += b[q].w;
+        }
+      }
     }
     if (BF16) {
       u32x4 v;
