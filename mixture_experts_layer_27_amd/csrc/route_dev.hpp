@@ -134,44 +134,68 @@ __device__ void topk_select(const TopkParams& p, int t, TopkLds& sh, int& out_id
   }
   if (mode == 2 && p.n_group > 0 && p.topk_group > 0) {
     // group score = sum of the two largest biased scores of a contiguous group of
-    // gsz = E / n_group experts.  Top-2 pairs are first merged across aligned lane
-    // segments of `sub` lanes (sub = the largest power of two <= 16 dividing gsz) with
-    // DPP moves; lane g then merges the gsz/sub segment pairs of group g from LDS.
-    // Only values enter the score, so the merge order does not change it.
+    // gsz = E / n_group experts.  Only values enter the score, so the merge order does not
+    // change it.
     const int gsz = E / p.n_group;
-    const int sub = min(16, gsz & -gsz);
-    const int sub_sh = __builtin_ctz(static_cast<unsigned>(sub));
     // group of expert e: a shift when gsz is a power of two (uniform branch)
     const int gsz_sh = (gsz & (gsz - 1)) == 0 ? __builtin_ctz(static_cast<unsigned>(gsz)) : -1;
     auto group_of = [&](int e) { return gsz_sh >= 0 ? e >> gsz_sh : e / gsz; };
+    float gs = kNegInf;                            // lane g < n_group: score of group g
     float m1[NSLOT], m2[NSLOT];
 #pragma unroll
     for (int i = 0; i < NSLOT; ++i) { m1[i] = sel[i]; m2[i] = kNegInf; }
-    if (sub >= 2) top2_steps<dpp::kQuadXor1, NSLOT>(m1, m2);
-    if (sub >= 4) top2_steps<dpp::kQuadXor2, NSLOT>(m1, m2);
-    if (sub >= 8) top2_steps<dpp::kRowHalfMirror, NSLOT>(m1, m2);
-    if (sub >= 16) top2_steps<dpp::kRowMirror, NSLOT>(m1, m2);
-    // segment pairs: first value at cval[s], second at cval[256 + s] (sub >= 2 leaves at
-    // most 256 segments; with sub == 1 every second value is -inf and not stored)
+    if ((gsz == 16 || gsz == 32 || gsz == 64) && E == gsz * p.n_group) {
+      // a group is one, two or four whole 16-lane rows of a slot: top-2 pairs within each
+      // row by DPP moves, then across rows by lane swaps, so that every lane of a group
+      // holds its pair; lane g then reads group g's score from the lane that opens it
+      top2_steps<dpp::kQuadXor1, NSLOT>(m1, m2);
+      top2_steps<dpp::kQuadXor2, NSLOT>(m1, m2);
+      top2_steps<dpp::kRowHalfMirror, NSLOT>(m1, m2);
+      top2_steps<dpp::kRowMirror, NSLOT>(m1, m2);
+      for (int x = 16; x < gsz; x <<= 1) {
 #pragma unroll
-    for (int i = 0; i < NSLOT; ++i) {
-      const int e = lane + kWave * i;
-      if (e < E && (lane & (sub - 1)) == 0) {
-        const int sg = e >> sub_sh;
-        sh.cval[sg] = m1[i];
-        if (sub > 1) sh.cval[256 + sg] = m2[i];
+        for (int i = 0; i < NSLOT; ++i)
+          top2_merge(m1[i], m2[i], __shfl_xor(m1[i], x, kWave), __shfl_xor(m2[i], x, kWave));
       }
-    }
-    wave_sync();
-    float gs = kNegInf;
-    if (lane < p.n_group) {
-      const int nps = gsz >> sub_sh;
-      const int s0 = lane * nps;
-      float g1 = sh.cval[s0];
-      float g2 = sub > 1 ? sh.cval[256 + s0] : kNegInf;
-      for (int q = 1; q < nps; ++q)
-        top2_merge(g1, g2, sh.cval[s0 + q], sub > 1 ? sh.cval[256 + s0 + q] : kNegInf);
-      gs = g1 + g2;
+      const int e0 = min(lane, p.n_group - 1) * gsz;   // first expert of group `lane`
+      float g[NSLOT];
+#pragma unroll
+      for (int i = 0; i < NSLOT; ++i) g[i] = __shfl(m1[i] + m2[i], e0 & (kWave - 1), kWave);
+      const int slot = e0 >> 6;
+#pragma unroll
+      for (int i = 0; i < NSLOT; ++i) gs = slot == i ? g[i] : gs;
+      if (lane >= p.n_group) gs = kNegInf;
+    } else {
+      // segments of `sub` lanes (the largest power of two <= 16 dividing gsz) merged
+      // with DPP moves; lane g then merges the gsz/sub segment pairs of group g from LDS
+      const int sub = min(16, gsz & -gsz);
+      const int sub_sh = __builtin_ctz(static_cast<unsigned>(sub));
+      if (sub >= 2) top2_steps<dpp::kQuadXor1, NSLOT>(m1, m2);
+      if (sub >= 4) top2_steps<dpp::kQuadXor2, NSLOT>(m1, m2);
+      if (sub >= 8) top2_steps<dpp::kRowHalfMirror, NSLOT>(m1, m2);
+      if (sub >= 16) top2_steps<dpp::kRowMirror, NSLOT>(m1, m2);
+      // segment pairs: first value at cval[s], second at cval[256 + s] (sub >= 2 leaves
+      // at most 256 segments; with sub == 1 every second value is -inf and not stored)
+#pragma unroll
+      for (int i = 0; i < NSLOT; ++i) {
+        const int e = lane + kWave * i;
+        if (e < E && (lane & (sub - 1)) == 0) {
+          const int sg = e >> sub_sh;
+          sh.cval[sg] = m1[i];
+          if (sub > 1) sh.cval[256 + sg] = m2[i];
+        }
+      }
+      wave_sync();
+      if (lane < p.n_group) {
+        const int nps = gsz >> sub_sh;
+        const int s0 = lane * nps;
+        float g1 = sh.cval[s0];
+        float g2 = sub > 1 ? sh.cval[256 + s0] : kNegInf;
+        for (int q = 1; q < nps; ++q)
+          top2_merge(g1, g2, sh.cval[s0 + q], sub > 1 ? sh.cval[256 + s0 + q] : kNegInf);
+        gs = g1 + g2;
+      }
+      wave_sync();                                 // cval is reused by the next token
     }
     // keep the topk_group groups of highest score (ties to the lower group index):
     // group g is kept when fewer than topk_group groups beat it
@@ -186,7 +210,6 @@ __device__ void topk_select(const TopkParams& p, int t, TopkLds& sh, int& out_id
       const int e = min(lane + kWave * i, E - 1);
       sel[i] = (keep >> group_of(e)) & 1ull ? sel[i] : kNegInf;
     }
-    wave_sync();                                   // cval is reused by the next token
   }
   // k selections; lane j keeps the j-th chosen (id, weight source) pair.  Candidates are
   // 32-bit keys: the selection value's bits mapped to an unsigned order (-0 folded into
