@@ -37,7 +37,7 @@ PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=24)
+    ap.add_argument("--steps", type=int, default=48)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="mixtral")
     ap.add_argument("--T", type=int, default=None)

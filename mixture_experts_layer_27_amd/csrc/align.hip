@@ -27,8 +27,8 @@ __global__ void __launch_bounds__(kAlignThreads)
 align_small_kernel(const int32_t* __restrict__ ids, int R, int E, int bm, int64_t cap,
                    int32_t* __restrict__ sorted_ids, int32_t* __restrict__ expert_ids,
                    int32_t* __restrict__ ntpp, int32_t* __restrict__ counts,
-                   const int32_t* __restrict__ emap) {
-  align_small_body(ids, R, E, bm, cap, sorted_ids, expert_ids, ntpp, counts, emap);
+                   const int32_t* __restrict__ emap, int2* __restrict__ tile_run) {
+  align_small_body(ids, R, E, bm, cap, sorted_ids, expert_ids, ntpp, counts, emap, tile_run);
 }
 
 // ---------------------------------------------------------------- multi-launch path
@@ -63,7 +63,8 @@ align_hist_kernel(const int32_t* __restrict__ ids, int R, int E, int nseg, int64
 __global__ void __launch_bounds__(kAlignThreads)
 align_scan_kernel(int R, int E, int bm, int64_t cap, int nseg, int32_t* __restrict__ hist,
                   int32_t* __restrict__ expert_ids, int32_t* __restrict__ ntpp,
-                  int32_t* __restrict__ counts, const int32_t* __restrict__ emap) {
+                  int32_t* __restrict__ counts, const int32_t* __restrict__ emap,
+                  int2* __restrict__ tile_run) {
   constexpr int kB = 8;                         // loads in flight per thread
   __shared__ int part[kAlignThreads];           // [g][e]: count, then the group's base
   __shared__ int cnt[kMaxE], start[kMaxE];
@@ -119,7 +120,7 @@ align_scan_kernel(int R, int E, int bm, int64_t cap, int nseg, int32_t* __restri
     if (counts && g == 0) counts[e] = cnt[e];
   }
   if (threadIdx.x == 0) *ntpp = total;
-  fill_expert_ids(cnt, start, E, bm, total, cap, expert_ids, emap);
+  fill_expert_ids(cnt, start, E, bm, total, cap, expert_ids, emap, tile_run);
 }
 
 // Phase 3: one wave per segment, stable scatter from the segment's run bases.
@@ -148,10 +149,11 @@ size_t align_ws_bytes(int R, int E) {
 
 hipError_t launch_align(const int32_t* ids, int R, int E, int bm, int64_t cap,
                         int32_t* sorted_ids, int32_t* expert_ids, int32_t* ntpp,
-                        int32_t* counts, int32_t* ws_hist, const int32_t* emap, hipStream_t s) {
+                        int32_t* counts, int32_t* ws_hist, const int32_t* emap, hipStream_t s,
+                        int2* tile_run) {
   if (R <= kAlignSmallMaxRows) {
     hipLaunchKernelGGL(align_small_kernel, dim3(1), dim3(kAlignThreads), 0, s, ids, R, E, bm,
-                       cap, sorted_ids, expert_ids, ntpp, counts, emap);
+                       cap, sorted_ids, expert_ids, ntpp, counts, emap, tile_run);
     return hipGetLastError();
   }
   const int nseg = (R + kSegRows - 1) / kSegRows;
@@ -159,7 +161,7 @@ hipError_t launch_align(const int32_t* ids, int R, int E, int bm, int64_t cap,
   hipLaunchKernelGGL(align_hist_kernel, dim3(blocks), dim3(256), 0, s, ids, R, E, nseg, cap,
                      ws_hist, sorted_ids);
   hipLaunchKernelGGL(align_scan_kernel, dim3(1), dim3(kAlignThreads), 0, s, R, E, bm, cap, nseg,
-                     ws_hist, expert_ids, ntpp, counts, emap);
+                     ws_hist, expert_ids, ntpp, counts, emap, tile_run);
   hipLaunchKernelGGL(align_scatter_kernel, dim3(blocks), dim3(256), 0, s, ids, R, E, nseg,
                      ws_hist, sorted_ids);
   return hipGetLastError();

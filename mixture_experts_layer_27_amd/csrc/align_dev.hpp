@@ -80,11 +80,14 @@ __device__ inline void scan_padded(const int* __restrict__ cnt, int E, int bm,
 // expert_ids: thread e writes the tiles of expert e ([start_e, start_e + padded_e) / bm)
 // with its owner: e, or emap[e] when an expert map is given (expert parallelism: the
 // expert's index among this GPU's experts, -1 for an expert held elsewhere); the rest
-// of the first cap/bm entries gets -1.
+// of the first cap/bm entries gets -1.  tile_run (optional, cap/bm + 1 entries): each of
+// those tiles gets (first tile, number of tiles) of its expert's run, and entry cap/bm
+// gets (longest run, 0).  Called by every thread of the work-group.
 __device__ inline void fill_expert_ids(const int* __restrict__ cnt, const int* __restrict__ start,
                                        int E, int bm, int total, int64_t cap,
                                        int32_t* __restrict__ expert_ids,
-                                       const int32_t* __restrict__ emap) {
+                                       const int32_t* __restrict__ emap,
+                                       int2* __restrict__ tile_run = nullptr) {
   const int lg = log2_pow2(bm);
   for (int e = threadIdx.x; e < E; e += blockDim.x) {
     const int n = cnt[e];
@@ -92,6 +95,17 @@ __device__ inline void fill_expert_ids(const int* __restrict__ cnt, const int* _
     const int p1 = (s + n + bm - 1) >> lg;
     const int owner = emap ? emap[e] : e;
     for (int p = s >> lg; p < p1; ++p) expert_ids[p] = owner;
+    if (tile_run)
+      for (int p = s >> lg; p < p1; ++p) tile_run[p] = make_int2(s >> lg, p1 - (s >> lg));
+  }
+  if (tile_run) {
+    __shared__ int longest;
+    if (threadIdx.x == 0) longest = 0;
+    __syncthreads();
+    for (int e = threadIdx.x; e < E; e += blockDim.x)
+      atomicMax(&longest, (cnt[e] + bm - 1) >> lg);
+    __syncthreads();
+    if (threadIdx.x == 0) tile_run[cap >> lg] = make_int2(longest, 0);
   }
   const int ntiles_cap = static_cast<int>(cap >> lg);
   for (int p = (total >> lg) + threadIdx.x; p < ntiles_cap; p += blockDim.x) expert_ids[p] = -1;
@@ -105,7 +119,8 @@ __device__ inline void align_small_body(const int32_t* ids, int R, int E, int bm
                                         int32_t* __restrict__ sorted_ids,
                                         int32_t* __restrict__ expert_ids,
                                         int32_t* __restrict__ ntpp, int32_t* __restrict__ counts,
-                                        const int32_t* __restrict__ emap) {
+                                        const int32_t* __restrict__ emap,
+                                        int2* __restrict__ tile_run = nullptr) {
   __shared__ int hist[kAlignWaves][kMaxE];   // per-wave segment histogram, later run cursors
   __shared__ int cnt[kMaxE], start[kMaxE];
   __shared__ int total_s;
@@ -142,7 +157,7 @@ __device__ inline void align_small_body(const int32_t* ids, int R, int E, int bm
     if (counts) counts[e] = cnt[e];
   }
   if (threadIdx.x == 0) *ntpp = total;
-  fill_expert_ids(cnt, start, E, bm, total, cap, expert_ids, emap);
+  fill_expert_ids(cnt, start, E, bm, total, cap, expert_ids, emap, tile_run);
   __syncthreads();
   segment_scatter(ids, r0, r1, E, hist[w], sorted_ids);
 }

@@ -39,11 +39,15 @@ hipError_t launch_route_align_small(const float* logits, int nz, float* logits_o
                                     int32_t* ntpp, int32_t* counts, const int32_t* emap,
                                     hipStream_t s);
 
-// align; emap (nullable, [E]): expert parallelism, tiles carry emap[e] (-1: remote)
+// align; emap (nullable, [E]): expert parallelism, tiles carry emap[e] (-1: remote);
+// tile_run (nullable, [cap / bm + 1]): each table tile gets (first tile, tiles) of its
+// expert's run and the last entry (longest run, 0), for the expert-ordered raster of the
+// prefill GEMMs
 size_t align_ws_bytes(int R, int E);
 hipError_t launch_align(const int32_t* ids, int R, int E, int bm, int64_t cap,
                         int32_t* sorted_ids, int32_t* expert_ids, int32_t* ntpp,
-                        int32_t* counts, int32_t* ws_hist, const int32_t* emap, hipStream_t s);
+                        int32_t* counts, int32_t* ws_hist, const int32_t* emap, hipStream_t s,
+                        int2* tile_run = nullptr);
 
 // expert GEMMs
 struct GemmArgs {
@@ -60,6 +64,9 @@ struct GemmArgs {
   // bound on the routed rows any one expert holds (0: T * k).  The layer passes T: its
   // router picks k distinct experts per token.
   int max_rows = 0;
+  // (first tile, tiles) of each block_m tile's expert run (nullable): the prefill GEMMs
+  // then order their tiles by expert run (see moe_gemm_pipe_kernel)
+  const int2* tile_run = nullptr;
   // GEMM2 prefill: room for the partial sums of a split last round of
   // tiles (used when it holds one [256 x 256] fp32 tile per compute unit; else unsplit)
   float* split_ws = nullptr;

@@ -449,7 +449,7 @@ moe_status forward_impl(const void* x, const void* w13, const float* w13_scale, 
                         const int32_t* expert_ids, const int32_t* num_tokens_post_padded, int T,
                         int H, int I, int E, int k, int block_m, moe_dtype dt, int variant,
                         void* out, void* ws, size_t ws_bytes, void* stream,
-                        int max_rows = 0) {
+                        int max_rows = 0, const int2* tile_run = nullptr) {
   moe_status st = check_gemm_common(T, H, I, E, k, block_m, dt, variant);
   if (st != MOE_OK) return st;
   if ((st = check_scales(dt, w13_scale, w2_scale)) != MOE_OK) return st;
@@ -472,11 +472,13 @@ moe_status forward_impl(const void* x, const void* w13, const float* w13_scale, 
   moe::GemmArgs g1 = gemm_args(x, w13, w13_scale, a, nullptr, sorted_ids, expert_ids,
                                num_tokens_post_padded, T, H, I, E, k, block_m);
   g1.max_rows = max_rows;
+  g1.tile_run = tile_run;
   hipError_t e = moe::launch_gemm1(g1, bf, v, s);
   if (e != hipSuccess) return hip_status(e, "gemm1");
   moe::GemmArgs g2 = gemm_args(a, w2, w2_scale, y, topk_w, sorted_ids, expert_ids,
                                num_tokens_post_padded, T, H, I, E, k, block_m);
   g2.max_rows = max_rows;
+  g2.tile_run = tile_run;
   if (bf && v == MOE_VARIANT_PREFILL && ws_bytes >= need + moe::kSplitWsBytes) {
     g2.split_ws = reinterpret_cast<float*>(base + need);
     g2.split_ws_bytes = moe::kSplitWsBytes;
@@ -519,8 +521,8 @@ struct LayerPlan {
   bool fused_route_align;
   bool route_in_gemm1;     // one token: GEMM1 selects the experts from the logit slabs
   int64_t cap;
-  size_t off_logits, off_ids, off_w, off_sorted, off_eids, off_ntpp, off_counts, off_align,
-      off_fwd, total;
+  size_t off_logits, off_ids, off_w, off_sorted, off_eids, off_ntpp, off_counts, off_runs,
+      off_align, off_fwd, total;
 };
 
 // shared = 1: the routing gets one more slot (the shared expert, index E), so the table,
@@ -544,6 +546,7 @@ LayerPlan plan_layer(int T, int H, int I, int E, int k, moe_dtype dt, int shared
   p.off_eids = off; off += round_up(static_cast<size_t>(p.cap / p.bm) * sizeof(int32_t));
   p.off_ntpp = off; off += round_up(sizeof(int32_t));
   p.off_counts = off; off += round_up(static_cast<size_t>(ES) * sizeof(int32_t));
+  p.off_runs = off; off += round_up(static_cast<size_t>(p.cap / p.bm + 1) * sizeof(int2));
   p.off_align = off; off += round_up(moe::align_ws_bytes(static_cast<int>(R), ES));
   p.off_fwd = off; off += forward_ws_full(T, H, I, ES, KS, dt);
   p.total = off;
@@ -595,6 +598,7 @@ moe_status layer_impl(const void* x, const void* wg, const void* w13, const floa
   int32_t* eids = reinterpret_cast<int32_t*>(b + p.off_eids);
   int32_t* ntpp = reinterpret_cast<int32_t*>(b + p.off_ntpp);
   int32_t* counts = reinterpret_cast<int32_t*>(b + p.off_counts);
+  int2* runs = reinterpret_cast<int2*>(b + p.off_runs);
   hipStream_t s = static_cast<hipStream_t>(stream);
   moe::RouteArgs ra = route_args(cfg);
   ra.shared = shared;
@@ -624,11 +628,11 @@ moe_status layer_impl(const void* x, const void* wg, const void* w13, const floa
     e = moe::launch_route_fused(x, wg, T, H, E, k, ra, ids, tw, nullptr, s);
     if (e != hipSuccess) return hip_status(e, "router");
     e = moe::launch_align(ids, T * KS, ES, p.bm, p.cap, sorted, eids, ntpp, counts,
-                          reinterpret_cast<int32_t*>(b + p.off_align), expert_map, s);
+                          reinterpret_cast<int32_t*>(b + p.off_align), expert_map, s, runs);
     if (e != hipSuccess) return hip_status(e, "align");
     return forward_impl(x, w13, w13_scale, w2, w2_scale, tw, sorted, eids, ntpp, T, H, I, ES, KS,
                         p.bm, dt, MOE_VARIANT_AUTO, out, b + p.off_fwd,
-                        forward_ws_full(T, H, I, ES, KS, dt), stream, T);
+                        forward_ws_full(T, H, I, ES, KS, dt), stream, T, runs);
   }
   e = moe::launch_router_logits(x, wg, T, H, E, bf16_acts(dt), logits, s);
   if (e != hipSuccess) return hip_status(e, "router logits");
@@ -640,13 +644,14 @@ moe_status layer_impl(const void* x, const void* wg, const void* w13, const floa
     e = moe::launch_topk(logits, p.nz, nullptr, T, E, k, ra, ids, tw, s);
     if (e != hipSuccess) return hip_status(e, "top-k");
     e = moe::launch_align(ids, T * KS, ES, p.bm, p.cap, sorted, eids, ntpp, counts,
-                          reinterpret_cast<int32_t*>(b + p.off_align), expert_map, s);
+                          reinterpret_cast<int32_t*>(b + p.off_align), expert_map, s, runs);
     if (e != hipSuccess) return hip_status(e, "align");
   }
   return forward_impl(x, w13, w13_scale, w2, w2_scale, tw, sorted, eids, ntpp, T, H, I, ES, KS,
                       p.bm, dt, MOE_VARIANT_AUTO, out, b + p.off_fwd,
                       forward_ws_full(T, H, I, ES, KS, dt), stream,
-                      T);   // the router's k experts of a token are distinct
+                      T,    // the router's k experts of a token are distinct
+                      p.fused_route_align ? nullptr : runs);
 }
 
 }  // namespace
