@@ -45,6 +45,10 @@ def parse():
     ap.add_argument("--no-decode", action="store_true",
                     help="default Mixtral run: skip the DeepSeek decode sub-record and the "
                          "dense-GEMM calibration")
+    ap.add_argument("--no-stages", action="store_true",
+                    help="profiling runs: skip the per-stage timing (the standalone stage entry "
+                         "points), so that every GEMM dispatch of the run is the layer's own; "
+                         "the line then carries no roofline fraction")
     ap.add_argument("--eager", action="store_true",
                     help="time eager launches instead of HIP-graph replays of the step")
     ap.add_argument("--cpu-sample-tokens", type=int, default=None)
@@ -61,7 +65,8 @@ def parse():
     return ap.parse_args()
 
 
-KERNEL_SOURCES = ("gemm_pipe.hip", "decode.hip", "gemm.hip", "common.hpp", "dma.hpp")
+KERNEL_SOURCES = ("gemm_pipe.hip", "decode.hip", "gemm.hip", "common.hpp", "dma.hpp", "route_dev.hpp",
+                  "align_dev.hpp")
 
 
 def kernel_digest() -> str:
@@ -386,7 +391,9 @@ def measure(args, workload: str, T_override=None, with_cpu=True):
     # step left in the buffers)
     stage_names = ("route", "align", "gemm1", "gemm2", "combine")
     stages_ms = {}
-    if args.eager:
+    if args.no_stages:
+        pass
+    elif args.eager:
         marks = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
         for i in range(args.steps):
             launch_staged(i, cur_sp(), marks[i])
@@ -410,7 +417,7 @@ def measure(args, workload: str, T_override=None, with_cpu=True):
             torch.cuda.synchronize()
             stages_ms[nm] = e0.elapsed_time(e1) / args.steps
             del g
-    g1_ms = stages_ms["gemm1"]
+    g1_ms = stages_ms.get("gemm1")
     flops = 2 * T * K1 * 3 * H * I        # useful expert FLOPs (the shared slot included)
     g1_flops = 2 * R * 2 * I * H
     decode = T <= 256
@@ -427,7 +434,8 @@ def measure(args, workload: str, T_override=None, with_cpu=True):
         value, unit = wbytes / (ms * 1e-3) / 1e9, "GB/s"
         # GEMM1 streams W13: 2I*H weights (+ 2I row scales with FP8 weights)
         g1_bytes = n_act * (2 * I * H + 2 * I * 4 if fp8 else 2 * I * H * 2)
-        roof = {"bound": "hbm", "achieved": g1_bytes / (g1_ms * 1e-3) / 1e9, "peak": PEAK_HBM_GBS,
+        roof = {"bound": "hbm", "achieved": g1_bytes / (g1_ms * 1e-3) / 1e9 if g1_ms else None,
+                "peak": PEAK_HBM_GBS,
                 "unit": "GB/s", "traffic": measured_traffic(traffic_key)}
     else:
         if emap is not None:
@@ -441,10 +449,10 @@ def measure(args, workload: str, T_override=None, with_cpu=True):
             flops = 2 * r_local * 3 * H * I
             g1_flops = 2 * r_local * 2 * I * H
         value, unit = flops / (ms * 1e-3) / 1e12, "TFLOPS"
-        roof = {"bound": "mfma", "achieved": g1_flops / (g1_ms * 1e-3) / 1e12,
+        roof = {"bound": "mfma", "achieved": g1_flops / (g1_ms * 1e-3) / 1e12 if g1_ms else None,
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "traffic": measured_traffic(traffic_key)}
-    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["frac"] = roof["achieved"] / roof["peak"] if roof["achieved"] else None
     roof["kernel"] = ("moe_decode_kernel<GEMM1+SwiGLU>" if variant == m.VARIANT_DECODE
                       else "moe_gemm_pipe_kernel<GEMM1+SwiGLU>")
     roof["kernel_ms"] = g1_ms
@@ -460,8 +468,9 @@ def measure(args, workload: str, T_override=None, with_cpu=True):
                       "step": "stage-by-stage calls" if staged else "moe_layer",
                       "step_ms_p10_p50_p90": [pct(0.1), pct(0.5), pct(0.9)],
                       "stages_ms": {nm: round(v, 4) for nm, v in stages_ms.items()},
-                      "route_align_combine_share": (stages_ms["route"] + stages_ms["align"] +
-                                                    stages_ms["combine"]) / sum(stages_ms.values()),
+                      "route_align_combine_share": ((stages_ms["route"] + stages_ms["align"] +
+                                                     stages_ms["combine"]) / sum(stages_ms.values())
+                                                    if stages_ms else None),
                       "parallelism": "single-gpu"},
            "roofline": roof}
     if decode:

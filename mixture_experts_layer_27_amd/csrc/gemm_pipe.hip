@@ -90,9 +90,12 @@ struct PCfg {
 };
 
 // LDS swizzles (chunk c of row m lives at physical chunk c ^ sw(m)).  64-byte rows:
-// sw = ((m >> 1) ^ (m >> 3)) & 3; 128-byte rows: sw = (m >> 1) & 7.  Both spread the
-// MFMA operand reads (rows m..m+31 at one logical chunk) over all banks.
-__device__ __forceinline__ int sw4(int row) { return ((row >> 1) ^ (row >> 3)) & 3; }
+// sw = (m >> 2) & 3; 128-byte rows: sw = (m >> 1) & 7.  Both spread the MFMA operand
+// reads (rows m..m+31 at one logical chunk) over all banks: measured with
+// SQ_LDS_BANK_CONFLICT on the 128-row tiles (Qwen3 shape), (m >> 2) & 3 takes the
+// conflict cycles from half of the LDS-active cycles to none, where
+// ((m >> 1) ^ (m >> 3)) & 3 left them.
+__device__ __forceinline__ int sw4(int row) { return (row >> 2) & 3; }
 template <int ROWB>
 __device__ __forceinline__ int swz(int row) { return ROWB == 64 ? sw4(row) : ((row >> 1) & 7); }
 template <int ROWB>
