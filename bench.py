@@ -544,17 +544,20 @@ def main():
         print("bench.py measures one GPU: this layer's benchmark runs on a single MI355X "
               "(no sharding); run it with --gpus 1", file=sys.stderr)
         sys.exit(2)
+    headline = (args.workload == "mixtral" and args.T is None and args.block_m is None
+                and args.ep == 1 and not args.no_decode)
+    decode = {}
+    if headline:
+        # the second headline target, measured in the same run (first, so that the one-token
+        # step does not follow the dense calibration GEMMs): DeepSeek-V3-shaped decode
+        for T in (1, 16, 64):
+            decode[f"T{T}"] = decode_summary(measure(args, "deepseek_decode", T, with_cpu=False))
     rec = measure(args, args.workload, args.T)
-    if args.workload == "mixtral" and args.T is None and args.block_m is None and args.ep == 1 \
-            and not args.no_decode:
-        # the second headline target, measured in the same run: DeepSeek-V3-shaped decode
+    if headline:
         c = rec["config"]
         rec["calibration"] = dense_calibration(c["T"], c["H"], c["I"], c["k"], args.steps)
         rec["decode"] = {"workload": "deepseek_decode (E=256, k=8, H=7168, I=2048, bf16, "
-                                     "sigmoid + bias grouped routing)"}
-        for T in (1, 16, 64):
-            rec["decode"][f"T{T}"] = decode_summary(measure(args, "deepseek_decode", T,
-                                                            with_cpu=False))
+                                     "sigmoid + bias grouped routing)", **decode}
         if "cpu_baseline" in rec:
             rec["cpu_baseline"]["tiny_layer"] = tiny_oracle_timings()
     print(json.dumps(rec), flush=True)
