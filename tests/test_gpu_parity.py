@@ -525,12 +525,15 @@ def test_layer_reduced(lib, name, T, scale):
 @pytest.mark.parametrize("name,T", [("deepseek_decode", 1), ("deepseek_decode", 3),
                                     ("deepseek_decode", 8), ("deepseek_decode_fp8", 2),
                                     ("qwen3_skewed", 5), ("mixtral", 4), ("mixtral_fp8", 3),
-                                    ("deepseek_decode", 4)])
+                                    ("deepseek_decode", 4), ("mixtral", 1), ("qwen3_skewed", 1),
+                                    ("gptoss", 1), ("deepseek_decode_fp8", 1)])
 def test_layer_small_batch_repeated(lib, name, T):
     """Small decode batches (one-launch route + align, weight-streaming GEMMs): three calls
     in a row on the same buffers with new activations (so the experts change), each against
     the oracle.  Up to T = 4 the GEMMs stream only the first four token rows of a sub-tile
-    (an expert holds at most T rows); Mixtral's 8 experts at T = 4 fill all four."""
+    (an expert holds at most T rows); Mixtral's 8 experts at T = 4 fill all four.  At T = 1
+    GEMM1 routes the token itself and writes the table GEMM2 reads (every routing rule:
+    softmax with and without offsets, top-k then softmax, grouped sigmoid + bias)."""
     base = S.WORKLOADS[name]
     q = 128 if name.endswith("fp8") else 64
     wl = base.scaled(T=T, H=base.H // 4 // q * q, I=base.I // 4 // q * q)
@@ -751,7 +754,10 @@ def test_layer_ep(lib, name, T, scale):
 @pytest.mark.parametrize("name,T,scale", [("kimi_k2_decode", 1, 4), ("kimi_k2_decode", 8, 4),
                                           ("kimi_k2_decode", 64, 4), ("kimi_k2_decode", 600, 8),
                                           ("deepseek_decode", 16, 4), ("mixtral", 512, 16),
-                                          ("deepseek_decode_fp8", 8, 4)])
+                                          ("deepseek_decode_fp8", 8, 4),
+                                          # one token, E <= 256: routed inside GEMM1 with
+                                          # the shared slot as the (k+1)-th row
+                                          ("deepseek_decode", 1, 4), ("deepseek_decode_fp8", 1, 4)])
 def test_layer_shared_expert(lib, name, T, scale):
     """moe_layer_shared: the routing's extra column is the shared expert (E, weight 1) and
     the output matches the oracle's per-expert loop over k routed slots + the shared
