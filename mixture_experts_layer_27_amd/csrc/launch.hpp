@@ -20,6 +20,10 @@ struct RouteArgs {
 // bf16 logits at decode batch sizes are produced as router_slabs(T,H) partial slabs
 // [nz][T][E] that the top-k stage adds in ascending order (nz == 1: plain logits).
 int router_slabs(int T, int H, bool bf16);
+// one token, bf16 (H % 8 == 0): the E logits whole ([E] fp32, one one-wave work-group per
+// expert)
+hipError_t launch_router_logits_gemv(const void* x, const void* wg, int H, int E,
+                                     float* logits, hipStream_t s);
 hipError_t launch_router_logits(const void* x, const void* wg, int T, int H, int E, bool bf16,
                                 float* logits, hipStream_t s);
 // logits_out (nullable) receives the summed logits when nz > 1; ids / w are [T][k + a.shared]

@@ -604,17 +604,17 @@ moe_status layer_impl(const void* x, const void* wg, const void* w13, const floa
   ra.shared = shared;
   hipError_t e = hipSuccess;
   if (p.route_in_gemm1 && !expert_map) {
-    // one token: the router's logit slabs, then GEMM1 routes the token itself (every wave
+    // one token: the router logits (whole), then GEMM1 routes the token itself (every wave
     // selects and ranks the experts; work-group 0 writes the routing and the table),
     // GEMM2, the combine
-    e = moe::launch_router_logits(x, wg, T, H, E, true, logits, s);
+    e = moe::launch_router_logits_gemv(x, wg, H, E, logits, s);
     if (e != hipSuccess) return hip_status(e, "router logits");
     uint8_t* fw = b + p.off_fwd;
     void* a = fw;
     float* y = reinterpret_cast<float*>(fw + round_up(static_cast<size_t>(KS) * I * esize(dt)));
     moe::GemmArgs g1 = gemm_args(x, w13, w13_scale, a, nullptr, sorted, eids, ntpp, T, H, I, ES,
                                  KS, p.bm);
-    e = moe::launch_decode_gemm1_routed(g1, logits, p.nz, ra, E, k, ids, tw, counts, s);
+    e = moe::launch_decode_gemm1_routed(g1, logits, 1, ra, E, k, ids, tw, counts, s);
     if (e != hipSuccess) return hip_status(e, "gemm1 (routed)");
     moe::GemmArgs g2 = gemm_args(a, w2, w2_scale, y, tw, sorted, eids, ntpp, T, H, I, ES, KS,
                                  p.bm);

@@ -319,6 +319,45 @@ route_fused_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ 
   }
 }
 
+// One token, bf16: one one-wave work-group per expert (spread over every CU) computes the
+// whole dot product x . Wg[e] (lane l
+// takes the 8 elements at 512 c + 8 l of each 512-element chunk c, all chunks' loads in
+// flight together, fp32 FMAs in chunk order, then a fixed butterfly over the lanes), so
+// the logits come out whole and the selection reads one value per expert instead of
+// summing K slabs.
+__global__ void __launch_bounds__(64)
+router_logits_gemv_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ wg,
+                          int H, int E, float* __restrict__ logits) {
+  constexpr int kB = 16;                           // chunks loaded per round trip (H <= 8192: one)
+  const int lane = lane_id();
+  const int e = blockIdx.x;
+  const uint16_t* wr = wg + static_cast<int64_t>(e) * H;
+  const int nch = (H + 511) / 512;
+  float acc = 0.f;
+  for (int c0 = 0; c0 < nch; c0 += kB) {
+    u32x4 a[kB], b[kB];
+#pragma unroll
+    for (int q = 0; q < kB; ++q) {
+      const int k = min((c0 + q) * 512 + lane * 8, H - 8);   // H % 8 == 0
+      a[q] = *reinterpret_cast<const u32x4*>(x + k);
+      b[q] = *reinterpret_cast<const u32x4*>(wr + k);
+    }
+#pragma unroll
+    for (int q = 0; q < kB; ++q) {
+      if (c0 + q < nch && (c0 + q) * 512 + lane * 8 < H) {
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          acc = fmaf(__uint_as_float(a[q][d] << 16), __uint_as_float(b[q][d] << 16), acc);
+          acc = fmaf(__uint_as_float(a[q][d] & 0xffff0000u), __uint_as_float(b[q][d] & 0xffff0000u), acc);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, kWave);
+  if (lane == 0) logits[e] = acc;
+}
+
 // K slabs of the bf16 logits: at decode batch sizes enough work-groups to stream Wg
 // from many CUs, each slab a multiple of 256 columns (64 per wave).
 int slab_cols(int T, int H) {
@@ -392,6 +431,15 @@ hipError_t launch_router_logits(const void* x, const void* wg, int T, int H, int
                        dim3(static_cast<unsigned>((T + kRt - 1) / kRt), (E + kRt - 1) / kRt),
                        dim3(256), 0, s, xb, wb, T, H, E, logits);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_router_logits_gemv(const void* x, const void* wg, int H, int E,
+                                     float* logits, hipStream_t s) {
+  if (H % 8) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(router_logits_gemv_kernel, dim3(static_cast<unsigned>(E)),
+                     dim3(64), 0, s, static_cast<const uint16_t*>(x),
+                     static_cast<const uint16_t*>(wg), H, E, logits);
   return hipGetLastError();
 }
 
