@@ -119,10 +119,13 @@ int preferred_bm(int T, int H, int I, int E, int k, moe_dtype dt) {
   if (dt == MOE_F32) return 16;
   if (auto_variant(T, H, I, E, k, dt) == MOE_VARIANT_DECODE)
     return moe::decode_block_m(static_cast<int>(static_cast<int64_t>(T) * k), E);
-  // 256-row MFMA tiles once the average expert fills several of them (the padding of
-  // each expert's last tile is then a small fraction); 128-row tiles otherwise
+  // 256-row MFMA tiles halve the weight-tile reloads per row but pad each expert's last
+  // tile further.  Measured crossovers (average rows per expert): bf16 weights gain from
+  // 128 rows when the K loop is long (H >= 4096) and from 256 rows otherwise; FP8
+  // weights, whose 128-row tiles already stream half the bytes, gain only from 1024.
   const int64_t avg = static_cast<int64_t>(T) * k / E;
-  return avg >= 1024 ? 256 : 128;
+  if (dt == MOE_BF16_FP8W) return avg >= 1024 ? 256 : 128;
+  return avg >= (H >= 4096 ? 128 : 256) ? 256 : 128;
 }
 
 int resolve_variant(int variant, int T, int H, int I, int E, int k, moe_dtype dt) {
