@@ -170,7 +170,8 @@ moe_status moe_align_ep(const int32_t* topk_ids, int T, int k, int E, int block_
 /* Variant of the expert GEMMs: 0 = automatic (from T, k, E, H, I on the host),
  * 1 = prefill (MFMA tiles staged through LDS), 2 = decode (weight streaming, small M).
  * bf16 block_m limits: prefill >= 32, decode >= 16 (MOE_ERR_UNSUPPORTED otherwise);
- * fp32 takes any block_m.  FP8 weights: prefill block_m >= 128, decode >= 16.  The
+ * fp32 takes any block_m (16 x 64 MFMA tiles when block_m is a multiple of 16, one
+ * thread per output below that).  FP8 weights: prefill block_m >= 128, decode >= 16.  The
  * decode variant takes tables of at most 65536 rows (moe_align_capacity), larger
  * requests are MOE_ERR_UNSUPPORTED. */
 enum { MOE_VARIANT_AUTO = 0, MOE_VARIANT_PREFILL = 1, MOE_VARIANT_DECODE = 2 };

@@ -234,7 +234,85 @@ moe_gemm_bf16_kernel(KArgs p) {
   }
 }
 
-// ------------------------------------------------------------------ fp32 path (plain FMA)
+// ------------------------------------------------------------------ fp32 path
+// v_mfma_f32_16x16x4_f32 tiles for tables whose block_m is a multiple of 16 (every 16-row
+// tile then lies in one expert's block): a work-group of 4 waves computes 16 table rows x
+// 64 output columns (GEMM1: 64 gate columns and the matching 64 up columns), with K staged
+// through LDS in 32-element chunks (rows padded by one word, so that the 16 rows a step
+// reads fall in distinct banks).  Lane layout of one 16x16x4 step: lane i supplies
+// A[i % 16][i / 16] and B[i / 16][i % 16]; accumulator element j of lane i is
+// D[4 (i / 16) + j][i % 16].
+constexpr int kF32M = 16, kF32N = 64, kF32K = 32;
+
+template <int MODE>   // 1: GEMM1 + SwiGLU; 2: GEMM2 x router weight
+__global__ void __launch_bounds__(256)
+gemm_f32_mfma_kernel(const float* __restrict__ A, const float* __restrict__ W,
+                     const float* __restrict__ topk_w, const int32_t* __restrict__ sorted_ids,
+                     const int32_t* __restrict__ expert_ids, const int32_t* __restrict__ ntpp,
+                     int R, int gather_div, int K, int N, int block_m, float* __restrict__ out) {
+  constexpr int NB = MODE == 1 ? 2 : 1;          // weight blocks: gate and up, or W2 rows
+  __shared__ float sa[kF32M][kF32K + 1];
+  __shared__ float sb[NB * kF32N][kF32K + 1];
+  __shared__ int srow[kF32M];
+  const int m0 = blockIdx.x * kF32M, n0 = blockIdx.y * kF32N;
+  if (m0 >= *ntpp) return;
+  const int e = expert_ids[m0 / block_m];
+  if (MODE == 1 && e < 0) return;                // expert held by another GPU
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  if (tid < kF32M) srow[tid] = sorted_ids[m0 + tid];
+  __syncthreads();
+  if (MODE == 2 && e < 0) {
+    // zeros in this tile's slice of y, so the combine adds nothing for these rows
+    for (int idx = tid; idx < kF32M * kF32N; idx += 256) {
+      const int r = srow[idx / kF32N], col = n0 + idx % kF32N;
+      if (r < R && col < N) out[static_cast<int64_t>(r) * N + col] = 0.f;
+    }
+    return;
+  }
+  const int64_t wrows = MODE == 1 ? 2 * static_cast<int64_t>(N) : N;   // weight rows per expert
+  const float* we = W + static_cast<int64_t>(e) * wrows * K;
+  f32x4 acc[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int k0 = 0; k0 < K; k0 += kF32K) {
+    for (int idx = tid; idx < kF32M * kF32K; idx += 256) {
+      const int m = idx / kF32K, kk = idx % kF32K, r = srow[m];
+      sa[m][kk] = (r < R && k0 + kk < K)
+                      ? A[static_cast<int64_t>(r / gather_div) * K + k0 + kk] : 0.f;
+    }
+    for (int idx = tid; idx < NB * kF32N * kF32K; idx += 256) {
+      const int n = idx / kF32K, kk = idx % kF32K, col = n0 + n % kF32N;
+      const int64_t wrow = (MODE == 1 && n >= kF32N) ? N + col : col;
+      sb[n][kk] = (col < N && k0 + kk < K) ? we[wrow * K + k0 + kk] : 0.f;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int ks = 0; ks < kF32K / 4; ++ks) {
+      const float av = sa[lane & 15][4 * ks + (lane >> 4)];
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        const float bv = sb[b * kF32N + 16 * w + (lane & 15)][4 * ks + (lane >> 4)];
+        acc[b] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, acc[b], 0, 0, 0);
+      }
+    }
+    __syncthreads();
+  }
+  const int col = n0 + 16 * w + (lane & 15);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int r = srow[4 * (lane >> 4) + j];
+    if (r >= R || col >= N) continue;
+    if (MODE == 1) {
+      const float g = acc[0][j], u = acc[1][j];
+      out[static_cast<int64_t>(r) * N + col] = g / (1.f + expf(-g)) * u;
+    } else {
+      out[static_cast<int64_t>(r) * N + col] = topk_w[r] * acc[0][j];
+    }
+  }
+}
+
+// Scalar kernels for tables with block_m not a multiple of 16 (a 16-row tile would span
+// experts there): one thread per output, K walked in order.
 __global__ void __launch_bounds__(256)
 gemm1_f32_kernel(const float* __restrict__ x, const float* __restrict__ w13,
                  const int32_t* __restrict__ sorted_ids, const int32_t* __restrict__ expert_ids,
@@ -393,6 +471,14 @@ int prefill_tile_m(int block_m) {
 hipError_t launch_gemm1(const GemmArgs& g, bool bf16, int variant, hipStream_t s) {
   if (g.T == 0 || g.cap == 0) return hipSuccess;
   if (bf16) return dispatch_bf16<1>(g, variant, s);
+  if (g.block_m % kF32M == 0) {
+    hipLaunchKernelGGL(gemm_f32_mfma_kernel<1>,
+                       dim3(static_cast<unsigned>(g.cap / kF32M), static_cast<unsigned>((g.I + kF32N - 1) / kF32N)),
+                       dim3(256), 0, s, static_cast<const float*>(g.A), static_cast<const float*>(g.B),
+                       nullptr, g.sorted_ids, g.expert_ids, g.ntpp, g.T * g.k, g.k, g.H, g.I,
+                       g.block_m, static_cast<float*>(g.C));
+    return hipGetLastError();
+  }
   const int64_t n = g.cap * g.I;
   hipLaunchKernelGGL(gemm1_f32_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0,
                      s, static_cast<const float*>(g.A), static_cast<const float*>(g.B),
@@ -404,6 +490,14 @@ hipError_t launch_gemm1(const GemmArgs& g, bool bf16, int variant, hipStream_t s
 hipError_t launch_gemm2(const GemmArgs& g, bool bf16, int variant, hipStream_t s) {
   if (g.T == 0 || g.cap == 0) return hipSuccess;
   if (bf16) return dispatch_bf16<2>(g, variant, s);
+  if (g.block_m % kF32M == 0) {
+    hipLaunchKernelGGL(gemm_f32_mfma_kernel<2>,
+                       dim3(static_cast<unsigned>(g.cap / kF32M), static_cast<unsigned>((g.H + kF32N - 1) / kF32N)),
+                       dim3(256), 0, s, static_cast<const float*>(g.A), static_cast<const float*>(g.B),
+                       g.topk_w, g.sorted_ids, g.expert_ids, g.ntpp, g.T * g.k, 1, g.I, g.H,
+                       g.block_m, static_cast<float*>(g.C));
+    return hipGetLastError();
+  }
   const int64_t n = g.cap * g.H;
   hipLaunchKernelGGL(gemm2_f32_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0,
                      s, static_cast<const float*>(g.A), static_cast<const float*>(g.B), g.topk_w,

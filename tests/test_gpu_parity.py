@@ -248,6 +248,19 @@ def test_forward_fp32_tiny_layer(lib):
         _forward_case(lib, lay.x, lay.wg, lay.w13, lay.w2, 2, 0, bm, 0)
 
 
+@pytest.mark.parametrize("T,H,I,E,k,bm", [(37, 40, 72, 5, 2, 16), (37, 40, 72, 5, 2, 32),
+                                          (130, 200, 136, 6, 3, 64), (1, 96, 33, 4, 2, 16)])
+def test_forward_fp32_ragged(lib, T, H, I, E, k, bm):
+    """fp32 MFMA tiles with K and N that are not multiples of the 32-element K chunk or
+    the 64-column tile (and a block_m of several 16-row tiles), against the oracle loop."""
+    g = torch.Generator().manual_seed(T + H + I)
+    x = torch.randn(T, H, generator=g)
+    wg = torch.randn(E, H, generator=g) / H ** 0.5
+    w13 = torch.randn(E, 2 * I, H, generator=g) / H ** 0.5
+    w2 = torch.randn(E, H, I, generator=g) / I ** 0.5
+    assert _forward_case(lib, x, wg, w13, w2, k, 0, bm, 0) <= 1e-5
+
+
 @pytest.mark.parametrize("case", ["uniform", "skewed", "decode", "top1"])
 def test_forward_page_test_matrix(lib, case):
     x, wg, w1, w3, w2, k = S.page_test_case(case)
