@@ -139,7 +139,7 @@ struct Frags<FM, FN, 1> {
 // groups in flight at once on the 8 XCDs cover many m-tiles of the same weight
 // columns); otherwise m-groups outer (an XCD's consecutive groups reuse the same token
 // rows while the weight columns advance).  The host picks n_outer when there are more
-// m-tiles than n-blocks.  Returns false for the padding slots of the last groups.
+// m-tiles than n-blocks.  Returns false for the slots past the last group.
 template <int GM, int GN>
 __device__ __forceinline__ bool grouped_slot(int bid, int mtiles, int nblocks, bool n_outer,
                                              int& mt, int& nb) {
@@ -287,8 +287,12 @@ moe_gemm_pipe_kernel(PArgs p) {
     const int64_t q = n * xcd / 8 + j;
     if (q >= n * (xcd + 1) / 8) return;
     expert_tile(q, p, mt, nb);
-  } else if (!grouped_slot<kGroupM, kGroupN>(blockIdx.x, p.mtiles, p.nblocks, p.n_outer, mt, nb)) {
-    return;
+  } else {
+    // groups over the m-tiles that hold routed rows (from the padded total), not over the
+    // table's capacity: the slots past them then come last in every XCD's order instead
+    // of interleaving empty work-groups with the real ones
+    const int mreal = min(p.mtiles, (*p.ntpp + BM - 1) / BM);
+    if (!grouped_slot<kGroupM, kGroupN>(blockIdx.x, mreal, p.nblocks, p.n_outer, mt, nb)) return;
   }
   const int total = *p.ntpp;
   if (mt * BM >= total) return;
