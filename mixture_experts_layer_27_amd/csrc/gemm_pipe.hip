@@ -207,9 +207,20 @@ constexpr int kRunChunk = 8;
 // runs (a few hot experts holding most rows) the grouped raster measured faster (Qwen3
 // skewed routing: 3.58 against 3.80 ms for the layer)
 constexpr int kRunOrderMax = 32;
+// stands in for the longest-run entry when align supplied no run table, so that the
+// kernel's first loads (padded total, longest run) issue together without a branch
+__device__ const int2 kNoRunTable = {1 << 29, 0};
+template <typename Args>
+__device__ __forceinline__ const int2* longest_run_entry(const Args& p) {
+  return p.tile_run ? p.tile_run + p.mtiles / p.tile_div : &kNoRunTable;
+}
+template <typename Args>
+__device__ __forceinline__ bool use_run_order(const Args& p, int longest) {
+  return p.tile_run && longest * p.tile_div <= kRunOrderMax;
+}
 template <typename Args>
 __device__ __forceinline__ bool use_run_order(const Args& p) {
-  return p.tile_run && p.tile_run[p.mtiles / p.tile_div].x * p.tile_div <= kRunOrderMax;
+  return use_run_order(p, longest_run_entry(p)->x);
 }
 template <typename Args>
 __device__ __forceinline__ void expert_tile(int64_t q, const Args& p, int& mt, int& nb) {
@@ -253,13 +264,17 @@ moe_gemm_pipe_kernel(PArgs p) {
   __shared__ float sscale[WB == 1 ? BN : 1];      // FP8: scale of each B tile row
   __shared__ __attribute__((aligned(256))) uint8_t pf_sink[PFD > 0 ? 256 : 4];
 
+  // the two independent loads that every tile's mapping starts from, issued together (the
+  // mapping, the tile's expert and its row ids follow: three round trips in all)
+  const int total = *p.ntpp;                      // padded total
+  const int longest = longest_run_entry(p)->x;
   int mt, nb;
   int kb = 0, ke = p.K / C::BK;   // the K stages of this work-group
   int unit = -1;                  // >= 0: a K range of a split tile (writes partial sums)
   SplitPlan sp{0, 0, 0, 1};
   if (MODE == 2 && p.split_max > 1)
-    sp = split_plan(*p.ntpp, BM, p.nblocks, p.ncu, p.split_max, ke);
-  const bool run_order = use_run_order(p);
+    sp = split_plan(total, BM, p.nblocks, p.ncu, p.split_max, ke);
+  const bool run_order = use_run_order(p, longest);
   if (sp.parts > 1) {
     const int xcd = blockIdx.x & 7, j = blockIdx.x >> 3;
     const int x0 = static_cast<int>(static_cast<int64_t>(sp.full) * xcd / 8);
@@ -282,7 +297,7 @@ moe_gemm_pipe_kernel(PArgs p) {
     if (run_order) expert_tile(q, p, mt, nb);
     else strip_tile(q, sp.mreal, p.nblocks, mt, nb);
   } else if (run_order) {
-    const int64_t n = static_cast<int64_t>(*p.ntpp / BM) * p.nblocks;
+    const int64_t n = static_cast<int64_t>(total / BM) * p.nblocks;
     const int xcd = blockIdx.x & 7, j = blockIdx.x >> 3;
     const int64_t q = n * xcd / 8 + j;
     if (q >= n * (xcd + 1) / 8) return;
@@ -291,27 +306,24 @@ moe_gemm_pipe_kernel(PArgs p) {
     // groups over the m-tiles that hold routed rows (from the padded total), not over the
     // table's capacity: the slots past them then come last in every XCD's order instead
     // of interleaving empty work-groups with the real ones
-    const int mreal = min(p.mtiles, (*p.ntpp + BM - 1) / BM);
+    const int mreal = min(p.mtiles, (total + BM - 1) / BM);
     if (!grouped_slot<kGroupM, kGroupN>(blockIdx.x, mreal, p.nblocks, p.n_outer, mt, nb)) return;
   }
-  const int total = *p.ntpp;
   if (mt * BM >= total) return;
-  const int e = p.expert_ids[(mt * BM) / p.block_m];
-  if (MODE == 1 && e < 0) return;       // expert held by another GPU: nothing to compute
-
   const int tid = threadIdx.x, lane = lane_id(), w = wave_id();
   const int K = p.K;
-
-  // rows of the tile (sentinels read row 0 and are never stored); GEMM2 also stages the
-  // router weights here, so its epilogue issues no dependent global loads
+  // the tile's expert and its row ids are independent loads, issued together
   static_assert(C::NT >= BM, "one tile row per thread");
-  int valid = 0;
-  for (int m = tid; m < BM; m += C::NT) {
-    const int r = p.sorted_ids[static_cast<int64_t>(mt) * BM + m];
-    srow[m] = r;
-    if (MODE == 2) swt[m] = r < p.R ? p.topk_w[r] : 0.f;
-    valid = r < p.R;
-  }
+  const int e = p.expert_ids[(mt * BM) / p.block_m];
+  const int rid = tid < BM ? p.sorted_ids[static_cast<int64_t>(mt) * BM + tid] : p.R;
+  if (MODE == 1 && e < 0) return;       // expert held by another GPU: nothing to compute
+
+  // rows of the tile (sentinels read row 0 and are never stored).  GEMM2 also stages the
+  // router weights in LDS, so its epilogue issues no dependent global loads; they are
+  // stored there after the K loop, under which their loads complete.
+  const float wrow = (MODE == 2 && rid < p.R) ? p.topk_w[rid] : 0.f;
+  if (tid < BM) srow[tid] = rid;
+  const int valid = rid < p.R;
   if (MODE == 2 && e < 0) {
     // expert held by another GPU: zeros in this tile's slice of y, so the combine adds
     // nothing for these rows (the fix-up writes them for a split tile)
@@ -635,6 +647,10 @@ moe_gemm_pipe_kernel(PArgs p) {
   // (FP8 tiles always run the full-tile loop: the second instance would not fit their registers)
   if (WB == 1 || na == C::FM) kloop(T_{});
   else kloop(F_{});
+  if (MODE == 2 && unit < 0) {
+    if (tid < BM) swt[tid] = wrow;
+    __syncthreads();
+  }
 
   // ---- epilogue.  D layout (32x32): lane holds column (lane & 31),
   //      rows 8*(v/4) + 4*(lane/32) + (v%4), v = 0..15.
