@@ -319,10 +319,12 @@ moe_gemm_pipe_kernel(PArgs p) {
   if (MODE == 1 && e < 0) return;       // expert held by another GPU: nothing to compute
 
   // rows of the tile (sentinels read row 0 and are never stored).  GEMM2 also stages the
-  // router weights in LDS, so its epilogue issues no dependent global loads; they are
-  // stored there after the K loop, under which their loads complete.
+  // router weights in LDS, so its epilogue issues no dependent global loads; with bf16
+  // weights they are stored there after the K loop, under which their loads complete (the
+  // FP8 tiles, at the register limit, store them now)
   const float wrow = (MODE == 2 && rid < p.R) ? p.topk_w[rid] : 0.f;
   if (tid < BM) srow[tid] = rid;
+  if (MODE == 2 && WB == 1 && tid < BM) swt[tid] = wrow;
   const int valid = rid < p.R;
   if (MODE == 2 && e < 0) {
     // expert held by another GPU: zeros in this tile's slice of y, so the combine adds
@@ -413,9 +415,16 @@ moe_gemm_pipe_kernel(PArgs p) {
   };
 
   const int wm = w / WN, wn = w % WN;
+  // First tile row of this wave.  When the routed rows fit the tile's first half (an
+  // expert's last tile, mostly padding), each wave row takes half as many rows, so that
+  // both waves sharing a SIMD have MFMAs to issue instead of one row of waves doing all
+  // of them (bf16 weights; the FP8 tiles always run their fragments whole).
+  const bool half = WB == 2 && nv <= BM / 2;
+  const int wr0 = wm * (half ? C::WTM / 2 : C::WTM);
   // 32-row fragments of this wave holding routed rows; the rest of the tile is padding,
   // whose MFMAs and A-operand reads are skipped
-  const int na = __builtin_amdgcn_readfirstlane(min(C::FM, max(0, (nv - wm * C::WTM + 31) >> 5)));
+  const int na = __builtin_amdgcn_readfirstlane(
+      min(half ? C::FM / 2 : C::FM, max(0, (nv - wr0 + 31) >> 5)));
   f32x16 acc[C::FM][C::FN];
 #pragma unroll
   for (int i = 0; i < C::FM; ++i)
@@ -440,7 +449,7 @@ moe_gemm_pipe_kernel(PArgs p) {
       const int ch = 2 * ks + (lane >> 5);
 #pragma unroll
       for (int i = 0; i < C::FM; ++i) {
-        const int row = wm * C::WTM + i * 32 + (lane & 31);
+        const int row = wr0 + i * 32 + (lane & 31);
         if (decltype(full)::value || i < na) f.a[i] = *reinterpret_cast<const bf16x8*>(sa + pswz<C::ROWA>(row, ch));
       }
 #pragma unroll
@@ -452,7 +461,7 @@ moe_gemm_pipe_kernel(PArgs p) {
       const int h = lane >> 5;
 #pragma unroll
       for (int i = 0; i < C::FM; ++i) {
-        const int row = wm * C::WTM + i * 32 + (lane & 31);
+        const int row = wr0 + i * 32 + (lane & 31);
         if (decltype(full)::value || i < na) {
           f.a0[i] = *reinterpret_cast<const bf16x8*>(sa + pswz<C::ROWA>(row, 4 * ks + 2 * h));
           f.a1[i] = *reinterpret_cast<const bf16x8*>(sa + pswz<C::ROWA>(row, 4 * ks + 2 * h + 1));
@@ -532,7 +541,7 @@ moe_gemm_pipe_kernel(PArgs p) {
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
       if (q < C::FM) {
         if (decltype(full)::value || q < na)
-          g.a[q] = *reinterpret_cast<const bf16x8*>(sa + pswz<C::ROWA>(wm * C::WTM + q * 32 + (lane & 31), ch));
+          g.a[q] = *reinterpret_cast<const bf16x8*>(sa + pswz<C::ROWA>(wr0 + q * 32 + (lane & 31), ch));
       } else if (q < C::FM + C::FN) {
         g.b[q - C::FM] = *reinterpret_cast<const bf16x8*>(
             sb + pswz<C::ROWB>(wn * C::WTN + (q - C::FM) * 32 + (lane & 31), ch));
@@ -647,7 +656,7 @@ moe_gemm_pipe_kernel(PArgs p) {
   // (FP8 tiles always run the full-tile loop: the second instance would not fit their registers)
   if (WB == 1 || na == C::FM) kloop(T_{});
   else kloop(F_{});
-  if (MODE == 2 && unit < 0) {
+  if (MODE == 2 && WB == 2 && unit < 0) {
     if (tid < BM) swt[tid] = wrow;
     __syncthreads();
   }
@@ -664,6 +673,7 @@ moe_gemm_pipe_kernel(PArgs p) {
     __syncthreads();
 #pragma unroll
     for (int i = 0; i < C::FM; ++i) {
+      if (half && i >= C::FM / 2) continue;        // those rows belong to the next wave row
 #pragma unroll
       for (int q = 0; q < C::FN / 2; ++q) {
         const int lc = (wn * C::WTN) / 2 + q * 32 + (lane & 31);
@@ -673,7 +683,7 @@ moe_gemm_pipe_kernel(PArgs p) {
         const float su = WB == 1 ? sscale[wn * C::WTN + (2 * q + 1) * 32 + (lane & 31)] : 1.f;
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-          const int m = wm * C::WTM + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+          const int m = wr0 + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
           float g = acc[i][2 * q][v], u = acc[i][2 * q + 1][v];
           if (WB == 1) {
             g *= sg;
@@ -698,21 +708,24 @@ moe_gemm_pipe_kernel(PArgs p) {
     // split tile: raw fp32 sums of this K range, [BM][BN] per part
     float* part = p.partial + static_cast<int64_t>(unit) * BM * BN;
 #pragma unroll
-    for (int i = 0; i < C::FM; ++i)
+    for (int i = 0; i < C::FM; ++i) {
+      if (half && i >= C::FM / 2) continue;
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int m = wm * C::WTM + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+        const int m = wr0 + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
 #pragma unroll
         for (int j = 0; j < C::FN; ++j)
           part[m * BN + wn * C::WTN + j * 32 + (lane & 31)] = acc[i][j][v];
       }
+    }
   } else {
     float* out = static_cast<float*>(p.C);
 #pragma unroll
     for (int i = 0; i < C::FM; ++i) {
+      if (half && i >= C::FM / 2) continue;
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int m = wm * C::WTM + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+        const int m = wr0 + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
         const int r = srow[m];
         if (r >= p.R) continue;
         const float wr = swt[m];
