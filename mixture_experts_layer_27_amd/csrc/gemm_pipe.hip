@@ -415,16 +415,21 @@ moe_gemm_pipe_kernel(PArgs p) {
   };
 
   const int wm = w / WN, wn = w % WN;
-  // First tile row of this wave.  When the routed rows fit the tile's first half (an
-  // expert's last tile, mostly padding), each wave row takes half as many rows, so that
-  // both waves sharing a SIMD have MFMAs to issue instead of one row of waves doing all
-  // of them (bf16 weights; the FP8 tiles always run their fragments whole).
-  const bool half = WB == 2 && nv <= BM / 2;
-  const int wr0 = wm * (half ? C::WTM / 2 : C::WTM);
-  // 32-row fragments of this wave holding routed rows; the rest of the tile is padding,
-  // whose MFMAs and A-operand reads are skipped
+  // The 32-row fragments holding routed rows (the rest of the tile is padding, whose
+  // MFMAs and A-operand reads are skipped).  With bf16 weights they are split evenly over
+  // the two wave rows, the first row taking the odd one: an expert's last tile, partly
+  // padding, then keeps both waves of every SIMD issuing MFMAs instead of leaving the
+  // second row idle.  The FP8 tiles always run their fragments whole, at fixed rows.
+  static_assert(WM == 2, "two wave rows");
+  int wr0 = wm * C::WTM, nown = C::FM;             // first tile row, fragments owned
+  if constexpr (WB == 2) {
+    const int nf = min(2 * C::FM, (nv + 31) >> 5);
+    const int fa = min(C::FM, (nf + 1) >> 1);
+    wr0 = wm == 0 ? 0 : 32 * fa;
+    nown = wm == 0 ? fa : nf - fa;
+  }
   const int na = __builtin_amdgcn_readfirstlane(
-      min(half ? C::FM / 2 : C::FM, max(0, (nv - wr0 + 31) >> 5)));
+      WB == 2 ? nown : min(C::FM, max(0, (nv - wr0 + 31) >> 5)));
   f32x16 acc[C::FM][C::FN];
 #pragma unroll
   for (int i = 0; i < C::FM; ++i)
@@ -673,7 +678,7 @@ moe_gemm_pipe_kernel(PArgs p) {
     __syncthreads();
 #pragma unroll
     for (int i = 0; i < C::FM; ++i) {
-      if (half && i >= C::FM / 2) continue;        // those rows belong to the next wave row
+      if (i >= nown) continue;                     // rows of the other wave row, or padding
 #pragma unroll
       for (int q = 0; q < C::FN / 2; ++q) {
         const int lc = (wn * C::WTN) / 2 + q * 32 + (lane & 31);
@@ -709,7 +714,7 @@ moe_gemm_pipe_kernel(PArgs p) {
     float* part = p.partial + static_cast<int64_t>(unit) * BM * BN;
 #pragma unroll
     for (int i = 0; i < C::FM; ++i) {
-      if (half && i >= C::FM / 2) continue;
+      if (i >= nown) continue;
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int m = wr0 + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
@@ -722,7 +727,7 @@ moe_gemm_pipe_kernel(PArgs p) {
     float* out = static_cast<float*>(p.C);
 #pragma unroll
     for (int i = 0; i < C::FM; ++i) {
-      if (half && i >= C::FM / 2) continue;
+      if (i >= nown) continue;
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int m = wr0 + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
