@@ -121,11 +121,12 @@ int preferred_bm(int T, int H, int I, int E, int k, moe_dtype dt) {
     return moe::decode_block_m(static_cast<int>(static_cast<int64_t>(T) * k), E);
   // 256-row MFMA tiles halve the weight-tile reloads per row but pad each expert's last
   // tile further.  Measured crossovers (average rows per expert): bf16 weights gain from
-  // 128 rows when the K loop is long (H >= 4096) and from 256 rows otherwise; FP8
-  // weights, whose 128-row tiles already stream half the bytes, gain only from 1024.
+  // 128 rows (level there on the gpt-oss shape, H = 2880); FP8 weights, whose 128-row
+  // tiles already stream half the bytes, gain only from 1024.
+  (void)H;
   const int64_t avg = static_cast<int64_t>(T) * k / E;
   if (dt == MOE_BF16_FP8W) return avg >= 1024 ? 256 : 128;
-  return avg >= (H >= 4096 ? 128 : 256) ? 256 : 128;
+  return avg >= 128 ? 256 : 128;
 }
 
 int resolve_variant(int variant, int T, int H, int I, int E, int k, moe_dtype dt) {

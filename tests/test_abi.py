@@ -196,12 +196,12 @@ def test_fp8_weight_entry_points_validate(L):
     assert lib.moe_preferred_block_m(1, 7168, 2048, 256, 8, FP8) == 16
     assert lib.moe_preferred_block_m(4096, 4096, 14336, 8, 2, FP8) == 256
     assert lib.moe_preferred_block_m(2048, 4096, 14336, 8, 2, FP8) == 128
-    # bf16 prefill: 256-row tiles from 128 rows per expert at H >= 4096, from 256 below
+    # bf16 prefill: 256-row tiles from 128 rows per expert on average
     assert lib.moe_preferred_block_m(512, 4096, 14336, 8, 2, 1) == 256
     assert lib.moe_preferred_block_m(256, 4096, 14336, 8, 2, 1) == 128
     assert lib.moe_preferred_block_m(2048, 4096, 1536, 128, 8, 1) == 256
-    assert lib.moe_preferred_block_m(4096, 2880, 2880, 128, 4, 1) == 128
-    assert lib.moe_preferred_block_m(8192, 2880, 2880, 128, 4, 1) == 256
+    assert lib.moe_preferred_block_m(2048, 2880, 2880, 128, 4, 1) == 128
+    assert lib.moe_preferred_block_m(4096, 2880, 2880, 128, 4, 1) == 256
     # size queries reject sizes they cannot plan for instead of dividing by E = 0
     assert lib.moe_preferred_block_m(4, 64, 64, 0, 2, 1) == 0
     assert lib.moe_auto_variant(4, 64, 64, 8, 0, 1) == 0
