@@ -472,6 +472,28 @@ def test_forward_tile_boundary_loads(lib, bm, variant, fp8):
         _forward_given_routing(lib, x, w13, w2, ids, w32, bm, variant)
 
 
+@pytest.mark.parametrize("bm", [128, 256])
+def test_forward_partial_tile_fills(lib, bm):
+    """Prefill tiles holding every count of routed 32-row fragments, 1 .. bm/32: an expert
+    with 32j - 5 rows ends on a tile of j fragments, one with bm + 32j - 31 rows on a full
+    tile and a tile of j fragments (the routed fragments of a partly filled tile are
+    split over the two wave rows), against the oracle on every element."""
+    f = bm // 32
+    loads = [32 * j - 5 for j in range(1, f + 1)] + [bm + 32 * j - 31 for j in range(1, f + 1)]
+    k = 2
+    loads[-1] += sum(loads) % k
+    ids = S.ids_with_counts(loads, k, seed=bm).numpy()
+    T = ids.shape[0]
+    E = len(loads)
+    H, I = 256, 192
+    g = torch.Generator(device="cpu").manual_seed(bm + 11)
+    x = torch.randn(T, H, generator=g).to(torch.bfloat16)
+    w32 = _routing_weights(T, k, bm + 2)
+    w13 = (torch.randn(E, 2 * I, H, generator=g) / H ** 0.5).to(torch.bfloat16)
+    w2 = (torch.randn(E, H, I, generator=g) / I ** 0.5).to(torch.bfloat16)
+    _forward_given_routing(lib, x, w13, w2, ids, w32, bm, 1)
+
+
 @pytest.mark.parametrize("fp8", [False, True])
 @pytest.mark.parametrize("bm,variant", EDGE_CASES)
 def test_forward_one_expert_takes_every_token(lib, bm, variant, fp8):
