@@ -27,14 +27,6 @@ __device__ __forceinline__ void dma16_nt(const void* gptr, const MOE_LDS void* l
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off nt" : : "v"(gptr), "s"(l) : "memory", "m0");
 }
 
-// 4-byte global -> LDS DMA used as an L2 prefetch: each lane touches one cache line;
-// the bytes land in a scratch LDS slot nobody reads.
-__device__ __forceinline__ void prefetch_line(const void* gptr, const MOE_LDS void* lds_base) {
-  const uint32_t l = __builtin_amdgcn_readfirstlane(
-      static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds_base)));
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" : : "v"(gptr), "s"(l) : "memory", "m0");
-}
-
 // work-group barrier that also keeps the compiler from moving LDS accesses across it,
 // without the vmcnt(0) that __syncthreads() implies (the DMA ring stays in flight)
 __device__ __forceinline__ void barrier_keep_vm() {

@@ -8,18 +8,19 @@
 // * NSTAGE-deep ring of BK-element stages: BK = 64 (128-byte LDS rows, chunk c of row m
 //   at c ^ ((m >> 1) & 7)) for 256-row tiles, BK = 32 (64-byte rows, c ^ sw4(m)) for
 //   128-row tiles, whose 73 KB ring lets two work-groups share a CU; both swizzles are
-//   conflict-free for the DMA writes and the 32-row MFMA operand reads.  One barrier per
-//   stage, preceded by an explicit vmcnt wait for this wave's own loads, placed before
-//   the stage's last k16 step so that it and the next stage's first fragment reads sit in
-//   the shadow of the MFMAs already issued.  With two 64-element stages (bf16 256-row
-//   tiles) the slot just read is refilled right after that barrier, one DMA instruction
-//   between each two MFMAs; deeper rings refill the slot read one stage earlier.
+//   conflict-free for the DMA writes and the 32-row MFMA operand reads.
 // * v_mfma_f32_32x32x16_bf16, WM x WN waves each holding a (BM/WM) x (BN/WN) fp32
-//   accumulator tile: 2 x 2 (one wave per SIMD, up to 128 x 128), or 2 x 4 for the bf16
-//   256-row tiles (two waves per SIMD, 128 x 64 each); LDS fragments are double-buffered in
-//   registers and the reads of the next k16 step are spread between the MFMAs of this
-//   one; GEMM1 B tiles interleave 32-row gate and up blocks so that SwiGLU runs in
-//   registers.
+//   accumulator tile; GEMM1 B tiles interleave 32-row gate and up blocks so that SwiGLU
+//   runs in registers.
+// * bf16 256-row tiles: 2 x 4 waves (two per SIMD, 128 x 64 each) in a ping-pong schedule
+//   over two 64-element stages: the two waves of a SIMD alternate between loading a
+//   half-stage of fragments from LDS and a burst of MFMAs from registers, with a barrier
+//   at each turn and the DMAs between the MFMAs (see the K loop).
+// * Other tiles: 2 x 2 waves (one per SIMD, up to 128 x 128) and a ring of three or four
+//   stages, one barrier per stage preceded by an explicit vmcnt wait for the wave's own
+//   loads and placed before the stage's last k16 step; LDS fragments are double-buffered
+//   in registers and the reads of the next k16 step are spread between the MFMAs of this
+//   one.
 // * GEMM2 splits a short last round of tiles in K over every CU (see split_plan).
 // * FP8 expert weights (OCP E4M3 bytes, one fp32 scale per weight row; section 8 of the
 //   same page prices an expert at one byte per weight): the B tile is staged as bytes
@@ -251,10 +252,10 @@ __device__ __forceinline__ void strip_tile(int q, int mreal, int nblocks, int& m
 }
 
 // Two waves per SIMD: with 32-element stages (two work-groups per CU) and with 8-wave
-// work-groups (GEMM1 256 x 256 tiles: each wave a 128 x 64 accumulator, so a second wave
-// per SIMD issues MFMAs while the other waits on a barrier or an LDS read); the register
-// budget is held to that
-template <int MODE, int BM, int BN, int WM, int WN, int BK, int NSTAGE, int PFD, int WB>
+// work-groups (bf16 256 x 256 tiles: each wave a 128 x 64 accumulator, the two waves of a
+// SIMD taking turns at the MFMA pipe, see the ping-pong K loop); the register budget is
+// held to that
+template <int MODE, int BM, int BN, int WM, int WN, int BK, int NSTAGE, int WB>
 __global__ void __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu((BK == 32 || WM * WN == 8) ? 2 : 1)))
 moe_gemm_pipe_kernel(PArgs p) {
   using C = PCfg<MODE, BM, BN, WM, WN, BK, NSTAGE, WB>;
@@ -262,7 +263,6 @@ moe_gemm_pipe_kernel(PArgs p) {
   __shared__ int srow[BM];
   __shared__ float swt[MODE == 2 ? BM : 1];       // GEMM2: router weight of each tile row
   __shared__ float sscale[WB == 1 ? BN : 1];      // FP8: scale of each B tile row
-  __shared__ __attribute__((aligned(256))) uint8_t pf_sink[PFD > 0 ? 256 : 4];
 
   // the two independent loads that every tile's mapping starts from, issued together (the
   // mapping, the tile's expert and its row ids follow: three round trips in all)
@@ -384,25 +384,6 @@ moe_gemm_pipe_kernel(PArgs p) {
                ((pchb ^ swz<C::ROWB>(n)) << 4);
   }
 
-  // L2 prefetch of stage kt+PFD: lane l of wave w touches A row and B row
-  // (BM/NW)*w + l (rows wrap when a wave has fewer than 64 of them)
-  const uint16_t* pfa = nullptr;
-  const uint8_t* pfb = nullptr;
-  if constexpr (PFD > 0) {
-    const int m = (BM / C::NW) * w + lane % (BM / C::NW);
-    const int r = srow[m];
-    pfa = p.A + static_cast<int64_t>(r < p.R ? r / p.gather_div : 0) * K + kb * C::BK;
-    const int n = (BN / C::NW) * w + lane % (BN / C::NW);
-    pfb = b_base + static_cast<int64_t>(b_row(n)) * K * WB + kb * C::BK * WB;
-  }
-  auto prefetch = [&](int kt) {
-    if constexpr (PFD > 0) {
-      prefetch_line(pfa + kt * C::BK, (MOE_LDS void*)pf_sink);
-      prefetch_line(pfb + kt * C::BK * WB, (MOE_LDS void*)pf_sink);
-    }
-  };
-  constexpr int P = PFD > 0 ? 2 : 0;      // prefetch instructions per wave per stage
-
   auto issue = [&](int kt) {
     uint8_t* st = smem + (kt % NSTAGE) * C::STAGE;
     const int k0 = kt * C::BK;
@@ -502,32 +483,6 @@ moe_gemm_pipe_kernel(PArgs p) {
     }
   };
 
-  // The MFMAs of one k16 step with stage kt's DMA instructions spread between them (bf16
-  // two-stage ring): one DMA after each MFMA while both last.
-  auto mfma_issue_interleaved = [&](auto full, const auto& f, int kt) {
-    static_assert(WB == 2, "bf16 weights");
-    uint8_t* st = smem + (kt % NSTAGE) * C::STAGE;
-    const int k0 = kt * C::BK;
-    constexpr int NM = C::FM * C::FN;
-    if constexpr (C::NW == 8) __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-    for (int q = 0; q < NM; ++q) {
-      const int i = q / C::FN, j = q % C::FN;
-      if (decltype(full)::value || i < na) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
-#pragma unroll
-      for (int d = q * C::L / NM; d < (q + 1) * C::L / NM; ++d) {
-        if (d < C::LA) dma16(a_src[d] + k0, (MOE_LDS void*)(st + 1024 * (w + C::NW * d)));
-        else dma16(b_src[d - C::LA] + k0 * WB, (MOE_LDS void*)(st + C::SA + 1024 * (w + C::NW * (d - C::LA))));
-      }
-    }
-    if constexpr (C::NW == 8) __builtin_amdgcn_s_setprio(0);
-#pragma unroll
-    for (int d = (NM >= C::L ? C::L : NM * (C::L / NM)); d < C::L; ++d) {
-      if (d < C::LA) dma16(a_src[d] + k0, (MOE_LDS void*)(st + 1024 * (w + C::NW * d)));
-      else dma16(b_src[d - C::LA] + k0 * WB, (MOE_LDS void*)(st + C::SA + 1024 * (w + C::NW * (d - C::LA))));
-    }
-  };
-
   // The MFMAs of fragments f (bf16 weights) with the LDS reads of the next k16 step's
   // fragments g spread between them, so the operand reads of the waves sharing a SIMD do
   // not arrive at the LDS in one burst; with two waves per SIMD the MFMA cluster runs at
@@ -565,7 +520,146 @@ moe_gemm_pipe_kernel(PArgs p) {
   // The K loop, instantiated for full tiles and for a tile whose last fragments are padding
   auto kloop = [&](auto full) {
 
-  if constexpr (NSTAGE >= 3) {
+  if constexpr (NSTAGE == 2) {
+    // Ping-pong over a two-stage ring of 64-element stages (128-byte LDS rows, so each DMA
+    // request fetches whole 128-byte lines), consumed in 32-element half-stages.  Wave row 0
+    // (waves 0-3) and wave row 1 (waves 4-7) put one wave of each row on every SIMD and run
+    // half a phase apart: a wave alternates a load phase (the fragments of half-stage u from
+    // LDS into registers, awaited) and a compute phase (the MFMAs of half-stage u from
+    // registers); a barrier ends each phase and row 1 starts one barrier late, so on each
+    // SIMD one wave's MFMA burst runs while the other loads.  Barrier b ends phase b of row
+    // 0 and phase b-1 of row 1, so half-stage u is read after barrier 2u (row 0) and 2u+1
+    // (row 1).  Row 0 reads A rows 0-127 (in a tile that is partly padding, row 1 may start
+    // below 128), row 1 the rest, both all of B.
+    //
+    // Refills.  Stage S is read out once row 1 passes barrier 4S+4; stage S+2 then goes into
+    // its slot, and is first read after barrier 4S+8 (A rows 0-127 and B, by row 0) and
+    // 4S+9 (A rows 128-255, by row 1).  Row 1 fetches what is needed first, A rows 0-127
+    // and all of B (12 DMAs per wave), during its compute phase of half-stage 2S+1 right
+    // after barrier 4S+4, and waits for them before barrier 4S+8; row 0 fetches A rows
+    // 128-255 (4 per wave) during its compute phase of half-stage 2S+2 and waits for them
+    // before barrier 4S+9.  Each row thus has about three and a half phases of latency to
+    // cover.  The DMAs sit between the MFMAs at fixed positions (a branch around an MFMA
+    // costs more issue time than the DMA it would spread).  Every wave passes 4 nk + 1
+    // barriers here.
+    static_assert(NSTAGE == 2 && C::KS == 4 && WB == 2, "two 64-element bf16 stages");
+    static_assert(C::RPIA == 8 && C::RPIB == 8 && BM == 256 && BN == 256 && C::NW == 8, "tile");
+    constexpr int NM = 2 * C::FM * C::FN;               // MFMAs per compute phase (16)
+    constexpr int ND1 = 12, ND0 = 4;                    // DMAs per wave and stage (rows 1, 0)
+    const int grp = __builtin_amdgcn_readfirstlane(wm);
+    const int v = __builtin_amdgcn_readfirstlane(w & 3);          // wave within its row
+    // DMA j of this wave: j < 4 A rows (row 1: 8 (v + 4 j) .. +7; row 0: 128 + the same),
+    // j >= 4 (row 1 only) B rows 8 (v + 4 (j - 4)) .. +7; lanes as in issue()
+    const uint8_t* src[ND1];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int m = (grp ? 0 : 128) + 8 * (v + 4 * j) + lrow;
+      const int r = srow[m];
+      const int arow = r < p.R ? r / p.gather_div : 0;
+      src[j] = reinterpret_cast<const uint8_t*>(p.A + static_cast<int64_t>(arow) * K + kb * C::BK +
+                                                ((pch ^ swz<C::ROWA>(m)) << 3));
+    }
+#pragma unroll
+    for (int j = 4; j < ND1; ++j) {
+      const int n = 8 * (v + 4 * (j - 4)) + lrowb;
+      src[j] = b_base + static_cast<int64_t>(b_row(n)) * K * WB + kb * C::BK * WB +
+               ((pchb ^ swz<C::ROWB>(n)) << 4);
+    }
+    const int aofs = __builtin_amdgcn_readfirstlane((grp ? 0 : 128 * C::ROWA) + 1024 * v);
+    const int bofs = __builtin_amdgcn_readfirstlane(C::SA + 1024 * v);
+    auto dma_j = [&](int j, uint8_t* st, int kbytes) {
+      if (j < 4) dma16(src[j] + kbytes, (MOE_LDS void*)(st + aofs + 4096 * j));
+      else dma16(src[j] + kbytes, (MOE_LDS void*)(st + bofs + 4096 * (j - 4)));
+    };
+    auto issue_pp = [&](int S2) {
+      uint8_t* st = smem + (S2 % NSTAGE) * C::STAGE;
+      if (grp) {
+#pragma unroll
+        for (int j = 0; j < ND1; ++j) dma_j(j, st, S2 * C::BK * 2);
+      } else {
+#pragma unroll
+        for (int j = 0; j < ND0; ++j) dma_j(j, st, S2 * C::BK * 2);
+      }
+    };
+    auto load = [&](int S, int h) {
+      read_frags(full, S, 2 * h, fr[0]);
+      read_frags(full, S, 2 * h + 1, fr[1]);
+      wait_lgkm0();
+    };
+    // the MFMAs of the registers' half-stage; with ndma > 0, DMA d of stage S2 after MFMA
+    // d + d / 3 (12 DMAs) or 4 d (4 DMAs)
+    auto compute = [&](auto ndma, int S2) {
+      constexpr int ND = decltype(ndma)::value;
+      static_assert(ND == 0 || ND == ND0 || ND == ND1, "DMA count");
+      uint8_t* st = smem + (S2 % NSTAGE) * C::STAGE;
+      const int kbytes = S2 * C::BK * 2;
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int q = 0; q < NM; ++q) {
+        const int ks = q / (C::FM * C::FN), i = (q / C::FN) % C::FM, j = q % C::FN;
+        if (decltype(full)::value || i < na)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[ks].a[i], fr[ks].b[j], acc[i][j], 0, 0, 0);
+        const bool has = ND == ND1 ? (q % 4 != 3) : (ND == ND0 ? q % 4 == 0 : false);
+        if (has) {
+          const int d = ND == ND1 ? q - q / 4 : q / 4;
+          __builtin_amdgcn_sched_barrier(0);     // the DMA stays between these MFMAs
+          dma_j(d, st, kbytes);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    using N0 = std::integral_constant<int, 0>;
+    using NR0 = std::integral_constant<int, ND0>;
+    using NR1 = std::integral_constant<int, ND1>;
+    // Each row runs its own loop, peeled so that whether a compute phase refills is known
+    // at compile time (a runtime choice between the two forms makes the register
+    // allocation spill).
+    issue_pp(0);
+    if (nk > 1) issue_pp(1);
+    wait_vm(nk > 1 ? (grp ? ND1 : ND0) : 0);
+    barrier_keep_vm();
+    if (grp == 0) {
+      // half-stage 2S (after a wait for this row's part of stage S, S >= 1), refilling stage
+      // S+1 for 1 <= S < nk-1; half-stage 2S+1
+      auto iter = [&](auto nd, int S) {
+        load(S, 0);
+        if (S > 0) wait_vm_c<0>();
+        barrier_keep_vm();
+        compute(nd, S + 1);
+        barrier_keep_vm();
+        load(S, 1);
+        barrier_keep_vm();
+        compute(N0{}, 0);
+        barrier_keep_vm();
+      };
+      int S = 0;
+      for (; S < nk && (S == 0 || S + 1 >= nk); ++S) iter(N0{}, S);
+      for (; S + 1 < nk; ++S) iter(NR0{}, S);
+      for (; S < nk; ++S) iter(N0{}, S);
+      barrier_keep_vm();
+    } else {
+      barrier_keep_vm();
+      // half-stage 2S; half-stage 2S+1 (after a wait for this row's part of stage S+1),
+      // refilling stage S+2 for S < nk-2
+      auto iter = [&](auto nd, int S) {
+        load(S, 0);
+        barrier_keep_vm();
+        compute(N0{}, 0);
+        barrier_keep_vm();
+        load(S, 1);
+        wait_vm_c<0>();
+        barrier_keep_vm();
+        compute(nd, S + 2);
+        barrier_keep_vm();
+      };
+      int S = 0;
+      for (; S + 2 < nk; ++S) iter(NR1{}, S);
+      for (; S < nk; ++S) iter(N0{}, S);
+    }
+    wait_vm_c<0>();
+  } else {
+    static_assert(NSTAGE >= 3, "ring depth");
     // Ring of NSTAGE stages, NSTAGE-1 in flight.  The barrier that publishes stage kt+1
     // sits before the last k16 step of stage kt, so the first fragments of kt+1 are read
     // while that step computes.  The slot refilled after it, (kt+NSTAGE-1) % NSTAGE, held
@@ -608,53 +702,6 @@ moe_gemm_pipe_kernel(PArgs p) {
     for (; kt + NSTAGE <= nk; ++kt) stage(T_{}, T_{}, kt, 0);
     for (; kt + 1 < nk; ++kt) stage(T_{}, F_{}, kt, (min(kt + NSTAGE - 2, nk - 1) - (kt + 1)) * C::L);
     stage(F_{}, F_{}, kt, 0);
-  } else {
-    // Two stages.  Stage kt+1 is published at a barrier placed before the last k16 step of
-    // stage kt, so the barrier and the first fragment reads of stage kt+1 sit in the shadow
-    // of the MFMAs already issued; every wave has read all of stage kt by then (its LDS
-    // reads are awaited before the barrier), so the slot of stage kt is refilled with stage
-    // kt+2 right after it, one DMA instruction after each MFMA of that last step so the
-    // MFMA pipe keeps running while the DMAs issue.  With PFD > 0, stage kt+2+PFD is also
-    // touched into L2 after that refill; the waits leave those prefetches in flight.
-    int npf = 0;                                  // prefetch instructions issued, not yet covered
-    issue(0);
-    if (nk > 1) issue(1);
-    if constexpr (PFD > 0) {
-      for (int d = 2; d < 2 + PFD && d < nk; ++d, npf += P) prefetch(d);
-    }
-    wait_vm((nk > 1 ? C::L : 0) + npf);
-    barrier_keep_vm();
-    read_frags(full, 0, 0, fr[0]);
-    // pf: prefetch instructions issued after stage kt+1's DMAs (they may stay in flight)
-    auto stage = [&](auto refill, int kt, int pf) {
-#pragma unroll
-      for (int ks = 0; ks < NSTEP; ++ks) {
-        if (ks + 1 < NSTEP) {
-          mfma_reads(full, fr[ks & 1], kt, ks + 1, fr[(ks + 1) & 1]);
-          __builtin_amdgcn_sched_barrier(0);
-          continue;
-        }
-        if (kt + 1 < nk) {
-          wait_lgkm0();
-          wait_vm(pf);
-          barrier_keep_vm();
-          read_frags(full, kt + 1, 0, fr[0]);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-        if constexpr (decltype(refill)::value) {
-          mfma_issue_interleaved(full, fr[ks & 1], kt + 2);
-          if (kt + 2 + PFD < nk) prefetch(kt + 2 + PFD);
-        } else {
-          mfma_all(full, fr[ks & 1]);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    };
-    int kt = 0;
-    // prefetch instructions issued after the refill of stage kt+1 (at stage kt-1)
-    for (; kt + 2 < nk; ++kt) stage(T_{}, kt, (kt >= 1 && kt + 1 + PFD < nk) ? P : (kt == 0 ? npf : 0));
-    for (; kt < nk; ++kt) stage(F_{}, kt, (kt >= 1 && kt + 1 + PFD < nk) ? P : (kt == 0 ? npf : 0));
-    wait_vm_c<0>();
   }
 
   };
@@ -797,7 +844,7 @@ int device_cu_count() {
   return v;
 }
 
-template <int MODE, int BM, int BN, int WM, int WN, int BK, int NSTAGE, int PFD, int WB = 2>
+template <int MODE, int BM, int BN, int WM, int WN, int BK, int NSTAGE, int WB = 2>
 hipError_t run_pipe(const GemmArgs& g, hipStream_t s) {
   PArgs p{};
   const bool g1 = MODE == 1;
@@ -829,8 +876,9 @@ hipError_t run_pipe(const GemmArgs& g, hipStream_t s) {
   if (G == 0) return hipSuccess;
   p.split_max = 1;
   if (MODE == 2 && g.split_ws) {
-    // 32-element stages run two work-groups per CU (see the kernel's register budget)
-    const int ncu = device_cu_count() * (BK == 32 ? 2 : 1);
+    // 4-wave work-groups with 32-element stages run two per CU (two waves per SIMD, 72 KB
+    // of LDS each); the others one
+    const int ncu = device_cu_count() * (BK == 32 && WM * WN == 4 ? 2 : 1);
     if (ncu > 0 && g.split_ws_bytes >= static_cast<size_t>(ncu) * BM * BN * sizeof(float)) {
       p.split_max = 4;
       p.ncu = ncu;
@@ -840,7 +888,7 @@ hipError_t run_pipe(const GemmArgs& g, hipStream_t s) {
       G = std::max<int64_t>(G, (static_cast<int64_t>(p.mtiles) * p.nblocks + ncu + 16 + 7) / 8 * 8);
     }
   }
-  hipLaunchKernelGGL((moe_gemm_pipe_kernel<MODE, BM, BN, WM, WN, BK, NSTAGE, PFD, WB>),
+  hipLaunchKernelGGL((moe_gemm_pipe_kernel<MODE, BM, BN, WM, WN, BK, NSTAGE, WB>),
                      dim3(static_cast<unsigned>(G)), dim3(WM * WN * 64), 0, s, p);
   if (MODE == 2 && p.split_max > 1)
     hipLaunchKernelGGL((gemm2_split_fixup_kernel<BM, BN, BK>),
@@ -854,27 +902,27 @@ hipError_t run_pipe(const GemmArgs& g, hipStream_t s) {
 // block_m does not allow a 128/256-row tile (callers fall back to gemm.hip's tiles).
 hipError_t launch_pipe_gemm1(const GemmArgs& g, int tile_m, hipStream_t s) {
   if (g.w_scale) {     // FP8 weights: the half-size B tile leaves room for a deeper ring
-    if (tile_m == 256) return run_pipe<1, 256, 256, 2, 2, 64, 3, 0, 1>(g, s);
-    if (tile_m == 128) return run_pipe<1, 128, 256, 2, 2, 64, 4, 0, 1>(g, s);
+    if (tile_m == 256) return run_pipe<1, 256, 256, 2, 2, 64, 3, 1>(g, s);
+    if (tile_m == 128) return run_pipe<1, 128, 256, 2, 2, 64, 4, 1>(g, s);
     return hipErrorInvalidValue;
   }
-  // 8 waves (2 x 4, two per SIMD) for the 256-row tile: with the operand reads spread
-  // between the MFMAs they measure faster than 4 (Mixtral-8x7B shape: 1.84 vs 1.88 ms)
-  if (tile_m == 256) return run_pipe<1, 256, 256, 2, 4, 64, 2, 0>(g, s);
-  if (tile_m == 128) return run_pipe<1, 128, 256, 2, 2, 32, 3, 0>(g, s);
+  // 8 waves (2 x 4, two per SIMD) in the ping-pong schedule for the 256-row tile
+  // (Mixtral-8x7B shape: 1.70 ms against 1.84 ms for the same 8 waves with the operand
+  // reads and DMAs spread between the MFMAs of every wave)
+  if (tile_m == 256) return run_pipe<1, 256, 256, 2, 4, 64, 2>(g, s);
+  if (tile_m == 128) return run_pipe<1, 128, 256, 2, 2, 32, 3>(g, s);
   return hipErrorInvalidValue;
 }
 
 hipError_t launch_pipe_gemm2(const GemmArgs& g, int tile_m, hipStream_t s) {
   if (g.w_scale) {
-    if (tile_m == 256) return run_pipe<2, 256, 256, 2, 2, 64, 3, 0, 1>(g, s);
-    if (tile_m == 128) return run_pipe<2, 128, 256, 2, 2, 64, 4, 0, 1>(g, s);
+    if (tile_m == 256) return run_pipe<2, 256, 256, 2, 2, 64, 3, 1>(g, s);
+    if (tile_m == 128) return run_pipe<2, 128, 256, 2, 2, 64, 4, 1>(g, s);
     return hipErrorInvalidValue;
   }
-  // 8 waves as GEMM1; no L2 prefetch (Mixtral-8x7B shape: 1.08 ms against 1.15 ms for 4
-  // waves with a prefetch two stages ahead)
-  if (tile_m == 256) return run_pipe<2, 256, 256, 2, 4, 64, 2, 0>(g, s);
-  if (tile_m == 128) return run_pipe<2, 128, 256, 2, 2, 32, 3, 0>(g, s);
+  // the ping-pong schedule as GEMM1 (Mixtral-8x7B shape: 1.00 ms against 1.08 ms)
+  if (tile_m == 256) return run_pipe<2, 256, 256, 2, 4, 64, 2>(g, s);
+  if (tile_m == 128) return run_pipe<2, 128, 256, 2, 2, 32, 3>(g, s);
   return hipErrorInvalidValue;
 }
 
