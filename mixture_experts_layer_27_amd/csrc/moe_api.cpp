@@ -119,14 +119,18 @@ int preferred_bm(int T, int H, int I, int E, int k, moe_dtype dt) {
   if (dt == MOE_F32) return 16;
   if (auto_variant(T, H, I, E, k, dt) == MOE_VARIANT_DECODE)
     return moe::decode_block_m(static_cast<int>(static_cast<int64_t>(T) * k), E);
-  // 256-row MFMA tiles halve the weight-tile reloads per row but pad each expert's last
-  // tile further.  Measured crossovers (average rows per expert): bf16 weights gain from
-  // 128 rows (level there on the gpt-oss shape, H = 2880); FP8 weights, whose 128-row
-  // tiles already stream half the bytes, gain only from 1024.
+  // 256-row MFMA tiles halve the weight-tile reloads per row and, with bf16 weights, run
+  // the ping-pong schedule, but pad each expert's last tile further.  Measured crossovers
+  // (average rows per expert, layer time with 128- vs 256-row tiles): with a few large
+  // experts (E = 8, I = 14336) 256 rows win from 32 rows (0.752 vs 0.695 ms at 32, 0.768
+  // vs 0.724 at 64); with E = 128 small experts 128 rows still win at 32 (1.063 vs 1.080
+  // ms, H = 4096, I = 1536) and 64 (1.166 vs 1.188; level at H = 2880) and lose from 96
+  // (1.327 vs 1.249).  FP8 weights, whose 128-row tiles already stream half the bytes,
+  // gain only from 1024.
   (void)H;
   const int64_t avg = static_cast<int64_t>(T) * k / E;
   if (dt == MOE_BF16_FP8W) return avg >= 1024 ? 256 : 128;
-  return avg >= 128 ? 256 : 128;
+  return avg >= (E <= 32 ? 32 : 96) ? 256 : 128;
 }
 
 int resolve_variant(int variant, int T, int H, int I, int E, int k, moe_dtype dt) {
