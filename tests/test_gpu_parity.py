@@ -593,6 +593,25 @@ def test_layer_prefill_split_round(lib, name, seed):
     _layer_vs_oracle(lib, wl, lay)
 
 
+@pytest.mark.parametrize("dtype,T,H,I", [("bf16", 700, 64, 192), ("bf16", 700, 192, 64),
+                                         ("bf16", 700, 320, 128), ("bf16", 700, 256, 320),
+                                         ("bf16_fp8w", 1100, 128, 384),
+                                         ("bf16_fp8w", 1100, 384, 128),
+                                         ("bf16_fp8w", 1100, 256, 640)])
+def test_layer_pingpong_short_k(lib, dtype, T, H, I):
+    """256-row tiles (the ping-pong K loops) over K loops of 1 to 10 stages of 64 elements:
+    each wave row runs a loop peeled by whether its compute phases refill, with the first
+    and last stages special.  About 175 (bf16) or 275 (FP8) rows per expert make each
+    expert's tile partly padding, and GEMM2's few tiles form a short last round that the
+    layer splits in K, so single-stage parts starting at kb > 0 run too.  Against the
+    oracle on every element."""
+    wl = S.WORKLOADS["mixtral"].scaled(T=T, H=H, I=I, dtype=dtype)
+    dt = lib.BF16_FP8W if dtype == "bf16_fp8w" else lib.BF16
+    assert lib.moe_preferred_block_m(T, H, I, wl.E, wl.k, dt) == 256
+    lay = S.make_layer(wl, device=DEV, seed=11)
+    _layer_vs_oracle(lib, wl, lay)
+
+
 @pytest.mark.parametrize("name,T,scale", [("deepseek_decode_fp8", 1, 4),
                                           ("deepseek_decode_fp8", 8, 4),
                                           ("deepseek_decode_fp8", 64, 4),
