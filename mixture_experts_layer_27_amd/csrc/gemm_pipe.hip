@@ -27,8 +27,8 @@
 //   same page prices an expert at one byte per weight): the B tile is staged as bytes
 //   (64-byte LDS rows per 64-element stage, half the bf16 tile, so the 256-row tile fits
 //   a 3-stage ring), each 16-byte chunk is expanded to bf16 after the LDS read (exact,
-//   in the load phase of the ping-pong) and feeds two bf16 MFMAs, and the row scales (staged in LDS with the tile's rows)
-//   multiply the fp32 accumulators in the epilogue.
+//   in the load phase of the ping-pong) and feeds two bf16 MFMAs, and the row scales
+//   (staged in LDS with the tile's rows) multiply the fp32 accumulators in the epilogue.
 #include <algorithm>
 #include <atomic>
 #include <type_traits>
@@ -398,20 +398,21 @@ moe_gemm_pipe_kernel(PArgs p) {
 
   const int wm = w / WN, wn = w % WN;
   // The 32-row fragments holding routed rows (the rest of the tile is padding, whose
-  // MFMAs and A-operand reads are skipped).  With bf16 weights they are split evenly over
-  // the two wave rows, the first row taking the odd one: an expert's last tile, partly
-  // padding, then keeps both waves of every SIMD issuing MFMAs instead of leaving the
-  // second row idle.  The FP8 tiles always run their fragments whole, at fixed rows.
+  // MFMAs and A-operand reads are skipped).  With bf16 weights, and in the 8-wave FP8
+  // tiles, they are split evenly over the two wave rows, the first row taking the odd one:
+  // an expert's last tile, partly padding, then keeps both waves of every SIMD issuing
+  // MFMAs instead of leaving the second row idle.  The 4-wave FP8 tiles run their
+  // fragments whole, at fixed rows.
   static_assert(WM == 2, "two wave rows");
   int wr0 = wm * C::WTM, nown = C::FM;             // first tile row, fragments owned
-  if constexpr (WB == 2) {
+  if constexpr (WB == 2 || C::NW == 8) {
     const int nf = min(2 * C::FM, (nv + 31) >> 5);
     const int fa = min(C::FM, (nf + 1) >> 1);
     wr0 = wm == 0 ? 0 : 32 * fa;
     nown = wm == 0 ? fa : nf - fa;
   }
   const int na = __builtin_amdgcn_readfirstlane(
-      WB == 2 ? nown : min(C::FM, max(0, (nv - wr0 + 31) >> 5)));
+      (WB == 2 || C::NW == 8) ? nown : min(C::FM, max(0, (nv - wr0 + 31) >> 5)));
   f32x16 acc[C::FM][C::FN];
 #pragma unroll
   for (int i = 0; i < C::FM; ++i)
@@ -802,8 +803,9 @@ moe_gemm_pipe_kernel(PArgs p) {
   }
 
   };
-  // (FP8 tiles always run the full-tile loop: the second instance would not fit their registers)
-  if (WB == 1 || na == C::FM) kloop(T_{});
+  // (the 4-wave FP8 tiles always run the full-tile loop: a second instance would not fit
+  // their registers)
+  if ((WB == 1 && C::NW == 4) || na == C::FM) kloop(T_{});
   else kloop(F_{});
   if (MODE == 2 && WB == 2 && unit < 0) {
     if (tid < BM) swt[tid] = wrow;
