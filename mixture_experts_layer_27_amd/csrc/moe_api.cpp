@@ -126,11 +126,12 @@ int preferred_bm(int T, int H, int I, int E, int k, moe_dtype dt) {
   // vs 0.724 at 64); with E = 128 small experts 128 rows still win at 32 (1.063 vs 1.080
   // ms, H = 4096, I = 1536) and 64 (1.166 vs 1.188; level at H = 2880) and lose from 96
   // (1.327 vs 1.249).  FP8 weights, whose 128-row tiles already stream half the bytes,
-  // gain later: with E = 8 from 256 rows (0.68 vs 0.77 ms at 128, 1.07 vs 1.01 at 256),
-  // with E = 256 (H = 7168, I = 2048) from 128 (2.50 vs 2.68 ms at 64, 4.21 vs 4.04 at 128).
+  // gain later: with E = 8 from 256 rows (0.669 vs 0.684 ms at 128, 1.056 vs 0.905 at
+  // 256), with E = 256 (H = 7168, I = 2048) from 64 (2.48 vs 2.32 ms at 64; 1.71 vs 1.97
+  // at 32 before the 256-row FP8 tiles skipped their padding fragments).
   (void)H;
   const int64_t avg = static_cast<int64_t>(T) * k / E;
-  if (dt == MOE_BF16_FP8W) return avg >= (E <= 32 ? 256 : 128) ? 256 : 128;
+  if (dt == MOE_BF16_FP8W) return avg >= (E <= 32 ? 256 : 64) ? 256 : 128;
   return avg >= (E <= 32 ? 32 : 96) ? 256 : 128;
 }
 
