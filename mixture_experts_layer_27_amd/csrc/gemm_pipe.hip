@@ -5,22 +5,21 @@
 // * Global -> LDS without registers: global_load_lds_dwordx4 writes each lane's 16 bytes
 //   at (wave base + 16 * lane), so the LDS swizzle is applied on the global side: lane i
 //   of an instruction fetches the logical chunk that belongs at physical slot i.
-// * NSTAGE-deep ring of BK-element stages: BK = 64 (128-byte LDS rows, chunk c of row m
-//   at c ^ ((m >> 1) & 7)) for 256-row tiles, BK = 32 (64-byte rows, c ^ sw4(m)) for
-//   128-row tiles, whose 73 KB ring lets two work-groups share a CU; both swizzles are
+// * A ring of 64-element stages: 128-byte LDS rows (bf16; chunk c of row m at
+//   c ^ ((m >> 1) & 7)) and 64-byte rows (FP8 B; c ^ sw4(m)); both swizzles are
 //   conflict-free for the DMA writes and the 32-row MFMA operand reads.
 // * v_mfma_f32_32x32x16_bf16, WM x WN waves each holding a (BM/WM) x (BN/WN) fp32
 //   accumulator tile; GEMM1 B tiles interleave 32-row gate and up blocks so that SwiGLU
 //   runs in registers.
-// * 256-row tiles: 2 x 4 waves (two per SIMD, 128 x 64 each) in a ping-pong schedule over
-//   two 64-element stages (bf16 weights) or three (FP8 weights): the two waves of a SIMD
-//   alternate between loading a half-stage of fragments from LDS and a burst of MFMAs
-//   from registers, with a barrier at each turn and the DMAs between the MFMAs (see the
-//   K loop).
-// * Other tiles: 2 x 2 waves (one per SIMD, up to 128 x 128) and a ring of three or four
-//   stages, one barrier per stage preceded by an explicit vmcnt wait for the wave's own
-//   loads and placed before the stage's last k16 step; LDS fragments are double-buffered
-//   in registers and the reads of the next k16 step are spread between the MFMAs of this
+// * 256-row tiles and bf16 128-row tiles: 2 x 4 waves (two per SIMD, 128 x 64 or 64 x 64
+//   each) in a ping-pong schedule over two 64-element stages (bf16 256-row) or three
+//   (FP8 256-row, bf16 128-row): the two waves of a SIMD alternate between loading a
+//   half-stage of fragments from LDS and a burst of MFMAs from registers, with a barrier
+//   at each turn and the DMAs between the MFMAs (see the K loop).
+// * FP8 128-row tiles: 2 x 2 waves (one per SIMD, 64 x 128) and a ring of four stages, one
+//   barrier per stage preceded by an explicit vmcnt wait for the wave's own loads and
+//   placed before the stage's last k16 step; LDS fragments are double-buffered in
+//   registers and the reads of the next k16 step are spread between the MFMAs of this
 //   one.
 // * GEMM2 splits a short last round of tiles in K over every CU (see split_plan).
 // * FP8 expert weights (OCP E4M3 bytes, one fp32 scale per weight row; section 8 of the
@@ -68,7 +67,7 @@ template <int MODE, int BM, int BN, int WM, int WN, int BK_, int NSTAGE, int WB 
 struct PCfg {
   static constexpr int NW = WM * WN;
   static constexpr int NT = NW * kWave;
-  static constexpr int BK = BK_;                      // K elements per stage (32 or 64)
+  static constexpr int BK = BK_;                      // K elements per stage (64)
   static constexpr int ROWA = BK * 2;                 // bytes per LDS row of A (bf16)
   static constexpr int ROWB = BK * WB;                // bytes per LDS row of B (bf16 / E4M3)
   static constexpr int CPRA = ROWA / 16, CPRB = ROWB / 16;   // 16-byte chunks per row
@@ -83,8 +82,7 @@ struct PCfg {
   static constexpr int SA = BM * ROWA, SB = BN * ROWB;
   static constexpr int STAGE = SA + SB;
   static constexpr int EXTRA = BM * 4 + (MODE == 2 ? BM * 4 : 0) + (WB == 1 ? BN * 4 : 0);
-  static_assert(BK == 32 || BK == 64, "stage depth");
-  static_assert(WB == 2 || BK == 64, "FP8 tiles: 64-element stages (64-byte B rows)");
+  static_assert(BK == 64, "64-element stages");
   static_assert(BM % (RPIA * NW) == 0 && BN % (RPIB * NW) == 0, "DMA rows per wave");
   static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile");
   static_assert(MODE != 1 || WTN % 64 == 0, "GEMM1 wave tile holds gate/up pairs");
@@ -252,12 +250,11 @@ __device__ __forceinline__ void strip_tile(int q, int mreal, int nblocks, int& m
   }
 }
 
-// Two waves per SIMD: with 32-element stages (two work-groups per CU) and with 8-wave
-// work-groups (bf16 256 x 256 tiles: each wave a 128 x 64 accumulator, the two waves of a
-// SIMD taking turns at the MFMA pipe, see the ping-pong K loop); the register budget is
-// held to that
+// Two waves per SIMD with 8-wave work-groups (the ping-pong tiles: the two waves of a SIMD
+// take turns at the MFMA pipe, see the K loop); the register budget is held to that.  One
+// work-group per CU in every configuration (its ring takes 128 or 144 KB of LDS).
 template <int MODE, int BM, int BN, int WM, int WN, int BK, int NSTAGE, int WB>
-__global__ void __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu((BK == 32 || WM * WN == 8) ? 2 : 1)))
+__global__ void __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(WM * WN == 8 ? 2 : 1)))
 moe_gemm_pipe_kernel(PArgs p) {
   using C = PCfg<MODE, BM, BN, WM, WN, BK, NSTAGE, WB>;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[NSTAGE * C::STAGE];
@@ -485,33 +482,6 @@ moe_gemm_pipe_kernel(PArgs p) {
     }
   };
 
-  // The MFMAs of fragments f (bf16 weights) with the LDS reads of the next k16 step's
-  // fragments g spread between them, so the operand reads of the waves sharing a SIMD do
-  // not arrive at the LDS in one burst; with two waves per SIMD the MFMA cluster runs at
-  // raised issue priority.
-  auto mfma_reads = [&](auto full, const auto& f, int kt, int ks, auto& g) {
-    static_assert(WB == 2, "bf16 weights");
-    const uint8_t* sa = smem + (kt % NSTAGE) * C::STAGE;
-    const uint8_t* sb = sa + C::SA;
-    const int ch = 2 * ks + (lane >> 5);
-    constexpr int NM = C::FM * C::FN;
-    if constexpr (C::NW == 8) __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-    for (int q = 0; q < NM; ++q) {
-      const int i = q / C::FN, j = q % C::FN;
-      if (decltype(full)::value || i < na)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
-      if (q < C::FM) {
-        if (decltype(full)::value || q < na)
-          g.a[q] = *reinterpret_cast<const bf16x8*>(sa + pswz<C::ROWA>(wr0 + q * 32 + (lane & 31), ch));
-      } else if (q < C::FM + C::FN) {
-        g.b[q - C::FM] = *reinterpret_cast<const bf16x8*>(
-            sb + pswz<C::ROWB>(wn * C::WTN + (q - C::FM) * 32 + (lane & 31), ch));
-      }
-    }
-    if constexpr (C::NW == 8) __builtin_amdgcn_s_setprio(0);
-  };
-
   // Fragments are double-buffered in registers: the reads of k16 step q+1 are issued
   // before the MFMAs of step q.  sched_barrier(0) pins each group in place so the
   // scheduler does not sink the reads next to their first use (exposing LDS latency).
@@ -522,32 +492,39 @@ moe_gemm_pipe_kernel(PArgs p) {
   // The K loop, instantiated for full tiles and for a tile whose last fragments are padding
   auto kloop = [&](auto full) {
 
-  if constexpr (C::NW == 8 && WB == 1) {
-    // Ping-pong for FP8 weights over a three-stage ring of 64-element stages (128-byte A
-    // rows, 64-byte B rows of E4M3 bytes: 48 KB a stage).  The phases are those of the bf16
-    // two-stage ring below: wave row 0 (waves 0-3) and row 1 (waves 4-7) put one wave of
-    // each row on every SIMD and run half a phase apart; a load phase reads the fragments
-    // of a 32-element half-stage from LDS and expands its B bytes to bf16, a compute phase
-    // runs their 16 MFMAs, a barrier ends each phase and row 1 starts one barrier late.
+  if constexpr (C::NW == 8 && NSTAGE == 3) {
+    // Ping-pong over a three-stage ring of 64-element stages, 48 KB each: the FP8 256-row
+    // tile (128-byte A rows, 64-byte B rows of E4M3 bytes) and the bf16 128-row tile.  The
+    // phases are those of the bf16 two-stage ring below: wave row 0 (waves 0-3) and row 1
+    // (waves 4-7) put one wave of each row on every SIMD and run half a phase apart; a
+    // load phase reads the fragments of a 32-element half-stage from LDS (and expands FP8
+    // B bytes to bf16), a compute phase runs their MFMAs, a barrier ends each phase and
+    // row 1 starts one barrier late.
     // With three stages each wave keeps its usual share of every stage's DMAs: stage S is
     // read out at barrier 4S+4 and its slot takes stage S+3, whose share row 1 issues in
     // its next compute phase (half-stage 2S+1) and row 0 in its (half-stage 2S+2); stage
     // S+3 is first read after barrier 4S+12, so both have about seven phases of latency to
     // cover.  Before barrier 4X (stage X first read) a wave has issued its share up to
     // stage X+1, which may stay in flight.  Every wave passes 4 nk + 1 barriers here.
-    static_assert(NSTAGE == 3 && C::KS == 4 && NSTEP == 2, "three 64-element FP8 stages");
-    constexpr int NM = 2 * C::FM * C::FN;               // MFMAs per compute phase (16)
+    static_assert(C::KS == 4 && NSTEP == (WB == 1 ? 2 : 4), "64-element stages");
+    constexpr int NM = 2 * C::FM * C::FN;               // MFMAs per compute phase
     const int grp = __builtin_amdgcn_readfirstlane(wm);
-    bf16x8 bq0[C::FN], bq1[C::FN];                      // the half-stage's B, expanded
+    bf16x8 bq0[C::FN], bq1[C::FN];                      // FP8: the half-stage's B, expanded
     auto load = [&](int S, int h) {
-      read_frags(full, S, h, fr[0]);
-      wait_lgkm0();
+      if constexpr (WB == 1) {
+        read_frags(full, S, h, fr[0]);
+        wait_lgkm0();
 #pragma unroll
-      for (int j = 0; j < C::FN; ++j) fp8x16_to_bf16x2(fr[0].q[j], bq0[j], bq1[j]);
-      __builtin_amdgcn_sched_barrier(0);     // the expansion stays in the load phase
+        for (int j = 0; j < C::FN; ++j) fp8x16_to_bf16x2(fr[0].q[j], bq0[j], bq1[j]);
+        __builtin_amdgcn_sched_barrier(0);   // the expansion stays in the load phase
+      } else {
+        read_frags(full, S, 2 * h, fr[0]);
+        read_frags(full, S, 2 * h + 1, fr[1]);
+        wait_lgkm0();
+      }
     };
-    // all first-k16 MFMAs, then all second-k16 ones (dependent MFMAs 8 apart); with
-    // refill, DMA d of this wave's share of stage S2 after MFMA (8 d) / 3
+    // all first-k16 MFMAs, then all second-k16 ones (dependent MFMAs FM x FN apart); with
+    // refill, DMA d of this wave's share of stage S2 after MFMA (NM d) / L
     auto compute = [&](auto refill, int S2) {
       uint8_t* st = smem + (S2 % NSTAGE) * C::STAGE;
       const int k0 = S2 * C::BK;
@@ -555,9 +532,13 @@ moe_gemm_pipe_kernel(PArgs p) {
 #pragma unroll
       for (int q = 0; q < NM; ++q) {
         const int half = q / (C::FM * C::FN), i = (q / C::FN) % C::FM, j = q % C::FN;
-        if (decltype(full)::value || i < na)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(half ? fr[0].a1[i] : fr[0].a0[i],
-                                                              half ? bq1[j] : bq0[j], acc[i][j], 0, 0, 0);
+        if (decltype(full)::value || i < na) {
+          if constexpr (WB == 1)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(half ? fr[0].a1[i] : fr[0].a0[i],
+                                                                half ? bq1[j] : bq0[j], acc[i][j], 0, 0, 0);
+          else
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[half].a[i], fr[half].b[j], acc[i][j], 0, 0, 0);
+        }
         if constexpr (decltype(refill)::value) {
 #pragma unroll
           for (int d = 0; d < C::L; ++d) {
@@ -757,7 +738,7 @@ moe_gemm_pipe_kernel(PArgs p) {
     }
     wait_vm_c<0>();
   } else {
-    static_assert(NSTAGE >= 3, "ring depth");
+    static_assert(NSTAGE >= 3 && WB == 1, "the 4-wave ring runs the FP8 128-row tile");
     // Ring of NSTAGE stages, NSTAGE-1 in flight.  The barrier that publishes stage kt+1
     // sits before the last k16 step of stage kt, so the first fragments of kt+1 are read
     // while that step computes.  The slot refilled after it, (kt+NSTAGE-1) % NSTAGE, held
@@ -769,11 +750,6 @@ moe_gemm_pipe_kernel(PArgs p) {
     auto stage = [&](auto has_next, auto refill, int kt, int vm_allowed) {
 #pragma unroll
       for (int ks = 0; ks < NSTEP; ++ks) {
-        if (WB == 2 && ks + 1 < NSTEP) {
-          if constexpr (WB == 2) mfma_reads(full, fr[ks & 1], kt, ks + 1, fr[(ks + 1) & 1]);
-          __builtin_amdgcn_sched_barrier(0);
-          continue;
-        }
         if (ks + 1 < NSTEP) {
           read_frags(full, kt, ks + 1, fr[(ks + 1) & 1]);
         } else if constexpr (decltype(has_next)::value) {
@@ -975,9 +951,7 @@ hipError_t run_pipe(const GemmArgs& g, hipStream_t s) {
   if (G == 0) return hipSuccess;
   p.split_max = 1;
   if (MODE == 2 && g.split_ws) {
-    // 4-wave work-groups with 32-element stages run two per CU (two waves per SIMD, 72 KB
-    // of LDS each); the others one
-    const int ncu = device_cu_count() * (BK == 32 && WM * WN == 4 ? 2 : 1);
+    const int ncu = device_cu_count();              // one work-group per CU
     if (ncu > 0 && g.split_ws_bytes >= static_cast<size_t>(ncu) * BM * BN * sizeof(float)) {
       p.split_max = 4;
       p.ncu = ncu;
@@ -1011,7 +985,9 @@ hipError_t launch_pipe_gemm1(const GemmArgs& g, int tile_m, hipStream_t s) {
   // (Mixtral-8x7B shape: 1.70 ms against 1.84 ms for the same 8 waves with the operand
   // reads and DMAs spread between the MFMAs of every wave)
   if (tile_m == 256) return run_pipe<1, 256, 256, 2, 4, 64, 2>(g, s);
-  if (tile_m == 128) return run_pipe<1, 128, 256, 2, 2, 32, 3>(g, s);
+  // 128-row tile: the same 8 waves over three 64-element stages (Qwen3 shape, T = 1024:
+  // layer 1.12 ms against 1.17 ms for 4 waves over 32-element stages, two work-groups a CU)
+  if (tile_m == 128) return run_pipe<1, 128, 256, 2, 4, 64, 3>(g, s);
   return hipErrorInvalidValue;
 }
 
@@ -1023,7 +999,7 @@ hipError_t launch_pipe_gemm2(const GemmArgs& g, int tile_m, hipStream_t s) {
   }
   // the ping-pong schedule as GEMM1 (Mixtral-8x7B shape: 1.00 ms against 1.08 ms)
   if (tile_m == 256) return run_pipe<2, 256, 256, 2, 4, 64, 2>(g, s);
-  if (tile_m == 128) return run_pipe<2, 128, 256, 2, 2, 32, 3>(g, s);
+  if (tile_m == 128) return run_pipe<2, 128, 256, 2, 4, 64, 3>(g, s);
   return hipErrorInvalidValue;
 }
 

@@ -119,20 +119,19 @@ int preferred_bm(int T, int H, int I, int E, int k, moe_dtype dt) {
   if (dt == MOE_F32) return 16;
   if (auto_variant(T, H, I, E, k, dt) == MOE_VARIANT_DECODE)
     return moe::decode_block_m(static_cast<int>(static_cast<int64_t>(T) * k), E);
-  // 256-row MFMA tiles halve the weight-tile reloads per row and, with bf16 weights, run
-  // the ping-pong schedule, but pad each expert's last tile further.  Measured crossovers
-  // (average rows per expert, layer time with 128- vs 256-row tiles): with a few large
-  // experts (E = 8, I = 14336) 256 rows win from 32 rows (0.752 vs 0.695 ms at 32, 0.768
-  // vs 0.724 at 64); with E = 128 small experts 128 rows still win at 32 (1.063 vs 1.080
-  // ms, H = 4096, I = 1536) and 64 (1.166 vs 1.188; level at H = 2880) and lose from 96
-  // (1.327 vs 1.249).  FP8 weights, whose 128-row tiles already stream half the bytes,
-  // gain later: with E = 8 from 256 rows (0.669 vs 0.684 ms at 128, 1.056 vs 0.905 at
-  // 256), with E = 256 (H = 7168, I = 2048) from 64 (2.48 vs 2.32 ms at 64; 1.71 vs 1.97
-  // at 32 before the 256-row FP8 tiles skipped their padding fragments).
+  // 256-row MFMA tiles halve the weight-tile reloads per row but pad each expert's last
+  // tile further; both heights run the ping-pong schedule with bf16 weights.  Measured
+  // crossovers (average rows per expert, layer time with 128- vs 256-row tiles): with a
+  // few large experts (E = 8, I = 14336) 128 rows win up to 128 (0.796 vs 0.824 ms) and lose
+  // at 256 (1.185 vs 1.047); with E = 128 or 256 they are level at 128 (Qwen3 1.354 vs
+  // 1.344, gpt-oss 1.805 vs 1.844, DeepSeek-V3 4.25 vs 3.98) and lose from 192 (Qwen3
+  // 1.675 vs 1.501).  FP8 weights (128-row tiles on four waves, 256-row on the ping-pong):
+  // with E = 8 from 256 rows (0.669 vs 0.684 ms at 128, 1.056 vs 0.905 at 256), with
+  // E = 256 (H = 7168, I = 2048) from 64 (2.48 vs 2.32 ms at 64).
   (void)H;
   const int64_t avg = static_cast<int64_t>(T) * k / E;
   if (dt == MOE_BF16_FP8W) return avg >= (E <= 32 ? 256 : 64) ? 256 : 128;
-  return avg >= (E <= 32 ? 32 : 96) ? 256 : 128;
+  return avg >= (E <= 32 ? 256 : 128) ? 256 : 128;
 }
 
 int resolve_variant(int variant, int T, int H, int I, int E, int k, moe_dtype dt) {

@@ -593,21 +593,26 @@ def test_layer_prefill_split_round(lib, name, seed):
     _layer_vs_oracle(lib, wl, lay)
 
 
-@pytest.mark.parametrize("dtype,T,H,I", [("bf16", 700, 64, 192), ("bf16", 700, 192, 64),
-                                         ("bf16", 700, 320, 128), ("bf16", 700, 256, 320),
-                                         ("bf16_fp8w", 1100, 128, 384),
-                                         ("bf16_fp8w", 1100, 384, 128),
-                                         ("bf16_fp8w", 1100, 256, 640)])
-def test_layer_pingpong_short_k(lib, dtype, T, H, I):
-    """256-row tiles (the ping-pong K loops) over K loops of 1 to 10 stages of 64 elements:
+@pytest.mark.parametrize("dtype,T,H,I,bm", [("bf16", 1100, 64, 192, 256),
+                                            ("bf16", 1100, 192, 64, 256),
+                                            ("bf16", 1100, 320, 128, 256),
+                                            ("bf16", 1100, 256, 320, 256),
+                                            ("bf16", 700, 64, 192, 128),
+                                            ("bf16", 700, 192, 64, 128),
+                                            ("bf16", 700, 320, 256, 128),
+                                            ("bf16_fp8w", 1100, 128, 384, 256),
+                                            ("bf16_fp8w", 1100, 384, 128, 256),
+                                            ("bf16_fp8w", 1100, 256, 640, 256)])
+def test_layer_pingpong_short_k(lib, dtype, T, H, I, bm):
+    """The ping-pong K loops (256-row tiles; bf16 128-row tiles) over 1 to 10 stages of 64:
     each wave row runs a loop peeled by whether its compute phases refill, with the first
-    and last stages special.  About 175 (bf16) or 275 (FP8) rows per expert make each
-    expert's tile partly padding, and GEMM2's few tiles form a short last round that the
-    layer splits in K, so single-stage parts starting at kb > 0 run too.  Against the
+    and last stages special.  About 275 rows per expert (175 with 128-row tiles) leave each
+    expert's last tile partly padding, and GEMM2's few tiles form a short last round that
+    the layer splits in K, so single-stage parts starting at kb > 0 run too.  Against the
     oracle on every element."""
     wl = S.WORKLOADS["mixtral"].scaled(T=T, H=H, I=I, dtype=dtype)
     dt = lib.BF16_FP8W if dtype == "bf16_fp8w" else lib.BF16
-    assert lib.moe_preferred_block_m(T, H, I, wl.E, wl.k, dt) == 256
+    assert lib.moe_preferred_block_m(T, H, I, wl.E, wl.k, dt) == bm
     lay = S.make_layer(wl, device=DEV, seed=11)
     _layer_vs_oracle(lib, wl, lay)
 
