@@ -11,16 +11,11 @@
 // * v_mfma_f32_32x32x16_bf16, WM x WN waves each holding a (BM/WM) x (BN/WN) fp32
 //   accumulator tile; GEMM1 B tiles interleave 32-row gate and up blocks so that SwiGLU
 //   runs in registers.
-// * 256-row tiles and bf16 128-row tiles: 2 x 4 waves (two per SIMD, 128 x 64 or 64 x 64
-//   each) in a ping-pong schedule over two 64-element stages (bf16 256-row) or three
-//   (FP8 256-row, bf16 128-row): the two waves of a SIMD alternate between loading a
-//   half-stage of fragments from LDS and a burst of MFMAs from registers, with a barrier
-//   at each turn and the DMAs between the MFMAs (see the K loop).
-// * FP8 128-row tiles: 2 x 2 waves (one per SIMD, 64 x 128) and a ring of four stages, one
-//   barrier per stage preceded by an explicit vmcnt wait for the wave's own loads and
-//   placed before the stage's last k16 step; LDS fragments are double-buffered in
-//   registers and the reads of the next k16 step are spread between the MFMAs of this
-//   one.
+// * 2 x 4 waves (two per SIMD, 128 x 64 or 64 x 64 each) in a ping-pong schedule over
+//   two 64-element stages (bf16 256-row tiles) or three (the other tiles): the two waves
+//   of a SIMD alternate between loading a half-stage of fragments from LDS and a burst of
+//   MFMAs from registers, with a barrier at each turn and the DMAs between the MFMAs (see
+//   the K loop).
 // * GEMM2 splits a short last round of tiles in K over every CU (see split_plan).
 // * FP8 expert weights (OCP E4M3 bytes, one fp32 scale per weight row; section 8 of the
 //   same page prices an expert at one byte per weight): the B tile is staged as bytes
@@ -252,7 +247,7 @@ __device__ __forceinline__ void strip_tile(int q, int mreal, int nblocks, int& m
 
 // Two waves per SIMD with 8-wave work-groups (the ping-pong tiles: the two waves of a SIMD
 // take turns at the MFMA pipe, see the K loop); the register budget is held to that.  One
-// work-group per CU in every configuration (its ring takes 128 or 144 KB of LDS).
+// work-group per CU in every configuration (its ring takes 96 to 144 KB of LDS).
 template <int MODE, int BM, int BN, int WM, int WN, int BK, int NSTAGE, int WB>
 __global__ void __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(WM * WN == 8 ? 2 : 1)))
 moe_gemm_pipe_kernel(PArgs p) {
@@ -395,21 +390,15 @@ moe_gemm_pipe_kernel(PArgs p) {
 
   const int wm = w / WN, wn = w % WN;
   // The 32-row fragments holding routed rows (the rest of the tile is padding, whose
-  // MFMAs and A-operand reads are skipped).  With bf16 weights, and in the 8-wave FP8
-  // tiles, they are split evenly over the two wave rows, the first row taking the odd one:
-  // an expert's last tile, partly padding, then keeps both waves of every SIMD issuing
-  // MFMAs instead of leaving the second row idle.  The 4-wave FP8 tiles run their
-  // fragments whole, at fixed rows.
-  static_assert(WM == 2, "two wave rows");
-  int wr0 = wm * C::WTM, nown = C::FM;             // first tile row, fragments owned
-  if constexpr (WB == 2 || C::NW == 8) {
-    const int nf = min(2 * C::FM, (nv + 31) >> 5);
-    const int fa = min(C::FM, (nf + 1) >> 1);
-    wr0 = wm == 0 ? 0 : 32 * fa;
-    nown = wm == 0 ? fa : nf - fa;
-  }
-  const int na = __builtin_amdgcn_readfirstlane(
-      (WB == 2 || C::NW == 8) ? nown : min(C::FM, max(0, (nv - wr0 + 31) >> 5)));
+  // MFMAs and A-operand reads are skipped) are split evenly over the two wave rows, the
+  // first row taking the odd one: an expert's last tile, partly padding, then keeps both
+  // waves of every SIMD issuing MFMAs instead of leaving the second row idle.
+  static_assert(WM == 2 && C::NW == 8, "two wave rows of four waves");
+  const int nf = min(2 * C::FM, (nv + 31) >> 5);
+  const int fa = min(C::FM, (nf + 1) >> 1);
+  const int wr0 = wm == 0 ? 0 : 32 * fa;           // first tile row of this wave's fragments
+  const int nown = wm == 0 ? fa : nf - fa;         // fragments owned
+  const int na = __builtin_amdgcn_readfirstlane(nown);
   f32x16 acc[C::FM][C::FN];
 #pragma unroll
   for (int i = 0; i < C::FM; ++i)
@@ -459,32 +448,7 @@ moe_gemm_pipe_kernel(PArgs p) {
       }
     }
   };
-  auto mfma_all = [&](auto full, const Fr& f) {
-    if constexpr (WB == 2) {
-#pragma unroll
-      for (int i = 0; i < C::FM; ++i)
-#pragma unroll
-        for (int j = 0; j < C::FN; ++j)
-          if (decltype(full)::value || i < na) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
-    } else {
-#pragma unroll
-      for (int j = 0; j < C::FN; ++j) {
-        bf16x8 b0, b1;
-        fp8x16_to_bf16x2(f.q[j], b0, b1);
-#pragma unroll
-        for (int i = 0; i < C::FM; ++i) {
-          if (decltype(full)::value || i < na) {
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a0[i], b0, acc[i][j], 0, 0, 0);
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a1[i], b1, acc[i][j], 0, 0, 0);
-          }
-        }
-      }
-    }
-  };
-
-  // Fragments are double-buffered in registers: the reads of k16 step q+1 are issued
-  // before the MFMAs of step q.  sched_barrier(0) pins each group in place so the
-  // scheduler does not sink the reads next to their first use (exposing LDS latency).
+  // the fragments of one half-stage (two k16 steps with bf16 weights, one Frags with FP8)
   Fr fr[2];
   using T_ = std::true_type;
   using F_ = std::false_type;
@@ -492,7 +456,7 @@ moe_gemm_pipe_kernel(PArgs p) {
   // The K loop, instantiated for full tiles and for a tile whose last fragments are padding
   auto kloop = [&](auto full) {
 
-  if constexpr (C::NW == 8 && NSTAGE == 3) {
+  if constexpr (NSTAGE == 3) {
     // Ping-pong over a three-stage ring of 64-element stages, 48 KB each: the FP8 256-row
     // tile (128-byte A rows, 64-byte B rows of E4M3 bytes) and the bf16 128-row tile.  The
     // phases are those of the bf16 two-stage ring below: wave row 0 (waves 0-3) and row 1
@@ -737,51 +701,10 @@ moe_gemm_pipe_kernel(PArgs p) {
       for (; S < nk; ++S) iter(N0{}, S);
     }
     wait_vm_c<0>();
-  } else {
-    static_assert(NSTAGE >= 3 && WB == 1, "the 4-wave ring runs the FP8 128-row tile");
-    // Ring of NSTAGE stages, NSTAGE-1 in flight.  The barrier that publishes stage kt+1
-    // sits before the last k16 step of stage kt, so the first fragments of kt+1 are read
-    // while that step computes.  The slot refilled after it, (kt+NSTAGE-1) % NSTAGE, held
-    // stage kt-1, which every wave finished reading before reaching the barrier.  The
-    // loop is split into branch-free phases so the compiler's LDS wait counts are exact:
-    //   steady (stage kt+NSTAGE-1 exists): wait for kt+1, refill the ring;
-    //   drain  (kt+1 exists, nothing left to issue): wait for kt+1 only;
-    //   last   (kt = nk-1): no barrier.
-    auto stage = [&](auto has_next, auto refill, int kt, int vm_allowed) {
-#pragma unroll
-      for (int ks = 0; ks < NSTEP; ++ks) {
-        if (ks + 1 < NSTEP) {
-          read_frags(full, kt, ks + 1, fr[(ks + 1) & 1]);
-        } else if constexpr (decltype(has_next)::value) {
-          // issued so far: stages 0 .. kt+NSTAGE-2; stage kt+1 must be complete, so
-          // only the NSTAGE-3 stages after it may still be in flight
-          if constexpr (decltype(refill)::value) wait_vm_c<(NSTAGE - 3) * C::L>();
-          else wait_vm(vm_allowed);
-          barrier_keep_vm();
-          if constexpr (decltype(refill)::value) issue(kt + NSTAGE - 1);
-          read_frags(full, kt + 1, 0, fr[0]);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-        mfma_all(full, fr[ks & 1]);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    };
-#pragma unroll
-    for (int s = 0; s < NSTAGE - 1; ++s)
-      if (s < nk) issue(s);
-    wait_vm(min(NSTAGE - 2, nk - 1) * C::L);
-    barrier_keep_vm();
-    read_frags(full, 0, 0, fr[0]);
-    int kt = 0;
-    for (; kt + NSTAGE <= nk; ++kt) stage(T_{}, T_{}, kt, 0);
-    for (; kt + 1 < nk; ++kt) stage(T_{}, F_{}, kt, (min(kt + NSTAGE - 2, nk - 1) - (kt + 1)) * C::L);
-    stage(F_{}, F_{}, kt, 0);
   }
 
   };
-  // (the 4-wave FP8 tiles always run the full-tile loop: a second instance would not fit
-  // their registers)
-  if ((WB == 1 && C::NW == 4) || na == C::FM) kloop(T_{});
+  if (na == C::FM) kloop(T_{});
   else kloop(F_{});
   if (MODE == 2 && WB == 2 && unit < 0) {
     if (tid < BM) swt[tid] = wrow;
@@ -976,9 +899,10 @@ hipError_t run_pipe(const GemmArgs& g, hipStream_t s) {
 hipError_t launch_pipe_gemm1(const GemmArgs& g, int tile_m, hipStream_t s) {
   if (g.w_scale) {     // FP8 weights: the half-size B tile leaves room for a deeper ring
     // 256-row tile: 8 waves in the ping-pong schedule over three stages (Mixtral-8x7B
-    // shape: 1.63 ms against 1.87 ms for 4 waves, one per SIMD)
+    // shape: 1.63 ms against 1.87 ms for 4 waves, one per SIMD; the 128-row tile likewise,
+    // DeepSeek-V3-shaped FP8 layer at T = 1024: 1.50 against 1.65 ms)
     if (tile_m == 256) return run_pipe<1, 256, 256, 2, 4, 64, 3, 1>(g, s);
-    if (tile_m == 128) return run_pipe<1, 128, 256, 2, 2, 64, 4, 1>(g, s);
+    if (tile_m == 128) return run_pipe<1, 128, 256, 2, 4, 64, 3, 1>(g, s);
     return hipErrorInvalidValue;
   }
   // 8 waves (2 x 4, two per SIMD) in the ping-pong schedule for the 256-row tile
@@ -994,7 +918,7 @@ hipError_t launch_pipe_gemm1(const GemmArgs& g, int tile_m, hipStream_t s) {
 hipError_t launch_pipe_gemm2(const GemmArgs& g, int tile_m, hipStream_t s) {
   if (g.w_scale) {
     if (tile_m == 256) return run_pipe<2, 256, 256, 2, 4, 64, 3, 1>(g, s);   // 0.95 against 1.15 ms
-    if (tile_m == 128) return run_pipe<2, 128, 256, 2, 2, 64, 4, 1>(g, s);
+    if (tile_m == 128) return run_pipe<2, 128, 256, 2, 4, 64, 3, 1>(g, s);
     return hipErrorInvalidValue;
   }
   // the ping-pong schedule as GEMM1 (Mixtral-8x7B shape: 1.00 ms against 1.08 ms)
