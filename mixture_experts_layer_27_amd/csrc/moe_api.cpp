@@ -120,17 +120,14 @@ int preferred_bm(int T, int H, int I, int E, int k, moe_dtype dt) {
   if (auto_variant(T, H, I, E, k, dt) == MOE_VARIANT_DECODE)
     return moe::decode_block_m(static_cast<int>(static_cast<int64_t>(T) * k), E);
   // 256-row MFMA tiles halve the weight-tile reloads per row but pad each expert's last
-  // tile further; both heights run the ping-pong schedule with bf16 weights.  Measured
-  // crossovers (average rows per expert, layer time with 128- vs 256-row tiles): with a
-  // few large experts (E = 8, I = 14336) 128 rows win up to 128 (0.796 vs 0.824 ms) and lose
-  // at 256 (1.185 vs 1.047); with E = 128 or 256 they are level at 128 (Qwen3 1.354 vs
-  // 1.344, gpt-oss 1.805 vs 1.844, DeepSeek-V3 4.25 vs 3.98) and lose from 192 (Qwen3
-  // 1.675 vs 1.501).  FP8 weights (128-row tiles on four waves, 256-row on the ping-pong):
-  // with E = 8 from 256 rows (0.669 vs 0.684 ms at 128, 1.056 vs 0.905 at 256), with
-  // E = 256 (H = 7168, I = 2048) from 64 (2.48 vs 2.32 ms at 64).
+  // tile further; both heights run the ping-pong schedule.  Measured crossovers (average
+  // rows per expert, layer time with 128- vs 256-row tiles): with a few large experts
+  // (E = 8, I = 14336) 128 rows win up to 128 (bf16 0.796 vs 0.824 ms, FP8 0.622 vs 0.677)
+  // and lose at 256 (bf16 1.185 vs 1.047, FP8 0.957 vs 0.890); with E = 128 or 256 they
+  // are level at 128 (Qwen3 1.354 vs 1.344, gpt-oss 1.805 vs 1.844, DeepSeek-V3 4.25 vs
+  // 3.98, its FP8 form 3.775 vs 3.701) and lose from 192 (Qwen3 1.675 vs 1.501).
   (void)H;
   const int64_t avg = static_cast<int64_t>(T) * k / E;
-  if (dt == MOE_BF16_FP8W) return avg >= (E <= 32 ? 256 : 64) ? 256 : 128;
   return avg >= (E <= 32 ? 256 : 128) ? 256 : 128;
 }
 

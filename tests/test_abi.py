@@ -199,7 +199,7 @@ def test_fp8_weight_entry_points_validate(L):
     assert lib.moe_preferred_block_m(1024, 4096, 14336, 8, 2, FP8) == 256
     assert lib.moe_preferred_block_m(512, 4096, 14336, 8, 2, FP8) == 128
     assert lib.moe_preferred_block_m(4096, 7168, 2048, 256, 8, FP8) == 256
-    assert lib.moe_preferred_block_m(2048, 7168, 2048, 256, 8, FP8) == 256
+    assert lib.moe_preferred_block_m(2048, 7168, 2048, 256, 8, FP8) == 128
     assert lib.moe_preferred_block_m(1024, 7168, 2048, 256, 8, FP8) == 128
     # bf16 prefill: 256-row tiles from 256 rows per expert on average with E <= 32, from 128
     # with more experts
