@@ -77,8 +77,8 @@ struct GemmArgs {
   size_t split_ws_bytes = 0;
 };
 
-// workspace the split last round of GEMM2 may use (one fp32 tile per work-group in flight:
-// 256 tiles of 256 x 256 or 512 of 128 x 256, i.e. up to 256 CUs)
+// workspace the split last round of GEMM2 may use (one fp32 tile per work-group in flight,
+// one work-group per CU: 256 tiles of up to 256 x 256, i.e. up to 256 CUs)
 constexpr size_t kSplitWsBytes = static_cast<size_t>(256) * 256 * 256 * sizeof(float);
 
 // variant: 1 prefill, 2 decode
