@@ -19,8 +19,8 @@
 // * GEMM2 splits a short last round of tiles in K over every CU (see split_plan).
 // * FP8 expert weights (OCP E4M3 bytes, one fp32 scale per weight row; section 8 of the
 //   same page prices an expert at one byte per weight): the B tile is staged as bytes
-//   (64-byte LDS rows per 64-element stage, half the bf16 tile, so the 256-row tile fits
-//   a 3-stage ring), each 16-byte chunk is expanded to bf16 after the LDS read (exact,
+//   (64-byte LDS rows per 64-element stage, half the bf16 B tile, so the 256-row tile
+//   fits a 3-stage ring), each 16-byte chunk is expanded to bf16 after the LDS read (exact,
 //   in the load phase of the ping-pong) and feeds two bf16 MFMAs, and the row scales
 //   (staged in LDS with the tile's rows) multiply the fp32 accumulators in the epilogue.
 #include <algorithm>
@@ -87,9 +87,9 @@ struct PCfg {
 // LDS swizzles (chunk c of row m lives at physical chunk c ^ sw(m)).  64-byte rows:
 // sw = (m >> 2) & 3; 128-byte rows: sw = (m >> 1) & 7.  Both spread the MFMA operand
 // reads (rows m..m+31 at one logical chunk) over all banks: measured with
-// SQ_LDS_BANK_CONFLICT on the 128-row tiles (Qwen3 shape), (m >> 2) & 3 takes the
-// conflict cycles from half of the LDS-active cycles to none, where
-// ((m >> 1) ^ (m >> 3)) & 3 left them.
+// SQ_LDS_BANK_CONFLICT on 64-byte rows (Qwen3 shape, then in bf16 tiles of 32-element
+// stages), (m >> 2) & 3 takes the conflict cycles from half of the LDS-active cycles to
+// none, where ((m >> 1) ^ (m >> 3)) & 3 left them.
 __device__ __forceinline__ int sw4(int row) { return (row >> 2) & 3; }
 template <int ROWB>
 __device__ __forceinline__ int swz(int row) { return ROWB == 64 ? sw4(row) : ((row >> 1) & 7); }
@@ -457,8 +457,9 @@ moe_gemm_pipe_kernel(PArgs p) {
   auto kloop = [&](auto full) {
 
   if constexpr (NSTAGE == 3) {
-    // Ping-pong over a three-stage ring of 64-element stages, 48 KB each: the FP8 256-row
-    // tile (128-byte A rows, 64-byte B rows of E4M3 bytes) and the bf16 128-row tile.  The
+    // Ping-pong over a three-stage ring of 64-element stages: the FP8 256-row tile (48 KB
+    // stages: 128-byte A rows, 64-byte B rows of E4M3 bytes), the bf16 128-row tile (48 KB)
+    // and the FP8 128-row tile (32 KB).  The
     // phases are those of the bf16 two-stage ring below: wave row 0 (waves 0-3) and row 1
     // (waves 4-7) put one wave of each row on every SIMD and run half a phase apart; a
     // load phase reads the fragments of a 32-element half-stage from LDS (and expands FP8
