@@ -59,6 +59,75 @@ __device__ inline void segment_scatter(const int32_t* __restrict__ ids, int r0, 
   }
 }
 
+// Register-resident forms for the single work-group path, where a wave's segment is at
+// most NC chunks of 64 rows: the ids are loaded once, all at the same time (row
+// r0 + 64 c + lane in idr[c], -1 past r1), and both passes read them from registers
+// instead of walking the segment twice with a memory round trip per chunk.
+template <int NC>
+__device__ __forceinline__ void load_segment(const int32_t* __restrict__ ids, int r0, int r1,
+                                             int (&idr)[NC]) {
+  const int lane = lane_id();
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    const int r = r0 + c * kWave + lane;
+    idr[c] = r < r1 ? ids[r] : -1;
+  }
+}
+
+template <int NC>
+__device__ __forceinline__ void histogram_regs(const int (&idr)[NC], int E,
+                                               int* __restrict__ lds_cnt) {
+#pragma unroll
+  for (int c = 0; c < NC; ++c)
+    if (static_cast<unsigned>(idr[c]) < static_cast<unsigned>(E)) atomicAdd(&lds_cnt[idr[c]], 1);
+}
+
+// The stable scatter of segment_scatter over register-resident ids.  With E <= 64 the
+// cursor of expert e lives in lane e and a chunk takes one ballot per expert, all
+// independent of each other (a row's position: its expert's cursor plus the rows of that
+// expert in lower lanes), then one store, instead of a serial match loop over the experts
+// present; the ranks are the same.
+template <int NC>
+__device__ inline void scatter_regs(const int (&idr)[NC], int r0, int r1, int E,
+                                    int* __restrict__ run, int32_t* __restrict__ sorted_ids) {
+  const int lane = lane_id();
+  const uint64_t lt = lanemask_lt();
+  const bool in_lanes = E <= kWave;
+  int cur = in_lanes && lane < E ? run[lane] : 0;
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    const int base = r0 + c * kWave;
+    if (base >= r1) break;
+    const int r = base + lane;
+    const bool valid = static_cast<unsigned>(idr[c]) < static_cast<unsigned>(E);
+    const int e = valid ? idr[c] : -1;
+    if (in_lanes) {
+      int pos = 0;
+      for (int x = 0; x < E; ++x) {
+        const uint64_t m = __ballot(e == x);
+        if (m == 0) continue;
+        const int start = read_lane(cur, x);
+        if (e == x) pos = start + __popcll(m & lt);
+        if (lane == x) cur = start + __popcll(m);
+      }
+      if (valid) sorted_ids[pos] = r;
+      continue;
+    }
+    uint64_t remaining = __ballot(valid);
+    while (remaining) {
+      const int leader = __ffsll(static_cast<unsigned long long>(remaining)) - 1;
+      const int le = read_lane(e, leader);
+      const uint64_t m = __ballot(e == le);
+      const int start = run[le];                       // every lane reads before the leader writes
+      if (e == le) sorted_ids[start + __popcll(m & lt)] = r;
+      __builtin_amdgcn_wave_barrier();
+      if (lane == leader) run[le] = start + __popcll(m);
+      __builtin_amdgcn_wave_barrier();
+      remaining &= ~m;
+    }
+  }
+}
+
 // Exclusive scan of the padded counts by the first wave: start[e] for every e and
 // *total_out = sum of padded counts.  cnt[e] must be final.
 __device__ inline void scan_padded(const int* __restrict__ cnt, int E, int bm,
@@ -128,12 +197,19 @@ __device__ inline void align_small_body(const int32_t* ids, int R, int E, int bm
   // contiguous segments, one per wave, in ascending row order
   const int per = (R + kAlignWaves - 1) / kAlignWaves;
   const int r0 = min(R, w * per), r1 = min(R, r0 + per);
+  // the callers keep R <= 8192, so a segment fits in registers; the loads are issued
+  // first and complete under the clearing below
+  constexpr int kChunks = 8;
+  const bool regs = per <= kChunks * kWave;
+  int idr[kChunks];
+  if (regs) load_segment(ids, r0, r1, idr);
   for (int i = threadIdx.x; i < kAlignWaves * kMaxE; i += blockDim.x) {
     if ((i & (kMaxE - 1)) < E) (&hist[0][0])[i] = 0;
   }
   for (int64_t p = threadIdx.x; p < cap; p += blockDim.x) sorted_ids[p] = R;
   __syncthreads();
-  segment_histogram(ids, r0, r1, E, hist[w]);
+  if (regs) histogram_regs(idr, E, hist[w]);
+  else segment_histogram(ids, r0, r1, E, hist[w]);
   __syncthreads();
   for (int e = threadIdx.x; e < E; e += blockDim.x) {
     int s = 0;
@@ -159,7 +235,8 @@ __device__ inline void align_small_body(const int32_t* ids, int R, int E, int bm
   if (threadIdx.x == 0) *ntpp = total;
   fill_expert_ids(cnt, start, E, bm, total, cap, expert_ids, emap, tile_run);
   __syncthreads();
-  segment_scatter(ids, r0, r1, E, hist[w], sorted_ids);
+  if (regs) scatter_regs(idr, r0, r1, E, hist[w], sorted_ids);
+  else segment_scatter(ids, r0, r1, E, hist[w], sorted_ids);
 }
 
 }  // namespace alignd

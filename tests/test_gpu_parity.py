@@ -47,6 +47,8 @@ def test_align_worked_example(lib):
 @pytest.mark.parametrize("T,k,E,skew", [
     (1, 8, 256, 0.0), (16, 8, 256, 0.0), (64, 8, 256, 0.5), (37, 1, 8, 0.0), (64, 2, 8, 0.0),
     (1000, 8, 128, 1.2),          # single work-group path, skewed
+    (513, 4, 64, 0.3),            # E = 64: run cursors held in lanes, ragged last chunk
+    (513, 4, 65, 0.0),            # E = 65: run cursors in LDS
     (2048, 8, 256, 0.0),          # R = 16384: multi-launch path
     (8192, 8, 128, 0.0),          # R = 65536: multi-launch path, many segments
     (4096, 2, 8, 0.0),            # R = 8192: largest single work-group case
